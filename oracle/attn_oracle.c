@@ -1,0 +1,546 @@
+/*
+ * attn_oracle.c -- plain fp64 CPU reference for attention and its gradient.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU product path
+ * never calls it and shares no code, header or constant with it.
+ *
+ * What it computes (per sequence s and query head h, KV head g = h / (H/Hk)):
+ *
+ *   S_ij  = scale * sum_d Q_id K_jd                       (scores)
+ *   visible(i,j) = !causal || j <= i + Lk - Lq            (bottom-right causal)
+ *   LSE_i = log sum_{visible j} exp(S_ij)                 (-inf if none visible)
+ *   P_ij  = exp(S_ij - LSE_i) if visible else 0           (softmax)
+ *   O_i   = sum_j P_ij V_j
+ *
+ *   backward of f = sum(dO * O):
+ *   dP_ij = sum_d dO_id V_jd
+ *   dS_i  = J_i dP_i,   J_i = diag(P_i) - P_i P_i^T       (softmax Jacobian)
+ *   dQ_i  = scale * sum_j dS_ij K_j
+ *   dK_j  = scale * sum_{h in group g} sum_i dS^(h)_ij Q^(h)_i
+ *   dV_j  =         sum_{h in group g} sum_i P^(h)_ij dO^(h)_i
+ *
+ * Passages followed (page titles as listed in the design notes):
+ *   - sm90 backward kernel page (FlashAttentionBackwardSm90), mma_one_m_block:
+ *     the five products S = Q K^T, dP = dO V^T, dV += P^T dO, dQ = dS K,
+ *     dK += dS^T Q, the pointwise P = exp(S - LSE) and dS = P (dP - rowsum);
+ *     epilogue_dKV for the single final softmax_scale on dK.
+ *   - Triton FA2 teaching page, backward dQ kernel: dq is multiplied by the
+ *     softmax scale once at the end.
+ *   - GQA/MQA page, causal block bound: the key limit of query row i is
+ *     i + seqlen_k - seqlen_q (bottom-right alignment); backward GQA section:
+ *     dK/dV of the query heads are summed over each head group.
+ *   - Backward call-trace page, GQA reduce: the group sum over the H/Hk heads.
+ *
+ * Two backward evaluations are provided and tested against each other:
+ *   oracle_backward_explicit -- materialises P, dP and each row's Jacobian
+ *                               J_i (O(Lk^2) per row; small inputs only);
+ *   oracle_backward          -- the same Jacobian-vector product written as
+ *                               dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik), row
+ *                               pass for dQ, key pass for dK/dV; any size.
+ * Neither uses the GPU's rowsum(dO * O) shortcut; that identity is checked by
+ * the tests, not assumed.
+ *
+ * Layouts: tokens-major packed rows.  q, dout, out, dq: [total_q][H][D];
+ * k, v, dk, dv: [total_k][Hk][D]; lse, dj: [total_q][H].  Sequence s owns
+ * rows cu_q[s] .. cu_q[s+1]-1 (and cu_k likewise).  A dense batch of B
+ * sequences of equal length is the special case cu_q = {0, Sq, 2Sq, ...}.
+ * All inputs are fp64 (bf16 values upcast exactly by the caller).
+ *
+ * Optional `mask` (only with nseq == 1): additive [Lq][Lk] matrix of 0 / -inf
+ * applied to every head on top of the causal rule; used by the tests to show
+ * that the causal rule equals an explicit -inf mask.
+ *
+ * Return value: 0 on success, -1 on bad arguments, -2 on allocation failure.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Dot product over the head dimension.  Fixed summation order: four
+ * interleaved partial sums (d = 0,4,8.. / 1,5,9.. / ...) added as
+ * (p0 + p1) + (p2 + p3), then the tail in ascending d.  Every dot product in
+ * this file goes through here, so all evaluations of one score agree bit for
+ * bit. */
+static double dot(const double *a, const double *b, int D)
+{
+    double p0 = 0.0, p1 = 0.0, p2 = 0.0, p3 = 0.0;
+    int d = 0;
+    for (; d + 4 <= D; d += 4) {
+        p0 += a[d] * b[d];
+        p1 += a[d + 1] * b[d + 1];
+        p2 += a[d + 2] * b[d + 2];
+        p3 += a[d + 3] * b[d + 3];
+    }
+    double acc = (p0 + p1) + (p2 + p3);
+    for (; d < D; d++)
+        acc += a[d] * b[d];
+    return acc;
+}
+
+/* One score S_ij, or -inf when the pair is not visible. */
+static double score(const double *qi, const double *kj, int D, double scale,
+                    int i, int j, int Lq, int Lk, int causal,
+                    const double *mask_row)
+{
+    if (causal && (int64_t)j > (int64_t)i + Lk - Lq)
+        return -INFINITY;
+    if (mask_row && mask_row[j] == -INFINITY)
+        return -INFINITY;
+    double s = scale * dot(qi, kj, D);
+    if (mask_row)
+        s += mask_row[j];
+    return s;
+}
+
+/* Natural-log log-sum-exp of one row of scores (-inf if all are -inf). */
+static double row_lse(const double *s, int Lk)
+{
+    double m = -INFINITY;
+    for (int j = 0; j < Lk; j++)
+        if (s[j] > m)
+            m = s[j];
+    if (m == -INFINITY)
+        return -INFINITY;
+    double l = 0.0;
+    for (int j = 0; j < Lk; j++)
+        l += exp(s[j] - m);
+    return m + log(l);
+}
+
+static int check_common(int nseq, const int64_t *cu_q, const int64_t *cu_k,
+                        int H, int Hk, int D, const double *mask)
+{
+    if (nseq < 0 || H <= 0 || Hk <= 0 || D <= 0 || H % Hk != 0)
+        return -1;
+    if (!cu_q || !cu_k)
+        return -1;
+    if (mask && nseq != 1)
+        return -1;
+    for (int s = 0; s < nseq; s++)
+        if (cu_q[s + 1] < cu_q[s] || cu_k[s + 1] < cu_k[s])
+            return -1;
+    return 0;
+}
+
+static int max_len(int nseq, const int64_t *cu)
+{
+    int64_t m = 0;
+    for (int s = 0; s < nseq; s++)
+        if (cu[s + 1] - cu[s] > m)
+            m = cu[s + 1] - cu[s];
+    return (int)m;
+}
+
+/* Forward: O and LSE for every (row, head). */
+int oracle_forward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
+                   int H, int Hk, int D, double scale, int causal,
+                   const double *mask,
+                   const double *q, const double *k, const double *v,
+                   double *out, double *lse)
+{
+    if (check_common(nseq, cu_q, cu_k, H, Hk, D, mask))
+        return -1;
+    const int G = H / Hk;
+    const int Lk_max = max_len(nseq, cu_k);
+    const int64_t nunits = (int64_t)nseq * H;
+    int failed = 0;
+
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(Lk_max + 1));
+        if (!s) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t u = 0; u < nunits; u++) {
+            if (!s)
+                continue;
+            const int b = (int)(u / H), h = (int)(u % H), g = h / G;
+            const int64_t q0 = cu_q[b], k0 = cu_k[b];
+            const int Lq = (int)(cu_q[b + 1] - q0), Lk = (int)(cu_k[b + 1] - k0);
+            for (int i = 0; i < Lq; i++) {
+                const double *qi = q + ((q0 + i) * H + h) * D;
+                const double *mrow = mask ? mask + (int64_t)i * Lk : NULL;
+                for (int j = 0; j < Lk; j++)
+                    s[j] = score(qi, k + ((k0 + j) * Hk + g) * D, D, scale,
+                                 i, j, Lq, Lk, causal, mrow);
+                const double L = row_lse(s, Lk);
+                double *o = out + ((q0 + i) * H + h) * D;
+                for (int d = 0; d < D; d++)
+                    o[d] = 0.0;
+                lse[(q0 + i) * H + h] = L;
+                if (L == -INFINITY)
+                    continue;
+                for (int j = 0; j < Lk; j++) {
+                    if (s[j] == -INFINITY)
+                        continue;
+                    const double p = exp(s[j] - L);
+                    const double *vj = v + ((k0 + j) * Hk + g) * D;
+                    for (int d = 0; d < D; d++)
+                        o[d] += p * vj[d];
+                }
+            }
+        }
+        free(s);
+    }
+    return failed ? -2 : 0;
+}
+
+/* D^O diagnostic: sum_d dO_id * O_id for every (row, head), O as given. */
+int oracle_rowdot(int64_t total_q, int H, int D, const double *dout,
+                  const double *out, double *res)
+{
+    if (total_q < 0 || H <= 0 || D <= 0)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < total_q * H; r++) {
+        res[r] = dot(dout + r * D, out + r * D, D);
+    }
+    return 0;
+}
+
+/* Sum the per-query-head gradients of one KV head in ascending head order:
+ * dst[row][g] = sum_{h = gG}^{gG+G-1} src[row][h]. */
+static void group_sum(int64_t total_k, int H, int Hk, int D,
+                      const double *src, double *dst)
+{
+    const int G = H / Hk;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < total_k; r++)
+        for (int g = 0; g < Hk; g++) {
+            double *o = dst + (r * Hk + g) * D;
+            for (int d = 0; d < D; d++)
+                o[d] = 0.0;
+            for (int h = g * G; h < (g + 1) * G; h++) {
+                const double *x = src + (r * H + h) * D;
+                for (int d = 0; d < D; d++)
+                    o[d] += x[d];
+            }
+        }
+}
+
+/*
+ * Explicit-Jacobian backward.  For every (sequence, head) it materialises
+ * P and dP (Lq x Lk), and for every row the Lk x Lk Jacobian of the softmax,
+ * then forms dS = J dP row by row and the three products with plain loops.
+ * ds_out (nullable, nseq == 1 only): [H][Lq][Lk].  dj_out (nullable):
+ * sum_k P_ik dP_ik per (row, head).
+ */
+int oracle_backward_explicit(int nseq, const int64_t *cu_q, const int64_t *cu_k,
+                             int H, int Hk, int D, double scale, int causal,
+                             const double *mask,
+                             const double *q, const double *k, const double *v,
+                             const double *dout,
+                             double *dq, double *dk, double *dv,
+                             double *ds_out, double *dj_out)
+{
+    if (check_common(nseq, cu_q, cu_k, H, Hk, D, mask))
+        return -1;
+    if (ds_out && nseq != 1)
+        return -1;
+    const int G = H / Hk;
+    const int64_t total_k = cu_k[nseq];
+    const int64_t nunits = (int64_t)nseq * H;
+    /* per-query-head dK, dV before the group sum: [total_k][H][D] */
+    double *dkh = (double *)calloc((size_t)(total_k * H * D) + 1, sizeof(double));
+    double *dvh = (double *)calloc((size_t)(total_k * H * D) + 1, sizeof(double));
+    if (!dkh || !dvh) {
+        free(dkh);
+        free(dvh);
+        return -2;
+    }
+    int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t u = 0; u < nunits; u++) {
+        const int b = (int)(u / H), h = (int)(u % H), g = h / G;
+        const int64_t q0 = cu_q[b], k0 = cu_k[b];
+        const int Lq = (int)(cu_q[b + 1] - q0), Lk = (int)(cu_k[b + 1] - k0);
+        const size_t n = (size_t)Lq * Lk + 1;
+        double *S = (double *)malloc(n * sizeof(double));
+        double *P = (double *)malloc(n * sizeof(double));
+        double *dP = (double *)malloc(n * sizeof(double));
+        double *dS = (double *)malloc(n * sizeof(double));
+        double *J = (double *)malloc(((size_t)Lk * Lk + 1) * sizeof(double));
+        if (!S || !P || !dP || !dS || !J) {
+#pragma omp atomic write
+            failed = 1;
+            free(S); free(P); free(dP); free(dS); free(J);
+            continue;
+        }
+#define QP(i) (q + ((q0 + (i)) * H + h) * D)
+#define DOP(i) (dout + ((q0 + (i)) * H + h) * D)
+#define KP(j) (k + ((k0 + (j)) * Hk + g) * D)
+#define VP(j) (v + ((k0 + (j)) * Hk + g) * D)
+        /* scores and softmax */
+        for (int i = 0; i < Lq; i++) {
+            const double *mrow = mask ? mask + (int64_t)i * Lk : NULL;
+            for (int j = 0; j < Lk; j++)
+                S[(size_t)i * Lk + j] = score(QP(i), KP(j), D, scale, i, j, Lq, Lk,
+                                              causal, mrow);
+            const double L = row_lse(S + (size_t)i * Lk, Lk);
+            for (int j = 0; j < Lk; j++) {
+                const double sij = S[(size_t)i * Lk + j];
+                P[(size_t)i * Lk + j] = (L == -INFINITY || sij == -INFINITY) ? 0.0 : exp(sij - L);
+            }
+        }
+        /* dP = dO V^T */
+        for (int i = 0; i < Lq; i++)
+            for (int j = 0; j < Lk; j++) {
+                dP[(size_t)i * Lk + j] = dot(DOP(i), VP(j), D);
+            }
+        /* dS_i = J_i dP_i with J_i = diag(P_i) - P_i P_i^T */
+        for (int i = 0; i < Lq; i++) {
+            const double *Pi = P + (size_t)i * Lk;
+            for (int j = 0; j < Lk; j++)
+                for (int c = 0; c < Lk; c++)
+                    J[(size_t)j * Lk + c] = (j == c ? Pi[j] : 0.0) - Pi[j] * Pi[c];
+            for (int j = 0; j < Lk; j++) {
+                double acc = 0.0;
+                for (int c = 0; c < Lk; c++)
+                    acc += J[(size_t)j * Lk + c] * dP[(size_t)i * Lk + c];
+                dS[(size_t)i * Lk + j] = acc;
+            }
+            if (dj_out) {
+                double acc = 0.0;
+                for (int c = 0; c < Lk; c++)
+                    acc += Pi[c] * dP[(size_t)i * Lk + c];
+                dj_out[(q0 + i) * H + h] = acc;
+            }
+        }
+        /* dQ = scale * dS K */
+        for (int i = 0; i < Lq; i++) {
+            double *o = dq + ((q0 + i) * H + h) * D;
+            for (int d = 0; d < D; d++) {
+                double acc = 0.0;
+                for (int j = 0; j < Lk; j++)
+                    acc += dS[(size_t)i * Lk + j] * KP(j)[d];
+                o[d] = scale * acc;
+            }
+        }
+        /* dK^(h) = scale * dS^T Q,  dV^(h) = P^T dO */
+        for (int j = 0; j < Lk; j++) {
+            double *ok = dkh + ((k0 + j) * H + h) * D;
+            double *ov = dvh + ((k0 + j) * H + h) * D;
+            for (int d = 0; d < D; d++) {
+                double acck = 0.0, accv = 0.0;
+                for (int i = 0; i < Lq; i++) {
+                    acck += dS[(size_t)i * Lk + j] * QP(i)[d];
+                    accv += P[(size_t)i * Lk + j] * DOP(i)[d];
+                }
+                ok[d] = scale * acck;
+                ov[d] = accv;
+            }
+        }
+        if (ds_out)
+            memcpy(ds_out + (size_t)h * Lq * Lk, dS, (size_t)Lq * Lk * sizeof(double));
+#undef QP
+#undef DOP
+#undef KP
+#undef VP
+        free(S); free(P); free(dP); free(dS); free(J);
+    }
+    if (!failed) {
+        group_sum(total_k, H, Hk, D, dkh, dk);
+        group_sum(total_k, H, Hk, D, dvh, dv);
+    }
+    free(dkh);
+    free(dvh);
+    return failed ? -2 : 0;
+}
+
+/*
+ * Contracted backward for any size.  The softmax Jacobian-vector product is
+ * written out as dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik), which is J_i dP_i
+ * expanded.  Row pass (one task per query row and head): scores, LSE, P, dP,
+ * the row contraction D^J_i, dS and dQ_i.  Key pass (one task per key row and
+ * KV head): for each query head of the group in ascending order, the column
+ * sums over query rows of dS_ij Q_i and P_ij dO_i, with P and dS recomputed
+ * from the same scores, the row pass's LSE_i and D^J_i; the per-head results
+ * are then added in ascending head order.
+ * dj_out, lse_out (nullable): D^J and LSE per (row, head).
+ */
+int oracle_backward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
+                    int H, int Hk, int D, double scale, int causal,
+                    const double *mask,
+                    const double *q, const double *k, const double *v,
+                    const double *dout,
+                    double *dq, double *dk, double *dv,
+                    double *dj_out, double *lse_out)
+{
+    if (check_common(nseq, cu_q, cu_k, H, Hk, D, mask))
+        return -1;
+    const int G = H / Hk;
+    const int64_t total_q = cu_q[nseq];
+    const int Lk_max = max_len(nseq, cu_k);
+    double *LSE = (double *)malloc(sizeof(double) * (size_t)(total_q * H + 1));
+    double *DJ = (double *)malloc(sizeof(double) * (size_t)(total_q * H + 1));
+    /* row -> sequence map for the row pass */
+    int *seq_of_row = (int *)malloc(sizeof(int) * (size_t)(total_q + 1));
+    if (!LSE || !DJ || !seq_of_row) {
+        free(LSE); free(DJ); free(seq_of_row);
+        return -2;
+    }
+    for (int s = 0; s < nseq; s++)
+        for (int64_t r = cu_q[s]; r < cu_q[s + 1]; r++)
+            seq_of_row[r] = s;
+    int failed = 0;
+
+    /* ---- row pass: LSE, P, dP, D^J, dS, dQ ---- */
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(Lk_max + 1));
+        double *dp = (double *)malloc(sizeof(double) * (size_t)(Lk_max + 1));
+        if (!s || !dp) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t t = 0; t < total_q * H; t++) {
+            if (!s || !dp)
+                continue;
+            const int64_t r = t / H;
+            const int h = (int)(t % H), g = h / G, b = seq_of_row[r];
+            const int64_t q0 = cu_q[b], k0 = cu_k[b];
+            const int Lq = (int)(cu_q[b + 1] - q0), Lk = (int)(cu_k[b + 1] - k0);
+            const int i = (int)(r - q0);
+            const double *qi = q + (r * H + h) * D;
+            const double *doi = dout + (r * H + h) * D;
+            const double *mrow = mask ? mask + (int64_t)i * Lk : NULL;
+            for (int j = 0; j < Lk; j++)
+                s[j] = score(qi, k + ((k0 + j) * Hk + g) * D, D, scale, i, j, Lq, Lk,
+                             causal, mrow);
+            const double L = row_lse(s, Lk);
+            LSE[r * H + h] = L;
+            double *o = dq + (r * H + h) * D;
+            for (int d = 0; d < D; d++)
+                o[d] = 0.0;
+            double dj = 0.0;
+            if (L != -INFINITY) {
+                for (int j = 0; j < Lk; j++) {
+                    if (s[j] == -INFINITY) {
+                        s[j] = 0.0; /* P_ij = 0 */
+                        dp[j] = 0.0;
+                        continue;
+                    }
+                    s[j] = exp(s[j] - L); /* s now holds P_ij */
+                    const double *vj = v + ((k0 + j) * Hk + g) * D;
+                    dp[j] = dot(doi, vj, D);
+                }
+                for (int j = 0; j < Lk; j++)
+                    dj += s[j] * dp[j];
+                for (int j = 0; j < Lk; j++) {
+                    if (s[j] == 0.0)
+                        continue;
+                    const double dsij = s[j] * (dp[j] - dj);
+                    const double *kj = k + ((k0 + j) * Hk + g) * D;
+                    for (int d = 0; d < D; d++)
+                        o[d] += dsij * kj[d];
+                }
+                for (int d = 0; d < D; d++)
+                    o[d] *= scale;
+            }
+            DJ[r * H + h] = dj;
+        }
+        free(s);
+        free(dp);
+    }
+
+    /* ---- key pass: dK, dV ---- */
+    const int64_t total_k = cu_k[nseq];
+    int *seq_of_key = (int *)malloc(sizeof(int) * (size_t)(total_k + 1));
+    if (!seq_of_key)
+        failed = 1;
+    else
+        for (int s2 = 0; s2 < nseq; s2++)
+            for (int64_t r = cu_k[s2]; r < cu_k[s2 + 1]; r++)
+                seq_of_key[r] = s2;
+    if (!failed) {
+#pragma omp parallel
+        {
+            double *acck = (double *)malloc(sizeof(double) * (size_t)D);
+            double *accv = (double *)malloc(sizeof(double) * (size_t)D);
+            if (!acck || !accv) {
+#pragma omp atomic write
+                failed = 1;
+            }
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t t = 0; t < total_k * Hk; t++) {
+                if (!acck || !accv)
+                    continue;
+                const int64_t rk = t / Hk;
+                const int g = (int)(t % Hk), b = seq_of_key[rk];
+                const int64_t q0 = cu_q[b], k0 = cu_k[b];
+                const int Lq = (int)(cu_q[b + 1] - q0), Lk = (int)(cu_k[b + 1] - k0);
+                const int j = (int)(rk - k0);
+                const double *kj = k + (rk * Hk + g) * D;
+                const double *vj = v + (rk * Hk + g) * D;
+                double *ok = dk + (rk * Hk + g) * D;
+                double *ov = dv + (rk * Hk + g) * D;
+                for (int d = 0; d < D; d++) {
+                    ok[d] = 0.0;
+                    ov[d] = 0.0;
+                }
+                for (int h = g * G; h < (g + 1) * G; h++) {
+                    for (int d = 0; d < D; d++) {
+                        acck[d] = 0.0;
+                        accv[d] = 0.0;
+                    }
+                    for (int i = 0; i < Lq; i++) {
+                        const int64_t r = q0 + i;
+                        const double L = LSE[r * H + h];
+                        if (L == -INFINITY)
+                            continue;
+                        const double *qi = q + (r * H + h) * D;
+                        const double *mrow = mask ? mask + (int64_t)i * Lk : NULL;
+                        const double sij = score(qi, kj, D, scale, i, j, Lq, Lk, causal, mrow);
+                        if (sij == -INFINITY)
+                            continue;
+                        const double p = exp(sij - L);
+                        const double *doi = dout + (r * H + h) * D;
+                        const double dpij = dot(doi, vj, D);
+                        const double dsij = p * (dpij - DJ[r * H + h]);
+                        for (int d = 0; d < D; d++) {
+                            acck[d] += dsij * qi[d];
+                            accv[d] += p * doi[d];
+                        }
+                    }
+                    for (int d = 0; d < D; d++) {
+                        ok[d] += scale * acck[d];
+                        ov[d] += accv[d];
+                    }
+                }
+            }
+            free(acck);
+            free(accv);
+        }
+    }
+    if (!failed) {
+        if (dj_out)
+            memcpy(dj_out, DJ, sizeof(double) * (size_t)(total_q * H));
+        if (lse_out)
+            memcpy(lse_out, LSE, sizeof(double) * (size_t)(total_q * H));
+    }
+    free(LSE);
+    free(DJ);
+    free(seq_of_row);
+    free(seq_of_key);
+    return failed ? -2 : 0;
+}
+
+/* Number of OpenMP threads a parallel region of this library would use. */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,144 @@
+"""ctypes wrapper of the fp64 CPU attention oracle.
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg.  The GPU product path never imports it.
+
+Every array is numpy fp64 in the oracle's packed, tokens-major layout:
+q, dout, out, dq: [total_q, H, D]; k, v, dk, dv: [total_k, Hk, D];
+lse, dj: [total_q, H].  cu_q / cu_k are the int64 row offsets of each
+sequence (a dense batch of B equal-length sequences is cu = [0, S, 2S, ...]).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+_dp = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        common = [ctypes.c_int, _i64p, _i64p, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_double, ctypes.c_int, _dp]
+        lib.oracle_forward.argtypes = common + [_dp, _dp, _dp, _dp, _dp]
+        lib.oracle_backward.argtypes = common + [_dp] * 4 + [_dp] * 3 + [_dp, _dp]
+        lib.oracle_backward_explicit.argtypes = common + [_dp] * 4 + [_dp] * 3 + [_dp, _dp]
+        lib.oracle_rowdot.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                      _dp, _dp, _dp]
+        for f in (lib.oracle_forward, lib.oracle_backward,
+                  lib.oracle_backward_explicit, lib.oracle_rowdot):
+            f.restype = ctypes.c_int
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
+        _LIB = lib
+    return _LIB
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(_dp)
+
+
+def _cu(cu):
+    return np.ascontiguousarray(cu, dtype=np.int64)
+
+
+def _shapes(q, k, cu_q, cu_k):
+    if q.ndim != 3 or k.ndim != 3:
+        raise ValueError("q and k must be [total, heads, dim]")
+    total_q, H, D = q.shape
+    total_k, Hk, Dk = k.shape
+    if Dk != D or H % Hk:
+        raise ValueError("bad head dims / head counts")
+    if cu_q[-1] != total_q or cu_k[-1] != total_k or len(cu_q) != len(cu_k):
+        raise ValueError("cu_seqlens do not match the packed rows")
+    return len(cu_q) - 1, H, Hk, D
+
+
+def num_threads() -> int:
+    return int(_lib().oracle_num_threads())
+
+
+def forward(q, k, v, cu_q, cu_k, scale, causal, mask=None):
+    """Returns (out [total_q,H,D], lse [total_q,H]) in fp64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cu_q, cu_k = _cu(cu_q), _cu(cu_k)
+    nseq, H, Hk, D = _shapes(q, k, cu_q, cu_k)
+    mask = None if mask is None else _f64(mask)
+    out = np.empty(q.shape, np.float64)
+    lse = np.empty(q.shape[:2], np.float64)
+    rc = _lib().oracle_forward(nseq, cu_q.ctypes.data_as(_i64p), cu_k.ctypes.data_as(_i64p),
+                               H, Hk, D, float(scale), int(bool(causal)), _ptr(mask),
+                               _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse))
+    if rc:
+        raise RuntimeError("oracle_forward failed (%d)" % rc)
+    return out, lse
+
+
+def backward(q, k, v, dout, cu_q, cu_k, scale, causal, mask=None,
+             mode="contracted", want_ds=False):
+    """Exact attention gradient in fp64.
+
+    mode="contracted": any size; mode="explicit": materialised softmax
+    Jacobian, small inputs only (want_ds=True returns dS [H, Lq, Lk] for a
+    single sequence).  Returns a dict with dq, dk, dv, dj (sum_k P_ik dP_ik)
+    and, in contracted mode, lse; in explicit mode with want_ds, ds.
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    cu_q, cu_k = _cu(cu_q), _cu(cu_k)
+    nseq, H, Hk, D = _shapes(q, k, cu_q, cu_k)
+    if dout.shape != q.shape or v.shape != k.shape:
+        raise ValueError("dout/v shape mismatch")
+    mask = None if mask is None else _f64(mask)
+    dq = np.empty(q.shape, np.float64)
+    dk = np.empty(k.shape, np.float64)
+    dv = np.empty(k.shape, np.float64)
+    dj = np.empty(q.shape[:2], np.float64)
+    res = {"dq": dq, "dk": dk, "dv": dv, "dj": dj}
+    lib = _lib()
+    common = (nseq, cu_q.ctypes.data_as(_i64p), cu_k.ctypes.data_as(_i64p), H, Hk, D,
+              float(scale), int(bool(causal)), _ptr(mask), _ptr(q), _ptr(k), _ptr(v),
+              _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv))
+    if mode == "contracted":
+        lse = np.empty(q.shape[:2], np.float64)
+        rc = lib.oracle_backward(*common, _ptr(dj), _ptr(lse))
+        res["lse"] = lse
+    elif mode == "explicit":
+        ds = None
+        if want_ds:
+            if nseq != 1:
+                raise ValueError("want_ds needs a single sequence")
+            ds = np.empty((H, int(cu_q[1]), int(cu_k[1])), np.float64)
+            res["ds"] = ds
+        rc = lib.oracle_backward_explicit(*common, _ptr(ds), _ptr(dj))
+    else:
+        raise ValueError(mode)
+    if rc:
+        raise RuntimeError("oracle backward failed (%d)" % rc)
+    return res
+
+
+def rowdot(dout, out):
+    """sum_d dout * out per (row, head), fp64, with `out` exactly as given."""
+    dout, out = _f64(dout), _f64(out)
+    if dout.shape != out.shape or dout.ndim != 3:
+        raise ValueError("shape mismatch")
+    T, H, D = dout.shape
+    res = np.empty((T, H), np.float64)
+    rc = _lib().oracle_rowdot(T, H, D, _ptr(dout), _ptr(out), _ptr(res))
+    if rc:
+        raise RuntimeError("oracle_rowdot failed")
+    return res

@@ -1,0 +1,275 @@
+"""Pins of the fp64 CPU oracle against things other than itself.
+
+Each test fixes the oracle to mathematics it cannot share code with:
+central finite differences of its own forward (the gradient definition),
+hand-derived closed forms (tests/golden), invariants of the softmax
+Jacobian, a library softmax (scipy) for the forward, and structural
+identities of the method (GQA = repeated-KV MHA, causal = explicit -inf mask,
+packed = per-sequence).  CPU only.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+from oracle import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _problem(seed, lens_q, lens_k, H, Hk, D, zero_q=False, equal_k=False):
+    rng = np.random.default_rng(seed)
+    Tq, Tk = sum(lens_q), sum(lens_k)
+    q = np.zeros((Tq, H, D)) if zero_q else rng.standard_normal((Tq, H, D))
+    k = rng.standard_normal((Tk, Hk, D))
+    if equal_k:
+        k[:] = k[:1]
+    v = rng.standard_normal((Tk, Hk, D))
+    do = rng.standard_normal((Tq, H, D))
+    cu_q = np.cumsum([0] + list(lens_q))
+    cu_k = np.cumsum([0] + list(lens_k))
+    return q, k, v, do, cu_q, cu_k
+
+
+def _loss(q, k, v, do, cu_q, cu_k, scale, causal):
+    out, _ = O.forward(q, k, v, cu_q, cu_k, scale, causal)
+    return float(np.sum(do * out))
+
+
+def _central_diff(x, f, h=1e-5):
+    g = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        idx = it.multi_index
+        old = x[idx]
+        x[idx] = old + h
+        fp = f()
+        x[idx] = old - h
+        fm = f()
+        x[idx] = old
+        g[idx] = (fp - fm) / (2 * h)
+    return g
+
+
+FD_CASES = [
+    # (name, lens_q, lens_k, H, Hk, D, causal)
+    ("dense_noncausal", [5], [7], 2, 1, 3, False),
+    ("dense_causal_sq_lt_sk", [5], [7], 2, 1, 3, True),
+    ("causal_sq_gt_sk_empty_rows", [7], [5], 2, 1, 3, True),
+    ("varlen_two_seqs_causal", [3, 5], [4, 2], 2, 1, 3, True),
+    ("varlen_two_seqs_noncausal_d5", [3, 5], [4, 2], 2, 2, 5, False),
+]
+
+
+@pytest.mark.parametrize("case", FD_CASES, ids=[c[0] for c in FD_CASES])
+@pytest.mark.parametrize("mode", ["contracted", "explicit"])
+def test_gradient_matches_central_differences(case, mode):
+    name, lq, lk, H, Hk, D, causal = case
+    q, k, v, do, cu_q, cu_k = _problem(11, lq, lk, H, Hk, D)
+    scale = 0.7
+    g = O.backward(q, k, v, do, cu_q, cu_k, scale, causal, mode=mode)
+    f = lambda: _loss(q, k, v, do, cu_q, cu_k, scale, causal)  # noqa: E731
+    for key, x in (("dq", q), ("dk", k), ("dv", v)):
+        fd = _central_diff(x, f)
+        err = np.abs(g[key] - fd)
+        assert np.all(err <= 1e-7 * np.maximum(1.0, np.abs(g[key]))), (key, err.max())
+
+
+@pytest.mark.parametrize("fname", ["closed_form_one_query_two_keys.json",
+                                   "closed_form_causal_bottom_right_2x3.json"])
+@pytest.mark.parametrize("mode", ["contracted", "explicit"])
+def test_hand_derived_closed_forms(fname, mode):
+    gd = json.load(open(os.path.join(GOLDEN, fname)))
+    A = {k: np.array(gd[k], dtype=np.float64)
+         for k in ("q", "k", "v", "dout", "out", "lse", "dq", "dk", "dv")}
+    cu_q = [0, gd["shape"]["Sq"]]
+    cu_k = [0, gd["shape"]["Sk"]]
+    out, lse = O.forward(A["q"], A["k"], A["v"], cu_q, cu_k, gd["scale"], gd["causal"])
+    np.testing.assert_allclose(out, A["out"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, A["lse"], rtol=0, atol=1e-14)
+    g = O.backward(A["q"], A["k"], A["v"], A["dout"], cu_q, cu_k, gd["scale"],
+                   gd["causal"], mode=mode)
+    for key in ("dq", "dk", "dv"):
+        np.testing.assert_allclose(g[key], A[key], rtol=0, atol=1e-14, err_msg=key)
+
+
+@pytest.mark.parametrize("causal,lq,lk", [(False, 9, 13), (True, 9, 13), (True, 13, 9),
+                                           (True, 12, 12)])
+def test_forward_matches_library_softmax(causal, lq, lk):
+    q, k, v, _, cu_q, cu_k = _problem(5, [lq], [lk], 4, 2, 8)
+    scale = 0.35
+    out, lse = O.forward(q, k, v, cu_q, cu_k, scale, causal)
+    for h in range(4):
+        g = h // 2
+        S = scale * (q[:, h, :] @ k[:, g, :].T)
+        if causal:
+            i = np.arange(lq)[:, None]
+            j = np.arange(lk)[None, :]
+            S = np.where(j <= i + lk - lq, S, -np.inf)
+        empty = np.all(np.isinf(S), axis=1)
+        Sf = np.where(empty[:, None], 0.0, S)
+        ref_lse = np.where(empty, -np.inf, scipy.special.logsumexp(Sf, axis=1))
+        P = np.where(empty[:, None], 0.0, scipy.special.softmax(Sf, axis=1))
+        P = np.where(np.isinf(S), 0.0, P)
+        np.testing.assert_allclose(out[:, h, :], P @ v[:, g, :], rtol=1e-12, atol=1e-13)
+        fin = ~empty
+        np.testing.assert_allclose(lse[fin, h], ref_lse[fin], rtol=1e-13, atol=1e-13)
+        assert np.all(lse[empty, h] == -np.inf)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_softmax_jacobian_rows_sum_to_zero(causal):
+    q, k, v, do, cu_q, cu_k = _problem(3, [16], [24], 2, 1, 8)
+    g = O.backward(q, k, v, do, cu_q, cu_k, 0.5, causal, mode="explicit", want_ds=True)
+    ds = g["ds"]
+    tol = 1e-12 * ds.shape[-1] * np.abs(ds).max()
+    assert np.abs(ds.sum(axis=-1)).max() <= tol
+
+
+@pytest.mark.parametrize("causal,lq,lk", [(False, 17, 23), (True, 17, 23), (True, 23, 17),
+                                           (True, 20, 20)])
+def test_explicit_jacobian_equals_contracted(causal, lq, lk):
+    q, k, v, do, cu_q, cu_k = _problem(7, [lq], [lk], 4, 2, 16)
+    a = O.backward(q, k, v, do, cu_q, cu_k, 0.25, causal, mode="explicit")
+    b = O.backward(q, k, v, do, cu_q, cu_k, 0.25, causal, mode="contracted")
+    for key in ("dq", "dk", "dv", "dj"):
+        scale = max(1.0, np.abs(a[key]).max())
+        assert np.abs(a[key] - b[key]).max() <= 1e-12 * scale, key
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_equals_mha_with_repeated_kv(causal):
+    G = 3
+    q, k, v, do, cu_q, cu_k = _problem(9, [11, 6], [13, 6], 6, 2, 8)
+    gq = O.backward(q, k, v, do, cu_q, cu_k, 0.3, causal)
+    kr, vr = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)
+    mh = O.backward(q, kr, vr, do, cu_q, cu_k, 0.3, causal)
+    assert np.array_equal(gq["dq"], mh["dq"])
+    for key in ("dk", "dv"):
+        summed = np.zeros_like(gq[key])
+        for g in range(2):
+            acc = np.zeros_like(summed[:, g])
+            for h in range(g * G, (g + 1) * G):   # ascending head order
+                acc = acc + mh[key][:, h]
+            summed[:, g] = acc
+        assert np.array_equal(gq[key], summed), key
+
+
+@pytest.mark.parametrize("lq,lk", [(5, 9), (8, 8), (9, 5)])
+@pytest.mark.parametrize("mode", ["contracted", "explicit"])
+def test_causal_equals_explicit_minus_inf_mask(lq, lk, mode):
+    q, k, v, do, cu_q, cu_k = _problem(13, [lq], [lk], 2, 1, 4)
+    i = np.arange(lq)[:, None]
+    j = np.arange(lk)[None, :]
+    mask = np.where(j <= i + lk - lq, 0.0, -np.inf)
+    a = O.backward(q, k, v, do, cu_q, cu_k, 0.6, True, mode=mode)
+    b = O.backward(q, k, v, do, cu_q, cu_k, 0.6, False, mask=mask, mode=mode)
+    for key in ("dq", "dk", "dv"):
+        assert np.array_equal(a[key], b[key]), key
+    oa, la = O.forward(q, k, v, cu_q, cu_k, 0.6, True)
+    ob, lb = O.forward(q, k, v, cu_q, cu_k, 0.6, False, mask=mask)
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_contraction_equals_rowdot_of_output(causal):
+    """sum_k P_ik dP_ik == sum_d dO_id O_id: the identity the GPU preprocess
+    relies on, checked on the oracle's own fp64 O."""
+    q, k, v, do, cu_q, cu_k = _problem(21, [10, 19], [14, 19], 4, 4, 12)
+    out, _ = O.forward(q, k, v, cu_q, cu_k, 0.4, causal)
+    g = O.backward(q, k, v, do, cu_q, cu_k, 0.4, causal)
+    rd = O.rowdot(do, out)
+    np.testing.assert_allclose(g["dj"], rd, rtol=1e-12, atol=1e-12)
+
+
+def test_rowdot_is_plain_sum():
+    rng = np.random.default_rng(0)
+    a, b = rng.standard_normal((7, 3, 10)), rng.standard_normal((7, 3, 10))
+    np.testing.assert_allclose(O.rowdot(a, b), np.einsum("thd,thd->th", a, b),
+                               rtol=1e-14, atol=1e-14)
+
+
+def test_single_key_gives_zero_dq_dk_and_summed_dv():
+    q, k, v, do, cu_q, cu_k = _problem(4, [6], [1], 4, 2, 5)
+    out, _ = O.forward(q, k, v, cu_q, cu_k, 0.5, False)
+    for h in range(4):
+        np.testing.assert_array_equal(out[:, h], np.repeat(v[:, h // 2], 6, axis=0))
+    g = O.backward(q, k, v, do, cu_q, cu_k, 0.5, False)
+    assert np.all(g["dq"] == 0) and np.all(g["dk"] == 0)
+    for gk in range(2):
+        ref = do[:, 2 * gk].sum(0) + do[:, 2 * gk + 1].sum(0)
+        np.testing.assert_allclose(g["dv"][0, gk], ref, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_equal_keys_give_uniform_softmax_and_zero_dq(causal):
+    q, k, v, do, cu_q, cu_k = _problem(8, [9], [12], 2, 1, 6, equal_k=True)
+    out, _ = O.forward(q, k, v, cu_q, cu_k, 0.5, causal)
+    g = O.backward(q, k, v, do, cu_q, cu_k, 0.5, causal)
+    assert np.abs(g["dq"]).max() <= 1e-13
+    for i in range(9):
+        nvis = min(12, i + 12 - 9 + 1) if causal else 12
+        np.testing.assert_allclose(out[i, 0], v[:nvis, 0].mean(0), rtol=1e-13, atol=1e-13)
+
+
+def test_causal_first_row_of_aligned_square_has_zero_dq():
+    q, k, v, do, cu_q, cu_k = _problem(10, [8], [8], 2, 2, 4)
+    g = O.backward(q, k, v, do, cu_q, cu_k, 0.5, True)
+    assert np.all(g["dq"][0] == 0)
+
+
+def test_zero_queries_give_uniform_attention():
+    Sq, Sk = 7, 5
+    q, k, v, do, cu_q, cu_k = _problem(12, [Sq], [Sk], 2, 1, 4, zero_q=True)
+    g = O.backward(q, k, v, do, cu_q, cu_k, 0.9, False)
+    assert np.all(g["dk"] == 0)
+    ref = (do[:, 0].sum(0) + do[:, 1].sum(0)) / Sk
+    for j in range(Sk):
+        np.testing.assert_allclose(g["dv"][j, 0], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_gradient_is_linear_in_dout():
+    q, k, v, do1, cu_q, cu_k = _problem(14, [8], [10], 2, 1, 4)
+    do2 = np.random.default_rng(15).standard_normal(do1.shape)
+    a = 1.75
+    g1 = O.backward(q, k, v, do1, cu_q, cu_k, 0.5, True)
+    g2 = O.backward(q, k, v, do2, cu_q, cu_k, 0.5, True)
+    g3 = O.backward(q, k, v, a * do1 + do2, cu_q, cu_k, 0.5, True)
+    for key in ("dq", "dk", "dv"):
+        np.testing.assert_allclose(g3[key], a * g1[key] + g2[key], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_equals_per_sequence(causal):
+    lq, lk = [5, 9, 3], [7, 9, 2]
+    q, k, v, do, cu_q, cu_k = _problem(16, lq, lk, 4, 2, 6)
+    g = O.backward(q, k, v, do, cu_q, cu_k, 0.5, causal)
+    out, lse = O.forward(q, k, v, cu_q, cu_k, 0.5, causal)
+    for s in range(3):
+        qs, qe, ks, ke = cu_q[s], cu_q[s + 1], cu_k[s], cu_k[s + 1]
+        gs = O.backward(q[qs:qe], k[ks:ke], v[ks:ke], do[qs:qe], [0, qe - qs], [0, ke - ks],
+                        0.5, causal)
+        os_, ls = O.forward(q[qs:qe], k[ks:ke], v[ks:ke], [0, qe - qs], [0, ke - ks], 0.5,
+                            causal)
+        assert np.array_equal(g["dq"][qs:qe], gs["dq"])
+        assert np.array_equal(g["dk"][ks:ke], gs["dk"])
+        assert np.array_equal(g["dv"][ks:ke], gs["dv"])
+        assert np.array_equal(out[qs:qe], os_) and np.array_equal(lse[qs:qe], ls)
+
+
+def test_empty_rows_have_zero_gradient_and_minus_inf_lse():
+    q, k, v, do, cu_q, cu_k = _problem(17, [6], [3], 2, 1, 4)
+    out, lse = O.forward(q, k, v, cu_q, cu_k, 0.5, True)
+    # key limit of row i is i + 3 - 6 = i - 3: rows 0..2 see nothing
+    assert np.all(lse[:3] == -np.inf) and np.all(out[:3] == 0)
+    g = O.backward(q, k, v, do, cu_q, cu_k, 0.5, True)
+    assert np.all(g["dq"][:3] == 0)
+    assert np.all(np.isfinite(g["dq"])) and np.all(np.isfinite(g["dk"]))
+
+
+def test_oracle_rejects_bad_arguments():
+    q, k, v, do, cu_q, cu_k = _problem(1, [4], [4], 3, 2, 4)
+    with pytest.raises(ValueError):
+        O.backward(q, k, v, do, cu_q, cu_k, 0.5, False)
