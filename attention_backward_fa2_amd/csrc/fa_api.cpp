@@ -1,0 +1,275 @@
+// fa_api.cpp -- host side of the C ABI in include/fa_bwd.h: argument
+// validation (all on the host, before any launch), workspace layout, and the
+// three-kernel launch sequence on the caller's stream.
+//
+// Checks follow the validations listed on the Triton FA2 teaching page
+// (AttentionMetadata.validate_inputs: null pointers, head-count divisibility,
+// head dim <= 256, contiguous last dim) and the sm90 backward page
+// (_check_type: 16-bit input dtype, fp32 LSE / accumulators; __call__: every
+// stride but the last a multiple of 128 bits).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/fa_bwd.h"
+#include "fa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fa_status fail(fa_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int pad_head_dim(int d)
+{
+    if (d <= 64)
+        return 64;
+    if (d <= 96)
+        return 96;
+    if (d <= 128)
+        return 128;
+    return 0;
+}
+
+struct Plan {
+    fa::Params p;
+    fa_bwd_ws_layout ws;
+    int dpad;
+};
+
+fa_status check_strides(const char *name, const int64_t s[3], bool varlen)
+{
+    for (int i = varlen ? 1 : 0; i < 3; ++i)
+        if (s[i] % 8 != 0)
+            return fail(FA_ERR_INVALID_ARG,
+                        "%s stride[%d] = %lld is not a multiple of 8 elements (16 bytes)", name,
+                        i, (long long)s[i]);
+    return FA_OK;
+}
+
+// Validates everything that can be checked on the host and fills the plan.
+// need_ws: also require a large-enough workspace.
+fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
+{
+    if (!a)
+        return fail(FA_ERR_INVALID_ARG, "args is NULL");
+    if (a->dtype != FA_DTYPE_BF16)
+        return fail(FA_ERR_UNSUPPORTED, "dtype %d unsupported (only bf16)", a->dtype);
+    if (a->batch < 0 || a->seqlen_q < 0 || a->seqlen_k < 0)
+        return fail(FA_ERR_INVALID_ARG, "negative batch or sequence length");
+    if (a->num_heads <= 0 || a->num_heads_k <= 0 || a->head_dim <= 0)
+        return fail(FA_ERR_INVALID_ARG, "num_heads, num_heads_k and head_dim must be positive");
+    if (a->num_heads % a->num_heads_k != 0)
+        return fail(FA_ERR_INVALID_ARG, "num_heads (%d) is not a multiple of num_heads_k (%d)",
+                    a->num_heads, a->num_heads_k);
+    if (a->head_dim > 256)
+        return fail(FA_ERR_UNSUPPORTED, "head_dim %d > 256", a->head_dim);
+    if (a->head_dim % 8 != 0)
+        return fail(FA_ERR_UNSUPPORTED, "head_dim %d is not a multiple of 8 (pad it first)",
+                    a->head_dim);
+    const int dpad = pad_head_dim(a->head_dim);
+    if (!dpad)
+        return fail(FA_ERR_UNSUPPORTED, "head_dim %d > 128 is not built", a->head_dim);
+    const bool varlen = a->cu_seqlens_q || a->cu_seqlens_k;
+    if (varlen && !(a->cu_seqlens_q && a->cu_seqlens_k))
+        return fail(FA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k must be given together");
+    if (varlen && (a->total_q < 0 || a->total_k < 0))
+        return fail(FA_ERR_INVALID_ARG, "negative total_q / total_k");
+    // Tensors with no elements may be NULL (an empty torch tensor has no
+    // storage); every other tensor pointer must be set.
+    const int64_t nq = varlen ? a->total_q : (int64_t)a->batch * a->seqlen_q;
+    const int64_t nk = varlen ? a->total_k : (int64_t)a->batch * a->seqlen_k;
+    if (nq > 0 && (!a->dout || !a->q || !a->out || !a->lse || !a->dq))
+        return fail(FA_ERR_INVALID_ARG, "a query-side tensor pointer is NULL");
+    if (nk > 0 && (!a->k || !a->v || !a->dk || !a->dv))
+        return fail(FA_ERR_INVALID_ARG, "a key-side tensor pointer is NULL");
+    const void *ptrs[] = {a->dout, a->q, a->k, a->v, a->out, a->dq, a->dk, a->dv};
+    const char *names[] = {"dout", "q", "k", "v", "out", "dq", "dk", "dv"};
+    for (int i = 0; i < 8; ++i)
+        if (!aligned(ptrs[i], 16))
+            return fail(FA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+    if (!aligned(a->lse, 4))
+        return fail(FA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+    fa_status st;
+    if ((st = check_strides("dout", a->do_stride, varlen)) ||
+        (st = check_strides("q", a->q_stride, varlen)) ||
+        (st = check_strides("k", a->k_stride, varlen)) ||
+        (st = check_strides("v", a->v_stride, varlen)) ||
+        (st = check_strides("out", a->o_stride, varlen)) ||
+        (st = check_strides("dq", a->dq_stride, varlen)) ||
+        (st = check_strides("dk", a->dk_stride, varlen)) ||
+        (st = check_strides("dv", a->dv_stride, varlen)))
+        return st;
+    if (a->softmax_scale != a->softmax_scale || std::isinf(a->softmax_scale))
+        return fail(FA_ERR_INVALID_ARG, "softmax_scale is not finite");
+    if ((a->causal != 0 && a->causal != 1) || (a->deterministic != 0 && a->deterministic != 1))
+        return fail(FA_ERR_INVALID_ARG, "causal and deterministic must be 0 or 1");
+
+    fa::Params &p = pl->p;
+    std::memset(&p, 0, sizeof p);
+    p.q = (const uint16_t *)a->q;
+    p.k = (const uint16_t *)a->k;
+    p.v = (const uint16_t *)a->v;
+    p.o = (const uint16_t *)a->out;
+    p.dout = (const uint16_t *)a->dout;
+    p.lse = a->lse;
+    p.dq = (uint16_t *)a->dq;
+    p.dk = (uint16_t *)a->dk;
+    p.dv = (uint16_t *)a->dv;
+    p.cu_q = a->cu_seqlens_q;
+    p.cu_k = a->cu_seqlens_k;
+#define STR(dst, src) p.dst##_sb = a->src[0], p.dst##_ss = a->src[1], p.dst##_sh = a->src[2]
+    STR(q, q_stride);
+    STR(k, k_stride);
+    STR(v, v_stride);
+    STR(o, o_stride);
+    STR(do, do_stride);
+    STR(dq, dq_stride);
+    STR(dk, dk_stride);
+    STR(dv, dv_stride);
+#undef STR
+    p.lse_sb = a->lse_stride[0];
+    p.lse_sh = a->lse_stride[1];
+    p.batch = a->batch;
+    p.H = a->num_heads;
+    p.Hk = a->num_heads_k;
+    p.G = a->num_heads / a->num_heads_k;
+    p.D = a->head_dim;
+    p.Sq = a->seqlen_q;
+    p.Sk = a->seqlen_k;
+    p.varlen = varlen ? 1 : 0;
+    p.rows = varlen ? a->total_q : (int64_t)a->batch * a->seqlen_q;
+    p.mtiles = (a->seqlen_q + fa::kQTile - 1) / fa::kQTile;
+    p.ntiles = (a->seqlen_k + fa::kKTile - 1) / fa::kKTile;
+    p.scale = a->softmax_scale;
+    p.scale_log2 = (float)((double)a->softmax_scale * 1.4426950408889634);
+    p.causal = a->causal;
+    p.deterministic = a->deterministic;
+
+    // Workspace layout.
+    fa_bwd_ws_layout &ws = pl->ws;
+    std::memset(&ws, 0, sizeof ws);
+    ws.rows = p.rows;
+    ws.head_dim_pad = dpad;
+    ws.q_tile = fa::kQTile;
+    ws.k_tile = fa::kKTile;
+    size_t off = 0;
+    const size_t hr = (size_t)p.H * (size_t)p.rows;
+    ws.off_lse2 = off;
+    off = align256(off + hr * sizeof(float));
+    ws.off_rowdot = off;
+    off = align256(off + hr * sizeof(float));
+    ws.off_dq_acc = off;
+    off = align256(off + hr * (size_t)dpad * sizeof(float));
+    ws.off_turns = off;
+    off = align256(off + (size_t)p.batch * p.H * p.mtiles * sizeof(int32_t));
+    ws.off_flags = off;
+    off = align256(off + 4 * sizeof(int32_t));
+    ws.total_bytes = off;
+    pl->dpad = dpad;
+
+    if (need_ws) {
+        if (!a->workspace)
+            return fail(FA_ERR_WORKSPACE, "workspace is NULL");
+        if (!aligned(a->workspace, 256))
+            return fail(FA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+        if (a->workspace_bytes < ws.total_bytes)
+            return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu",
+                        a->workspace_bytes, ws.total_bytes);
+        char *base = (char *)a->workspace;
+        p.lse2 = (float *)(base + ws.off_lse2);
+        p.rowdot = (float *)(base + ws.off_rowdot);
+        p.dq_acc = (float *)(base + ws.off_dq_acc);
+        p.turns = (int *)(base + ws.off_turns);
+        p.flags = (int *)(base + ws.off_flags);
+    }
+    g_last_error.clear();
+    return FA_OK;
+}
+
+fa_status hip_status(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(FA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return FA_OK;
+}
+
+enum Step { kPre = 1, kMain = 2, kConv = 4 };
+
+fa_status run(const fa_bwd_args *a, void *stream, int steps)
+{
+    Plan pl;
+    fa_status st = make_plan(a, &pl, true);
+    if (st)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    const fa::Params &p = pl.p;
+    const bool has_rows = p.batch > 0 && p.Sq > 0 && p.rows > 0;
+    const bool has_keys = p.batch > 0 && p.ntiles > 0;
+    if ((steps & kPre) && has_rows)
+        if ((st = hip_status(fa::launch_preprocess(p, pl.dpad, s), "preprocess launch")))
+            return st;
+    if ((steps & kMain) && has_keys)
+        if ((st = hip_status(fa::launch_main(p, pl.dpad, s), "main launch")))
+            return st;
+    if ((steps & kConv) && has_rows)
+        if ((st = hip_status(fa::launch_convert(p, pl.dpad, s), "dq_convert launch")))
+            return st;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_bwd_workspace_size(const fa_bwd_args *a)
+{
+    Plan pl;
+    if (make_plan(a, &pl, false))
+        return 0;
+    return pl.ws.total_bytes;
+}
+
+fa_status fa_bwd_workspace_layout(const fa_bwd_args *a, fa_bwd_ws_layout *out)
+{
+    if (!out)
+        return fail(FA_ERR_INVALID_ARG, "out is NULL");
+    Plan pl;
+    fa_status st = make_plan(a, &pl, false);
+    if (st)
+        return st;
+    *out = pl.ws;
+    return FA_OK;
+}
+
+fa_status fa_bwd_validate(const fa_bwd_args *a)
+{
+    Plan pl;
+    return make_plan(a, &pl, true);
+}
+
+fa_status fa_bwd(const fa_bwd_args *a, void *stream) { return run(a, stream, kPre | kMain | kConv); }
+fa_status fa_bwd_preprocess(const fa_bwd_args *a, void *stream) { return run(a, stream, kPre); }
+fa_status fa_bwd_main(const fa_bwd_args *a, void *stream) { return run(a, stream, kMain); }
+fa_status fa_bwd_dq_convert(const fa_bwd_args *a, void *stream) { return run(a, stream, kConv); }
+
+const char *fa_bwd_last_error(void) { return g_last_error.c_str(); }
+
+int32_t fa_bwd_abi_version(void) { return FA_BWD_ABI_VERSION; }
+
+}  // extern "C"

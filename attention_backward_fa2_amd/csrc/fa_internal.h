@@ -1,0 +1,109 @@
+// fa_internal.h -- parameters and device helpers shared by the gfx950 kernels
+// of the attention backward and their host launcher.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Tile sizes of the main kernel.  One workgroup owns kKTile keys of one KV
+// head; it streams query tiles of kQTile rows.  Four wave64s, each owning 32
+// of the keys.
+constexpr int kQTile = 64;
+constexpr int kKTile = 128;
+constexpr int kThreads = 256;
+
+// Rows per workgroup of the preprocess and dq_convert kernels (16 lanes per
+// row, 16 rows per 256-thread workgroup).
+constexpr int kRowsPerBlock = 16;
+
+// Bound on the iterations of an ordered (deterministic) wait.  A wait that
+// runs out sets flags[0] and proceeds, so every wave always exits.
+constexpr int kSpinLimit = 1 << 24;
+
+// Everything a kernel needs, passed by value.  Strides are in elements:
+// *_sb batch, *_ss row (token), *_sh head.  For packed inputs the batch
+// stride is unused and the row index is cu_seqlens[s] + i.
+struct Params {
+    const uint16_t *q, *k, *v, *o, *dout;
+    const float *lse;
+    uint16_t *dq, *dk, *dv;
+    float *lse2, *rowdot, *dq_acc;
+    int *turns, *flags;
+    const int *cu_q, *cu_k;
+
+    int64_t q_sb, q_ss, q_sh;
+    int64_t k_sb, k_ss, k_sh;
+    int64_t v_sb, v_ss, v_sh;
+    int64_t o_sb, o_ss, o_sh;
+    int64_t do_sb, do_ss, do_sh;
+    int64_t dq_sb, dq_ss, dq_sh;
+    int64_t dk_sb, dk_ss, dk_sh;
+    int64_t dv_sb, dv_ss, dv_sh;
+    int64_t lse_sb, lse_sh;
+
+    int64_t rows;       // workspace rows (batch*Sq dense, total_q packed)
+    int batch, H, Hk, G, D;
+    int Sq, Sk;         // dense lengths, or the maxima for packed input
+    int mtiles;         // ceil(Sq / kQTile)
+    int ntiles;         // ceil(Sk / kKTile)
+    float scale;        // softmax scale
+    float scale_log2;   // softmax scale * log2(e)
+    int causal, deterministic, varlen;
+};
+
+// Lengths and first rows of sequence b.
+struct SeqInfo {
+    int Lq, Lk;
+    int64_t tok_q, tok_k;   // first token row (packed) -- 0 for dense
+    int64_t ws_row;         // workspace row of query 0
+};
+
+__device__ inline SeqInfo seq_info(const Params &p, int b)
+{
+    SeqInfo s;
+    if (p.varlen) {
+        const int q0 = p.cu_q[b], q1 = p.cu_q[b + 1];
+        const int k0 = p.cu_k[b], k1 = p.cu_k[b + 1];
+        s.Lq = q1 - q0;
+        s.Lk = k1 - k0;
+        s.tok_q = q0;
+        s.tok_k = k0;
+        s.ws_row = q0;
+    } else {
+        s.Lq = p.Sq;
+        s.Lk = p.Sk;
+        s.tok_q = 0;
+        s.tok_k = 0;
+        s.ws_row = (int64_t)b * p.Sq;
+    }
+    return s;
+}
+
+// Element offset of row `i` of sequence `b` in a tensor with the given
+// batch / row strides.
+__device__ inline int64_t row_offset(const Params &p, int b, int64_t tok0, int64_t i,
+                                     int64_t sb, int64_t ss)
+{
+    return p.varlen ? (tok0 + i) * ss : (int64_t)b * sb + i * ss;
+}
+
+// fp32 -> bf16, round to nearest even (hardware convert on gfx950).
+__device__ inline uint16_t f2bf(float x)
+{
+    const __bf16 h = (__bf16)x;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ inline float bf2f(uint16_t x)
+{
+    return __builtin_bit_cast(float, (uint32_t)x << 16);
+}
+
+// Host-side launchers (one translation unit each).
+hipError_t launch_preprocess(const Params &p, int dpad, hipStream_t st);
+hipError_t launch_main(const Params &p, int dpad, hipStream_t st);
+hipError_t launch_convert(const Params &p, int dpad, hipStream_t st);
+
+}  // namespace fa

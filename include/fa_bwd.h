@@ -1,0 +1,194 @@
+/*
+ * fa_bwd.h -- C ABI of the MI355X (gfx950) FlashAttention-2 backward library.
+ *
+ * Given Q, K, V, the forward output O, the upstream gradient dO and the
+ * forward's per-row log-sum-exp, the library computes dQ, dK and dV of
+ *     O = softmax(scale * Q K^T + causal mask) V
+ * without ever forming the Sq x Sk score matrix: it recomputes each score tile
+ * from Q, K and the saved LSE (sm90 backward kernel page, mma_one_m_block:
+ * the scores, P = exp(S - LSE), dP = dO V^T, dS = P (dP - rowsum(dO * O)),
+ * then dV += P^T dO, dQ = dS K, dK += dS^T Q).
+ *
+ * Work is enqueued on the caller's HIP stream as three kernels:
+ *   1. preprocess : rowsum(dO * O) per query row and head (the softmax_d /
+ *                   dsoftmax_sum buffer of the backward call-trace page,
+ *                   set_params_dgrad), LSE converted to base 2, and the fp32
+ *                   dQ accumulator cleared;
+ *   2. main       : one workgroup per 128-key tile of one KV head; it keeps
+ *                   the K/V tile and its dK/dV accumulators on chip, loops
+ *                   over every query head of the KV head's group (the GQA
+ *                   reduction of the GQA/MQA page's backward section happens
+ *                   in registers) and over the visible 64-row query tiles,
+ *                   and adds each dQ partial into the fp32 accumulator;
+ *   3. dq_convert : dQ = bf16(scale * accumulator) (the dq_accum reduction
+ *                   step named on the backward call-trace page).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers; all strides are in ELEMENTS.
+ *   - The caller owns every buffer, the workspace included.  The library
+ *     allocates nothing and keeps no state apart from a thread-local error
+ *     string.  Inputs are never written.
+ *   - Calls return as soon as the work is enqueued (asynchronous, like the
+ *     current-stream launch on the backward call-trace page).  `stream` is a
+ *     hipStream_t passed as void*; NULL means the default stream.
+ *   - Validation happens entirely on the host before any launch: on error
+ *     nothing is enqueued, the status code says which class of error, and
+ *     fa_bwd_last_error() says why.
+ *   - Device-side contents (cu_seqlens values) cannot be validated on the
+ *     host; the caller guarantees them (see fa_bwd_args).
+ */
+#ifndef FA_BWD_H
+#define FA_BWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_BWD_ABI_VERSION 1
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1, /* null pointer, bad size, H % Hk != 0, bad stride */
+    FA_ERR_UNSUPPORTED = 2, /* dtype other than bf16, head_dim > 128 or not a multiple of 8 */
+    FA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than fa_bwd_workspace_size() */
+    FA_ERR_HIP = 4          /* a HIP launch or attribute call failed */
+} fa_status;
+
+typedef enum {
+    FA_DTYPE_BF16 = 0
+} fa_dtype;
+
+/*
+ * Arguments of one backward call.  The field order follows the backward
+ * call-trace page's mha_bwd / _flash_attn_backward argument list:
+ * (dout, q, k, v, out, softmax_lse, dq, dk, dv, softmax_scale, causal,
+ *  cu_seqlens_q/k, deterministic).
+ *
+ * Shapes and layouts (bshd = batch, seq, head, dim), as on the backward
+ * call-trace page's mha_bwd:
+ *   dense  (cu_seqlens_q == cu_seqlens_k == NULL):
+ *     q, out, dout, dq : (batch, seqlen_q, num_heads,   head_dim)
+ *     k, v, dk, dv     : (batch, seqlen_k, num_heads_k, head_dim)
+ *     lse              : (batch, num_heads, seqlen_q) fp32
+ *   packed variable length (both cu_seqlens given; Triton FA2 teaching page,
+ *   flash_attn_varlen_func and the backward kernels' varlen branch):
+ *     q, out, dout, dq : (total_q, num_heads,   head_dim)
+ *     k, v, dk, dv     : (total_k, num_heads_k, head_dim)
+ *     lse              : (batch, num_heads, seqlen_q) fp32, where batch is the
+ *                        number of sequences and seqlen_q the maximum query
+ *                        length; sequence s uses lse[s, h, 0 : len_q(s)]
+ *     cu_seqlens_q/k   : device int32[batch + 1], cu[0] = 0, non-decreasing,
+ *                        cu_seqlens_q[batch] == total_q (and k likewise);
+ *                        every len_q(s) <= seqlen_q and len_k(s) <= seqlen_k.
+ * Strides: x_stride[0] = batch stride (ignored for packed inputs),
+ *          x_stride[1] = row (token) stride, x_stride[2] = head stride;
+ *          the head_dim stride must be 1.  All three must be multiples of 8
+ *          elements and every base pointer 16-byte aligned (128-bit rows, as
+ *          the sm90 backward page's __call__ requires of its strides).
+ *          lse_stride[0] = batch/sequence stride, lse_stride[1] = head stride,
+ *          row stride 1.
+ *
+ * Semantics:
+ *   - Scores are S = softmax_scale * Q K^T.  Query head h reads KV head
+ *     h / (num_heads / num_heads_k) (GQA/MQA page, KV head mapping).
+ *   - causal = 1 masks key j for query i unless j <= i + len_k - len_q
+ *     (bottom-right aligned, GQA/MQA page, causal block bound).
+ *   - lse is the NATURAL-log log-sum-exp of the scaled scores of each row,
+ *     -inf for a row with no visible key (its dQ is then 0).
+ *   - dq, dk, dv are fully overwritten over their valid rows and the first
+ *     head_dim columns; dk/dv of keys no query can see are written as 0.
+ *     They must not alias any input or the workspace.
+ *   - head_dim padding: head_dim must be a multiple of 8 and <= 128; kernels
+ *     run at a padded tile width of 64, 96 or 128 with zero-filled loads and
+ *     masked stores (sm90 backward page, __init__: head dim rounded up to
+ *     the tile multiple; backward call-trace page, dout padding step).
+ *   - deterministic = 1: dQ partial sums are added in a fixed order (per
+ *     query tile, in descending key-tile order), so repeated calls with the
+ *     same inputs and workspace size give bit-identical dq, dk, dv.
+ *     deterministic = 0: dQ partials use unordered fp32 atomics; dk and dv
+ *     are bit-reproducible in both modes.
+ *   - Empty inputs: batch == 0 enqueues nothing.  A sequence with no query
+ *     rows gets dk = dv = 0 for its keys; one with no keys gets dq = 0.
+ *     Pointers of tensors with no elements may be NULL.
+ */
+typedef struct fa_bwd_args {
+    int32_t dtype;                 /* fa_dtype; only FA_DTYPE_BF16 */
+    int32_t batch;                 /* dense: B; packed: number of sequences */
+    int32_t seqlen_q, seqlen_k;    /* dense: Sq, Sk; packed: maximum lengths */
+    int32_t num_heads, num_heads_k, head_dim;
+    const int32_t *cu_seqlens_q;   /* device; NULL for dense */
+    const int32_t *cu_seqlens_k;   /* device; NULL for dense */
+    int64_t total_q, total_k;      /* packed: cu_seqlens_q/k[batch] (host copies) */
+
+    const void *dout, *q, *k, *v, *out;  /* bf16 */
+    const float *lse;                    /* fp32, natural log */
+    void *dq, *dk, *dv;                  /* bf16 outputs */
+
+    int64_t do_stride[3], q_stride[3], k_stride[3], v_stride[3], o_stride[3];
+    int64_t dq_stride[3], dk_stride[3], dv_stride[3];
+    int64_t lse_stride[2];
+
+    float softmax_scale;           /* the caller passes it (usually 1/sqrt(head_dim)) */
+    int32_t causal;                /* 0 or 1 */
+    int32_t deterministic;         /* 0 or 1 */
+
+    void *workspace;               /* device, 256-byte aligned, caller-owned */
+    size_t workspace_bytes;
+} fa_bwd_args;
+
+/*
+ * Workspace layout (byte offsets from `workspace`, each 256-byte aligned).
+ * rows = batch * seqlen_q (dense) or total_q (packed); row index of query i
+ * of sequence s is s * seqlen_q + i (dense) or cu_seqlens_q[s] + i (packed).
+ *   lse2   : float[num_heads][rows]   LSE * log2(e), +inf for rows with no key
+ *   rowdot : float[num_heads][rows]   sum_d dO * O (fp32 accumulation)
+ *   dq_acc : float[num_heads][rows][head_dim_pad]  unscaled fp32 dQ sums
+ *   turns  : int32[batch][num_heads][ceil(seqlen_q / 64)] ordering counters
+ *   flags  : int32[4]  flags[0] != 0 if an ordered wait gave up (should
+ *                      never happen; dq is then not bit-reproducible)
+ */
+typedef struct fa_bwd_ws_layout {
+    int64_t rows;
+    int32_t head_dim_pad;
+    int32_t q_tile;                /* 64: rows per query tile */
+    int32_t k_tile;                /* 128: keys per workgroup */
+    size_t off_lse2, off_rowdot, off_dq_acc, off_turns, off_flags;
+    size_t total_bytes;
+} fa_bwd_ws_layout;
+
+/* Bytes of workspace the call needs; 0 if the arguments are invalid (host
+ * only, touches no device memory). */
+size_t fa_bwd_workspace_size(const fa_bwd_args *a);
+
+/* Fills *out with the workspace layout of these arguments.  Host only. */
+fa_status fa_bwd_workspace_layout(const fa_bwd_args *a, fa_bwd_ws_layout *out);
+
+/* Checks every host-visible argument (pointers, sizes, strides, alignment,
+ * workspace size).  Host only: no GPU access, nothing enqueued. */
+fa_status fa_bwd_validate(const fa_bwd_args *a);
+
+/* The whole backward: preprocess, main and dq_convert, enqueued on `stream`. */
+fa_status fa_bwd(const fa_bwd_args *a, void *stream);
+
+/* The three steps one at a time, in this order, on one stream (each
+ * validates like fa_bwd).  Used to time and test the kernels separately;
+ * fa_bwd_main needs a completed fa_bwd_preprocess on the same workspace and
+ * fa_bwd_dq_convert a completed fa_bwd_main. */
+fa_status fa_bwd_preprocess(const fa_bwd_args *a, void *stream);
+fa_status fa_bwd_main(const fa_bwd_args *a, void *stream);
+fa_status fa_bwd_dq_convert(const fa_bwd_args *a, void *stream);
+
+/* Reason of the last non-FA_OK status on this thread ("" if none). */
+const char *fa_bwd_last_error(void);
+
+/* FA_BWD_ABI_VERSION of the built library. */
+int32_t fa_bwd_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_BWD_H */

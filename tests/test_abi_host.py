@@ -1,0 +1,158 @@
+"""Host-only checks of the C ABI: the built library loads, exports every
+function include/fa_bwd.h declares, and rejects bad arguments with the right
+status before touching the GPU.  Fake (never dereferenced) aligned addresses
+stand in for device pointers."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_backward_fa2_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_bwd.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_bwd\w*)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = fa.load_library()
+    names = _declared_functions()
+    assert len(names) >= 9, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(fa.EXPORTED)
+    assert lib.fa_bwd_abi_version() == 1
+
+
+def test_struct_mirror_matches_header_field_order():
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct fa_bwd_args"):text.index("} fa_bwd_args;")]
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    decl = re.findall(r"(\*?\w+)(?:\[\d\])?\s*[,;]", body)
+    names = [d.lstrip("*") for d in decl]
+    assert names == [f[0] for f in fa.FaBwdArgs._fields_]
+
+
+BASE = 0x7f0000000000
+
+
+def _args(**over):
+    a = fa.FaBwdArgs()
+    a.dtype = fa.FA_DTYPE_BF16
+    a.batch, a.seqlen_q, a.seqlen_k = 2, 256, 384
+    a.num_heads, a.num_heads_k, a.head_dim = 8, 2, 128
+    H, Hk, D, Sq, Sk = 8, 2, 128, 256, 384
+    addr = BASE
+    for name in ("dout", "q", "k", "v", "out", "lse", "dq", "dk", "dv"):
+        setattr(a, name, addr)
+        addr += 1 << 30
+    for name in ("do_stride", "q_stride", "o_stride", "dq_stride"):
+        getattr(a, name)[:] = (Sq * H * D, H * D, D)
+    for name in ("k_stride", "v_stride", "dk_stride", "dv_stride"):
+        getattr(a, name)[:] = (Sk * Hk * D, Hk * D, D)
+    a.lse_stride[:] = (H * Sq, Sq)
+    a.softmax_scale = D ** -0.5
+    a.causal = 1
+    for k, v in over.items():
+        if isinstance(getattr(a, k), ctypes.Array):
+            getattr(a, k)[:] = v
+        else:
+            setattr(a, k, v)
+    return a
+
+
+def _with_ws(a):
+    n = fa.workspace_size(a)
+    a.workspace = BASE + (40 << 30)
+    a.workspace_bytes = n
+    return a
+
+
+def test_workspace_layout_formula():
+    a = _args()
+    lay = fa.workspace_layout(a)
+    rows = 2 * 256
+    assert lay.rows == rows and lay.head_dim_pad == 128
+    assert lay.q_tile == 64 and lay.k_tile == 128
+
+    def al(x):
+        return (x + 255) // 256 * 256
+    assert lay.off_lse2 == 0
+    assert lay.off_rowdot == al(8 * rows * 4)
+    assert lay.off_dq_acc == lay.off_rowdot + al(8 * rows * 4)
+    assert lay.off_turns == lay.off_dq_acc + al(8 * rows * 128 * 4)
+    assert lay.off_flags == lay.off_turns + al(2 * 8 * 4 * 4)
+    assert lay.total_bytes == lay.off_flags + 256
+    assert fa.workspace_size(a) == lay.total_bytes
+
+
+@pytest.mark.parametrize("d,pad", [(8, 64), (64, 64), (72, 96), (96, 96), (104, 128),
+                                   (128, 128)])
+def test_head_dim_padding(d, pad):
+    a = _args(head_dim=d, do_stride=(256 * 8 * d, 8 * d, d), q_stride=(256 * 8 * d, 8 * d, d),
+              o_stride=(256 * 8 * d, 8 * d, d), dq_stride=(256 * 8 * d, 8 * d, d),
+              k_stride=(384 * 2 * d, 2 * d, d), v_stride=(384 * 2 * d, 2 * d, d),
+              dk_stride=(384 * 2 * d, 2 * d, d), dv_stride=(384 * 2 * d, 2 * d, d))
+    assert fa.workspace_layout(a).head_dim_pad == pad
+
+
+def test_valid_args_pass_validation():
+    assert fa.validate(_with_ws(_args())) == fa.FA_OK
+
+
+@pytest.mark.parametrize("over,status", [
+    ({"num_heads_k": 3}, fa.FA_ERR_INVALID_ARG),          # H % Hk != 0
+    ({"q": 0}, fa.FA_ERR_INVALID_ARG),                    # null pointer
+    ({"lse": 0}, fa.FA_ERR_INVALID_ARG),
+    ({"dk": BASE + 8}, fa.FA_ERR_INVALID_ARG),            # misaligned
+    ({"q_stride": (256 * 8 * 128, 8 * 128 + 4, 128)}, fa.FA_ERR_INVALID_ARG),
+    ({"batch": -1}, fa.FA_ERR_INVALID_ARG),
+    ({"head_dim": 0}, fa.FA_ERR_INVALID_ARG),
+    ({"causal": 2}, fa.FA_ERR_INVALID_ARG),
+    ({"softmax_scale": float("nan")}, fa.FA_ERR_INVALID_ARG),
+    ({"cu_seqlens_q": BASE}, fa.FA_ERR_INVALID_ARG),      # only one cu_seqlens
+    ({"dtype": 1}, fa.FA_ERR_UNSUPPORTED),
+    ({"head_dim": 300}, fa.FA_ERR_UNSUPPORTED),
+    ({"head_dim": 100}, fa.FA_ERR_UNSUPPORTED),           # not a multiple of 8
+    ({"head_dim": 192}, fa.FA_ERR_UNSUPPORTED),           # > 128 not built
+])
+def test_validation_errors(over, status):
+    a = _args(**over)
+    a.workspace = BASE + (40 << 30)
+    a.workspace_bytes = 1 << 40
+    assert fa.validate(a) == status
+    assert fa.load_library().fa_bwd_last_error().decode() != ""
+    assert fa.load_library().fa_bwd_workspace_size(ctypes.byref(a)) == 0
+
+
+def test_workspace_errors():
+    a = _args()
+    assert fa.validate(a) == fa.FA_ERR_WORKSPACE            # none given
+    _with_ws(a)
+    a.workspace_bytes -= 1
+    assert fa.validate(a) == fa.FA_ERR_WORKSPACE            # too small
+    _with_ws(a)
+    a.workspace += 64
+    assert fa.validate(a) == fa.FA_ERR_WORKSPACE            # misaligned
+
+
+def test_launch_entry_points_reject_before_touching_the_gpu():
+    lib = fa.load_library()
+    a = _args(num_heads_k=3)
+    for name in ("fa_bwd", "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_dq_convert"):
+        assert getattr(lib, name)(ctypes.byref(a), None) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_bwd(None, None) == fa.FA_ERR_INVALID_ARG
+
+
+def test_varlen_layout_uses_total_rows():
+    a = _args(cu_seqlens_q=BASE, cu_seqlens_k=BASE + 256, total_q=1000, total_k=1200,
+              batch=5, seqlen_q=300, seqlen_k=400)
+    lay = fa.workspace_layout(a)
+    assert lay.rows == 1000
+    assert lay.off_flags - lay.off_turns == ((5 * 8 * 5 * 4 + 255) // 256) * 256

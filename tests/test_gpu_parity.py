@@ -1,0 +1,208 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on
+the same seeded inputs.  Bar: per gradient tensor max|gpu - ref| <= 1e-2 *
+max|ref| (bf16 I/O); ordered mode bit-identical across runs; preprocess and
+dq_convert checked against their exact definitions."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests import parity as PT
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _flush(msg):
+    print(msg, flush=True)
+
+
+# Small cases: full oracle, several tiles, ragged tails.
+SMALL = {
+    "c1_mha_s128_d64": lambda: W.make_inputs(W.WORKLOADS[1]),
+    "dense_causal_ragged_gqa2_d64": lambda: W.make_inputs(
+        W.custom("r1", 2, 4, 2, 200, 200, 64, True, seed=101)),
+    "causal_sq_lt_sk_mqa_d128": lambda: W.make_inputs(
+        W.custom("r2", 1, 4, 1, 130, 300, 128, True, seed=102)),
+    "causal_sq_gt_sk_empty_rows_d128": lambda: W.make_inputs(
+        W.custom("r3", 1, 4, 2, 300, 130, 128, True, seed=103)),
+    "noncausal_gqa4_d128": lambda: W.make_inputs(
+        W.custom("r4", 1, 8, 2, 256, 192, 128, False, seed=104)),
+    "headdim72_padded_noncausal": lambda: W.make_inputs(
+        W.custom("r5", 1, 2, 2, 150, 150, 72, False, seed=105)),
+    "varlen_d96_causal": lambda: W.make_inputs(
+        W.Workload("r6", 3, 2, 2, 0, 0, 96, True, varlen=True, seed=106),
+        lengths=[100, 257, 64]),
+    "varlen_unequal_and_empty_causal_d64": lambda: W.custom_varlen(
+        "r7", [70, 0, 190, 33], [130, 50, 190, 0], 4, 2, 64, True, seed=107),
+    "varlen_unequal_noncausal_d128": lambda: W.custom_varlen(
+        "r8", [70, 129, 1], [200, 64, 300], 2, 1, 128, False, seed=108),
+}
+
+
+@pytest.fixture(scope="module")
+def prepared():
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            cache[name] = PT.Prepared(SMALL[name]())
+        return cache[name]
+    return get
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_small_full_parity(gpu_lib, prepared, name, deterministic):
+    _flush("case %s deterministic=%s" % (name, deterministic))
+    pr = prepared(name)
+    res = PT.run_gpu(pr, deterministic=deterministic)
+    ref = PT.oracle_backward(pr)
+    for key in ("dq", "dk", "dv"):
+        PT.compare(pr.inp.packed(res[key]), ref[key], "%s %s" % (name, key))
+    flags = PT.ws_view(res, "flags", torch.int32, 4, (4,))
+    assert int(flags[0]) == 0
+
+
+@pytest.mark.parametrize("name", ["dense_causal_ragged_gqa2_d64", "varlen_d96_causal",
+                                  "causal_sq_gt_sk_empty_rows_d128"])
+def test_ordered_mode_is_bit_reproducible(gpu_lib, prepared, name):
+    _flush("case %s ordered x3" % name)
+    pr = prepared(name)
+    runs = [PT.run_gpu(pr, deterministic=True) for _ in range(3)]
+    for key in ("dq", "dk", "dv"):
+        for r in runs[1:]:
+            assert torch.equal(r[key].view(torch.int16), runs[0][key].view(torch.int16)), key
+
+
+def test_dk_dv_reproducible_in_atomic_mode(gpu_lib, prepared):
+    pr = prepared("noncausal_gqa4_d128")
+    a = PT.run_gpu(pr)
+    b = PT.run_gpu(pr)
+    for key in ("dk", "dv"):
+        assert torch.equal(a[key].view(torch.int16), b[key].view(torch.int16)), key
+
+
+@pytest.mark.parametrize("name", ["headdim72_padded_noncausal",
+                                  "varlen_unequal_and_empty_causal_d64"])
+def test_columns_past_head_dim_untouched(gpu_lib, prepared, name):
+    pr = prepared(name)
+    res = PT.run_gpu(pr, out_pad=8)
+    D = pr.inp.wl.head_dim
+    for key in ("dq_buf", "dk_buf", "dv_buf"):
+        assert torch.isnan(res[key][..., D:].float()).all(), key
+    ref = PT.oracle_backward(pr)
+    for key in ("dq", "dk", "dv"):
+        PT.compare(pr.inp.packed(res[key]), ref[key], key)
+
+
+def test_step_by_step_entry_points_match_fused_call(gpu_lib, prepared):
+    pr = prepared("dense_causal_ragged_gqa2_d64")
+    a = PT.run_gpu(pr, deterministic=True)
+    b = PT.run_gpu(pr, deterministic=True, step_split=True)
+    for key in ("dq", "dk", "dv"):
+        assert torch.equal(a[key].view(torch.int16), b[key].view(torch.int16)), key
+
+
+@pytest.mark.parametrize("name", ["dense_causal_ragged_gqa2_d64", "varlen_d96_causal",
+                                  "causal_sq_gt_sk_empty_rows_d128"])
+def test_preprocess_rowdot_and_lse2(gpu_lib, prepared, name):
+    """rowdot = sum_d dO*O with fp32 accumulation of exact bf16 products:
+    within the summation bound (D+1) 2^-24 sum|dO*O| of the fp64 value;
+    lse2 = LSE*log2(e) (+inf for rows without a visible key)."""
+    pr = prepared(name)
+    res = PT.run_gpu(pr)
+    H, T, D = pr.inp.wl.heads, int(pr.cu_q[-1]), pr.inp.wl.head_dim
+    rowdot = PT.ws_view(res, "rowdot", torch.float32, H * T, (H, T)).numpy().T
+    lse2 = PT.ws_view(res, "lse2", torch.float32, H * T, (H, T)).numpy().T
+    ref = O.rowdot(pr.do64, pr.o64)
+    absum = O.rowdot(np.abs(pr.do64), np.abs(pr.o64))
+    bound = (D + 1) * 2.0 ** -24 * absum + 1e-30
+    assert np.all(np.abs(rowdot - ref) <= bound)
+    lse32 = pr.lse_rows.astype(np.float32)
+    empty = np.isneginf(lse32)
+    assert np.all(np.isposinf(lse2[empty]))
+    want = lse32[~empty].astype(np.float64) * np.log2(np.e)
+    assert np.all(np.abs(lse2[~empty] - want) <= 2e-7 * np.maximum(1.0, np.abs(want)))
+
+
+def test_dq_convert_is_exact_scaled_rne(gpu_lib, prepared):
+    pr = prepared("varlen_unequal_noncausal_d128")
+    res = PT.run_gpu(pr)
+    lay = res["layout"]
+    H, T, DP, D = pr.inp.wl.heads, int(pr.cu_q[-1]), lay.head_dim_pad, pr.inp.wl.head_dim
+    acc = PT.ws_view(res, "dq_acc", torch.float32, H * T * DP, (H, T, DP))
+    scale = torch.tensor(pr.inp.wl.scale, dtype=torch.float32)
+    want = (acc[:, :, :D] * scale).to(torch.bfloat16).permute(1, 0, 2)
+    got = pr.inp.packed(res["dq"])
+    assert torch.equal(got.view(torch.int16), want.contiguous().view(torch.int16))
+
+
+def test_dk_dv_column_sum_invariants(gpu_lib, prepared):
+    """sum_j dK_j = 0 (softmax is invariant to shifting all keys) and
+    sum_j dV_j = sum over rows with a visible key of dO_i, per KV head."""
+    pr = prepared("causal_sq_lt_sk_mqa_d128")
+    res = PT.run_gpu(pr)
+    dk = pr.inp.packed(res["dk"]).double().numpy()
+    dv = pr.inp.packed(res["dv"]).double().numpy()
+    G = pr.inp.wl.heads // pr.inp.wl.heads_k
+    vis = ~np.isneginf(pr.lse_rows)               # [T, H]
+    for g in range(pr.inp.wl.heads_k):
+        s_dk = dk[:, g].sum(0)
+        assert np.abs(s_dk).max() <= 1e-2 * np.abs(dk[:, g]).sum(0).max()
+        want = sum((pr.do64[:, h] * vis[:, h:h + 1]).sum(0) for h in range(g * G, (g + 1) * G))
+        assert np.abs(dv[:, g].sum(0) - want).max() <= 1e-2 * np.abs(dv[:, g]).sum(0).max()
+
+
+def test_zero_query_rows_write_zero_dk_dv(gpu_lib):
+    """Dense seqlen_q == 0 with keys: dk and dv are written as zeros."""
+    dev = torch.device("cuda")
+    B, Sk, H, D = 1, 200, 2, 64
+    q = torch.zeros(B, 0, H, D, dtype=torch.bfloat16, device=dev)
+    k = torch.randn(B, Sk, H, D, device=dev).to(torch.bfloat16)
+    v = torch.randn(B, Sk, H, D, device=dev).to(torch.bfloat16)
+    lse = torch.zeros(B, H, 0, dtype=torch.float32, device=dev)
+    dq = torch.empty_like(q)
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(v, float("nan"))
+    import attention_backward_fa2_amd as fa
+    fa.fa_bwd(q, q, k, v, q, lse, dq, dk, dv, D ** -0.5, True)
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)
+
+
+# ---------------- reference workloads at full size ----------------
+
+def _full(cid):
+    return PT.Prepared(W.make_inputs(W.WORKLOADS[cid]))
+
+
+@pytest.mark.slow
+def test_config2_full_parity(gpu_lib):
+    _flush("config 2 full")
+    pr = _full(2)
+    for det in (False, True):
+        res = PT.run_gpu(pr, deterministic=det)
+        ref = PT.oracle_backward(pr)
+        for key in ("dq", "dk", "dv"):
+            PT.compare(pr.inp.packed(res[key]), ref[key], "c2 %s det=%s" % (key, det))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cid,units", [(3, [(0, 0), (1, 5)]), (4, [(0, 3)]),
+                                       (5, [(0, 0), (7, 9)])])
+def test_full_size_sampled_units(gpu_lib, cid, units):
+    """Full-size launch (the configuration the benchmark times); the oracle
+    computes sampled (sequence, KV-head group) units exactly."""
+    _flush("config %d full size, sampled units %s" % (cid, units))
+    pr = _full(cid)
+    res = PT.run_gpu(pr)
+    dq, dk, dv = (pr.inp.packed(res[k]) for k in ("dq", "dk", "dv"))
+    for (s, g) in units:
+        s = min(s, len(pr.inp.lens_q) - 1)
+        rq, heads, rk, ref = PT.oracle_backward_unit(pr, s, g)
+        PT.compare(dq[rq][:, heads], ref["dq"], "c%d dq s%d g%d" % (cid, s, g))
+        PT.compare(dk[rk][:, [g]], ref["dk"], "c%d dk s%d g%d" % (cid, s, g))
+        PT.compare(dv[rk][:, [g]], ref["dv"], "c%d dv s%d g%d" % (cid, s, g))
+    for key in ("dq", "dk", "dv"):
+        assert torch.isfinite(res[key].float()).all(), key
