@@ -22,19 +22,28 @@
 //   A (32 x 16, M x K): row l32, k = 8*g2 + t (t = 0..7, one 16-byte vector)
 //   B (16 x 32, K x N): col l32, k = 8*g2 + t
 //   C (32 x 32):        col l32, row 8*(r/4) + 4*g2 + r%4 for r = 0..15
-// Each wave owns keys 32w .. 32w+31 of the tile.  With keys as the N index of
-// S and dP, the accumulator of P (and dS) holds one key and 16 query rows per
-// lane, which is exactly a B operand for dV^T = dO^T P and dK^T = Q^T dS
-// with the query index (the contraction index) permuted within each group
-// of 16: MFMA k-slot 8*g2 + t  <->  query 4*g2 + t (t < 4) or 8 + 4*g2 + t-4.
-// The A operands dO^T and Q^T are read from transposed LDS copies stored in
-// that same permuted order, so each is one 16-byte LDS read.  dQ = dS K
-// needs dS with keys as the contraction index, so dS goes through LDS.
+// Each wave owns keys 32w .. 32w+31 of the tile; their K and V rows stay in
+// registers as the B operands of S and dP.  With keys as the N index, the
+// accumulator of P (and dS) holds one key and 16 query rows per lane, which
+// is directly a B operand of dV^T = dO^T P and dK^T = Q^T dS once the query
+// (contraction) index is permuted within each group of 16:
+//   k-slot 8*g2 + t  <->  query 4*g2 + t (t < 4) or 8 + 4*g2 + t - 4.
+// Operands whose contraction index runs down the rows of a row-major LDS
+// tile (dO^T, Q^T, and both operands of dQ = dS K) are read with the gfx950
+// transposing LDS read ds_read_b64_tr_b16: within each 16-lane group the 16
+// 8-byte reads form a 4 x 16 block (lanes 4r..4r+3 read row r) and lane c
+// receives column c.  Two such reads give one 8-element operand, and the row
+// base of each read implements the permutation above.  No transposed copies
+// are stored.
 //
-// LDS (D_pad = 128): Q, dO row-major 2 x 17 KB, Q^T, dO^T 2 x 18 KB, dS
-// 17 KB, K^T 34 KB, two 256-byte row vectors: 121.5 KB per workgroup, one
-// workgroup per CU.  Rows are padded by 16 bytes so that the 16-byte reads
-// of 16 consecutive rows fall in distinct banks.
+// LDS (D_pad = 128): Q and dO row-major, double buffered (4 x 18 KB), dS^T
+// 20 KB, K 36 KB, row vectors 1 KB: 129 KB, one workgroup per CU.  Row
+// pitches are D + 16 elements (dS^T: 64 + 16) so that both the 16-byte row
+// reads and the transposing reads hit distinct banks.
+//
+// Pipelining: the next query tile is loaded from global memory into
+// registers while the current one is computed, then written to the other
+// LDS buffer; two workgroup barriers per tile.
 #include "fa_internal.h"
 
 namespace fa {
@@ -42,6 +51,9 @@ namespace fa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
 {
@@ -49,65 +61,41 @@ __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
 }
 
 template <int DP>
-struct Smem {
-    static constexpr int RQ = DP + 8;       // row stride of q / dO (elements)
-    static constexpr int RT = kQTile + 8;   // row stride of q^T / dO^T
-    static constexpr int RS = kKTile + 8;   // row stride of dS / K^T
-    uint16_t q[kQTile * RQ];
-    uint16_t dO[kQTile * RQ];
-    uint16_t qt[DP * RT];
-    uint16_t dOt[DP * RT];
-    uint16_t ds[kQTile * RS];
-    uint16_t kt[DP * RS];
-    float lse2[kQTile];
-    float rowdot[kQTile];
+struct __attribute__((aligned(16))) Smem {
+    static constexpr int RQ = DP + 16;       // pitch of q / dO / k (elements)
+    static constexpr int RD = kQTile + 16;   // pitch of dS^T
+    uint16_t q[2][kQTile * RQ];
+    uint16_t dO[2][kQTile * RQ];
+    uint16_t dsT[kKTile * RD];
+    uint16_t k[kKTile * RQ];
+    float lse2[2][kQTile];
+    float rowdot[2][kQTile];
 };
-
-// Slot of query row q (0..63) in the transposed copies: within each group of
-// 16 rows the two middle groups of 4 swap places, so that k-slots
-// 8*g2 .. 8*g2+7 of an MFMA step hold rows {4*g2..4*g2+3, 8+4*g2..8+4*g2+3}.
-__device__ inline int qslot(int q)
-{
-    const int a = (q >> 2) & 3;
-    const int na = ((a & 1) << 1) | (a >> 1);
-    return (q & ~12) | (na << 2);
-}
 
 __device__ inline bf16x8 lds16(const uint16_t *p)
 {
     return *reinterpret_cast<const bf16x8 *>(p);
 }
 
-template <int DP>
-__device__ inline void load_q_tile(const Params &p, Smem<DP> &sm, const uint16_t *qbase,
-                                   const uint16_t *dobase, int rows_valid, int tid)
+__device__ inline i16x4 lds_tr(const uint16_t *p)
 {
-    constexpr int CPR = DP / 8;             // 16-byte chunks per row
-    constexpr int NCH = kQTile * CPR;
-    static_assert(NCH % kThreads == 0, "tile load must divide evenly");
-#pragma unroll
-    for (int it = 0; it < NCH / kThreads; ++it) {
-        const int c = tid + it * kThreads;
-        const int r = c / CPR, cc = c % CPR;
-        uint4 vq = make_uint4(0, 0, 0, 0), vd = make_uint4(0, 0, 0, 0);
-        if (r < rows_valid && cc * 8 < p.D) {
-            vq = *reinterpret_cast<const uint4 *>(qbase + r * p.q_ss + cc * 8);
-            vd = *reinterpret_cast<const uint4 *>(dobase + r * p.do_ss + cc * 8);
-        }
-        *reinterpret_cast<uint4 *>(&sm.q[r * Smem<DP>::RQ + cc * 8]) = vq;
-        *reinterpret_cast<uint4 *>(&sm.dO[r * Smem<DP>::RQ + cc * 8]) = vd;
-        const int slot = qslot(r);
-        const uint32_t wq[4] = {vq.x, vq.y, vq.z, vq.w};
-        const uint32_t wd[4] = {vd.x, vd.y, vd.z, vd.w};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int d = cc * 8 + 2 * t;
-            sm.qt[d * Smem<DP>::RT + slot] = (uint16_t)(wq[t] & 0xffff);
-            sm.qt[(d + 1) * Smem<DP>::RT + slot] = (uint16_t)(wq[t] >> 16);
-            sm.dOt[d * Smem<DP>::RT + slot] = (uint16_t)(wd[t] & 0xffff);
-            sm.dOt[(d + 1) * Smem<DP>::RT + slot] = (uint16_t)(wd[t] >> 16);
-        }
-    }
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)((lds_u16 *)p));
+}
+
+// MFMA operand fragment from a row-major LDS matrix whose rows run along the
+// contraction index: the lane receives column c0 + l32 at rows r0 .. r0+3
+// (elements 0..3) and r1 .. r1+3 (elements 4..7).  r0 and r1 may depend on
+// g2 only.
+__device__ inline bf16x8 frag_tr(const uint16_t *base, int pitch, int r0, int r1, int c0,
+                                 int lane)
+{
+    const int c16 = lane & 15;
+    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (c16 & 3);
+    const int rr = c16 >> 2;
+    const i16x4 lo = lds_tr(base + (r0 + rr) * pitch + col);
+    const i16x4 hi = lds_tr(base + (r1 + rr) * pitch + col);
+    const i16x4 v8[2] = {lo, hi};
+    return __builtin_bit_cast(bf16x8, v8);
 }
 
 template <int DP>
@@ -115,7 +103,10 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
 {
     constexpr int KS = DP / 16;       // MFMA k-steps over the head dim
     constexpr int DB = DP / 32;       // 32-wide blocks of the head dim
-    constexpr int RQ = Smem<DP>::RQ, RT = Smem<DP>::RT, RS = Smem<DP>::RS;
+    constexpr int RQ = Smem<DP>::RQ, RD = Smem<DP>::RD;
+    constexpr int CPR = DP / 8;       // 16-byte chunks per tile row
+    constexpr int NCH = kQTile * CPR / kThreads;   // chunks per thread per tile
+    static_assert(kQTile * CPR % kThreads == 0, "tile load must divide evenly");
     __shared__ Smem<DP> sm;
 
     const int tid = threadIdx.x;
@@ -139,7 +130,8 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
     const int key_local = w * 32 + l32;
     const int key = n0 + key_local;
 
-    // ---- K, V fragments of this wave's 32 keys (B operands of S and dP) ----
+    // ---- K, V rows of this wave's 32 keys: B operands of S and dP; the K
+    //      tile also goes to LDS row-major for dQ = dS K. ----
     bf16x8 kf[KS], vf[KS];
     {
         const uint16_t *krow = p.k + row_offset(p, b, si.tok_k, key, p.k_sb, p.k_ss) + hk * p.k_sh;
@@ -154,13 +146,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             }
             kf[ks] = __builtin_bit_cast(bf16x8, kv);
             vf[ks] = __builtin_bit_cast(bf16x8, vv);
-            // K^T in LDS for dQ = dS K (B operand: col d, 8 consecutive keys).
-            const uint32_t wk[4] = {kv.x, kv.y, kv.z, kv.w};
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                sm.kt[(d0 + 2 * t) * RS + key_local] = (uint16_t)(wk[t] & 0xffff);
-                sm.kt[(d0 + 2 * t + 1) * RS + key_local] = (uint16_t)(wk[t] >> 16);
-            }
+            *reinterpret_cast<uint4 *>(&sm.k[key_local * RQ + d0]) = kv;
         }
     }
 
@@ -178,156 +164,221 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
     if (first_q < Lq) {
         const int m_begin = first_q / kQTile;
         const int m_end = (Lq + kQTile - 1) / kQTile;
+        const int nm = m_end - m_begin;
+        const int total = p.G * nm;
         const int nt_b = (Lk + kKTile - 1) / kKTile;
-        for (int hh = 0; hh < p.G; ++hh) {
+
+        // Prefetch registers for one query tile: NCH 16-byte chunks of Q
+        // and of dO per thread, plus one lse2 / rowdot pair (threads < 64).
+        uint4 pq[NCH], pd[NCH];
+        float pl2 = INFINITY, prd = 0.f;
+        auto prefetch = [&](int it) {
+            const int hh = it / nm, m = m_begin + it % nm;
             const int h = hk * p.G + hh;
-            const uint16_t *qhead = p.q + h * p.q_sh;
-            const uint16_t *dohead = p.dout + h * p.do_sh;
+            const int q0 = m * kQTile;
+            const int rows_valid = min(kQTile, Lq - q0);
+            const uint16_t *qb =
+                p.q + h * p.q_sh + row_offset(p, b, si.tok_q, q0, p.q_sb, p.q_ss);
+            const uint16_t *db =
+                p.dout + h * p.do_sh + row_offset(p, b, si.tok_q, q0, p.do_sb, p.do_ss);
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int idx = tid + c * kThreads;
+                const int r = idx / CPR, cc = idx % CPR;
+                pq[c] = make_uint4(0, 0, 0, 0);
+                pd[c] = make_uint4(0, 0, 0, 0);
+                if (r < rows_valid && cc * 8 < p.D) {
+                    pq[c] = *reinterpret_cast<const uint4 *>(qb + r * p.q_ss + cc * 8);
+                    pd[c] = *reinterpret_cast<const uint4 *>(db + r * p.do_ss + cc * 8);
+                }
+            }
+            pl2 = INFINITY;
+            prd = 0.f;
+            if (tid < rows_valid) {
+                const int64_t wr = (int64_t)h * p.rows + si.ws_row + q0 + tid;
+                pl2 = p.lse2[wr];
+                prd = p.rowdot[wr];
+            }
+        };
+        auto stage = [&](int buf) {
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int idx = tid + c * kThreads;
+                const int r = idx / CPR, cc = idx % CPR;
+                *reinterpret_cast<uint4 *>(&sm.q[buf][r * RQ + cc * 8]) = pq[c];
+                *reinterpret_cast<uint4 *>(&sm.dO[buf][r * RQ + cc * 8]) = pd[c];
+            }
+            if (tid < kQTile) {
+                sm.lse2[buf][tid] = pl2;
+                sm.rowdot[buf][tid] = prd;
+            }
+        };
+
+        prefetch(0);
+        stage(0);
+        __syncthreads();
+
+        for (int it = 0; it < total; ++it) {
+            const int buf = it & 1;
+            const int hh = it / nm, m = m_begin + it % nm;
+            const int h = hk * p.G + hh;
+            const int q0 = m * kQTile;
+            const int rows_valid = min(kQTile, Lq - q0);
             const int64_t wsbase = (int64_t)h * p.rows + si.ws_row;
-            for (int m = m_begin; m < m_end; ++m) {
-                const int q0 = m * kQTile;
-                const int rows_valid = min(kQTile, Lq - q0);
+            if (it + 1 < total)
+                prefetch(it + 1);
+            const uint16_t *sq = sm.q[buf];
+            const uint16_t *sdo = sm.dO[buf];
 
-                __syncthreads();   // previous tile fully consumed
-                load_q_tile<DP>(p, sm,
-                                qhead + row_offset(p, b, si.tok_q, q0, p.q_sb, p.q_ss),
-                                dohead + row_offset(p, b, si.tok_q, q0, p.do_sb, p.do_ss),
-                                rows_valid, tid);
-                if (tid < kQTile) {
-                    float l2 = INFINITY, rd = 0.f;
-                    if (tid < rows_valid) {
-                        l2 = p.lse2[wsbase + q0 + tid];
-                        rd = p.rowdot[wsbase + q0 + tid];
-                    }
-                    sm.lse2[tid] = l2;
-                    sm.rowdot[tid] = rd;
+            // ---- S = Q K^T and dP = dO V^T (64 queries x 32 keys per wave) ----
+            f32x16 s[2], dp[2];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    s[mb][r] = 0.f;
+                    dp[mb][r] = 0.f;
                 }
-                __syncthreads();
-
-                // ---- S = Q K^T and dP = dO V^T (64 queries x 32 keys per wave) ----
-                f32x16 s[2], dp[2];
+            }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        s[mb][r] = 0.f;
-                        dp[mb][r] = 0.f;
-                    }
+                    const int o = (32 * mb + l32) * RQ + 16 * ks + 8 * g2;
+                    s[mb] = mfma32(lds16(sq + o), kf[ks], s[mb]);
+                    dp[mb] = mfma32(lds16(sdo + o), vf[ks], dp[mb]);
                 }
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-                    for (int mb = 0; mb < 2; ++mb) {
-                        const int row = (32 * mb + l32) * RQ + 16 * ks + 8 * g2;
-                        s[mb] = mfma32(lds16(&sm.q[row]), kf[ks], s[mb]);
-                        dp[mb] = mfma32(lds16(&sm.dO[row]), vf[ks], dp[mb]);
-                    }
-                }
+            }
 
-                // ---- P, dS (fp32), masked; bf16 copies as MFMA B operands ----
-                const bool need_mask =
-                    (n0 + kKTile > Lk) || (p.causal && (n0 + kKTile - 1 > q0 + off));
-                bf16x8 pb[4], dsb[4];
+            // ---- P, dS (fp32), masked; bf16 copies as MFMA B operands;
+            //      dS^T to LDS (4 consecutive query rows per 8-byte store) ----
+            const bool need_mask =
+                (n0 + kKTile > Lk) || (p.causal && (n0 + kKTile - 1 > q0 + off));
+            bf16x8 pb[4], dsb[4];
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb) {
+            for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int qi = 32 * mb + 8 * (r >> 2) + 4 * g2 + (r & 3);
-                        float pv = __builtin_amdgcn_exp2f(s[mb][r] * p.scale_log2 - sm.lse2[qi]);
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int qi0 = 32 * mb + 8 * r4 + 4 * g2;
+                    const float4 l2v = *reinterpret_cast<const float4 *>(&sm.lse2[buf][qi0]);
+                    const float4 rdv = *reinterpret_cast<const float4 *>(&sm.rowdot[buf][qi0]);
+                    const float l2a[4] = {l2v.x, l2v.y, l2v.z, l2v.w};
+                    const float rda[4] = {rdv.x, rdv.y, rdv.z, rdv.w};
+                    u16x4 dsv4;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int r = 4 * r4 + t;
+                        float pv = __builtin_amdgcn_exp2f(s[mb][r] * p.scale_log2 - l2a[t]);
                         if (need_mask &&
-                            (key >= Lk || (p.causal && key > q0 + qi + off)))
+                            (key >= Lk || (p.causal && key > q0 + qi0 + t + off)))
                             pv = 0.f;
-                        const float dsv = pv * (dp[mb][r] - sm.rowdot[qi]);
+                        const float dsv = pv * (dp[mb][r] - rda[t]);
                         const uint16_t pbits = f2bf(pv), dbits = f2bf(dsv);
                         pb[2 * mb + (r >> 3)][r & 7] = __builtin_bit_cast(__bf16, pbits);
                         dsb[2 * mb + (r >> 3)][r & 7] = __builtin_bit_cast(__bf16, dbits);
-                        sm.ds[qi * RS + key_local] = dbits;
+                        dsv4[t] = dbits;
                     }
-                }
-
-                // ---- dV^T += dO^T P,  dK^T += Q^T dS  (k = 64 queries) ----
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const int row = (32 * db + l32) * RT + 16 * kk + 8 * g2;
-                        dv_acc[db] = mfma32(lds16(&sm.dOt[row]), pb[kk], dv_acc[db]);
-                        dk_acc[db] = mfma32(lds16(&sm.qt[row]), dsb[kk], dk_acc[db]);
-                    }
-                }
-                __syncthreads();   // dS of all four waves in LDS
-
-                // ---- dQ partial = dS K: 2*DB blocks of 32x32 spread over 4 waves ----
-                constexpr int NBLK = 2 * DB;
-                constexpr int PERW = (NBLK + 3) / 4;
-                f32x16 qacc[PERW];
-#pragma unroll
-                for (int u = 0; u < PERW; ++u) {
-                    const int blk = w + 4 * u;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        qacc[u][r] = 0.f;
-                    if (blk < NBLK) {
-                        const int mb = blk & 1, db = blk >> 1;
-#pragma unroll
-                        for (int ks = 0; ks < kKTile / 16; ++ks) {
-                            const bf16x8 a = lds16(&sm.ds[(32 * mb + l32) * RS + 16 * ks + 8 * g2]);
-                            const bf16x8 bb = lds16(&sm.kt[(32 * db + l32) * RS + 16 * ks + 8 * g2]);
-                            qacc[u] = mfma32(a, bb, qacc[u]);
-                        }
-                    }
-                }
-
-                int *turn = nullptr;
-                if (p.deterministic) {
-                    // Rank of this key tile among the tiles adding into query
-                    // tile m, highest key tile first.
-                    int jmax = nt_b - 1;
-                    if (p.causal) {
-                        const int lim = min(q0 + kQTile, Lq) + off;
-                        jmax = min(jmax, (lim + kKTile - 1) / kKTile - 1);
-                    }
-                    const int rank = jmax - j;
-                    turn = p.turns + ((int64_t)b * p.H + h) * p.mtiles + m;
-                    if (tid == 0) {
-                        int spins = 0;
-                        while (__hip_atomic_load(turn, __ATOMIC_ACQUIRE,
-                                                 __HIP_MEMORY_SCOPE_AGENT) != rank) {
-                            __builtin_amdgcn_s_sleep(2);
-                            if (++spins > kSpinLimit) {
-                                __hip_atomic_fetch_or(p.flags, 1, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT);
-                                break;
-                            }
-                        }
-                    }
-                    __syncthreads();
-                }
-#pragma unroll
-                for (int u = 0; u < PERW; ++u) {
-                    const int blk = w + 4 * u;
-                    if (blk < NBLK) {
-                        const int mb = blk & 1, db = blk >> 1;
-                        const int d = 32 * db + l32;
-                        if (d < p.D) {
-                            float *dst = p.dq_acc + (wsbase + q0) * DP + d;
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                const int qi = 32 * mb + 8 * (r >> 2) + 4 * g2 + (r & 3);
-                                if (qi < rows_valid)
-                                    unsafeAtomicAdd(dst + (int64_t)qi * DP, qacc[u][r]);
-                            }
-                        }
-                    }
-                }
-                if (p.deterministic) {
-                    __threadfence();
-                    __syncthreads();
-                    if (tid == 0)
-                        __hip_atomic_fetch_add(turn, 1, __ATOMIC_RELEASE,
-                                               __HIP_MEMORY_SCOPE_AGENT);
+                    *reinterpret_cast<u16x4 *>(&sm.dsT[key_local * RD + qi0]) = dsv4;
                 }
             }
+
+            // ---- dV^T += dO^T P,  dK^T += Q^T dS  (k = 64 queries) ----
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int r0 = 16 * kk + 4 * g2, r1 = r0 + 8;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    dv_acc[db] = mfma32(frag_tr(sdo, RQ, r0, r1, 32 * db, lane), pb[kk], dv_acc[db]);
+                    dk_acc[db] = mfma32(frag_tr(sq, RQ, r0, r1, 32 * db, lane), dsb[kk], dk_acc[db]);
+                }
+            }
+            __syncthreads();   // dS^T of all four waves in LDS
+
+            // ---- dQ partial = dS K: 2*DB blocks of 32x32 spread over 4 waves
+            //      (block -> head-dim block blk % DB, query block blk / DB) ----
+            constexpr int NBLK = 2 * DB;
+            constexpr int PERW = (NBLK + 3) / 4;
+            f32x16 qacc[PERW];
+#pragma unroll
+            for (int u = 0; u < PERW; ++u)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    qacc[u][r] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < kKTile / 16; ++ks) {
+                const int r0 = 16 * ks + 8 * g2, r1 = r0 + 4;
+                if constexpr (DB == 4) {
+                    // every wave owns head-dim block w for both query blocks
+                    const bf16x8 bk = frag_tr(sm.k, RQ, r0, r1, 32 * w, lane);
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        qacc[u] = mfma32(frag_tr(sm.dsT, RD, r0, r1, 32 * u, lane), bk, qacc[u]);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < PERW; ++u) {
+                        const int blk = w + 4 * u;
+                        if (blk < NBLK) {
+                            const int mb = blk / DB, db = blk % DB;
+                            qacc[u] = mfma32(frag_tr(sm.dsT, RD, r0, r1, 32 * mb, lane),
+                                             frag_tr(sm.k, RQ, r0, r1, 32 * db, lane), qacc[u]);
+                        }
+                    }
+                }
+            }
+
+            int *turn = nullptr;
+            if (p.deterministic) {
+                // Rank of this key tile among the tiles adding into query
+                // tile m, highest key tile first.
+                int jmax = nt_b - 1;
+                if (p.causal) {
+                    const int lim = min(q0 + kQTile, Lq) + off;
+                    jmax = min(jmax, (lim + kKTile - 1) / kKTile - 1);
+                }
+                const int rank = jmax - j;
+                turn = p.turns + ((int64_t)b * p.H + h) * p.mtiles + m;
+                if (tid == 0) {
+                    int spins = 0;
+                    while (__hip_atomic_load(turn, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) !=
+                           rank) {
+                        __builtin_amdgcn_s_sleep(2);
+                        if (++spins > kSpinLimit) {
+                            __hip_atomic_fetch_or(p.flags, 1, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+                            break;
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+#pragma unroll
+            for (int u = 0; u < PERW; ++u) {
+                const int blk = (DB == 4) ? w + 4 * u : w + 4 * u;
+                if (blk < NBLK) {
+                    const int mb = (DB == 4) ? u : blk / DB;
+                    const int db = (DB == 4) ? w : blk % DB;
+                    const int d = 32 * db + l32;
+                    if (d < p.D) {
+                        float *dst = p.dq_acc + (wsbase + q0) * DP + d;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int qi = 32 * mb + 8 * (r >> 2) + 4 * g2 + (r & 3);
+                            if (qi < rows_valid)
+                                unsafeAtomicAdd(dst + (int64_t)qi * DP, qacc[u][r]);
+                        }
+                    }
+                }
+            }
+            if (p.deterministic) {
+                __threadfence();
+                __syncthreads();
+                if (tid == 0)
+                    __hip_atomic_fetch_add(turn, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            }
+
+            if (it + 1 < total)
+                stage(buf ^ 1);
+            __syncthreads();   // next tile staged; dS^T and this buffer free
         }
     }
 

@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X attention backward (dQ, dK, dV).
+
+One step = one whole backward (preprocess, main, dq_convert) over the
+headline workload: B=2, H=32, Hk=8, Sq=Sk=4096, D=128, causal, bf16, inputs
+resident in HBM.  Prints ONE JSON line.
+
+FLOP convention: 2.5 x the forward's 4*B*H*Sq*Sk*D, halved for causal.
+The roofline object is for the main kernel (the dominant one), timed with
+HIP events recorded on the stream it is launched on.
+
+Inputs: Q, K, V, dO from the seeded generator (workloads.py); O and LSE from a
+plain fp32 torch forward on the GPU (input preparation only, not timed).
+The CPU baseline leg times the fp64 oracle on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "bwd TFLOP/s (dQ+dK+dV) bf16 and % of MFMA peak, S=4096 D=128 causal GQA"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X published dense bf16 MFMA peak
+PEAK_HBM_GBS = 8000.0         # MI355X published HBM3E bandwidth
+
+
+def conv_flops(B, H, Sq, Sk, D, causal):
+    f = 2.5 * 4.0 * B * H * Sq * Sk * D
+    return f * 0.5 if causal else f
+
+
+def forward_inputs_torch(q, k, v, scale, causal):
+    """O (bf16) and natural-log LSE (fp32, (B,H,Sq)) by a plain fp32 torch
+    forward, one (batch, head) at a time.  Dense bshd inputs on the GPU."""
+    import torch
+    B, Sq, H, D = q.shape
+    Sk, Hk = k.shape[1], k.shape[2]
+    G = H // Hk
+    out = torch.empty_like(q)
+    lse = torch.empty(B, H, Sq, dtype=torch.float32, device=q.device)
+    if causal:
+        i = torch.arange(Sq, device=q.device)[:, None]
+        j = torch.arange(Sk, device=q.device)[None, :]
+        masked = j > i + (Sk - Sq)
+    for b in range(B):
+        for h in range(H):
+            qh = q[b, :, h, :].float().contiguous()
+            kt = k[b, :, h // G, :].float().t().contiguous()
+            vh = v[b, :, h // G, :].float().contiguous()
+            s = torch.matmul(qh, kt) * scale
+            if causal:
+                s.masked_fill_(masked, float("-inf"))
+            l = torch.logsumexp(s, dim=-1)
+            p = torch.exp(s - l[:, None])
+            p = torch.nan_to_num(p, nan=0.0)
+            out[b, :, h, :] = torch.matmul(p, vh).to(torch.bfloat16)
+            lse[b, h] = l
+    return out, lse
+
+
+def cpu_baseline(wl, units):
+    """fp64 oracle backward on a bounded sample: `units` (batch, KV-head
+    group) pairs of the workload, each its own exact sub-problem."""
+    import numpy as np
+    import workloads as W
+    from oracle import oracle as O
+    inp = W.make_inputs(wl)
+    G = wl.heads // wl.heads_k
+    t_total = 0.0
+    flops = 0.0
+    for (b, g) in units:
+        hs = list(range(g * G, (g + 1) * G))
+
+        def f64(t):
+            return t.float().numpy().astype(np.float64)
+        q = f64(inp.q[b][:, hs])
+        k = f64(inp.k[b][:, [g]])
+        v = f64(inp.v[b][:, [g]])
+        do = f64(inp.dout[b][:, hs])
+        t0 = time.perf_counter()
+        O.backward(q, k, v, do, [0, wl.seqlen_q], [0, wl.seqlen_k], wl.scale, wl.causal)
+        t_total += time.perf_counter() - t0
+        flops += conv_flops(1, G, wl.seqlen_q, wl.seqlen_k, wl.head_dim, wl.causal)
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(),
+            "kind": "oracle",
+            "sample": "%d of %d (batch, KV-head group) units of the workload, fp64 "
+                      "contracted-Jacobian backward incl. its forward recompute, %.1f s"
+                      % (len(units), wl.batch * wl.heads_k, t_total)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload id (workloads.py)")
+    ap.add_argument("--deterministic", action="store_true",
+                    help="time the ordered (bit-reproducible) dQ mode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-units", type=int, default=8)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+              "(the backward splits into independent (batch, KV-head) units that need "
+              "no communication; N GPUs would each run 1/N of them)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import attention_backward_fa2_amd as fa
+
+    fa.load_library()
+    wl = W.WORKLOADS[args.config]
+    if wl.varlen:
+        print("bench.py times dense workloads only", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = W.make_inputs(wl)
+    q, k, v, do = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v, inp.dout))
+    o, lse = forward_inputs_torch(q, k, v, wl.scale, wl.causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    a = fa.make_args(do, q, k, v, o, lse, dq, dk, dv, wl.scale, wl.causal,
+                     deterministic=args.deterministic)
+    ws = fa.alloc_workspace(a, dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step(evs=None):
+        if evs is None:
+            fa.run(a, "all", stream)
+            return
+        evs[0].record(stream)
+        fa.run(a, "preprocess", stream)
+        evs[1].record(stream)
+        fa.run(a, "main", stream)
+        evs[2].record(stream)
+        fa.run(a, "dq_convert", stream)
+        evs[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = evs[0][0].elapsed_time(evs[-1][3])
+    pre_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K
+    main_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / K
+    conv_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / K
+    ms_per_step = gpu_ms / K
+
+    B, H, Hk, Sq, Sk, D = wl.batch, wl.heads, wl.heads_k, wl.seqlen_q, wl.seqlen_k, wl.head_dim
+    flops = conv_flops(B, H, Sq, Sk, D, wl.causal)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    main_tflops = flops / (main_ms * 1e-3) / 1e12
+    # HBM-bound helpers: algorithmic bytes per launch.
+    rows = B * Sq
+    pre_bytes = rows * H * (2 * D * 2 + 4) + rows * H * (8 + 4 * D)
+    conv_bytes = rows * H * (4 * D + 2 * D)
+    off_flags = fa.workspace_layout(a).off_flags
+    flags = ws[off_flags:off_flags + 16].cpu().view(torch.int32)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "heads": H, "heads_k": Hk,
+                   "seqlen_q": Sq, "seqlen_k": Sk, "head_dim": D, "causal": wl.causal,
+                   "dq_mode": "ordered" if args.deterministic else "atomic"},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "flops_per_step": flops,
+        "kernel_ms": {"preprocess": round(pre_ms, 4), "main": round(main_ms, 4),
+                      "dq_convert": round(conv_ms, 4)},
+        "hbm_kernels_GBs": {"preprocess": round(pre_bytes / (pre_ms * 1e-3) / 1e9, 1),
+                            "dq_convert": round(conv_bytes / (conv_ms * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "mfma", "achieved": round(main_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "wall_s": round(wall, 3),
+        "ordered_wait_gave_up": bool(int(flags[0]) != 0),
+    }
+    if not args.no_cpu_baseline:
+        all_units = [(b, g) for b in range(B) for g in range(Hk)]
+        pick = [all_units[(i * len(all_units)) // args.cpu_units]
+                for i in range(min(args.cpu_units, len(all_units)))]
+        rec["cpu_baseline"] = cpu_baseline(wl, pick)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
