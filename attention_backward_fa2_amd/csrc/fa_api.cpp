@@ -115,6 +115,9 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
         (st = check_strides("dk", a->dk_stride, varlen)) ||
         (st = check_strides("dv", a->dv_stride, varlen)))
         return st;
+    // The main kernel addresses a 64-row query tile with 32-bit offsets.
+    if (a->q_stride[1] >= (int64_t(1) << 24) || a->do_stride[1] >= (int64_t(1) << 24))
+        return fail(FA_ERR_UNSUPPORTED, "q / dout row stride >= 2^24 elements is not supported");
     if (a->softmax_scale != a->softmax_scale || std::isinf(a->softmax_scale))
         return fail(FA_ERR_INVALID_ARG, "softmax_scale is not finite");
     if ((a->causal != 0 && a->causal != 1) || (a->deterministic != 0 && a->deterministic != 1))

@@ -37,13 +37,18 @@
 // are stored.
 //
 // LDS (D_pad = 128): Q and dO row-major, double buffered (4 x 18 KB), dS^T
-// 20 KB, K 36 KB, row vectors 1 KB: 129 KB, one workgroup per CU.  Row
+// double buffered (2 x 20 KB), K 36 KB, row vectors 1 KB: 149 KB, one
+// workgroup per CU.  Row
 // pitches are D + 16 elements (dS^T: 64 + 16) so that both the 16-byte row
 // reads and the transposing reads hit distinct banks.
 //
 // Pipelining: the next query tile is loaded from global memory into
-// registers while the current one is computed, then written to the other
-// LDS buffer; two workgroup barriers per tile.
+// registers while the current one is computed and written to the other LDS
+// buffer before the dQ atomics of the current tile are issued.  One
+// workgroup barrier per tile: every LDS buffer written in tile t was last
+// read before the barrier of tile t-1.
+#include <climits>
+
 #include "fa_internal.h"
 
 namespace fa {
@@ -51,6 +56,7 @@ namespace fa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
@@ -66,7 +72,7 @@ struct __attribute__((aligned(16))) Smem {
     static constexpr int RD = kQTile + 16;   // pitch of dS^T
     uint16_t q[2][kQTile * RQ];
     uint16_t dO[2][kQTile * RQ];
-    uint16_t dsT[kKTile * RD];
+    uint16_t dsT[2][kKTile * RD];
     uint16_t k[kKTile * RQ];
     float lse2[2][kQTile];
     float rowdot[2][kQTile];
@@ -96,6 +102,63 @@ __device__ inline bf16x8 frag_tr(const uint16_t *base, int pitch, int r0, int r1
     const i16x4 hi = lds_tr(base + (r1 + rr) * pitch + col);
     const i16x4 v8[2] = {lo, hi};
     return __builtin_bit_cast(bf16x8, v8);
+}
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// Asks the scheduler to issue `ahead` LDS reads first and then alternate one
+// MFMA with `per` reads, so each MFMA's operands were requested several
+// MFMAs earlier (one wave per SIMD: the wave itself must hide LDS latency).
+template <int N_MFMA, int PER, int AHEAD>
+__device__ inline void pipeline_reads()
+{
+    constexpr int NR = N_MFMA * PER;
+    static_assert(AHEAD <= NR && AHEAD % PER == 0, "bad pipeline shape");
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, AHEAD, 0);
+#pragma unroll
+    for (int i = 0; i < N_MFMA - AHEAD / PER; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PER, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, AHEAD / PER, 0);
+}
+
+// P = exp2(S*scale*log2e - lse2) and dS = P (dP - rowdot) for one wave's
+// 64 x 32 tile; bf16 copies in MFMA B-operand order, dS^T row to LDS.
+// MASK: query row qi (0..63 in the tile) sees this lane's key iff
+// keyok && qi >= lim.
+template <bool MASK>
+__device__ inline void pointwise(const f32x16 (&s)[2], const f32x16 (&dp)[2], bf16x8 (&pb)[4],
+                                 bf16x8 (&dsb)[4], uint16_t *dsT_row, const float *l2s,
+                                 const float *rds, float scale_log2, int g2, int lim, bool keyok)
+{
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int qi0 = 32 * mb + 8 * r4 + 4 * g2;
+            const float4 l2v = *reinterpret_cast<const float4 *>(l2s + qi0);
+            const float4 rdv = *reinterpret_cast<const float4 *>(rds + qi0);
+            const float l2a[4] = {l2v.x, l2v.y, l2v.z, l2v.w};
+            const float rda[4] = {rdv.x, rdv.y, rdv.z, rdv.w};
+            u16x4 dsv4;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int r = 4 * r4 + t;
+                float pv = __builtin_amdgcn_exp2f(s[mb][r] * scale_log2 - l2a[t]);
+                if constexpr (MASK)
+                    pv = (keyok && qi0 + t >= lim) ? pv : 0.f;
+                const float dsv = pv * (dp[mb][r] - rda[t]);
+                const uint16_t pbits = f2bf(pv), dbits = f2bf(dsv);
+                pb[2 * mb + (r >> 3)][r & 7] = __builtin_bit_cast(__bf16, pbits);
+                dsb[2 * mb + (r >> 3)][r & 7] = __builtin_bit_cast(__bf16, dbits);
+                dsv4[t] = dbits;
+            }
+            *reinterpret_cast<u16x4 *>(dsT_row + qi0) = dsv4;
+        }
+    }
 }
 
 template <int DP>
@@ -169,14 +232,20 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         const int nt_b = (Lk + kKTile - 1) / kKTile;
 
         // Prefetch registers for one query tile: NCH 16-byte chunks of Q
-        // and of dO per thread, plus one lse2 / rowdot pair (threads < 64).
-        uint4 pq[NCH], pd[NCH];
+        // and of dO per thread, plus one lse2 / rowdot value pair.  Chunk c
+        // of this thread is tile row (tid + c*256) / CPR, 16-byte column
+        // (tid + c*256) % CPR.  Loads always use an in-bounds (clamped)
+        // address; the zero fill of rows past the sequence end and of
+        // columns past head_dim is applied when staging, so issuing a
+        // prefetch never has to wait for older memory traffic.
+        u32x4 pq[NCH], pd[NCH];
         float pl2 = INFINITY, prd = 0.f;
+        int rv_next = kQTile;             // valid rows of the prefetched tile
         auto prefetch = [&](int it) {
             const int hh = it / nm, m = m_begin + it % nm;
             const int h = hk * p.G + hh;
             const int q0 = m * kQTile;
-            const int rows_valid = min(kQTile, Lq - q0);
+            rv_next = min(kQTile, Lq - q0);
             const uint16_t *qb =
                 p.q + h * p.q_sh + row_offset(p, b, si.tok_q, q0, p.q_sb, p.q_ss);
             const uint16_t *db =
@@ -184,33 +253,29 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
                 const int idx = tid + c * kThreads;
-                const int r = idx / CPR, cc = idx % CPR;
-                pq[c] = make_uint4(0, 0, 0, 0);
-                pd[c] = make_uint4(0, 0, 0, 0);
-                if (r < rows_valid && cc * 8 < p.D) {
-                    pq[c] = *reinterpret_cast<const uint4 *>(qb + r * p.q_ss + cc * 8);
-                    pd[c] = *reinterpret_cast<const uint4 *>(db + r * p.do_ss + cc * 8);
-                }
+                const int r = min(idx / CPR, rv_next - 1);
+                const int col = (idx % CPR) * 8 < p.D ? (idx % CPR) * 8 : 0;
+                pq[c] = *reinterpret_cast<const u32x4 *>(qb + r * (int)p.q_ss + col);
+                pd[c] = *reinterpret_cast<const u32x4 *>(db + r * (int)p.do_ss + col);
             }
-            pl2 = INFINITY;
-            prd = 0.f;
-            if (tid < rows_valid) {
-                const int64_t wr = (int64_t)h * p.rows + si.ws_row + q0 + tid;
-                pl2 = p.lse2[wr];
-                prd = p.rowdot[wr];
-            }
+            const int lr = min(tid & (kQTile - 1), rv_next - 1);
+            const int64_t wr = (int64_t)h * p.rows + si.ws_row + q0 + lr;
+            pl2 = p.lse2[wr];
+            prd = p.rowdot[wr];
         };
         auto stage = [&](int buf) {
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
                 const int idx = tid + c * kThreads;
-                const int r = idx / CPR, cc = idx % CPR;
-                *reinterpret_cast<uint4 *>(&sm.q[buf][r * RQ + cc * 8]) = pq[c];
-                *reinterpret_cast<uint4 *>(&sm.dO[buf][r * RQ + cc * 8]) = pd[c];
+                const uint32_t keep = (idx / CPR < rv_next && (idx % CPR) * 8 < p.D) ? ~0u : 0u;
+                const int o = (idx / CPR) * RQ + (idx % CPR) * 8;
+                *reinterpret_cast<u32x4 *>(&sm.q[buf][o]) = pq[c] & keep;
+                *reinterpret_cast<u32x4 *>(&sm.dO[buf][o]) = pd[c] & keep;
             }
             if (tid < kQTile) {
-                sm.lse2[buf][tid] = pl2;
-                sm.rowdot[buf][tid] = prd;
+                const bool ok = tid < rv_next;
+                sm.lse2[buf][tid] = ok ? pl2 : INFINITY;
+                sm.rowdot[buf][tid] = ok ? prd : 0.f;
             }
         };
 
@@ -249,37 +314,20 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     dp[mb] = mfma32(lds16(sdo + o), vf[ks], dp[mb]);
                 }
             }
+            pipeline_reads<4 * KS, 1, 8>();
 
-            // ---- P, dS (fp32), masked; bf16 copies as MFMA B operands;
-            //      dS^T to LDS (4 consecutive query rows per 8-byte store) ----
+            // ---- P, dS (fp32), masked only on diagonal / tail tiles ----
             const bool need_mask =
                 (n0 + kKTile > Lk) || (p.causal && (n0 + kKTile - 1 > q0 + off));
             bf16x8 pb[4], dsb[4];
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const int qi0 = 32 * mb + 8 * r4 + 4 * g2;
-                    const float4 l2v = *reinterpret_cast<const float4 *>(&sm.lse2[buf][qi0]);
-                    const float4 rdv = *reinterpret_cast<const float4 *>(&sm.rowdot[buf][qi0]);
-                    const float l2a[4] = {l2v.x, l2v.y, l2v.z, l2v.w};
-                    const float rda[4] = {rdv.x, rdv.y, rdv.z, rdv.w};
-                    u16x4 dsv4;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const int r = 4 * r4 + t;
-                        float pv = __builtin_amdgcn_exp2f(s[mb][r] * p.scale_log2 - l2a[t]);
-                        if (need_mask &&
-                            (key >= Lk || (p.causal && key > q0 + qi0 + t + off)))
-                            pv = 0.f;
-                        const float dsv = pv * (dp[mb][r] - rda[t]);
-                        const uint16_t pbits = f2bf(pv), dbits = f2bf(dsv);
-                        pb[2 * mb + (r >> 3)][r & 7] = __builtin_bit_cast(__bf16, pbits);
-                        dsb[2 * mb + (r >> 3)][r & 7] = __builtin_bit_cast(__bf16, dbits);
-                        dsv4[t] = dbits;
-                    }
-                    *reinterpret_cast<u16x4 *>(&sm.dsT[key_local * RD + qi0]) = dsv4;
-                }
+            if (need_mask) {
+                // causal: key visible to tile row qi iff key <= q0 + qi + off
+                const int lim = p.causal ? key - q0 - off : INT_MIN;
+                pointwise<true>(s, dp, pb, dsb, &sm.dsT[buf][key_local * RD], sm.lse2[buf],
+                                sm.rowdot[buf], p.scale_log2, g2, lim, key < Lk);
+            } else {
+                pointwise<false>(s, dp, pb, dsb, &sm.dsT[buf][key_local * RD], sm.lse2[buf],
+                                 sm.rowdot[buf], p.scale_log2, g2, 0, true);
             }
 
             // ---- dV^T += dO^T P,  dK^T += Q^T dS  (k = 64 queries) ----
@@ -292,10 +340,21 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     dk_acc[db] = mfma32(frag_tr(sq, RQ, r0, r1, 32 * db, lane), dsb[kk], dk_acc[db]);
                 }
             }
-            __syncthreads();   // dS^T of all four waves in LDS
+            pipeline_reads<8 * DB, 2, 8>();
 
-            // ---- dQ partial = dS K: 2*DB blocks of 32x32 spread over 4 waves
-            //      (block -> head-dim block blk % DB, query block blk / DB) ----
+            // Stage the prefetched next tile now, before this tile's dQ
+            // atomics are issued, so waiting for its loads never waits for
+            // the atomics.  Buffer buf^1 was last read before the previous
+            // barrier.
+            if (it + 1 < total)
+                stage(buf ^ 1);
+            __syncthreads();   // dS^T[buf] complete; next tile staged
+
+            // ---- dQ partial = dS K: 2*DB blocks of 32x32 spread over 4 waves.
+            //      DB = 4: wave w owns head-dim block w for both query blocks
+            //      (one K fragment feeds two MFMAs); DB = 2: one block per
+            //      wave; DB = 3: blocks w and w + 4 of (query block, head-dim
+            //      block) = (blk / 3, blk % 3). ----
             constexpr int NBLK = 2 * DB;
             constexpr int PERW = (NBLK + 3) / 4;
             f32x16 qacc[PERW];
@@ -304,23 +363,36 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     qacc[u][r] = 0.f;
+            auto qblk_mb = [&](int u) { return DB == 4 ? u : (DB == 2 ? (w >> 1) : (w + 4 * u) / 3); };
+            auto qblk_db = [&](int u) { return DB == 4 ? w : (DB == 2 ? (w & 1) : (w + 4 * u) % 3); };
+            if constexpr (DB == 4) {
 #pragma unroll
-            for (int ks = 0; ks < kKTile / 16; ++ks) {
-                const int r0 = 16 * ks + 8 * g2, r1 = r0 + 4;
-                if constexpr (DB == 4) {
-                    // every wave owns head-dim block w for both query blocks
+                for (int ks = 0; ks < kKTile / 16; ++ks) {
+                    const int r0 = 16 * ks + 8 * g2, r1 = r0 + 4;
                     const bf16x8 bk = frag_tr(sm.k, RQ, r0, r1, 32 * w, lane);
 #pragma unroll
                     for (int u = 0; u < 2; ++u)
-                        qacc[u] = mfma32(frag_tr(sm.dsT, RD, r0, r1, 32 * u, lane), bk, qacc[u]);
-                } else {
+                        qacc[u] = mfma32(frag_tr(sm.dsT[buf], RD, r0, r1, 32 * u, lane), bk, qacc[u]);
+                }
+                pipeline_reads<16, 3, 12>();
+            } else if constexpr (DB == 2) {
 #pragma unroll
-                    for (int u = 0; u < PERW; ++u) {
-                        const int blk = w + 4 * u;
-                        if (blk < NBLK) {
-                            const int mb = blk / DB, db = blk % DB;
-                            qacc[u] = mfma32(frag_tr(sm.dsT, RD, r0, r1, 32 * mb, lane),
-                                             frag_tr(sm.k, RQ, r0, r1, 32 * db, lane), qacc[u]);
+                for (int ks = 0; ks < kKTile / 16; ++ks) {
+                    const int r0 = 16 * ks + 8 * g2, r1 = r0 + 4;
+                    qacc[0] = mfma32(frag_tr(sm.dsT[buf], RD, r0, r1, 32 * qblk_mb(0), lane),
+                                     frag_tr(sm.k, RQ, r0, r1, 32 * qblk_db(0), lane), qacc[0]);
+                }
+                pipeline_reads<8, 4, 12>();
+            } else {
+#pragma unroll
+                for (int u = 0; u < PERW; ++u) {
+                    if (w + 4 * u < NBLK) {
+#pragma unroll
+                        for (int ks = 0; ks < kKTile / 16; ++ks) {
+                            const int r0 = 16 * ks + 8 * g2, r1 = r0 + 4;
+                            qacc[u] = mfma32(frag_tr(sm.dsT[buf], RD, r0, r1, 32 * qblk_mb(u), lane),
+                                             frag_tr(sm.k, RQ, r0, r1, 32 * qblk_db(u), lane),
+                                             qacc[u]);
                         }
                     }
                 }
@@ -351,20 +423,24 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 }
                 __syncthreads();
             }
+            // fp32 adds of the partial: one 128-byte row segment per
+            // (lane half, accumulator row); unconditional on full tiles.
 #pragma unroll
             for (int u = 0; u < PERW; ++u) {
-                const int blk = (DB == 4) ? w + 4 * u : w + 4 * u;
-                if (blk < NBLK) {
-                    const int mb = (DB == 4) ? u : blk / DB;
-                    const int db = (DB == 4) ? w : blk % DB;
-                    const int d = 32 * db + l32;
+                if (w + 4 * u < NBLK) {
+                    const int d = 32 * qblk_db(u) + l32;
+                    float *dst = p.dq_acc + (wsbase + q0 + 32 * qblk_mb(u) + 4 * g2) * DP + d;
                     if (d < p.D) {
-                        float *dst = p.dq_acc + (wsbase + q0) * DP + d;
+                        if (rows_valid == kQTile) {
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int qi = 32 * mb + 8 * (r >> 2) + 4 * g2 + (r & 3);
-                            if (qi < rows_valid)
-                                unsafeAtomicAdd(dst + (int64_t)qi * DP, qacc[u][r]);
+                            for (int r = 0; r < 16; ++r)
+                                unsafeAtomicAdd(dst + (8 * (r >> 2) + (r & 3)) * DP, qacc[u][r]);
+                        } else {
+                            const int lim_r = rows_valid - 32 * qblk_mb(u) - 4 * g2;
+#pragma unroll
+                            for (int r = 0; r < 16; ++r)
+                                if (8 * (r >> 2) + (r & 3) < lim_r)
+                                    unsafeAtomicAdd(dst + (8 * (r >> 2) + (r & 3)) * DP, qacc[u][r]);
                         }
                     }
                 }
@@ -375,10 +451,6 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 if (tid == 0)
                     __hip_atomic_fetch_add(turn, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
             }
-
-            if (it + 1 < total)
-                stage(buf ^ 1);
-            __syncthreads();   // next tile staged; dS^T and this buffer free
         }
     }
 
