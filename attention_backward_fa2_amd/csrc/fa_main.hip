@@ -175,13 +175,28 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, g2 = lane >> 5;
 
-    // Workgroup -> (batch, KV head, key tile).  Within one (batch, KV head)
-    // the key tiles run in descending order along the linear id, so that in
-    // ordered mode every workgroup waits only on one with a lower id.
+    // Workgroup -> (batch, KV head, key tile).
+    //  - atomic mode: longest work first.  Key tile 0 sees the most query
+    //    tiles under the causal mask, so all workgroups of key tile 0 (every
+    //    batch and KV head) come first, then key tile 1, ...; the
+    //    (batch, KV head) index is the fast one, which keeps one
+    //    (batch, KV head) on one XCD of the round-robin dispatch when
+    //    batch * Hk is a multiple of the XCD count.
+    //  - ordered mode: within one (batch, KV head) the key tiles run in
+    //    descending order along the linear id, so every workgroup waits only
+    //    on one with a lower id (which the in-order dispatch has already
+    //    placed on a CU).
     const int nt = p.ntiles;
+    const int nbg = p.batch * p.Hk;
     const int lin = blockIdx.x;
-    const int j = nt - 1 - (lin % nt);
-    const int bg = lin / nt;
+    int j, bg;
+    if (p.deterministic) {
+        j = nt - 1 - (lin % nt);
+        bg = lin / nt;
+    } else {
+        j = lin / nbg;
+        bg = lin % nbg;
+    }
     const int hk = bg % p.Hk, b = bg / p.Hk;
 
     const SeqInfo si = seq_info(p, b);
