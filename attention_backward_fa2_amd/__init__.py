@@ -44,6 +44,7 @@ class FaBwdArgs(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("causal", ctypes.c_int32),
         ("deterministic", ctypes.c_int32),
+        ("dq_accumulate", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
     ]
@@ -63,7 +64,7 @@ class FaBwdWsLayout(ctypes.Structure):
     ]
 
 
-EXPORTED = ("fa_bwd", "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_dq_convert",
+EXPORTED = ("fa_bwd", "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_dq", "fa_bwd_dq_convert",
             "fa_bwd_validate", "fa_bwd_workspace_size", "fa_bwd_workspace_layout",
             "fa_bwd_last_error", "fa_bwd_abi_version")
 
@@ -80,7 +81,7 @@ def load_library(path: str = LIB_PATH):
             "libfa_bwd.so is not built (run python -c 'import __graft_entry__ as g; g.build()')")
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER(FaBwdArgs)
-    for name in ("fa_bwd", "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_dq_convert"):
+    for name in ("fa_bwd", "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_dq", "fa_bwd_dq_convert"):
         f = getattr(lib, name)
         f.argtypes = [P, ctypes.c_void_p]
         f.restype = ctypes.c_int
@@ -131,9 +132,13 @@ class Problem:
 
 def make_args(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
               cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
-              max_seqlen_k=None, deterministic=False, workspace=None) -> FaBwdArgs:
+              max_seqlen_k=None, deterministic=False, workspace=None,
+              dq_accumulate=False) -> FaBwdArgs:
     """Fill fa_bwd_args from tensors.  Dense tensors are (B, S, H, D); packed
-    ones (total, H, D) with int32 device cu_seqlens and host max lengths."""
+    ones (total, H, D) with int32 device cu_seqlens and host max lengths.
+    dq_accumulate=False: dQ by the separate query-tile pass (default);
+    True: dQ partials accumulated in fp32 by the key-tile pass (atomic, or
+    ordered when deterministic) and converted afterwards."""
     varlen = cu_seqlens_q is not None or cu_seqlens_k is not None
     a = FaBwdArgs()
     a.dtype = FA_DTYPE_BF16 if q.dtype == torch.bfloat16 else 99
@@ -163,6 +168,7 @@ def make_args(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
     a.softmax_scale = float(softmax_scale)
     a.causal = int(bool(causal))
     a.deterministic = int(bool(deterministic))
+    a.dq_accumulate = int(bool(dq_accumulate))
     if workspace is not None:
         a.workspace = workspace.data_ptr()
         a.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -208,16 +214,16 @@ def _stream(stream) -> int:
 
 
 def run(args: FaBwdArgs, step: str = "all", stream=None):
-    """Enqueue one of 'all', 'preprocess', 'main', 'dq_convert'."""
+    """Enqueue one of 'all', 'preprocess', 'main', 'dq', 'dq_convert'."""
     lib = load_library()
     f = {"all": lib.fa_bwd, "preprocess": lib.fa_bwd_preprocess, "main": lib.fa_bwd_main,
-         "dq_convert": lib.fa_bwd_dq_convert}[step]
+         "dq": lib.fa_bwd_dq, "dq_convert": lib.fa_bwd_dq_convert}[step]
     _check(f(ctypes.byref(args), _stream(stream)))
 
 
 def fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
            cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
-           deterministic=False, workspace=None, stream=None):
+           deterministic=False, workspace=None, stream=None, dq_accumulate=False):
     """dQ, dK, dV of attention, written into dq, dk, dv (same layouts as q, k, v).
 
     lse is the forward's natural-log log-sum-exp, (B, H, Sq) fp32 (packed:
@@ -225,7 +231,7 @@ def fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
     holds the fp32 dQ accumulator and the row sums afterwards)."""
     args = make_args(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
                      cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                     deterministic, workspace)
+                     deterministic, workspace, dq_accumulate)
     if workspace is None:
         workspace = alloc_workspace(args, q.device)
     run(args, "all", stream)

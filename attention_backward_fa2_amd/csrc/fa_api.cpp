@@ -120,8 +120,9 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
         return fail(FA_ERR_UNSUPPORTED, "q / dout row stride >= 2^24 elements is not supported");
     if (a->softmax_scale != a->softmax_scale || std::isinf(a->softmax_scale))
         return fail(FA_ERR_INVALID_ARG, "softmax_scale is not finite");
-    if ((a->causal != 0 && a->causal != 1) || (a->deterministic != 0 && a->deterministic != 1))
-        return fail(FA_ERR_INVALID_ARG, "causal and deterministic must be 0 or 1");
+    if ((a->causal != 0 && a->causal != 1) || (a->deterministic != 0 && a->deterministic != 1) ||
+        (a->dq_accumulate != 0 && a->dq_accumulate != 1))
+        return fail(FA_ERR_INVALID_ARG, "causal, deterministic and dq_accumulate must be 0 or 1");
 
     fa::Params &p = pl->p;
     std::memset(&p, 0, sizeof p);
@@ -163,6 +164,7 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
     p.scale_log2 = (float)((double)a->softmax_scale * 1.4426950408889634);
     p.causal = a->causal;
     p.deterministic = a->deterministic;
+    p.fused_dq = a->dq_accumulate;
 
     // Workspace layout.
     fa_bwd_ws_layout &ws = pl->ws;
@@ -177,10 +179,14 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
     off = align256(off + hr * sizeof(float));
     ws.off_rowdot = off;
     off = align256(off + hr * sizeof(float));
+    // The fp32 dQ accumulator and the turn counters exist in accumulate
+    // mode only (zero bytes otherwise).
     ws.off_dq_acc = off;
-    off = align256(off + hr * (size_t)dpad * sizeof(float));
+    if (p.fused_dq)
+        off = align256(off + hr * (size_t)dpad * sizeof(float));
     ws.off_turns = off;
-    off = align256(off + (size_t)p.batch * p.H * p.mtiles * sizeof(int32_t));
+    if (p.fused_dq)
+        off = align256(off + (size_t)p.batch * p.H * p.mtiles * sizeof(int32_t));
     ws.off_flags = off;
     off = align256(off + 4 * sizeof(int32_t));
     ws.total_bytes = off;
@@ -197,8 +203,8 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
         char *base = (char *)a->workspace;
         p.lse2 = (float *)(base + ws.off_lse2);
         p.rowdot = (float *)(base + ws.off_rowdot);
-        p.dq_acc = (float *)(base + ws.off_dq_acc);
-        p.turns = (int *)(base + ws.off_turns);
+        p.dq_acc = p.fused_dq ? (float *)(base + ws.off_dq_acc) : nullptr;
+        p.turns = p.fused_dq ? (int *)(base + ws.off_turns) : nullptr;
         p.flags = (int *)(base + ws.off_flags);
     }
     g_last_error.clear();
@@ -212,7 +218,7 @@ fa_status hip_status(hipError_t e, const char *what)
     return FA_OK;
 }
 
-enum Step { kPre = 1, kMain = 2, kConv = 4 };
+enum Step { kPre = 1, kMain = 2, kConv = 4, kDq = 8 };
 
 fa_status run(const fa_bwd_args *a, void *stream, int steps)
 {
@@ -230,8 +236,15 @@ fa_status run(const fa_bwd_args *a, void *stream, int steps)
     if ((steps & kMain) && has_keys)
         if ((st = hip_status(fa::launch_main(p, pl.dpad, s), "main launch")))
             return st;
+    if ((steps & kConv) && !p.fused_dq)
+        return fail(FA_ERR_INVALID_ARG, "dq_convert needs dq_accumulate = 1");
+    if ((steps & kDq) && p.fused_dq)
+        return fail(FA_ERR_INVALID_ARG, "the separate dQ pass needs dq_accumulate = 0");
     if ((steps & kConv) && has_rows)
         if ((st = hip_status(fa::launch_convert(p, pl.dpad, s), "dq_convert launch")))
+            return st;
+    if ((steps & kDq) && has_rows)
+        if ((st = hip_status(fa::launch_dq(p, pl.dpad, s), "dq launch")))
             return st;
     return FA_OK;
 }
@@ -266,10 +279,16 @@ fa_status fa_bwd_validate(const fa_bwd_args *a)
     return make_plan(a, &pl, true);
 }
 
-fa_status fa_bwd(const fa_bwd_args *a, void *stream) { return run(a, stream, kPre | kMain | kConv); }
+fa_status fa_bwd(const fa_bwd_args *a, void *stream)
+{
+    if (!a)
+        return fail(FA_ERR_INVALID_ARG, "args is NULL");
+    return run(a, stream, kPre | kMain | (a->dq_accumulate ? kConv : kDq));
+}
 fa_status fa_bwd_preprocess(const fa_bwd_args *a, void *stream) { return run(a, stream, kPre); }
 fa_status fa_bwd_main(const fa_bwd_args *a, void *stream) { return run(a, stream, kMain); }
 fa_status fa_bwd_dq_convert(const fa_bwd_args *a, void *stream) { return run(a, stream, kConv); }
+fa_status fa_bwd_dq(const fa_bwd_args *a, void *stream) { return run(a, stream, kDq); }
 
 const char *fa_bwd_last_error(void) { return g_last_error.c_str(); }
 

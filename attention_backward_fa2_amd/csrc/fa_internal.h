@@ -51,6 +51,7 @@ struct Params {
     float scale;        // softmax scale
     float scale_log2;   // softmax scale * log2(e)
     int causal, deterministic, varlen;
+    int fused_dq;       // 1: dQ partials added into dq_acc by the key-tile kernel
 };
 
 // Lengths and first rows of sequence b.
@@ -105,5 +106,6 @@ __device__ inline float bf2f(uint16_t x)
 hipError_t launch_preprocess(const Params &p, int dpad, hipStream_t st);
 hipError_t launch_main(const Params &p, int dpad, hipStream_t st);
 hipError_t launch_convert(const Params &p, int dpad, hipStream_t st);
+hipError_t launch_dq(const Params &p, int dpad, hipStream_t st);
 
 }  // namespace fa

@@ -1,0 +1,96 @@
+// fa_mfma.h -- gfx950 MFMA and LDS operand helpers shared by the two
+// tile kernels of the attention backward.
+//
+// MFMA: v_mfma_f32_32x32x16_bf16.  Per lane l (l32 = l % 32, g2 = l / 32):
+//   A (32 x 16, M x K): row l32, k = 8*g2 + t (t = 0..7, one 16-byte vector)
+//   B (16 x 32, K x N): col l32, k = 8*g2 + t
+//   C (32 x 32):        col l32, row 8*(r/4) + 4*g2 + r%4 for r = 0..15
+// A and B have the same lane layout, so an accumulator that holds one
+// column and 16 rows per lane is directly an A or B operand of a product
+// that contracts over those rows, provided the other operand lists the
+// contraction index in the same (permuted) order:
+//   k-slot 8*g2 + t  <->  row 4*g2 + t (t < 4) or 8 + 4*g2 + t - 4
+// within each group of 16 rows (rows 16h .. 16h + 15 are accumulator
+// elements 8h .. 8h + 7 of the lane).
+//
+// Operands whose contraction index runs down the rows of a row-major LDS
+// tile are read with ds_read_b64_tr_b16: within each 16-lane group the 16
+// 8-byte reads form a 4 x 16 block (lanes 4r .. 4r+3 read row r) and lane c
+// receives column c.  Two such reads give one 8-element operand; the row
+// base of each read implements the permutation above.  It moves half as
+// many bytes per clock as ds_read_b128, which is used wherever the operand
+// is contiguous in LDS.
+#pragma once
+
+#include "fa_internal.h"
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+__device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline void zero(f32x16 &c)
+{
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        c[r] = 0.f;
+}
+
+__device__ inline bf16x8 lds16(const uint16_t *p)
+{
+    return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+__device__ inline i16x4 lds_tr(const uint16_t *p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)((lds_u16 *)p));
+}
+
+// MFMA operand from a row-major LDS matrix whose rows run along the
+// contraction index: the lane receives column c0 + l32 at rows r0 .. r0+3
+// (elements 0..3) and r1 .. r1+3 (elements 4..7).  r0 and r1 may depend on
+// g2 only.
+__device__ inline bf16x8 frag_tr(const uint16_t *base, int pitch, int r0, int r1, int c0,
+                                 int lane)
+{
+    const int c16 = lane & 15;
+    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (c16 & 3);
+    const int rr = c16 >> 2;
+    const i16x4 lo = lds_tr(base + (r0 + rr) * pitch + col);
+    const i16x4 hi = lds_tr(base + (r1 + rr) * pitch + col);
+    const i16x4 v8[2] = {lo, hi};
+    return __builtin_bit_cast(bf16x8, v8);
+}
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// Asks the scheduler to issue AHEAD LDS reads first and then alternate one
+// MFMA with PER reads, so each MFMA's operands were requested several MFMAs
+// earlier (one wave per SIMD: the wave itself must hide LDS latency).
+template <int N_MFMA, int PER, int AHEAD>
+__device__ inline void pipeline_reads()
+{
+    constexpr int NR = N_MFMA * PER;
+    static_assert(AHEAD <= NR && AHEAD % PER == 0, "bad pipeline shape");
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, AHEAD, 0);
+#pragma unroll
+    for (int i = 0; i < N_MFMA - AHEAD / PER; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PER, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, AHEAD / PER, 0);
+}
+
+}  // namespace fa

@@ -12,11 +12,12 @@
 //                    exactly 0 there instead of NaN.  The base-2 form is the
 //                    exp2 with folded log2(e) of the sm90 backward page
 //                    (mma_one_m_block pointwise step 1).
-//   dq_acc[h][row][:] = 0, and (ordered mode) the turn counter of the row's
-//                    query tile = 0.
+//   accumulate mode only: dq_acc[h][row][:] = 0, and (ordered adds) the
+//                    turn counter of the row's query tile = 0.
 //
 // HBM-bound: reads O and dO once (2 * 2 * D bytes per row and head), writes
-// 8 + 4 * D_pad bytes.  16 lanes per row; each lane owns 16-byte chunks.
+// 8 bytes (+ 4 * D_pad in accumulate mode).  16 lanes per row; each lane owns
+// 16-byte chunks.
 #include "fa_internal.h"
 
 namespace fa {
@@ -63,9 +64,11 @@ __global__ void __launch_bounds__(kThreads) fa_bwd_preprocess_kernel(Params p)
         const float lse = p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + i];
         p.rowdot[wr] = acc;
         p.lse2[wr] = (lse == -INFINITY) ? INFINITY : lse * 1.4426950408889634f;
-        if (p.deterministic && (i % kQTile) == 0)
+        if (p.fused_dq && p.deterministic && (i % kQTile) == 0)
             p.turns[((int64_t)b * p.H + h) * p.mtiles + i / kQTile] = 0;
     }
+    if (!p.fused_dq)
+        return;
     // Clear this row of the fp32 dQ accumulator: DP / 16 floats per lane.
     constexpr int PER = DP / 16;
     float *dst = p.dq_acc + wr * DP + c * PER;

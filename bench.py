@@ -97,8 +97,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload id (workloads.py)")
+    ap.add_argument("--dq-accumulate", action="store_true",
+                    help="form dQ by fp32 partial adds in the key-tile pass (+ convert) "
+                         "instead of the separate query-tile pass")
     ap.add_argument("--deterministic", action="store_true",
-                    help="time the ordered (bit-reproducible) dQ mode")
+                    help="with --dq-accumulate: ordered (bit-reproducible) partial adds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=8)
     args = ap.parse_args()
@@ -125,7 +128,8 @@ def main():
     o, lse = forward_inputs_torch(q, k, v, wl.scale, wl.causal)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     a = fa.make_args(do, q, k, v, o, lse, dq, dk, dv, wl.scale, wl.causal,
-                     deterministic=args.deterministic)
+                     deterministic=args.deterministic, dq_accumulate=args.dq_accumulate)
+    last_step = "dq_convert" if args.dq_accumulate else "dq"
     ws = fa.alloc_workspace(a, dev)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
@@ -139,7 +143,7 @@ def main():
         evs[1].record(stream)
         fa.run(a, "main", stream)
         evs[2].record(stream)
-        fa.run(a, "dq_convert", stream)
+        fa.run(a, last_step, stream)
         evs[3].record(stream)
 
     for _ in range(args.warmup):
@@ -157,17 +161,23 @@ def main():
     gpu_ms = evs[0][0].elapsed_time(evs[-1][3])
     pre_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K
     main_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / K
-    conv_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / K
+    last_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / K
     ms_per_step = gpu_ms / K
 
     B, H, Hk, Sq, Sk, D = wl.batch, wl.heads, wl.heads_k, wl.seqlen_q, wl.seqlen_k, wl.head_dim
     flops = conv_flops(B, H, Sq, Sk, D, wl.causal)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    main_tflops = flops / (main_ms * 1e-3) / 1e12
-    # HBM-bound helpers: algorithmic bytes per launch.
+    # Algorithmic work per launch.  MFMA-bound kernels: the key-tile pass
+    # does 4 of the 5 products (S, dP, dV, dK; + dQ in accumulate mode), the
+    # separate dQ pass 3 (S, dP, dQ); FLOPs counted over the causal half like
+    # the headline convention.  HBM-bound kernels: compulsory bytes.
     rows = B * Sq
-    pre_bytes = rows * H * (2 * D * 2 + 4) + rows * H * (8 + 4 * D)
+    gemm = flops / 5.0                   # one of the five products
+    main_flops = 5 * gemm if args.dq_accumulate else 4 * gemm
+    dq_flops = 0.0 if args.dq_accumulate else 3 * gemm
+    pre_bytes = rows * H * (2 * D * 2 + 4 + 8) + (rows * H * 4 * D if args.dq_accumulate else 0)
     conv_bytes = rows * H * (4 * D + 2 * D)
+    main_tflops = main_flops / (main_ms * 1e-3) / 1e12
     off_flags = fa.workspace_layout(a).off_flags
     flags = ws[off_flags:off_flags + 16].cpu().view(torch.int32)
 
@@ -186,13 +196,17 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "heads": H, "heads_k": Hk,
                    "seqlen_q": Sq, "seqlen_k": Sk, "head_dim": D, "causal": wl.causal,
-                   "dq_mode": "ordered" if args.deterministic else "atomic"},
+                   "dq_mode": ("ordered" if args.deterministic else "atomic")
+                   if args.dq_accumulate else "separate"},
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "flops_per_step": flops,
         "kernel_ms": {"preprocess": round(pre_ms, 4), "main": round(main_ms, 4),
-                      "dq_convert": round(conv_ms, 4)},
-        "hbm_kernels_GBs": {"preprocess": round(pre_bytes / (pre_ms * 1e-3) / 1e9, 1),
-                            "dq_convert": round(conv_bytes / (conv_ms * 1e-3) / 1e9, 1)},
+                      last_step: round(last_ms, 4)},
+        "kernel_tflops": {"main": round(main_tflops, 1)} if args.dq_accumulate else
+        {"main": round(main_tflops, 1), "dq": round(dq_flops / (last_ms * 1e-3) / 1e12, 1)},
+        "hbm_kernels_GBs": {"preprocess": round(pre_bytes / (pre_ms * 1e-3) / 1e9, 1)} |
+        ({"dq_convert": round(conv_bytes / (last_ms * 1e-3) / 1e9, 1)} if args.dq_accumulate
+         else {}),
         "roofline": {"bound": "mfma", "achieved": round(main_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},

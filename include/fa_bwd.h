@@ -12,16 +12,25 @@
  * Work is enqueued on the caller's HIP stream as three kernels:
  *   1. preprocess : rowsum(dO * O) per query row and head (the softmax_d /
  *                   dsoftmax_sum buffer of the backward call-trace page,
- *                   set_params_dgrad), LSE converted to base 2, and the fp32
- *                   dQ accumulator cleared;
+ *                   set_params_dgrad) and the LSE converted to base 2;
  *   2. main       : one workgroup per 128-key tile of one KV head; it keeps
  *                   the K/V tile and its dK/dV accumulators on chip, loops
  *                   over every query head of the KV head's group (the GQA
  *                   reduction of the GQA/MQA page's backward section happens
- *                   in registers) and over the visible 64-row query tiles,
- *                   and adds each dQ partial into the fp32 accumulator;
- *   3. dq_convert : dQ = bf16(scale * accumulator) (the dq_accum reduction
- *                   step named on the backward call-trace page).
+ *                   in registers) and over the visible 64-row query tiles;
+ *   3. dQ, in one of two ways (fa_bwd_args.dq_accumulate):
+ *      0 (default) dq  : one workgroup per 128 query rows of one head loops
+ *                        over the visible key tiles and forms dQ = scale *
+ *                        dS K directly (dS recomputed; no atomics; the way
+ *                        the Triton FA2 teaching page's dQ kernel works);
+ *      1 accumulate    : the main kernel adds each tile's dQ partial into an
+ *                        fp32 accumulator (hardware atomics, or a fixed
+ *                        order when deterministic = 1), which the preprocess
+ *                        clears, and dq_convert forms dQ = bf16(scale * acc)
+ *                        (the dq_accum buffer and its reduction step on the
+ *                        backward call-trace page).
+ *   On MI355X the fp32 atomic rate of the L2 bounds mode 1 at large sizes;
+ *   mode 0 does three extra products per tile pair instead and is faster.
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers; all strides are in ELEMENTS.
@@ -47,7 +56,7 @@
 extern "C" {
 #endif
 
-#define FA_BWD_ABI_VERSION 1
+#define FA_BWD_ABI_VERSION 2
 
 typedef enum {
     FA_OK = 0,
@@ -105,11 +114,13 @@ typedef enum {
  *     run at a padded tile width of 64, 96 or 128 with zero-filled loads and
  *     masked stores (sm90 backward page, __init__: head dim rounded up to
  *     the tile multiple; backward call-trace page, dout padding step).
- *   - deterministic = 1: dQ partial sums are added in a fixed order (per
- *     query tile, in descending key-tile order), so repeated calls with the
- *     same inputs and workspace size give bit-identical dq, dk, dv.
- *     deterministic = 0: dQ partials use unordered fp32 atomics; dk and dv
- *     are bit-reproducible in both modes.
+ *   - Reproducibility: with dq_accumulate = 0 every output is a fixed-order
+ *     sum, so repeated calls give bit-identical dq, dk, dv whatever
+ *     `deterministic` says.  With dq_accumulate = 1, deterministic = 1 adds
+ *     the dQ partials in a fixed order (per query tile, in descending
+ *     key-tile order) and is bit-reproducible too; deterministic = 0 uses
+ *     unordered fp32 atomics, so dq may differ in the last bits between
+ *     calls (dk and dv never do).
  *   - Empty inputs: batch == 0 enqueues nothing.  A sequence with no query
  *     rows gets dk = dv = 0 for its keys; one with no keys gets dq = 0.
  *     Pointers of tensors with no elements may be NULL.
@@ -133,7 +144,8 @@ typedef struct fa_bwd_args {
 
     float softmax_scale;           /* the caller passes it (usually 1/sqrt(head_dim)) */
     int32_t causal;                /* 0 or 1 */
-    int32_t deterministic;         /* 0 or 1 */
+    int32_t deterministic;         /* 0 or 1 (see Reproducibility) */
+    int32_t dq_accumulate;         /* 0: separate dQ pass (default); 1: fp32 accumulator */
 
     void *workspace;               /* device, 256-byte aligned, caller-owned */
     size_t workspace_bytes;
@@ -146,7 +158,9 @@ typedef struct fa_bwd_args {
  *   lse2   : float[num_heads][rows]   LSE * log2(e), +inf for rows with no key
  *   rowdot : float[num_heads][rows]   sum_d dO * O (fp32 accumulation)
  *   dq_acc : float[num_heads][rows][head_dim_pad]  unscaled fp32 dQ sums
+ *            (dq_accumulate = 1 only; zero bytes otherwise)
  *   turns  : int32[batch][num_heads][ceil(seqlen_q / 64)] ordering counters
+ *            (dq_accumulate = 1 only)
  *   flags  : int32[4]  flags[0] != 0 if an ordered wait gave up (should
  *                      never happen; dq is then not bit-reproducible)
  */
@@ -170,15 +184,19 @@ fa_status fa_bwd_workspace_layout(const fa_bwd_args *a, fa_bwd_ws_layout *out);
  * workspace size).  Host only: no GPU access, nothing enqueued. */
 fa_status fa_bwd_validate(const fa_bwd_args *a);
 
-/* The whole backward: preprocess, main and dq_convert, enqueued on `stream`. */
+/* The whole backward, enqueued on `stream`: preprocess, main, then dq
+ * (dq_accumulate = 0) or dq_convert (dq_accumulate = 1). */
 fa_status fa_bwd(const fa_bwd_args *a, void *stream);
 
-/* The three steps one at a time, in this order, on one stream (each
- * validates like fa_bwd).  Used to time and test the kernels separately;
- * fa_bwd_main needs a completed fa_bwd_preprocess on the same workspace and
- * fa_bwd_dq_convert a completed fa_bwd_main. */
+/* The steps one at a time, on one stream, in the order above (each
+ * validates like fa_bwd).  Used to time and test the kernels separately.
+ * fa_bwd_main and fa_bwd_dq need a completed fa_bwd_preprocess on the same
+ * workspace (fa_bwd_dq does not need fa_bwd_main); fa_bwd_dq_convert needs a
+ * completed fa_bwd_main.  fa_bwd_dq requires dq_accumulate = 0 and
+ * fa_bwd_dq_convert dq_accumulate = 1 (FA_ERR_INVALID_ARG otherwise). */
 fa_status fa_bwd_preprocess(const fa_bwd_args *a, void *stream);
 fa_status fa_bwd_main(const fa_bwd_args *a, void *stream);
+fa_status fa_bwd_dq(const fa_bwd_args *a, void *stream);
 fa_status fa_bwd_dq_convert(const fa_bwd_args *a, void *stream);
 
 /* Reason of the last non-FA_OK status on this thread ("" if none). */

@@ -52,7 +52,7 @@ class Prepared:
         return self.inp.wl.varlen
 
 
-def run_gpu(pr: Prepared, deterministic=False, out_pad=0, step_split=False):
+def run_gpu(pr: Prepared, deterministic=False, out_pad=0, step_split=False, dq_accumulate=False):
     """Backward on cuda:0.  Outputs start as NaN so unwritten elements show.
     out_pad > 0 gives dq/dk/dv a row pitch of head_dim + out_pad (strided
     views) to check that columns past head_dim are left alone."""
@@ -75,11 +75,11 @@ def run_gpu(pr: Prepared, deterministic=False, out_pad=0, step_split=False):
                   cu_seqlens_k=torch.tensor(pr.cu_k, dtype=torch.int32, device=dev),
                   max_seqlen_q=max(inp.lens_q), max_seqlen_k=max(inp.lens_k))
     args = fa.make_args(do, q, k, v, o, lse, dq, dk, dv, wl.scale, wl.causal,
-                        deterministic=deterministic, **kw)
+                        deterministic=deterministic, dq_accumulate=dq_accumulate, **kw)
     ws = fa.alloc_workspace(args, dev)
     ws.fill_(0xA5)   # garbage: the preprocess must clear what it uses
     if step_split:
-        for step in ("preprocess", "main", "dq_convert"):
+        for step in ("preprocess", "main", "dq_convert" if dq_accumulate else "dq"):
             fa.run(args, step)
     else:
         fa.run(args, "all")

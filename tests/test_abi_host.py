@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(fa.EXPORTED)
-    assert lib.fa_bwd_abi_version() == 1
+    assert lib.fa_bwd_abi_version() == 2
 
 
 def test_struct_mirror_matches_header_field_order():
@@ -75,7 +75,7 @@ def _with_ws(a):
 
 
 def test_workspace_layout_formula():
-    a = _args()
+    a = _args(dq_accumulate=1)
     lay = fa.workspace_layout(a)
     rows = 2 * 256
     assert lay.rows == rows and lay.head_dim_pad == 128
@@ -100,6 +100,28 @@ def test_head_dim_padding(d, pad):
               k_stride=(384 * 2 * d, 2 * d, d), v_stride=(384 * 2 * d, 2 * d, d),
               dk_stride=(384 * 2 * d, 2 * d, d), dv_stride=(384 * 2 * d, 2 * d, d))
     assert fa.workspace_layout(a).head_dim_pad == pad
+
+
+def test_separate_dq_mode_needs_no_accumulator():
+    a = _args()
+    lay = fa.workspace_layout(a)
+    rows = 2 * 256
+
+    def al(x):
+        return (x + 255) // 256 * 256
+    assert lay.off_dq_acc == lay.off_turns == lay.off_flags == 2 * al(8 * rows * 4)
+    assert lay.total_bytes == lay.off_flags + 256
+
+
+def test_step_entry_points_check_the_dq_mode_before_launching():
+    lib = fa.load_library()
+    a = _with_ws(_args())
+    assert lib.fa_bwd_dq_convert(ctypes.byref(a), None) == fa.FA_ERR_INVALID_ARG
+    b = _with_ws(_args(dq_accumulate=1))
+    assert lib.fa_bwd_dq(ctypes.byref(b), None) == fa.FA_ERR_INVALID_ARG
+    c = _args(dq_accumulate=2)
+    c.workspace, c.workspace_bytes = BASE + (40 << 30), 1 << 40
+    assert lib.fa_bwd(ctypes.byref(c), None) == fa.FA_ERR_INVALID_ARG
 
 
 def test_valid_args_pass_validation():
@@ -145,14 +167,14 @@ def test_workspace_errors():
 def test_launch_entry_points_reject_before_touching_the_gpu():
     lib = fa.load_library()
     a = _args(num_heads_k=3)
-    for name in ("fa_bwd", "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_dq_convert"):
+    for name in ("fa_bwd", "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_dq", "fa_bwd_dq_convert"):
         assert getattr(lib, name)(ctypes.byref(a), None) == fa.FA_ERR_INVALID_ARG
     assert lib.fa_bwd(None, None) == fa.FA_ERR_INVALID_ARG
 
 
 def test_varlen_layout_uses_total_rows():
     a = _args(cu_seqlens_q=BASE, cu_seqlens_k=BASE + 256, total_q=1000, total_k=1200,
-              batch=5, seqlen_q=300, seqlen_k=400)
+              batch=5, seqlen_q=300, seqlen_k=400, dq_accumulate=1)
     lay = fa.workspace_layout(a)
     assert lay.rows == 1000
     assert lay.off_flags - lay.off_turns == ((5 * 8 * 5 * 4 + 255) // 256) * 256

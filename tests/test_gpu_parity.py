@@ -51,12 +51,17 @@ def prepared():
     return get
 
 
+# dQ strategies: (dq_accumulate, deterministic)
+MODES = {"separate": (False, False), "atomic": (True, False), "ordered": (True, True)}
+
+
 @pytest.mark.parametrize("name", list(SMALL))
-@pytest.mark.parametrize("deterministic", [False, True])
-def test_small_full_parity(gpu_lib, prepared, name, deterministic):
-    _flush("case %s deterministic=%s" % (name, deterministic))
+@pytest.mark.parametrize("mode", list(MODES))
+def test_small_full_parity(gpu_lib, prepared, name, mode):
+    _flush("case %s mode=%s" % (name, mode))
     pr = prepared(name)
-    res = PT.run_gpu(pr, deterministic=deterministic)
+    acc, det = MODES[mode]
+    res = PT.run_gpu(pr, deterministic=det, dq_accumulate=acc)
     ref = PT.oracle_backward(pr)
     for key in ("dq", "dk", "dv"):
         PT.compare(pr.inp.packed(res[key]), ref[key], "%s %s" % (name, key))
@@ -66,10 +71,12 @@ def test_small_full_parity(gpu_lib, prepared, name, deterministic):
 
 @pytest.mark.parametrize("name", ["dense_causal_ragged_gqa2_d64", "varlen_d96_causal",
                                   "causal_sq_gt_sk_empty_rows_d128"])
-def test_ordered_mode_is_bit_reproducible(gpu_lib, prepared, name):
-    _flush("case %s ordered x3" % name)
+@pytest.mark.parametrize("mode", ["separate", "ordered"])
+def test_reproducible_modes_are_bit_identical(gpu_lib, prepared, name, mode):
+    _flush("case %s %s x3" % (name, mode))
     pr = prepared(name)
-    runs = [PT.run_gpu(pr, deterministic=True) for _ in range(3)]
+    acc, det = MODES[mode]
+    runs = [PT.run_gpu(pr, deterministic=det, dq_accumulate=acc) for _ in range(3)]
     for key in ("dq", "dk", "dv"):
         for r in runs[1:]:
             assert torch.equal(r[key].view(torch.int16), runs[0][key].view(torch.int16)), key
@@ -77,17 +84,18 @@ def test_ordered_mode_is_bit_reproducible(gpu_lib, prepared, name):
 
 def test_dk_dv_reproducible_in_atomic_mode(gpu_lib, prepared):
     pr = prepared("noncausal_gqa4_d128")
-    a = PT.run_gpu(pr)
-    b = PT.run_gpu(pr)
+    a = PT.run_gpu(pr, dq_accumulate=True)
+    b = PT.run_gpu(pr, dq_accumulate=True)
     for key in ("dk", "dv"):
         assert torch.equal(a[key].view(torch.int16), b[key].view(torch.int16)), key
 
 
 @pytest.mark.parametrize("name", ["headdim72_padded_noncausal",
                                   "varlen_unequal_and_empty_causal_d64"])
-def test_columns_past_head_dim_untouched(gpu_lib, prepared, name):
+@pytest.mark.parametrize("mode", ["separate", "atomic"])
+def test_columns_past_head_dim_untouched(gpu_lib, prepared, name, mode):
     pr = prepared(name)
-    res = PT.run_gpu(pr, out_pad=8)
+    res = PT.run_gpu(pr, out_pad=8, dq_accumulate=MODES[mode][0])
     D = pr.inp.wl.head_dim
     for key in ("dq_buf", "dk_buf", "dv_buf"):
         assert torch.isnan(res[key][..., D:].float()).all(), key
@@ -96,10 +104,12 @@ def test_columns_past_head_dim_untouched(gpu_lib, prepared, name):
         PT.compare(pr.inp.packed(res[key]), ref[key], key)
 
 
-def test_step_by_step_entry_points_match_fused_call(gpu_lib, prepared):
+@pytest.mark.parametrize("mode", ["separate", "ordered"])
+def test_step_by_step_entry_points_match_whole_call(gpu_lib, prepared, mode):
     pr = prepared("dense_causal_ragged_gqa2_d64")
-    a = PT.run_gpu(pr, deterministic=True)
-    b = PT.run_gpu(pr, deterministic=True, step_split=True)
+    acc, det = MODES[mode]
+    a = PT.run_gpu(pr, deterministic=det, dq_accumulate=acc)
+    b = PT.run_gpu(pr, deterministic=det, dq_accumulate=acc, step_split=True)
     for key in ("dq", "dk", "dv"):
         assert torch.equal(a[key].view(torch.int16), b[key].view(torch.int16)), key
 
@@ -128,7 +138,7 @@ def test_preprocess_rowdot_and_lse2(gpu_lib, prepared, name):
 
 def test_dq_convert_is_exact_scaled_rne(gpu_lib, prepared):
     pr = prepared("varlen_unequal_noncausal_d128")
-    res = PT.run_gpu(pr)
+    res = PT.run_gpu(pr, dq_accumulate=True)
     lay = res["layout"]
     H, T, DP, D = pr.inp.wl.heads, int(pr.cu_q[-1]), lay.head_dim_pad, pr.inp.wl.head_dim
     acc = PT.ws_view(res, "dq_acc", torch.float32, H * T * DP, (H, T, DP))
@@ -181,11 +191,11 @@ def _full(cid):
 def test_config2_full_parity(gpu_lib):
     _flush("config 2 full")
     pr = _full(2)
-    for det in (False, True):
-        res = PT.run_gpu(pr, deterministic=det)
-        ref = PT.oracle_backward(pr)
+    ref = PT.oracle_backward(pr)
+    for mode, (acc, det) in MODES.items():
+        res = PT.run_gpu(pr, deterministic=det, dq_accumulate=acc)
         for key in ("dq", "dk", "dv"):
-            PT.compare(pr.inp.packed(res[key]), ref[key], "c2 %s det=%s" % (key, det))
+            PT.compare(pr.inp.packed(res[key]), ref[key], "c2 %s %s" % (key, mode))
 
 
 @pytest.mark.slow
@@ -197,6 +207,9 @@ def test_full_size_sampled_units(gpu_lib, cid, units):
     _flush("config %d full size, sampled units %s" % (cid, units))
     pr = _full(cid)
     res = PT.run_gpu(pr)
+    acc = PT.run_gpu(pr, dq_accumulate=True)
+    for key in ("dk", "dv"):   # the two dQ strategies share the dK/dV pass
+        assert torch.equal(acc[key].view(torch.int16), res[key].view(torch.int16)), key
     dq, dk, dv = (pr.inp.packed(res[k]) for k in ("dq", "dk", "dv"))
     for (s, g) in units:
         s = min(s, len(pr.inp.lens_q) - 1)
