@@ -156,17 +156,14 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_dq_kernel(Params p)
 
             // ---- S^T = K Q^T, dP^T = V dO^T (64 keys x 32 rows per wave) ----
             f32x16 st[2], dpt[2];
-            zero(st[0]);
-            zero(st[1]);
-            zero(dpt[0]);
-            zero(dpt[1]);
+            const f32x16 z = {};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb) {
                     const int o = (32 * mb + l32) * RK + 16 * ks + 8 * g2;
-                    st[mb] = mfma32(lds16(sk + o), qf[ks], st[mb]);
-                    dpt[mb] = mfma32(lds16(sv + o), of[ks], dpt[mb]);
+                    st[mb] = mfma32(lds16(sk + o), qf[ks], ks == 0 ? z : st[mb]);
+                    dpt[mb] = mfma32(lds16(sv + o), of[ks], ks == 0 ? z : dpt[mb]);
                 }
             }
             pipeline_reads<4 * KS, 1, 8>();
@@ -177,20 +174,29 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_dq_kernel(Params p)
             const bool need_mask =
                 (n0 + kDqKeys > Lk) || (p.causal && (n0 + kDqKeys - 1 > q0 + off));
             const int klim = p.causal ? min(Lk - 1, qrow + off) : Lk - 1;
-            bf16x8 dsa[4];
+            bf16x4 dh[8];
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float pvv = __builtin_amdgcn_exp2f(st[mb][r] * p.scale_log2 - l2);
-                    if (need_mask) {
-                        const int key = n0 + 32 * mb + 8 * (r >> 2) + 4 * g2 + (r & 3);
-                        pvv = key <= klim ? pvv : 0.f;
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    f32x4 dv;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int r = 4 * r4 + t;
+                        float e = __builtin_amdgcn_exp2f(st[mb][r] * p.scale_log2 - l2);
+                        if (need_mask) {
+                            const int key = n0 + 32 * mb + 8 * r4 + 4 * g2 + t;
+                            e = key <= klim ? e : 0.f;
+                        }
+                        dv[t] = e * (dpt[mb][r] - rd);
                     }
-                    const float dsv = pvv * (dpt[mb][r] - rd);
-                    dsa[2 * mb + (r >> 3)][r & 7] = __builtin_bit_cast(__bf16, f2bf(dsv));
+                    dh[4 * mb + r4] = to_bf16(dv);
                 }
             }
+            bf16x8 dsa[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                dsa[kk] = concat(dh[2 * kk], dh[2 * kk + 1]);
 
             // ---- dQ += dS K  (k = 64 keys; K read transposed) ----
 #pragma unroll

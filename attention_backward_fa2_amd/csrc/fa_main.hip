@@ -70,31 +70,35 @@ __device__ inline void pointwise(const f32x16 (&s)[2], const f32x16 (&dp)[2], bf
                                  bf16x8 (&dsb)[4], uint16_t *dsT_row, const float *l2s,
                                  const float *rds, float scale_log2, int g2, int lim, bool keyok)
 {
+    // Accumulator rows 4*r4 .. 4*r4+3 of block mb are tile rows qi0 .. qi0+3
+    // and elements 4*(r4&1) .. +3 of operand 2*mb + r4/2.
+    bf16x4 ph[8], dh[8];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
             const int qi0 = 32 * mb + 8 * r4 + 4 * g2;
-            const float4 l2v = *reinterpret_cast<const float4 *>(l2s + qi0);
-            const float4 rdv = *reinterpret_cast<const float4 *>(rds + qi0);
-            const float l2a[4] = {l2v.x, l2v.y, l2v.z, l2v.w};
-            const float rda[4] = {rdv.x, rdv.y, rdv.z, rdv.w};
-            u16x4 dsv4;
+            const f32x4 l2v = *reinterpret_cast<const f32x4 *>(l2s + qi0);
+            const f32x4 rdv = *reinterpret_cast<const f32x4 *>(rds + qi0);
+            f32x4 pv, dv;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const int r = 4 * r4 + t;
-                float pv = __builtin_amdgcn_exp2f(s[mb][r] * scale_log2 - l2a[t]);
+                float e = __builtin_amdgcn_exp2f(s[mb][4 * r4 + t] * scale_log2 - l2v[t]);
                 if constexpr (MASK)
-                    pv = (keyok && qi0 + t >= lim) ? pv : 0.f;
-                const float dsv = pv * (dp[mb][r] - rda[t]);
-                const uint16_t pbits = f2bf(pv), dbits = f2bf(dsv);
-                pb[2 * mb + (r >> 3)][r & 7] = __builtin_bit_cast(__bf16, pbits);
-                dsb[2 * mb + (r >> 3)][r & 7] = __builtin_bit_cast(__bf16, dbits);
-                dsv4[t] = dbits;
+                    e = (keyok && qi0 + t >= lim) ? e : 0.f;
+                pv[t] = e;
+                dv[t] = e * (dp[mb][4 * r4 + t] - rdv[t]);
             }
+            ph[4 * mb + r4] = to_bf16(pv);
+            dh[4 * mb + r4] = to_bf16(dv);
             if constexpr (WRITE_DS)
-                *reinterpret_cast<u16x4 *>(dsT_row + qi0) = dsv4;
+                *reinterpret_cast<bf16x4 *>(dsT_row + qi0) = dh[4 * mb + r4];
         }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        pb[kk] = concat(ph[2 * kk], ph[2 * kk + 1]);
+        dsb[kk] = concat(dh[2 * kk], dh[2 * kk + 1]);
     }
 }
 
@@ -361,17 +365,14 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
 
             // ---- S = Q K^T and dP = dO V^T (64 queries x 32 keys per wave) ----
             f32x16 s[2], dp[2];
-            zero(s[0]);
-            zero(s[1]);
-            zero(dp[0]);
-            zero(dp[1]);
+            const f32x16 z = {};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb) {
                     const int o = (32 * mb + l32) * RQ + 16 * ks + 8 * g2;
-                    s[mb] = mfma32(lds16(sq + o), kf[ks], s[mb]);
-                    dp[mb] = mfma32(lds16(sdo + o), vf[ks], dp[mb]);
+                    s[mb] = mfma32(lds16(sq + o), kf[ks], ks == 0 ? z : s[mb]);
+                    dp[mb] = mfma32(lds16(sdo + o), vf[ks], ks == 0 ? z : dp[mb]);
                 }
             }
             pipeline_reads<4 * KS, 1, 8>();

@@ -30,6 +30,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
@@ -37,6 +39,18 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp32 -> bf16 (round to nearest even) of four values: two packed
+// hardware converts.
+__device__ inline bf16x4 to_bf16(f32x4 x)
+{
+    return __builtin_convertvector(x, bf16x4);
+}
+
+__device__ inline bf16x8 concat(bf16x4 lo, bf16x4 hi)
+{
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 __device__ inline void zero(f32x16 &c)

@@ -103,7 +103,10 @@ def main():
     ap.add_argument("--deterministic", action="store_true",
                     help="with --dq-accumulate: ordered (bit-reproducible) partial adds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-units", type=int, default=8)
+    ap.add_argument("--cpu-units", type=int, default=16)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of 1 GiB (4 times), the reference "
+                         "kernel for scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -115,6 +118,17 @@ def main():
     import torch
     import workloads as W
     import attention_backward_fa2_amd as fa
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_dispatch": {"read": n, "write": n},
+                          "dispatches": 4}), flush=True)
+        return
 
     fa.load_library()
     wl = W.WORKLOADS[args.config]
