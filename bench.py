@@ -27,6 +27,174 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0         # MI355X published HBM3E bandwidth
 
 
+# Sources of the key-tile kernel: the committed HBM-traffic summary applies to
+# the kernel built from exactly these files (sha256 recorded with it).
+KERNEL_SOURCES = ["attention_backward_fa2_amd/csrc/fa_main.hip",
+                  "attention_backward_fa2_amd/csrc/fa_mfma.h",
+                  "attention_backward_fa2_amd/csrc/fa_internal.h"]
+TRAFFIC_SUMMARY = "profiles/hbm_traffic_main_kernel_gqa_b2_h32_hk8_s4096_d128_causal.json"
+TRACE_SUMMARY = "profiles/kernel_trace_gqa_b2_h32_hk8_s4096_d128_causal.md"
+MAIN_KERNEL = "fa_bwd_main_kernel<128, false>"
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def committed_traffic():
+    """Per-launch HBM bytes of the key-tile kernel from the committed counter
+    summary, or None if there is none or the kernel changed since."""
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("source_sha256") != kernel_source_hash():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as fh:
+        return list(csv.DictReader(fh))
+
+
+def _find(root, suffix):
+    for dp, _, files in os.walk(root):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(dp, f)
+    raise FileNotFoundError("%s under %s" % (suffix, root))
+
+
+WORKLOAD_TAG = "gqa_b2_h32_hk8_s4096_d128_causal"
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof/trace -o c3 -- "
+             "python bench.py")
+PMC_RUN = "python bench.py --no-cpu-baseline --steps 3 --warmup 1"
+SQ_PASSES = [
+    "SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY "
+    "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS",
+    "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_VALU_MFMA_BUSY_CYCLES "
+    "SQ_LDS_BANK_CONFLICT SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_VMEM"]
+
+
+def _kname(raw):
+    return raw.replace("void fa::", "").split("(fa::Params)")[0]
+
+
+def _pmc_means(path):
+    import collections
+    acc = collections.defaultdict(list)
+    for r in _csv_rows(path):
+        acc[(r["Kernel_Name"], r["Counter_Name"])].append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def summarize_profile(prof_dir, out_dir):
+    """Write the profile summaries committed under profiles/ from the
+    rocprofv3 outputs of the commands they list, run from the repo root
+    with the outputs under PROF_DIR (trace/ + trace.log, FETCH_SIZE/,
+    WRITE_SIZE/, copy_FETCH_SIZE/, copy_WRITE_SIZE/, sq1/, sq2/)."""
+    # -- kernel trace: per-kernel durations, all calls and the timed steps --
+    stats = _csv_rows(_find(os.path.join(prof_dir, "trace"), "kernel_stats.csv"))
+    trace = _csv_rows(_find(os.path.join(prof_dir, "trace"), "kernel_trace.csv"))
+    bench_line = None
+    with open(os.path.join(prof_dir, "trace.log")) as fh:
+        for line in fh:
+            if line.startswith("{") and '"metric"' in line:
+                bench_line = json.loads(line)
+    steps = bench_line["steps"]
+    per_kernel = {}
+    for r in trace:
+        if "fa::" in r["Kernel_Name"]:
+            per_kernel.setdefault(_kname(r["Kernel_Name"]), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["# Kernel trace: %s" % WORKLOAD_TAG, "",
+             "B=2, H=32, Hk=8, Sq=Sk=4096, D=128, causal, bf16; dQ by the separate "
+             "query-tile kernel (the default path of `fa_bwd`).", "",
+             "Command (repo root, MI355X):", "", "    " + TRACE_CMD, "",
+             "| kernel | calls | average (us) | min (us) | max (us) | average of the %d timed "
+             "steps (us) |" % steps, "|---|---|---|---|---|---|"]
+    for r in stats:
+        if "fa::" in r["Name"]:
+            name = _kname(r["Name"])
+            timed = per_kernel[name][-steps:]
+            lines.append("| %s | %s | %.1f | %.1f | %.1f | %.1f |" % (
+                name, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                float(r["MaxNs"]) / 1e3, sum(timed) / len(timed)))
+    lines += ["", "Calls = warm-up + timed steps of bench.py (%d + %d)." % (
+        bench_line["warmup"], steps), "",
+        "The same run's bench line measured these kernels with HIP events on the launch "
+        "stream (ms per launch): `%s`; whole step %.4f ms, %.1f TFLOP/s." % (
+            json.dumps(bench_line["kernel_ms"]), bench_line["ms_per_step"],
+            bench_line["value"])]
+    with open(os.path.join(out_dir, os.path.basename(TRACE_SUMMARY)), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+    # -- HBM traffic of the key-tile kernel, scaled by a plain copy --
+    res = {"kernel": MAIN_KERNEL, "workload": WORKLOAD_TAG,
+           "source_files": KERNEL_SOURCES, "source_sha256": kernel_source_hash(),
+           "commands": [
+               "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof/FETCH_SIZE -o c3 -- " + PMC_RUN,
+               "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof/WRITE_SIZE -o c3 -- " + PMC_RUN,
+               "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof/copy_FETCH_SIZE -o copy -- "
+               "python bench.py --copy-calibration",
+               "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof/copy_WRITE_SIZE -o copy -- "
+               "python bench.py --copy-calibration"],
+           "note": "kib_per_dispatch is the counter's mean over the kernel's dispatches; "
+                   "scale_factor = copied bytes / (counter KiB * 1024) of a 1 GiB "
+                   "device-to-device copy"}
+    copy_bytes = float(1 << 30)
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        m = _pmc_means(_find(os.path.join(prof_dir, c), "counter_collection.csv"))
+        kib, n = next(v for (k, cn), v in m.items() if MAIN_KERNEL in k and cn == c)
+        cm = _pmc_means(_find(os.path.join(prof_dir, "copy_" + c), "counter_collection.csv"))
+        ckib, cn_ = next(v for (k, cn), v in cm.items() if "copyBuffer" in k and cn == c)
+        factor = copy_bytes / (ckib * 1024.0)
+        res[c] = {"kib_per_dispatch": kib, "dispatches": n, "copy_kib_per_dispatch": ckib,
+                  "copy_dispatches": cn_, "scale_factor": factor,
+                  "bytes_per_launch": kib * 1024.0 * factor}
+    res["traffic_bytes_per_launch"] = (res["FETCH_SIZE"]["bytes_per_launch"] +
+                                       res["WRITE_SIZE"]["bytes_per_launch"])
+    with open(os.path.join(out_dir, os.path.basename(TRAFFIC_SUMMARY)), "w") as fh:
+        json.dump(res, fh, indent=1)
+        fh.write("\n")
+
+    # -- SQ counters per kernel --
+    sq = {}
+    for sub in ("sq1", "sq2"):
+        for (k, c), (v, _) in _pmc_means(
+                _find(os.path.join(prof_dir, sub), "counter_collection.csv")).items():
+            if "fa::" in k:
+                sq.setdefault(_kname(k), {})[c] = v
+    names = sorted(sq)
+    cols = sorted({c for d in sq.values() for c in d})
+    lines = ["# SQ counters per dispatch: %s" % WORKLOAD_TAG, "", "Commands (repo root, MI355X):", ""]
+    for i, cs in enumerate(SQ_PASSES):
+        lines.append("    rocprofv3 --pmc %s -f csv -d gpurun_out/prof/sq%d -o c3 -- %s" % (
+            cs, i + 1, PMC_RUN))
+    lines += ["", "| counter | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
+    for c in cols:
+        lines.append("| %s | %s |" % (c, " | ".join("%.4g" % sq[n].get(c, float("nan"))
+                                                      for n in names)))
+    lines += ["", "Derived (SQ_VALU_MFMA_BUSY_CYCLES is summed over the SIMDs):", ""]
+    for n in names:
+        d = sq[n]
+        if d.get("SQ_INSTS_MFMA"):
+            lines.append("- %s: %.1f VALU instructions per MFMA; %.0f MFMA busy cycles per MFMA"
+                         % (n, d["SQ_INSTS_VALU"] / d["SQ_INSTS_MFMA"],
+                            d["SQ_VALU_MFMA_BUSY_CYCLES"] / d["SQ_INSTS_MFMA"]))
+    with open(os.path.join(out_dir, "sq_counters_%s.md" % WORKLOAD_TAG), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("wrote profile summaries to", out_dir)
+
+
 def conv_flops(B, H, Sq, Sk, D, causal):
     f = 2.5 * 4.0 * B * H * Sq * Sk * D
     return f * 0.5 if causal else f
@@ -94,8 +262,8 @@ def cpu_baseline(wl, units):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--config", type=int, default=3, help="workload id (workloads.py)")
     ap.add_argument("--dq-accumulate", action="store_true",
                     help="form dQ by fp32 partial adds in the key-tile pass (+ convert) "
@@ -104,11 +272,17 @@ def main():
                     help="with --dq-accumulate: ordered (bit-reproducible) partial adds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=16)
+    ap.add_argument("--summarize-profile", metavar="PROF_DIR",
+                    help="write the profiles/ summaries from rocprofv3 outputs in PROF_DIR "
+                         "(trace/, FETCH_SIZE/, WRITE_SIZE/, copy_FETCH_SIZE/, copy_WRITE_SIZE/)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB (4 times), the reference "
                          "kernel for scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
 
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, os.path.join(ROOT, "profiles"))
+        return
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
               "(the backward splits into independent (batch, KV-head) units that need "
@@ -223,7 +397,11 @@ def main():
          else {}),
         "roofline": {"bound": "mfma", "achieved": round(main_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None if args.dq_accumulate else committed_traffic(),
+                     "kernel": MAIN_KERNEL if not args.dq_accumulate else
+                     "fa_bwd_main_kernel<128, true>",
+                     "algorithmic_flops_per_launch": main_flops},
         "wall_s": round(wall, 3),
         "ordered_wait_gave_up": bool(int(flags[0]) != 0),
     }
