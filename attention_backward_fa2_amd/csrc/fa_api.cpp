@@ -115,7 +115,11 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
         (st = check_strides("dk", a->dk_stride, varlen)) ||
         (st = check_strides("dv", a->dv_stride, varlen)))
         return st;
-    // The main kernel addresses a 64-row query tile with 32-bit offsets.
+    // The main kernel addresses a 64-row query tile with 32-bit offsets and
+    // bounds its loads at the end of the tile's last valid row, which needs
+    // rows that do not overlap.
+    if (a->q_stride[1] < a->head_dim || a->do_stride[1] < a->head_dim)
+        return fail(FA_ERR_INVALID_ARG, "q / dout row stride is smaller than head_dim");
     if (a->q_stride[1] >= (int64_t(1) << 24) || a->do_stride[1] >= (int64_t(1) << 24))
         return fail(FA_ERR_UNSUPPORTED, "q / dout row stride >= 2^24 elements is not supported");
     if (a->softmax_scale != a->softmax_scale || std::isinf(a->softmax_scale))

@@ -27,17 +27,20 @@
 // Q^T come from the row-major tiles through transposing LDS reads.  In fused
 // mode dS^T goes through LDS for dQ = dS K.
 //
-// LDS (D_pad = 128): Q and dO row-major, double buffered (4 x 18 KB), row
-// vectors 1 KB: 73 KB; fused mode adds dS^T double buffered (2 x 20 KB) and
-// K row-major (36 KB): 149 KB.  One workgroup per CU.  Row pitches are
-// D + 16 elements (dS^T: 64 + 16) so that both the 16-byte row reads and the
-// transposing reads hit distinct banks.
+// LDS (D_pad = 128): Q and dO tiles, double buffered (4 x 16 KB) in the
+// swizzled unpadded layout of fa_mfma.h, plus lse2 / rowdot (1 KB): 65 KB;
+// fused mode adds dS^T double buffered (2 x 20 KB) and K row-major (36 KB,
+// pitch D + 16): 141 KB.  One workgroup per CU.
 //
-// Pipelining: the next query tile is loaded from global memory into
-// registers while the current one is computed and written to the other LDS
-// buffer before any dQ atomic of the current tile is issued.  One workgroup
-// barrier per tile: every LDS buffer written in tile t was last read before
-// the barrier of tile t-1.
+// Pipelining: the next query tile is loaded by buffer loads that write LDS
+// directly (no staging registers, zero fill of tail rows / padded columns
+// by the buffer bound) while the current one is computed; one workgroup
+// barrier per tile, after the wave's loads have landed.  Within a tile the
+// products are ordered so that the MFMA pipe always has independent work
+// while the vector ALU computes P and dS: S and dP of query rows 0-31, then
+// rows 32-63 alongside the pointwise math of rows 0-31, then the dV / dK
+// k-steps over rows 0-31 alongside the pointwise math of rows 32-63, then
+// the k-steps over rows 32-63.
 #include <climits>
 #include <type_traits>
 
@@ -45,61 +48,72 @@
 
 namespace fa {
 
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// Query-side tile geometry in LDS.
+template <int DP>
+struct QTile {
+    static constexpr int PCH = DP <= 64 ? 8 : 16;   // 16-byte chunks per LDS row
+    static constexpr int PB = 16 * PCH;             // row pitch (bytes)
+    static constexpr int BYTES = kQTile * PB;
+    static constexpr int NLOAD = BYTES / 1024;      // 1 KB wave loads per tile
+    static constexpr int PERW = NLOAD / 4;          // ... per wave
+    static constexpr int RPL = 1024 / PB;           // rows per wave load
+};
+
 template <int DP>
 struct __attribute__((aligned(16))) TileSmem {
-    static constexpr int RQ = DP + 16;       // pitch of q / dO / k (elements)
-    static constexpr int RD = kQTile + 16;   // pitch of dS^T
-    uint16_t q[2][kQTile * RQ];
-    uint16_t dO[2][kQTile * RQ];
+    uint8_t q[2][QTile<DP>::BYTES];
+    uint8_t dO[2][QTile<DP>::BYTES];
     float lse2[2][kQTile];
     float rowdot[2][kQTile];
 };
 
 template <int DP>
 struct __attribute__((aligned(16))) FusedSmem : TileSmem<DP> {
-    uint16_t dsT[2][kKTile * TileSmem<DP>::RD];
-    uint16_t k[kKTile * TileSmem<DP>::RQ];
+    static constexpr int RQ = DP + 16;       // pitch of k (elements)
+    static constexpr int RD = kQTile + 16;   // pitch of dS^T
+    uint16_t dsT[2][kKTile * RD];
+    uint16_t k[kKTile * RQ];
 };
 
-// P = exp2(S*scale*log2e - lse2) and dS = P (dP - rowdot) for one wave's
-// 64 x 32 tile; bf16 copies in MFMA B-operand order and (fused mode) the
-// lane's dS^T row to LDS.  MASK: query row qi (0..63 in the tile) sees this
-// lane's key iff keyok && qi >= lim.
+// P = exp2(S*scale*log2e - lse2) and dS = P (dP - rowdot) for query rows
+// 32*mb .. 32*mb+31 of the tile (one accumulator block per product), as
+// bf16 B operands pb[0..1] / dsb[0..1] of the k-steps over those rows, and
+// (fused mode) the lane's dS^T row segment to LDS.  MASK: tile row qi sees
+// this lane's key iff keyok && qi >= lim.
 template <bool MASK, bool WRITE_DS>
-__device__ inline void pointwise(const f32x16 (&s)[2], const f32x16 (&dp)[2], bf16x8 (&pb)[4],
-                                 bf16x8 (&dsb)[4], uint16_t *dsT_row, const float *l2s,
-                                 const float *rds, float scale_log2, int g2, int lim, bool keyok)
+__device__ inline void pointwise_half(const f32x16 &s, const f32x16 &dp, bf16x8 *pb, bf16x8 *dsb,
+                                      uint16_t *dsT_row, const float *l2s, const float *rds,
+                                      float scale_log2, int g2, int mb, int lim, bool keyok)
 {
-    // Accumulator rows 4*r4 .. 4*r4+3 of block mb are tile rows qi0 .. qi0+3
-    // and elements 4*(r4&1) .. +3 of operand 2*mb + r4/2.
-    bf16x4 ph[8], dh[8];
+    // Accumulator rows 4*r4 .. 4*r4+3 are tile rows qi0 .. qi0+3 and
+    // elements 4*(r4&1) .. +3 of operand r4/2.
+    bf16x4 ph[4], dh[4];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int r4 = 0; r4 < 4; ++r4) {
+        const int qi0 = 32 * mb + 8 * r4 + 4 * g2;
+        const f32x4 l2v = *reinterpret_cast<const f32x4 *>(l2s + qi0);
+        const f32x4 rdv = *reinterpret_cast<const f32x4 *>(rds + qi0);
+        f32x4 pv, dv;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const int qi0 = 32 * mb + 8 * r4 + 4 * g2;
-            const f32x4 l2v = *reinterpret_cast<const f32x4 *>(l2s + qi0);
-            const f32x4 rdv = *reinterpret_cast<const f32x4 *>(rds + qi0);
-            f32x4 pv, dv;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                float e = __builtin_amdgcn_exp2f(s[mb][4 * r4 + t] * scale_log2 - l2v[t]);
-                if constexpr (MASK)
-                    e = (keyok && qi0 + t >= lim) ? e : 0.f;
-                pv[t] = e;
-                dv[t] = e * (dp[mb][4 * r4 + t] - rdv[t]);
-            }
-            ph[4 * mb + r4] = to_bf16(pv);
-            dh[4 * mb + r4] = to_bf16(dv);
-            if constexpr (WRITE_DS)
-                *reinterpret_cast<bf16x4 *>(dsT_row + qi0) = dh[4 * mb + r4];
+        for (int t = 0; t < 4; ++t) {
+            float e = __builtin_amdgcn_exp2f(s[4 * r4 + t] * scale_log2 - l2v[t]);
+            if constexpr (MASK)
+                e = (keyok && qi0 + t >= lim) ? e : 0.f;
+            pv[t] = e;
+            dv[t] = e * (dp[4 * r4 + t] - rdv[t]);
         }
+        ph[r4] = to_bf16(pv);
+        dh[r4] = to_bf16(dv);
+        if constexpr (WRITE_DS)
+            *reinterpret_cast<bf16x4 *>(dsT_row + qi0) = dh[r4];
     }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        pb[kk] = concat(ph[2 * kk], ph[2 * kk + 1]);
-        dsb[kk] = concat(dh[2 * kk], dh[2 * kk + 1]);
-    }
+    pb[0] = concat(ph[0], ph[1]);
+    pb[1] = concat(ph[2], ph[3]);
+    dsb[0] = concat(dh[0], dh[1]);
+    dsb[1] = concat(dh[2], dh[3]);
 }
 
 // Fused mode: dQ partial of one query tile = dS K over this workgroup's 128
@@ -112,7 +126,7 @@ __device__ inline void dq_partial(const Params &p, FusedSmem<DP> &sm, int buf, i
                                   int rows_valid, int Lq, int off, int nt_b, int64_t ws_row)
 {
     constexpr int DB = DP / 32;
-    constexpr int RQ = TileSmem<DP>::RQ, RD = TileSmem<DP>::RD;
+    constexpr int RQ = FusedSmem<DP>::RQ, RD = FusedSmem<DP>::RD;
     const int64_t wsbase = (int64_t)h * p.rows + ws_row;
                 // ---- dQ partial = dS K: 2*DB blocks of 32x32 spread over 4 waves.
                 //      DB = 4: wave w owns head-dim block w for both query blocks
@@ -222,15 +236,13 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
 {
     constexpr int KS = DP / 16;       // MFMA k-steps over the head dim
     constexpr int DB = DP / 32;       // 32-wide blocks of the head dim
-    constexpr int RQ = TileSmem<DP>::RQ, RD = TileSmem<DP>::RD;
-    constexpr int CPR = DP / 8;       // 16-byte chunks per tile row
-    constexpr int NCH = kQTile * CPR / kThreads;   // chunks per thread per tile
-    static_assert(kQTile * CPR % kThreads == 0, "tile load must divide evenly");
+    using L = QTile<DP>;
     using Smem = std::conditional_t<FUSED, FusedSmem<DP>, TileSmem<DP>>;
     __shared__ Smem sm;
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, g2 = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, g2 = lane >> 5;
 
     // Workgroup -> (batch, KV head, key tile).
     //  - default: longest work first.  Key tile 0 sees the most query tiles
@@ -282,7 +294,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             kf[ks] = __builtin_bit_cast(bf16x8, kv);
             vf[ks] = __builtin_bit_cast(bf16x8, vv);
             if constexpr (FUSED)
-                *reinterpret_cast<u32x4 *>(&sm.k[key_local * RQ + d0]) = kv;
+                *reinterpret_cast<u32x4 *>(&sm.k[key_local * FusedSmem<DP>::RQ + d0]) = kv;
         }
     }
 
@@ -300,123 +312,180 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         const int nm = m_end - m_begin;
         const int total = p.G * nm;
         const int nt_b = (Lk + kKTile - 1) / kKTile;
-        // Prefetch registers for one query tile: NCH 16-byte chunks of Q
-        // and of dO per thread, plus one lse2 / rowdot value pair.  Chunk c
-        // of this thread is tile row (tid + c*256) / CPR, 16-byte column
-        // (tid + c*256) % CPR.  Loads always use an in-bounds (clamped)
-        // address; the zero fill of rows past the sequence end and of
-        // columns past head_dim is applied when staging, so issuing a
-        // prefetch never has to wait for older memory traffic.
-        u32x4 pq[NCH], pd[NCH];
-        float pl2 = INFINITY, prd = 0.f;
-        int rv_next = kQTile;             // valid rows of the prefetched tile
-        auto prefetch = [&](int it) {
-            const int hh = it / nm, m = m_begin + it % nm;
+
+        // Global byte offset of the 16-byte chunk each lane loads for wave
+        // load i of this wave: LDS row pr, LDS chunk lane % PCH, which holds
+        // tile chunk c = (lane % PCH) ^ swz(pr).  Chunks past head_dim (and
+        // the unused chunks of a padded row) load zeros.
+        uint32_t voq[L::PERW], vod[L::PERW];
+#pragma unroll
+        for (int i = 0; i < L::PERW; ++i) {
+            const int pr = (w * L::PERW + i) * L::RPL + lane / L::PCH;
+            const int c = (lane % L::PCH) ^ swz(pr);
+            const bool ok = c * 8 < p.D;
+            voq[i] = ok ? (uint32_t)(pr * (int)p.q_ss * 2 + c * 16) : kOutOfRange;
+            vod[i] = ok ? (uint32_t)(pr * (int)p.do_ss * 2 + c * 16) : kOutOfRange;
+        }
+        // LDS byte offsets (within a tile) of this lane's operand reads:
+        //  gq[k4]: 16-byte read of row l32, tile chunk 2*ks + g2 (ks % 4 = k4;
+        //          + 128 bytes per 4 k-steps, + 32 rows per query block);
+        //  tq[x]:  transposing read of rows 4*g2 + rr (+ 16 per k-step, + 8
+        //          for the second half), tile chunk 4*x + 2*h16 + b1 (+ 128
+        //          bytes per two head-dim blocks), 8-byte half c16 & 1.
+        int gq[4], tq[2];
+        {
+            const int sw = swz(l32);
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4)
+                gq[k4] = l32 * L::PB + (((2 * k4 + g2) ^ sw) << 4);
+            const int c16 = lane & 15, rr = c16 >> 2, h16 = (lane >> 4) & 1, b1 = (c16 >> 1) & 1;
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+                tq[x] = (4 * g2 + rr) * L::PB + (((4 * x + 2 * h16 + b1) ^ (2 * rr + g2)) << 4) +
+                        (c16 & 1) * 8;
+        }
+
+        // Query tile of step `it`: heads of the group in turn; within a head
+        // the last query tile first, so the workgroups of one (batch, KV
+        // head) running side by side on an XCD read the same tile at about
+        // the same time (L2 reuse).  Ordered dQ adds keep the ascending
+        // order, in which no workgroup waits on its first tile.
+        const bool ascending = FUSED && p.deterministic;
+        auto tile_m = [&](int it) {
+            const int r = it % nm;
+            return ascending ? m_begin + r : m_end - 1 - r;
+        };
+
+        // Issue the loads of query tile `it` into LDS buffer BF.
+        auto issue = [&](int it, auto bufc) {
+            constexpr int BF = decltype(bufc)::value;
+            const int hh = it / nm, m = tile_m(it);
             const int h = hk * p.G + hh;
             const int q0 = m * kQTile;
-            rv_next = min(kQTile, Lq - q0);
-            const uint16_t *qb =
-                p.q + h * p.q_sh + row_offset(p, b, si.tok_q, q0, p.q_sb, p.q_ss);
+            const int rv = min(kQTile, Lq - q0);
+            const uint16_t *qb = p.q + h * p.q_sh + row_offset(p, b, si.tok_q, q0, p.q_sb, p.q_ss);
             const uint16_t *db =
                 p.dout + h * p.do_sh + row_offset(p, b, si.tok_q, q0, p.do_sb, p.do_ss);
+            const auto rq = make_rsrc(qb, (uint32_t)((rv - 1) * (int)p.q_ss * 2 + p.D * 2));
+            const auto rd = make_rsrc(db, (uint32_t)((rv - 1) * (int)p.do_ss * 2 + p.D * 2));
 #pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                const int idx = tid + c * kThreads;
-                const int r = min(idx / CPR, rv_next - 1);
-                const int col = (idx % CPR) * 8 < p.D ? (idx % CPR) * 8 : 0;
-                pq[c] = *reinterpret_cast<const u32x4 *>(qb + r * (int)p.q_ss + col);
-                pd[c] = *reinterpret_cast<const u32x4 *>(db + r * (int)p.do_ss + col);
+            for (int i = 0; i < L::PERW; ++i) {
+                const int ld = (w * L::PERW + i) * 1024;
+                load16_to_lds(rq, sm.q[BF] + ld, voq[i]);
+                load16_to_lds(rd, sm.dO[BF] + ld, vod[i]);
             }
-            const int lr = min(tid & (kQTile - 1), rv_next - 1);
-            const int64_t wr = (int64_t)h * p.rows + si.ws_row + q0 + lr;
-            pl2 = p.lse2[wr];
-            prd = p.rowdot[wr];
-        };
-        auto stage = [&](int buf) {
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                const int idx = tid + c * kThreads;
-                const uint32_t keep = (idx / CPR < rv_next && (idx % CPR) * 8 < p.D) ? ~0u : 0u;
-                const int o = (idx / CPR) * RQ + (idx % CPR) * 8;
-                *reinterpret_cast<u32x4 *>(&sm.q[buf][o]) = pq[c] & keep;
-                *reinterpret_cast<u32x4 *>(&sm.dO[buf][o]) = pd[c] & keep;
-            }
-            if (tid < kQTile) {
-                const bool ok = tid < rv_next;
-                sm.lse2[buf][tid] = ok ? pl2 : INFINITY;
-                sm.rowdot[buf][tid] = ok ? prd : 0.f;
+            if (w < 2) {
+                const float *src = (w == 0 ? p.lse2 : p.rowdot) + (int64_t)h * p.rows + si.ws_row + q0;
+                load4_to_lds(make_rsrc(src, (uint32_t)rv * 4), w == 0 ? sm.lse2[BF] : sm.rowdot[BF],
+                               (uint32_t)lane * 4);
             }
         };
 
-        prefetch(0);
-        stage(0);
-        __syncthreads();
+        // One query tile from LDS buffer BF; MASKED: causal / tail masking.
+        auto body = [&](int it, auto bufc, auto maskc) {
+            constexpr int BF = decltype(bufc)::value;
+            constexpr bool MASKED = decltype(maskc)::value != 0;
+            const int q0 = tile_m(it) * kQTile;
+            const uint8_t *sq = sm.q[BF];
+            const uint8_t *sdo = sm.dO[BF];
+            const int lim = MASKED && p.causal ? key - q0 - off : INT_MIN;
+            const bool keyok = key < Lk;
+            uint16_t *dsrow = nullptr;
+            if constexpr (FUSED)
+                dsrow = &sm.dsT[BF][key_local * FusedSmem<DP>::RD];
 
-        for (int it = 0; it < total; ++it) {
-            const int buf = it & 1;
-            const int hh = it / nm, m = m_begin + it % nm;
-            const int h = hk * p.G + hh;
-            const int q0 = m * kQTile;
-            const int rows_valid = min(kQTile, Lq - q0);
-            if (it + 1 < total)
-                prefetch(it + 1);
-            const uint16_t *sq = sm.q[buf];
-            const uint16_t *sdo = sm.dO[buf];
-
-            // ---- S = Q K^T and dP = dO V^T (64 queries x 32 keys per wave) ----
+            // S = Q K^T and dP = dO V^T, query rows 0-31 then 32-63.
             f32x16 s[2], dp[2];
             const f32x16 z = {};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
+            for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb) {
-                    const int o = (32 * mb + l32) * RQ + 16 * ks + 8 * g2;
-                    s[mb] = mfma32(lds16(sq + o), kf[ks], ks == 0 ? z : s[mb]);
-                    dp[mb] = mfma32(lds16(sdo + o), vf[ks], ks == 0 ? z : dp[mb]);
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int o = gq[ks & 3] + 32 * mb * L::PB + 128 * (ks >> 2);
+                    s[mb] = mfma32(lds16b(sq + o), kf[ks], ks == 0 ? z : s[mb]);
+                    dp[mb] = mfma32(lds16b(sdo + o), vf[ks], ks == 0 ? z : dp[mb]);
                 }
             }
-            pipeline_reads<4 * KS, 1, 8>();
-
-            // ---- P, dS (fp32), masked only on diagonal / tail tiles ----
-            const bool need_mask =
-                (n0 + kKTile > Lk) || (p.causal && (n0 + kKTile - 1 > q0 + off));
             bf16x8 pb[4], dsb[4];
-            uint16_t *dsrow = nullptr;
-            if constexpr (FUSED)
-                dsrow = &sm.dsT[buf][key_local * RD];
-            if (need_mask) {
-                // causal: key visible to tile row qi iff key <= q0 + qi + off
-                const int lim = p.causal ? key - q0 - off : INT_MIN;
-                pointwise<true, FUSED>(s, dp, pb, dsb, dsrow, sm.lse2[buf], sm.rowdot[buf],
-                                       p.scale_log2, g2, lim, key < Lk);
-            } else {
-                pointwise<false, FUSED>(s, dp, pb, dsb, dsrow, sm.lse2[buf], sm.rowdot[buf],
-                                        p.scale_log2, g2, 0, true);
-            }
-
-            // ---- dV^T += dO^T P,  dK^T += Q^T dS  (k = 64 queries) ----
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int r0 = 16 * kk + 4 * g2, r1 = r0 + 8;
+            pointwise_half<MASKED, FUSED>(s[0], dp[0], pb, dsb, dsrow, sm.lse2[BF], sm.rowdot[BF],
+                                          p.scale_log2, g2, 0, lim, keyok);
+            // dV^T += dO^T P, dK^T += Q^T dS over k-steps kk (16 query rows each).
+            auto g35 = [&](int kk) {
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    dv_acc[db] = mfma32(frag_tr(sdo, RQ, r0, r1, 32 * db, lane), pb[kk], dv_acc[db]);
-                    dk_acc[db] = mfma32(frag_tr(sq, RQ, r0, r1, 32 * db, lane), dsb[kk], dk_acc[db]);
+                    const int o0 = tq[db & 1] + 16 * kk * L::PB + 128 * (db >> 1);
+                    const int o1 = o0 + 8 * L::PB;
+                    dv_acc[db] = mfma32(tr_pair(sdo + o0, sdo + o1), pb[kk], dv_acc[db]);
+                    dk_acc[db] = mfma32(tr_pair(sq + o0, sq + o1), dsb[kk], dk_acc[db]);
                 }
+            };
+            g35(0);
+            g35(1);
+            pointwise_half<MASKED, FUSED>(s[1], dp[1], pb + 2, dsb + 2, dsrow, sm.lse2[BF],
+                                          sm.rowdot[BF], p.scale_log2, g2, 1, lim, keyok);
+            g35(2);
+            g35(3);
+
+            // Instruction order: reads run ahead of the MFMAs that use them;
+            // the pointwise math of each half fills the gaps between the
+            // MFMAs of the next product block.
+            constexpr int NB = 2 * KS;       // MFMAs per query block of S / dP
+            constexpr int NG = 4 * DB;       // MFMAs per two k-steps of dV / dK
+            sched<kSchedDsRead, 6>();
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                sched<kSchedMfma, 1>();
+                sched<kSchedDsRead, 1>();
             }
-            pipeline_reads<8 * DB, 2, 8>();
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                sched<kSchedMfma, 1>();
+                sched<kSchedDsRead, 1>();
+                sched<kSchedValu, 5>();
+            }
+#pragma unroll
+            for (int i = 0; i < NG; ++i) {
+                sched<kSchedMfma, 1>();
+                sched<kSchedDsRead, 2>();
+                sched<kSchedValu, 5>();
+            }
+#pragma unroll
+            for (int i = 0; i < NG; ++i) {
+                sched<kSchedMfma, 1>();
+                sched<kSchedDsRead, 2>();
+            }
+        };
 
-            // Stage the prefetched next tile now, before this tile's dQ
-            // atomics are issued, so waiting for its loads never waits for
-            // the atomics.  Buffer buf^1 was last read before the previous
-            // barrier.
+        // One pipeline step: loads of the next tile, this tile, barrier.
+        auto step = [&](int it, auto bufc) {
+            constexpr int BF = decltype(bufc)::value;
             if (it + 1 < total)
-                stage(buf ^ 1);
-            __syncthreads();   // next tile staged (fused: dS^T[buf] complete)
-
-            if constexpr (FUSED)
-                dq_partial<DP>(p, sm, buf, w, lane, l32, g2, tid, b, h, m, j, q0, rows_valid, Lq,
+                issue(it + 1, IC<1 - BF>{});
+            const int m = tile_m(it);
+            const int q0 = m * kQTile;
+            const bool need_mask =
+                (n0 + kKTile > Lk) || (p.causal && (n0 + kKTile - 1 > q0 + off));
+            if (need_mask)
+                body(it, bufc, IC<1>{});
+            else
+                body(it, bufc, IC<0>{});
+            wait_loads();
+            __syncthreads();   // next tile in LDS; buffer BF free (fused: dS^T[BF] complete)
+            if constexpr (FUSED) {
+                const int h = hk * p.G + it / nm;
+                const int rows_valid = min(kQTile, Lq - q0);
+                dq_partial<DP>(p, sm, BF, w, lane, l32, g2, tid, b, h, m, j, q0, rows_valid, Lq,
                                off, nt_b, si.ws_row);
+            }
+        };
+
+        issue(0, IC<0>{});
+        wait_loads();
+        __syncthreads();
+        for (int it = 0; it < total; it += 2) {
+            step(it, IC<0>{});
+            if (it + 1 < total)
+                step(it + 1, IC<1>{});
         }
     }
 

@@ -87,8 +87,73 @@ __device__ inline bf16x8 frag_tr(const uint16_t *base, int pitch, int r0, int r1
 }
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002;
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedDsWrite = 0x200;
+
+// ---- Buffer loads straight into LDS ----
+// A raw buffer resource covers `bytes` bytes from `base`; loads at offsets at
+// or past that bound return zeros without touching memory, which is how tile
+// rows past the end of a sequence and columns past head_dim are zero-filled.
+// Each wave load of W bytes per lane writes 64 * W contiguous bytes of LDS
+// (lane l at lds + l * W), so a tile's LDS layout is chosen through the
+// global offset each lane loads from.
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit elements
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
+}
+
+__device__ inline void load16_to_lds(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voffset)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voffset, 0, 0, 0);
+}
+
+__device__ inline void load4_to_lds(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voffset)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 4, voffset, 0, 0, 0);
+}
+
+// Wait until every load this wave issued (including loads into LDS) landed.
+__device__ inline void wait_loads()
+{
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt unchanged
+}
+
+// ---- Swizzled row-major tiles in LDS ----
+// Rows of 16-byte chunks with no padding; chunk c of row r is stored at
+// chunk position c ^ swz(r).  swz is a bijection on r % 8, so eight
+// consecutive rows read at the same chunk (16-byte operand reads) hit eight
+// different 16-byte bank groups, and swz(r) >> 1 differs between the four
+// rows of an aligned group of four, so the two chunks that four such rows
+// supply to one transposing read also land in eight different bank groups.
+__device__ __host__ constexpr int swz(int r)
+{
+    return 2 * (r & 3) + ((r >> 2) & 1);
+}
+
+__device__ inline bf16x8 lds16b(const uint8_t *p)
+{
+    return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+// Transposing operand read from two byte addresses (see frag_tr).
+__device__ inline bf16x8 tr_pair(const uint8_t *p0, const uint8_t *p1)
+{
+    const i16x4 v8[2] = {lds_tr(reinterpret_cast<const uint16_t *>(p0)),
+                         lds_tr(reinterpret_cast<const uint16_t *>(p1))};
+    return __builtin_bit_cast(bf16x8, v8);
+}
+
+template <int MASK, int N>
+__device__ inline void sched()
+{
+    __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
+}
 
 // Asks the scheduler to issue AHEAD LDS reads first and then alternate one
 // MFMA with PER reads, so each MFMA's operands were requested several MFMAs

@@ -97,6 +97,9 @@ typedef enum {
  *          the head_dim stride must be 1.  All three must be multiples of 8
  *          elements and every base pointer 16-byte aligned (128-bit rows, as
  *          the sm90 backward page's __call__ requires of its strides).
+ *          The row strides of q and dout must lie in [head_dim, 2^24):
+ *          rows may not overlap (FA_ERR_INVALID_ARG) and a 64-row query
+ *          tile must be addressable with 32-bit offsets (FA_ERR_UNSUPPORTED).
  *          lse_stride[0] = batch/sequence stride, lse_stride[1] = head stride,
  *          row stride 1.
  *

@@ -134,6 +134,7 @@ def test_valid_args_pass_validation():
     ({"lse": 0}, fa.FA_ERR_INVALID_ARG),
     ({"dk": BASE + 8}, fa.FA_ERR_INVALID_ARG),            # misaligned
     ({"q_stride": (256 * 8 * 128, 8 * 128 + 4, 128)}, fa.FA_ERR_INVALID_ARG),
+    ({"do_stride": (256 * 64, 64, 128 * 256)}, fa.FA_ERR_INVALID_ARG),   # rows overlap
     ({"batch": -1}, fa.FA_ERR_INVALID_ARG),
     ({"head_dim": 0}, fa.FA_ERR_INVALID_ARG),
     ({"causal": 2}, fa.FA_ERR_INVALID_ARG),
