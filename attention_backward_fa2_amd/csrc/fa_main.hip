@@ -43,6 +43,7 @@
 // the k-steps over rows 32-63.
 #include <climits>
 #include <type_traits>
+#include <utility>
 
 #include "fa_mfma.h"
 
@@ -50,6 +51,19 @@ namespace fa {
 
 template <int V>
 using IC = std::integral_constant<int, V>;
+
+template <typename F, int... I>
+__device__ inline void static_for_impl(F &f, std::integer_sequence<int, I...>)
+{
+    (f(IC<I>{}), ...);
+}
+
+// f(IC<0>), f(IC<1>), ..., f(IC<N-1>), fully unrolled.
+template <int N, typename F>
+__device__ inline void static_for(F &&f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Query-side tile geometry in LDS.
 template <int DP>
@@ -62,16 +76,22 @@ struct QTile {
     static constexpr int RPL = 1024 / PB;           // rows per wave load
 };
 
+// One query tile in LDS: Q and dO in the swizzled layout, lse2, rowdot.
 template <int DP>
+struct __attribute__((aligned(16))) QBuf {
+    uint8_t q[QTile<DP>::BYTES];
+    uint8_t dO[QTile<DP>::BYTES];
+    float lse2[kQTile];
+    float rowdot[kQTile];
+};
+
+template <int DP, int NBUF>
 struct __attribute__((aligned(16))) TileSmem {
-    uint8_t q[2][QTile<DP>::BYTES];
-    uint8_t dO[2][QTile<DP>::BYTES];
-    float lse2[2][kQTile];
-    float rowdot[2][kQTile];
+    QBuf<DP> buf[NBUF];
 };
 
 template <int DP>
-struct __attribute__((aligned(16))) FusedSmem : TileSmem<DP> {
+struct __attribute__((aligned(16))) FusedSmem : TileSmem<DP, 2> {
     static constexpr int RQ = DP + 16;       // pitch of k (elements)
     static constexpr int RD = kQTile + 16;   // pitch of dS^T
     uint16_t dsT[2][kKTile * RD];
@@ -81,34 +101,34 @@ struct __attribute__((aligned(16))) FusedSmem : TileSmem<DP> {
 // P = exp2(S*scale*log2e - lse2) and dS = P (dP - rowdot) for query rows
 // 32*mb .. 32*mb+31 of the tile (one accumulator block per product), as
 // bf16 B operands pb[0..1] / dsb[0..1] of the k-steps over those rows, and
-// (fused mode) the lane's dS^T row segment to LDS.  MASK: tile row qi sees
-// this lane's key iff keyok && qi >= lim.
-template <bool MASK, bool WRITE_DS>
+// (fused mode) the lane's dS^T row segment to LDS.  Accumulator rows
+// 4*r4 .. 4*r4+3 are tile rows 32*mb + 8*r4 + 4*g2 + t (t = 0..3) and
+// elements 4*(r4&1) .. +3 of operand r4/2.  l2s, rds and dsT_row already
+// point at row 4*g2; the element is kept iff 32*mb + 8*r4 + t >= limv
+// (visibility of the lane's key, folded into one threshold per tile).
+template <bool WRITE_DS>
 __device__ inline void pointwise_half(const f32x16 &s, const f32x16 &dp, bf16x8 *pb, bf16x8 *dsb,
                                       uint16_t *dsT_row, const float *l2s, const float *rds,
-                                      float scale_log2, int g2, int mb, int lim, bool keyok)
+                                      float scale_log2, int mb, int limv)
 {
-    // Accumulator rows 4*r4 .. 4*r4+3 are tile rows qi0 .. qi0+3 and
-    // elements 4*(r4&1) .. +3 of operand r4/2.
     bf16x4 ph[4], dh[4];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-        const int qi0 = 32 * mb + 8 * r4 + 4 * g2;
-        const f32x4 l2v = *reinterpret_cast<const f32x4 *>(l2s + qi0);
-        const f32x4 rdv = *reinterpret_cast<const f32x4 *>(rds + qi0);
+        const int qc = 32 * mb + 8 * r4;
+        const f32x4 l2v = *reinterpret_cast<const f32x4 *>(l2s + qc);
+        const f32x4 rdv = *reinterpret_cast<const f32x4 *>(rds + qc);
         f32x4 pv, dv;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             float e = __builtin_amdgcn_exp2f(s[4 * r4 + t] * scale_log2 - l2v[t]);
-            if constexpr (MASK)
-                e = (keyok && qi0 + t >= lim) ? e : 0.f;
+            e = qc + t >= limv ? e : 0.f;
             pv[t] = e;
             dv[t] = e * (dp[4 * r4 + t] - rdv[t]);
         }
         ph[r4] = to_bf16(pv);
         dh[r4] = to_bf16(dv);
         if constexpr (WRITE_DS)
-            *reinterpret_cast<bf16x4 *>(dsT_row + qi0) = dh[r4];
+            *reinterpret_cast<bf16x4 *>(dsT_row + qc) = dh[r4];
     }
     pb[0] = concat(ph[0], ph[1]);
     pb[1] = concat(ph[2], ph[3]);
@@ -237,7 +257,10 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
     constexpr int KS = DP / 16;       // MFMA k-steps over the head dim
     constexpr int DB = DP / 32;       // 32-wide blocks of the head dim
     using L = QTile<DP>;
-    using Smem = std::conditional_t<FUSED, FusedSmem<DP>, TileSmem<DP>>;
+    // Query-tile buffers in flight: three (loads run two tiles ahead) unless
+    // the fused mode's dS^T and K tiles leave LDS room for only two.
+    constexpr int NBUF = FUSED ? 2 : 3;
+    using Smem = std::conditional_t<FUSED, FusedSmem<DP>, TileSmem<DP, NBUF>>;
     __shared__ Smem sm;
 
     const int tid = threadIdx.x;
@@ -296,6 +319,10 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             if constexpr (FUSED)
                 *reinterpret_cast<u32x4 *>(&sm.k[key_local * FusedSmem<DP>::RQ + d0]) = kv;
         }
+        // Land them before the tile loop: the loop's own loads are not
+        // tracked by the compiler, so a wait for these inside the loop
+        // would also wait for the query-tile prefetch.
+        wait_loads<0>();
     }
 
     f32x16 dk_acc[DB], dv_acc[DB];
@@ -321,29 +348,41 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
 #pragma unroll
         for (int i = 0; i < L::PERW; ++i) {
             const int pr = (w * L::PERW + i) * L::RPL + lane / L::PCH;
-            const int c = (lane % L::PCH) ^ swz(pr);
+            const int c = (lane % L::PCH) ^ swz<L::PCH>(pr);
             const bool ok = c * 8 < p.D;
             voq[i] = ok ? (uint32_t)(pr * (int)p.q_ss * 2 + c * 16) : kOutOfRange;
             vod[i] = ok ? (uint32_t)(pr * (int)p.do_ss * 2 + c * 16) : kOutOfRange;
         }
-        // LDS byte offsets (within a tile) of this lane's operand reads:
-        //  gq[k4]: 16-byte read of row l32, tile chunk 2*ks + g2 (ks % 4 = k4;
-        //          + 128 bytes per 4 k-steps, + 32 rows per query block);
-        //  tq[x]:  transposing read of rows 4*g2 + rr (+ 16 per k-step, + 8
-        //          for the second half), tile chunk 4*x + 2*h16 + b1 (+ 128
-        //          bytes per two head-dim blocks), 8-byte half c16 & 1.
-        int gq[4], tq[2];
+
+        // LDS byte offsets of this lane's operand reads in the current
+        // buffer (the swizzle reaches every bit of the chunk index, so there
+        // is one offset per k-step / head-dim block; dO is BYTES further):
+        //  gq[ks]:    16-byte read of Q row l32, tile chunk 2*ks + g2 (+ 32
+        //             rows per query block);
+        //  tq[db][h]: transposing read of rows 4*g2 + rr + 8*h (+ 16 rows per
+        //             k-step), tile chunk 4*db + 2*h16 + b1, 8-byte half
+        //             c16 & 1;
+        //  rv0:       lse2 / rowdot of row 4*g2.
+        // All move to the next buffer (cyclically) after each tile.
+        constexpr int BUFB = (int)sizeof(QBuf<DP>);
+        int gq[KS], tq[DB][2], rv0;
         {
-            const int sw = swz(l32);
+            const int sw = swz<L::PCH>(l32);
 #pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4)
-                gq[k4] = l32 * L::PB + (((2 * k4 + g2) ^ sw) << 4);
+            for (int ks = 0; ks < KS; ++ks)
+                gq[ks] = l32 * L::PB + (((2 * ks + g2) ^ sw) << 4);
             const int c16 = lane & 15, rr = c16 >> 2, h16 = (lane >> 4) & 1, b1 = (c16 >> 1) & 1;
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
-                tq[x] = (4 * g2 + rr) * L::PB + (((4 * x + 2 * h16 + b1) ^ (2 * rr + g2)) << 4) +
-                        (c16 & 1) * 8;
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int row = 4 * g2 + rr + 8 * hf;
+                    tq[db][hf] = row * L::PB +
+                                 (((4 * db + 2 * h16 + b1) ^ swz<L::PCH>(row)) << 4) + (c16 & 1) * 8;
+                }
+            rv0 = 2 * L::BYTES + 16 * g2;
         }
+        const uint8_t *lds = reinterpret_cast<const uint8_t *>(&sm.buf[0]);
 
         // Query tile of step `it`: heads of the group in turn; within a head
         // the last query tile first, so the workgroups of one (batch, KV
@@ -356,137 +395,253 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             return ascending ? m_begin + r : m_end - 1 - r;
         };
 
-        // Issue the loads of query tile `it` into LDS buffer BF.
-        auto issue = [&](int it, auto bufc) {
-            constexpr int BF = decltype(bufc)::value;
-            const int hh = it / nm, m = tile_m(it);
+        // Issue the loads of query tile `it` into LDS buffer bf; past the
+        // last tile the loads are issued with an empty bound (no memory
+        // access, zeros written) so that the tile loop has no branch.  All
+        // address arithmetic is scalar and branch-free: row q0 of head h
+        // starts at base + h * head stride + q0 * row stride.
+        const uint16_t *q_base = p.q + row_offset(p, b, si.tok_q, 0, p.q_sb, p.q_ss);
+        const uint16_t *do_base = p.dout + row_offset(p, b, si.tok_q, 0, p.do_sb, p.do_ss);
+        const float *rowvec_base = ((w & 1) ? p.rowdot : p.lse2) + si.ws_row;   // see below
+        auto issue = [&](int it, int bf) {
+            const bool real = it < total;
+            const int itc = real ? it : total - 1;
+            const int hh = itc / nm, m = tile_m(itc);
             const int h = hk * p.G + hh;
             const int q0 = m * kQTile;
-            const int rv = min(kQTile, Lq - q0);
-            const uint16_t *qb = p.q + h * p.q_sh + row_offset(p, b, si.tok_q, q0, p.q_sb, p.q_ss);
-            const uint16_t *db =
-                p.dout + h * p.do_sh + row_offset(p, b, si.tok_q, q0, p.do_sb, p.do_ss);
-            const auto rq = make_rsrc(qb, (uint32_t)((rv - 1) * (int)p.q_ss * 2 + p.D * 2));
-            const auto rd = make_rsrc(db, (uint32_t)((rv - 1) * (int)p.do_ss * 2 + p.D * 2));
+            const int rv = real ? min(kQTile, Lq - q0) : 0;
+            const uint16_t *qb = q_base + h * p.q_sh + (int64_t)q0 * p.q_ss;
+            const uint16_t *db = do_base + h * p.do_sh + (int64_t)q0 * p.do_ss;
+            const uint32_t nq = rv ? (uint32_t)((rv - 1) * (int)p.q_ss * 2 + p.D * 2) : 0u;
+            const uint32_t nd = rv ? (uint32_t)((rv - 1) * (int)p.do_ss * 2 + p.D * 2) : 0u;
+            const auto rq = make_rsrc(qb, nq);
+            const auto rd = make_rsrc(db, nd);
+            QBuf<DP> &qbuf = sm.buf[bf];
 #pragma unroll
             for (int i = 0; i < L::PERW; ++i) {
                 const int ld = (w * L::PERW + i) * 1024;
-                load16_to_lds(rq, sm.q[BF] + ld, voq[i]);
-                load16_to_lds(rd, sm.dO[BF] + ld, vod[i]);
+                load16_to_lds(rq, qbuf.q + ld, voq[i]);
+                load16_to_lds(rd, qbuf.dO + ld, vod[i]);
             }
-            if (w < 2) {
-                const float *src = (w == 0 ? p.lse2 : p.rowdot) + (int64_t)h * p.rows + si.ws_row + q0;
-                load4_to_lds(make_rsrc(src, (uint32_t)rv * 4), w == 0 ? sm.lse2[BF] : sm.rowdot[BF],
-                               (uint32_t)lane * 4);
-            }
+            // lse2 (even waves) / rowdot (odd waves): the two waves of a kind
+            // write the same values.
+            const float *src = rowvec_base + (int64_t)h * p.rows + q0;
+            load4_to_lds(make_rsrc(src, (uint32_t)rv * 4), (w & 1) ? qbuf.rowdot : qbuf.lse2,
+                         (uint32_t)lane * 4);
         };
 
-        // One query tile from LDS buffer BF; MASKED: causal / tail masking.
-        auto body = [&](int it, auto bufc, auto maskc) {
-            constexpr int BF = decltype(bufc)::value;
-            constexpr bool MASKED = decltype(maskc)::value != 0;
-            const int q0 = tile_m(it) * kQTile;
-            const uint8_t *sq = sm.q[BF];
-            const uint8_t *sdo = sm.dO[BF];
-            const int lim = MASKED && p.causal ? key - q0 - off : INT_MIN;
-            const bool keyok = key < Lk;
-            uint16_t *dsrow = nullptr;
+        // Loads per wave per tile (each Q / dO wave load, and lse2 / rowdot).
+        constexpr int LPT = 2 * L::PERW + 1;
+#pragma unroll
+        for (int t = 0; t < NBUF - 1; ++t)
+            issue(t, t);
+        wait_loads<LPT * (NBUF - 2)>();
+        __syncthreads();
+
+        // ---- Each query tile as NSLOT MFMA slots, issued in this order: ----
+        //   S, dP  of rows 0-31 (k-steps over D)      slots 0 .. NB-1
+        //   S, dP  of rows 32-63                      NB .. 2NB-1       + P, dS of rows 0-31
+        //   dV, dK over rows 0-31 (k-steps 0, 1)      2NB .. 2NB+NG-1   + P, dS of rows 32-63
+        //   dV, dK over rows 32-63 (k-steps 2, 3)     2NB+NG .. NSLOT-1
+        // Each slot issues the LDS operand read of the slot RA ahead, its
+        // MFMA and a share of the vector work; a scheduling fence after
+        // every slot keeps this order.  Without the fused dQ, the reads run
+        // ahead across the tile boundary, and the wait for the next tile's
+        // loads, the workgroup barrier and the issue of the loads of the tile
+        // after next sit at slot BAR, in the shadow of the MFMAs (with three
+        // buffers, a buffer refilled after the barrier of tile t held tile
+        // t-1, which every wave has finished by then).
+        constexpr int NB = 2 * KS;            // S / dP MFMAs per query block
+        constexpr int NG = 4 * DB;            // dV / dK MFMAs per two k-steps
+        constexpr int NSLOT = 2 * NB + 2 * NG;
+        constexpr int RA = 8;                 // read-ahead distance (slots)
+        constexpr int BAR = 2 * NB + NG / 2;  // barrier slot (non-fused)
+        // The ring of in-flight operands continues across tiles, so its
+        // length must divide the slot count; the barrier (and the move of
+        // the 16-byte read offsets to the next buffer) must come after the
+        // last such read and row-vector read of the tile and before the
+        // first read of the next tile.
+        static_assert(NB >= 8 && NG >= 8 && NSLOT % RA == 0, "slot plan");
+        static_assert(BAR >= 2 * NB && BAR + RA < NSLOT, "barrier slot");
+
+        // A operand of slot i of a tile (offsets of the tile's buffer).
+        auto op_read = [&](auto ic) -> bf16x8 {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (i < 2 * NB) {
+                constexpr int mb = i / NB, jj = i % NB, ks = jj >> 1;
+                return lds16b(lds + gq[ks] + 32 * mb * L::PB + ((jj & 1) ? L::BYTES : 0));
+            } else {
+                constexpr int jj = (i - 2 * NB) % NG, kk = 2 * ((i - 2 * NB) / NG) + jj / (2 * DB);
+                constexpr int db = (jj % (2 * DB)) >> 1;
+                constexpr int base = (jj & 1) ? 0 : L::BYTES;   // even: dO^T (dV), odd: Q^T (dK)
+                return tr_pair(lds + base + tq[db][0] + 16 * kk * L::PB,
+                               lds + base + tq[db][1] + 16 * kk * L::PB);
+            }
+        };
+        // dK / dV stay in accumulation registers for the whole loop
+        // (without these pins the allocator parks some of them in ordinary
+        // registers during the S / dP products and copies them back every
+        // tile).
+        auto pin_acc = [&]() {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                asm volatile("" : "+a"(dk_acc[db]), "+a"(dv_acc[db]));
+        };
+
+        bf16x8 ring[RA];
+        static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
+
+        int cur = 0;
+        for (int it = 0; it < total; ++it) {
             if constexpr (FUSED)
-                dsrow = &sm.dsT[BF][key_local * FusedSmem<DP>::RD];
-
-            // S = Q K^T and dP = dO V^T, query rows 0-31 then 32-63.
-            f32x16 s[2], dp[2];
-            const f32x16 z = {};
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const int o = gq[ks & 3] + 32 * mb * L::PB + 128 * (ks >> 2);
-                    s[mb] = mfma32(lds16b(sq + o), kf[ks], ks == 0 ? z : s[mb]);
-                    dp[mb] = mfma32(lds16b(sdo + o), vf[ks], ks == 0 ? z : dp[mb]);
-                }
-            }
-            bf16x8 pb[4], dsb[4];
-            pointwise_half<MASKED, FUSED>(s[0], dp[0], pb, dsb, dsrow, sm.lse2[BF], sm.rowdot[BF],
-                                          p.scale_log2, g2, 0, lim, keyok);
-            // dV^T += dO^T P, dK^T += Q^T dS over k-steps kk (16 query rows each).
-            auto g35 = [&](int kk) {
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const int o0 = tq[db & 1] + 16 * kk * L::PB + 128 * (db >> 1);
-                    const int o1 = o0 + 8 * L::PB;
-                    dv_acc[db] = mfma32(tr_pair(sdo + o0, sdo + o1), pb[kk], dv_acc[db]);
-                    dk_acc[db] = mfma32(tr_pair(sq + o0, sq + o1), dsb[kk], dk_acc[db]);
-                }
-            };
-            g35(0);
-            g35(1);
-            pointwise_half<MASKED, FUSED>(s[1], dp[1], pb + 2, dsb + 2, dsrow, sm.lse2[BF],
-                                          sm.rowdot[BF], p.scale_log2, g2, 1, lim, keyok);
-            g35(2);
-            g35(3);
-
-            // Instruction order: reads run ahead of the MFMAs that use them;
-            // the pointwise math of each half fills the gaps between the
-            // MFMAs of the next product block.
-            constexpr int NB = 2 * KS;       // MFMAs per query block of S / dP
-            constexpr int NG = 4 * DB;       // MFMAs per two k-steps of dV / dK
-            sched<kSchedDsRead, 6>();
-#pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                sched<kSchedMfma, 1>();
-                sched<kSchedDsRead, 1>();
-            }
-#pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                sched<kSchedMfma, 1>();
-                sched<kSchedDsRead, 1>();
-                sched<kSchedValu, 5>();
-            }
-#pragma unroll
-            for (int i = 0; i < NG; ++i) {
-                sched<kSchedMfma, 1>();
-                sched<kSchedDsRead, 2>();
-                sched<kSchedValu, 5>();
-            }
-#pragma unroll
-            for (int i = 0; i < NG; ++i) {
-                sched<kSchedMfma, 1>();
-                sched<kSchedDsRead, 2>();
-            }
-        };
-
-        // One pipeline step: loads of the next tile, this tile, barrier.
-        auto step = [&](int it, auto bufc) {
-            constexpr int BF = decltype(bufc)::value;
-            if (it + 1 < total)
-                issue(it + 1, IC<1 - BF>{});
+                issue(it + 1, cur ^ 1);
             const int m = tile_m(it);
             const int q0 = m * kQTile;
-            const bool need_mask =
-                (n0 + kKTile > Lk) || (p.causal && (n0 + kKTile - 1 > q0 + off));
-            if (need_mask)
-                body(it, bufc, IC<1>{});
-            else
-                body(it, bufc, IC<0>{});
-            wait_loads();
-            __syncthreads();   // next tile in LDS; buffer BF free (fused: dS^T[BF] complete)
+            // Visibility threshold of this lane's key over tile rows
+            // 4*g2 + (32*mb + 8*r4 + t): keys past the end see nothing;
+            // causal: key <= q0 + row + off.
+            const int limv = key >= Lk ? INT_MAX : (p.causal ? key - q0 - off - 4 * g2 : INT_MIN);
+            uint16_t *dsrow = nullptr;
+            if constexpr (FUSED)
+                dsrow = &sm.dsT[cur][key_local * FusedSmem<DP>::RD + 4 * g2];
+            const float *l2s = reinterpret_cast<const float *>(lds + rv0);
+            const float *rds = l2s + kQTile;
+            // offset step to the next tile's buffer
+            const int delta = cur == NBUF - 1 ? -(NBUF - 1) * BUFB : BUFB;
+
+            f32x16 s[2], dp[2];
+            const f32x16 z = {};
+            bf16x8 pb[4], dsb[4];
+            bf16x4 ph[4], dh[4];
+            f32x4 l2v[4], rdv[4];
+            f32x4 pv, dv;
+
+            // element e (0..15) of query block mb: exp, mask, dS; packs a
+            // 4-row group into bf16 after its last element.
+            auto pw_elem = [&](auto mbc, auto ec) {
+                constexpr int mb = decltype(mbc)::value, e = decltype(ec)::value;
+                constexpr int r4 = e >> 2, t = e & 3;
+                constexpr int qc = 32 * mb + 8 * r4;
+                float x = __builtin_amdgcn_exp2f(s[mb][e] * p.scale_log2 - l2v[r4][t]);
+                x = qc + t >= limv ? x : 0.f;
+                pv[t] = x;
+                dv[t] = x * (dp[mb][e] - rdv[r4][t]);
+                if constexpr (t == 3) {
+                    ph[r4] = to_bf16(pv);
+                    dh[r4] = to_bf16(dv);
+                    if constexpr (FUSED)
+                        *reinterpret_cast<bf16x4 *>(dsrow + qc) = dh[r4];
+                    if constexpr ((r4 & 1) != 0) {
+                        pb[2 * mb + (r4 >> 1)] = concat(ph[r4 - 1], ph[r4]);
+                        dsb[2 * mb + (r4 >> 1)] = concat(dh[r4 - 1], dh[r4]);
+                    }
+                }
+            };
+
+            pin_acc();
+            static_for<NSLOT>([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                const bf16x8 a = ring[i % RA];
+                if constexpr (i + RA < NSLOT)
+                    ring[i % RA] = op_read(IC<i + RA>{});
+                else if constexpr (!FUSED)
+                    ring[i % RA] = op_read(IC<i + RA - NSLOT>{});   // next tile
+                // row vectors of block 0, read during the slots before its
+                // pointwise work starts
+                if constexpr (i >= NB / 2 && i < NB / 2 + 4) {
+                    constexpr int r4 = i - NB / 2;
+                    l2v[r4] = *reinterpret_cast<const f32x4 *>(l2s + 8 * r4);
+                    rdv[r4] = *reinterpret_cast<const f32x4 *>(rds + 8 * r4);
+                }
+                if constexpr (i < 2 * NB) {
+                    constexpr int mb = i / NB, jj = i % NB, ks = jj >> 1;
+                    if constexpr ((jj & 1) != 0)
+                        dp[mb] = mfma32(a, vf[ks], ks == 0 ? z : dp[mb]);
+                    else
+                        s[mb] = mfma32(a, kf[ks], ks == 0 ? z : s[mb]);
+                } else {
+                    constexpr int jj = (i - 2 * NB) % NG;
+                    constexpr int kk = 2 * ((i - 2 * NB) / NG) + jj / (2 * DB);
+                    constexpr int db = (jj % (2 * DB)) >> 1;
+                    if constexpr ((jj & 1) != 0)
+                        dk_acc[db] = mfma32(a, dsb[kk], dk_acc[db]);
+                    else
+                        dv_acc[db] = mfma32(a, pb[kk], dv_acc[db]);
+                }
+                // vector work: the 16 elements of P, dS of block 0 spread over
+                // slots NB .. 2NB-1 (the row vectors of block 1 are read in
+                // the last four of them), of block 1 over 2NB .. 2NB+NG-1
+                if constexpr (i >= NB && i < 2 * NB) {
+                    constexpr int u = i - NB;
+                    static_for<16 * (u + 1) / NB - 16 * u / NB>(
+                        [&](auto ec) { pw_elem(IC<0>{}, IC<16 * u / NB + decltype(ec)::value>{}); });
+                    if constexpr (u >= NB - 4) {
+                        constexpr int r4 = u - (NB - 4);
+                        l2v[r4] = *reinterpret_cast<const f32x4 *>(l2s + 32 + 8 * r4);
+                        rdv[r4] = *reinterpret_cast<const f32x4 *>(rds + 32 + 8 * r4);
+                    }
+                }
+                if constexpr (i >= 2 * NB && i < 2 * NB + NG) {
+                    constexpr int u = i - 2 * NB;
+                    static_for<16 * (u + 1) / NG - 16 * u / NG>(
+                        [&](auto ec) { pw_elem(IC<1>{}, IC<16 * u / NG + decltype(ec)::value>{}); });
+                }
+                if constexpr (i == NB || i == 2 * NB)
+                    pin_acc();
+                if constexpr (!FUSED && i == BAR) {
+                    // The 16-byte operand reads of this tile and its row
+                    // vectors are all issued: move them to the next buffer.
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        gq[ks] += delta;
+                    rv0 += delta;
+                    // The only loads in flight are the next tile's (issued
+                    // at this slot of the previous tile).
+                    // (A bare barrier: the LDS reads still in flight read
+                    // this tile's buffer, which no load issued after the
+                    // barrier touches.)
+                    wait_loads<0>();
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                    issue(it + NBUF - 1, cur == 0 ? NBUF - 1 : cur - 1);
+                }
+                if constexpr (!FUSED && i == NSLOT - RA - 1) {
+                    // last transposing read of this tile issued
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        tq[db][0] += delta;
+                        tq[db][1] += delta;
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            pin_acc();
+
             if constexpr (FUSED) {
+                // Next tile's buffer.
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    gq[ks] += delta;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    tq[db][0] += delta;
+                    tq[db][1] += delta;
+                }
+                rv0 += delta;
+                wait_loads<0>();
+                __syncthreads();   // next tile in LDS; dS^T[cur] complete
                 const int h = hk * p.G + it / nm;
                 const int rows_valid = min(kQTile, Lq - q0);
-                dq_partial<DP>(p, sm, BF, w, lane, l32, g2, tid, b, h, m, j, q0, rows_valid, Lq,
+                dq_partial<DP>(p, sm, cur, w, lane, l32, g2, tid, b, h, m, j, q0, rows_valid, Lq,
                                off, nt_b, si.ws_row);
+                static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
             }
-        };
-
-        issue(0, IC<0>{});
-        wait_loads();
-        __syncthreads();
-        for (int it = 0; it < total; it += 2) {
-            step(it, IC<0>{});
-            if (it + 1 < total)
-                step(it + 1, IC<1>{});
+            cur = cur == NBUF - 1 ? 0 : cur + 1;
         }
+        // The last iterations issued loads past the final tile (empty bound,
+        // zeros into LDS); let them land before the workgroup's LDS is
+        // released.
+        wait_loads<0>();
     }
 
     // ---- epilogue: dK = scale * acc, dV = acc, bf16, keys < Lk, d < D ----

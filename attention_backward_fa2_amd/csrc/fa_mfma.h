@@ -99,41 +99,73 @@ constexpr int kSchedDsWrite = 0x200;
 // Each wave load of W bytes per lane writes 64 * W contiguous bytes of LDS
 // (lane l at lds + l * W), so a tile's LDS layout is chosen through the
 // global offset each lane loads from.
+//
+// The loads are written as inline assembly: the compiler then does not
+// track them, and does not make LDS reads that it cannot prove disjoint from
+// them (the transposing reads) wait for them.  Their completion is awaited
+// explicitly with wait_loads() before the workgroup barrier that publishes
+// the buffer; compiler-issued memory waits only become stricter through
+// them.
 typedef __attribute__((address_space(3))) void lds_void;
-constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit elements
+typedef uint32_t u32x4_rsrc __attribute__((ext_vector_type(4)));
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit elements
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+__device__ inline u32x4_rsrc make_rsrc(const void *base, uint32_t bytes)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    u32x4_rsrc r;
+    r[0] = (uint32_t)a;
+    r[1] = (uint32_t)(a >> 32) & 0xffffu;    // stride 0, no swizzle
+    r[2] = bytes;
+    r[3] = kRsrcWord3;
+    return r;
 }
 
-__device__ inline void load16_to_lds(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voffset)
+__device__ inline uint32_t lds_addr(const void *p)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voffset, 0, 0, 0);
+    return (uint32_t)reinterpret_cast<uintptr_t>((const lds_void *)p);
 }
 
-__device__ inline void load4_to_lds(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voffset)
+__device__ inline void load16_to_lds(u32x4_rsrc r, void *lds, uint32_t voffset)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 4, voffset, 0, 0, 0);
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset), "s"(r),
+                 "{m0}"(lds_addr(lds))
+                 : "memory");
 }
 
-// Wait until every load this wave issued (including loads into LDS) landed.
+__device__ inline void load4_to_lds(u32x4_rsrc r, void *lds, uint32_t voffset)
+{
+    asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voffset), "s"(r),
+                 "{m0}"(lds_addr(lds))
+                 : "memory");
+}
+
+// Wait until at most N of the memory loads this wave issued (including loads
+// into LDS) are still in flight; they complete in issue order.
+template <int N = 0>
 __device__ inline void wait_loads()
 {
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt unchanged
+    static_assert(N >= 0 && N < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);   // vmcnt(N); expcnt, lgkmcnt unchanged
 }
 
 // ---- Swizzled row-major tiles in LDS ----
 // Rows of 16-byte chunks with no padding; chunk c of row r is stored at
-// chunk position c ^ swz(r).  swz is a bijection on r % 8, so eight
-// consecutive rows read at the same chunk (16-byte operand reads) hit eight
-// different 16-byte bank groups, and swz(r) >> 1 differs between the four
-// rows of an aligned group of four, so the two chunks that four such rows
-// supply to one transposing read also land in eight different bank groups.
+// chunk position c ^ swz<PCH>(r) (PCH = chunks per row, 16 or 8).  The LDS
+// serves 256 bytes (64 banks) per clock: a 16-byte read by 16 lanes or an
+// 8-byte read by 32 lanes.  The swizzle makes both conflict-free for the
+// operand reads of the tile kernels:
+//  - 16 consecutive rows read at one chunk (row-major operand reads): swz
+//    is a bijection on r % 16 (PCH = 16) or, for the 8 rows of one parity
+//    that share a 256-byte bank line, on r / 2 % 8 (PCH = 8);
+//  - transposing reads, 4 consecutive rows (aligned) x 4 consecutive
+//    chunks (aligned) per 32 lanes: swz differs in bits 2-3 between rows
+//    of one bank line, so the 16 chunks land in distinct bank groups.
+template <int PCH>
 __device__ __host__ constexpr int swz(int r)
 {
-    return 2 * (r & 3) + ((r >> 2) & 1);
+    return PCH == 16 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
 __device__ inline bf16x8 lds16b(const uint8_t *p)
