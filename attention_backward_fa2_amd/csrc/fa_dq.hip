@@ -15,14 +15,25 @@
 // owns rows 32w .. 32w+31, whose Q and dO rows stay in registers as the B
 // operands of
 //     S^T  = K Q^T        dP^T = V dO^T        (64 keys x 32 rows per wave)
-// for each 64-key tile streamed through double-buffered LDS.  The
-// accumulator of S^T holds one query row and 16 keys per lane, so dS (in
-// bf16) is directly the A operand of dQ = dS K with the key index permuted
-// as described in fa_mfma.h; K then enters as a B operand through
-// transposing LDS reads.  dQ (32 x D per wave) accumulates in registers over
-// all key tiles and is scaled and stored once.
+// for each 64-key tile.  The accumulator of S^T holds one query row and 16
+// keys per lane, so lse2 and rowdot are one register each, and dS (in bf16)
+// is directly the A operand of dQ = dS K with the key index permuted as
+// described in fa_mfma.h; K then enters as a B operand through transposing
+// LDS reads.  dQ (32 x D per wave) accumulates in registers over all key
+// tiles and is scaled and stored once.
 //
-// LDS (D_pad = 128): K and V tiles, double buffered: 4 x 18 KB = 72 KB.
+// K and V tiles are loaded by buffer loads straight into the swizzled LDS
+// layout of fa_mfma.h (zero fill of keys past the end and of padded
+// head-dim columns by the buffer bound), three buffers deep.  Each key tile
+// runs as a fixed sequence of MFMA slots (the same scheme as the key-tile
+// kernel): S^T, dP^T of keys 0-31, of keys 32-63 alongside the pointwise
+// math of keys 0-31, the dQ k-steps over keys 0-31 alongside the pointwise
+// math of keys 32-63, the dQ k-steps over keys 32-63.  Operand reads run a
+// fixed number of slots ahead, across tile boundaries; the wait for the next
+// tile, the workgroup barrier and the loads of the tile after next sit at
+// one slot of the dQ phase.
+//
+// LDS (D_pad = 128): 3 x (K, V) x 16 KB = 96 KB.
 #include "fa_mfma.h"
 
 namespace fa {
@@ -31,10 +42,14 @@ constexpr int kDqRows = 128;    // query rows per workgroup
 constexpr int kDqKeys = 64;     // keys per streamed tile
 
 template <int DP>
+struct __attribute__((aligned(16))) KVBuf {
+    uint8_t k[Tile64<DP>::BYTES];
+    uint8_t v[Tile64<DP>::BYTES];
+};
+
+template <int DP>
 struct __attribute__((aligned(16))) DqSmem {
-    static constexpr int RK = DP + 16;   // pitch of the K / V tiles (elements)
-    uint16_t k[2][kDqKeys * RK];
-    uint16_t v[2][kDqKeys * RK];
+    KVBuf<DP> buf[3];
 };
 
 template <int DP>
@@ -42,14 +57,13 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_dq_kernel(Params p)
 {
     constexpr int KS = DP / 16;                  // k-steps over the head dim
     constexpr int DB = DP / 32;                  // 32-wide head-dim blocks
-    constexpr int RK = DqSmem<DP>::RK;
-    constexpr int CPR = DP / 8;                  // 16-byte chunks per row
-    constexpr int NCH = kDqKeys * CPR / kThreads;   // chunks per thread per tile
-    static_assert(kDqKeys * CPR % kThreads == 0, "tile load must divide evenly");
+    constexpr int NBUF = 3;
+    using L = Tile64<DP>;
     __shared__ DqSmem<DP> sm;
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, g2 = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, g2 = lane >> 5;
 
     // Workgroup -> (query tile, batch, KV head, head in group).  Under the
     // causal mask the last query tiles see the most keys, so they come
@@ -99,6 +113,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_dq_kernel(Params p)
         l2 = p.lse2[wr];
         rd = p.rowdot[wr];
     }
+    wait_loads();   // land them before the tile loop
 
     f32x16 acc[DB];
 #pragma unroll
@@ -110,108 +125,189 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_dq_kernel(Params p)
     int nkt = (Lk + kDqKeys - 1) / kDqKeys;
     if (p.causal)
         nkt = min(nkt, max(0, (q_last + off + kDqKeys) / kDqKeys));
+    // Visible keys of this lane's row: key <= klim.
+    const int klim = qok ? (p.causal ? min(Lk - 1, qrow + off) : Lk - 1) : -1;
 
     if (nkt > 0) {
-        // Prefetch registers for one K/V tile (clamped rows, masked at
-        // staging -- see the key-tile kernel for why).
-        u32x4 pk[NCH], pv[NCH];
-        int kv_valid = kDqKeys;
-        auto prefetch = [&](int t) {
+        // Global byte offsets of the 16-byte chunk each lane loads for wave
+        // load i (LDS row pr holds tile chunk (lane % PCH) ^ swz(pr)).
+        uint32_t vok[L::PERW], vov[L::PERW];
+#pragma unroll
+        for (int i = 0; i < L::PERW; ++i) {
+            const int pr = (w * L::PERW + i) * L::RPL + lane / L::PCH;
+            const int c = (lane % L::PCH) ^ swz<L::PCH>(pr);
+            const bool ok = c * 8 < p.D;
+            vok[i] = ok ? (uint32_t)(pr * (int)p.k_ss * 2 + c * 16) : kOutOfRange;
+            vov[i] = ok ? (uint32_t)(pr * (int)p.v_ss * 2 + c * 16) : kOutOfRange;
+        }
+        // LDS byte offsets of this lane's operand reads in the current
+        // buffer (V is BYTES further):
+        //  gq[ks]:    16-byte read of K / V row l32, tile chunk 2*ks + g2 (+ 32
+        //             rows per key block);
+        //  tq[db][h]: transposing read of K rows 4*g2 + rr + 8*h (+ 16 rows per
+        //             k-step), tile chunk 4*db + 2*h16 + b1, 8-byte half c16 & 1.
+        constexpr int BUFB = (int)sizeof(KVBuf<DP>);
+        int gq[KS], tq[DB][2];
+        {
+            const int sw = swz<L::PCH>(l32);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                gq[ks] = l32 * L::PB + (((2 * ks + g2) ^ sw) << 4);
+            const int c16 = lane & 15, rr = c16 >> 2, h16 = (lane >> 4) & 1, b1 = (c16 >> 1) & 1;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int row = 4 * g2 + rr + 8 * hf;
+                    tq[db][hf] = row * L::PB +
+                                 (((4 * db + 2 * h16 + b1) ^ swz<L::PCH>(row)) << 4) + (c16 & 1) * 8;
+                }
+        }
+        const uint8_t *lds = reinterpret_cast<const uint8_t *>(&sm.buf[0]);
+
+        // Issue the loads of key tile t into buffer bf (past the last tile:
+        // empty bound, zeros, no memory access).
+        const uint16_t *k_base = p.k + hk * p.k_sh + row_offset(p, b, si.tok_k, 0, p.k_sb, p.k_ss);
+        const uint16_t *v_base = p.v + hk * p.v_sh + row_offset(p, b, si.tok_k, 0, p.v_sb, p.v_ss);
+        auto issue = [&](int t, int bf) {
             const int n0 = t * kDqKeys;
-            kv_valid = min(kDqKeys, Lk - n0);
-            const uint16_t *kb = p.k + hk * p.k_sh + row_offset(p, b, si.tok_k, n0, p.k_sb, p.k_ss);
-            const uint16_t *vb = p.v + hk * p.v_sh + row_offset(p, b, si.tok_k, n0, p.v_sb, p.v_ss);
+            const int kv = t < nkt ? min(kDqKeys, Lk - n0) : 0;
+            const int n0c = t < nkt ? n0 : 0;
+            const uint32_t nk = kv ? (uint32_t)((kv - 1) * (int)p.k_ss * 2 + p.D * 2) : 0u;
+            const uint32_t nv = kv ? (uint32_t)((kv - 1) * (int)p.v_ss * 2 + p.D * 2) : 0u;
+            const auto rk = make_rsrc(k_base + (int64_t)n0c * p.k_ss, nk);
+            const auto rv = make_rsrc(v_base + (int64_t)n0c * p.v_ss, nv);
+            KVBuf<DP> &kb = sm.buf[bf];
 #pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                const int idx = tid + c * kThreads;
-                const int r = min(idx / CPR, kv_valid - 1);
-                const int col = (idx % CPR) * 8 < p.D ? (idx % CPR) * 8 : 0;
-                pk[c] = *reinterpret_cast<const u32x4 *>(kb + r * (int)p.k_ss + col);
-                pv[c] = *reinterpret_cast<const u32x4 *>(vb + r * (int)p.v_ss + col);
-            }
-        };
-        auto stage = [&](int buf) {
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                const int idx = tid + c * kThreads;
-                const uint32_t keep =
-                    (idx / CPR < kv_valid && (idx % CPR) * 8 < p.D) ? ~0u : 0u;
-                const int o = (idx / CPR) * RK + (idx % CPR) * 8;
-                *reinterpret_cast<u32x4 *>(&sm.k[buf][o]) = pk[c] & keep;
-                *reinterpret_cast<u32x4 *>(&sm.v[buf][o]) = pv[c] & keep;
+            for (int i = 0; i < L::PERW; ++i) {
+                const int ld = (w * L::PERW + i) * 1024;
+                load16_to_lds(rk, kb.k + ld, vok[i]);
+                load16_to_lds(rv, kb.v + ld, vov[i]);
             }
         };
 
-        prefetch(0);
-        stage(0);
+        // ---- Each key tile as NSLOT MFMA slots, issued in this order: ----
+        //   S^T, dP^T of keys 0-31 (k-steps over D)   slots 0 .. NB-1
+        //   S^T, dP^T of keys 32-63                   NB .. 2NB-1        + dS of keys 0-31
+        //   dQ k-steps over keys 0-31                 2NB .. 2NB+NQ-1    + dS of keys 32-63
+        //   dQ k-steps over keys 32-63                2NB+NQ .. NSLOT-1
+        constexpr int NB = 2 * KS;
+        constexpr int NQ = 2 * DB;
+        constexpr int NSLOT = 2 * NB + 2 * NQ;
+        constexpr int RA = NSLOT % 8 == 0 ? 8 : 6;   // read-ahead (divides NSLOT)
+        constexpr int BAR = (2 * NB + NQ / 2 < NSLOT - RA) ? 2 * NB + NQ / 2 : NSLOT - RA - 1;
+        static_assert(NSLOT % RA == 0, "ring length must divide the slot count");
+        static_assert(BAR >= 2 * NB - RA && BAR + RA < NSLOT, "barrier slot");
+        constexpr int LPT = 2 * L::PERW;             // loads per wave per tile
+
+        auto op_read = [&](auto ic) -> bf16x8 {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (i < 2 * NB) {
+                constexpr int mb = i / NB, jj = i % NB, ks = jj >> 1;
+                return lds16b(lds + gq[ks] + 32 * mb * L::PB + ((jj & 1) ? L::BYTES : 0));
+            } else {
+                constexpr int jj = i - 2 * NB, kk = jj / DB, db = jj % DB;
+                return tr_pair(lds + tq[db][0] + 16 * kk * L::PB, lds + tq[db][1] + 16 * kk * L::PB);
+            }
+        };
+        auto pin_acc = [&]() {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                asm volatile("" : "+a"(acc[db]));
+        };
+
+        issue(0, 0);
+        issue(1, 1);
+        wait_loads<LPT>();
         __syncthreads();
+        bf16x8 ring[RA];
+        static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
 
+        int cur = 0;
         for (int t = 0; t < nkt; ++t) {
-            const int buf = t & 1;
             const int n0 = t * kDqKeys;
-            if (t + 1 < nkt)
-                prefetch(t + 1);
-            const uint16_t *sk = sm.k[buf];
-            const uint16_t *sv = sm.v[buf];
+            // element (32*mb + 8*r4 + t) of the lane's keys (+ 4*g2) is kept
+            // iff it is <= kthr
+            const int kthr = klim - n0 - 4 * g2;
+            const int delta = cur == NBUF - 1 ? -(NBUF - 1) * BUFB : BUFB;
 
-            // ---- S^T = K Q^T, dP^T = V dO^T (64 keys x 32 rows per wave) ----
             f32x16 st[2], dpt[2];
             const f32x16 z = {};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb) {
-                    const int o = (32 * mb + l32) * RK + 16 * ks + 8 * g2;
-                    st[mb] = mfma32(lds16(sk + o), qf[ks], ks == 0 ? z : st[mb]);
-                    dpt[mb] = mfma32(lds16(sv + o), of[ks], ks == 0 ? z : dpt[mb]);
-                }
-            }
-            pipeline_reads<4 * KS, 1, 8>();
-
-            // ---- P, dS; bf16 dS as A operands of dQ = dS K ----
-            // key of accumulator element r of block mb: n0 + 32 mb + 8 (r/4)
-            // + 4 g2 + r%4; visible iff key < Lk and (causal) key <= qrow + off.
-            const bool need_mask =
-                (n0 + kDqKeys > Lk) || (p.causal && (n0 + kDqKeys - 1 > q0 + off));
-            const int klim = p.causal ? min(Lk - 1, qrow + off) : Lk - 1;
-            bf16x4 dh[8];
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    f32x4 dv;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const int r = 4 * r4 + t;
-                        float e = __builtin_amdgcn_exp2f(st[mb][r] * p.scale_log2 - l2);
-                        if (need_mask) {
-                            const int key = n0 + 32 * mb + 8 * r4 + 4 * g2 + t;
-                            e = key <= klim ? e : 0.f;
-                        }
-                        dv[t] = e * (dpt[mb][r] - rd);
-                    }
-                    dh[4 * mb + r4] = to_bf16(dv);
-                }
-            }
+            bf16x4 dh[4];
             bf16x8 dsa[4];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                dsa[kk] = concat(dh[2 * kk], dh[2 * kk + 1]);
+            f32x4 dv;
 
-            // ---- dQ += dS K  (k = 64 keys; K read transposed) ----
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int r0 = 16 * kk + 4 * g2, r1 = r0 + 8;
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-                    acc[db] = mfma32(dsa[kk], frag_tr(sk, RK, r0, r1, 32 * db, lane), acc[db]);
-            }
-            pipeline_reads<4 * DB, 2, 8>();
+            auto pw_elem = [&](auto mbc, auto ec) {
+                constexpr int mb = decltype(mbc)::value, e = decltype(ec)::value;
+                constexpr int r4 = e >> 2, tt = e & 3;
+                float x = __builtin_amdgcn_exp2f(st[mb][e] * p.scale_log2 - l2);
+                x = 32 * mb + 8 * r4 + tt <= kthr ? x : 0.f;
+                dv[tt] = x * (dpt[mb][e] - rd);
+                if constexpr (tt == 3) {
+                    dh[r4] = to_bf16(dv);
+                    if constexpr ((r4 & 1) != 0)
+                        dsa[2 * mb + (r4 >> 1)] = concat(dh[r4 - 1], dh[r4]);
+                }
+            };
 
-            if (t + 1 < nkt)
-                stage(buf ^ 1);
-            __syncthreads();   // next tile staged; buffer buf free for t + 2
+            pin_acc();
+            static_for<NSLOT>([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                const bf16x8 a = ring[i % RA];
+                if constexpr (i + RA < NSLOT)
+                    ring[i % RA] = op_read(IC<i + RA>{});
+                else
+                    ring[i % RA] = op_read(IC<i + RA - NSLOT>{});   // next tile
+                if constexpr (i < 2 * NB) {
+                    constexpr int mb = i / NB, jj = i % NB, ks = jj >> 1;
+                    if constexpr ((jj & 1) != 0)
+                        dpt[mb] = mfma32(a, of[ks], ks == 0 ? z : dpt[mb]);
+                    else
+                        st[mb] = mfma32(a, qf[ks], ks == 0 ? z : st[mb]);
+                } else {
+                    constexpr int jj = i - 2 * NB, kk = jj / DB, db = jj % DB;
+                    acc[db] = mfma32(dsa[kk], a, acc[db]);
+                }
+                // dS of keys 0-31 over slots NB .. 2NB-1, of keys 32-63 over
+                // 2NB .. 2NB+NQ-1 (16 elements each)
+                if constexpr (i >= NB && i < 2 * NB) {
+                    constexpr int u = i - NB;
+                    static_for<16 * (u + 1) / NB - 16 * u / NB>(
+                        [&](auto ec) { pw_elem(IC<0>{}, IC<16 * u / NB + decltype(ec)::value>{}); });
+                }
+                if constexpr (i >= 2 * NB && i < 2 * NB + NQ) {
+                    constexpr int u = i - 2 * NB;
+                    static_for<16 * (u + 1) / NQ - 16 * u / NQ>(
+                        [&](auto ec) { pw_elem(IC<1>{}, IC<16 * u / NQ + decltype(ec)::value>{}); });
+                }
+                if constexpr (i == BAR) {
+                    // every 16-byte read of this tile is issued: move them on
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        gq[ks] += delta;
+                    // the only loads in flight are the next tile's; a bare
+                    // barrier (reads in flight touch this tile's buffer only)
+                    wait_loads<0>();
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                    issue(t + NBUF - 1, cur == 0 ? NBUF - 1 : cur - 1);
+                }
+                if constexpr (i == NSLOT - RA - 1) {
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        tq[db][0] += delta;
+                        tq[db][1] += delta;
+                    }
+                }
+                if constexpr (i == NB || i == 2 * NB)
+                    pin_acc();
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            pin_acc();
+            cur = cur == NBUF - 1 ? 0 : cur + 1;
         }
+        // loads issued past the last tile must land before LDS is released
+        wait_loads<0>();
     }
 
     // ---- dQ = scale * acc -> bf16.  Accumulator: column d = 32 db + l32,

@@ -43,44 +43,16 @@
 // the k-steps over rows 32-63.
 #include <climits>
 #include <type_traits>
-#include <utility>
 
 #include "fa_mfma.h"
 
 namespace fa {
 
-template <int V>
-using IC = std::integral_constant<int, V>;
-
-template <typename F, int... I>
-__device__ inline void static_for_impl(F &f, std::integer_sequence<int, I...>)
-{
-    (f(IC<I>{}), ...);
-}
-
-// f(IC<0>), f(IC<1>), ..., f(IC<N-1>), fully unrolled.
-template <int N, typename F>
-__device__ inline void static_for(F &&f)
-{
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// Query-side tile geometry in LDS.
-template <int DP>
-struct QTile {
-    static constexpr int PCH = DP <= 64 ? 8 : 16;   // 16-byte chunks per LDS row
-    static constexpr int PB = 16 * PCH;             // row pitch (bytes)
-    static constexpr int BYTES = kQTile * PB;
-    static constexpr int NLOAD = BYTES / 1024;      // 1 KB wave loads per tile
-    static constexpr int PERW = NLOAD / 4;          // ... per wave
-    static constexpr int RPL = 1024 / PB;           // rows per wave load
-};
-
 // One query tile in LDS: Q and dO in the swizzled layout, lse2, rowdot.
 template <int DP>
 struct __attribute__((aligned(16))) QBuf {
-    uint8_t q[QTile<DP>::BYTES];
-    uint8_t dO[QTile<DP>::BYTES];
+    uint8_t q[Tile64<DP>::BYTES];
+    uint8_t dO[Tile64<DP>::BYTES];
     float lse2[kQTile];
     float rowdot[kQTile];
 };
@@ -256,7 +228,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
 {
     constexpr int KS = DP / 16;       // MFMA k-steps over the head dim
     constexpr int DB = DP / 32;       // 32-wide blocks of the head dim
-    using L = QTile<DP>;
+    using L = Tile64<DP>;
     // Query-tile buffers in flight: three (loads run two tiles ahead) unless
     // the fused mode's dS^T and K tiles leave LDS room for only two.
     constexpr int NBUF = FUSED ? 2 : 3;

@@ -22,6 +22,9 @@
 // is contiguous in LDS.
 #pragma once
 
+#include <type_traits>
+#include <utility>
+
 #include "fa_internal.h"
 
 namespace fa {
@@ -203,5 +206,33 @@ __device__ inline void pipeline_reads()
     }
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, AHEAD / PER, 0);
 }
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+template <typename F, int... I>
+__device__ inline void static_for_impl(F &f, std::integer_sequence<int, I...>)
+{
+    (f(IC<I>{}), ...);
+}
+
+// f(IC<0>), f(IC<1>), ..., f(IC<N-1>), fully unrolled.
+template <int N, typename F>
+__device__ inline void static_for(F &&f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Geometry of a 64-row tile of head-dim DP in the swizzled LDS layout
+// (64 query rows in the key-tile kernel, 64 keys in the query-tile kernel).
+template <int DP>
+struct Tile64 {
+    static constexpr int PCH = DP <= 64 ? 8 : 16;   // 16-byte chunks per LDS row
+    static constexpr int PB = 16 * PCH;             // row pitch (bytes)
+    static constexpr int BYTES = 64 * PB;
+    static constexpr int NLOAD = BYTES / 1024;      // 1 KB wave loads per tile
+    static constexpr int PERW = NLOAD / 4;          // ... per wave
+    static constexpr int RPL = 1024 / PB;           // rows per wave load
+};
 
 }  // namespace fa
