@@ -38,8 +38,10 @@
 
 namespace fa {
 
-constexpr int kDqRows = 128;    // query rows per workgroup
-constexpr int kDqKeys = 64;     // keys per streamed tile
+constexpr int kDqWaves = 8;                 // two waves per SIMD
+constexpr int kDqThreads = 64 * kDqWaves;
+constexpr int kDqRows = 32 * kDqWaves;      // query rows per workgroup
+constexpr int kDqKeys = 64;                 // keys per streamed tile
 
 template <int DP>
 struct __attribute__((aligned(16))) KVBuf {
@@ -53,12 +55,14 @@ struct __attribute__((aligned(16))) DqSmem {
 };
 
 template <int DP>
-__global__ void __launch_bounds__(kThreads, 1) fa_bwd_dq_kernel(Params p)
+__global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
 {
     constexpr int KS = DP / 16;                  // k-steps over the head dim
     constexpr int DB = DP / 32;                  // 32-wide head-dim blocks
     constexpr int NBUF = 3;
     using L = Tile64<DP>;
+    constexpr int PERW = L::NLOAD / kDqWaves;    // 1 KB wave loads per tensor per wave
+    static_assert(PERW >= 1 && L::NLOAD % kDqWaves == 0, "tile load split");
     __shared__ DqSmem<DP> sm;
 
     const int tid = threadIdx.x;
@@ -131,10 +135,10 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_dq_kernel(Params p)
     if (nkt > 0) {
         // Global byte offsets of the 16-byte chunk each lane loads for wave
         // load i (LDS row pr holds tile chunk (lane % PCH) ^ swz(pr)).
-        uint32_t vok[L::PERW], vov[L::PERW];
+        uint32_t vok[PERW], vov[PERW];
 #pragma unroll
-        for (int i = 0; i < L::PERW; ++i) {
-            const int pr = (w * L::PERW + i) * L::RPL + lane / L::PCH;
+        for (int i = 0; i < PERW; ++i) {
+            const int pr = (w * PERW + i) * L::RPL + lane / L::PCH;
             const int c = (lane % L::PCH) ^ swz<L::PCH>(pr);
             const bool ok = c * 8 < p.D;
             vok[i] = ok ? (uint32_t)(pr * (int)p.k_ss * 2 + c * 16) : kOutOfRange;
@@ -179,8 +183,8 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_dq_kernel(Params p)
             const auto rv = make_rsrc(v_base + (int64_t)n0c * p.v_ss, nv);
             KVBuf<DP> &kb = sm.buf[bf];
 #pragma unroll
-            for (int i = 0; i < L::PERW; ++i) {
-                const int ld = (w * L::PERW + i) * 1024;
+            for (int i = 0; i < PERW; ++i) {
+                const int ld = (w * PERW + i) * 1024;
                 load16_to_lds(rk, kb.k + ld, vok[i]);
                 load16_to_lds(rv, kb.v + ld, vov[i]);
             }
@@ -194,11 +198,11 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_dq_kernel(Params p)
         constexpr int NB = 2 * KS;
         constexpr int NQ = 2 * DB;
         constexpr int NSLOT = 2 * NB + 2 * NQ;
-        constexpr int RA = NSLOT % 8 == 0 ? 8 : 6;   // read-ahead (divides NSLOT)
+        constexpr int RA = 4;                        // read-ahead (divides NSLOT)
         constexpr int BAR = (2 * NB + NQ / 2 < NSLOT - RA) ? 2 * NB + NQ / 2 : NSLOT - RA - 1;
         static_assert(NSLOT % RA == 0, "ring length must divide the slot count");
         static_assert(BAR >= 2 * NB - RA && BAR + RA < NSLOT, "barrier slot");
-        constexpr int LPT = 2 * L::PERW;             // loads per wave per tile
+        constexpr int LPT = 2 * PERW;             // loads per wave per tile
 
         auto op_read = [&](auto ic) -> bf16x8 {
             constexpr int i = decltype(ic)::value;
@@ -331,7 +335,7 @@ hipError_t launch_dq(const Params &p, int dpad, hipStream_t st)
 {
     const int nqt = (p.Sq + kDqRows - 1) / kDqRows;
     const dim3 grid((unsigned)nqt * p.H * p.batch);
-    const dim3 block(kThreads);
+    const dim3 block(kDqThreads);
     switch (dpad) {
     case 64:
         hipLaunchKernelGGL(fa_bwd_dq_kernel<64>, grid, block, 0, st, p);
