@@ -234,21 +234,23 @@ fa_status run(const fa_bwd_args *a, void *stream, int steps)
     const fa::Params &p = pl.p;
     const bool has_rows = p.batch > 0 && p.Sq > 0 && p.rows > 0;
     const bool has_keys = p.batch > 0 && p.ntiles > 0;
-    if ((steps & kPre) && has_rows)
-        if ((st = hip_status(fa::launch_preprocess(p, pl.dpad, s), "preprocess launch")))
-            return st;
-    if ((steps & kMain) && has_keys)
-        if ((st = hip_status(fa::launch_main(p, pl.dpad, s), "main launch")))
-            return st;
     if ((steps & kConv) && !p.fused_dq)
         return fail(FA_ERR_INVALID_ARG, "dq_convert needs dq_accumulate = 1");
     if ((steps & kDq) && p.fused_dq)
         return fail(FA_ERR_INVALID_ARG, "the separate dQ pass needs dq_accumulate = 0");
-    if ((steps & kConv) && has_rows)
-        if ((st = hip_status(fa::launch_convert(p, pl.dpad, s), "dq_convert launch")))
+    if ((steps & kPre) && has_rows)
+        if ((st = hip_status(fa::launch_preprocess(p, pl.dpad, s), "preprocess launch")))
             return st;
+    // The separate dQ pass writes lse2 / rowdot itself, so it runs before
+    // the key-tile kernel that reads them.
     if ((steps & kDq) && has_rows)
         if ((st = hip_status(fa::launch_dq(p, pl.dpad, s), "dq launch")))
+            return st;
+    if ((steps & kMain) && has_keys)
+        if ((st = hip_status(fa::launch_main(p, pl.dpad, s), "main launch")))
+            return st;
+    if ((steps & kConv) && has_rows)
+        if ((st = hip_status(fa::launch_convert(p, pl.dpad, s), "dq_convert launch")))
             return st;
     return FA_OK;
 }
@@ -287,7 +289,7 @@ fa_status fa_bwd(const fa_bwd_args *a, void *stream)
 {
     if (!a)
         return fail(FA_ERR_INVALID_ARG, "args is NULL");
-    return run(a, stream, kPre | kMain | (a->dq_accumulate ? kConv : kDq));
+    return run(a, stream, a->dq_accumulate ? kPre | kMain | kConv : kDq | kMain);
 }
 fa_status fa_bwd_preprocess(const fa_bwd_args *a, void *stream) { return run(a, stream, kPre); }
 fa_status fa_bwd_main(const fa_bwd_args *a, void *stream) { return run(a, stream, kMain); }

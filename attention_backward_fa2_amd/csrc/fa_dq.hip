@@ -83,6 +83,8 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
     const int hk = bg % p.Hk, b = bg / p.Hk;
     const int h = hk * p.G + hh;
 
+    if (lin == 0 && tid < 4)
+        p.flags[tid] = 0;   // the workspace flags (this pass never raises one)
     const SeqInfo si = seq_info(p, b);
     const int q0 = mt * kDqRows;
     if (q0 >= si.Lq)
@@ -91,6 +93,52 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
     const int off = Lk - Lq;
     const int qrow = q0 + 32 * w + l32;          // this lane's query row
     const bool qok = qrow < Lq;
+
+    // Key tiles visible to some row of this query tile.
+    const int q_last = min(q0 + kDqRows, Lq) - 1;
+    int nkt = (Lk + kDqKeys - 1) / kDqKeys;
+    if (p.causal)
+        nkt = min(nkt, max(0, (q_last + off + kDqKeys) / kDqKeys));
+    // Visible keys of this lane's row: key <= klim.
+    const int klim = qok ? (p.causal ? min(Lk - 1, qrow + off) : Lk - 1) : -1;
+
+    // Global byte offsets of the 16-byte chunk each lane loads for wave
+    // load i (LDS row pr holds tile chunk (lane % PCH) ^ swz(pr)).
+    uint32_t vok[PERW], vov[PERW];
+#pragma unroll
+    for (int i = 0; i < PERW; ++i) {
+        const int pr = (w * PERW + i) * L::RPL + lane / L::PCH;
+        const int c = (lane % L::PCH) ^ swz<L::PCH>(pr);
+        const bool ok = c * 8 < p.D;
+        vok[i] = ok ? (uint32_t)(pr * (int)p.k_ss * 2 + c * 16) : kOutOfRange;
+        vov[i] = ok ? (uint32_t)(pr * (int)p.v_ss * 2 + c * 16) : kOutOfRange;
+    }
+    // Issue the loads of key tile t into buffer bf (past the last tile:
+    // empty bound, zeros, no memory access).
+    const uint16_t *k_base = p.k + hk * p.k_sh + row_offset(p, b, si.tok_k, 0, p.k_sb, p.k_ss);
+    const uint16_t *v_base = p.v + hk * p.v_sh + row_offset(p, b, si.tok_k, 0, p.v_sb, p.v_ss);
+    auto issue = [&](int t, int bf) {
+        const int n0 = t * kDqKeys;
+        const int kv = t < nkt ? min(kDqKeys, Lk - n0) : 0;
+        const int n0c = t < nkt ? n0 : 0;
+        const uint32_t nk = kv ? (uint32_t)((kv - 1) * (int)p.k_ss * 2 + p.D * 2) : 0u;
+        const uint32_t nv = kv ? (uint32_t)((kv - 1) * (int)p.v_ss * 2 + p.D * 2) : 0u;
+        const auto rk = make_rsrc(k_base + (int64_t)n0c * p.k_ss, nk);
+        const auto rv = make_rsrc(v_base + (int64_t)n0c * p.v_ss, nv);
+        KVBuf<DP> &kb = sm.buf[bf];
+#pragma unroll
+        for (int i = 0; i < PERW; ++i) {
+            const int ld = (w * PERW + i) * 1024;
+            load16_to_lds(rk, kb.k + ld, vok[i]);
+            load16_to_lds(rv, kb.v + ld, vov[i]);
+        }
+    };
+    // The first two key tiles are in flight while the row vectors below
+    // are formed.
+    if (nkt > 0) {
+        issue(0, 0);
+        issue(1, 1);
+    }
 
     // ---- Q and dO rows of the lane (B operands), lse2 / rowdot ----
     bf16x8 qf[KS], of[KS];
@@ -111,39 +159,66 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
             of[ks] = __builtin_bit_cast(bf16x8, c);
         }
     }
+    // ---- lse2 and rowdot of the lane's row, written for the key-tile kernel
+    //      (which runs after this one).  rowdot = sum_d dO * O with the same
+    //      operations in the same order as the preprocess kernel: each
+    //      16-byte chunk j of the row summed left to right, then the chunk
+    //      sums combined as the preprocess's butterfly over 16 lanes does
+    //      (partners j^8, j^4, j^2, j^1); chunk j = 2*ks + g2 lives in lane
+    //      half g2, so the first three steps are in-lane and the last one
+    //      pairs the two lane halves.  The results are bit-identical. ----
     float l2 = INFINITY, rd = 0.f;
-    if (qok) {
-        const int64_t wr = (int64_t)h * p.rows + si.ws_row + qrow;
-        l2 = p.lse2[wr];
-        rd = p.rowdot[wr];
+    {
+        float cs[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+            cs[ks] = 0.f;
+        if (qok) {
+            const uint16_t *orow = p.o + row_offset(p, b, si.tok_q, qrow, p.o_sb, p.o_ss) + h * p.o_sh;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int d0 = 16 * ks + 8 * g2;
+                if (d0 < p.D) {
+                    const uint4 ov = *reinterpret_cast<const uint4 *>(orow + d0);
+                    const u32x4 dw = __builtin_bit_cast(u32x4, of[ks]);
+                    const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w};
+                    float acc = 0.f;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        acc += bf2f((uint16_t)(ow[t] & 0xffff)) * bf2f((uint16_t)(dw[t] & 0xffff));
+                        acc += bf2f((uint16_t)(ow[t] >> 16)) * bf2f((uint16_t)(dw[t] >> 16));
+                    }
+                    cs[ks] = acc;
+                }
+            }
+        }
+        float a4[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            a4[ks] = cs[ks] + cs[ks ^ 4];
+        const float a2_0 = a4[0] + a4[2], a2_1 = a4[1] + a4[3];
+        const float half = a2_0 + a2_1;
+        const float sum = half + __shfl_xor(half, 32);
+        if (qok) {
+            const float lse = p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + qrow];
+            l2 = (lse == -INFINITY) ? INFINITY : lse * 1.4426950408889634f;
+            rd = sum;
+            if (g2 == 0) {
+                const int64_t wr = (int64_t)h * p.rows + si.ws_row + qrow;
+                p.lse2[wr] = l2;
+                p.rowdot[wr] = rd;
+            }
+        }
     }
-    wait_loads();   // land them before the tile loop
+    wait_loads();   // land them and the first key tiles before the tile loop
 
     f32x16 acc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
         zero(acc[db]);
 
-    // Key tiles visible to some row of this query tile.
-    const int q_last = min(q0 + kDqRows, Lq) - 1;
-    int nkt = (Lk + kDqKeys - 1) / kDqKeys;
-    if (p.causal)
-        nkt = min(nkt, max(0, (q_last + off + kDqKeys) / kDqKeys));
-    // Visible keys of this lane's row: key <= klim.
-    const int klim = qok ? (p.causal ? min(Lk - 1, qrow + off) : Lk - 1) : -1;
 
     if (nkt > 0) {
-        // Global byte offsets of the 16-byte chunk each lane loads for wave
-        // load i (LDS row pr holds tile chunk (lane % PCH) ^ swz(pr)).
-        uint32_t vok[PERW], vov[PERW];
-#pragma unroll
-        for (int i = 0; i < PERW; ++i) {
-            const int pr = (w * PERW + i) * L::RPL + lane / L::PCH;
-            const int c = (lane % L::PCH) ^ swz<L::PCH>(pr);
-            const bool ok = c * 8 < p.D;
-            vok[i] = ok ? (uint32_t)(pr * (int)p.k_ss * 2 + c * 16) : kOutOfRange;
-            vov[i] = ok ? (uint32_t)(pr * (int)p.v_ss * 2 + c * 16) : kOutOfRange;
-        }
         // LDS byte offsets of this lane's operand reads in the current
         // buffer (V is BYTES further):
         //  gq[ks]:    16-byte read of K / V row l32, tile chunk 2*ks + g2 (+ 32
@@ -169,26 +244,6 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
         }
         const uint8_t *lds = reinterpret_cast<const uint8_t *>(&sm.buf[0]);
 
-        // Issue the loads of key tile t into buffer bf (past the last tile:
-        // empty bound, zeros, no memory access).
-        const uint16_t *k_base = p.k + hk * p.k_sh + row_offset(p, b, si.tok_k, 0, p.k_sb, p.k_ss);
-        const uint16_t *v_base = p.v + hk * p.v_sh + row_offset(p, b, si.tok_k, 0, p.v_sb, p.v_ss);
-        auto issue = [&](int t, int bf) {
-            const int n0 = t * kDqKeys;
-            const int kv = t < nkt ? min(kDqKeys, Lk - n0) : 0;
-            const int n0c = t < nkt ? n0 : 0;
-            const uint32_t nk = kv ? (uint32_t)((kv - 1) * (int)p.k_ss * 2 + p.D * 2) : 0u;
-            const uint32_t nv = kv ? (uint32_t)((kv - 1) * (int)p.v_ss * 2 + p.D * 2) : 0u;
-            const auto rk = make_rsrc(k_base + (int64_t)n0c * p.k_ss, nk);
-            const auto rv = make_rsrc(v_base + (int64_t)n0c * p.v_ss, nv);
-            KVBuf<DP> &kb = sm.buf[bf];
-#pragma unroll
-            for (int i = 0; i < PERW; ++i) {
-                const int ld = (w * PERW + i) * 1024;
-                load16_to_lds(rk, kb.k + ld, vok[i]);
-                load16_to_lds(rv, kb.v + ld, vov[i]);
-            }
-        };
 
         // ---- Each key tile as NSLOT MFMA slots, issued in this order: ----
         //   S^T, dP^T of keys 0-31 (k-steps over D)   slots 0 .. NB-1
@@ -220,9 +275,6 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                 asm volatile("" : "+a"(acc[db]));
         };
 
-        issue(0, 0);
-        issue(1, 1);
-        wait_loads<LPT>();
         __syncthreads();
         bf16x8 ring[RA];
         static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });

@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the MI355X attention backward (dQ, dK, dV).
 
-One step = one whole backward (preprocess, main, dq_convert) over the
+One step = one whole backward (dq then main; with --dq-accumulate preprocess,
+main, dq_convert) over the
 headline workload: B=2, H=32, Hk=8, Sq=Sk=4096, D=128, causal, bf16, inputs
 resident in HBM.  Prints ONE JSON line.
 
@@ -317,7 +318,8 @@ def main():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     a = fa.make_args(do, q, k, v, o, lse, dq, dk, dv, wl.scale, wl.causal,
                      deterministic=args.deterministic, dq_accumulate=args.dq_accumulate)
-    last_step = "dq_convert" if args.dq_accumulate else "dq"
+    # the steps of one backward, in the order fa_bwd enqueues them
+    seq = ["preprocess", "main", "dq_convert"] if args.dq_accumulate else ["dq", "main"]
     ws = fa.alloc_workspace(a, dev)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
@@ -327,29 +329,25 @@ def main():
             fa.run(a, "all", stream)
             return
         evs[0].record(stream)
-        fa.run(a, "preprocess", stream)
-        evs[1].record(stream)
-        fa.run(a, "main", stream)
-        evs[2].record(stream)
-        fa.run(a, last_step, stream)
-        evs[3].record(stream)
+        for i, name in enumerate(seq):
+            fa.run(a, name, stream)
+            evs[i + 1].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 1)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
         step(evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = evs[0][0].elapsed_time(evs[-1][3])
-    pre_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K
-    main_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / K
-    last_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / K
+    gpu_ms = evs[0][0].elapsed_time(evs[-1][-1])
+    kms = {name: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / K for i, name in enumerate(seq)}
+    main_ms = kms["main"]
     ms_per_step = gpu_ms / K
 
     B, H, Hk, Sq, Sk, D = wl.batch, wl.heads, wl.heads_k, wl.seqlen_q, wl.seqlen_k, wl.head_dim
@@ -363,7 +361,7 @@ def main():
     gemm = flops / 5.0                   # one of the five products
     main_flops = 5 * gemm if args.dq_accumulate else 4 * gemm
     dq_flops = 0.0 if args.dq_accumulate else 3 * gemm
-    pre_bytes = rows * H * (2 * D * 2 + 4 + 8) + (rows * H * 4 * D if args.dq_accumulate else 0)
+    pre_bytes = rows * H * (2 * D * 2 + 4 + 8) + rows * H * 4 * D   # accumulate mode
     conv_bytes = rows * H * (4 * D + 2 * D)
     main_tflops = main_flops / (main_ms * 1e-3) / 1e12
     off_flags = fa.workspace_layout(a).off_flags
@@ -388,13 +386,12 @@ def main():
                    if args.dq_accumulate else "separate"},
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "flops_per_step": flops,
-        "kernel_ms": {"preprocess": round(pre_ms, 4), "main": round(main_ms, 4),
-                      last_step: round(last_ms, 4)},
+        "kernel_ms": {name: round(t, 4) for name, t in kms.items()},
         "kernel_tflops": {"main": round(main_tflops, 1)} if args.dq_accumulate else
-        {"main": round(main_tflops, 1), "dq": round(dq_flops / (last_ms * 1e-3) / 1e12, 1)},
-        "hbm_kernels_GBs": {"preprocess": round(pre_bytes / (pre_ms * 1e-3) / 1e9, 1)} |
-        ({"dq_convert": round(conv_bytes / (last_ms * 1e-3) / 1e9, 1)} if args.dq_accumulate
-         else {}),
+        {"main": round(main_tflops, 1), "dq": round(dq_flops / (kms["dq"] * 1e-3) / 1e12, 1)},
+        "hbm_kernels_GBs": {"preprocess": round(pre_bytes / (kms["preprocess"] * 1e-3) / 1e9, 1),
+                            "dq_convert": round(conv_bytes / (kms["dq_convert"] * 1e-3) / 1e9, 1)}
+        if args.dq_accumulate else {},
         "roofline": {"bound": "mfma", "achieved": round(main_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),

@@ -9,26 +9,29 @@
  * the scores, P = exp(S - LSE), dP = dO V^T, dS = P (dP - rowsum(dO * O)),
  * then dV += P^T dO, dQ = dS K, dK += dS^T Q).
  *
- * Work is enqueued on the caller's HIP stream as three kernels:
- *   1. preprocess : rowsum(dO * O) per query row and head (the softmax_d /
- *                   dsoftmax_sum buffer of the backward call-trace page,
- *                   set_params_dgrad) and the LSE converted to base 2;
- *   2. main       : one workgroup per 128-key tile of one KV head; it keeps
- *                   the K/V tile and its dK/dV accumulators on chip, loops
- *                   over every query head of the KV head's group (the GQA
- *                   reduction of the GQA/MQA page's backward section happens
- *                   in registers) and over the visible 64-row query tiles;
- *   3. dQ, in one of two ways (fa_bwd_args.dq_accumulate):
- *      0 (default) dq  : one workgroup per 128 query rows of one head loops
+ * Work is enqueued on the caller's HIP stream as two or three kernels:
+ *   - preprocess : rowsum(dO * O) per query row and head (the softmax_d /
+ *                  dsoftmax_sum buffer of the backward call-trace page,
+ *                  set_params_dgrad) and the LSE converted to base 2;
+ *   - main       : one workgroup per 128-key tile of one KV head; it keeps
+ *                  the K/V tile and its dK/dV accumulators on chip, loops
+ *                  over every query head of the KV head's group (the GQA
+ *                  reduction of the GQA/MQA page's backward section happens
+ *                  in registers) and over the visible 64-row query tiles;
+ *   - dQ, in one of two ways (fa_bwd_args.dq_accumulate):
+ *      0 (default) dq  : one workgroup per 256 query rows of one head loops
  *                        over the visible key tiles and forms dQ = scale *
  *                        dS K directly (dS recomputed; no atomics; the way
- *                        the Triton FA2 teaching page's dQ kernel works);
+ *                        the Triton FA2 teaching page's dQ kernel works).
+ *                        It also forms the preprocess's two row vectors, so
+ *                        the sequence is dq, then main;
  *      1 accumulate    : the main kernel adds each tile's dQ partial into an
  *                        fp32 accumulator (hardware atomics, or a fixed
  *                        order when deterministic = 1), which the preprocess
  *                        clears, and dq_convert forms dQ = bf16(scale * acc)
  *                        (the dq_accum buffer and its reduction step on the
- *                        backward call-trace page).
+ *                        backward call-trace page); the sequence is
+ *                        preprocess, main, dq_convert.
  *   On MI355X the fp32 atomic rate of the L2 bounds mode 1 at large sizes;
  *   mode 0 does three extra products per tile pair instead and is faster.
  *
@@ -187,15 +190,18 @@ fa_status fa_bwd_workspace_layout(const fa_bwd_args *a, fa_bwd_ws_layout *out);
  * workspace size).  Host only: no GPU access, nothing enqueued. */
 fa_status fa_bwd_validate(const fa_bwd_args *a);
 
-/* The whole backward, enqueued on `stream`: preprocess, main, then dq
- * (dq_accumulate = 0) or dq_convert (dq_accumulate = 1). */
+/* The whole backward, enqueued on `stream`: dq then main (dq_accumulate = 0;
+ * the dq step also writes lse2 / rowdot, so no preprocess step is needed), or
+ * preprocess, main, dq_convert (dq_accumulate = 1). */
 fa_status fa_bwd(const fa_bwd_args *a, void *stream);
 
 /* The steps one at a time, on one stream, in the order above (each
  * validates like fa_bwd).  Used to time and test the kernels separately.
- * fa_bwd_main and fa_bwd_dq need a completed fa_bwd_preprocess on the same
- * workspace (fa_bwd_dq does not need fa_bwd_main); fa_bwd_dq_convert needs a
- * completed fa_bwd_main.  fa_bwd_dq requires dq_accumulate = 0 and
+ * fa_bwd_preprocess writes lse2 / rowdot (and, with dq_accumulate = 1, clears
+ * the accumulator); fa_bwd_dq writes the same lse2 / rowdot values (bit for
+ * bit) itself and needs nothing before it; fa_bwd_main needs a completed
+ * fa_bwd_preprocess or fa_bwd_dq on the same workspace; fa_bwd_dq_convert
+ * needs a completed fa_bwd_main.  fa_bwd_dq requires dq_accumulate = 0 and
  * fa_bwd_dq_convert dq_accumulate = 1 (FA_ERR_INVALID_ARG otherwise). */
 fa_status fa_bwd_preprocess(const fa_bwd_args *a, void *stream);
 fa_status fa_bwd_main(const fa_bwd_args *a, void *stream);

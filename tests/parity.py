@@ -52,7 +52,8 @@ class Prepared:
         return self.inp.wl.varlen
 
 
-def run_gpu(pr: Prepared, deterministic=False, out_pad=0, step_split=False, dq_accumulate=False):
+def run_gpu(pr: Prepared, deterministic=False, out_pad=0, step_split=False, dq_accumulate=False,
+            steps=None):
     """Backward on cuda:0.  Outputs start as NaN so unwritten elements show.
     out_pad > 0 gives dq/dk/dv a row pitch of head_dim + out_pad (strided
     views) to check that columns past head_dim are left alone."""
@@ -78,7 +79,10 @@ def run_gpu(pr: Prepared, deterministic=False, out_pad=0, step_split=False, dq_a
                         deterministic=deterministic, dq_accumulate=dq_accumulate, **kw)
     ws = fa.alloc_workspace(args, dev)
     ws.fill_(0xA5)   # garbage: the preprocess must clear what it uses
-    if step_split:
+    if steps is not None:
+        for step in steps:
+            fa.run(args, step)
+    elif step_split:
         for step in ("preprocess", "main", "dq_convert" if dq_accumulate else "dq"):
             fa.run(args, step)
     else:

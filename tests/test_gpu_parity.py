@@ -136,6 +136,22 @@ def test_preprocess_rowdot_and_lse2(gpu_lib, prepared, name):
     assert np.all(np.abs(lse2[~empty] - want) <= 2e-7 * np.maximum(1.0, np.abs(want)))
 
 
+@pytest.mark.parametrize("name", ["dense_causal_ragged_gqa2_d64", "varlen_d96_causal",
+                                  "causal_sq_gt_sk_empty_rows_d128"])
+def test_dq_step_writes_the_preprocess_row_vectors_bit_for_bit(gpu_lib, prepared, name):
+    """The separate dQ kernel forms lse2 and rowdot itself (the key-tile
+    kernel then runs after it); they must equal the preprocess kernel's to
+    the bit, so that every step order gives the same dK/dV."""
+    pr = prepared(name)
+    a = PT.run_gpu(pr, steps=["preprocess"])
+    b = PT.run_gpu(pr, steps=["dq"])
+    H, T = pr.inp.wl.heads, int(pr.cu_q[-1])
+    for vec in ("lse2", "rowdot"):
+        va = PT.ws_view(a, vec, torch.float32, H * T, (H, T)).view(torch.int32)
+        vb = PT.ws_view(b, vec, torch.float32, H * T, (H, T)).view(torch.int32)
+        assert torch.equal(va, vb), vec
+
+
 def test_dq_convert_is_exact_scaled_rne(gpu_lib, prepared):
     pr = prepared("varlen_unequal_noncausal_d128")
     res = PT.run_gpu(pr, dq_accumulate=True)
