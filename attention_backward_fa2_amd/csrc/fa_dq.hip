@@ -269,12 +269,6 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                 return tr_pair(lds + tq[db][0] + 16 * kk * L::PB, lds + tq[db][1] + 16 * kk * L::PB);
             }
         };
-        auto pin_acc = [&]() {
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-                asm volatile("" : "+a"(acc[db]));
-        };
-
         __syncthreads();
         bf16x8 ring[RA];
         static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
@@ -306,7 +300,6 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                 }
             };
 
-            pin_acc();
             static_for<NSLOT>([&](auto ic) {
                 constexpr int i = decltype(ic)::value;
                 const bf16x8 a = ring[i % RA];
@@ -355,11 +348,8 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                         tq[db][1] += delta;
                     }
                 }
-                if constexpr (i == NB || i == 2 * NB)
-                    pin_acc();
                 __builtin_amdgcn_sched_barrier(0);
             });
-            pin_acc();
             cur = cur == NBUF - 1 ? 0 : cur + 1;
         }
         // loads issued past the last tile must land before LDS is released
