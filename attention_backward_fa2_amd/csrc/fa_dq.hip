@@ -273,8 +273,18 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
         bf16x8 ring[RA];
         static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
 
+        // Smallest visible-key limit over the wave's rows (-1 if any row is
+        // past the end): key tiles wholly at or below it need no mask.
+        const int r0w = q0 + 32 * w;
+        const int kmin_w = r0w + 31 < Lq ? (p.causal ? min(Lk - 1, r0w + off) : Lk - 1) : -1;
+
+        // Key tiles 0 .. nfull-1 are fully visible to every row of the wave.
+        const int nfull = min(nkt, max(0, (kmin_w + 1) / kDqKeys));
+
         int cur = 0;
-        for (int t = 0; t < nkt; ++t) {
+        // One key tile, with or without the element mask (the same slots
+        // otherwise).
+        auto tile = [&](int t, auto maskc) {
             const int n0 = t * kDqKeys;
             // element (32*mb + 8*r4 + t) of the lane's keys (+ 4*g2) is kept
             // iff it is <= kthr
@@ -291,7 +301,8 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                 constexpr int mb = decltype(mbc)::value, e = decltype(ec)::value;
                 constexpr int r4 = e >> 2, tt = e & 3;
                 float x = __builtin_amdgcn_exp2f(st[mb][e] * p.scale_log2 - l2);
-                x = 32 * mb + 8 * r4 + tt <= kthr ? x : 0.f;
+                if constexpr (decltype(maskc)::value)
+                    x = 32 * mb + 8 * r4 + tt <= kthr ? x : 0.f;
                 dv[tt] = x * (dpt[mb][e] - rd);
                 if constexpr (tt == 3) {
                     dh[r4] = to_bf16(dv);
@@ -351,7 +362,12 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                 __builtin_amdgcn_sched_barrier(0);
             });
             cur = cur == NBUF - 1 ? 0 : cur + 1;
-        }
+        };
+        int t = 0;
+        for (; t < nfull; ++t)
+            tile(t, std::false_type{});
+        for (; t < nkt; ++t)
+            tile(t, std::true_type{});
         // loads issued past the last tile must land before LDS is released
         wait_loads<0>();
     }
