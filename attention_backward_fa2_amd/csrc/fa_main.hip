@@ -464,7 +464,9 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
 
         int cur = 0;
-        for (int it = 0; it < total; ++it) {
+        // One query tile, with or without the element mask (the same slots
+        // otherwise).
+        auto tile = [&](int it, auto maskc) {
             if constexpr (FUSED)
                 issue(it + 1, cur ^ 1);
             const int m = tile_m(it);
@@ -495,7 +497,8 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 constexpr int r4 = e >> 2, t = e & 3;
                 constexpr int qc = 32 * mb + 8 * r4;
                 float x = __builtin_amdgcn_exp2f(s[mb][e] * p.scale_log2 - l2v[r4][t]);
-                x = qc + t >= limv ? x : 0.f;
+                if constexpr (decltype(maskc)::value)
+                    x = qc + t >= limv ? x : 0.f;
                 pv[t] = x;
                 dv[t] = x * (dp[mb][e] - rdv[r4][t]);
                 if constexpr (t == 3) {
@@ -609,6 +612,29 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
             }
             cur = cur == NBUF - 1 ? 0 : cur + 1;
+        };
+        if constexpr (FUSED) {
+            for (int it = 0; it < total; ++it)
+                tile(it, std::true_type{});
+        } else {
+            // The wave's keys are visible to every row of query tiles m >=
+            // m_vis (and to none past the sequence end); within each head
+            // those come first in the descending order.
+            const int kw_last = n0 + 32 * w + 31;
+            int nun = 0;
+            if (kw_last < Lk) {
+                const int need = kw_last - off;
+                const int m_vis = !p.causal || need <= 0 ? 0 : (need + kQTile - 1) / kQTile;
+                nun = max(0, m_end - max(m_begin, m_vis));
+            }
+            int it = 0;
+            for (int hh = 0; hh < p.G; ++hh) {
+                const int it_u = it + nun, it_e = it + nm;
+                for (; it < it_u; ++it)
+                    tile(it, std::false_type{});
+                for (; it < it_e; ++it)
+                    tile(it, std::true_type{});
+            }
         }
         // The last iterations issued loads past the final tile (empty bound,
         // zeros into LDS); let them land before the workgroup's LDS is
