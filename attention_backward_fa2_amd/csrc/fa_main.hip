@@ -458,6 +458,9 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
 #pragma unroll
             for (int db = 0; db < DB; ++db)
                 asm volatile("" : "+a"(dk_acc[db]), "+a"(dv_acc[db]));
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                asm volatile("" : "+a"(kf[ks]), "+a"(vf[ks]));
         };
 
         bf16x8 ring[RA];
@@ -484,7 +487,6 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             const int delta = cur == NBUF - 1 ? -(NBUF - 1) * BUFB : BUFB;
 
             f32x16 s[2], dp[2];
-            const f32x16 z = {};
             bf16x8 pb[4], dsb[4];
             bf16x4 ph[4], dh[4];
             f32x4 l2v[4], rdv[4];
@@ -530,10 +532,12 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 }
                 if constexpr (i < 2 * NB) {
                     constexpr int mb = i / NB, jj = i % NB, ks = jj >> 1;
-                    if constexpr ((jj & 1) != 0)
-                        dp[mb] = mfma32(a, vf[ks], ks == 0 ? z : dp[mb]);
+                    f32x16 &d = (jj & 1) != 0 ? dp[mb] : s[mb];
+                    const bf16x8 &bop = (jj & 1) != 0 ? vf[ks] : kf[ks];
+                    if constexpr (ks == 0)
+                        mfma32_vz(d, a, bop);
                     else
-                        s[mb] = mfma32(a, kf[ks], ks == 0 ? z : s[mb]);
+                        mfma32_vacc(d, a, bop);
                 } else {
                     constexpr int jj = (i - 2 * NB) % NG;
                     constexpr int kk = 2 * ((i - 2 * NB) / NG) + jj / (2 * DB);
@@ -548,6 +552,8 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 // the last four of them), of block 1 over 2NB .. 2NB+NG-1
                 if constexpr (i >= NB && i < 2 * NB) {
                     constexpr int u = i - NB;
+                    if constexpr (u == 0)
+                        mfma_settle(s[0], dp[0]);
                     static_for<16 * (u + 1) / NB - 16 * u / NB>(
                         [&](auto ec) { pw_elem(IC<0>{}, IC<16 * u / NB + decltype(ec)::value>{}); });
                     if constexpr (u >= NB - 4) {
@@ -558,6 +564,8 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 }
                 if constexpr (i >= 2 * NB && i < 2 * NB + NG) {
                     constexpr int u = i - 2 * NB;
+                    if constexpr (u == 0)
+                        mfma_settle(s[1], dp[1]);
                     static_for<16 * (u + 1) / NG - 16 * u / NG>(
                         [&](auto ec) { pw_elem(IC<1>{}, IC<16 * u / NG + decltype(ec)::value>{}); });
                 }

@@ -44,6 +44,34 @@ __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// The same product as inline assembly: accumulator in ordinary registers,
+// B operand in accumulation registers (A in ordinary ones).  The compiler
+// gives every MFMA of a kernel one register form; a kernel whose long-lived
+// accumulators must live in accumulation registers would otherwise get its
+// short-lived products there as well, and each element would need a copy
+// before the vector math can read it.  These are not MFMAs to the compiler,
+// so the caller covers the hazards it would otherwise cover (gfx950,
+// 32x32x16: a vector read of the result needs 12 wait states after the last
+// product -- mfma_settle(); an accumulation chain needs none; operand A must
+// not come from a vector instruction of the two preceding wait states -- the
+// callers feed it straight from LDS reads).
+__device__ inline void mfma32_vz(f32x16 &d, bf16x8 a, bf16x8 b)   // d = A B
+{
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+
+__device__ inline void mfma32_vacc(f32x16 &d, bf16x8 a, bf16x8 b)   // d += A B
+{
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+
+// 12 wait states, ordered after the last product into s and t and before
+// any read of them.
+__device__ inline void mfma_settle(f32x16 &s, f32x16 &t)
+{
+    asm volatile("s_nop 11" : "+v"(s), "+v"(t));
+}
+
 // fp32 -> bf16 (round to nearest even) of four values: two packed
 // hardware converts.
 __device__ inline bf16x4 to_bf16(f32x4 x)
