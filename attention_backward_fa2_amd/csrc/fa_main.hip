@@ -11,7 +11,7 @@
 // accumulation:
 //     S  = Q K^T            dP = dO V^T
 //     P  = exp2(S * scale * log2e - lse2)      (0 where masked)
-//     dS = P * (dP - rowdot)
+//     dS = P * (dP - rowdot)   (the dP product starts from rowdot, with -V)
 //     dV += P^T dO          dK += dS^T Q       (registers, whole group)
 //   fused mode only:
 //     dQ_partial = dS K  -> fp32 adds into the dQ accumulator
@@ -69,44 +69,6 @@ struct __attribute__((aligned(16))) FusedSmem : TileSmem<DP, 2> {
     uint16_t dsT[2][kKTile * RD];
     uint16_t k[kKTile * RQ];
 };
-
-// P = exp2(S*scale*log2e - lse2) and dS = P (dP - rowdot) for query rows
-// 32*mb .. 32*mb+31 of the tile (one accumulator block per product), as
-// bf16 B operands pb[0..1] / dsb[0..1] of the k-steps over those rows, and
-// (fused mode) the lane's dS^T row segment to LDS.  Accumulator rows
-// 4*r4 .. 4*r4+3 are tile rows 32*mb + 8*r4 + 4*g2 + t (t = 0..3) and
-// elements 4*(r4&1) .. +3 of operand r4/2.  l2s, rds and dsT_row already
-// point at row 4*g2; the element is kept iff 32*mb + 8*r4 + t >= limv
-// (visibility of the lane's key, folded into one threshold per tile).
-template <bool WRITE_DS>
-__device__ inline void pointwise_half(const f32x16 &s, const f32x16 &dp, bf16x8 *pb, bf16x8 *dsb,
-                                      uint16_t *dsT_row, const float *l2s, const float *rds,
-                                      float scale_log2, int mb, int limv)
-{
-    bf16x4 ph[4], dh[4];
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-        const int qc = 32 * mb + 8 * r4;
-        const f32x4 l2v = *reinterpret_cast<const f32x4 *>(l2s + qc);
-        const f32x4 rdv = *reinterpret_cast<const f32x4 *>(rds + qc);
-        f32x4 pv, dv;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            float e = __builtin_amdgcn_exp2f(s[4 * r4 + t] * scale_log2 - l2v[t]);
-            e = qc + t >= limv ? e : 0.f;
-            pv[t] = e;
-            dv[t] = e * (dp[4 * r4 + t] - rdv[t]);
-        }
-        ph[r4] = to_bf16(pv);
-        dh[r4] = to_bf16(dv);
-        if constexpr (WRITE_DS)
-            *reinterpret_cast<bf16x4 *>(dsT_row + qc) = dh[r4];
-    }
-    pb[0] = concat(ph[0], ph[1]);
-    pb[1] = concat(ph[2], ph[3]);
-    dsb[0] = concat(dh[0], dh[1]);
-    dsb[1] = concat(dh[2], dh[3]);
-}
 
 // Fused mode: dQ partial of one query tile = dS K over this workgroup's 128
 // keys, added into the fp32 accumulator -- unordered hardware atomics, or
@@ -287,7 +249,9 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 vv = *reinterpret_cast<const u32x4 *>(vrow + d0);
             }
             kf[ks] = __builtin_bit_cast(bf16x8, kv);
-            vf[ks] = __builtin_bit_cast(bf16x8, vv);
+            // -V: the dP product then starts from rowdot and yields
+            // rowdot - dP (sign flips are exact in bf16)
+            vf[ks] = __builtin_bit_cast(bf16x8, vv ^ 0x80008000u);
             if constexpr (FUSED)
                 *reinterpret_cast<u32x4 *>(&sm.k[key_local * FusedSmem<DP>::RQ + d0]) = kv;
         }
@@ -465,6 +429,20 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
 
         bf16x8 ring[RA];
         static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
+        // rowdot of the rows of query block mb (accumulator layout: element
+        // 4*r4 + t is row 32*mb + 8*r4 + 4*g2 + t): the initial value of the
+        // dP accumulator.  Block 0 of the next tile is read once its buffer
+        // is published, block 1 at the start of its own tile.
+        f32x16 rdc[2];
+        auto read_rowdot = [&](int mb, int r4) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(lds + rv0 + 4 * kQTile + 128 * mb + 32 * r4);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                rdc[mb][4 * r4 + t] = v[t];
+        };
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+            read_rowdot(0, r4);
 
         int cur = 0;
         // One query tile, with or without the element mask (the same slots
@@ -482,14 +460,13 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             if constexpr (FUSED)
                 dsrow = &sm.dsT[cur][key_local * FusedSmem<DP>::RD + 4 * g2];
             const float *l2s = reinterpret_cast<const float *>(lds + rv0);
-            const float *rds = l2s + kQTile;
             // offset step to the next tile's buffer
             const int delta = cur == NBUF - 1 ? -(NBUF - 1) * BUFB : BUFB;
 
             f32x16 s[2], dp[2];
             bf16x8 pb[4], dsb[4];
             bf16x4 ph[4], dh[4];
-            f32x4 l2v[4], rdv[4];
+            f32x4 l2v[4];
             f32x4 pv, dv;
 
             // element e (0..15) of query block mb: exp, mask, dS; packs a
@@ -502,7 +479,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 if constexpr (decltype(maskc)::value)
                     x = qc + t >= limv ? x : 0.f;
                 pv[t] = x;
-                dv[t] = x * (dp[mb][e] - rdv[r4][t]);
+                dv[t] = x * -dp[mb][e];   // dp holds rowdot - dP
                 if constexpr (t == 3) {
                     ph[r4] = to_bf16(pv);
                     dh[r4] = to_bf16(dv);
@@ -528,16 +505,22 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 if constexpr (i >= NB / 2 && i < NB / 2 + 4) {
                     constexpr int r4 = i - NB / 2;
                     l2v[r4] = *reinterpret_cast<const f32x4 *>(l2s + 8 * r4);
-                    rdv[r4] = *reinterpret_cast<const f32x4 *>(rds + 8 * r4);
                 }
+                // rowdot of block 1, needed by its first dP step
+                if constexpr (i < 4)
+                    read_rowdot(1, i);
                 if constexpr (i < 2 * NB) {
                     constexpr int mb = i / NB, jj = i % NB, ks = jj >> 1;
-                    f32x16 &d = (jj & 1) != 0 ? dp[mb] : s[mb];
-                    const bf16x8 &bop = (jj & 1) != 0 ? vf[ks] : kf[ks];
-                    if constexpr (ks == 0)
-                        mfma32_vz(d, a, bop);
-                    else
-                        mfma32_vacc(d, a, bop);
+                    if constexpr ((jj & 1) != 0) {
+                        // dp = rowdot - dO V^T (vf holds -V)
+                        if constexpr (ks == 0)
+                            dp[mb] = rdc[mb];
+                        mfma32_vacc(dp[mb], a, vf[ks]);
+                    } else if constexpr (ks == 0) {
+                        mfma32_vz(s[mb], a, kf[ks]);
+                    } else {
+                        mfma32_vacc(s[mb], a, kf[ks]);
+                    }
                 } else {
                     constexpr int jj = (i - 2 * NB) % NG;
                     constexpr int kk = 2 * ((i - 2 * NB) / NG) + jj / (2 * DB);
@@ -559,7 +542,6 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     if constexpr (u >= NB - 4) {
                         constexpr int r4 = u - (NB - 4);
                         l2v[r4] = *reinterpret_cast<const f32x4 *>(l2s + 32 + 8 * r4);
-                        rdv[r4] = *reinterpret_cast<const f32x4 *>(rds + 32 + 8 * r4);
                     }
                 }
                 if constexpr (i >= 2 * NB && i < 2 * NB + NG) {
@@ -588,6 +570,8 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     asm volatile("" ::: "memory");
                     issue(it + NBUF - 1, cur == 0 ? NBUF - 1 : cur - 1);
                 }
+                if constexpr (!FUSED && i > BAR && i <= BAR + 4)
+                    read_rowdot(0, i - BAR - 1);   // next tile (buffer published at BAR)
                 if constexpr (!FUSED && i == NSLOT - RA - 1) {
                     // last transposing read of this tile issued
 #pragma unroll
@@ -618,6 +602,9 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 dq_partial<DP>(p, sm, cur, w, lane, l32, g2, tid, b, h, m, j, q0, rows_valid, Lq,
                                off, nt_b, si.ws_row);
                 static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4)
+                    read_rowdot(0, r4);
             }
             cur = cur == NBUF - 1 ? 0 : cur + 1;
         };
