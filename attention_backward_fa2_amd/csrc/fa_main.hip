@@ -331,27 +331,31 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             return ascending ? m_begin + r : m_end - 1 - r;
         };
 
-        // Issue the loads of query tile `it` into LDS buffer bf; past the
+        // Loads of the query tiles into LDS, strictly in the order they are
+        // computed: issue(bf) loads the next tile into buffer bf.  Past the
         // last tile the loads are issued with an empty bound (no memory
-        // access, zeros written) so that the tile loop has no branch.  All
-        // address arithmetic is scalar and branch-free: row q0 of head h
-        // starts at base + h * head stride + q0 * row stride.
-        const uint16_t *q_base = p.q + row_offset(p, b, si.tok_q, 0, p.q_sb, p.q_ss);
-        const uint16_t *do_base = p.dout + row_offset(p, b, si.tok_q, 0, p.do_sb, p.do_ss);
-        const float *rowvec_base = ((w & 1) ? p.rowdot : p.lse2) + si.ws_row;   // see below
-        auto issue = [&](int it, int bf) {
-            const bool real = it < total;
-            const int itc = real ? it : total - 1;
-            const int hh = itc / nm, m = tile_m(itc);
-            const int h = hk * p.G + hh;
-            const int q0 = m * kQTile;
-            const int rv = real ? min(kQTile, Lq - q0) : 0;
-            const uint16_t *qb = q_base + h * p.q_sh + (int64_t)q0 * p.q_ss;
-            const uint16_t *db = do_base + h * p.do_sh + (int64_t)q0 * p.do_ss;
+        // access, zeros written) so that the tile loop has no branch.  The
+        // tile's row pointers advance incrementally (scalar registers):
+        // within a head by one tile, at the end of a head to the first tile
+        // of the next head of the group.
+        const int q0_first = (ascending ? m_begin : m_end - 1) * kQTile;
+        const int dq0 = ascending ? kQTile : -kQTile;
+        const int h0 = hk * p.G;
+        const uint16_t *nq_head = p.q + row_offset(p, b, si.tok_q, q0_first, p.q_sb, p.q_ss) + h0 * p.q_sh;
+        const uint16_t *nd_head =
+            p.dout + row_offset(p, b, si.tok_q, q0_first, p.do_sb, p.do_ss) + h0 * p.do_sh;
+        // lse2 (even waves) / rowdot (odd waves), see below
+        const float *nr_head = ((w & 1) ? p.rowdot : p.lse2) + si.ws_row + (int64_t)h0 * p.rows + q0_first;
+        const uint16_t *nq_ptr = nq_head, *nd_ptr = nd_head;
+        const float *nr_ptr = nr_head;
+        int n_r = 0, n_q0 = q0_first, n_left = total;
+        const int64_t step_q = (int64_t)dq0 * p.q_ss, step_d = (int64_t)dq0 * p.do_ss;
+        auto issue = [&](int bf) {
+            const int rv = n_left > 0 ? min(kQTile, Lq - n_q0) : 0;
             const uint32_t nq = rv ? (uint32_t)((rv - 1) * (int)p.q_ss * 2 + p.D * 2) : 0u;
             const uint32_t nd = rv ? (uint32_t)((rv - 1) * (int)p.do_ss * 2 + p.D * 2) : 0u;
-            const auto rq = make_rsrc(qb, nq);
-            const auto rd = make_rsrc(db, nd);
+            const auto rq = make_rsrc(nq_ptr, nq);
+            const auto rd = make_rsrc(nd_ptr, nd);
             QBuf<DP> &qbuf = sm.buf[bf];
 #pragma unroll
             for (int i = 0; i < L::PERW; ++i) {
@@ -361,16 +365,26 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             }
             // lse2 (even waves) / rowdot (odd waves): the two waves of a kind
             // write the same values.
-            const float *src = rowvec_base + (int64_t)h * p.rows + q0;
-            load4_to_lds(make_rsrc(src, (uint32_t)rv * 4), (w & 1) ? qbuf.rowdot : qbuf.lse2,
+            load4_to_lds(make_rsrc(nr_ptr, (uint32_t)rv * 4), (w & 1) ? qbuf.rowdot : qbuf.lse2,
                          (uint32_t)lane * 4);
+            // advance to the next tile (branch-free selects)
+            --n_left;
+            const bool wrap = n_r == nm - 1;
+            n_r = wrap ? 0 : n_r + 1;
+            n_q0 = wrap ? q0_first : n_q0 + dq0;
+            nq_head = wrap ? nq_head + p.q_sh : nq_head;
+            nd_head = wrap ? nd_head + p.do_sh : nd_head;
+            nr_head = wrap ? nr_head + p.rows : nr_head;
+            nq_ptr = wrap ? nq_head : nq_ptr + step_q;
+            nd_ptr = wrap ? nd_head : nd_ptr + step_d;
+            nr_ptr = wrap ? nr_head : nr_ptr + dq0;
         };
 
         // Loads per wave per tile (each Q / dO wave load, and lse2 / rowdot).
         constexpr int LPT = 2 * L::PERW + 1;
 #pragma unroll
         for (int t = 0; t < NBUF - 1; ++t)
-            issue(t, t);
+            issue(t);
         wait_loads<LPT * (NBUF - 2)>();
         __syncthreads();
 
@@ -447,10 +461,9 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         int cur = 0;
         // One query tile, with or without the element mask (the same slots
         // otherwise).
-        auto tile = [&](int it, auto maskc) {
+        auto tile = [&](int it, int m, auto maskc) {
             if constexpr (FUSED)
-                issue(it + 1, cur ^ 1);
-            const int m = tile_m(it);
+                issue(cur ^ 1);
             const int q0 = m * kQTile;
             // Visibility threshold of this lane's key over tile rows
             // 4*g2 + (32*mb + 8*r4 + t): keys past the end see nothing;
@@ -568,7 +581,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     wait_loads<0>();
                     __builtin_amdgcn_s_barrier();
                     asm volatile("" ::: "memory");
-                    issue(it + NBUF - 1, cur == 0 ? NBUF - 1 : cur - 1);
+                    issue(cur == 0 ? NBUF - 1 : cur - 1);
                 }
                 if constexpr (!FUSED && i > BAR && i <= BAR + 4)
                     read_rowdot(0, i - BAR - 1);   // next tile (buffer published at BAR)
@@ -610,7 +623,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         };
         if constexpr (FUSED) {
             for (int it = 0; it < total; ++it)
-                tile(it, std::true_type{});
+                tile(it, tile_m(it), std::true_type{});
         } else {
             // The wave's keys are visible to every row of query tiles m >=
             // m_vis (and to none past the sequence end); within each head
@@ -624,11 +637,12 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             }
             int it = 0;
             for (int hh = 0; hh < p.G; ++hh) {
+                int m = m_end - 1;
                 const int it_u = it + nun, it_e = it + nm;
-                for (; it < it_u; ++it)
-                    tile(it, std::false_type{});
-                for (; it < it_e; ++it)
-                    tile(it, std::true_type{});
+                for (; it < it_u; ++it, --m)
+                    tile(it, m, std::false_type{});
+                for (; it < it_e; ++it, --m)
+                    tile(it, m, std::true_type{});
             }
         }
         // The last iterations issued loads past the final tile (empty bound,
