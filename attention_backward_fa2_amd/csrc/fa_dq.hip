@@ -212,6 +212,16 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
     }
     wait_loads();   // land them and the first key tiles before the tile loop
 
+    // -dO as the dP operand and rowdot as its initial value: the product
+    // then yields rowdot - dP (sign flips are exact in bf16).
+    f32x16 rdt;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        of[ks] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, of[ks]) ^ 0x80008000u);
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        rdt[e] = rd;
+
     f32x16 acc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -303,7 +313,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                 float x = __builtin_amdgcn_exp2f(st[mb][e] * p.scale_log2 - l2);
                 if constexpr (decltype(maskc)::value)
                     x = 32 * mb + 8 * r4 + tt <= kthr ? x : 0.f;
-                dv[tt] = x * (dpt[mb][e] - rd);
+                dv[tt] = x * -dpt[mb][e];   // dpt holds rowdot - dP
                 if constexpr (tt == 3) {
                     dh[r4] = to_bf16(dv);
                     if constexpr ((r4 & 1) != 0)
@@ -321,7 +331,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                 if constexpr (i < 2 * NB) {
                     constexpr int mb = i / NB, jj = i % NB, ks = jj >> 1;
                     if constexpr ((jj & 1) != 0)
-                        dpt[mb] = mfma32(a, of[ks], ks == 0 ? z : dpt[mb]);
+                        dpt[mb] = mfma32(a, of[ks], ks == 0 ? rdt : dpt[mb]);
                     else
                         st[mb] = mfma32(a, qf[ks], ks == 0 ? z : st[mb]);
                 } else {
