@@ -17,9 +17,8 @@
 // tile are read with ds_read_b64_tr_b16: within each 16-lane group the 16
 // 8-byte reads form a 4 x 16 block (lanes 4r .. 4r+3 read row r) and lane c
 // receives column c.  Two such reads give one 8-element operand; the row
-// base of each read implements the permutation above.  It moves half as
-// many bytes per clock as ds_read_b128, which is used wherever the operand
-// is contiguous in LDS.
+// base of each read implements the permutation above.  ds_read_b128 is used
+// wherever the operand is contiguous in LDS (one instruction instead of two).
 #pragma once
 
 #include <type_traits>
