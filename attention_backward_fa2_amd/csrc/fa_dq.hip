@@ -113,18 +113,26 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
         vok[i] = ok ? (uint32_t)(pr * (int)p.k_ss * 2 + c * 16) : kOutOfRange;
         vov[i] = ok ? (uint32_t)(pr * (int)p.v_ss * 2 + c * 16) : kOutOfRange;
     }
-    // Issue the loads of key tile t into buffer bf (past the last tile:
-    // empty bound, zeros, no memory access).
-    const uint16_t *k_base = p.k + hk * p.k_sh + row_offset(p, b, si.tok_k, 0, p.k_sb, p.k_ss);
-    const uint16_t *v_base = p.v + hk * p.v_sh + row_offset(p, b, si.tok_k, 0, p.v_sb, p.v_ss);
-    auto issue = [&](int t, int bf) {
-        const int n0 = t * kDqKeys;
-        const int kv = t < nkt ? min(kDqKeys, Lk - n0) : 0;
-        const int n0c = t < nkt ? n0 : 0;
+    // Issue the loads of the next key tile into buffer bf (tiles are loaded
+    // strictly in order; past the last tile: empty bound, zeros, no memory
+    // access).  The tile's row pointers advance by one tile per call, in
+    // scalar registers kept at the call's place in the instruction stream.
+    const uint16_t *k_next = p.k + hk * p.k_sh + row_offset(p, b, si.tok_k, 0, p.k_sb, p.k_ss);
+    const uint16_t *v_next = p.v + hk * p.v_sh + row_offset(p, b, si.tok_k, 0, p.v_sb, p.v_ss);
+    int n_next = 0, n_left = nkt;
+    const int64_t kstep = (int64_t)kDqKeys * p.k_ss, vstep = (int64_t)kDqKeys * p.v_ss;
+    auto issue = [&](int bf) {
+        keep_scalar_here(n_next, n_left, k_next, v_next);
+        const int kv = n_left > 0 ? min(kDqKeys, Lk - n_next) : 0;
         const uint32_t nk = kv ? (uint32_t)((kv - 1) * (int)p.k_ss * 2 + p.D * 2) : 0u;
         const uint32_t nv = kv ? (uint32_t)((kv - 1) * (int)p.v_ss * 2 + p.D * 2) : 0u;
-        const auto rk = make_rsrc(k_base + (int64_t)n0c * p.k_ss, nk);
-        const auto rv = make_rsrc(v_base + (int64_t)n0c * p.v_ss, nv);
+        const auto rk = make_rsrc(k_next, nk);
+        const auto rv = make_rsrc(v_next, nv);
+        n_next += kDqKeys;
+        --n_left;
+        k_next += kstep;
+        v_next += vstep;
+        keep_scalar_here(n_next, n_left, k_next, v_next);
         KVBuf<DP> &kb = sm.buf[bf];
 #pragma unroll
         for (int i = 0; i < PERW; ++i) {
@@ -136,8 +144,8 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
     // The first two key tiles are in flight while the row vectors below
     // are formed.
     if (nkt > 0) {
-        issue(0, 0);
-        issue(1, 1);
+        issue(0);
+        issue(1);
     }
 
     // ---- Q and dO rows of the lane (B operands), lse2 / rowdot ----
@@ -313,7 +321,9 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                 float x = __builtin_amdgcn_exp2f(st[mb][e] * p.scale_log2 - l2);
                 if constexpr (decltype(maskc)::value)
                     x = 32 * mb + 8 * r4 + tt <= kthr ? x : 0.f;
-                dv[tt] = x * -dpt[mb][e];   // dpt holds rowdot - dP
+                float d = x * -dpt[mb][e];   // dpt holds rowdot - dP
+                keep_here(d);
+                dv[tt] = d;
                 if constexpr (tt == 3) {
                     dh[r4] = to_bf16(dv);
                     if constexpr ((r4 & 1) != 0)
@@ -330,13 +340,17 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                     ring[i % RA] = op_read(IC<i + RA - NSLOT>{});   // next tile
                 if constexpr (i < 2 * NB) {
                     constexpr int mb = i / NB, jj = i % NB, ks = jj >> 1;
-                    if constexpr ((jj & 1) != 0)
+                    if constexpr ((jj & 1) != 0) {
                         dpt[mb] = mfma32(a, of[ks], ks == 0 ? rdt : dpt[mb]);
-                    else
+                        keep_here(dpt[mb]);
+                    } else {
                         st[mb] = mfma32(a, qf[ks], ks == 0 ? z : st[mb]);
+                        keep_here(st[mb]);
+                    }
                 } else {
                     constexpr int jj = i - 2 * NB, kk = jj / DB, db = jj % DB;
                     acc[db] = mfma32(dsa[kk], a, acc[db]);
+                    keep_here(acc[db]);
                 }
                 // dS of keys 0-31 over slots NB .. 2NB-1, of keys 32-63 over
                 // 2NB .. 2NB+NQ-1 (16 elements each)
@@ -360,7 +374,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                     wait_loads<0>();
                     __builtin_amdgcn_s_barrier();
                     asm volatile("" ::: "memory");
-                    issue(t + NBUF - 1, cur == 0 ? NBUF - 1 : cur - 1);
+                    issue(cur == 0 ? NBUF - 1 : cur - 1);
                 }
                 if constexpr (i == NSLOT - RA - 1) {
 #pragma unroll

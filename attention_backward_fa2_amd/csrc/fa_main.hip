@@ -350,38 +350,90 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         const float *nr_ptr = nr_head;
         int n_r = 0, n_q0 = q0_first, n_left = total;
         const int64_t step_q = (int64_t)dq0 * p.q_ss, step_d = (int64_t)dq0 * p.do_ss;
-        auto issue = [&](int bf) {
-            const int rv = n_left > 0 ? min(kQTile, Lq - n_q0) : 0;
-            const uint32_t nq = rv ? (uint32_t)((rv - 1) * (int)p.q_ss * 2 + p.D * 2) : 0u;
-            const uint32_t nd = rv ? (uint32_t)((rv - 1) * (int)p.do_ss * 2 + p.D * 2) : 0u;
-            const auto rq = make_rsrc(nq_ptr, nq);
-            const auto rd = make_rsrc(nd_ptr, nd);
-            QBuf<DP> &qbuf = sm.buf[bf];
-#pragma unroll
-            for (int i = 0; i < L::PERW; ++i) {
-                const int ld = (w * L::PERW + i) * 1024;
-                load16_to_lds(rq, qbuf.q + ld, voq[i]);
-                load16_to_lds(rd, qbuf.dO + ld, vod[i]);
+        // Buffer descriptors of the next tile (bounded by its valid rows),
+        // formed in three parts (q, dO, row vectors) that can sit in
+        // different MFMA slots.
+        u32x4_rsrc rq_n, rd_n, rr_n;
+        int n_rv = 0;
+        auto prep_part = [&](auto pc) {
+            constexpr int part = decltype(pc)::value;
+            if constexpr (part == 0) {
+                keep_scalar_here(n_left, n_q0, nq_ptr);
+                n_rv = n_left > 0 ? min(kQTile, Lq - n_q0) : 0;
+                const uint32_t nq = n_rv ? (uint32_t)((n_rv - 1) * (int)p.q_ss * 2 + p.D * 2) : 0u;
+                rq_n = make_rsrc(nq_ptr, nq);
+                keep_scalar_here(rq_n, n_rv);
+            } else if constexpr (part == 1) {
+                keep_scalar_here(n_rv, nd_ptr);
+                const uint32_t nd = n_rv ? (uint32_t)((n_rv - 1) * (int)p.do_ss * 2 + p.D * 2) : 0u;
+                rd_n = make_rsrc(nd_ptr, nd);
+                keep_scalar_here(rd_n);
+            } else {
+                keep_scalar_here(n_rv, nr_ptr);
+                rr_n = make_rsrc(nr_ptr, (uint32_t)n_rv * 4);
+                keep_scalar_here(rr_n);
             }
-            // lse2 (even waves) / rowdot (odd waves): the two waves of a kind
-            // write the same values.
-            load4_to_lds(make_rsrc(nr_ptr, (uint32_t)rv * 4), (w & 1) ? qbuf.rowdot : qbuf.lse2,
-                         (uint32_t)lane * 4);
-            // advance to the next tile (branch-free selects)
-            --n_left;
-            const bool wrap = n_r == nm - 1;
-            n_r = wrap ? 0 : n_r + 1;
-            n_q0 = wrap ? q0_first : n_q0 + dq0;
-            nq_head = wrap ? nq_head + p.q_sh : nq_head;
-            nd_head = wrap ? nd_head + p.do_sh : nd_head;
-            nr_head = wrap ? nr_head + p.rows : nr_head;
-            nq_ptr = wrap ? nq_head : nq_ptr + step_q;
-            nd_ptr = wrap ? nd_head : nd_ptr + step_d;
-            nr_ptr = wrap ? nr_head : nr_ptr + dq0;
         };
-
         // Loads per wave per tile (each Q / dO wave load, and lse2 / rowdot).
         constexpr int LPT = 2 * L::PERW + 1;
+        // Load j of the next tile into buffer bf.
+        auto issue_one = [&](auto jc, int bf) {
+            constexpr int j = decltype(jc)::value;
+            QBuf<DP> &qbuf = sm.buf[bf];
+            if constexpr (j < 2 * L::PERW) {
+                constexpr int i = j >> 1;
+                const int ld = (w * L::PERW + i) * 1024;
+                if constexpr ((j & 1) != 0)
+                    load16_to_lds(rd_n, qbuf.dO + ld, vod[i]);
+                else
+                    load16_to_lds(rq_n, qbuf.q + ld, voq[i]);
+            } else {
+                // lse2 (even waves) / rowdot (odd waves): the two waves of a
+                // kind write the same values.
+                load4_to_lds(rr_n, (w & 1) ? qbuf.rowdot : qbuf.lse2, (uint32_t)lane * 4);
+            }
+        };
+        // Move the row pointers on to the tile after (branch-free selects),
+        // in three parts like the descriptors.
+        int n_wrap = 0;
+        auto advance_part = [&](auto pc) {
+            constexpr int part = decltype(pc)::value;
+            if constexpr (part == 0) {
+                keep_scalar_here(n_left, n_r, n_q0);
+                --n_left;
+                n_wrap = __builtin_amdgcn_readfirstlane(n_r == nm - 1 ? 1 : 0);   // scalar
+                n_r = n_wrap ? 0 : n_r + 1;
+                n_q0 = n_wrap ? q0_first : n_q0 + dq0;
+                keep_scalar_here(n_left, n_r, n_q0, n_wrap);
+            } else if constexpr (part == 1) {
+                keep_scalar_here(n_wrap, nq_head, nq_ptr, nd_head, nd_ptr);
+                nq_head = n_wrap ? nq_head + p.q_sh : nq_head;
+                nd_head = n_wrap ? nd_head + p.do_sh : nd_head;
+                nq_ptr = n_wrap ? nq_head : nq_ptr + step_q;
+                nd_ptr = n_wrap ? nd_head : nd_ptr + step_d;
+                keep_scalar_here(nq_head, nq_ptr, nd_head, nd_ptr);
+            } else {
+                keep_scalar_here(n_wrap, nr_head, nr_ptr);
+                nr_head = n_wrap ? nr_head + p.rows : nr_head;
+                nr_ptr = n_wrap ? nr_head : nr_ptr + dq0;
+                keep_scalar_here(nr_head, nr_ptr);
+            }
+        };
+        // Advance and prepare parts in order: three of each.
+        auto setup_part = [&](auto pc) {
+            constexpr int part = decltype(pc)::value;
+            if constexpr (part < 3)
+                advance_part(IC<part>{});
+            else
+                prep_part(IC<part - 3>{});
+        };
+        // All loads of the next tile at once, then prepare the one after.
+        auto issue = [&](int bf) {
+            static_for<LPT>([&](auto jc) { issue_one(jc, bf); });
+            static_for<6>([&](auto pc) { setup_part(pc); });
+        };
+
+        static_for<3>([&](auto pc) { prep_part(pc); });
 #pragma unroll
         for (int t = 0; t < NBUF - 1; ++t)
             issue(t);
@@ -413,6 +465,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         // first read of the next tile.
         static_assert(NB >= 8 && NG >= 8 && NSLOT % RA == 0, "slot plan");
         static_assert(BAR >= 2 * NB && BAR + RA < NSLOT, "barrier slot");
+        static_assert(BAR + (LPT + 1) / 2 + 6 <= NSLOT, "tile loads after the barrier");
 
         // A operand of slot i of a tile (offsets of the tile's buffer).
         auto op_read = [&](auto ic) -> bf16x8 {
@@ -491,8 +544,11 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 float x = __builtin_amdgcn_exp2f(s[mb][e] * p.scale_log2 - l2v[r4][t]);
                 if constexpr (decltype(maskc)::value)
                     x = qc + t >= limv ? x : 0.f;
+                float d = x * -dp[mb][e];   // dp holds rowdot - dP
+                keep_here(x);
+                keep_here(d);
                 pv[t] = x;
-                dv[t] = x * -dp[mb][e];   // dp holds rowdot - dP
+                dv[t] = d;
                 if constexpr (t == 3) {
                     ph[r4] = to_bf16(pv);
                     dh[r4] = to_bf16(dv);
@@ -538,10 +594,13 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     constexpr int jj = (i - 2 * NB) % NG;
                     constexpr int kk = 2 * ((i - 2 * NB) / NG) + jj / (2 * DB);
                     constexpr int db = (jj % (2 * DB)) >> 1;
-                    if constexpr ((jj & 1) != 0)
+                    if constexpr ((jj & 1) != 0) {
                         dk_acc[db] = mfma32(a, dsb[kk], dk_acc[db]);
-                    else
+                        keep_here_acc(dk_acc[db]);
+                    } else {
                         dv_acc[db] = mfma32(a, pb[kk], dv_acc[db]);
+                        keep_here_acc(dv_acc[db]);
+                    }
                 }
                 // vector work: the 16 elements of P, dS of block 0 spread over
                 // slots NB .. 2NB-1 (the row vectors of block 1 are read in
@@ -581,8 +640,20 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     wait_loads<0>();
                     __builtin_amdgcn_s_barrier();
                     asm volatile("" ::: "memory");
-                    issue(cur == 0 ? NBUF - 1 : cur - 1);
                 }
+                // The loads of the tile after next, two per slot from the
+                // barrier on, into the buffer every wave has finished with;
+                // then the pointers and descriptors for the tile after that
+                // (the scalar work spread over slots in the MFMAs' shadow).
+                if constexpr (!FUSED && i >= BAR && i < BAR + (LPT + 1) / 2) {
+                    constexpr int j0 = 2 * (i - BAR);
+                    const int bf = cur == 0 ? NBUF - 1 : cur - 1;
+                    issue_one(IC<j0>{}, bf);
+                    if constexpr (j0 + 1 < LPT)
+                        issue_one(IC<j0 + 1>{}, bf);
+                }
+                if constexpr (!FUSED && i >= BAR + (LPT + 1) / 2 && i < BAR + (LPT + 1) / 2 + 6)
+                    setup_part(IC<i - BAR - (LPT + 1) / 2>{});
                 if constexpr (!FUSED && i > BAR && i <= BAR + 4)
                     read_rowdot(0, i - BAR - 1);   // next tile (buffer published at BAR)
                 if constexpr (!FUSED && i == NSLOT - RA - 1) {

@@ -71,6 +71,42 @@ __device__ inline void mfma_settle(f32x16 &s, f32x16 &t)
     asm volatile("s_nop 11" : "+v"(s), "+v"(t));
 }
 
+// Keeps the computation of x at this point of the instruction stream.  The
+// compiler's basic-block scheduler places pure arithmetic next to its first
+// use, across the scheduling fences that separate the MFMA slots; an empty
+// volatile statement that takes x as an operand ties it to the slot.
+__device__ inline void keep_here(float &x)
+{
+    asm volatile("" : "+v"(x));
+}
+
+// The same for an MFMA result (ordinary / accumulation registers): keeps the
+// product in its slot.
+__device__ inline void keep_here(f32x16 &x)
+{
+    asm volatile("" : "+v"(x));
+}
+
+__device__ inline void keep_here_acc(f32x16 &x)
+{
+    asm volatile("" : "+a"(x));
+}
+
+// The same for wave-uniform values in scalar registers: placed before a
+// computation, it keeps the computation from being hoisted above this point;
+// placed after, from being sunk below it.
+template <class T>
+__device__ inline void keep_scalar_one(T &x)
+{
+    asm volatile("" : "+s"(x));
+}
+
+template <class... T>
+__device__ inline void keep_scalar_here(T &...x)
+{
+    (keep_scalar_one(x), ...);
+}
+
 // fp32 -> bf16 (round to nearest even) of four values: two packed
 // hardware converts.
 __device__ inline bf16x4 to_bf16(f32x4 x)
