@@ -1,7 +1,8 @@
-"""Python binding of the MI355X attention-backward C ABI (include/fa_bwd.h).
+"""Python binding of the MI355X attention C ABI (include/fa_bwd.h for the
+backward, include/fa_fwd.h for the forward).
 
 Argument marshalling only: torch tensors supply device memory and the current
-HIP stream; every step of the backward runs in the library's gfx950 kernels.
+HIP stream; every step runs in the library's gfx950 kernels.
 There is no CPU fallback -- if the built library is missing this module
 raises instead of computing anything.
 """
@@ -64,9 +65,29 @@ class FaBwdWsLayout(ctypes.Structure):
     ]
 
 
+class FaFwdArgs(ctypes.Structure):
+    """Mirror of fa_fwd_args."""
+    _fields_ = [
+        ("dtype", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("seqlen_q", ctypes.c_int32), ("seqlen_k", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32), ("num_heads_k", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+        ("total_q", ctypes.c_int64), ("total_k", ctypes.c_int64),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
+        ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+        ("lse_stride", ctypes.c_int64 * 2),
+        ("softmax_scale", ctypes.c_float),
+        ("causal", ctypes.c_int32),
+    ]
+
+
 EXPORTED = ("fa_bwd", "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_dq", "fa_bwd_dq_convert",
             "fa_bwd_validate", "fa_bwd_workspace_size", "fa_bwd_workspace_layout",
-            "fa_bwd_last_error", "fa_bwd_abi_version")
+            "fa_bwd_last_error", "fa_bwd_abi_version", "fa_fwd", "fa_fwd_validate")
 
 _LIB = None
 
@@ -95,6 +116,11 @@ def load_library(path: str = LIB_PATH):
     lib.fa_bwd_last_error.restype = ctypes.c_char_p
     lib.fa_bwd_abi_version.argtypes = []
     lib.fa_bwd_abi_version.restype = ctypes.c_int32
+    PF = ctypes.POINTER(FaFwdArgs)
+    lib.fa_fwd.argtypes = [PF, ctypes.c_void_p]
+    lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_fwd_validate.argtypes = [PF]
+    lib.fa_fwd_validate.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -236,3 +262,52 @@ def fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
         workspace = alloc_workspace(args, q.device)
     run(args, "all", stream)
     return workspace
+
+
+def make_fwd_args(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q=None,
+                  cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None) -> FaFwdArgs:
+    """Fill fa_fwd_args from tensors (layouts as in make_args)."""
+    varlen = cu_seqlens_q is not None or cu_seqlens_k is not None
+    a = FaFwdArgs()
+    a.dtype = FA_DTYPE_BF16 if q.dtype == torch.bfloat16 else 99
+    if varlen:
+        if cu_seqlens_q is None or cu_seqlens_k is None:
+            raise ValueError("cu_seqlens_q and cu_seqlens_k go together")
+        a.batch = cu_seqlens_q.numel() - 1
+        a.seqlen_q, a.seqlen_k = int(max_seqlen_q), int(max_seqlen_k)
+        a.num_heads, a.head_dim = q.shape[1], q.shape[2]
+        a.num_heads_k = k.shape[1]
+        a.total_q, a.total_k = q.shape[0], k.shape[0]
+        a.cu_seqlens_q, a.cu_seqlens_k = _ptr(cu_seqlens_q), _ptr(cu_seqlens_k)
+    else:
+        a.batch, a.seqlen_q, a.num_heads, a.head_dim = q.shape
+        a.seqlen_k, a.num_heads_k = k.shape[1], k.shape[2]
+    for t in (q, k, v, out):
+        if t.stride(-1) != 1:
+            raise ValueError("the head_dim stride must be 1")
+    a.q, a.k, a.v, a.out = (_ptr(x) for x in (q, k, v, out))
+    a.lse = _ptr(lse)
+    for name, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", out)):
+        getattr(a, name)[:] = _strides3(t, varlen)
+    a.lse_stride[:] = (lse.stride(0), lse.stride(1))
+    a.softmax_scale = float(softmax_scale)
+    a.causal = int(bool(causal))
+    return a
+
+
+def validate_fwd(args: FaFwdArgs) -> int:
+    return load_library().fa_fwd_validate(ctypes.byref(args))
+
+
+def run_fwd(args: FaFwdArgs, stream=None):
+    """Enqueue the forward."""
+    _check(load_library().fa_fwd(ctypes.byref(args), _stream(stream)))
+
+
+def fa_fwd(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q=None, cu_seqlens_k=None,
+           max_seqlen_q=None, max_seqlen_k=None, stream=None):
+    """O and the natural-log LSE of attention, written into out (layout of q)
+    and lse ((B, H, Sq) fp32; packed: (num_seqs, H, max_seqlen_q))."""
+    args = make_fwd_args(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q, cu_seqlens_k,
+                         max_seqlen_q, max_seqlen_k)
+    run_fwd(args, stream)

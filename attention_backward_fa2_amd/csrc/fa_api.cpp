@@ -1,6 +1,7 @@
-// fa_api.cpp -- host side of the C ABI in include/fa_bwd.h: argument
-// validation (all on the host, before any launch), workspace layout, and the
-// three-kernel launch sequence on the caller's stream.
+// fa_api.cpp -- host side of the C ABI in include/fa_bwd.h and
+// include/fa_fwd.h: argument validation (all on the host, before any launch),
+// the backward's workspace layout and launch sequence, and the forward's
+// launch, on the caller's stream.
 //
 // Checks follow the validations listed on the Triton FA2 teaching page
 // (AttentionMetadata.validate_inputs: null pointers, head-count divisibility,
@@ -14,6 +15,7 @@
 #include <string>
 
 #include "../../include/fa_bwd.h"
+#include "../../include/fa_fwd.h"
 #include "fa_internal.h"
 
 namespace {
@@ -122,6 +124,9 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
         return fail(FA_ERR_INVALID_ARG, "q / dout row stride is smaller than head_dim");
     if (a->q_stride[1] >= (int64_t(1) << 24) || a->do_stride[1] >= (int64_t(1) << 24))
         return fail(FA_ERR_UNSUPPORTED, "q / dout row stride >= 2^24 elements is not supported");
+    // The dQ kernel addresses a 64-key tile with 32-bit byte offsets too.
+    if (a->k_stride[1] >= (int64_t(1) << 24) || a->v_stride[1] >= (int64_t(1) << 24))
+        return fail(FA_ERR_UNSUPPORTED, "k / v row stride >= 2^24 elements is not supported");
     if (a->softmax_scale != a->softmax_scale || std::isinf(a->softmax_scale))
         return fail(FA_ERR_INVALID_ARG, "softmax_scale is not finite");
     if ((a->causal != 0 && a->causal != 1) || (a->deterministic != 0 && a->deterministic != 1) ||
@@ -255,9 +260,117 @@ fa_status run(const fa_bwd_args *a, void *stream, int steps)
     return FA_OK;
 }
 
+// Forward: the same checks on the subset of tensors it touches.
+fa_status make_fwd_plan(const fa_fwd_args *a, fa::Params *pp, int *dpad_out)
+{
+    if (!a)
+        return fail(FA_ERR_INVALID_ARG, "args is NULL");
+    if (a->dtype != FA_DTYPE_BF16)
+        return fail(FA_ERR_UNSUPPORTED, "dtype %d unsupported (only bf16)", a->dtype);
+    if (a->batch < 0 || a->seqlen_q < 0 || a->seqlen_k < 0)
+        return fail(FA_ERR_INVALID_ARG, "negative batch or sequence length");
+    if (a->num_heads <= 0 || a->num_heads_k <= 0 || a->head_dim <= 0)
+        return fail(FA_ERR_INVALID_ARG, "num_heads, num_heads_k and head_dim must be positive");
+    if (a->num_heads % a->num_heads_k != 0)
+        return fail(FA_ERR_INVALID_ARG, "num_heads (%d) is not a multiple of num_heads_k (%d)",
+                    a->num_heads, a->num_heads_k);
+    if (a->head_dim > 256)
+        return fail(FA_ERR_UNSUPPORTED, "head_dim %d > 256", a->head_dim);
+    if (a->head_dim % 8 != 0)
+        return fail(FA_ERR_UNSUPPORTED, "head_dim %d is not a multiple of 8 (pad it first)",
+                    a->head_dim);
+    const int dpad = pad_head_dim(a->head_dim);
+    if (!dpad)
+        return fail(FA_ERR_UNSUPPORTED, "head_dim %d > 128 is not built", a->head_dim);
+    const bool varlen = a->cu_seqlens_q || a->cu_seqlens_k;
+    if (varlen && !(a->cu_seqlens_q && a->cu_seqlens_k))
+        return fail(FA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k must be given together");
+    if (varlen && (a->total_q < 0 || a->total_k < 0))
+        return fail(FA_ERR_INVALID_ARG, "negative total_q / total_k");
+    const int64_t nq = varlen ? a->total_q : (int64_t)a->batch * a->seqlen_q;
+    const int64_t nk = varlen ? a->total_k : (int64_t)a->batch * a->seqlen_k;
+    if (nq > 0 && (!a->q || !a->out || !a->lse))
+        return fail(FA_ERR_INVALID_ARG, "a query-side tensor pointer is NULL");
+    if (nk > 0 && (!a->k || !a->v))
+        return fail(FA_ERR_INVALID_ARG, "a key-side tensor pointer is NULL");
+    const void *ptrs[] = {a->q, a->k, a->v, a->out};
+    const char *names[] = {"q", "k", "v", "out"};
+    for (int i = 0; i < 4; ++i)
+        if (!aligned(ptrs[i], 16))
+            return fail(FA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+    if (!aligned(a->lse, 4))
+        return fail(FA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+    fa_status st;
+    if ((st = check_strides("q", a->q_stride, varlen)) ||
+        (st = check_strides("k", a->k_stride, varlen)) ||
+        (st = check_strides("v", a->v_stride, varlen)) ||
+        (st = check_strides("out", a->o_stride, varlen)))
+        return st;
+    // A 64-key tile is addressed with 32-bit byte offsets.
+    if (a->k_stride[1] >= (int64_t(1) << 24) || a->v_stride[1] >= (int64_t(1) << 24))
+        return fail(FA_ERR_UNSUPPORTED, "k / v row stride >= 2^24 elements is not supported");
+    if (a->softmax_scale != a->softmax_scale || std::isinf(a->softmax_scale))
+        return fail(FA_ERR_INVALID_ARG, "softmax_scale is not finite");
+    if (a->causal != 0 && a->causal != 1)
+        return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+
+    fa::Params &p = *pp;
+    std::memset(&p, 0, sizeof p);
+    p.q = (const uint16_t *)a->q;
+    p.k = (const uint16_t *)a->k;
+    p.v = (const uint16_t *)a->v;
+    p.o_w = (uint16_t *)a->out;
+    p.lse_w = a->lse;
+    p.cu_q = a->cu_seqlens_q;
+    p.cu_k = a->cu_seqlens_k;
+#define STR(dst, src) p.dst##_sb = a->src[0], p.dst##_ss = a->src[1], p.dst##_sh = a->src[2]
+    STR(q, q_stride);
+    STR(k, k_stride);
+    STR(v, v_stride);
+    STR(o, o_stride);
+#undef STR
+    p.lse_sb = a->lse_stride[0];
+    p.lse_sh = a->lse_stride[1];
+    p.batch = a->batch;
+    p.H = a->num_heads;
+    p.Hk = a->num_heads_k;
+    p.G = a->num_heads / a->num_heads_k;
+    p.D = a->head_dim;
+    p.Sq = a->seqlen_q;
+    p.Sk = a->seqlen_k;
+    p.varlen = varlen ? 1 : 0;
+    p.rows = nq;
+    p.scale = a->softmax_scale;
+    p.scale_log2 = (float)((double)a->softmax_scale * 1.4426950408889634);
+    p.causal = a->causal;
+    *dpad_out = dpad;
+    g_last_error.clear();
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+fa_status fa_fwd_validate(const fa_fwd_args *a)
+{
+    fa::Params p;
+    int dpad;
+    return make_fwd_plan(a, &p, &dpad);
+}
+
+fa_status fa_fwd(const fa_fwd_args *a, void *stream)
+{
+    fa::Params p;
+    int dpad;
+    fa_status st = make_fwd_plan(a, &p, &dpad);
+    if (st)
+        return st;
+    if (p.batch > 0 && p.Sq > 0 && p.rows > 0)
+        return hip_status(fa::launch_fwd(p, dpad, (hipStream_t)stream), "forward launch");
+    return FA_OK;
+}
+
 
 size_t fa_bwd_workspace_size(const fa_bwd_args *a)
 {

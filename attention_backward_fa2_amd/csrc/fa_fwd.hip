@@ -1,0 +1,402 @@
+// fa_fwd.hip -- query-stationary attention forward on gfx950 (CDNA4): the
+// output O and the per-row log-sum-exp that the backward consumes.
+//
+// For each query row i the forward computes the softmax of the scaled scores
+// over the visible keys and O_i = sum_j P_ij V_j, keeping only a running
+// maximum, a running sum and the unnormalised output while it streams key
+// tiles (the online softmax of the Triton FA2 teaching page's forward inner
+// loop: per key block the block maximum, exponentials of the shifted scores
+// in base 2, the partial output and sum rescaled by exp2(old max - new max),
+// one division by the sum at the end; its outer kernel stores max + log2(sum)
+// for the backward).  Unlike that page, Q is not pre-scaled and rounded to
+// bf16: the scale enters in fp32, and the stored LSE is the natural log the
+// backward's interface expects.
+//
+// Layout of the work (the same as the query-stationary dQ kernel): one
+// workgroup of 8 wave64s (two per SIMD) owns 256 query rows of one head;
+// wave w owns rows 32w .. 32w+31, whose Q rows stay in registers as the B
+// operand of S^T = K Q^T over 64-key tiles.  The accumulator of S^T holds
+// one query row and 16 keys per lane, so the running maximum and sum are
+// one register each (the two lane halves hold the two halves of a block's
+// keys and combine with one cross-half exchange), and P (bf16) is directly
+// the B operand of O^T += V^T P^T, with V^T read through transposing LDS
+// reads; the accumulator of O^T again holds one query row per lane, so the
+// rescale factor is lane-local.
+//
+// The rescale is lazy: the running maximum only moves (and O^T and the sum
+// are rescaled) when some row of the wave sees a tile maximum more than
+// 2^8 above it, so P stays below 256 and the exponentials stay exact in
+// fp32; the final division by the sum makes the result independent of which
+// maximum was used.
+//
+// K and V tiles arrive by buffer loads straight into the swizzled LDS layout
+// of fa_mfma.h, three buffers deep; the tile body is a fixed sequence of
+// MFMA slots: S^T of keys 0-31, S^T of keys 32-63 (with the maximum of keys
+// 0-31), then the O^T k-steps, with P of keys 0-31 formed before them and P
+// of keys 32-63 alongside the first half.
+#include "fa_mfma.h"
+
+namespace fa {
+
+constexpr int kFwdWaves = 8;                 // two waves per SIMD
+constexpr int kFwdThreads = 64 * kFwdWaves;
+constexpr int kFwdRows = 32 * kFwdWaves;     // query rows per workgroup
+constexpr int kFwdKeys = 64;                 // keys per streamed tile
+
+template <int DP>
+struct __attribute__((aligned(16))) FwdKV {
+    uint8_t k[Tile64<DP>::BYTES];
+    uint8_t v[Tile64<DP>::BYTES];
+};
+
+template <int DP>
+struct __attribute__((aligned(16))) FwdSmem {
+    FwdKV<DP> buf[3];
+};
+
+template <int DP>
+__global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
+{
+    constexpr int KS = DP / 16;                  // k-steps over the head dim
+    constexpr int DB = DP / 32;                  // 32-wide head-dim blocks
+    constexpr int NBUF = 3;
+    using L = Tile64<DP>;
+    constexpr int PERW = L::NLOAD / kFwdWaves;   // 1 KB wave loads per tensor per wave
+    static_assert(PERW >= 1 && L::NLOAD % kFwdWaves == 0, "tile load split");
+    __shared__ FwdSmem<DP> sm;
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, g2 = lane >> 5;
+
+    // Workgroup -> (query tile, batch, KV head, head in group), longest
+    // (last query tile under the causal mask) first; the (batch, KV head)
+    // index is the fastest.
+    const int nbg = p.batch * p.Hk;
+    const int nqt = (p.Sq + kFwdRows - 1) / kFwdRows;
+    const int lin = blockIdx.x;
+    const int bg = lin % nbg;
+    const int hh = (lin / nbg) % p.G;
+    const int mt = nqt - 1 - lin / (nbg * p.G);
+    const int hk = bg % p.Hk, b = bg / p.Hk;
+    const int h = hk * p.G + hh;
+
+    const SeqInfo si = seq_info(p, b);
+    const int q0 = mt * kFwdRows;
+    if (q0 >= si.Lq)
+        return;
+    const int Lq = si.Lq, Lk = si.Lk;
+    const int off = Lk - Lq;                     // bottom-right causal offset
+    const int qrow = q0 + 32 * w + l32;          // this lane's query row
+    const bool qok = qrow < Lq;
+
+    // Key tiles visible to some row of this query tile.
+    const int q_last = min(q0 + kFwdRows, Lq) - 1;
+    int nkt = (Lk + kFwdKeys - 1) / kFwdKeys;
+    if (p.causal)
+        nkt = min(nkt, max(0, (q_last + off + kFwdKeys) / kFwdKeys));
+    // Visible keys of this lane's row: key <= klim.
+    const int klim = qok ? (p.causal ? min(Lk - 1, qrow + off) : Lk - 1) : -1;
+
+    // Global byte offsets of the 16-byte chunk each lane loads for wave
+    // load i (LDS row pr holds tile chunk (lane % PCH) ^ swz(pr)).
+    uint32_t vok[PERW], vov[PERW];
+#pragma unroll
+    for (int i = 0; i < PERW; ++i) {
+        const int pr = (w * PERW + i) * L::RPL + lane / L::PCH;
+        const int c = (lane % L::PCH) ^ swz<L::PCH>(pr);
+        const bool ok = c * 8 < p.D;
+        vok[i] = ok ? (uint32_t)(pr * (int)p.k_ss * 2 + c * 16) : kOutOfRange;
+        vov[i] = ok ? (uint32_t)(pr * (int)p.v_ss * 2 + c * 16) : kOutOfRange;
+    }
+    // Loads of the next key tile into buffer bf (tiles strictly in order;
+    // past the last tile: empty bound, zeros, no memory access).
+    const uint16_t *k_next = p.k + hk * p.k_sh + row_offset(p, b, si.tok_k, 0, p.k_sb, p.k_ss);
+    const uint16_t *v_next = p.v + hk * p.v_sh + row_offset(p, b, si.tok_k, 0, p.v_sb, p.v_ss);
+    int n_next = 0, n_left = nkt;
+    const int64_t kstep = (int64_t)kFwdKeys * p.k_ss, vstep = (int64_t)kFwdKeys * p.v_ss;
+    auto issue = [&](int bf) {
+        keep_scalar_here(n_next, n_left, k_next, v_next);
+        const int kv = n_left > 0 ? min(kFwdKeys, Lk - n_next) : 0;
+        const uint32_t nk = kv ? (uint32_t)((kv - 1) * (int)p.k_ss * 2 + p.D * 2) : 0u;
+        const uint32_t nv = kv ? (uint32_t)((kv - 1) * (int)p.v_ss * 2 + p.D * 2) : 0u;
+        const auto rk = make_rsrc(k_next, nk);
+        const auto rv = make_rsrc(v_next, nv);
+        n_next += kFwdKeys;
+        --n_left;
+        k_next += kstep;
+        v_next += vstep;
+        keep_scalar_here(n_next, n_left, k_next, v_next);
+        FwdKV<DP> &kb = sm.buf[bf];
+#pragma unroll
+        for (int i = 0; i < PERW; ++i) {
+            const int ld = (w * PERW + i) * 1024;
+            load16_to_lds(rk, kb.k + ld, vok[i]);
+            load16_to_lds(rv, kb.v + ld, vov[i]);
+        }
+    };
+    if (nkt > 0) {
+        issue(0);
+        issue(1);
+    }
+
+    // ---- Q rows of the lane (B operand of S^T) ----
+    bf16x8 qf[KS];
+    {
+        const int qr = qok ? qrow : Lq - 1;
+        const uint16_t *qp = p.q + row_offset(p, b, si.tok_q, qr, p.q_sb, p.q_ss) + h * p.q_sh;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int d0 = 16 * ks + 8 * g2;
+            u32x4 a = 0;
+            if (qok && d0 < p.D)
+                a = *reinterpret_cast<const u32x4 *>(qp + d0);
+            qf[ks] = __builtin_bit_cast(bf16x8, a);
+        }
+    }
+    wait_loads();   // land them and the first key tiles before the tile loop
+
+    f32x16 acc[DB];                 // O^T: column = the lane's row, rows = d
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+        zero(acc[db]);
+    // Running maximum of S * scale * log2(e) (base-2 units) and the lane's
+    // part of the running sum of P (the lane half g2 sums its half of the
+    // keys; the halves are added at the end).
+    float mrun = -INFINITY, lsum = 0.f;
+
+    if (nkt > 0) {
+        // LDS byte offsets of this lane's operand reads in the current
+        // buffer: gq[ks] the 16-byte read of K row l32, tile chunk
+        // 2*ks + g2 (+ 32 rows per key block); tq[db][h] the transposing
+        // read of V rows 4*g2 + rr + 8*h (+ 16 rows per k-step), tile chunk
+        // 4*db + 2*h16 + b1, 8-byte half c16 & 1 (V is BYTES after K).
+        constexpr int BUFB = (int)sizeof(FwdKV<DP>);
+        int gq[KS], tq[DB][2];
+        {
+            const int sw = swz<L::PCH>(l32);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                gq[ks] = l32 * L::PB + (((2 * ks + g2) ^ sw) << 4);
+            const int c16 = lane & 15, rr = c16 >> 2, h16 = (lane >> 4) & 1, b1 = (c16 >> 1) & 1;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int row = 4 * g2 + rr + 8 * hf;
+                    tq[db][hf] = L::BYTES + row * L::PB +
+                                 (((4 * db + 2 * h16 + b1) ^ swz<L::PCH>(row)) << 4) + (c16 & 1) * 8;
+                }
+        }
+        const uint8_t *lds = reinterpret_cast<const uint8_t *>(&sm.buf[0]);
+
+        // ---- Each key tile as NSLOT MFMA slots: ----
+        //   S^T of keys 0-31 (k-steps over D)        slots 0 .. NB-1
+        //   S^T of keys 32-63                        NB .. 2NB-1      + maximum of keys 0-31
+        //   (tile maximum, lazy rescale, P of keys 0-31 at the end of slot 2NB-1)
+        //   O^T k-steps over keys 0-31               2NB .. 2NB+2DB-1 + P of keys 32-63
+        //   O^T k-steps over keys 32-63              2NB+2DB .. NSLOT-1
+        constexpr int NB = KS;
+        constexpr int NO = 4 * DB;
+        constexpr int NSLOT = 2 * NB + NO;
+        constexpr int RA = 4;                        // read-ahead (divides NSLOT)
+        constexpr int BAR = (2 * NB + NO / 2 < NSLOT - RA) ? 2 * NB + NO / 2 : NSLOT - RA - 1;
+        static_assert(NSLOT % RA == 0, "ring length must divide the slot count");
+        static_assert(BAR >= 2 * NB - RA && BAR + RA < NSLOT, "barrier slot");
+
+        auto op_read = [&](auto ic) -> bf16x8 {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (i < 2 * NB) {
+                constexpr int mb = i / NB, ks = i % NB;
+                return lds16b(lds + gq[ks] + 32 * mb * L::PB);
+            } else {
+                constexpr int jj = i - 2 * NB, kk = jj / DB, db = jj % DB;
+                return tr_pair(lds + tq[db][0] + 16 * kk * L::PB, lds + tq[db][1] + 16 * kk * L::PB);
+            }
+        };
+        __syncthreads();
+        bf16x8 ring[RA];
+        static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
+
+        // Smallest visible-key limit over the wave's rows (-1 if any row is
+        // past the end): key tiles wholly at or below it need no mask.
+        const int r0w = q0 + 32 * w;
+        const int kmin_w = r0w + 31 < Lq ? (p.causal ? min(Lk - 1, r0w + off) : Lk - 1) : -1;
+        const int nfull = min(nkt, max(0, (kmin_w + 1) / kFwdKeys));
+        const float c2 = p.scale_log2;
+
+        int cur = 0;
+        auto tile = [&](int t, auto maskc) {
+            constexpr bool MASK = decltype(maskc)::value;
+            const int n0 = t * kFwdKeys;
+            // element (32*mb + 8*r4 + tt) of the lane's keys (+ 4*g2) is
+            // visible iff it is <= kthr
+            const int kthr = klim - n0 - 4 * g2;
+            const int delta = cur == NBUF - 1 ? -(NBUF - 1) * BUFB : BUFB;
+
+            f32x16 st[2];
+            const f32x16 z = {};
+            float mx0 = -INFINITY, mx1 = -INFINITY;   // raw-score maxima of the two blocks
+            float mu = 0.f;                           // maximum used for P (base 2)
+            bf16x4 ph[4];
+            bf16x8 pb[4];
+            f32x4 pv;
+
+            auto visible = [&](auto mbc, auto ec) -> bool {
+                constexpr int mb = decltype(mbc)::value, e = decltype(ec)::value;
+                if constexpr (MASK)
+                    return 32 * mb + 8 * (e >> 2) + (e & 3) <= kthr;
+                else
+                    return true;
+            };
+            auto max_elem = [&](auto mbc, auto ec) {
+                constexpr int mb = decltype(mbc)::value, e = decltype(ec)::value;
+                const float s = visible(mbc, ec) ? st[mb][e] : -INFINITY;
+                float &m = mb == 0 ? mx0 : mx1;
+                m = fmaxf(m, s);
+                keep_here(m);
+            };
+            auto p_elem = [&](auto mbc, auto ec) {
+                constexpr int mb = decltype(mbc)::value, e = decltype(ec)::value;
+                constexpr int r4 = e >> 2, tt = e & 3;
+                float x = __builtin_amdgcn_exp2f(st[mb][e] * c2 - mu);
+                if constexpr (MASK)
+                    x = visible(mbc, ec) ? x : 0.f;
+                keep_here(x);
+                lsum += x;
+                pv[tt] = x;
+                if constexpr (tt == 3) {
+                    ph[r4] = to_bf16(pv);
+                    if constexpr ((r4 & 1) != 0)
+                        pb[2 * mb + (r4 >> 1)] = concat(ph[r4 - 1], ph[r4]);
+                }
+            };
+
+            static_for<NSLOT>([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                const bf16x8 a = ring[i % RA];
+                if constexpr (i + RA < NSLOT)
+                    ring[i % RA] = op_read(IC<i + RA>{});
+                else
+                    ring[i % RA] = op_read(IC<i + RA - NSLOT>{});   // next tile
+                if constexpr (i < 2 * NB) {
+                    constexpr int mb = i / NB, ks = i % NB;
+                    st[mb] = mfma32(a, qf[ks], ks == 0 ? z : st[mb]);
+                    keep_here(st[mb]);
+                } else {
+                    constexpr int jj = i - 2 * NB, kk = jj / DB, db = jj % DB;
+                    acc[db] = mfma32(a, pb[kk], acc[db]);
+                    keep_here(acc[db]);
+                }
+                // maximum of keys 0-31 over the S^T slots of keys 32-63
+                if constexpr (i >= NB && i < 2 * NB) {
+                    constexpr int u = i - NB;
+                    static_for<16 * (u + 1) / NB - 16 * u / NB>(
+                        [&](auto ec) { max_elem(IC<0>{}, IC<16 * u / NB + decltype(ec)::value>{}); });
+                }
+                if constexpr (i == 2 * NB - 1) {
+                    // tile maximum of the row (both blocks, both lane halves)
+                    static_for<16>([&](auto ec) { max_elem(IC<1>{}, ec); });
+                    float mt = fmaxf(mx0, mx1);
+                    mt = fmaxf(mt, __shfl_xor(mt, 32));
+                    const float mt2 = mt * c2;        // -inf if no key of the tile is visible
+                    // Lazy rescale: move the running maximum only if some row
+                    // of the wave would see P above 2^8 otherwise.
+                    const bool need = mt2 > mrun + 8.f;
+                    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+                        const float mnew = fmaxf(mrun, mt2);
+                        const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mrun - mnew);
+                        mrun = mnew;
+                        lsum *= alpha;
+#pragma unroll
+                        for (int db = 0; db < DB; ++db)
+                            acc[db] *= alpha;
+                    }
+                    mu = mrun == -INFINITY ? 0.f : mrun;
+                    static_for<16>([&](auto ec) { p_elem(IC<0>{}, ec); });
+                }
+                // P of keys 32-63 over the O^T slots of keys 0-31
+                if constexpr (i >= 2 * NB && i < 2 * NB + 2 * DB) {
+                    constexpr int u = i - 2 * NB;
+                    static_for<16 * (u + 1) / (2 * DB) - 16 * u / (2 * DB)>(
+                        [&](auto ec) { p_elem(IC<1>{}, IC<16 * u / (2 * DB) + decltype(ec)::value>{}); });
+                }
+                if constexpr (i == BAR) {
+                    // every 16-byte read of this tile is issued: move them on
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        gq[ks] += delta;
+                    // the only loads in flight are the next tile's; a bare
+                    // barrier (reads in flight touch this tile's buffer only)
+                    wait_loads<0>();
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                    issue(cur == 0 ? NBUF - 1 : cur - 1);
+                }
+                if constexpr (i == NSLOT - RA - 1) {
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        tq[db][0] += delta;
+                        tq[db][1] += delta;
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            cur = cur == NBUF - 1 ? 0 : cur + 1;
+        };
+        int t = 0;
+        for (; t < nfull; ++t)
+            tile(t, std::false_type{});
+        for (; t < nkt; ++t)
+            tile(t, std::true_type{});
+        // loads issued past the last tile must land before LDS is released
+        wait_loads<0>();
+    }
+
+    // ---- O = O^T / sum, LSE = (max + log2(sum)) * ln 2 (natural log of the
+    //      scaled scores); rows without a visible key: O = 0, LSE = -inf. ----
+    const float l = lsum + __shfl_xor(lsum, 32);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    if (qok) {
+        uint16_t *orow = p.o_w + row_offset(p, b, si.tok_q, qrow, p.o_sb, p.o_ss) + h * p.o_sh;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d = 32 * db + 8 * j + 4 * g2;
+                if (d < p.D) {
+                    f32x4 o4;
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt)
+                        o4[tt] = acc[db][4 * j + tt] * inv;
+                    *reinterpret_cast<bf16x4 *>(orow + d) = to_bf16(o4);
+                }
+            }
+        if (g2 == 0)
+            p.lse_w[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + qrow] =
+                l > 0.f ? (mrun + __builtin_amdgcn_logf(l)) * 0.6931471805599453f : -INFINITY;
+    }
+}
+
+hipError_t launch_fwd(const Params &p, int dpad, hipStream_t st)
+{
+    const int nqt = (p.Sq + kFwdRows - 1) / kFwdRows;
+    const dim3 grid((unsigned)nqt * p.H * p.batch);
+    const dim3 block(kFwdThreads);
+    switch (dpad) {
+    case 64:
+        hipLaunchKernelGGL(fa_fwd_kernel<64>, grid, block, 0, st, p);
+        break;
+    case 96:
+        hipLaunchKernelGGL(fa_fwd_kernel<96>, grid, block, 0, st, p);
+        break;
+    case 128:
+        hipLaunchKernelGGL(fa_fwd_kernel<128>, grid, block, 0, st, p);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fa

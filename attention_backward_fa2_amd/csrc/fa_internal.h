@@ -32,6 +32,8 @@ struct Params {
     float *lse2, *rowdot, *dq_acc;
     int *turns, *flags;
     const int *cu_q, *cu_k;
+    uint16_t *o_w;      // forward: O (output)
+    float *lse_w;       // forward: LSE (output, natural log)
 
     int64_t q_sb, q_ss, q_sh;
     int64_t k_sb, k_ss, k_sh;
@@ -107,5 +109,6 @@ hipError_t launch_preprocess(const Params &p, int dpad, hipStream_t st);
 hipError_t launch_main(const Params &p, int dpad, hipStream_t st);
 hipError_t launch_convert(const Params &p, int dpad, hipStream_t st);
 hipError_t launch_dq(const Params &p, int dpad, hipStream_t st);
+hipError_t launch_fwd(const Params &p, int dpad, hipStream_t st);
 
 }  // namespace fa

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define FA_BWD_ABI_VERSION 2
+#define FA_BWD_ABI_VERSION 3
 
 typedef enum {
     FA_OK = 0,
@@ -102,7 +102,9 @@ typedef enum {
  *          the sm90 backward page's __call__ requires of its strides).
  *          The row strides of q and dout must lie in [head_dim, 2^24):
  *          rows may not overlap (FA_ERR_INVALID_ARG) and a 64-row query
- *          tile must be addressable with 32-bit offsets (FA_ERR_UNSUPPORTED).
+ *          tile must be addressable with 32-bit offsets (FA_ERR_UNSUPPORTED);
+ *          the row strides of k and v must be below 2^24 for the same
+ *          reason (FA_ERR_UNSUPPORTED).
  *          lse_stride[0] = batch/sequence stride, lse_stride[1] = head stride,
  *          row stride 1.
  *

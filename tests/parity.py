@@ -127,3 +127,35 @@ def oracle_backward_unit(pr: Prepared, s: int, g: int):
                      pr.do64[qs:qe][:, heads], [0, qe - qs], [0, ke - ks], wl.scale,
                      wl.causal)
     return (slice(qs, qe), heads, slice(ks, ke), ref)
+
+
+def run_gpu_fwd(inp: W.Inputs):
+    """Forward on cuda:0 through the C ABI.  out and lse start as NaN so
+    unwritten elements show.  Returns (out [same layout as q], lse
+    (B|nseq, H, Sq|max_q) fp32), both on the CPU."""
+    wl = inp.wl
+    dev = torch.device("cuda")
+    q, k, v = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v))
+    out = torch.full_like(q, float("nan"))
+    nseq = len(inp.lens_q)
+    maxq = max(inp.lens_q) if inp.lens_q else 0
+    lse = torch.full((nseq, wl.heads, maxq), float("nan"), dtype=torch.float32, device=dev)
+    kw = {}
+    if wl.varlen:
+        kw = dict(cu_seqlens_q=torch.tensor(cu_np(inp.lens_q), dtype=torch.int32, device=dev),
+                  cu_seqlens_k=torch.tensor(cu_np(inp.lens_k), dtype=torch.int32, device=dev),
+                  max_seqlen_q=maxq, max_seqlen_k=max(inp.lens_k))
+    args = fa.make_fwd_args(q, k, v, out, lse, wl.scale, wl.causal, **kw)
+    fa.run_fwd(args)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+def lse_rows(inp: W.Inputs, lse: torch.Tensor) -> np.ndarray:
+    """(B|nseq, H, Sq|max_q) -> [total_q, H] fp64 (valid rows only)."""
+    cu = cu_np(inp.lens_q)
+    L = lse.numpy().astype(np.float64)
+    rows = np.empty((int(cu[-1]), inp.wl.heads), np.float64)
+    for s in range(len(inp.lens_q)):
+        rows[cu[s]:cu[s + 1]] = L[s, :, :inp.lens_q[s]].T
+    return rows

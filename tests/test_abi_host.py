@@ -1,8 +1,9 @@
 """Host-only checks of the C ABI: the built library loads, exports every
-function include/fa_bwd.h declares, and rejects bad arguments with the right
+function include/*.h declares, and rejects bad arguments with the right
 status before touching the GPU.  Fake (never dereferenced) aligned addresses
 stand in for device pointers."""
 import ctypes
+import glob
 import os
 import re
 
@@ -12,31 +13,38 @@ import attention_backward_fa2_amd as fa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa_bwd.h")
+FWD_HEADER = os.path.join(ROOT, "include", "fa_fwd.h")
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_bwd\w*)\s*\(", text)))
+    names = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(fa_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
     lib = fa.load_library()
     names = _declared_functions()
-    assert len(names) >= 9, names
+    assert len(names) >= 12, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(fa.EXPORTED)
-    assert lib.fa_bwd_abi_version() == 2
+    assert lib.fa_bwd_abi_version() == 3
 
 
-def test_struct_mirror_matches_header_field_order():
-    text = open(HEADER).read()
-    body = text[text.index("typedef struct fa_bwd_args"):text.index("} fa_bwd_args;")]
+@pytest.mark.parametrize("header,struct,mirror", [
+    (HEADER, "fa_bwd_args", fa.FaBwdArgs),
+    (FWD_HEADER, "fa_fwd_args", fa.FaFwdArgs),
+])
+def test_struct_mirror_matches_header_field_order(header, struct, mirror):
+    text = open(header).read()
+    body = text[text.index("typedef struct " + struct):text.index("} %s;" % struct)]
     body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
     decl = re.findall(r"(\*?\w+)(?:\[\d\])?\s*[,;]", body)
     names = [d.lstrip("*") for d in decl]
-    assert names == [f[0] for f in fa.FaBwdArgs._fields_]
+    assert names == [f[0] for f in mirror._fields_]
 
 
 BASE = 0x7f0000000000
@@ -135,6 +143,7 @@ def test_valid_args_pass_validation():
     ({"dk": BASE + 8}, fa.FA_ERR_INVALID_ARG),            # misaligned
     ({"q_stride": (256 * 8 * 128, 8 * 128 + 4, 128)}, fa.FA_ERR_INVALID_ARG),
     ({"do_stride": (256 * 64, 64, 128 * 256)}, fa.FA_ERR_INVALID_ARG),   # rows overlap
+    ({"k_stride": (1 << 30, 1 << 24, 128)}, fa.FA_ERR_UNSUPPORTED),      # 32-bit tile offsets
     ({"batch": -1}, fa.FA_ERR_INVALID_ARG),
     ({"head_dim": 0}, fa.FA_ERR_INVALID_ARG),
     ({"causal": 2}, fa.FA_ERR_INVALID_ARG),
@@ -179,3 +188,58 @@ def test_varlen_layout_uses_total_rows():
     lay = fa.workspace_layout(a)
     assert lay.rows == 1000
     assert lay.off_flags - lay.off_turns == ((5 * 8 * 5 * 4 + 255) // 256) * 256
+
+
+def _fwd_args(**over):
+    a = fa.FaFwdArgs()
+    a.dtype = fa.FA_DTYPE_BF16
+    a.batch, a.seqlen_q, a.seqlen_k = 2, 256, 384
+    a.num_heads, a.num_heads_k, a.head_dim = 8, 2, 128
+    H, Hk, D, Sq, Sk = 8, 2, 128, 256, 384
+    addr = BASE
+    for name in ("q", "k", "v", "out", "lse"):
+        setattr(a, name, addr)
+        addr += 1 << 30
+    for name in ("q_stride", "o_stride"):
+        getattr(a, name)[:] = (Sq * H * D, H * D, D)
+    for name in ("k_stride", "v_stride"):
+        getattr(a, name)[:] = (Sk * Hk * D, Hk * D, D)
+    a.lse_stride[:] = (H * Sq, Sq)
+    a.softmax_scale = D ** -0.5
+    a.causal = 1
+    for k, v in over.items():
+        if isinstance(getattr(a, k), ctypes.Array):
+            getattr(a, k)[:] = v
+        else:
+            setattr(a, k, v)
+    return a
+
+
+def test_forward_valid_args_pass_validation():
+    assert fa.validate_fwd(_fwd_args()) == fa.FA_OK
+    assert fa.validate_fwd(_fwd_args(cu_seqlens_q=BASE, cu_seqlens_k=BASE + 256, total_q=1000,
+                                     total_k=1200, batch=5, seqlen_q=300)) == fa.FA_OK
+
+
+@pytest.mark.parametrize("over,status", [
+    ({"num_heads_k": 3}, fa.FA_ERR_INVALID_ARG),
+    ({"out": 0}, fa.FA_ERR_INVALID_ARG),
+    ({"lse": 0}, fa.FA_ERR_INVALID_ARG),
+    ({"k": 0}, fa.FA_ERR_INVALID_ARG),
+    ({"v": BASE + 8}, fa.FA_ERR_INVALID_ARG),
+    ({"lse": BASE + 2}, fa.FA_ERR_INVALID_ARG),
+    ({"o_stride": (256 * 8 * 128, 8 * 128 + 4, 128)}, fa.FA_ERR_INVALID_ARG),
+    ({"causal": 2}, fa.FA_ERR_INVALID_ARG),
+    ({"softmax_scale": float("inf")}, fa.FA_ERR_INVALID_ARG),
+    ({"cu_seqlens_k": BASE}, fa.FA_ERR_INVALID_ARG),
+    ({"dtype": 1}, fa.FA_ERR_UNSUPPORTED),
+    ({"head_dim": 192}, fa.FA_ERR_UNSUPPORTED),
+    ({"v_stride": (1 << 30, 1 << 24, 128)}, fa.FA_ERR_UNSUPPORTED),
+])
+def test_forward_validation_errors(over, status):
+    lib = fa.load_library()
+    a = _fwd_args(**over)
+    assert fa.validate_fwd(a) == status
+    assert lib.fa_bwd_last_error().decode() != ""
+    assert lib.fa_fwd(ctypes.byref(a), None) == status     # rejected before any launch
+    assert lib.fa_fwd(None, None) == fa.FA_ERR_INVALID_ARG
