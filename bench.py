@@ -13,6 +13,10 @@ HIP events recorded on the stream it is launched on.
 Inputs: Q, K, V, dO from the seeded generator (workloads.py); O and LSE from a
 plain fp32 torch forward on the GPU (input preparation only, not timed).
 The CPU baseline leg times the fp64 oracle on a bounded sample.
+
+--forward measures the forward kernel (O and LSE) on the same workload
+instead and prints one JSON line of the same shape for it (not the headline
+metric).
 """
 import argparse
 import json
@@ -77,6 +81,8 @@ def _find(root, suffix):
 WORKLOAD_TAG = "gqa_b2_h32_hk8_s4096_d128_causal"
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof/trace -o c3 -- "
              "python bench.py")
+FWD_TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof/fwd_trace -o c3 -- "
+                 "python bench.py --forward")
 PMC_RUN = "python bench.py --no-cpu-baseline --steps 3 --warmup 1"
 SQ_PASSES = [
     "SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY "
@@ -193,6 +199,31 @@ def summarize_profile(prof_dir, out_dir):
                             d["SQ_VALU_MFMA_BUSY_CYCLES"] / d["SQ_INSTS_MFMA"]))
     with open(os.path.join(out_dir, "sq_counters_%s.md" % WORKLOAD_TAG), "w") as fh:
         fh.write("\n".join(lines) + "\n")
+
+    # -- forward kernel trace (if that run is present) --
+    if os.path.isdir(os.path.join(prof_dir, "fwd_trace")):
+        stats = _csv_rows(_find(os.path.join(prof_dir, "fwd_trace"), "kernel_stats.csv"))
+        fwd_line = None
+        with open(os.path.join(prof_dir, "fwd_trace.log")) as fh:
+            for line in fh:
+                if line.startswith("{") and '"metric"' in line:
+                    fwd_line = json.loads(line)
+        lines = ["# Kernel trace: forward, %s" % WORKLOAD_TAG, "",
+                 "B=2, H=32, Hk=8, Sq=Sk=4096, D=128, causal, bf16; O and LSE by `fa_fwd`.",
+                 "", "Command (repo root, MI355X):", "", "    " + FWD_TRACE_CMD, "",
+                 "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+        for r in stats:
+            if "fa::" in r["Name"]:
+                lines.append("| %s | %s | %.1f | %.1f | %.1f |" % (
+                    _kname(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
+                    float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+        lines += ["", "Calls = warm-up + timed steps of `bench.py --forward` (%d + %d)." % (
+            fwd_line["warmup"], fwd_line["steps"]), "",
+            "The same run's bench line: %.4f ms per launch (HIP events on the launch stream), "
+            "%.1f TFLOP/s on the forward's two products." % (fwd_line["ms_per_step"],
+                                                             fwd_line["value"])]
+        with open(os.path.join(out_dir, "kernel_trace_fwd_%s.md" % WORKLOAD_TAG), "w") as fh:
+            fh.write("\n".join(lines) + "\n")
     print("wrote profile summaries to", out_dir)
 
 
@@ -260,6 +291,92 @@ def cpu_baseline(wl, units):
                       % (len(units), wl.batch * wl.heads_k, t_total)}
 
 
+FWD_METRIC = "fwd TFLOP/s (O, LSE) bf16 and % of MFMA peak, S=4096 D=128 causal GQA"
+FWD_KERNEL = "fa_fwd_kernel<128>"
+
+
+def fwd_flops(B, H, Sq, Sk, D, causal):
+    """The forward's two products (S = Q K^T, O = P V): 4*B*H*Sq*Sk*D, halved
+    for causal."""
+    f = 4.0 * B * H * Sq * Sk * D
+    return f * 0.5 if causal else f
+
+
+def cpu_baseline_fwd(wl, units):
+    """fp64 oracle forward on a bounded sample of (batch, head) units."""
+    import numpy as np
+    import workloads as W
+    from oracle import oracle as O
+    inp = W.make_inputs(wl)
+    G = wl.heads // wl.heads_k
+    t_total, flops = 0.0, 0.0
+    for (b, h) in units:
+        def f64(t):
+            return t.float().numpy().astype(np.float64)
+        q = f64(inp.q[b][:, [h]])
+        k = f64(inp.k[b][:, [h // G]])
+        v = f64(inp.v[b][:, [h // G]])
+        t0 = time.perf_counter()
+        O.forward(q, k, v, [0, wl.seqlen_q], [0, wl.seqlen_k], wl.scale, wl.causal)
+        t_total += time.perf_counter() - t0
+        flops += fwd_flops(1, 1, wl.seqlen_q, wl.seqlen_k, wl.head_dim, wl.causal)
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(),
+            "kind": "oracle",
+            "sample": "%d of %d (batch, head) units of the workload, fp64 forward, %.1f s"
+                      % (len(units), wl.batch * wl.heads, t_total)}
+
+
+def bench_forward(args, wl, dev):
+    import torch
+    import workloads as W
+    import attention_backward_fa2_amd as fa
+    inp = W.make_inputs(wl)
+    q, k, v = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v))
+    out = torch.empty_like(q)
+    lse = torch.empty(wl.batch, wl.heads, wl.seqlen_q, dtype=torch.float32, device=dev)
+    a = fa.make_fwd_args(q, k, v, out, lse, wl.scale, wl.causal)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        fa.run_fwd(a, stream)
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for s in range(K):
+        fa.run_fwd(a, stream)
+        evs[s + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = evs[0].elapsed_time(evs[-1]) / K
+    B, H, Hk, Sq, Sk, D = wl.batch, wl.heads, wl.heads_k, wl.seqlen_q, wl.seqlen_k, wl.head_dim
+    flops = fwd_flops(B, H, Sq, Sk, D, wl.causal)
+    tf = flops / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": FWD_METRIC, "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "heads": H, "heads_k": Hk,
+                   "seqlen_q": Sq, "seqlen_k": Sk, "head_dim": D, "causal": wl.causal,
+                   "pass": "forward"},
+        "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
+        "flops_per_step": flops,
+        "kernel_ms": {"fwd": round(ms, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": FWD_KERNEL,
+                     "algorithmic_flops_per_launch": flops},
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        units = [(b, h) for b in range(B) for h in range(H)]
+        n = min(args.cpu_units, len(units))
+        rec["cpu_baseline"] = cpu_baseline_fwd(wl, [units[(i * len(units)) // n]
+                                                    for i in range(n)])
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -272,6 +389,8 @@ def main():
     ap.add_argument("--deterministic", action="store_true",
                     help="with --dq-accumulate: ordered (bit-reproducible) partial adds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--forward", action="store_true",
+                    help="time the forward kernel (O, LSE) instead of the backward")
     ap.add_argument("--cpu-units", type=int, default=16)
     ap.add_argument("--summarize-profile", metavar="PROF_DIR",
                     help="write the profiles/ summaries from rocprofv3 outputs in PROF_DIR "
@@ -312,6 +431,9 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.forward:
+        bench_forward(args, wl, dev)
+        return
     inp = W.make_inputs(wl)
     q, k, v, do = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v, inp.dout))
     o, lse = forward_inputs_torch(q, k, v, wl.scale, wl.causal)
