@@ -249,11 +249,13 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
                 else
                     return true;
             };
-            auto max_elem = [&](auto mbc, auto ec) {
+            // elements e, e+1 of block mb into its maximum (one three-input max)
+            auto max_pair = [&](auto mbc, auto ec) {
                 constexpr int mb = decltype(mbc)::value, e = decltype(ec)::value;
-                const float s = visible(mbc, ec) ? st[mb][e] : -INFINITY;
+                const float s0 = visible(mbc, ec) ? st[mb][e] : -INFINITY;
+                const float s1 = visible(mbc, IC<e + 1>{}) ? st[mb][e + 1] : -INFINITY;
                 float &m = mb == 0 ? mx0 : mx1;
-                m = fmaxf(m, s);
+                m = fmaxf(m, fmaxf(s0, s1));
                 keep_here(m);
             };
             auto p_elem = [&](auto mbc, auto ec) {
@@ -291,12 +293,12 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
                 // maximum of keys 0-31 over the S^T slots of keys 32-63
                 if constexpr (i >= NB && i < 2 * NB) {
                     constexpr int u = i - NB;
-                    static_for<16 * (u + 1) / NB - 16 * u / NB>(
-                        [&](auto ec) { max_elem(IC<0>{}, IC<16 * u / NB + decltype(ec)::value>{}); });
+                    static_for<8 * (u + 1) / NB - 8 * u / NB>(
+                        [&](auto ec) { max_pair(IC<0>{}, IC<2 * (8 * u / NB + decltype(ec)::value)>{}); });
                 }
                 if constexpr (i == 2 * NB - 1) {
                     // tile maximum of the row (both blocks, both lane halves)
-                    static_for<16>([&](auto ec) { max_elem(IC<1>{}, ec); });
+                    static_for<8>([&](auto ec) { max_pair(IC<1>{}, IC<2 * decltype(ec)::value>{}); });
                     float mt = fmaxf(mx0, mx1);
                     mt = fmaxf(mt, __shfl_xor(mt, 32));
                     const float mt2 = mt * c2;        // -inf if no key of the tile is visible
