@@ -37,6 +37,7 @@ class Prepared:
         self.do64 = to64(inp.packed(inp.dout))
         out, lse = O.forward(self.q64, self.k64, self.v64, self.cu_q, self.cu_k, wl.scale,
                              wl.causal)
+        self.o64_exact = out                      # [total_q, H, D] fp64
         self.lse_rows = lse                       # [total_q, H] fp64
         self.o = torch.from_numpy(out).to(torch.bfloat16).reshape(inp.q.shape)
         self.o64 = to64(inp.packed(self.o))
