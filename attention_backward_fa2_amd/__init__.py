@@ -17,7 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa_bwd.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
-FA_DTYPE_BF16 = 0
+FA_DTYPE_BF16, FA_DTYPE_F16 = 0, 1
+_DTYPES = {torch.bfloat16: FA_DTYPE_BF16, torch.float16: FA_DTYPE_F16}
 _STATUS = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED",
            3: "FA_ERR_WORKSPACE", 4: "FA_ERR_HIP"}
 
@@ -167,7 +168,7 @@ def make_args(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
     ordered when deterministic) and converted afterwards."""
     varlen = cu_seqlens_q is not None or cu_seqlens_k is not None
     a = FaBwdArgs()
-    a.dtype = FA_DTYPE_BF16 if q.dtype == torch.bfloat16 else 99
+    a.dtype = _DTYPES.get(q.dtype, 99)
     if varlen:
         if cu_seqlens_q is None or cu_seqlens_k is None:
             raise ValueError("cu_seqlens_q and cu_seqlens_k go together")
@@ -269,7 +270,7 @@ def make_fwd_args(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q=None,
     """Fill fa_fwd_args from tensors (layouts as in make_args)."""
     varlen = cu_seqlens_q is not None or cu_seqlens_k is not None
     a = FaFwdArgs()
-    a.dtype = FA_DTYPE_BF16 if q.dtype == torch.bfloat16 else 99
+    a.dtype = _DTYPES.get(q.dtype, 99)
     if varlen:
         if cu_seqlens_q is None or cu_seqlens_k is None:
             raise ValueError("cu_seqlens_q and cu_seqlens_k go together")

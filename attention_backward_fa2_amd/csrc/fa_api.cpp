@@ -70,8 +70,8 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
 {
     if (!a)
         return fail(FA_ERR_INVALID_ARG, "args is NULL");
-    if (a->dtype != FA_DTYPE_BF16)
-        return fail(FA_ERR_UNSUPPORTED, "dtype %d unsupported (only bf16)", a->dtype);
+    if (a->dtype != FA_DTYPE_BF16 && a->dtype != FA_DTYPE_F16)
+        return fail(FA_ERR_UNSUPPORTED, "dtype %d unsupported (bf16 or fp16)", a->dtype);
     if (a->batch < 0 || a->seqlen_q < 0 || a->seqlen_k < 0)
         return fail(FA_ERR_INVALID_ARG, "negative batch or sequence length");
     if (a->num_heads <= 0 || a->num_heads_k <= 0 || a->head_dim <= 0)
@@ -174,6 +174,7 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
     p.causal = a->causal;
     p.deterministic = a->deterministic;
     p.fused_dq = a->dq_accumulate;
+    p.f16 = a->dtype == FA_DTYPE_F16;
 
     // Workspace layout.
     fa_bwd_ws_layout &ws = pl->ws;
@@ -265,8 +266,8 @@ fa_status make_fwd_plan(const fa_fwd_args *a, fa::Params *pp, int *dpad_out)
 {
     if (!a)
         return fail(FA_ERR_INVALID_ARG, "args is NULL");
-    if (a->dtype != FA_DTYPE_BF16)
-        return fail(FA_ERR_UNSUPPORTED, "dtype %d unsupported (only bf16)", a->dtype);
+    if (a->dtype != FA_DTYPE_BF16 && a->dtype != FA_DTYPE_F16)
+        return fail(FA_ERR_UNSUPPORTED, "dtype %d unsupported (bf16 or fp16)", a->dtype);
     if (a->batch < 0 || a->seqlen_q < 0 || a->seqlen_k < 0)
         return fail(FA_ERR_INVALID_ARG, "negative batch or sequence length");
     if (a->num_heads <= 0 || a->num_heads_k <= 0 || a->head_dim <= 0)
@@ -343,6 +344,7 @@ fa_status make_fwd_plan(const fa_fwd_args *a, fa::Params *pp, int *dpad_out)
     p.scale = a->softmax_scale;
     p.scale_log2 = (float)((double)a->softmax_scale * 1.4426950408889634);
     p.causal = a->causal;
+    p.f16 = a->dtype == FA_DTYPE_F16;
     *dpad_out = dpad;
     g_last_error.clear();
     return FA_OK;

@@ -9,7 +9,7 @@
 
 namespace fa {
 
-template <int DP>
+template <int DP, bool F16>
 __global__ void __launch_bounds__(kThreads) fa_bwd_convert_kernel(Params p)
 {
     const int b = blockIdx.z, h = blockIdx.y;
@@ -24,10 +24,10 @@ __global__ void __launch_bounds__(kThreads) fa_bwd_convert_kernel(Params p)
     const float4 bq = *reinterpret_cast<const float4 *>(src + 4);
     const float s = p.scale;
     uint4 out;
-    out.x = (uint32_t)f2bf(a.x * s) | ((uint32_t)f2bf(a.y * s) << 16);
-    out.y = (uint32_t)f2bf(a.z * s) | ((uint32_t)f2bf(a.w * s) << 16);
-    out.z = (uint32_t)f2bf(bq.x * s) | ((uint32_t)f2bf(bq.y * s) << 16);
-    out.w = (uint32_t)f2bf(bq.z * s) | ((uint32_t)f2bf(bq.w * s) << 16);
+    out.x = (uint32_t)f2elem<F16>(a.x * s) | ((uint32_t)f2elem<F16>(a.y * s) << 16);
+    out.y = (uint32_t)f2elem<F16>(a.z * s) | ((uint32_t)f2elem<F16>(a.w * s) << 16);
+    out.z = (uint32_t)f2elem<F16>(bq.x * s) | ((uint32_t)f2elem<F16>(bq.y * s) << 16);
+    out.w = (uint32_t)f2elem<F16>(bq.z * s) | ((uint32_t)f2elem<F16>(bq.w * s) << 16);
     uint16_t *dst = p.dq + row_offset(p, b, si.tok_q, i, p.dq_sb, p.dq_ss) + h * p.dq_sh + c * 8;
     *reinterpret_cast<uint4 *>(dst) = out;
 }
@@ -38,13 +38,22 @@ hipError_t launch_convert(const Params &p, int dpad, hipStream_t st)
     const dim3 block(kThreads);
     switch (dpad) {
     case 64:
-        hipLaunchKernelGGL(fa_bwd_convert_kernel<64>, grid, block, 0, st, p);
+        if (p.f16)
+            hipLaunchKernelGGL((fa_bwd_convert_kernel<64, true>), grid, block, 0, st, p);
+        else
+            hipLaunchKernelGGL((fa_bwd_convert_kernel<64, false>), grid, block, 0, st, p);
         break;
     case 96:
-        hipLaunchKernelGGL(fa_bwd_convert_kernel<96>, grid, block, 0, st, p);
+        if (p.f16)
+            hipLaunchKernelGGL((fa_bwd_convert_kernel<96, true>), grid, block, 0, st, p);
+        else
+            hipLaunchKernelGGL((fa_bwd_convert_kernel<96, false>), grid, block, 0, st, p);
         break;
     case 128:
-        hipLaunchKernelGGL(fa_bwd_convert_kernel<128>, grid, block, 0, st, p);
+        if (p.f16)
+            hipLaunchKernelGGL((fa_bwd_convert_kernel<128, true>), grid, block, 0, st, p);
+        else
+            hipLaunchKernelGGL((fa_bwd_convert_kernel<128, false>), grid, block, 0, st, p);
         break;
     default:
         return hipErrorInvalidValue;

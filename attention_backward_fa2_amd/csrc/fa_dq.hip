@@ -54,7 +54,7 @@ struct __attribute__((aligned(16))) DqSmem {
     KVBuf<DP> buf[3];
 };
 
-template <int DP>
+template <int DP, bool F16>
 __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
 {
     constexpr int KS = DP / 16;                  // k-steps over the head dim
@@ -149,7 +149,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
     }
 
     // ---- Q and dO rows of the lane (B operands), lse2 / rowdot ----
-    bf16x8 qf[KS], of[KS];
+    e16x8 qf[KS], of[KS];
     {
         const int qr = qok ? qrow : Lq - 1;
         const uint16_t *qp = p.q + row_offset(p, b, si.tok_q, qr, p.q_sb, p.q_ss) + h * p.q_sh;
@@ -163,8 +163,8 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                 a = *reinterpret_cast<const u32x4 *>(qp + d0);
                 c = *reinterpret_cast<const u32x4 *>(dp_ + d0);
             }
-            qf[ks] = __builtin_bit_cast(bf16x8, a);
-            of[ks] = __builtin_bit_cast(bf16x8, c);
+            qf[ks] = __builtin_bit_cast(e16x8, a);
+            of[ks] = __builtin_bit_cast(e16x8, c);
         }
     }
     // ---- lse2 and rowdot of the lane's row, written for the key-tile kernel
@@ -193,8 +193,8 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                     float acc = 0.f;
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
-                        acc += bf2f((uint16_t)(ow[t] & 0xffff)) * bf2f((uint16_t)(dw[t] & 0xffff));
-                        acc += bf2f((uint16_t)(ow[t] >> 16)) * bf2f((uint16_t)(dw[t] >> 16));
+                        acc += elem2f<F16>((uint16_t)(ow[t] & 0xffff)) * elem2f<F16>((uint16_t)(dw[t] & 0xffff));
+                        acc += elem2f<F16>((uint16_t)(ow[t] >> 16)) * elem2f<F16>((uint16_t)(dw[t] >> 16));
                     }
                     cs[ks] = acc;
                 }
@@ -225,7 +225,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
     f32x16 rdt;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-        of[ks] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, of[ks]) ^ 0x80008000u);
+        of[ks] = __builtin_bit_cast(e16x8, __builtin_bit_cast(u32x4, of[ks]) ^ 0x80008000u);
 #pragma unroll
     for (int e = 0; e < 16; ++e)
         rdt[e] = rd;
@@ -277,7 +277,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
         static_assert(BAR >= 2 * NB - RA && BAR + RA < NSLOT, "barrier slot");
         constexpr int LPT = 2 * PERW;             // loads per wave per tile
 
-        auto op_read = [&](auto ic) -> bf16x8 {
+        auto op_read = [&](auto ic) -> e16x8 {
             constexpr int i = decltype(ic)::value;
             if constexpr (i < 2 * NB) {
                 constexpr int mb = i / NB, jj = i % NB, ks = jj >> 1;
@@ -288,7 +288,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
             }
         };
         __syncthreads();
-        bf16x8 ring[RA];
+        e16x8 ring[RA];
         static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
 
         // Smallest visible-key limit over the wave's rows (-1 if any row is
@@ -311,8 +311,8 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
 
             f32x16 st[2], dpt[2];
             const f32x16 z = {};
-            bf16x4 dh[4];
-            bf16x8 dsa[4];
+            e16x4 dh[4];
+            e16x8 dsa[4];
             f32x4 dv;
 
             auto pw_elem = [&](auto mbc, auto ec) {
@@ -325,7 +325,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                 keep_here(d);
                 dv[tt] = d;
                 if constexpr (tt == 3) {
-                    dh[r4] = to_bf16(dv);
+                    dh[r4] = to_elem<F16>(dv);
                     if constexpr ((r4 & 1) != 0)
                         dsa[2 * mb + (r4 >> 1)] = concat(dh[r4 - 1], dh[r4]);
                 }
@@ -333,7 +333,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
 
             static_for<NSLOT>([&](auto ic) {
                 constexpr int i = decltype(ic)::value;
-                const bf16x8 a = ring[i % RA];
+                const e16x8 a = ring[i % RA];
                 if constexpr (i + RA < NSLOT)
                     ring[i % RA] = op_read(IC<i + RA>{});
                 else
@@ -341,15 +341,15 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                 if constexpr (i < 2 * NB) {
                     constexpr int mb = i / NB, jj = i % NB, ks = jj >> 1;
                     if constexpr ((jj & 1) != 0) {
-                        dpt[mb] = mfma32(a, of[ks], ks == 0 ? rdt : dpt[mb]);
+                        dpt[mb] = mfma32<F16>(a, of[ks], ks == 0 ? rdt : dpt[mb]);
                         keep_here(dpt[mb]);
                     } else {
-                        st[mb] = mfma32(a, qf[ks], ks == 0 ? z : st[mb]);
+                        st[mb] = mfma32<F16>(a, qf[ks], ks == 0 ? z : st[mb]);
                         keep_here(st[mb]);
                     }
                 } else {
                     constexpr int jj = i - 2 * NB, kk = jj / DB, db = jj % DB;
-                    acc[db] = mfma32(dsa[kk], a, acc[db]);
+                    acc[db] = mfma32<F16>(dsa[kk], a, acc[db]);
                     keep_here(acc[db]);
                 }
                 // dS of keys 0-31 over slots NB .. 2NB-1, of keys 32-63 over
@@ -407,7 +407,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                 const int qr = q0 + 32 * w + 8 * (r >> 2) + 4 * g2 + (r & 3);
                 if (qr < Lq)
                     p.dq[row_offset(p, b, si.tok_q, qr, p.dq_sb, p.dq_ss) + h * p.dq_sh + d] =
-                        f2bf(acc[db][r] * p.scale);
+                        f2elem<F16>(acc[db][r] * p.scale);
             }
         }
     }
@@ -420,13 +420,22 @@ hipError_t launch_dq(const Params &p, int dpad, hipStream_t st)
     const dim3 block(kDqThreads);
     switch (dpad) {
     case 64:
-        hipLaunchKernelGGL(fa_bwd_dq_kernel<64>, grid, block, 0, st, p);
+        if (p.f16)
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<64, true>), grid, block, 0, st, p);
+        else
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<64, false>), grid, block, 0, st, p);
         break;
     case 96:
-        hipLaunchKernelGGL(fa_bwd_dq_kernel<96>, grid, block, 0, st, p);
+        if (p.f16)
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<96, true>), grid, block, 0, st, p);
+        else
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<96, false>), grid, block, 0, st, p);
         break;
     case 128:
-        hipLaunchKernelGGL(fa_bwd_dq_kernel<128>, grid, block, 0, st, p);
+        if (p.f16)
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<128, true>), grid, block, 0, st, p);
+        else
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<128, false>), grid, block, 0, st, p);
         break;
     default:
         return hipErrorInvalidValue;

@@ -54,7 +54,7 @@ struct __attribute__((aligned(16))) FwdSmem {
     FwdKV<DP> buf[3];
 };
 
-template <int DP>
+template <int DP, bool F16>
 __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
 {
     constexpr int KS = DP / 16;                  // k-steps over the head dim
@@ -141,7 +141,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
     }
 
     // ---- Q rows of the lane (B operand of S^T) ----
-    bf16x8 qf[KS];
+    e16x8 qf[KS];
     {
         const int qr = qok ? qrow : Lq - 1;
         const uint16_t *qp = p.q + row_offset(p, b, si.tok_q, qr, p.q_sb, p.q_ss) + h * p.q_sh;
@@ -151,7 +151,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
             u32x4 a = 0;
             if (qok && d0 < p.D)
                 a = *reinterpret_cast<const u32x4 *>(qp + d0);
-            qf[ks] = __builtin_bit_cast(bf16x8, a);
+            qf[ks] = __builtin_bit_cast(e16x8, a);
         }
     }
     wait_loads();   // land them and the first key tiles before the tile loop
@@ -204,7 +204,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
         static_assert(NSLOT % RA == 0, "ring length must divide the slot count");
         static_assert(BAR >= 2 * NB - RA && BAR + RA < NSLOT, "barrier slot");
 
-        auto op_read = [&](auto ic) -> bf16x8 {
+        auto op_read = [&](auto ic) -> e16x8 {
             constexpr int i = decltype(ic)::value;
             if constexpr (i < 2 * NB) {
                 constexpr int mb = i / NB, ks = i % NB;
@@ -215,7 +215,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
             }
         };
         __syncthreads();
-        bf16x8 ring[RA];
+        e16x8 ring[RA];
         static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
 
         // Smallest visible-key limit over the wave's rows (-1 if any row is
@@ -238,8 +238,8 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
             const f32x16 z = {};
             float mx0 = -INFINITY, mx1 = -INFINITY;   // raw-score maxima of the two blocks
             float mu = 0.f;                           // maximum used for P (base 2)
-            bf16x4 ph[4];
-            bf16x8 pb[4];
+            e16x4 ph[4];
+            e16x8 pb[4];
             f32x4 pv;
 
             auto visible = [&](auto mbc, auto ec) -> bool {
@@ -268,7 +268,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
                 lsum += x;
                 pv[tt] = x;
                 if constexpr (tt == 3) {
-                    ph[r4] = to_bf16(pv);
+                    ph[r4] = to_elem<F16>(pv);
                     if constexpr ((r4 & 1) != 0)
                         pb[2 * mb + (r4 >> 1)] = concat(ph[r4 - 1], ph[r4]);
                 }
@@ -276,18 +276,18 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
 
             static_for<NSLOT>([&](auto ic) {
                 constexpr int i = decltype(ic)::value;
-                const bf16x8 a = ring[i % RA];
+                const e16x8 a = ring[i % RA];
                 if constexpr (i + RA < NSLOT)
                     ring[i % RA] = op_read(IC<i + RA>{});
                 else
                     ring[i % RA] = op_read(IC<i + RA - NSLOT>{});   // next tile
                 if constexpr (i < 2 * NB) {
                     constexpr int mb = i / NB, ks = i % NB;
-                    st[mb] = mfma32(a, qf[ks], ks == 0 ? z : st[mb]);
+                    st[mb] = mfma32<F16>(a, qf[ks], ks == 0 ? z : st[mb]);
                     keep_here(st[mb]);
                 } else {
                     constexpr int jj = i - 2 * NB, kk = jj / DB, db = jj % DB;
-                    acc[db] = mfma32(a, pb[kk], acc[db]);
+                    acc[db] = mfma32<F16>(a, pb[kk], acc[db]);
                     keep_here(acc[db]);
                 }
                 // maximum of keys 0-31 over the S^T slots of keys 32-63
@@ -371,7 +371,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt)
                         o4[tt] = acc[db][4 * j + tt] * inv;
-                    *reinterpret_cast<bf16x4 *>(orow + d) = to_bf16(o4);
+                    *reinterpret_cast<e16x4 *>(orow + d) = to_elem<F16>(o4);
                 }
             }
         if (g2 == 0)
@@ -387,13 +387,22 @@ hipError_t launch_fwd(const Params &p, int dpad, hipStream_t st)
     const dim3 block(kFwdThreads);
     switch (dpad) {
     case 64:
-        hipLaunchKernelGGL(fa_fwd_kernel<64>, grid, block, 0, st, p);
+        if (p.f16)
+            hipLaunchKernelGGL((fa_fwd_kernel<64, true>), grid, block, 0, st, p);
+        else
+            hipLaunchKernelGGL((fa_fwd_kernel<64, false>), grid, block, 0, st, p);
         break;
     case 96:
-        hipLaunchKernelGGL(fa_fwd_kernel<96>, grid, block, 0, st, p);
+        if (p.f16)
+            hipLaunchKernelGGL((fa_fwd_kernel<96, true>), grid, block, 0, st, p);
+        else
+            hipLaunchKernelGGL((fa_fwd_kernel<96, false>), grid, block, 0, st, p);
         break;
     case 128:
-        hipLaunchKernelGGL(fa_fwd_kernel<128>, grid, block, 0, st, p);
+        if (p.f16)
+            hipLaunchKernelGGL((fa_fwd_kernel<128, true>), grid, block, 0, st, p);
+        else
+            hipLaunchKernelGGL((fa_fwd_kernel<128, false>), grid, block, 0, st, p);
         break;
     default:
         return hipErrorInvalidValue;

@@ -54,6 +54,7 @@ struct Params {
     float scale_log2;   // softmax scale * log2(e)
     int causal, deterministic, varlen;
     int fused_dq;       // 1: dQ partials added into dq_acc by the key-tile kernel
+    int f16;            // 1: fp16 elements, 0: bf16
 };
 
 // Lengths and first rows of sequence b.
@@ -92,16 +93,26 @@ __device__ inline int64_t row_offset(const Params &p, int b, int64_t tok0, int64
     return p.varlen ? (tok0 + i) * ss : (int64_t)b * sb + i * ss;
 }
 
-// fp32 -> bf16, round to nearest even (hardware convert on gfx950).
-__device__ inline uint16_t f2bf(float x)
+// Inputs and outputs hold 16-bit elements, bf16 or fp16 (F16: the template
+// flag every kernel carries); they travel as their bit patterns.
+// fp32 -> element, round to nearest even (hardware converts on gfx950).
+template <bool F16>
+__device__ inline uint16_t f2elem(float x)
 {
-    const __bf16 h = (__bf16)x;
-    return __builtin_bit_cast(uint16_t, h);
+    if constexpr (F16)
+        return __builtin_bit_cast(uint16_t, (_Float16)x);
+    else
+        return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
-__device__ inline float bf2f(uint16_t x)
+// element -> fp32 (exact)
+template <bool F16>
+__device__ inline float elem2f(uint16_t x)
 {
-    return __builtin_bit_cast(float, (uint32_t)x << 16);
+    if constexpr (F16)
+        return (float)__builtin_bit_cast(_Float16, x);
+    else
+        return __builtin_bit_cast(float, (uint32_t)x << 16);
 }
 
 // Host-side launchers (one translation unit each).

@@ -74,7 +74,7 @@ struct __attribute__((aligned(16))) FusedSmem : TileSmem<DP, 2> {
 // keys, added into the fp32 accumulator -- unordered hardware atomics, or
 // (ordered mode) in descending key-tile order behind a per-(batch, head,
 // query tile) turn counter.
-template <int DP>
+template <int DP, bool F16>
 __device__ inline void dq_partial(const Params &p, FusedSmem<DP> &sm, int buf, int w, int lane,
                                   int l32, int g2, int tid, int b, int h, int m, int j, int q0,
                                   int rows_valid, int Lq, int off, int nt_b, int64_t ws_row)
@@ -101,17 +101,17 @@ __device__ inline void dq_partial(const Params &p, FusedSmem<DP> &sm, int buf, i
     #pragma unroll
                     for (int ks = 0; ks < kKTile / 16; ++ks) {
                         const int r0 = 16 * ks + 8 * g2, r1 = r0 + 4;
-                        const bf16x8 bk = frag_tr(sm.k, RQ, r0, r1, 32 * w, lane);
+                        const e16x8 bk = frag_tr(sm.k, RQ, r0, r1, 32 * w, lane);
     #pragma unroll
                         for (int u = 0; u < 2; ++u)
-                            qacc[u] = mfma32(frag_tr(sm.dsT[buf], RD, r0, r1, 32 * u, lane), bk, qacc[u]);
+                            qacc[u] = mfma32<F16>(frag_tr(sm.dsT[buf], RD, r0, r1, 32 * u, lane), bk, qacc[u]);
                     }
                     pipeline_reads<16, 3, 12>();
                 } else if constexpr (DB == 2) {
     #pragma unroll
                     for (int ks = 0; ks < kKTile / 16; ++ks) {
                         const int r0 = 16 * ks + 8 * g2, r1 = r0 + 4;
-                        qacc[0] = mfma32(frag_tr(sm.dsT[buf], RD, r0, r1, 32 * qblk_mb(0), lane),
+                        qacc[0] = mfma32<F16>(frag_tr(sm.dsT[buf], RD, r0, r1, 32 * qblk_mb(0), lane),
                                          frag_tr(sm.k, RQ, r0, r1, 32 * qblk_db(0), lane), qacc[0]);
                     }
                     pipeline_reads<8, 4, 12>();
@@ -122,7 +122,7 @@ __device__ inline void dq_partial(const Params &p, FusedSmem<DP> &sm, int buf, i
     #pragma unroll
                             for (int ks = 0; ks < kKTile / 16; ++ks) {
                                 const int r0 = 16 * ks + 8 * g2, r1 = r0 + 4;
-                                qacc[u] = mfma32(frag_tr(sm.dsT[buf], RD, r0, r1, 32 * qblk_mb(u), lane),
+                                qacc[u] = mfma32<F16>(frag_tr(sm.dsT[buf], RD, r0, r1, 32 * qblk_mb(u), lane),
                                                  frag_tr(sm.k, RQ, r0, r1, 32 * qblk_db(u), lane),
                                                  qacc[u]);
                             }
@@ -185,7 +185,7 @@ __device__ inline void dq_partial(const Params &p, FusedSmem<DP> &sm, int buf, i
                 }
 }
 
-template <int DP, bool FUSED>
+template <int DP, bool FUSED, bool F16>
 __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
 {
     constexpr int KS = DP / 16;       // MFMA k-steps over the head dim
@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
 
     // ---- K, V rows of this wave's 32 keys: B operands of S and dP; in
     //      fused mode the K tile also goes to LDS for dQ = dS K. ----
-    bf16x8 kf[KS], vf[KS];
+    e16x8 kf[KS], vf[KS];
     {
         const uint16_t *krow = p.k + row_offset(p, b, si.tok_k, key, p.k_sb, p.k_ss) + hk * p.k_sh;
         const uint16_t *vrow = p.v + row_offset(p, b, si.tok_k, key, p.v_sb, p.v_ss) + hk * p.v_sh;
@@ -248,10 +248,10 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 kv = *reinterpret_cast<const u32x4 *>(krow + d0);
                 vv = *reinterpret_cast<const u32x4 *>(vrow + d0);
             }
-            kf[ks] = __builtin_bit_cast(bf16x8, kv);
+            kf[ks] = __builtin_bit_cast(e16x8, kv);
             // -V: the dP product then starts from rowdot and yields
             // rowdot - dP (sign flips are exact in bf16)
-            vf[ks] = __builtin_bit_cast(bf16x8, vv ^ 0x80008000u);
+            vf[ks] = __builtin_bit_cast(e16x8, vv ^ 0x80008000u);
             if constexpr (FUSED)
                 *reinterpret_cast<u32x4 *>(&sm.k[key_local * FusedSmem<DP>::RQ + d0]) = kv;
         }
@@ -468,7 +468,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         static_assert(BAR + (LPT + 1) / 2 + 6 <= NSLOT, "tile loads after the barrier");
 
         // A operand of slot i of a tile (offsets of the tile's buffer).
-        auto op_read = [&](auto ic) -> bf16x8 {
+        auto op_read = [&](auto ic) -> e16x8 {
             constexpr int i = decltype(ic)::value;
             if constexpr (i < 2 * NB) {
                 constexpr int mb = i / NB, jj = i % NB, ks = jj >> 1;
@@ -494,7 +494,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 asm volatile("" : "+a"(kf[ks]), "+a"(vf[ks]));
         };
 
-        bf16x8 ring[RA];
+        e16x8 ring[RA];
         static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
         // rowdot of the rows of query block mb (accumulator layout: element
         // 4*r4 + t is row 32*mb + 8*r4 + 4*g2 + t): the initial value of the
@@ -530,8 +530,8 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             const int delta = cur == NBUF - 1 ? -(NBUF - 1) * BUFB : BUFB;
 
             f32x16 s[2], dp[2];
-            bf16x8 pb[4], dsb[4];
-            bf16x4 ph[4], dh[4];
+            e16x8 pb[4], dsb[4];
+            e16x4 ph[4], dh[4];
             f32x4 l2v[4];
             f32x4 pv, dv;
 
@@ -550,10 +550,10 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 pv[t] = x;
                 dv[t] = d;
                 if constexpr (t == 3) {
-                    ph[r4] = to_bf16(pv);
-                    dh[r4] = to_bf16(dv);
+                    ph[r4] = to_elem<F16>(pv);
+                    dh[r4] = to_elem<F16>(dv);
                     if constexpr (FUSED)
-                        *reinterpret_cast<bf16x4 *>(dsrow + qc) = dh[r4];
+                        *reinterpret_cast<e16x4 *>(dsrow + qc) = dh[r4];
                     if constexpr ((r4 & 1) != 0) {
                         pb[2 * mb + (r4 >> 1)] = concat(ph[r4 - 1], ph[r4]);
                         dsb[2 * mb + (r4 >> 1)] = concat(dh[r4 - 1], dh[r4]);
@@ -564,7 +564,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             pin_acc();
             static_for<NSLOT>([&](auto ic) {
                 constexpr int i = decltype(ic)::value;
-                const bf16x8 a = ring[i % RA];
+                const e16x8 a = ring[i % RA];
                 if constexpr (i + RA < NSLOT)
                     ring[i % RA] = op_read(IC<i + RA>{});
                 else if constexpr (!FUSED)
@@ -584,21 +584,21 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                         // dp = rowdot - dO V^T (vf holds -V)
                         if constexpr (ks == 0)
                             dp[mb] = rdc[mb];
-                        mfma32_vacc(dp[mb], a, vf[ks]);
+                        mfma32_vacc<F16>(dp[mb], a, vf[ks]);
                     } else if constexpr (ks == 0) {
-                        mfma32_vz(s[mb], a, kf[ks]);
+                        mfma32_vz<F16>(s[mb], a, kf[ks]);
                     } else {
-                        mfma32_vacc(s[mb], a, kf[ks]);
+                        mfma32_vacc<F16>(s[mb], a, kf[ks]);
                     }
                 } else {
                     constexpr int jj = (i - 2 * NB) % NG;
                     constexpr int kk = 2 * ((i - 2 * NB) / NG) + jj / (2 * DB);
                     constexpr int db = (jj % (2 * DB)) >> 1;
                     if constexpr ((jj & 1) != 0) {
-                        dk_acc[db] = mfma32(a, dsb[kk], dk_acc[db]);
+                        dk_acc[db] = mfma32<F16>(a, dsb[kk], dk_acc[db]);
                         keep_here_acc(dk_acc[db]);
                     } else {
-                        dv_acc[db] = mfma32(a, pb[kk], dv_acc[db]);
+                        dv_acc[db] = mfma32<F16>(a, pb[kk], dv_acc[db]);
                         keep_here_acc(dv_acc[db]);
                     }
                 }
@@ -683,7 +683,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 __syncthreads();   // next tile in LDS; dS^T[cur] complete
                 const int h = hk * p.G + it / nm;
                 const int rows_valid = min(kQTile, Lq - q0);
-                dq_partial<DP>(p, sm, cur, w, lane, l32, g2, tid, b, h, m, j, q0, rows_valid, Lq,
+                dq_partial<DP, F16>(p, sm, cur, w, lane, l32, g2, tid, b, h, m, j, q0, rows_valid, Lq,
                                off, nt_b, si.ws_row);
                 static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
 #pragma unroll
@@ -735,8 +735,8 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     u16x4 kq, vq;
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
-                        kq[t] = f2bf(dk_acc[db][4 * r4 + t] * p.scale);
-                        vq[t] = f2bf(dv_acc[db][4 * r4 + t]);
+                        kq[t] = f2elem<F16>(dk_acc[db][4 * r4 + t] * p.scale);
+                        vq[t] = f2elem<F16>(dv_acc[db][4 * r4 + t]);
                     }
                     *reinterpret_cast<u16x4 *>(dkrow + d) = kq;
                     *reinterpret_cast<u16x4 *>(dvrow + d) = vq;
@@ -750,11 +750,15 @@ hipError_t launch_main(const Params &p, int dpad, hipStream_t st)
 {
     const dim3 grid((unsigned)p.ntiles * p.Hk * p.batch);
     const dim3 block(kThreads);
-#define FA_LAUNCH_MAIN(D)                                                              \
-    if (p.fused_dq)                                                                    \
-        hipLaunchKernelGGL((fa_bwd_main_kernel<D, true>), grid, block, 0, st, p);      \
-    else                                                                               \
-        hipLaunchKernelGGL((fa_bwd_main_kernel<D, false>), grid, block, 0, st, p);
+#define FA_LAUNCH_MAIN(D)                                                                  \
+    if (p.fused_dq && p.f16)                                                               \
+        hipLaunchKernelGGL((fa_bwd_main_kernel<D, true, true>), grid, block, 0, st, p);    \
+    else if (p.fused_dq)                                                                   \
+        hipLaunchKernelGGL((fa_bwd_main_kernel<D, true, false>), grid, block, 0, st, p);   \
+    else if (p.f16)                                                                        \
+        hipLaunchKernelGGL((fa_bwd_main_kernel<D, false, true>), grid, block, 0, st, p);   \
+    else                                                                                   \
+        hipLaunchKernelGGL((fa_bwd_main_kernel<D, false, false>), grid, block, 0, st, p);
     switch (dpad) {
     case 64:
         FA_LAUNCH_MAIN(64);

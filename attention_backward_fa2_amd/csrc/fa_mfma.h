@@ -1,7 +1,8 @@
 // fa_mfma.h -- gfx950 MFMA and LDS operand helpers shared by the two
 // tile kernels of the attention backward.
 //
-// MFMA: v_mfma_f32_32x32x16_bf16.  Per lane l (l32 = l % 32, g2 = l / 32):
+// MFMA: v_mfma_f32_32x32x16_bf16 / _f16 (same lane layouts).  Per lane l
+// (l32 = l % 32, g2 = l / 32):
 //   A (32 x 16, M x K): row l32, k = 8*g2 + t (t = 0..7, one 16-byte vector)
 //   B (16 x 32, K x N): col l32, k = 8*g2 + t
 //   C (32 x 32):        col l32, row 8*(r/4) + 4*g2 + r%4 for r = 0..15
@@ -28,19 +29,29 @@
 
 namespace fa {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+// Operand containers: eight / four 16-bit elements, bf16 or fp16 bit
+// patterns (the MFMA wrappers and converts below take the element type as a
+// template flag).
+typedef __bf16 e16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 e16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
-__device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
+template <bool F16>
+__device__ inline f32x16 mfma32(e16x8 a, e16x8 b, f32x16 c)
 {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // The same product as inline assembly: accumulator in ordinary registers,
@@ -54,14 +65,22 @@ __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
 // product -- mfma_settle(); an accumulation chain needs none; operand A must
 // not come from a vector instruction of the two preceding wait states -- the
 // callers feed it straight from LDS reads).
-__device__ inline void mfma32_vz(f32x16 &d, bf16x8 a, bf16x8 b)   // d = A B
+template <bool F16>
+__device__ inline void mfma32_vz(f32x16 &d, e16x8 a, e16x8 b)   // d = A B
 {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+    if constexpr (F16)
+        asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+    else
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
 }
 
-__device__ inline void mfma32_vacc(f32x16 &d, bf16x8 a, bf16x8 b)   // d += A B
+template <bool F16>
+__device__ inline void mfma32_vacc(f32x16 &d, e16x8 a, e16x8 b)   // d += A B
 {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+    if constexpr (F16)
+        asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+    else
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
 
 // 12 wait states, ordered after the last product into s and t and before
@@ -107,14 +126,18 @@ __device__ inline void keep_scalar_here(T &...x)
     (keep_scalar_one(x), ...);
 }
 
-// fp32 -> bf16 (round to nearest even) of four values: two packed
+// fp32 -> element (round to nearest even) of four values: two packed
 // hardware converts.
-__device__ inline bf16x4 to_bf16(f32x4 x)
+template <bool F16>
+__device__ inline e16x4 to_elem(f32x4 x)
 {
-    return __builtin_convertvector(x, bf16x4);
+    if constexpr (F16)
+        return __builtin_bit_cast(e16x4, __builtin_convertvector(x, f16x4));
+    else
+        return __builtin_convertvector(x, e16x4);
 }
 
-__device__ inline bf16x8 concat(bf16x4 lo, bf16x4 hi)
+__device__ inline e16x8 concat(e16x4 lo, e16x4 hi)
 {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
@@ -126,9 +149,9 @@ __device__ inline void zero(f32x16 &c)
         c[r] = 0.f;
 }
 
-__device__ inline bf16x8 lds16(const uint16_t *p)
+__device__ inline e16x8 lds16(const uint16_t *p)
 {
-    return *reinterpret_cast<const bf16x8 *>(p);
+    return *reinterpret_cast<const e16x8 *>(p);
 }
 
 __device__ inline i16x4 lds_tr(const uint16_t *p)
@@ -140,7 +163,7 @@ __device__ inline i16x4 lds_tr(const uint16_t *p)
 // contraction index: the lane receives column c0 + l32 at rows r0 .. r0+3
 // (elements 0..3) and r1 .. r1+3 (elements 4..7).  r0 and r1 may depend on
 // g2 only.
-__device__ inline bf16x8 frag_tr(const uint16_t *base, int pitch, int r0, int r1, int c0,
+__device__ inline e16x8 frag_tr(const uint16_t *base, int pitch, int r0, int r1, int c0,
                                  int lane)
 {
     const int c16 = lane & 15;
@@ -149,7 +172,7 @@ __device__ inline bf16x8 frag_tr(const uint16_t *base, int pitch, int r0, int r1
     const i16x4 lo = lds_tr(base + (r0 + rr) * pitch + col);
     const i16x4 hi = lds_tr(base + (r1 + rr) * pitch + col);
     const i16x4 v8[2] = {lo, hi};
-    return __builtin_bit_cast(bf16x8, v8);
+    return __builtin_bit_cast(e16x8, v8);
 }
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
@@ -234,17 +257,17 @@ __device__ __host__ constexpr int swz(int r)
     return PCH == 16 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
-__device__ inline bf16x8 lds16b(const uint8_t *p)
+__device__ inline e16x8 lds16b(const uint8_t *p)
 {
-    return *reinterpret_cast<const bf16x8 *>(p);
+    return *reinterpret_cast<const e16x8 *>(p);
 }
 
 // Transposing operand read from two byte addresses (see frag_tr).
-__device__ inline bf16x8 tr_pair(const uint8_t *p0, const uint8_t *p1)
+__device__ inline e16x8 tr_pair(const uint8_t *p0, const uint8_t *p1)
 {
     const i16x4 v8[2] = {lds_tr(reinterpret_cast<const uint16_t *>(p0)),
                          lds_tr(reinterpret_cast<const uint16_t *>(p1))};
-    return __builtin_bit_cast(bf16x8, v8);
+    return __builtin_bit_cast(e16x8, v8);
 }
 
 template <int MASK, int N>

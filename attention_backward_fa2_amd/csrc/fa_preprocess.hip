@@ -22,7 +22,7 @@
 
 namespace fa {
 
-template <int DP>
+template <int DP, bool F16>
 __global__ void __launch_bounds__(kThreads) fa_bwd_preprocess_kernel(Params p)
 {
     const int b = blockIdx.z, h = blockIdx.y;
@@ -47,8 +47,8 @@ __global__ void __launch_bounds__(kThreads) fa_bwd_preprocess_kernel(Params p)
             const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                acc += bf2f((uint16_t)(ow[t] & 0xffff)) * bf2f((uint16_t)(dw[t] & 0xffff));
-                acc += bf2f((uint16_t)(ow[t] >> 16)) * bf2f((uint16_t)(dw[t] >> 16));
+                acc += elem2f<F16>((uint16_t)(ow[t] & 0xffff)) * elem2f<F16>((uint16_t)(dw[t] & 0xffff));
+                acc += elem2f<F16>((uint16_t)(ow[t] >> 16)) * elem2f<F16>((uint16_t)(dw[t] >> 16));
             }
         }
     }
@@ -89,13 +89,22 @@ hipError_t launch_preprocess(const Params &p, int dpad, hipStream_t st)
     const dim3 block(kThreads);
     switch (dpad) {
     case 64:
-        hipLaunchKernelGGL(fa_bwd_preprocess_kernel<64>, grid, block, 0, st, p);
+        if (p.f16)
+            hipLaunchKernelGGL((fa_bwd_preprocess_kernel<64, true>), grid, block, 0, st, p);
+        else
+            hipLaunchKernelGGL((fa_bwd_preprocess_kernel<64, false>), grid, block, 0, st, p);
         break;
     case 96:
-        hipLaunchKernelGGL(fa_bwd_preprocess_kernel<96>, grid, block, 0, st, p);
+        if (p.f16)
+            hipLaunchKernelGGL((fa_bwd_preprocess_kernel<96, true>), grid, block, 0, st, p);
+        else
+            hipLaunchKernelGGL((fa_bwd_preprocess_kernel<96, false>), grid, block, 0, st, p);
         break;
     case 128:
-        hipLaunchKernelGGL(fa_bwd_preprocess_kernel<128>, grid, block, 0, st, p);
+        if (p.f16)
+            hipLaunchKernelGGL((fa_bwd_preprocess_kernel<128, true>), grid, block, 0, st, p);
+        else
+            hipLaunchKernelGGL((fa_bwd_preprocess_kernel<128, false>), grid, block, 0, st, p);
         break;
     default:
         return hipErrorInvalidValue;

@@ -28,7 +28,8 @@
  *      1 accumulate    : the main kernel adds each tile's dQ partial into an
  *                        fp32 accumulator (hardware atomics, or a fixed
  *                        order when deterministic = 1), which the preprocess
- *                        clears, and dq_convert forms dQ = bf16(scale * acc)
+ *                        clears, and dq_convert forms dQ = scale * acc
+ *                        rounded to the element type
  *                        (the dq_accum buffer and its reduction step on the
  *                        backward call-trace page); the sequence is
  *                        preprocess, main, dq_convert.
@@ -64,13 +65,14 @@ extern "C" {
 typedef enum {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1, /* null pointer, bad size, H % Hk != 0, bad stride */
-    FA_ERR_UNSUPPORTED = 2, /* dtype other than bf16, head_dim > 128 or not a multiple of 8 */
+    FA_ERR_UNSUPPORTED = 2, /* dtype other than bf16 / fp16, head_dim > 128 or not a multiple of 8 */
     FA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than fa_bwd_workspace_size() */
     FA_ERR_HIP = 4          /* a HIP launch or attribute call failed */
 } fa_status;
 
 typedef enum {
-    FA_DTYPE_BF16 = 0
+    FA_DTYPE_BF16 = 0,
+    FA_DTYPE_F16 = 1
 } fa_dtype;
 
 /*
@@ -134,7 +136,7 @@ typedef enum {
  *     Pointers of tensors with no elements may be NULL.
  */
 typedef struct fa_bwd_args {
-    int32_t dtype;                 /* fa_dtype; only FA_DTYPE_BF16 */
+    int32_t dtype;                 /* fa_dtype: FA_DTYPE_BF16 or FA_DTYPE_F16 */
     int32_t batch;                 /* dense: B; packed: number of sequences */
     int32_t seqlen_q, seqlen_k;    /* dense: Sq, Sk; packed: maximum lengths */
     int32_t num_heads, num_heads_k, head_dim;
@@ -142,9 +144,9 @@ typedef struct fa_bwd_args {
     const int32_t *cu_seqlens_k;   /* device; NULL for dense */
     int64_t total_q, total_k;      /* packed: cu_seqlens_q/k[batch] (host copies) */
 
-    const void *dout, *q, *k, *v, *out;  /* bf16 */
+    const void *dout, *q, *k, *v, *out;  /* 16-bit elements of `dtype` */
     const float *lse;                    /* fp32, natural log */
-    void *dq, *dk, *dv;                  /* bf16 outputs */
+    void *dq, *dk, *dv;                  /* outputs, elements of `dtype` */
 
     int64_t do_stride[3], q_stride[3], k_stride[3], v_stride[3], o_stride[3];
     int64_t dq_stride[3], dk_stride[3], dv_stride[3];

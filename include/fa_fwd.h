@@ -38,10 +38,10 @@ extern "C" {
  * pointer 16-byte aligned (lse 4-byte aligned), head_dim a multiple of 8 and
  * <= 128 and the row strides of k and v below 2^24 elements (a 64-key tile
  * is addressed with 32-bit offsets) -- FA_ERR_UNSUPPORTED otherwise -- and
- * dtype bf16 only.
+ * dtype bf16 or fp16 (inputs and out share it).
  *
  * Results:
- *   - out = softmax(softmax_scale * Q K^T + mask) V in bf16 over the valid
+ *   - out = softmax(softmax_scale * Q K^T + mask) V in `dtype` over the valid
  *     rows and the first head_dim columns (other memory is not written);
  *   - lse = the natural-log log-sum-exp of the scaled scores of each row;
  *   - a row with no visible key (causal with len_q > len_k, or len_k = 0)
@@ -50,7 +50,7 @@ extern "C" {
  * bit-identical results (fixed-order sums).
  */
 typedef struct fa_fwd_args {
-    int32_t dtype;                 /* fa_dtype; only FA_DTYPE_BF16 */
+    int32_t dtype;                 /* fa_dtype: FA_DTYPE_BF16 or FA_DTYPE_F16 */
     int32_t batch;                 /* dense: B; packed: number of sequences */
     int32_t seqlen_q, seqlen_k;    /* dense: Sq, Sk; packed: maximum lengths */
     int32_t num_heads, num_heads_k, head_dim;
@@ -58,8 +58,8 @@ typedef struct fa_fwd_args {
     const int32_t *cu_seqlens_k;   /* device; NULL for dense */
     int64_t total_q, total_k;      /* packed: cu_seqlens_q/k[batch] (host copies) */
 
-    const void *q, *k, *v;         /* bf16 inputs */
-    void *out;                     /* bf16 output */
+    const void *q, *k, *v;         /* inputs, 16-bit elements of `dtype` */
+    void *out;                     /* output, elements of `dtype` */
     float *lse;                    /* fp32 output, natural log */
 
     int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];

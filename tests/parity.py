@@ -16,7 +16,7 @@ TOL = 1e-2
 
 
 def to64(t: torch.Tensor) -> np.ndarray:
-    """bf16 -> fp64, exact."""
+    """bf16 / fp16 -> fp64, exact."""
     return t.float().numpy().astype(np.float64)
 
 
@@ -39,7 +39,7 @@ class Prepared:
                              wl.causal)
         self.o64_exact = out                      # [total_q, H, D] fp64
         self.lse_rows = lse                       # [total_q, H] fp64
-        self.o = torch.from_numpy(out).to(torch.bfloat16).reshape(inp.q.shape)
+        self.o = torch.from_numpy(out).to(inp.q.dtype).reshape(inp.q.shape)
         self.o64 = to64(inp.packed(self.o))
         nseq, H = len(inp.lens_q), wl.heads
         maxq = max(inp.lens_q) if inp.lens_q else 0
@@ -67,7 +67,7 @@ def run_gpu(pr: Prepared, deterministic=False, out_pad=0, step_split=False, dq_a
     def out_like(t):
         shp = list(t.shape)
         shp[-1] += out_pad
-        buf = torch.full(shp, float("nan"), dtype=torch.bfloat16, device=dev)
+        buf = torch.full(shp, float("nan"), dtype=t.dtype, device=dev)
         return buf[..., :t.shape[-1]], buf
 
     (dq, dq_buf), (dk, dk_buf), (dv, dv_buf) = out_like(q), out_like(k), out_like(v)

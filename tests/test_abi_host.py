@@ -134,6 +134,7 @@ def test_step_entry_points_check_the_dq_mode_before_launching():
 
 def test_valid_args_pass_validation():
     assert fa.validate(_with_ws(_args())) == fa.FA_OK
+    assert fa.validate(_with_ws(_args(dtype=fa.FA_DTYPE_F16))) == fa.FA_OK
 
 
 @pytest.mark.parametrize("over,status", [
@@ -149,7 +150,7 @@ def test_valid_args_pass_validation():
     ({"causal": 2}, fa.FA_ERR_INVALID_ARG),
     ({"softmax_scale": float("nan")}, fa.FA_ERR_INVALID_ARG),
     ({"cu_seqlens_q": BASE}, fa.FA_ERR_INVALID_ARG),      # only one cu_seqlens
-    ({"dtype": 1}, fa.FA_ERR_UNSUPPORTED),
+    ({"dtype": 2}, fa.FA_ERR_UNSUPPORTED),
     ({"head_dim": 300}, fa.FA_ERR_UNSUPPORTED),
     ({"head_dim": 100}, fa.FA_ERR_UNSUPPORTED),           # not a multiple of 8
     ({"head_dim": 192}, fa.FA_ERR_UNSUPPORTED),           # > 128 not built
@@ -217,6 +218,7 @@ def _fwd_args(**over):
 
 def test_forward_valid_args_pass_validation():
     assert fa.validate_fwd(_fwd_args()) == fa.FA_OK
+    assert fa.validate_fwd(_fwd_args(dtype=fa.FA_DTYPE_F16)) == fa.FA_OK
     assert fa.validate_fwd(_fwd_args(cu_seqlens_q=BASE, cu_seqlens_k=BASE + 256, total_q=1000,
                                      total_k=1200, batch=5, seqlen_q=300)) == fa.FA_OK
 
@@ -232,7 +234,7 @@ def test_forward_valid_args_pass_validation():
     ({"causal": 2}, fa.FA_ERR_INVALID_ARG),
     ({"softmax_scale": float("inf")}, fa.FA_ERR_INVALID_ARG),
     ({"cu_seqlens_k": BASE}, fa.FA_ERR_INVALID_ARG),
-    ({"dtype": 1}, fa.FA_ERR_UNSUPPORTED),
+    ({"dtype": 2}, fa.FA_ERR_UNSUPPORTED),
     ({"head_dim": 192}, fa.FA_ERR_UNSUPPORTED),
     ({"v_stride": (1 << 30, 1 << 24, 128)}, fa.FA_ERR_UNSUPPORTED),
 ])

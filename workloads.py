@@ -6,7 +6,8 @@ that both the GPU path and the CPU oracle consume.
 
 Recipe (same for every workload): one CPU ``torch.Generator`` seeded with
 ``seed``; draw order is [sequence lengths], then Q, K, V, dO, each
-``torch.randn`` in fp32 and rounded to bf16 (round-to-nearest-even).
+``torch.randn`` in fp32 and rounded to bf16 (round-to-nearest-even; fp16 for
+the fp16 cases, ``dtype=torch.float16``).
 Dense workloads are laid out (batch, seq, heads, dim); packed variable-length
 workloads are (total_tokens, heads, dim) with int32 ``cu_seqlens`` prefix sums
 and equal query/key lengths per sequence.
@@ -58,7 +59,7 @@ WORKLOADS = {
 @dataclass
 class Inputs:
     wl: Workload
-    q: torch.Tensor            # bf16, (B,Sq,H,D) dense or (Tq,H,D) packed
+    q: torch.Tensor            # bf16 / fp16, (B,Sq,H,D) dense or (Tq,H,D) packed
     k: torch.Tensor
     v: torch.Tensor
     dout: torch.Tensor
@@ -85,15 +86,16 @@ def _prefix(lens: List[int]) -> torch.Tensor:
     return torch.tensor(cu, dtype=torch.int32)
 
 
-def _randn_bf16(gen: torch.Generator, shape) -> torch.Tensor:
-    return torch.randn(shape, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+def _randn(gen: torch.Generator, shape, dtype=torch.bfloat16) -> torch.Tensor:
+    return torch.randn(shape, generator=gen, dtype=torch.float32).to(dtype)
 
 
 def draw_lengths(gen: torch.Generator, n: int, lo: int, hi: int) -> List[int]:
     return [int(x) for x in torch.randint(lo, hi + 1, (n,), generator=gen)]
 
 
-def make_inputs(wl: Workload, lengths: Optional[List[int]] = None) -> Inputs:
+def make_inputs(wl: Workload, lengths: Optional[List[int]] = None,
+                dtype=torch.bfloat16) -> Inputs:
     """Draw Q, K, V, dO for a workload.  ``lengths`` overrides the drawn
     packed-sequence lengths (it still consumes no random numbers)."""
     gen = torch.Generator(device="cpu")
@@ -103,16 +105,16 @@ def make_inputs(wl: Workload, lengths: Optional[List[int]] = None) -> Inputs:
         lens = list(lengths) if lengths is not None else draw_lengths(
             gen, wl.batch, wl.len_lo, wl.len_hi)
         T = sum(lens)
-        q = _randn_bf16(gen, (T, H, D))
-        k = _randn_bf16(gen, (T, Hk, D))
-        v = _randn_bf16(gen, (T, Hk, D))
-        do = _randn_bf16(gen, (T, H, D))
+        q = _randn(gen, (T, H, D), dtype)
+        k = _randn(gen, (T, Hk, D), dtype)
+        v = _randn(gen, (T, Hk, D), dtype)
+        do = _randn(gen, (T, H, D), dtype)
         return Inputs(wl, q, k, v, do, list(lens), list(lens))
     B, Sq, Sk = wl.batch, wl.seqlen_q, wl.seqlen_k
-    q = _randn_bf16(gen, (B, Sq, H, D))
-    k = _randn_bf16(gen, (B, Sk, Hk, D))
-    v = _randn_bf16(gen, (B, Sk, Hk, D))
-    do = _randn_bf16(gen, (B, Sq, H, D))
+    q = _randn(gen, (B, Sq, H, D), dtype)
+    k = _randn(gen, (B, Sk, Hk, D), dtype)
+    v = _randn(gen, (B, Sk, Hk, D), dtype)
+    do = _randn(gen, (B, Sq, H, D), dtype)
     return Inputs(wl, q, k, v, do, [Sq] * B, [Sk] * B)
 
 
@@ -124,15 +126,16 @@ def custom(name: str, batch: int, heads: int, heads_k: int, seqlen_q: int,
 
 
 def custom_varlen(name: str, lens_q: List[int], lens_k: List[int], heads: int,
-                  heads_k: int, head_dim: int, causal: bool, seed: int) -> Inputs:
+                  heads_k: int, head_dim: int, causal: bool, seed: int,
+                  dtype=torch.bfloat16) -> Inputs:
     """Packed inputs with explicit (possibly unequal or zero) q/k lengths."""
     wl = Workload(name, len(lens_q), heads, heads_k, 0, 0, head_dim, causal,
                   varlen=True, seed=seed)
     gen = torch.Generator(device="cpu")
     gen.manual_seed(seed)
     Tq, Tk = sum(lens_q), sum(lens_k)
-    q = _randn_bf16(gen, (Tq, heads, head_dim))
-    k = _randn_bf16(gen, (Tk, heads_k, head_dim))
-    v = _randn_bf16(gen, (Tk, heads_k, head_dim))
-    do = _randn_bf16(gen, (Tq, heads, head_dim))
+    q = _randn(gen, (Tq, heads, head_dim), dtype)
+    k = _randn(gen, (Tk, heads_k, head_dim), dtype)
+    v = _randn(gen, (Tk, heads_k, head_dim), dtype)
+    do = _randn(gen, (Tq, heads, head_dim), dtype)
     return Inputs(wl, q, k, v, do, list(lens_q), list(lens_k))
