@@ -11,16 +11,18 @@
 // fp32 atomic rate of the L2 would otherwise bound the whole backward), no
 // fp32 accumulator and no convert pass, and the result is bit-reproducible.
 //
-// One workgroup (4 wave64s) owns 128 query rows of one query head; wave w
-// owns rows 32w .. 32w+31, whose Q and dO rows stay in registers as the B
-// operands of
-//     S^T  = K Q^T        dP^T = V dO^T        (64 keys x 32 rows per wave)
+// One workgroup (8 wave64s, two per SIMD) owns 256 query rows of one query
+// head; wave w owns rows 32w .. 32w+31, whose Q and dO rows stay in
+// registers as the B operands of
+//     S^T  = K Q^T        dP^T = V (-dO)^T + rowdot   (64 keys x 32 rows per wave)
 // for each 64-key tile.  The accumulator of S^T holds one query row and 16
-// keys per lane, so lse2 and rowdot are one register each, and dS (in bf16)
+// keys per lane, so lse2 and rowdot are one register each, and dS (16-bit)
 // is directly the A operand of dQ = dS K with the key index permuted as
 // described in fa_mfma.h; K then enters as a B operand through transposing
 // LDS reads.  dQ (32 x D per wave) accumulates in registers over all key
-// tiles and is scaled and stored once.
+// tiles and is scaled and stored once.  In the default mode this kernel
+// also forms lse2 and rowdot (written to the workspace for the key-tile
+// kernel, which runs after it).
 //
 // K and V tiles are loaded by buffer loads straight into the swizzled LDS
 // layout of fa_mfma.h (zero fill of keys past the end and of padded
