@@ -8,7 +8,9 @@
  * What it computes (per sequence s and query head h, KV head g = h / (H/Hk)):
  *
  *   S_ij  = scale * sum_d Q_id K_jd                       (scores)
- *   visible(i,j) = !causal || j <= i + Lk - Lq            (bottom-right causal)
+ *   visible(i,j) = (!causal || j <= i + Lk - Lq)          (bottom-right causal)
+ *                  && (wr < 0 || j <= i + Lk - Lq + wr)   (local window, right)
+ *                  && (wl < 0 || j >= i + Lk - Lq - wl)   (local window, left)
  *   LSE_i = log sum_{visible j} exp(S_ij)                 (-inf if none visible)
  *   P_ij  = exp(S_ij - LSE_i) if visible else 0           (softmax)
  *   O_i   = sum_j P_ij V_j
@@ -30,7 +32,12 @@
  *   - GQA/MQA page, causal block bound: the key limit of query row i is
  *     i + seqlen_k - seqlen_q (bottom-right alignment); backward GQA section:
  *     dK/dV of the query heads are summed over each head group.
- *   - Backward call-trace page, GQA reduce: the group sum over the H/Hk heads.
+ *   - Backward call-trace page, GQA reduce: the group sum over the H/Hk heads;
+ *     mha_bwd's window_size_left / window_size_right arguments, read as a
+ *     band around the bottom-right diagonal (query i sees keys
+ *     i + Lk - Lq - wl .. i + Lk - Lq + wr; a negative size leaves that
+ *     side unbounded), the plainest reading of names the pages do not
+ *     define further.
  *
  * Two backward evaluations are provided and tested against each other:
  *   oracle_backward_explicit -- materialises P, dP and each row's Jacobian
@@ -85,10 +92,15 @@ static double dot(const double *a, const double *b, int D)
 
 /* One score S_ij, or -inf when the pair is not visible. */
 static double score(const double *qi, const double *kj, int D, double scale,
-                    int i, int j, int Lq, int Lk, int causal,
+                    int i, int j, int Lq, int Lk, int causal, int wl, int wr,
                     const double *mask_row)
 {
-    if (causal && (int64_t)j > (int64_t)i + Lk - Lq)
+    const int64_t diag = (int64_t)i + Lk - Lq;   /* bottom-right diagonal key of row i */
+    if (causal && (int64_t)j > diag)
+        return -INFINITY;
+    if (wr >= 0 && (int64_t)j > diag + wr)
+        return -INFINITY;
+    if (wl >= 0 && (int64_t)j < diag - wl)
         return -INFINITY;
     if (mask_row && mask_row[j] == -INFINITY)
         return -INFINITY;
@@ -139,7 +151,7 @@ static int max_len(int nseq, const int64_t *cu)
 
 /* Forward: O and LSE for every (row, head). */
 int oracle_forward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
-                   int H, int Hk, int D, double scale, int causal,
+                   int H, int Hk, int D, double scale, int causal, int wl, int wr,
                    const double *mask,
                    const double *q, const double *k, const double *v,
                    double *out, double *lse)
@@ -170,7 +182,7 @@ int oracle_forward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
                 const double *mrow = mask ? mask + (int64_t)i * Lk : NULL;
                 for (int j = 0; j < Lk; j++)
                     s[j] = score(qi, k + ((k0 + j) * Hk + g) * D, D, scale,
-                                 i, j, Lq, Lk, causal, mrow);
+                                 i, j, Lq, Lk, causal, wl, wr, mrow);
                 const double L = row_lse(s, Lk);
                 double *o = out + ((q0 + i) * H + h) * D;
                 for (int d = 0; d < D; d++)
@@ -234,7 +246,7 @@ static void group_sum(int64_t total_k, int H, int Hk, int D,
  * sum_k P_ik dP_ik per (row, head).
  */
 int oracle_backward_explicit(int nseq, const int64_t *cu_q, const int64_t *cu_k,
-                             int H, int Hk, int D, double scale, int causal,
+                             int H, int Hk, int D, double scale, int causal, int wl, int wr,
                              const double *mask,
                              const double *q, const double *k, const double *v,
                              const double *dout,
@@ -284,7 +296,7 @@ int oracle_backward_explicit(int nseq, const int64_t *cu_q, const int64_t *cu_k,
             const double *mrow = mask ? mask + (int64_t)i * Lk : NULL;
             for (int j = 0; j < Lk; j++)
                 S[(size_t)i * Lk + j] = score(QP(i), KP(j), D, scale, i, j, Lq, Lk,
-                                              causal, mrow);
+                                              causal, wl, wr, mrow);
             const double L = row_lse(S + (size_t)i * Lk, Lk);
             for (int j = 0; j < Lk; j++) {
                 const double sij = S[(size_t)i * Lk + j];
@@ -368,7 +380,7 @@ int oracle_backward_explicit(int nseq, const int64_t *cu_q, const int64_t *cu_k,
  * dj_out, lse_out (nullable): D^J and LSE per (row, head).
  */
 int oracle_backward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
-                    int H, int Hk, int D, double scale, int causal,
+                    int H, int Hk, int D, double scale, int causal, int wl, int wr,
                     const double *mask,
                     const double *q, const double *k, const double *v,
                     const double *dout,
@@ -416,7 +428,7 @@ int oracle_backward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
             const double *mrow = mask ? mask + (int64_t)i * Lk : NULL;
             for (int j = 0; j < Lk; j++)
                 s[j] = score(qi, k + ((k0 + j) * Hk + g) * D, D, scale, i, j, Lq, Lk,
-                             causal, mrow);
+                             causal, wl, wr, mrow);
             const double L = row_lse(s, Lk);
             LSE[r * H + h] = L;
             double *o = dq + (r * H + h) * D;
@@ -500,7 +512,7 @@ int oracle_backward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
                             continue;
                         const double *qi = q + (r * H + h) * D;
                         const double *mrow = mask ? mask + (int64_t)i * Lk : NULL;
-                        const double sij = score(qi, kj, D, scale, i, j, Lq, Lk, causal, mrow);
+                        const double sij = score(qi, kj, D, scale, i, j, Lq, Lk, causal, wl, wr, mrow);
                         if (sij == -INFINITY)
                             continue;
                         const double p = exp(sij - L);

@@ -273,3 +273,75 @@ def test_oracle_rejects_bad_arguments():
     q, k, v, do, cu_q, cu_k = _problem(1, [4], [4], 3, 2, 4)
     with pytest.raises(ValueError):
         O.backward(q, k, v, do, cu_q, cu_k, 0.5, False)
+
+
+# ---- local (sliding-window) attention: query i sees keys
+#      i + Lk - Lq - left .. i + Lk - Lq + right (negative = unbounded) ----
+
+WINDOWS = [(3, 1), (0, 2), (4, -1), (-1, 2), (2, 0)]
+
+
+@pytest.mark.parametrize("lq,lk", [(6, 9), (8, 8), (9, 6)])
+@pytest.mark.parametrize("window", WINDOWS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_equals_explicit_minus_inf_mask(lq, lk, window, causal):
+    left, right = window
+    q, k, v, do, cu_q, cu_k = _problem(31, [lq], [lk], 2, 1, 4)
+    i = np.arange(lq)[:, None]
+    j = np.arange(lk)[None, :]
+    diag = i + lk - lq
+    vis = np.ones((lq, lk), bool)
+    if causal:
+        vis &= j <= diag
+    if right >= 0:
+        vis &= j <= diag + right
+    if left >= 0:
+        vis &= j >= diag - left
+    mask = np.where(vis, 0.0, -np.inf)
+    oa, la = O.forward(q, k, v, cu_q, cu_k, 0.6, causal, window=window)
+    ob, lb = O.forward(q, k, v, cu_q, cu_k, 0.6, False, mask=mask)
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+    for mode in ("contracted", "explicit"):
+        a = O.backward(q, k, v, do, cu_q, cu_k, 0.6, causal, mode=mode, window=window)
+        b = O.backward(q, k, v, do, cu_q, cu_k, 0.6, False, mask=mask, mode=mode)
+        for key in ("dq", "dk", "dv"):
+            assert np.array_equal(a[key], b[key]), (mode, key)
+
+
+def test_window_zero_is_the_identity_attention():
+    """window (0, 0) on a square problem: each query sees only its own key, so
+    P = I: O = V, LSE_i = S_ii, dQ = dK = 0 and dV = dO summed over the
+    query heads of the group."""
+    q, k, v, do, cu_q, cu_k = _problem(32, [7], [7], 4, 2, 5)
+    out, lse = O.forward(q, k, v, cu_q, cu_k, 0.7, False, window=(0, 0))
+    G = 2
+    for h in range(4):
+        assert np.allclose(out[:, h], v[:, h // G], rtol=0, atol=1e-14)
+        s_ii = 0.7 * np.einsum("id,id->i", q[:, h], k[:, h // G])
+        assert np.allclose(lse[:, h], s_ii, rtol=0, atol=1e-13)
+    g = O.backward(q, k, v, do, cu_q, cu_k, 0.7, False, window=(0, 0))
+    assert np.abs(g["dq"]).max() < 1e-13 and np.abs(g["dk"]).max() < 1e-13
+    for kv in range(2):
+        assert np.allclose(g["dv"][:, kv], do[:, 2 * kv] + do[:, 2 * kv + 1], rtol=0,
+                           atol=1e-13)
+
+
+def test_window_right_zero_equals_causal():
+    q, k, v, do, cu_q, cu_k = _problem(33, [5, 9], [8, 6], 2, 1, 4)
+    a = O.backward(q, k, v, do, cu_q, cu_k, 0.5, True)
+    b = O.backward(q, k, v, do, cu_q, cu_k, 0.5, False, window=(-1, 0))
+    for key in ("dq", "dk", "dv", "lse"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("window,causal", [((2, 1), False), ((1, -1), True)])
+def test_window_gradient_matches_central_differences(window, causal):
+    q, k, v, do, cu_q, cu_k = _problem(34, [4, 6], [5, 6], 2, 1, 3)
+
+    def loss():
+        out, _ = O.forward(q, k, v, cu_q, cu_k, 0.8, causal, window=window)
+        return float(np.sum(do * out))
+    g = O.backward(q, k, v, do, cu_q, cu_k, 0.8, causal, window=window)
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        fd = _central_diff(x, loss)
+        assert np.allclose(g[name], fd, rtol=1e-6, atol=1e-7), name
