@@ -45,6 +45,9 @@ class FaBwdArgs(ctypes.Structure):
         ("lse_stride", ctypes.c_int64 * 2),
         ("softmax_scale", ctypes.c_float),
         ("causal", ctypes.c_int32),
+        ("local_window", ctypes.c_int32),
+        ("window_size_left", ctypes.c_int32),
+        ("window_size_right", ctypes.c_int32),
         ("deterministic", ctypes.c_int32),
         ("dq_accumulate", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
@@ -83,6 +86,9 @@ class FaFwdArgs(ctypes.Structure):
         ("lse_stride", ctypes.c_int64 * 2),
         ("softmax_scale", ctypes.c_float),
         ("causal", ctypes.c_int32),
+        ("local_window", ctypes.c_int32),
+        ("window_size_left", ctypes.c_int32),
+        ("window_size_right", ctypes.c_int32),
     ]
 
 
@@ -157,10 +163,19 @@ class Problem:
     total_k: int = 0
 
 
+def _set_window(a, window):
+    """window = None (no local window) or (left, right), negative = unbounded."""
+    if window is None:
+        a.local_window, a.window_size_left, a.window_size_right = 0, -1, -1
+    else:
+        a.local_window = 1
+        a.window_size_left, a.window_size_right = int(window[0]), int(window[1])
+
+
 def make_args(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
               cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
               max_seqlen_k=None, deterministic=False, workspace=None,
-              dq_accumulate=False) -> FaBwdArgs:
+              dq_accumulate=False, window=None) -> FaBwdArgs:
     """Fill fa_bwd_args from tensors.  Dense tensors are (B, S, H, D); packed
     ones (total, H, D) with int32 device cu_seqlens and host max lengths.
     dq_accumulate=False: dQ by the separate query-tile pass (default);
@@ -194,6 +209,7 @@ def make_args(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
     a.lse_stride[:] = (lse.stride(0), lse.stride(1))
     a.softmax_scale = float(softmax_scale)
     a.causal = int(bool(causal))
+    _set_window(a, window)
     a.deterministic = int(bool(deterministic))
     a.dq_accumulate = int(bool(dq_accumulate))
     if workspace is not None:
@@ -250,7 +266,8 @@ def run(args: FaBwdArgs, step: str = "all", stream=None):
 
 def fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
            cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
-           deterministic=False, workspace=None, stream=None, dq_accumulate=False):
+           deterministic=False, workspace=None, stream=None, dq_accumulate=False,
+           window=None):
     """dQ, dK, dV of attention, written into dq, dk, dv (same layouts as q, k, v).
 
     lse is the forward's natural-log log-sum-exp, (B, H, Sq) fp32 (packed:
@@ -258,7 +275,7 @@ def fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
     holds the fp32 dQ accumulator and the row sums afterwards)."""
     args = make_args(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
                      cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                     deterministic, workspace, dq_accumulate)
+                     deterministic, workspace, dq_accumulate, window)
     if workspace is None:
         workspace = alloc_workspace(args, q.device)
     run(args, "all", stream)
@@ -266,7 +283,8 @@ def fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
 
 
 def make_fwd_args(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q=None,
-                  cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None) -> FaFwdArgs:
+                  cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
+                  window=None) -> FaFwdArgs:
     """Fill fa_fwd_args from tensors (layouts as in make_args)."""
     varlen = cu_seqlens_q is not None or cu_seqlens_k is not None
     a = FaFwdArgs()
@@ -293,6 +311,7 @@ def make_fwd_args(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q=None,
     a.lse_stride[:] = (lse.stride(0), lse.stride(1))
     a.softmax_scale = float(softmax_scale)
     a.causal = int(bool(causal))
+    _set_window(a, window)
     return a
 
 
@@ -306,9 +325,9 @@ def run_fwd(args: FaFwdArgs, stream=None):
 
 
 def fa_fwd(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q=None, cu_seqlens_k=None,
-           max_seqlen_q=None, max_seqlen_k=None, stream=None):
+           max_seqlen_q=None, max_seqlen_k=None, stream=None, window=None):
     """O and the natural-log LSE of attention, written into out (layout of q)
     and lse ((B, H, Sq) fp32; packed: (num_seqs, H, max_seqlen_q))."""
     args = make_fwd_args(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q, cu_seqlens_k,
-                         max_seqlen_q, max_seqlen_k)
+                         max_seqlen_q, max_seqlen_k, window)
     run_fwd(args, stream)

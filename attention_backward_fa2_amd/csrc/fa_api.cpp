@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <string>
 
@@ -34,6 +35,17 @@ fa_status fail(fa_status st, const char *fmt, ...)
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Sequence lengths and window sizes stay below 2^29 so that row + offset +
+// window sums fit in 32-bit integers in the kernels (a window of 2^29 or
+// more reaches past every key of such a sequence).
+constexpr int kMaxSeqlen = 1 << 29;
+
+void set_window(fa::Params &p, int causal, int left, int right)
+{
+    p.win_l = left < 0 ? -1 : std::min(left, kMaxSeqlen);
+    p.win_r = causal ? 0 : (right < 0 ? -1 : std::min(right, kMaxSeqlen));
+}
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -74,6 +86,8 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
         return fail(FA_ERR_UNSUPPORTED, "dtype %d unsupported (bf16 or fp16)", a->dtype);
     if (a->batch < 0 || a->seqlen_q < 0 || a->seqlen_k < 0)
         return fail(FA_ERR_INVALID_ARG, "negative batch or sequence length");
+    if (a->seqlen_q > kMaxSeqlen || a->seqlen_k > kMaxSeqlen)
+        return fail(FA_ERR_UNSUPPORTED, "sequence length above 2^29");
     if (a->num_heads <= 0 || a->num_heads_k <= 0 || a->head_dim <= 0)
         return fail(FA_ERR_INVALID_ARG, "num_heads, num_heads_k and head_dim must be positive");
     if (a->num_heads % a->num_heads_k != 0)
@@ -132,6 +146,11 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
     if ((a->causal != 0 && a->causal != 1) || (a->deterministic != 0 && a->deterministic != 1) ||
         (a->dq_accumulate != 0 && a->dq_accumulate != 1))
         return fail(FA_ERR_INVALID_ARG, "causal, deterministic and dq_accumulate must be 0 or 1");
+    if (a->local_window != 0 && a->local_window != 1)
+        return fail(FA_ERR_INVALID_ARG, "local_window must be 0 or 1");
+    if (a->local_window && a->causal && a->window_size_right > 0)
+        return fail(FA_ERR_INVALID_ARG, "causal = 1 with window_size_right = %d > 0",
+                    a->window_size_right);
 
     fa::Params &p = pl->p;
     std::memset(&p, 0, sizeof p);
@@ -172,6 +191,8 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
     p.scale = a->softmax_scale;
     p.scale_log2 = (float)((double)a->softmax_scale * 1.4426950408889634);
     p.causal = a->causal;
+    set_window(p, a->causal, a->local_window ? a->window_size_left : -1,
+               a->local_window ? a->window_size_right : -1);
     p.deterministic = a->deterministic;
     p.fused_dq = a->dq_accumulate;
     p.f16 = a->dtype == FA_DTYPE_F16;
@@ -270,6 +291,8 @@ fa_status make_fwd_plan(const fa_fwd_args *a, fa::Params *pp, int *dpad_out)
         return fail(FA_ERR_UNSUPPORTED, "dtype %d unsupported (bf16 or fp16)", a->dtype);
     if (a->batch < 0 || a->seqlen_q < 0 || a->seqlen_k < 0)
         return fail(FA_ERR_INVALID_ARG, "negative batch or sequence length");
+    if (a->seqlen_q > kMaxSeqlen || a->seqlen_k > kMaxSeqlen)
+        return fail(FA_ERR_UNSUPPORTED, "sequence length above 2^29");
     if (a->num_heads <= 0 || a->num_heads_k <= 0 || a->head_dim <= 0)
         return fail(FA_ERR_INVALID_ARG, "num_heads, num_heads_k and head_dim must be positive");
     if (a->num_heads % a->num_heads_k != 0)
@@ -314,6 +337,11 @@ fa_status make_fwd_plan(const fa_fwd_args *a, fa::Params *pp, int *dpad_out)
         return fail(FA_ERR_INVALID_ARG, "softmax_scale is not finite");
     if (a->causal != 0 && a->causal != 1)
         return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (a->local_window != 0 && a->local_window != 1)
+        return fail(FA_ERR_INVALID_ARG, "local_window must be 0 or 1");
+    if (a->local_window && a->causal && a->window_size_right > 0)
+        return fail(FA_ERR_INVALID_ARG, "causal = 1 with window_size_right = %d > 0",
+                    a->window_size_right);
 
     fa::Params &p = *pp;
     std::memset(&p, 0, sizeof p);
@@ -344,6 +372,8 @@ fa_status make_fwd_plan(const fa_fwd_args *a, fa::Params *pp, int *dpad_out)
     p.scale = a->softmax_scale;
     p.scale_log2 = (float)((double)a->softmax_scale * 1.4426950408889634);
     p.causal = a->causal;
+    set_window(p, a->causal, a->local_window ? a->window_size_left : -1,
+               a->local_window ? a->window_size_right : -1);
     p.f16 = a->dtype == FA_DTYPE_F16;
     *dpad_out = dpad;
     g_last_error.clear();

@@ -56,7 +56,10 @@ struct __attribute__((aligned(16))) DqSmem {
     KVBuf<DP> buf[3];
 };
 
-template <int DP, bool F16>
+// LOCAL: a left window bounds the visible keys from below (win_l >= 0);
+// otherwise win_l < 0 and only the upper bound (causal / right window / key
+// end) is masked.
+template <int DP, bool F16, bool LOCAL>
 __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
 {
     constexpr int KS = DP / 16;                  // k-steps over the head dim
@@ -96,13 +99,15 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
     const int qrow = q0 + 32 * w + l32;          // this lane's query row
     const bool qok = qrow < Lq;
 
-    // Key tiles visible to some row of this query tile.
+    // Key tiles t_lo .. nkt-1 hold the keys visible to some row of this
+    // query tile (rows q0 .. q_last see keys k_lo .. k_hi at most).
     const int q_last = min(q0 + kDqRows, Lq) - 1;
-    int nkt = (Lk + kDqKeys - 1) / kDqKeys;
-    if (p.causal)
-        nkt = min(nkt, max(0, (q_last + off + kDqKeys) / kDqKeys));
-    // Visible keys of this lane's row: key <= klim.
-    const int klim = qok ? (p.causal ? min(Lk - 1, qrow + off) : Lk - 1) : -1;
+    const int k_lo = LOCAL ? max(0, q0 + off - p.win_l) : 0;
+    const int k_hi = p.win_r >= 0 ? min(Lk - 1, q_last + off + p.win_r) : Lk - 1;
+    const int t_lo = k_lo / kDqKeys;
+    const int nkt = k_hi >= k_lo ? k_hi / kDqKeys + 1 : t_lo;
+    // Without a left window: the lane's row sees keys <= klim.
+    const int klim = qok ? (p.win_r >= 0 ? min(Lk - 1, qrow + off + p.win_r) : Lk - 1) : -1;
 
     // Global byte offsets of the 16-byte chunk each lane loads for wave
     // load i (LDS row pr holds tile chunk (lane % PCH) ^ swz(pr)).
@@ -121,8 +126,10 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
     // scalar registers kept at the call's place in the instruction stream.
     const uint16_t *k_next = p.k + hk * p.k_sh + row_offset(p, b, si.tok_k, 0, p.k_sb, p.k_ss);
     const uint16_t *v_next = p.v + hk * p.v_sh + row_offset(p, b, si.tok_k, 0, p.v_sb, p.v_ss);
-    int n_next = 0, n_left = nkt;
+    int n_next = t_lo * kDqKeys, n_left = nkt - t_lo;
     const int64_t kstep = (int64_t)kDqKeys * p.k_ss, vstep = (int64_t)kDqKeys * p.v_ss;
+    k_next += t_lo * kstep;
+    v_next += t_lo * vstep;
     auto issue = [&](int bf) {
         keep_scalar_here(n_next, n_left, k_next, v_next);
         const int kv = n_left > 0 ? min(kDqKeys, Lk - n_next) : 0;
@@ -145,7 +152,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
     };
     // The first two key tiles are in flight while the row vectors below
     // are formed.
-    if (nkt > 0) {
+    if (nkt > t_lo) {
         issue(0);
         issue(1);
     }
@@ -238,7 +245,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
         zero(acc[db]);
 
 
-    if (nkt > 0) {
+    if (nkt > t_lo) {
         // LDS byte offsets of this lane's operand reads in the current
         // buffer (V is BYTES further):
         //  gq[ks]:    16-byte read of K / V row l32, tile chunk 2*ks + g2 (+ 32
@@ -293,22 +300,38 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
         e16x8 ring[RA];
         static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
 
-        // Smallest visible-key limit over the wave's rows (-1 if any row is
-        // past the end): key tiles wholly at or below it need no mask.
+        // Smallest last visible key over the wave's rows (-1 if any row is
+        // past the end) and largest first visible key: key tiles wholly
+        // between the two are visible to every row of the wave and need no
+        // mask.  They are the tiles f_lo .. f_hi-1 (none if f_lo >= f_hi).
         const int r0w = q0 + 32 * w;
-        const int kmin_w = r0w + 31 < Lq ? (p.causal ? min(Lk - 1, r0w + off) : Lk - 1) : -1;
-
-        // Key tiles 0 .. nfull-1 are fully visible to every row of the wave.
-        const int nfull = min(nkt, max(0, (kmin_w + 1) / kDqKeys));
+        const int kmin_w =
+            r0w + 31 < Lq ? (p.win_r >= 0 ? min(Lk - 1, r0w + off + p.win_r) : Lk - 1) : -1;
+        const int kfirst_w = LOCAL ? r0w + 31 + off - p.win_l : 0;
+        const int f_lo = max(t_lo, kfirst_w <= 0 ? 0 : (kfirst_w + kDqKeys - 1) / kDqKeys);
+        const int f_hi = min(nkt, max(0, (kmin_w + 1) / kDqKeys));
 
         int cur = 0;
-        // One key tile, with or without the element mask (the same slots
-        // otherwise).
+        // One key tile, with (IC<1>) or without (IC<0>) the element mask (the
+        // same slots otherwise).
         auto tile = [&](int t, auto maskc) {
             const int n0 = t * kDqKeys;
-            // element (32*mb + 8*r4 + t) of the lane's keys (+ 4*g2) is kept
-            // iff it is <= kthr
-            const int kthr = klim - n0 - 4 * g2;
+            // Masked tiles: element (32*mb + 8*r4 + t) of the lane's keys (+
+            // 4*g2) is kept iff it is <= kthr and (LOCAL) >= kthr_lo (the
+            // lane's row sees keys row + off - win_l .. row + off + win_r,
+            // none past the key end, none if the row is past the end).  With
+            // a left window both are formed per tile from the lane index:
+            // every register of the wave is taken.
+            int kthr = 0, kthr_lo = 0;
+            if constexpr (!LOCAL) {
+                kthr = klim - n0 - 4 * g2;
+            } else if constexpr (decltype(maskc)::value != 0) {
+                const int ln = lane_here();
+                const int row = r0w + (ln & 31), kg = n0 + 4 * (ln >> 5);
+                const int hi = p.win_r >= 0 ? min(Lk - 1, row + off + p.win_r) : Lk - 1;
+                kthr = row < Lq ? hi - kg : -1;
+                kthr_lo = row + off - p.win_l - kg;
+            }
             const int delta = cur == NBUF - 1 ? -(NBUF - 1) * BUFB : BUFB;
 
             f32x16 st[2], dpt[2];
@@ -321,8 +344,10 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                 constexpr int mb = decltype(mbc)::value, e = decltype(ec)::value;
                 constexpr int r4 = e >> 2, tt = e & 3;
                 float x = __builtin_amdgcn_exp2f(st[mb][e] * p.scale_log2 - l2);
-                if constexpr (decltype(maskc)::value)
-                    x = 32 * mb + 8 * r4 + tt <= kthr ? x : 0.f;
+                if constexpr (decltype(maskc)::value) {
+                    constexpr int ke = 32 * mb + 8 * r4 + tt;
+                    x = ke <= kthr && (!LOCAL || ke >= kthr_lo) ? x : 0.f;
+                }
                 float d = x * -dpt[mb][e];   // dpt holds rowdot - dP
                 keep_here(d);
                 dv[tt] = d;
@@ -389,24 +414,34 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
             });
             cur = cur == NBUF - 1 ? 0 : cur + 1;
         };
-        int t = 0;
-        for (; t < nfull; ++t)
-            tile(t, std::false_type{});
+        // Masked tiles t_lo .. f_lo-1, unmasked f_lo .. f_hi-1, masked
+        // f_hi .. nkt-1 (three loops: one masked loop entered twice makes
+        // the register allocator spill).
+        int t = t_lo;
+        const int m_end = f_lo < f_hi ? f_lo : t_lo;
+        const int u_end = f_lo < f_hi ? f_hi : t_lo;
+        if constexpr (LOCAL)
+            for (; t < m_end; ++t)
+                tile(t, IC<1>{});
+        for (; t < u_end; ++t)
+            tile(t, IC<0>{});
         for (; t < nkt; ++t)
-            tile(t, std::true_type{});
+            tile(t, IC<1>{});
         // loads issued past the last tile must land before LDS is released
         wait_loads<0>();
     }
 
     // ---- dQ = scale * acc -> bf16.  Accumulator: column d = 32 db + l32,
-    //      rows 8 (r/4) + 4 g2 + r%4 of the wave's 32 query rows. ----
+    //      rows 8 (r/4) + 4 g2 + r%4 of the wave's 32 query rows (lane
+    //      index formed again: no register holds it across the loop). ----
+    const int ln = lane_here();
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-        const int d = 32 * db + l32;
+        const int d = 32 * db + (ln & 31);
         if (d < p.D) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int qr = q0 + 32 * w + 8 * (r >> 2) + 4 * g2 + (r & 3);
+                const int qr = q0 + 32 * w + 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
                 if (qr < Lq)
                     p.dq[row_offset(p, b, si.tok_q, qr, p.dq_sb, p.dq_ss) + h * p.dq_sh + d] =
                         f2elem<F16>(acc[db][r] * p.scale);
@@ -415,7 +450,8 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
     }
 }
 
-hipError_t launch_dq(const Params &p, int dpad, hipStream_t st)
+template <bool LOCAL>
+static hipError_t launch_dq_t(const Params &p, int dpad, hipStream_t st)
 {
     const int nqt = (p.Sq + kDqRows - 1) / kDqRows;
     const dim3 grid((unsigned)nqt * p.H * p.batch);
@@ -423,26 +459,31 @@ hipError_t launch_dq(const Params &p, int dpad, hipStream_t st)
     switch (dpad) {
     case 64:
         if (p.f16)
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<64, true>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<64, true, LOCAL>), grid, block, 0, st, p);
         else
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<64, false>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<64, false, LOCAL>), grid, block, 0, st, p);
         break;
     case 96:
         if (p.f16)
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<96, true>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<96, true, LOCAL>), grid, block, 0, st, p);
         else
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<96, false>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<96, false, LOCAL>), grid, block, 0, st, p);
         break;
     case 128:
         if (p.f16)
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<128, true>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<128, true, LOCAL>), grid, block, 0, st, p);
         else
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<128, false>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<128, false, LOCAL>), grid, block, 0, st, p);
         break;
     default:
         return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_dq(const Params &p, int dpad, hipStream_t st)
+{
+    return p.win_l >= 0 ? launch_dq_t<true>(p, dpad, st) : launch_dq_t<false>(p, dpad, st);
 }
 
 }  // namespace fa

@@ -54,7 +54,9 @@ struct __attribute__((aligned(16))) FwdSmem {
     FwdKV<DP> buf[3];
 };
 
-template <int DP, bool F16>
+// LOCAL: a left window bounds the visible keys from below (win_l >= 0);
+// otherwise win_l < 0 and only the upper bound is masked.
+template <int DP, bool F16, bool LOCAL>
 __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
 {
     constexpr int KS = DP / 16;                  // k-steps over the head dim
@@ -86,17 +88,20 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
     if (q0 >= si.Lq)
         return;
     const int Lq = si.Lq, Lk = si.Lk;
-    const int off = Lk - Lq;                     // bottom-right causal offset
+    const int off = Lk - Lq;                     // bottom-right alignment offset
     const int qrow = q0 + 32 * w + l32;          // this lane's query row
     const bool qok = qrow < Lq;
 
-    // Key tiles visible to some row of this query tile.
+    // Key tiles t_lo .. nkt-1 hold the keys visible to some row of this
+    // query tile (rows q0 .. q_last see keys k_lo .. k_hi at most).
     const int q_last = min(q0 + kFwdRows, Lq) - 1;
-    int nkt = (Lk + kFwdKeys - 1) / kFwdKeys;
-    if (p.causal)
-        nkt = min(nkt, max(0, (q_last + off + kFwdKeys) / kFwdKeys));
-    // Visible keys of this lane's row: key <= klim.
-    const int klim = qok ? (p.causal ? min(Lk - 1, qrow + off) : Lk - 1) : -1;
+    const int k_lo = LOCAL ? max(0, q0 + off - p.win_l) : 0;
+    const int k_hi = p.win_r >= 0 ? min(Lk - 1, q_last + off + p.win_r) : Lk - 1;
+    const int t_lo = k_lo / kFwdKeys;
+    const int nkt = k_hi >= k_lo ? k_hi / kFwdKeys + 1 : t_lo;
+    // Visible keys of this lane's row: kfirst <= key <= klim.
+    const int klim = qok ? (p.win_r >= 0 ? min(Lk - 1, qrow + off + p.win_r) : Lk - 1) : -1;
+    const int kfirst = LOCAL ? qrow + off - p.win_l : 0;
 
     // Global byte offsets of the 16-byte chunk each lane loads for wave
     // load i (LDS row pr holds tile chunk (lane % PCH) ^ swz(pr)).
@@ -113,8 +118,10 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
     // past the last tile: empty bound, zeros, no memory access).
     const uint16_t *k_next = p.k + hk * p.k_sh + row_offset(p, b, si.tok_k, 0, p.k_sb, p.k_ss);
     const uint16_t *v_next = p.v + hk * p.v_sh + row_offset(p, b, si.tok_k, 0, p.v_sb, p.v_ss);
-    int n_next = 0, n_left = nkt;
+    int n_next = t_lo * kFwdKeys, n_left = nkt - t_lo;
     const int64_t kstep = (int64_t)kFwdKeys * p.k_ss, vstep = (int64_t)kFwdKeys * p.v_ss;
+    k_next += t_lo * kstep;
+    v_next += t_lo * vstep;
     auto issue = [&](int bf) {
         keep_scalar_here(n_next, n_left, k_next, v_next);
         const int kv = n_left > 0 ? min(kFwdKeys, Lk - n_next) : 0;
@@ -135,7 +142,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
             load16_to_lds(rv, kb.v + ld, vov[i]);
         }
     };
-    if (nkt > 0) {
+    if (nkt > t_lo) {
         issue(0);
         issue(1);
     }
@@ -165,7 +172,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
     // keys; the halves are added at the end).
     float mrun = -INFINITY, lsum = 0.f;
 
-    if (nkt > 0) {
+    if (nkt > t_lo) {
         // LDS byte offsets of this lane's operand reads in the current
         // buffer: gq[ks] the 16-byte read of K row l32, tile chunk
         // 2*ks + g2 (+ 32 rows per key block); tq[db][h] the transposing
@@ -218,20 +225,26 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
         e16x8 ring[RA];
         static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
 
-        // Smallest visible-key limit over the wave's rows (-1 if any row is
-        // past the end): key tiles wholly at or below it need no mask.
+        // Smallest last visible key over the wave's rows (-1 if any row is
+        // past the end) and largest first visible key: key tiles wholly
+        // between the two are visible to every row of the wave and need no
+        // mask.  They are the tiles f_lo .. f_hi-1 (none if f_lo >= f_hi).
         const int r0w = q0 + 32 * w;
-        const int kmin_w = r0w + 31 < Lq ? (p.causal ? min(Lk - 1, r0w + off) : Lk - 1) : -1;
-        const int nfull = min(nkt, max(0, (kmin_w + 1) / kFwdKeys));
+        const int kmin_w =
+            r0w + 31 < Lq ? (p.win_r >= 0 ? min(Lk - 1, r0w + off + p.win_r) : Lk - 1) : -1;
+        const int kfirst_w = LOCAL ? r0w + 31 + off - p.win_l : 0;
+        const int f_lo = max(t_lo, kfirst_w <= 0 ? 0 : (kfirst_w + kFwdKeys - 1) / kFwdKeys);
+        const int f_hi = min(nkt, max(0, (kmin_w + 1) / kFwdKeys));
         const float c2 = p.scale_log2;
 
         int cur = 0;
         auto tile = [&](int t, auto maskc) {
-            constexpr bool MASK = decltype(maskc)::value;
+            constexpr bool MASK = decltype(maskc)::value != 0;
             const int n0 = t * kFwdKeys;
             // element (32*mb + 8*r4 + tt) of the lane's keys (+ 4*g2) is
-            // visible iff it is <= kthr
+            // visible iff it is <= kthr and (LOCAL) >= kthr_lo
             const int kthr = klim - n0 - 4 * g2;
+            const int kthr_lo = kfirst - n0 - 4 * g2;
             const int delta = cur == NBUF - 1 ? -(NBUF - 1) * BUFB : BUFB;
 
             f32x16 st[2];
@@ -244,8 +257,9 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
 
             auto visible = [&](auto mbc, auto ec) -> bool {
                 constexpr int mb = decltype(mbc)::value, e = decltype(ec)::value;
+                constexpr int ke = 32 * mb + 8 * (e >> 2) + (e & 3);
                 if constexpr (MASK)
-                    return 32 * mb + 8 * (e >> 2) + (e & 3) <= kthr;
+                    return ke <= kthr && (!LOCAL || ke >= kthr_lo);
                 else
                     return true;
             };
@@ -346,11 +360,19 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
             });
             cur = cur == NBUF - 1 ? 0 : cur + 1;
         };
-        int t = 0;
-        for (; t < nfull; ++t)
-            tile(t, std::false_type{});
+        // Masked tiles t_lo .. f_lo-1, unmasked f_lo .. f_hi-1, masked
+        // f_hi .. nkt-1 (three loops: one masked loop entered twice makes
+        // the register allocator spill).
+        int t = t_lo;
+        const int m_end = f_lo < f_hi ? f_lo : t_lo;
+        const int u_end = f_lo < f_hi ? f_hi : t_lo;
+        if constexpr (LOCAL)
+            for (; t < m_end; ++t)
+                tile(t, IC<1>{});
+        for (; t < u_end; ++t)
+            tile(t, IC<0>{});
         for (; t < nkt; ++t)
-            tile(t, std::true_type{});
+            tile(t, IC<1>{});
         // loads issued past the last tile must land before LDS is released
         wait_loads<0>();
     }
@@ -380,7 +402,8 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
     }
 }
 
-hipError_t launch_fwd(const Params &p, int dpad, hipStream_t st)
+template <bool LOCAL>
+static hipError_t launch_fwd_t(const Params &p, int dpad, hipStream_t st)
 {
     const int nqt = (p.Sq + kFwdRows - 1) / kFwdRows;
     const dim3 grid((unsigned)nqt * p.H * p.batch);
@@ -388,26 +411,31 @@ hipError_t launch_fwd(const Params &p, int dpad, hipStream_t st)
     switch (dpad) {
     case 64:
         if (p.f16)
-            hipLaunchKernelGGL((fa_fwd_kernel<64, true>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_fwd_kernel<64, true, LOCAL>), grid, block, 0, st, p);
         else
-            hipLaunchKernelGGL((fa_fwd_kernel<64, false>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_fwd_kernel<64, false, LOCAL>), grid, block, 0, st, p);
         break;
     case 96:
         if (p.f16)
-            hipLaunchKernelGGL((fa_fwd_kernel<96, true>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_fwd_kernel<96, true, LOCAL>), grid, block, 0, st, p);
         else
-            hipLaunchKernelGGL((fa_fwd_kernel<96, false>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_fwd_kernel<96, false, LOCAL>), grid, block, 0, st, p);
         break;
     case 128:
         if (p.f16)
-            hipLaunchKernelGGL((fa_fwd_kernel<128, true>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_fwd_kernel<128, true, LOCAL>), grid, block, 0, st, p);
         else
-            hipLaunchKernelGGL((fa_fwd_kernel<128, false>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_fwd_kernel<128, false, LOCAL>), grid, block, 0, st, p);
         break;
     default:
         return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_fwd(const Params &p, int dpad, hipStream_t st)
+{
+    return p.win_l >= 0 ? launch_fwd_t<true>(p, dpad, st) : launch_fwd_t<false>(p, dpad, st);
 }
 
 }  // namespace fa

@@ -53,6 +53,10 @@ struct Params {
     float scale;        // softmax scale
     float scale_log2;   // softmax scale * log2(e)
     int causal, deterministic, varlen;
+    // Visible keys of query row i: i + off - win_l .. i + off + win_r
+    // (off = Lk - Lq; a negative size leaves that side unbounded; causal is
+    // win_r = 0).
+    int win_l, win_r;
     int fused_dq;       // 1: dQ partials added into dq_acc by the key-tile kernel
     int f16;            // 1: fp16 elements, 0: bf16
 };

@@ -6,7 +6,9 @@
 // K and V loaded once, query tiles streamed).  It loops over every query head
 // of the KV head's group and, for each, over the 64-row query tiles that can
 // see at least one of its keys (causal block bound with the seqlen_k -
-// seqlen_q offset of the GQA/MQA page).  Per query tile it runs the products
+// seqlen_q offset of the GQA/MQA page; with a local window of mha_bwd's
+// window_size_left / _right on the backward call-trace page, the query
+// rows whose window meets the tile).  Per query tile it runs the products
 // of the sm90 backward page's mma_one_m_block on bf16 MFMA with fp32
 // accumulation:
 //     S  = Q K^T            dP = dO V^T
@@ -133,11 +135,12 @@ __device__ inline void dq_partial(const Params &p, FusedSmem<DP> &sm, int buf, i
                 int *turn = nullptr;
                 if (p.deterministic) {
                     // Rank of this key tile among the tiles adding into query
-                    // tile m, highest key tile first.
+                    // tile m, highest key tile first (the last row of the tile
+                    // sees keys up to lim, which this key tile reaches).
                     int jmax = nt_b - 1;
-                    if (p.causal) {
-                        const int lim = min(q0 + kQTile, Lq) + off;
-                        jmax = min(jmax, (lim + kKTile - 1) / kKTile - 1);
+                    if (p.win_r >= 0) {
+                        const int lim = min(q0 + kQTile, Lq) - 1 + off + p.win_r;
+                        jmax = min(jmax, lim / kKTile);
                     }
                     const int rank = jmax - j;
                     turn = p.turns + ((int64_t)b * p.H + h) * p.mtiles + m;
@@ -185,7 +188,9 @@ __device__ inline void dq_partial(const Params &p, FusedSmem<DP> &sm, int buf, i
                 }
 }
 
-template <int DP, bool FUSED, bool F16>
+// LOCAL: a left window bounds the visible keys from below (win_l >= 0);
+// otherwise win_l < 0 and only the upper bound is masked.
+template <int DP, bool FUSED, bool F16, bool LOCAL>
 __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
 {
     constexpr int KS = DP / 16;       // MFMA k-steps over the head dim
@@ -230,7 +235,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
     if (n0 >= si.Lk)
         return;
     const int Lq = si.Lq, Lk = si.Lk;
-    const int off = Lk - Lq;                // bottom-right causal offset
+    const int off = Lk - Lq;                // bottom-right alignment offset
     const int key_local = w * 32 + l32;
     const int key = n0 + key_local;
 
@@ -268,10 +273,14 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         zero(dv_acc[db]);
     }
 
-    const int first_q = p.causal ? max(0, n0 - off) : 0;
-    if (first_q < Lq) {
+    // Query rows first_q .. last_q see some key of this tile (query row i
+    // sees keys i + off - win_l .. i + off + win_r).
+    const int first_q = p.win_r >= 0 ? max(0, n0 - off - p.win_r) : 0;
+    const int last_q =
+        LOCAL ? min(Lq - 1, min(Lk - 1, n0 + kKTile - 1) - off + p.win_l) : Lq - 1;
+    if (first_q <= last_q) {
         const int m_begin = first_q / kQTile;
-        const int m_end = (Lq + kQTile - 1) / kQTile;
+        const int m_end = last_q / kQTile + 1;
         const int nm = m_end - m_begin;
         const int total = p.G * nm;
         const int nt_b = (Lk + kKTile - 1) / kKTile;
@@ -324,7 +333,8 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         // the last query tile first, so the workgroups of one (batch, KV
         // head) running side by side on an XCD read the same tile at about
         // the same time (L2 reuse).  Ordered dQ adds keep the ascending
-        // order, in which no workgroup waits on its first tile.
+        // order, in which no workgroup waits on its first tile unless a
+        // right window reaches into the next key tile.
         const bool ascending = FUSED && p.deterministic;
         auto tile_m = [&](int it) {
             const int r = it % nm;
@@ -512,16 +522,19 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             read_rowdot(0, r4);
 
         int cur = 0;
-        // One query tile, with or without the element mask (the same slots
-        // otherwise).
+        // One query tile, with (IC<1>) or without (IC<0>) the element mask
+        // (the same slots otherwise).
         auto tile = [&](int it, int m, auto maskc) {
             if constexpr (FUSED)
                 issue(cur ^ 1);
             const int q0 = m * kQTile;
-            // Visibility threshold of this lane's key over tile rows
-            // 4*g2 + (32*mb + 8*r4 + t): keys past the end see nothing;
-            // causal: key <= q0 + row + off.
-            const int limv = key >= Lk ? INT_MAX : (p.causal ? key - q0 - off - 4 * g2 : INT_MIN);
+            // This lane's key is visible to tile rows 4*g2 + (32*mb + 8*r4 +
+            // t) with limv <= 32*mb + 8*r4 + t <= limu: none past the key
+            // end; else rows with key <= q0 + row + off + win_r and key >=
+            // q0 + row + off - win_l.
+            const int limv =
+                key >= Lk ? INT_MAX : (p.win_r >= 0 ? key - q0 - off - p.win_r - 4 * g2 : INT_MIN);
+            const int limu = LOCAL ? key - q0 - off + p.win_l - 4 * g2 : INT_MAX;
             uint16_t *dsrow = nullptr;
             if constexpr (FUSED)
                 dsrow = &sm.dsT[cur][key_local * FusedSmem<DP>::RD + 4 * g2];
@@ -543,7 +556,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 constexpr int qc = 32 * mb + 8 * r4;
                 float x = __builtin_amdgcn_exp2f(s[mb][e] * p.scale_log2 - l2v[r4][t]);
                 if constexpr (decltype(maskc)::value)
-                    x = qc + t >= limv ? x : 0.f;
+                    x = qc + t >= limv && (!LOCAL || qc + t <= limu) ? x : 0.f;
                 float d = x * -dp[mb][e];   // dp holds rowdot - dP
                 keep_here(x);
                 keep_here(d);
@@ -694,26 +707,39 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         };
         if constexpr (FUSED) {
             for (int it = 0; it < total; ++it)
-                tile(it, tile_m(it), std::true_type{});
+                tile(it, tile_m(it), IC<1>{});
         } else {
-            // The wave's keys are visible to every row of query tiles m >=
-            // m_vis (and to none past the sequence end); within each head
-            // those come first in the descending order.
-            const int kw_last = n0 + 32 * w + 31;
-            int nun = 0;
+            // The wave's keys kw0 .. kw_last are visible to every row of the
+            // query tiles mf_lo .. mf_hi (none if a key is past the end):
+            // rows >= kw_last - off - win_r and rows <= kw0 - off + win_l.
+            // In the descending order of a head those come after nh masked
+            // tiles and before the masked rest.  (Three loops per head: a
+            // single masked loop spanning the heads makes the register
+            // allocator spill.)
+            const int kw0 = n0 + 32 * w, kw_last = kw0 + 31;
+            int nh = 0, nu = 0;
             if (kw_last < Lk) {
-                const int need = kw_last - off;
-                const int m_vis = !p.causal || need <= 0 ? 0 : (need + kQTile - 1) / kQTile;
-                nun = max(0, m_end - max(m_begin, m_vis));
+                const int need = kw_last - off - p.win_r;
+                const int mf_lo = max(m_begin, p.win_r < 0 || need <= 0 ? 0 : (need + kQTile - 1) / kQTile);
+                const int top = kw0 - off + p.win_l - (kQTile - 1);   // last row of tile m <= top + 63
+                const int mf_hi =
+                    !LOCAL ? m_end - 1 : min(m_end - 1, top >= 0 ? top / kQTile : -1);
+                if (mf_lo <= mf_hi) {
+                    nh = m_end - 1 - mf_hi;
+                    nu = mf_hi - mf_lo + 1;
+                }
             }
             int it = 0;
             for (int hh = 0; hh < p.G; ++hh) {
                 int m = m_end - 1;
-                const int it_u = it + nun, it_e = it + nm;
+                const int it_h = it + nh, it_u = it_h + nu, it_e = it + nm;
+                if constexpr (LOCAL)
+                    for (; it < it_h; ++it, --m)
+                        tile(it, m, IC<1>{});
                 for (; it < it_u; ++it, --m)
-                    tile(it, m, std::false_type{});
+                    tile(it, m, IC<0>{});
                 for (; it < it_e; ++it, --m)
-                    tile(it, m, std::true_type{});
+                    tile(it, m, IC<1>{});
             }
         }
         // The last iterations issued loads past the final tile (empty bound,
@@ -746,19 +772,20 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
     }
 }
 
-hipError_t launch_main(const Params &p, int dpad, hipStream_t st)
+template <bool LOCAL>
+static hipError_t launch_main_t(const Params &p, int dpad, hipStream_t st)
 {
     const dim3 grid((unsigned)p.ntiles * p.Hk * p.batch);
     const dim3 block(kThreads);
-#define FA_LAUNCH_MAIN(D)                                                                  \
-    if (p.fused_dq && p.f16)                                                               \
-        hipLaunchKernelGGL((fa_bwd_main_kernel<D, true, true>), grid, block, 0, st, p);    \
-    else if (p.fused_dq)                                                                   \
-        hipLaunchKernelGGL((fa_bwd_main_kernel<D, true, false>), grid, block, 0, st, p);   \
-    else if (p.f16)                                                                        \
-        hipLaunchKernelGGL((fa_bwd_main_kernel<D, false, true>), grid, block, 0, st, p);   \
-    else                                                                                   \
-        hipLaunchKernelGGL((fa_bwd_main_kernel<D, false, false>), grid, block, 0, st, p);
+#define FA_LAUNCH_MAIN(D)                                                                        \
+    if (p.fused_dq && p.f16)                                                                     \
+        hipLaunchKernelGGL((fa_bwd_main_kernel<D, true, true, LOCAL>), grid, block, 0, st, p);   \
+    else if (p.fused_dq)                                                                         \
+        hipLaunchKernelGGL((fa_bwd_main_kernel<D, true, false, LOCAL>), grid, block, 0, st, p);  \
+    else if (p.f16)                                                                              \
+        hipLaunchKernelGGL((fa_bwd_main_kernel<D, false, true, LOCAL>), grid, block, 0, st, p);  \
+    else                                                                                         \
+        hipLaunchKernelGGL((fa_bwd_main_kernel<D, false, false, LOCAL>), grid, block, 0, st, p);
     switch (dpad) {
     case 64:
         FA_LAUNCH_MAIN(64);
@@ -774,6 +801,11 @@ hipError_t launch_main(const Params &p, int dpad, hipStream_t st)
     }
 #undef FA_LAUNCH_MAIN
     return hipGetLastError();
+}
+
+hipError_t launch_main(const Params &p, int dpad, hipStream_t st)
+{
+    return p.win_l >= 0 ? launch_main_t<true>(p, dpad, st) : launch_main_t<false>(p, dpad, st);
 }
 
 }  // namespace fa

@@ -126,6 +126,16 @@ __device__ inline void keep_scalar_here(T &...x)
     (keep_scalar_one(x), ...);
 }
 
+// The lane index, formed where this is called: a volatile statement is
+// neither hoisted out of a loop nor merged with another, so values derived
+// from it take no register across the loop.
+__device__ inline int lane_here()
+{
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 // fp32 -> element (round to nearest even) of four values: two packed
 // hardware converts.
 template <bool F16>

@@ -39,7 +39,7 @@ KERNEL_SOURCES = ["attention_backward_fa2_amd/csrc/fa_main.hip",
                   "attention_backward_fa2_amd/csrc/fa_internal.h"]
 TRAFFIC_SUMMARY = "profiles/hbm_traffic_main_kernel_gqa_b2_h32_hk8_s4096_d128_causal.json"
 TRACE_SUMMARY = "profiles/kernel_trace_gqa_b2_h32_hk8_s4096_d128_causal.md"
-MAIN_KERNEL = "fa_bwd_main_kernel<128, false, false>"
+MAIN_KERNEL = "fa_bwd_main_kernel<128, false, false, false>"
 
 
 def kernel_source_hash():
@@ -292,7 +292,7 @@ def cpu_baseline(wl, units):
 
 
 FWD_METRIC = "fwd TFLOP/s (O, LSE) bf16 and % of MFMA peak, S=4096 D=128 causal GQA"
-FWD_KERNEL = "fa_fwd_kernel<128, false>"
+FWD_KERNEL = "fa_fwd_kernel<128, false, false>"
 
 
 def fwd_flops(B, H, Sq, Sk, D, causal):
@@ -519,7 +519,7 @@ def main():
                      "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None if args.dq_accumulate else committed_traffic(),
                      "kernel": MAIN_KERNEL if not args.dq_accumulate else
-                     "fa_bwd_main_kernel<128, true, false>",
+                     "fa_bwd_main_kernel<128, true, false, false>",
                      "algorithmic_flops_per_launch": main_flops},
         "wall_s": round(wall, 3),
         "ordered_wait_gave_up": bool(int(flags[0]) != 0),

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define FA_BWD_ABI_VERSION 3
+#define FA_BWD_ABI_VERSION 4
 
 typedef enum {
     FA_OK = 0,
@@ -115,6 +115,17 @@ typedef enum {
  *     h / (num_heads / num_heads_k) (GQA/MQA page, KV head mapping).
  *   - causal = 1 masks key j for query i unless j <= i + len_k - len_q
  *     (bottom-right aligned, GQA/MQA page, causal block bound).
+ *   - Local (sliding-window) attention, mha_bwd's window_size_left / _right
+ *     on the backward call-trace page, with local_window = 1 (0 leaves the
+ *     sizes unread, so a zero-filled struct has no window): key j is
+ *     visible to query i only if
+ *     i + len_k - len_q - window_size_left <= j (when window_size_left >= 0)
+ *     and j <= i + len_k - len_q + window_size_right (when
+ *     window_size_right >= 0); negative sizes leave that side unbounded.
+ *     causal = 1 is the right size 0 (a positive right size with causal = 1
+ *     is FA_ERR_INVALID_ARG).  Sizes above 2^29 act as 2^29 (which reaches
+ *     every key: seqlen_q and seqlen_k above 2^29 are FA_ERR_UNSUPPORTED).  Rows that see no key behave as under the
+ *     causal rule (dq = 0, and they add nothing to dk / dv).
  *   - lse is the NATURAL-log log-sum-exp of the scaled scores of each row,
  *     -inf for a row with no visible key (its dQ is then 0).
  *   - dq, dk, dv are fully overwritten over their valid rows and the first
@@ -154,6 +165,9 @@ typedef struct fa_bwd_args {
 
     float softmax_scale;           /* the caller passes it (usually 1/sqrt(head_dim)) */
     int32_t causal;                /* 0 or 1 */
+    int32_t local_window;          /* 0: no window (sizes ignored); 1: the sizes apply */
+    int32_t window_size_left;      /* local window (see Semantics); < 0: unbounded */
+    int32_t window_size_right;     /* < 0: unbounded; with causal = 1 only < 0 or 0 */
     int32_t deterministic;         /* 0 or 1 (see Reproducibility) */
     int32_t dq_accumulate;         /* 0: separate dQ pass (default); 1: fp32 accumulator */
 

@@ -25,7 +25,8 @@ extern "C" {
 
 /*
  * Arguments of one forward call.  Shapes, layouts, strides, GQA head mapping,
- * the causal rule, packed variable-length inputs and the LSE layout are
+ * the causal rule and the local window, packed variable-length inputs and
+ * the LSE layout are
  * exactly those of fa_bwd_args (fa_bwd.h), so the outputs of a forward call
  * are valid `out` / `lse` inputs of a backward call on the same q, k, v:
  *   dense : q, out (batch, seqlen_q, num_heads, head_dim); k, v (batch,
@@ -67,6 +68,9 @@ typedef struct fa_fwd_args {
 
     float softmax_scale;
     int32_t causal;                /* 0 or 1 */
+    int32_t local_window;          /* local window as in fa_bwd_args */
+    int32_t window_size_left;
+    int32_t window_size_right;
 } fa_fwd_args;
 
 /* FA_OK if fa_fwd would accept `args`; otherwise the error it would return. */

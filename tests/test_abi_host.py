@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(fa.EXPORTED)
-    assert lib.fa_bwd_abi_version() == 3
+    assert lib.fa_bwd_abi_version() == 4
 
 
 @pytest.mark.parametrize("header,struct,mirror", [
@@ -135,6 +135,15 @@ def test_step_entry_points_check_the_dq_mode_before_launching():
 def test_valid_args_pass_validation():
     assert fa.validate(_with_ws(_args())) == fa.FA_OK
     assert fa.validate(_with_ws(_args(dtype=fa.FA_DTYPE_F16))) == fa.FA_OK
+    # local windows: causal with a left size (right 0 or unbounded), and
+    # two-sided windows without causal, huge sizes included
+    for causal, left, right in [(1, 16, 0), (1, 3, -1), (0, -1, 8), (0, 5, 7), (0, 1 << 30, 2**31 - 1)]:
+        a = _with_ws(_args(causal=causal, local_window=1, window_size_left=left,
+                           window_size_right=right))
+        assert fa.validate(a) == fa.FA_OK
+    # without local_window the sizes are not read (a zero-filled struct has
+    # no window, and causal with a positive right size is no error then)
+    assert fa.validate(_with_ws(_args(causal=1, window_size_right=5))) == fa.FA_OK
 
 
 @pytest.mark.parametrize("over,status", [
@@ -148,6 +157,9 @@ def test_valid_args_pass_validation():
     ({"batch": -1}, fa.FA_ERR_INVALID_ARG),
     ({"head_dim": 0}, fa.FA_ERR_INVALID_ARG),
     ({"causal": 2}, fa.FA_ERR_INVALID_ARG),
+    ({"causal": 1, "local_window": 1, "window_size_right": 4}, fa.FA_ERR_INVALID_ARG),
+    ({"local_window": 2}, fa.FA_ERR_INVALID_ARG),
+    ({"seqlen_k": (1 << 29) + 1}, fa.FA_ERR_UNSUPPORTED),
     ({"softmax_scale": float("nan")}, fa.FA_ERR_INVALID_ARG),
     ({"cu_seqlens_q": BASE}, fa.FA_ERR_INVALID_ARG),      # only one cu_seqlens
     ({"dtype": 2}, fa.FA_ERR_UNSUPPORTED),
@@ -219,6 +231,10 @@ def _fwd_args(**over):
 def test_forward_valid_args_pass_validation():
     assert fa.validate_fwd(_fwd_args()) == fa.FA_OK
     assert fa.validate_fwd(_fwd_args(dtype=fa.FA_DTYPE_F16)) == fa.FA_OK
+    assert fa.validate_fwd(_fwd_args(local_window=1, window_size_left=32,
+                                     window_size_right=0)) == fa.FA_OK
+    assert fa.validate_fwd(_fwd_args(causal=0, local_window=1, window_size_left=-1,
+                                     window_size_right=9)) == fa.FA_OK
     assert fa.validate_fwd(_fwd_args(cu_seqlens_q=BASE, cu_seqlens_k=BASE + 256, total_q=1000,
                                      total_k=1200, batch=5, seqlen_q=300)) == fa.FA_OK
 
@@ -232,6 +248,9 @@ def test_forward_valid_args_pass_validation():
     ({"lse": BASE + 2}, fa.FA_ERR_INVALID_ARG),
     ({"o_stride": (256 * 8 * 128, 8 * 128 + 4, 128)}, fa.FA_ERR_INVALID_ARG),
     ({"causal": 2}, fa.FA_ERR_INVALID_ARG),
+    ({"local_window": 1, "window_size_right": 1}, fa.FA_ERR_INVALID_ARG),   # causal = 1
+    ({"local_window": -1}, fa.FA_ERR_INVALID_ARG),
+    ({"seqlen_q": (1 << 29) + 1}, fa.FA_ERR_UNSUPPORTED),
     ({"softmax_scale": float("inf")}, fa.FA_ERR_INVALID_ARG),
     ({"cu_seqlens_k": BASE}, fa.FA_ERR_INVALID_ARG),
     ({"dtype": 2}, fa.FA_ERR_UNSUPPORTED),

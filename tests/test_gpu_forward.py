@@ -25,7 +25,8 @@ def _flush(msg):
 def _reference(inp):
     pk = lambda t: PT.to64(inp.packed(t))
     cu_q, cu_k = PT.cu_np(inp.lens_q), PT.cu_np(inp.lens_k)
-    return O.forward(pk(inp.q), pk(inp.k), pk(inp.v), cu_q, cu_k, inp.wl.scale, inp.wl.causal)
+    return O.forward(pk(inp.q), pk(inp.k), pk(inp.v), cu_q, cu_k, inp.wl.scale, inp.wl.causal,
+                     window=inp.wl.window_sizes)
 
 
 def _check(inp, out, lse, what):

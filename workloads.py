@@ -13,7 +13,7 @@ workloads are (total_tokens, heads, dim) with int32 ``cu_seqlens`` prefix sums
 and equal query/key lengths per sequence.
 """
 from dataclasses import dataclass, field
-from typing import List, Optional
+from typing import List, Optional, Tuple
 
 import torch
 
@@ -34,6 +34,12 @@ class Workload:
     len_lo: int = 0            # packed: lengths uniform in [len_lo, len_hi]
     len_hi: int = 0
     seed: int = SEED_BASE
+    # local window (left, right), negative = unbounded; None: no window
+    window: Optional[Tuple[int, int]] = None
+
+    @property
+    def window_sizes(self) -> Tuple[int, int]:
+        return (-1, -1) if self.window is None else tuple(self.window)
 
     @property
     def scale(self) -> float:
@@ -119,18 +125,19 @@ def make_inputs(wl: Workload, lengths: Optional[List[int]] = None,
 
 
 def custom(name: str, batch: int, heads: int, heads_k: int, seqlen_q: int,
-           seqlen_k: int, head_dim: int, causal: bool, seed: int) -> Workload:
+           seqlen_k: int, head_dim: int, causal: bool, seed: int,
+           window: Optional[Tuple[int, int]] = None) -> Workload:
     """A dense workload of any shape (used for ragged / edge-case tests)."""
     return Workload(name, batch, heads, heads_k, seqlen_q, seqlen_k, head_dim,
-                    causal, seed=seed)
+                    causal, seed=seed, window=window)
 
 
 def custom_varlen(name: str, lens_q: List[int], lens_k: List[int], heads: int,
                   heads_k: int, head_dim: int, causal: bool, seed: int,
-                  dtype=torch.bfloat16) -> Inputs:
+                  dtype=torch.bfloat16, window: Optional[Tuple[int, int]] = None) -> Inputs:
     """Packed inputs with explicit (possibly unequal or zero) q/k lengths."""
     wl = Workload(name, len(lens_q), heads, heads_k, 0, 0, head_dim, causal,
-                  varlen=True, seed=seed)
+                  varlen=True, seed=seed, window=window)
     gen = torch.Generator(device="cpu")
     gen.manual_seed(seed)
     Tq, Tk = sum(lens_q), sum(lens_k)
