@@ -227,12 +227,28 @@ def summarize_profile(prof_dir, out_dir):
     print("wrote profile summaries to", out_dir)
 
 
-def conv_flops(B, H, Sq, Sk, D, causal):
-    f = 2.5 * 4.0 * B * H * Sq * Sk * D
-    return f * 0.5 if causal else f
+def visible_pairs(Sq, Sk, causal, window=None):
+    """(query, key) pairs of one (batch, head) that the products cover: the
+    usual convention Sq*Sk, halved for causal, without a local window; the
+    exact count of visible pairs with one (row i sees keys i + Sk - Sq - left
+    .. i + Sk - Sq + right, clipped to the sequence)."""
+    if window is None:
+        return 0.5 * Sq * Sk if causal else float(Sq * Sk)
+    import numpy as np
+    left, right = window
+    right = 0 if causal else right
+    i = np.arange(Sq, dtype=np.int64) + (Sk - Sq)
+    lo = np.maximum(0, i - left) if left >= 0 else np.zeros_like(i)
+    hi = np.minimum(Sk - 1, i + right) if right >= 0 else np.full_like(i, Sk - 1)
+    return float(np.maximum(0, hi - lo + 1).sum())
 
 
-def forward_inputs_torch(q, k, v, scale, causal):
+def conv_flops(B, H, Sq, Sk, D, causal, window=None):
+    """Five products of 2*D FLOPs per visible (query, key) pair each."""
+    return 2.5 * 4.0 * B * H * D * visible_pairs(Sq, Sk, causal, window)
+
+
+def forward_inputs_torch(q, k, v, scale, causal, window=None):
     """O (bf16) and natural-log LSE (fp32, (B,H,Sq)) by a plain fp32 torch
     forward, one (batch, head) at a time.  Dense bshd inputs on the GPU."""
     import torch
@@ -241,17 +257,24 @@ def forward_inputs_torch(q, k, v, scale, causal):
     G = H // Hk
     out = torch.empty_like(q)
     lse = torch.empty(B, H, Sq, dtype=torch.float32, device=q.device)
-    if causal:
-        i = torch.arange(Sq, device=q.device)[:, None]
+    masked = None
+    if causal or window is not None:
+        i = torch.arange(Sq, device=q.device)[:, None] + (Sk - Sq)
         j = torch.arange(Sk, device=q.device)[None, :]
-        masked = j > i + (Sk - Sq)
+        left, right = window if window is not None else (-1, -1)
+        right = 0 if causal else right
+        masked = torch.zeros(Sq, Sk, dtype=torch.bool, device=q.device)
+        if right >= 0:
+            masked |= j > i + right
+        if left >= 0:
+            masked |= j < i - left
     for b in range(B):
         for h in range(H):
             qh = q[b, :, h, :].float().contiguous()
             kt = k[b, :, h // G, :].float().t().contiguous()
             vh = v[b, :, h // G, :].float().contiguous()
             s = torch.matmul(qh, kt) * scale
-            if causal:
+            if masked is not None:
                 s.masked_fill_(masked, float("-inf"))
             l = torch.logsumexp(s, dim=-1)
             p = torch.exp(s - l[:, None])
@@ -281,9 +304,10 @@ def cpu_baseline(wl, units):
         v = f64(inp.v[b][:, [g]])
         do = f64(inp.dout[b][:, hs])
         t0 = time.perf_counter()
-        O.backward(q, k, v, do, [0, wl.seqlen_q], [0, wl.seqlen_k], wl.scale, wl.causal)
+        O.backward(q, k, v, do, [0, wl.seqlen_q], [0, wl.seqlen_k], wl.scale, wl.causal,
+                   window=wl.window_sizes)
         t_total += time.perf_counter() - t0
-        flops += conv_flops(1, G, wl.seqlen_q, wl.seqlen_k, wl.head_dim, wl.causal)
+        flops += conv_flops(1, G, wl.seqlen_q, wl.seqlen_k, wl.head_dim, wl.causal, wl.window)
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(),
             "kind": "oracle",
             "sample": "%d of %d (batch, KV-head group) units of the workload, fp64 "
@@ -291,15 +315,24 @@ def cpu_baseline(wl, units):
                       % (len(units), wl.batch * wl.heads_k, t_total)}
 
 
+def window_suffix(wl):
+    return "" if wl.window is None else ", local window (%d, %d)" % tuple(wl.window)
+
+
+def main_kernel_name(fused, wl):
+    local = wl.window is not None and wl.window[0] >= 0
+    return "fa_bwd_main_kernel<128, %s, false, %s>" % (str(bool(fused)).lower(),
+                                                       str(local).lower())
+
+
 FWD_METRIC = "fwd TFLOP/s (O, LSE) bf16 and % of MFMA peak, S=4096 D=128 causal GQA"
 FWD_KERNEL = "fa_fwd_kernel<128, false, false>"
 
 
-def fwd_flops(B, H, Sq, Sk, D, causal):
-    """The forward's two products (S = Q K^T, O = P V): 4*B*H*Sq*Sk*D, halved
-    for causal."""
-    f = 4.0 * B * H * Sq * Sk * D
-    return f * 0.5 if causal else f
+def fwd_flops(B, H, Sq, Sk, D, causal, window=None):
+    """The forward's two products (S = Q K^T, O = P V): 2*D FLOPs each per
+    visible (query, key) pair (Sq*Sk pairs, halved for causal)."""
+    return 4.0 * B * H * D * visible_pairs(Sq, Sk, causal, window)
 
 
 def cpu_baseline_fwd(wl, units):
@@ -317,9 +350,10 @@ def cpu_baseline_fwd(wl, units):
         k = f64(inp.k[b][:, [h // G]])
         v = f64(inp.v[b][:, [h // G]])
         t0 = time.perf_counter()
-        O.forward(q, k, v, [0, wl.seqlen_q], [0, wl.seqlen_k], wl.scale, wl.causal)
+        O.forward(q, k, v, [0, wl.seqlen_q], [0, wl.seqlen_k], wl.scale, wl.causal,
+                  window=wl.window_sizes)
         t_total += time.perf_counter() - t0
-        flops += fwd_flops(1, 1, wl.seqlen_q, wl.seqlen_k, wl.head_dim, wl.causal)
+        flops += fwd_flops(1, 1, wl.seqlen_q, wl.seqlen_k, wl.head_dim, wl.causal, wl.window)
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(),
             "kind": "oracle",
             "sample": "%d of %d (batch, head) units of the workload, fp64 forward, %.1f s"
@@ -334,7 +368,7 @@ def bench_forward(args, wl, dev):
     q, k, v = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v))
     out = torch.empty_like(q)
     lse = torch.empty(wl.batch, wl.heads, wl.seqlen_q, dtype=torch.float32, device=dev)
-    a = fa.make_fwd_args(q, k, v, out, lse, wl.scale, wl.causal)
+    a = fa.make_fwd_args(q, k, v, out, lse, wl.scale, wl.causal, window=wl.window)
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         fa.run_fwd(a, stream)
@@ -350,22 +384,24 @@ def bench_forward(args, wl, dev):
     wall = time.perf_counter() - t0
     ms = evs[0].elapsed_time(evs[-1]) / K
     B, H, Hk, Sq, Sk, D = wl.batch, wl.heads, wl.heads_k, wl.seqlen_q, wl.seqlen_k, wl.head_dim
-    flops = fwd_flops(B, H, Sq, Sk, D, wl.causal)
+    flops = fwd_flops(B, H, Sq, Sk, D, wl.causal, wl.window)
     tf = flops / (ms * 1e-3) / 1e12
     rec = {
-        "metric": FWD_METRIC, "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": FWD_METRIC + window_suffix(wl), "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "heads": H, "heads_k": Hk,
                    "seqlen_q": Sq, "seqlen_k": Sk, "head_dim": D, "causal": wl.causal,
-                   "pass": "forward"},
+                   "window": list(wl.window) if wl.window else None, "pass": "forward"},
         "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
         "flops_per_step": flops,
         "kernel_ms": {"fwd": round(ms, 4)},
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": FWD_KERNEL,
+                     "traffic": None,
+                     "kernel": FWD_KERNEL if wl.window is None or wl.window[0] < 0 else
+                     FWD_KERNEL.replace(", false>", ", true>"),
                      "algorithmic_flops_per_launch": flops},
         "wall_s": round(wall, 3),
     }
@@ -392,6 +428,8 @@ def main():
     ap.add_argument("--forward", action="store_true",
                     help="time the forward kernel (O, LSE) instead of the backward")
     ap.add_argument("--cpu-units", type=int, default=16)
+    ap.add_argument("--window", type=int, nargs=2, metavar=("LEFT", "RIGHT"),
+                    help="local window (negative = unbounded): times the workload with it")
     ap.add_argument("--summarize-profile", metavar="PROF_DIR",
                     help="write the profiles/ summaries from rocprofv3 outputs in PROF_DIR "
                          "(trace/, FETCH_SIZE/, WRITE_SIZE/, copy_FETCH_SIZE/, copy_WRITE_SIZE/)")
@@ -426,6 +464,10 @@ def main():
 
     fa.load_library()
     wl = W.WORKLOADS[args.config]
+    if args.window is not None:
+        import dataclasses
+        wl = dataclasses.replace(wl, name="%s_window%d_%d" % (wl.name, *args.window),
+                                 window=tuple(args.window))
     if wl.varlen:
         print("bench.py times dense workloads only", file=sys.stderr)
         sys.exit(2)
@@ -436,10 +478,11 @@ def main():
         return
     inp = W.make_inputs(wl)
     q, k, v, do = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v, inp.dout))
-    o, lse = forward_inputs_torch(q, k, v, wl.scale, wl.causal)
+    o, lse = forward_inputs_torch(q, k, v, wl.scale, wl.causal, wl.window)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     a = fa.make_args(do, q, k, v, o, lse, dq, dk, dv, wl.scale, wl.causal,
-                     deterministic=args.deterministic, dq_accumulate=args.dq_accumulate)
+                     deterministic=args.deterministic, dq_accumulate=args.dq_accumulate,
+                     window=wl.window)
     # the steps of one backward, in the order fa_bwd enqueues them
     seq = ["preprocess", "main", "dq_convert"] if args.dq_accumulate else ["dq", "main"]
     ws = fa.alloc_workspace(a, dev)
@@ -473,7 +516,7 @@ def main():
     ms_per_step = gpu_ms / K
 
     B, H, Hk, Sq, Sk, D = wl.batch, wl.heads, wl.heads_k, wl.seqlen_q, wl.seqlen_k, wl.head_dim
-    flops = conv_flops(B, H, Sq, Sk, D, wl.causal)
+    flops = conv_flops(B, H, Sq, Sk, D, wl.causal, wl.window)
     value = flops / (ms_per_step * 1e-3) / 1e12
     # Algorithmic work per launch.  MFMA-bound kernels: the key-tile pass
     # does 4 of the 5 products (S, dP, dV, dK; + dQ in accumulate mode), the
@@ -490,7 +533,7 @@ def main():
     flags = ws[off_flags:off_flags + 16].cpu().view(torch.int32)
 
     rec = {
-        "metric": METRIC,
+        "metric": METRIC + window_suffix(wl),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -504,6 +547,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "heads": H, "heads_k": Hk,
                    "seqlen_q": Sq, "seqlen_k": Sk, "head_dim": D, "causal": wl.causal,
+                   "window": list(wl.window) if wl.window else None,
                    "dq_mode": ("ordered" if args.deterministic else "atomic")
                    if args.dq_accumulate else "separate"},
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
@@ -517,9 +561,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(main_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None if args.dq_accumulate else committed_traffic(),
-                     "kernel": MAIN_KERNEL if not args.dq_accumulate else
-                     "fa_bwd_main_kernel<128, true, false, false>",
+                     "traffic": None if args.dq_accumulate or wl.window else committed_traffic(),
+                     "kernel": main_kernel_name(args.dq_accumulate, wl),
                      "algorithmic_flops_per_launch": main_flops},
         "wall_s": round(wall, 3),
         "ordered_wait_gave_up": bool(int(flags[0]) != 0),
