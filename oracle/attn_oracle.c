@@ -8,6 +8,7 @@
  * What it computes (per sequence s and query head h, KV head g = h / (H/Hk)):
  *
  *   S_ij  = scale * sum_d Q_id K_jd                       (scores)
+ *   S_ij <- c * tanh(S_ij / c)                 (only with softcap c > 0)
  *   visible(i,j) = (!causal || j <= i + Lk - Lq)          (bottom-right causal)
  *                  && (wr < 0 || j <= i + Lk - Lq + wr)   (local window, right)
  *                  && (wl < 0 || j >= i + Lk - Lq - wl)   (local window, left)
@@ -18,6 +19,7 @@
  *   backward of f = sum(dO * O):
  *   dP_ij = sum_d dO_id V_jd
  *   dS_i  = J_i dP_i,   J_i = diag(P_i) - P_i P_i^T       (softmax Jacobian)
+ *   dS_ij <- dS_ij * (1 - (S_ij / c)^2)       (softcap: d/dx c tanh(x/c))
  *   dQ_i  = scale * sum_j dS_ij K_j
  *   dK_j  = scale * sum_{h in group g} sum_i dS^(h)_ij Q^(h)_i
  *   dV_j  =         sum_{h in group g} sum_i P^(h)_ij dO^(h)_i
@@ -37,7 +39,9 @@
  *     band around the bottom-right diagonal (query i sees keys
  *     i + Lk - Lq - wl .. i + Lk - Lq + wr; a negative size leaves that
  *     side unbounded), the plainest reading of names the pages do not
- *     define further.
+ *     define further; its softcap argument (a kernel variant switched on by
+ *     softcap > 0), read as the usual logit soft-capping c * tanh(x / c) of
+ *     the scaled score x, with the gradient through it by the chain rule.
  *
  * Two backward evaluations are provided and tested against each other:
  *   oracle_backward_explicit -- materialises P, dP and each row's Jacobian
@@ -90,10 +94,11 @@ static double dot(const double *a, const double *b, int D)
     return acc;
 }
 
-/* One score S_ij, or -inf when the pair is not visible. */
+/* One score S_ij (soft-capped when softcap > 0), or -inf when the pair is
+ * not visible. */
 static double score(const double *qi, const double *kj, int D, double scale,
                     int i, int j, int Lq, int Lk, int causal, int wl, int wr,
-                    const double *mask_row)
+                    double softcap, const double *mask_row)
 {
     const int64_t diag = (int64_t)i + Lk - Lq;   /* bottom-right diagonal key of row i */
     if (causal && (int64_t)j > diag)
@@ -105,9 +110,23 @@ static double score(const double *qi, const double *kj, int D, double scale,
     if (mask_row && mask_row[j] == -INFINITY)
         return -INFINITY;
     double s = scale * dot(qi, kj, D);
+    if (softcap > 0.0)
+        s = softcap * tanh(s / softcap);
     if (mask_row)
         s += mask_row[j];
     return s;
+}
+
+/* Derivative of the capped score with respect to the uncapped one, from the
+ * capped value s = c tanh(x / c): 1 - tanh^2 = 1 - (s / c)^2 (1 without a
+ * cap).  The explicit masks add only 0, so s is the capped score itself. */
+static double cap_grad(double s, double softcap)
+{
+    if (softcap > 0.0) {
+        const double t = s / softcap;
+        return 1.0 - t * t;
+    }
+    return 1.0;
 }
 
 /* Natural-log log-sum-exp of one row of scores (-inf if all are -inf). */
@@ -152,7 +171,7 @@ static int max_len(int nseq, const int64_t *cu)
 /* Forward: O and LSE for every (row, head). */
 int oracle_forward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
                    int H, int Hk, int D, double scale, int causal, int wl, int wr,
-                   const double *mask,
+                   double softcap, const double *mask,
                    const double *q, const double *k, const double *v,
                    double *out, double *lse)
 {
@@ -182,7 +201,7 @@ int oracle_forward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
                 const double *mrow = mask ? mask + (int64_t)i * Lk : NULL;
                 for (int j = 0; j < Lk; j++)
                     s[j] = score(qi, k + ((k0 + j) * Hk + g) * D, D, scale,
-                                 i, j, Lq, Lk, causal, wl, wr, mrow);
+                                 i, j, Lq, Lk, causal, wl, wr, softcap, mrow);
                 const double L = row_lse(s, Lk);
                 double *o = out + ((q0 + i) * H + h) * D;
                 for (int d = 0; d < D; d++)
@@ -247,7 +266,7 @@ static void group_sum(int64_t total_k, int H, int Hk, int D,
  */
 int oracle_backward_explicit(int nseq, const int64_t *cu_q, const int64_t *cu_k,
                              int H, int Hk, int D, double scale, int causal, int wl, int wr,
-                             const double *mask,
+                             double softcap, const double *mask,
                              const double *q, const double *k, const double *v,
                              const double *dout,
                              double *dq, double *dk, double *dv,
@@ -296,7 +315,7 @@ int oracle_backward_explicit(int nseq, const int64_t *cu_q, const int64_t *cu_k,
             const double *mrow = mask ? mask + (int64_t)i * Lk : NULL;
             for (int j = 0; j < Lk; j++)
                 S[(size_t)i * Lk + j] = score(QP(i), KP(j), D, scale, i, j, Lq, Lk,
-                                              causal, wl, wr, mrow);
+                                              causal, wl, wr, softcap, mrow);
             const double L = row_lse(S + (size_t)i * Lk, Lk);
             for (int j = 0; j < Lk; j++) {
                 const double sij = S[(size_t)i * Lk + j];
@@ -308,7 +327,8 @@ int oracle_backward_explicit(int nseq, const int64_t *cu_q, const int64_t *cu_k,
             for (int j = 0; j < Lk; j++) {
                 dP[(size_t)i * Lk + j] = dot(DOP(i), VP(j), D);
             }
-        /* dS_i = J_i dP_i with J_i = diag(P_i) - P_i P_i^T */
+        /* dS_i = J_i dP_i with J_i = diag(P_i) - P_i P_i^T, then through the
+         * soft cap (invisible pairs have P = 0 and so dS = 0 already) */
         for (int i = 0; i < Lq; i++) {
             const double *Pi = P + (size_t)i * Lk;
             for (int j = 0; j < Lk; j++)
@@ -318,7 +338,8 @@ int oracle_backward_explicit(int nseq, const int64_t *cu_q, const int64_t *cu_k,
                 double acc = 0.0;
                 for (int c = 0; c < Lk; c++)
                     acc += J[(size_t)j * Lk + c] * dP[(size_t)i * Lk + c];
-                dS[(size_t)i * Lk + j] = acc;
+                const double sij = S[(size_t)i * Lk + j];
+                dS[(size_t)i * Lk + j] = sij == -INFINITY ? acc : acc * cap_grad(sij, softcap);
             }
             if (dj_out) {
                 double acc = 0.0;
@@ -381,7 +402,7 @@ int oracle_backward_explicit(int nseq, const int64_t *cu_q, const int64_t *cu_k,
  */
 int oracle_backward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
                     int H, int Hk, int D, double scale, int causal, int wl, int wr,
-                    const double *mask,
+                    double softcap, const double *mask,
                     const double *q, const double *k, const double *v,
                     const double *dout,
                     double *dq, double *dk, double *dv,
@@ -410,13 +431,14 @@ int oracle_backward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
     {
         double *s = (double *)malloc(sizeof(double) * (size_t)(Lk_max + 1));
         double *dp = (double *)malloc(sizeof(double) * (size_t)(Lk_max + 1));
-        if (!s || !dp) {
+        double *cg = (double *)malloc(sizeof(double) * (size_t)(Lk_max + 1));
+        if (!s || !dp || !cg) {
 #pragma omp atomic write
             failed = 1;
         }
 #pragma omp for schedule(dynamic, 16)
         for (int64_t t = 0; t < total_q * H; t++) {
-            if (!s || !dp)
+            if (!s || !dp || !cg)
                 continue;
             const int64_t r = t / H;
             const int h = (int)(t % H), g = h / G, b = seq_of_row[r];
@@ -428,7 +450,7 @@ int oracle_backward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
             const double *mrow = mask ? mask + (int64_t)i * Lk : NULL;
             for (int j = 0; j < Lk; j++)
                 s[j] = score(qi, k + ((k0 + j) * Hk + g) * D, D, scale, i, j, Lq, Lk,
-                             causal, wl, wr, mrow);
+                             causal, wl, wr, softcap, mrow);
             const double L = row_lse(s, Lk);
             LSE[r * H + h] = L;
             double *o = dq + (r * H + h) * D;
@@ -440,8 +462,10 @@ int oracle_backward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
                     if (s[j] == -INFINITY) {
                         s[j] = 0.0; /* P_ij = 0 */
                         dp[j] = 0.0;
+                        cg[j] = 0.0;
                         continue;
                     }
+                    cg[j] = cap_grad(s[j], softcap);
                     s[j] = exp(s[j] - L); /* s now holds P_ij */
                     const double *vj = v + ((k0 + j) * Hk + g) * D;
                     dp[j] = dot(doi, vj, D);
@@ -451,7 +475,7 @@ int oracle_backward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
                 for (int j = 0; j < Lk; j++) {
                     if (s[j] == 0.0)
                         continue;
-                    const double dsij = s[j] * (dp[j] - dj);
+                    const double dsij = s[j] * (dp[j] - dj) * cg[j];
                     const double *kj = k + ((k0 + j) * Hk + g) * D;
                     for (int d = 0; d < D; d++)
                         o[d] += dsij * kj[d];
@@ -463,6 +487,7 @@ int oracle_backward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
         }
         free(s);
         free(dp);
+        free(cg);
     }
 
     /* ---- key pass: dK, dV ---- */
@@ -512,13 +537,14 @@ int oracle_backward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
                             continue;
                         const double *qi = q + (r * H + h) * D;
                         const double *mrow = mask ? mask + (int64_t)i * Lk : NULL;
-                        const double sij = score(qi, kj, D, scale, i, j, Lq, Lk, causal, wl, wr, mrow);
+                        const double sij = score(qi, kj, D, scale, i, j, Lq, Lk, causal, wl, wr,
+                                                 softcap, mrow);
                         if (sij == -INFINITY)
                             continue;
                         const double p = exp(sij - L);
                         const double *doi = dout + (r * H + h) * D;
                         const double dpij = dot(doi, vj, D);
-                        const double dsij = p * (dpij - DJ[r * H + h]);
+                        const double dsij = p * (dpij - DJ[r * H + h]) * cap_grad(sij, softcap);
                         for (int d = 0; d < D; d++) {
                             acck[d] += dsij * qi[d];
                             accv[d] += p * doi[d];

@@ -27,7 +27,8 @@ def _lib():
             _build.build()
         lib = ctypes.CDLL(_build.LIB)
         common = [ctypes.c_int, _i64p, _i64p, ctypes.c_int, ctypes.c_int,
-                  ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp]
+                  ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_double, _dp]
         lib.oracle_forward.argtypes = common + [_dp, _dp, _dp, _dp, _dp]
         lib.oracle_backward.argtypes = common + [_dp] * 4 + [_dp] * 3 + [_dp, _dp]
         lib.oracle_backward_explicit.argtypes = common + [_dp] * 4 + [_dp] * 3 + [_dp, _dp]
@@ -72,10 +73,11 @@ def num_threads() -> int:
     return int(_lib().oracle_num_threads())
 
 
-def forward(q, k, v, cu_q, cu_k, scale, causal, mask=None, window=(-1, -1)):
+def forward(q, k, v, cu_q, cu_k, scale, causal, mask=None, window=(-1, -1), softcap=0.0):
     """Returns (out [total_q,H,D], lse [total_q,H]) in fp64.  window =
     (left, right): query i sees keys i + Lk - Lq - left .. i + Lk - Lq + right
-    (a negative size leaves that side unbounded)."""
+    (a negative size leaves that side unbounded).  softcap c > 0: every
+    scaled score x becomes c * tanh(x / c) (LSE of the capped scores)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     cu_q, cu_k = _cu(cu_q), _cu(cu_k)
     nseq, H, Hk, D = _shapes(q, k, cu_q, cu_k)
@@ -84,7 +86,7 @@ def forward(q, k, v, cu_q, cu_k, scale, causal, mask=None, window=(-1, -1)):
     lse = np.empty(q.shape[:2], np.float64)
     rc = _lib().oracle_forward(nseq, cu_q.ctypes.data_as(_i64p), cu_k.ctypes.data_as(_i64p),
                                H, Hk, D, float(scale), int(bool(causal)), int(window[0]),
-                               int(window[1]), _ptr(mask),
+                               int(window[1]), float(softcap), _ptr(mask),
                                _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse))
     if rc:
         raise RuntimeError("oracle_forward failed (%d)" % rc)
@@ -92,7 +94,7 @@ def forward(q, k, v, cu_q, cu_k, scale, causal, mask=None, window=(-1, -1)):
 
 
 def backward(q, k, v, dout, cu_q, cu_k, scale, causal, mask=None,
-             mode="contracted", want_ds=False, window=(-1, -1)):
+             mode="contracted", want_ds=False, window=(-1, -1), softcap=0.0):
     """Exact attention gradient in fp64.
 
     mode="contracted": any size; mode="explicit": materialised softmax
@@ -113,7 +115,8 @@ def backward(q, k, v, dout, cu_q, cu_k, scale, causal, mask=None,
     res = {"dq": dq, "dk": dk, "dv": dv, "dj": dj}
     lib = _lib()
     common = (nseq, cu_q.ctypes.data_as(_i64p), cu_k.ctypes.data_as(_i64p), H, Hk, D,
-              float(scale), int(bool(causal)), int(window[0]), int(window[1]), _ptr(mask),
+              float(scale), int(bool(causal)), int(window[0]), int(window[1]), float(softcap),
+              _ptr(mask),
               _ptr(q), _ptr(k), _ptr(v),
               _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv))
     if mode == "contracted":

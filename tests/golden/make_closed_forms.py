@@ -50,9 +50,33 @@ CAUSAL_BOTTOM_RIGHT_2X3 = {
     "dk": [[[-0.75]], [[0.75]], [[0.0]]], "dv": [[[1.25]], [[1.75]], [[1.0]]],
 }
 
+SOFTCAP_ONE_QUERY_TWO_KEYS = {
+    "citation": "Closed form with soft-capped scores: the softcap argument of mha_bwd on "
+                "the backward call-trace page, read as c * tanh(x / c) of the scaled score "
+                "x, and the method equations of the sm90 backward page, mma_one_m_block; "
+                "the gradient passes the cap by the chain rule.",
+    "derivation": [
+        "c = 2 ln 3, scale = 1/2, q = 2: x = scale*q*k = k = [0, (ln 3)^2]",
+        "x / c = [0, (ln 3)/2] and tanh((ln 3)/2) = (3-1)/(3+1) = 1/2, so the capped "
+        "scores are c*[0, 1/2] = [0, ln 3]",
+        "P = [1/4, 3/4]; O = 3/4*4 = 3; LSE = ln 4",
+        "dS with respect to the capped scores (as without a cap): [-3/4, 3/4]",
+        "cap derivative 1 - tanh^2 = [1, 3/4]; dS with respect to x: [-3/4, 9/16]",
+        "dQ = scale*sum_j dS_j k_j = (1/2)(9/16)(ln 3)^2 = (9/32)(ln 3)^2; "
+        "dK_j = scale*dS_j*q = [-3/4, 9/16]; dV_j = P_j*dO = [1/4, 3/4]"],
+    "shape": {"H": 1, "Hk": 1, "Sq": 1, "Sk": 2, "D": 1}, "scale": 0.5, "causal": False,
+    "softcap": 2.0 * ln3,
+    "q": [[[2.0]]], "k": [[[0.0]], [[ln3 * ln3]]], "v": [[[0.0]], [[4.0]]],
+    "dout": [[[1.0]]], "out": [[[3.0]]], "lse": [[math.log(4.0)]],
+    "dq": [[[9.0 / 32.0 * ln3 * ln3]]], "dk": [[[-0.75]], [[9.0 / 16.0]]],
+    "dv": [[[0.25]], [[0.75]]],
+}
+
 if __name__ == "__main__":
     for name, obj in (("closed_form_one_query_two_keys.json", ONE_QUERY_TWO_KEYS),
-                      ("closed_form_causal_bottom_right_2x3.json", CAUSAL_BOTTOM_RIGHT_2X3)):
+                      ("closed_form_causal_bottom_right_2x3.json", CAUSAL_BOTTOM_RIGHT_2X3),
+                      ("closed_form_softcap_one_query_two_keys.json",
+                       SOFTCAP_ONE_QUERY_TWO_KEYS)):
         with open(os.path.join(HERE, name), "w") as f:
             json.dump(obj, f, indent=1)
     print("written")

@@ -78,7 +78,8 @@ def test_gradient_matches_central_differences(case, mode):
 
 
 @pytest.mark.parametrize("fname", ["closed_form_one_query_two_keys.json",
-                                   "closed_form_causal_bottom_right_2x3.json"])
+                                   "closed_form_causal_bottom_right_2x3.json",
+                                   "closed_form_softcap_one_query_two_keys.json"])
 @pytest.mark.parametrize("mode", ["contracted", "explicit"])
 def test_hand_derived_closed_forms(fname, mode):
     gd = json.load(open(os.path.join(GOLDEN, fname)))
@@ -86,11 +87,13 @@ def test_hand_derived_closed_forms(fname, mode):
          for k in ("q", "k", "v", "dout", "out", "lse", "dq", "dk", "dv")}
     cu_q = [0, gd["shape"]["Sq"]]
     cu_k = [0, gd["shape"]["Sk"]]
-    out, lse = O.forward(A["q"], A["k"], A["v"], cu_q, cu_k, gd["scale"], gd["causal"])
+    cap = gd.get("softcap", 0.0)
+    out, lse = O.forward(A["q"], A["k"], A["v"], cu_q, cu_k, gd["scale"], gd["causal"],
+                         softcap=cap)
     np.testing.assert_allclose(out, A["out"], rtol=0, atol=1e-14)
     np.testing.assert_allclose(lse, A["lse"], rtol=0, atol=1e-14)
     g = O.backward(A["q"], A["k"], A["v"], A["dout"], cu_q, cu_k, gd["scale"],
-                   gd["causal"], mode=mode)
+                   gd["causal"], mode=mode, softcap=cap)
     for key in ("dq", "dk", "dv"):
         np.testing.assert_allclose(g[key], A[key], rtol=0, atol=1e-14, err_msg=key)
 
@@ -345,3 +348,73 @@ def test_window_gradient_matches_central_differences(window, causal):
     for name, x in (("dq", q), ("dk", k), ("dv", v)):
         fd = _central_diff(x, loss)
         assert np.allclose(g[name], fd, rtol=1e-6, atol=1e-7), name
+
+
+# ---- soft-capped scores: every scaled score x becomes c * tanh(x / c) ----
+
+SOFTCAP_FD_CASES = [
+    # (lens_q, lens_k, H, Hk, D, causal, window, cap)
+    ([5], [7], 2, 1, 3, False, (-1, -1), 0.9),
+    ([4, 6], [5, 6], 2, 1, 3, True, (2, 0), 1.3),
+    ([7], [5], 2, 2, 4, True, (-1, -1), 0.5),        # rows without keys
+]
+
+
+@pytest.mark.parametrize("case", SOFTCAP_FD_CASES)
+@pytest.mark.parametrize("mode", ["contracted", "explicit"])
+def test_softcap_gradient_matches_central_differences(case, mode):
+    lq, lk, H, Hk, D, causal, window, cap = case
+    q, k, v, do, cu_q, cu_k = _problem(41, lq, lk, H, Hk, D)
+    q *= 2.0   # scaled scores of several units: the cap is far from linear
+
+    def loss():
+        out, _ = O.forward(q, k, v, cu_q, cu_k, 0.8, causal, window=window, softcap=cap)
+        return float(np.sum(do * out))
+    g = O.backward(q, k, v, do, cu_q, cu_k, 0.8, causal, mode=mode, window=window,
+                   softcap=cap)
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        fd = _central_diff(x, loss)
+        err = np.abs(g[name] - fd)
+        assert np.all(err <= 1e-7 * np.maximum(1.0, np.abs(g[name]))), (name, err.max())
+
+
+def test_huge_softcap_is_no_cap():
+    """c tanh(x / c) = x - x^3 / (3 c^2) + ...: at c = 1e7 the cap moves the
+    scores by less than 1e-13."""
+    q, k, v, do, cu_q, cu_k = _problem(42, [6, 9], [8, 7], 4, 2, 5)
+    a = O.backward(q, k, v, do, cu_q, cu_k, 0.6, True)
+    b = O.backward(q, k, v, do, cu_q, cu_k, 0.6, True, softcap=1e7)
+    for key in ("dq", "dk", "dv", "lse"):
+        np.testing.assert_allclose(b[key], a[key], rtol=1e-10, atol=1e-12, err_msg=key)
+
+
+def test_tiny_softcap_gives_uniform_attention_and_no_score_gradient():
+    """c = 1e-12: |capped score| <= c, so each row attends uniformly to the
+    keys it sees (O = their mean V, LSE = ln n); every |x / c| is past 1e3,
+    where tanh is 1 in fp64, so the cap's derivative and with it dQ and dK are
+    exactly 0; dV_j = sum over the rows i that see j of dO_i / n_i."""
+    lq, lk = 6, 9
+    q, k, v, do, cu_q, cu_k = _problem(43, [lq], [lk], 2, 1, 4)
+    cap = 1e-12
+    out, lse = O.forward(q, k, v, cu_q, cu_k, 0.5, True, softcap=cap)
+    g = O.backward(q, k, v, do, cu_q, cu_k, 0.5, True, softcap=cap)
+    off = lk - lq
+    dv = np.zeros_like(v)
+    for i in range(lq):
+        n = i + off + 1                      # bottom-right causal: keys 0 .. i + off
+        for h in range(2):
+            np.testing.assert_allclose(out[i, h], v[:n, 0].mean(axis=0), rtol=1e-12, atol=1e-12)
+            assert abs(lse[i, h] - np.log(n)) <= 2 * cap
+            dv[:n, 0] += do[i, h] / n
+    assert np.all(g["dq"] == 0) and np.all(g["dk"] == 0)
+    np.testing.assert_allclose(g["dv"], dv, rtol=1e-12, atol=1e-12)
+
+
+def test_capped_scores_are_bounded_by_the_cap():
+    """|c tanh(x / c)| < c: LSE_i lies within c of ln(number of visible keys)."""
+    q, k, v, do, cu_q, cu_k = _problem(44, [10], [10], 2, 1, 8)
+    q *= 5.0
+    cap = 0.25
+    _, lse = O.forward(q, k, v, cu_q, cu_k, 1.0, True, softcap=cap)
+    n = np.arange(1, 11)[:, None]
+    assert np.all(np.abs(lse - np.log(n)) <= cap)
