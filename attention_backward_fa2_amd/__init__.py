@@ -48,6 +48,7 @@ class FaBwdArgs(ctypes.Structure):
         ("local_window", ctypes.c_int32),
         ("window_size_left", ctypes.c_int32),
         ("window_size_right", ctypes.c_int32),
+        ("softcap", ctypes.c_float),
         ("deterministic", ctypes.c_int32),
         ("dq_accumulate", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
@@ -89,6 +90,7 @@ class FaFwdArgs(ctypes.Structure):
         ("local_window", ctypes.c_int32),
         ("window_size_left", ctypes.c_int32),
         ("window_size_right", ctypes.c_int32),
+        ("softcap", ctypes.c_float),
     ]
 
 
@@ -175,7 +177,7 @@ def _set_window(a, window):
 def make_args(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
               cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
               max_seqlen_k=None, deterministic=False, workspace=None,
-              dq_accumulate=False, window=None) -> FaBwdArgs:
+              dq_accumulate=False, window=None, softcap=0.0) -> FaBwdArgs:
     """Fill fa_bwd_args from tensors.  Dense tensors are (B, S, H, D); packed
     ones (total, H, D) with int32 device cu_seqlens and host max lengths.
     dq_accumulate=False: dQ by the separate query-tile pass (default);
@@ -210,6 +212,7 @@ def make_args(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
     a.softmax_scale = float(softmax_scale)
     a.causal = int(bool(causal))
     _set_window(a, window)
+    a.softcap = float(softcap)
     a.deterministic = int(bool(deterministic))
     a.dq_accumulate = int(bool(dq_accumulate))
     if workspace is not None:
@@ -267,7 +270,7 @@ def run(args: FaBwdArgs, step: str = "all", stream=None):
 def fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
            cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
            deterministic=False, workspace=None, stream=None, dq_accumulate=False,
-           window=None):
+           window=None, softcap=0.0):
     """dQ, dK, dV of attention, written into dq, dk, dv (same layouts as q, k, v).
 
     lse is the forward's natural-log log-sum-exp, (B, H, Sq) fp32 (packed:
@@ -275,7 +278,7 @@ def fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
     holds the fp32 dQ accumulator and the row sums afterwards)."""
     args = make_args(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
                      cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                     deterministic, workspace, dq_accumulate, window)
+                     deterministic, workspace, dq_accumulate, window, softcap)
     if workspace is None:
         workspace = alloc_workspace(args, q.device)
     run(args, "all", stream)
@@ -284,7 +287,7 @@ def fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
 
 def make_fwd_args(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q=None,
                   cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
-                  window=None) -> FaFwdArgs:
+                  window=None, softcap=0.0) -> FaFwdArgs:
     """Fill fa_fwd_args from tensors (layouts as in make_args)."""
     varlen = cu_seqlens_q is not None or cu_seqlens_k is not None
     a = FaFwdArgs()
@@ -312,6 +315,7 @@ def make_fwd_args(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q=None,
     a.softmax_scale = float(softmax_scale)
     a.causal = int(bool(causal))
     _set_window(a, window)
+    a.softcap = float(softcap)
     return a
 
 
@@ -325,9 +329,9 @@ def run_fwd(args: FaFwdArgs, stream=None):
 
 
 def fa_fwd(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q=None, cu_seqlens_k=None,
-           max_seqlen_q=None, max_seqlen_k=None, stream=None, window=None):
+           max_seqlen_q=None, max_seqlen_k=None, stream=None, window=None, softcap=0.0):
     """O and the natural-log LSE of attention, written into out (layout of q)
     and lse ((B, H, Sq) fp32; packed: (num_seqs, H, max_seqlen_q))."""
     args = make_fwd_args(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q, cu_seqlens_k,
-                         max_seqlen_q, max_seqlen_k, window)
+                         max_seqlen_q, max_seqlen_k, window, softcap)
     run_fwd(args, stream)

@@ -8,6 +8,7 @@
 // head dim <= 256, contiguous last dim) and the sm90 backward page
 // (_check_type: 16-bit input dtype, fp32 LSE / accumulators; __call__: every
 // stride but the last a multiple of 128 bits).
+#include <cfloat>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -40,6 +41,20 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // window sums fit in 32-bit integers in the kernels (a window of 2^29 or
 // more reaches past every key of such a sequence).
 constexpr int kMaxSeqlen = 1 << 29;
+
+void set_softcap(fa::Params &p, float c)
+{
+    const double log2e = 1.4426950408889634;
+    p.softcap = c;
+    // (clamped: for a cap so small that the factor leaves the fp32 range,
+    // tanh is +-1 for every nonzero score either way, and 0 * FLT_MAX = 0)
+    p.cap_in = c > 0.f ? (float)std::min(2.0 * std::fabs((double)p.scale) * log2e / (double)c,
+                                         (double)FLT_MAX)
+                       : 0.f;
+    if (p.scale < 0.f)
+        p.cap_in = -p.cap_in;
+    p.cap_out = c > 0.f ? (float)((double)c * log2e) : 0.f;
+}
 
 void set_window(fa::Params &p, int causal, int left, int right)
 {
@@ -143,6 +158,8 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
         return fail(FA_ERR_UNSUPPORTED, "k / v row stride >= 2^24 elements is not supported");
     if (a->softmax_scale != a->softmax_scale || std::isinf(a->softmax_scale))
         return fail(FA_ERR_INVALID_ARG, "softmax_scale is not finite");
+    if (!(a->softcap >= 0.f) || std::isinf(a->softcap))
+        return fail(FA_ERR_INVALID_ARG, "softcap must be finite and >= 0");
     if ((a->causal != 0 && a->causal != 1) || (a->deterministic != 0 && a->deterministic != 1) ||
         (a->dq_accumulate != 0 && a->dq_accumulate != 1))
         return fail(FA_ERR_INVALID_ARG, "causal, deterministic and dq_accumulate must be 0 or 1");
@@ -190,6 +207,7 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
     p.ntiles = (a->seqlen_k + fa::kKTile - 1) / fa::kKTile;
     p.scale = a->softmax_scale;
     p.scale_log2 = (float)((double)a->softmax_scale * 1.4426950408889634);
+    set_softcap(p, a->softcap);
     p.causal = a->causal;
     set_window(p, a->causal, a->local_window ? a->window_size_left : -1,
                a->local_window ? a->window_size_right : -1);
@@ -335,6 +353,8 @@ fa_status make_fwd_plan(const fa_fwd_args *a, fa::Params *pp, int *dpad_out)
         return fail(FA_ERR_UNSUPPORTED, "k / v row stride >= 2^24 elements is not supported");
     if (a->softmax_scale != a->softmax_scale || std::isinf(a->softmax_scale))
         return fail(FA_ERR_INVALID_ARG, "softmax_scale is not finite");
+    if (!(a->softcap >= 0.f) || std::isinf(a->softcap))
+        return fail(FA_ERR_INVALID_ARG, "softcap must be finite and >= 0");
     if (a->causal != 0 && a->causal != 1)
         return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
     if (a->local_window != 0 && a->local_window != 1)
@@ -371,6 +391,7 @@ fa_status make_fwd_plan(const fa_fwd_args *a, fa::Params *pp, int *dpad_out)
     p.rows = nq;
     p.scale = a->softmax_scale;
     p.scale_log2 = (float)((double)a->softmax_scale * 1.4426950408889634);
+    set_softcap(p, a->softcap);
     p.causal = a->causal;
     set_window(p, a->causal, a->local_window ? a->window_size_left : -1,
                a->local_window ? a->window_size_right : -1);

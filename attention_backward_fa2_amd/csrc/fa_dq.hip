@@ -58,8 +58,8 @@ struct __attribute__((aligned(16))) DqSmem {
 
 // LOCAL: a left window bounds the visible keys from below (win_l >= 0);
 // otherwise win_l < 0 and only the upper bound (causal / right window / key
-// end) is masked.
-template <int DP, bool F16, bool LOCAL>
+// end) is masked.  SOFTCAP: scores soft-capped (softcap > 0).
+template <int DP, bool F16, bool LOCAL, bool SOFTCAP>
 __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
 {
     constexpr int KS = DP / 16;                  // k-steps over the head dim
@@ -343,12 +343,20 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
             auto pw_elem = [&](auto mbc, auto ec) {
                 constexpr int mb = decltype(mbc)::value, e = decltype(ec)::value;
                 constexpr int r4 = e >> 2, tt = e & 3;
-                float x = __builtin_amdgcn_exp2f(st[mb][e] * p.scale_log2 - l2);
+                float x, cg = 1.f;
+                if constexpr (SOFTCAP) {
+                    // capped score tanh * c (base 2); dS picks up 1 - tanh^2
+                    const float th = cap_tanh(st[mb][e], p.cap_in);
+                    x = __builtin_amdgcn_exp2f(fmaf(th, p.cap_out, -l2));
+                    cg = fmaf(-th, th, 1.f);
+                } else {
+                    x = __builtin_amdgcn_exp2f(st[mb][e] * p.scale_log2 - l2);
+                }
                 if constexpr (decltype(maskc)::value) {
                     constexpr int ke = 32 * mb + 8 * r4 + tt;
                     x = ke <= kthr && (!LOCAL || ke >= kthr_lo) ? x : 0.f;
                 }
-                float d = x * -dpt[mb][e];   // dpt holds rowdot - dP
+                float d = SOFTCAP ? x * cg * -dpt[mb][e] : x * -dpt[mb][e];   // dpt: rowdot - dP
                 keep_here(d);
                 dv[tt] = d;
                 if constexpr (tt == 3) {
@@ -450,7 +458,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
     }
 }
 
-template <bool LOCAL>
+template <bool LOCAL, bool SOFTCAP>
 static hipError_t launch_dq_t(const Params &p, int dpad, hipStream_t st)
 {
     const int nqt = (p.Sq + kDqRows - 1) / kDqRows;
@@ -459,21 +467,21 @@ static hipError_t launch_dq_t(const Params &p, int dpad, hipStream_t st)
     switch (dpad) {
     case 64:
         if (p.f16)
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<64, true, LOCAL>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<64, true, LOCAL, SOFTCAP>), grid, block, 0, st, p);
         else
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<64, false, LOCAL>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<64, false, LOCAL, SOFTCAP>), grid, block, 0, st, p);
         break;
     case 96:
         if (p.f16)
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<96, true, LOCAL>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<96, true, LOCAL, SOFTCAP>), grid, block, 0, st, p);
         else
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<96, false, LOCAL>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<96, false, LOCAL, SOFTCAP>), grid, block, 0, st, p);
         break;
     case 128:
         if (p.f16)
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<128, true, LOCAL>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<128, true, LOCAL, SOFTCAP>), grid, block, 0, st, p);
         else
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<128, false, LOCAL>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<128, false, LOCAL, SOFTCAP>), grid, block, 0, st, p);
         break;
     default:
         return hipErrorInvalidValue;
@@ -483,7 +491,11 @@ static hipError_t launch_dq_t(const Params &p, int dpad, hipStream_t st)
 
 hipError_t launch_dq(const Params &p, int dpad, hipStream_t st)
 {
-    return p.win_l >= 0 ? launch_dq_t<true>(p, dpad, st) : launch_dq_t<false>(p, dpad, st);
+    if (p.softcap > 0.f)
+        return p.win_l >= 0 ? launch_dq_t<true, true>(p, dpad, st)
+                            : launch_dq_t<false, true>(p, dpad, st);
+    return p.win_l >= 0 ? launch_dq_t<true, false>(p, dpad, st)
+                        : launch_dq_t<false, false>(p, dpad, st);
 }
 
 }  // namespace fa

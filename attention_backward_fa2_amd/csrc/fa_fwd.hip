@@ -55,8 +55,9 @@ struct __attribute__((aligned(16))) FwdSmem {
 };
 
 // LOCAL: a left window bounds the visible keys from below (win_l >= 0);
-// otherwise win_l < 0 and only the upper bound is masked.
-template <int DP, bool F16, bool LOCAL>
+// otherwise win_l < 0 and only the upper bound is masked.  SOFTCAP: scores
+// soft-capped (softcap > 0).
+template <int DP, bool F16, bool LOCAL, bool SOFTCAP>
 __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
 {
     constexpr int KS = DP / 16;                  // k-steps over the head dim
@@ -266,6 +267,11 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
             // elements e, e+1 of block mb into its maximum (one three-input max)
             auto max_pair = [&](auto mbc, auto ec) {
                 constexpr int mb = decltype(mbc)::value, e = decltype(ec)::value;
+                if constexpr (SOFTCAP) {
+                    // scores become the capped ones in base 2, tanh * c
+                    st[mb][e] = cap_tanh(st[mb][e], p.cap_in) * p.cap_out;
+                    st[mb][e + 1] = cap_tanh(st[mb][e + 1], p.cap_in) * p.cap_out;
+                }
                 const float s0 = visible(mbc, ec) ? st[mb][e] : -INFINITY;
                 const float s1 = visible(mbc, IC<e + 1>{}) ? st[mb][e + 1] : -INFINITY;
                 float &m = mb == 0 ? mx0 : mx1;
@@ -275,7 +281,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
             auto p_elem = [&](auto mbc, auto ec) {
                 constexpr int mb = decltype(mbc)::value, e = decltype(ec)::value;
                 constexpr int r4 = e >> 2, tt = e & 3;
-                float x = __builtin_amdgcn_exp2f(st[mb][e] * c2 - mu);
+                float x = __builtin_amdgcn_exp2f((SOFTCAP ? st[mb][e] : st[mb][e] * c2) - mu);
                 if constexpr (MASK)
                     x = visible(mbc, ec) ? x : 0.f;
                 keep_here(x);
@@ -315,7 +321,8 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
                     static_for<8>([&](auto ec) { max_pair(IC<1>{}, IC<2 * decltype(ec)::value>{}); });
                     float mt = fmaxf(mx0, mx1);
                     mt = fmaxf(mt, __shfl_xor(mt, 32));
-                    const float mt2 = mt * c2;        // -inf if no key of the tile is visible
+                    // -inf if no key of the tile is visible
+                    const float mt2 = SOFTCAP ? mt : mt * c2;
                     // Lazy rescale: move the running maximum only if some row
                     // of the wave would see P above 2^8 otherwise.
                     const bool need = mt2 > mrun + 8.f;
@@ -402,7 +409,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
     }
 }
 
-template <bool LOCAL>
+template <bool LOCAL, bool SOFTCAP>
 static hipError_t launch_fwd_t(const Params &p, int dpad, hipStream_t st)
 {
     const int nqt = (p.Sq + kFwdRows - 1) / kFwdRows;
@@ -411,21 +418,21 @@ static hipError_t launch_fwd_t(const Params &p, int dpad, hipStream_t st)
     switch (dpad) {
     case 64:
         if (p.f16)
-            hipLaunchKernelGGL((fa_fwd_kernel<64, true, LOCAL>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_fwd_kernel<64, true, LOCAL, SOFTCAP>), grid, block, 0, st, p);
         else
-            hipLaunchKernelGGL((fa_fwd_kernel<64, false, LOCAL>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_fwd_kernel<64, false, LOCAL, SOFTCAP>), grid, block, 0, st, p);
         break;
     case 96:
         if (p.f16)
-            hipLaunchKernelGGL((fa_fwd_kernel<96, true, LOCAL>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_fwd_kernel<96, true, LOCAL, SOFTCAP>), grid, block, 0, st, p);
         else
-            hipLaunchKernelGGL((fa_fwd_kernel<96, false, LOCAL>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_fwd_kernel<96, false, LOCAL, SOFTCAP>), grid, block, 0, st, p);
         break;
     case 128:
         if (p.f16)
-            hipLaunchKernelGGL((fa_fwd_kernel<128, true, LOCAL>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_fwd_kernel<128, true, LOCAL, SOFTCAP>), grid, block, 0, st, p);
         else
-            hipLaunchKernelGGL((fa_fwd_kernel<128, false, LOCAL>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_fwd_kernel<128, false, LOCAL, SOFTCAP>), grid, block, 0, st, p);
         break;
     default:
         return hipErrorInvalidValue;
@@ -435,7 +442,11 @@ static hipError_t launch_fwd_t(const Params &p, int dpad, hipStream_t st)
 
 hipError_t launch_fwd(const Params &p, int dpad, hipStream_t st)
 {
-    return p.win_l >= 0 ? launch_fwd_t<true>(p, dpad, st) : launch_fwd_t<false>(p, dpad, st);
+    if (p.softcap > 0.f)
+        return p.win_l >= 0 ? launch_fwd_t<true, true>(p, dpad, st)
+                            : launch_fwd_t<false, true>(p, dpad, st);
+    return p.win_l >= 0 ? launch_fwd_t<true, false>(p, dpad, st)
+                        : launch_fwd_t<false, false>(p, dpad, st);
 }
 
 }  // namespace fa

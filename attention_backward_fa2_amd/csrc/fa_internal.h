@@ -57,6 +57,10 @@ struct Params {
     // (off = Lk - Lq; a negative size leaves that side unbounded; causal is
     // win_r = 0).
     int win_l, win_r;
+    // Soft cap c > 0 of the scaled scores (0: none): with s the raw product
+    // q.k, tanh(s * scale / c) = 1 - 2 / (exp2(s * cap_in) + 1) and the capped
+    // score in base 2 is tanh * cap_out.
+    float softcap, cap_in, cap_out;
     int fused_dq;       // 1: dQ partials added into dq_acc by the key-tile kernel
     int f16;            // 1: fp16 elements, 0: bf16
 };
@@ -121,6 +125,7 @@ __device__ inline float elem2f(uint16_t x)
 
 // Host-side launchers (one translation unit each).
 hipError_t launch_preprocess(const Params &p, int dpad, hipStream_t st);
+hipError_t launch_main_softcap(const Params &p, int dpad, hipStream_t st);
 hipError_t launch_main(const Params &p, int dpad, hipStream_t st);
 hipError_t launch_convert(const Params &p, int dpad, hipStream_t st);
 hipError_t launch_dq(const Params &p, int dpad, hipStream_t st);

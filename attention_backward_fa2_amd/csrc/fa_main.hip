@@ -189,8 +189,9 @@ __device__ inline void dq_partial(const Params &p, FusedSmem<DP> &sm, int buf, i
 }
 
 // LOCAL: a left window bounds the visible keys from below (win_l >= 0);
-// otherwise win_l < 0 and only the upper bound is masked.
-template <int DP, bool FUSED, bool F16, bool LOCAL>
+// otherwise win_l < 0 and only the upper bound is masked.  SOFTCAP: scores
+// soft-capped (softcap > 0).
+template <int DP, bool FUSED, bool F16, bool LOCAL, bool SOFTCAP>
 __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
 {
     constexpr int KS = DP / 16;       // MFMA k-steps over the head dim
@@ -554,10 +555,18 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 constexpr int mb = decltype(mbc)::value, e = decltype(ec)::value;
                 constexpr int r4 = e >> 2, t = e & 3;
                 constexpr int qc = 32 * mb + 8 * r4;
-                float x = __builtin_amdgcn_exp2f(s[mb][e] * p.scale_log2 - l2v[r4][t]);
+                float x, cg = 1.f;
+                if constexpr (SOFTCAP) {
+                    // capped score tanh * c (base 2); dS picks up 1 - tanh^2
+                    const float th = cap_tanh(s[mb][e], p.cap_in);
+                    x = __builtin_amdgcn_exp2f(fmaf(th, p.cap_out, -l2v[r4][t]));
+                    cg = fmaf(-th, th, 1.f);
+                } else {
+                    x = __builtin_amdgcn_exp2f(s[mb][e] * p.scale_log2 - l2v[r4][t]);
+                }
                 if constexpr (decltype(maskc)::value)
                     x = qc + t >= limv && (!LOCAL || qc + t <= limu) ? x : 0.f;
-                float d = x * -dp[mb][e];   // dp holds rowdot - dP
+                float d = SOFTCAP ? x * cg * -dp[mb][e] : x * -dp[mb][e];   // dp: rowdot - dP
                 keep_here(x);
                 keep_here(d);
                 pv[t] = x;
@@ -772,40 +781,57 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
     }
 }
 
-template <bool LOCAL>
+template <bool LOCAL, bool SOFTCAP>
 static hipError_t launch_main_t(const Params &p, int dpad, hipStream_t st)
 {
     const dim3 grid((unsigned)p.ntiles * p.Hk * p.batch);
     const dim3 block(kThreads);
-#define FA_LAUNCH_MAIN(D)                                                                        \
+#define FA_LAUNCH_MAIN(D, FU, H16)                                                               \
+    hipLaunchKernelGGL((fa_bwd_main_kernel<D, FU, H16, LOCAL, SOFTCAP>), grid, block, 0, st, p)
+#define FA_LAUNCH_MAIN_D(D)                                                                      \
     if (p.fused_dq && p.f16)                                                                     \
-        hipLaunchKernelGGL((fa_bwd_main_kernel<D, true, true, LOCAL>), grid, block, 0, st, p);   \
+        FA_LAUNCH_MAIN(D, true, true);                                                           \
     else if (p.fused_dq)                                                                         \
-        hipLaunchKernelGGL((fa_bwd_main_kernel<D, true, false, LOCAL>), grid, block, 0, st, p);  \
+        FA_LAUNCH_MAIN(D, true, false);                                                          \
     else if (p.f16)                                                                              \
-        hipLaunchKernelGGL((fa_bwd_main_kernel<D, false, true, LOCAL>), grid, block, 0, st, p);  \
+        FA_LAUNCH_MAIN(D, false, true);                                                          \
     else                                                                                         \
-        hipLaunchKernelGGL((fa_bwd_main_kernel<D, false, false, LOCAL>), grid, block, 0, st, p);
+        FA_LAUNCH_MAIN(D, false, false);
     switch (dpad) {
     case 64:
-        FA_LAUNCH_MAIN(64);
+        FA_LAUNCH_MAIN_D(64);
         break;
     case 96:
-        FA_LAUNCH_MAIN(96);
+        FA_LAUNCH_MAIN_D(96);
         break;
     case 128:
-        FA_LAUNCH_MAIN(128);
+        FA_LAUNCH_MAIN_D(128);
         break;
     default:
         return hipErrorInvalidValue;
     }
+#undef FA_LAUNCH_MAIN_D
 #undef FA_LAUNCH_MAIN
     return hipGetLastError();
 }
 
+// The soft-capped instantiations build in a translation unit of their own
+// (fa_main_softcap.hip includes this file with FA_MAIN_SOFTCAP_TU defined),
+// so that the two halves compile in parallel.
+#ifdef FA_MAIN_SOFTCAP_TU
+hipError_t launch_main_softcap(const Params &p, int dpad, hipStream_t st)
+{
+    return p.win_l >= 0 ? launch_main_t<true, true>(p, dpad, st)
+                        : launch_main_t<false, true>(p, dpad, st);
+}
+#else
 hipError_t launch_main(const Params &p, int dpad, hipStream_t st)
 {
-    return p.win_l >= 0 ? launch_main_t<true>(p, dpad, st) : launch_main_t<false>(p, dpad, st);
+    if (p.softcap > 0.f)
+        return launch_main_softcap(p, dpad, st);
+    return p.win_l >= 0 ? launch_main_t<true, false>(p, dpad, st)
+                        : launch_main_t<false, false>(p, dpad, st);
 }
+#endif
 
 }  // namespace fa

@@ -126,6 +126,16 @@ __device__ inline void keep_scalar_here(T &...x)
     (keep_scalar_one(x), ...);
 }
 
+// tanh(s * scale / c) of a raw score product s, with cap_in = 2 scale
+// log2(e) / c: 1 - 2 / (exp2(s * cap_in) + 1) (the exp2 overflows to +inf for
+// large scores, giving 1, and underflows to 0 for very negative ones, giving
+// -1).  Two transcendental and two ordinary VALU operations.
+__device__ inline float cap_tanh(float s, float cap_in)
+{
+    const float e = __builtin_amdgcn_exp2f(s * cap_in);
+    return fmaf(-2.f, __builtin_amdgcn_rcpf(e + 1.f), 1.f);
+}
+
 // The lane index, formed where this is called: a volatile statement is
 // neither hoisted out of a loop nor merged with another, so values derived
 // from it take no register across the loop.

@@ -39,7 +39,7 @@ KERNEL_SOURCES = ["attention_backward_fa2_amd/csrc/fa_main.hip",
                   "attention_backward_fa2_amd/csrc/fa_internal.h"]
 TRAFFIC_SUMMARY = "profiles/hbm_traffic_main_kernel_gqa_b2_h32_hk8_s4096_d128_causal.json"
 TRACE_SUMMARY = "profiles/kernel_trace_gqa_b2_h32_hk8_s4096_d128_causal.md"
-MAIN_KERNEL = "fa_bwd_main_kernel<128, false, false, false>"
+MAIN_KERNEL = "fa_bwd_main_kernel<128, false, false, false, false>"
 
 
 def kernel_source_hash():
@@ -248,7 +248,7 @@ def conv_flops(B, H, Sq, Sk, D, causal, window=None):
     return 2.5 * 4.0 * B * H * D * visible_pairs(Sq, Sk, causal, window)
 
 
-def forward_inputs_torch(q, k, v, scale, causal, window=None):
+def forward_inputs_torch(q, k, v, scale, causal, window=None, softcap=0.0):
     """O (bf16) and natural-log LSE (fp32, (B,H,Sq)) by a plain fp32 torch
     forward, one (batch, head) at a time.  Dense bshd inputs on the GPU."""
     import torch
@@ -274,6 +274,8 @@ def forward_inputs_torch(q, k, v, scale, causal, window=None):
             kt = k[b, :, h // G, :].float().t().contiguous()
             vh = v[b, :, h // G, :].float().contiguous()
             s = torch.matmul(qh, kt) * scale
+            if softcap > 0:
+                s = softcap * torch.tanh(s / softcap)
             if masked is not None:
                 s.masked_fill_(masked, float("-inf"))
             l = torch.logsumexp(s, dim=-1)
@@ -305,7 +307,7 @@ def cpu_baseline(wl, units):
         do = f64(inp.dout[b][:, hs])
         t0 = time.perf_counter()
         O.backward(q, k, v, do, [0, wl.seqlen_q], [0, wl.seqlen_k], wl.scale, wl.causal,
-                   window=wl.window_sizes)
+                   window=wl.window_sizes, softcap=wl.softcap)
         t_total += time.perf_counter() - t0
         flops += conv_flops(1, G, wl.seqlen_q, wl.seqlen_k, wl.head_dim, wl.causal, wl.window)
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(),
@@ -316,17 +318,23 @@ def cpu_baseline(wl, units):
 
 
 def window_suffix(wl):
-    return "" if wl.window is None else ", local window (%d, %d)" % tuple(wl.window)
+    suffix = "" if wl.window is None else ", local window (%d, %d)" % tuple(wl.window)
+    return suffix + (", softcap %g" % wl.softcap if wl.softcap > 0 else "")
 
 
 def main_kernel_name(fused, wl):
     local = wl.window is not None and wl.window[0] >= 0
-    return "fa_bwd_main_kernel<128, %s, false, %s>" % (str(bool(fused)).lower(),
-                                                       str(local).lower())
+    return "fa_bwd_main_kernel<128, %s, false, %s, %s>" % (
+        str(bool(fused)).lower(), str(local).lower(), str(wl.softcap > 0).lower())
+
+
+def fwd_kernel_name(wl):
+    local = wl.window is not None and wl.window[0] >= 0
+    return "fa_fwd_kernel<128, false, %s, %s>" % (str(local).lower(), str(wl.softcap > 0).lower())
 
 
 FWD_METRIC = "fwd TFLOP/s (O, LSE) bf16 and % of MFMA peak, S=4096 D=128 causal GQA"
-FWD_KERNEL = "fa_fwd_kernel<128, false, false>"
+FWD_KERNEL = "fa_fwd_kernel<128, false, false, false>"
 
 
 def fwd_flops(B, H, Sq, Sk, D, causal, window=None):
@@ -351,7 +359,7 @@ def cpu_baseline_fwd(wl, units):
         v = f64(inp.v[b][:, [h // G]])
         t0 = time.perf_counter()
         O.forward(q, k, v, [0, wl.seqlen_q], [0, wl.seqlen_k], wl.scale, wl.causal,
-                  window=wl.window_sizes)
+                  window=wl.window_sizes, softcap=wl.softcap)
         t_total += time.perf_counter() - t0
         flops += fwd_flops(1, 1, wl.seqlen_q, wl.seqlen_k, wl.head_dim, wl.causal, wl.window)
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(),
@@ -368,7 +376,8 @@ def bench_forward(args, wl, dev):
     q, k, v = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v))
     out = torch.empty_like(q)
     lse = torch.empty(wl.batch, wl.heads, wl.seqlen_q, dtype=torch.float32, device=dev)
-    a = fa.make_fwd_args(q, k, v, out, lse, wl.scale, wl.causal, window=wl.window)
+    a = fa.make_fwd_args(q, k, v, out, lse, wl.scale, wl.causal, window=wl.window,
+                         softcap=wl.softcap)
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         fa.run_fwd(a, stream)
@@ -393,15 +402,15 @@ def bench_forward(args, wl, dev):
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "heads": H, "heads_k": Hk,
                    "seqlen_q": Sq, "seqlen_k": Sk, "head_dim": D, "causal": wl.causal,
-                   "window": list(wl.window) if wl.window else None, "pass": "forward"},
+                   "window": list(wl.window) if wl.window else None,
+                   "softcap": wl.softcap or None, "pass": "forward"},
         "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
         "flops_per_step": flops,
         "kernel_ms": {"fwd": round(ms, 4)},
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": None,
-                     "kernel": FWD_KERNEL if wl.window is None or wl.window[0] < 0 else
-                     FWD_KERNEL.replace(", false>", ", true>"),
+                     "kernel": fwd_kernel_name(wl),
                      "algorithmic_flops_per_launch": flops},
         "wall_s": round(wall, 3),
     }
@@ -430,6 +439,8 @@ def main():
     ap.add_argument("--cpu-units", type=int, default=16)
     ap.add_argument("--window", type=int, nargs=2, metavar=("LEFT", "RIGHT"),
                     help="local window (negative = unbounded): times the workload with it")
+    ap.add_argument("--softcap", type=float, default=0.0,
+                    help="soft cap c > 0 of the scaled scores: times the workload with it")
     ap.add_argument("--summarize-profile", metavar="PROF_DIR",
                     help="write the profiles/ summaries from rocprofv3 outputs in PROF_DIR "
                          "(trace/, FETCH_SIZE/, WRITE_SIZE/, copy_FETCH_SIZE/, copy_WRITE_SIZE/)")
@@ -468,6 +479,10 @@ def main():
         import dataclasses
         wl = dataclasses.replace(wl, name="%s_window%d_%d" % (wl.name, *args.window),
                                  window=tuple(args.window))
+    if args.softcap > 0:
+        import dataclasses
+        wl = dataclasses.replace(wl, name="%s_softcap%g" % (wl.name, args.softcap),
+                                 softcap=float(args.softcap))
     if wl.varlen:
         print("bench.py times dense workloads only", file=sys.stderr)
         sys.exit(2)
@@ -478,11 +493,11 @@ def main():
         return
     inp = W.make_inputs(wl)
     q, k, v, do = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v, inp.dout))
-    o, lse = forward_inputs_torch(q, k, v, wl.scale, wl.causal, wl.window)
+    o, lse = forward_inputs_torch(q, k, v, wl.scale, wl.causal, wl.window, wl.softcap)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     a = fa.make_args(do, q, k, v, o, lse, dq, dk, dv, wl.scale, wl.causal,
                      deterministic=args.deterministic, dq_accumulate=args.dq_accumulate,
-                     window=wl.window)
+                     window=wl.window, softcap=wl.softcap)
     # the steps of one backward, in the order fa_bwd enqueues them
     seq = ["preprocess", "main", "dq_convert"] if args.dq_accumulate else ["dq", "main"]
     ws = fa.alloc_workspace(a, dev)
@@ -548,6 +563,7 @@ def main():
         "config": {"workload": wl.name, "batch": B, "heads": H, "heads_k": Hk,
                    "seqlen_q": Sq, "seqlen_k": Sk, "head_dim": D, "causal": wl.causal,
                    "window": list(wl.window) if wl.window else None,
+                   "softcap": wl.softcap or None,
                    "dq_mode": ("ordered" if args.deterministic else "atomic")
                    if args.dq_accumulate else "separate"},
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
@@ -561,7 +577,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(main_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None if args.dq_accumulate or wl.window else committed_traffic(),
+                     "traffic": None if args.dq_accumulate or wl.window or wl.softcap > 0
+                     else committed_traffic(),
                      "kernel": main_kernel_name(args.dq_accumulate, wl),
                      "algorithmic_flops_per_launch": main_flops},
         "wall_s": round(wall, 3),

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define FA_BWD_ABI_VERSION 4
+#define FA_BWD_ABI_VERSION 5
 
 typedef enum {
     FA_OK = 0,
@@ -124,7 +124,13 @@ typedef enum {
  *     window_size_right >= 0); negative sizes leave that side unbounded.
  *     causal = 1 is the right size 0 (a positive right size with causal = 1
  *     is FA_ERR_INVALID_ARG).  Sizes above 2^29 act as 2^29 (which reaches
- *     every key: seqlen_q and seqlen_k above 2^29 are FA_ERR_UNSUPPORTED).  Rows that see no key behave as under the
+ *     every key: seqlen_q and seqlen_k above 2^29 are FA_ERR_UNSUPPORTED).
+ *   - softcap = c > 0 (mha_bwd's softcap on the backward call-trace page,
+ *     read as the usual logit soft-capping): every scaled score x =
+ *     softmax_scale * q.k becomes c * tanh(x / c) before the softmax, and lse
+ *     must be the forward's log-sum-exp of those capped scores; the gradients
+ *     pass the cap by the chain rule (factor 1 - tanh^2).  0 switches it off;
+ *     a negative or non-finite value is FA_ERR_INVALID_ARG.  Rows that see no key behave as under the
  *     causal rule (dq = 0, and they add nothing to dk / dv).
  *   - lse is the NATURAL-log log-sum-exp of the scaled scores of each row,
  *     -inf for a row with no visible key (its dQ is then 0).
@@ -168,6 +174,7 @@ typedef struct fa_bwd_args {
     int32_t local_window;          /* 0: no window (sizes ignored); 1: the sizes apply */
     int32_t window_size_left;      /* local window (see Semantics); < 0: unbounded */
     int32_t window_size_right;     /* < 0: unbounded; with causal = 1 only < 0 or 0 */
+    float softcap;                 /* > 0: soft-capped scores (see Semantics); 0: none */
     int32_t deterministic;         /* 0 or 1 (see Reproducibility) */
     int32_t dq_accumulate;         /* 0: separate dQ pass (default); 1: fp32 accumulator */
 

@@ -71,6 +71,7 @@ typedef struct fa_fwd_args {
     int32_t local_window;          /* local window as in fa_bwd_args */
     int32_t window_size_left;
     int32_t window_size_right;
+    float softcap;                 /* soft-capped scores as in fa_bwd_args; 0: none */
 } fa_fwd_args;
 
 /* FA_OK if fa_fwd would accept `args`; otherwise the error it would return. */

@@ -36,7 +36,7 @@ class Prepared:
         self.v64 = to64(inp.packed(inp.v))
         self.do64 = to64(inp.packed(inp.dout))
         out, lse = O.forward(self.q64, self.k64, self.v64, self.cu_q, self.cu_k, wl.scale,
-                             wl.causal, window=wl.window_sizes)
+                             wl.causal, window=wl.window_sizes, softcap=wl.softcap)
         self.o64_exact = out                      # [total_q, H, D] fp64
         self.lse_rows = lse                       # [total_q, H] fp64
         self.o = torch.from_numpy(out).to(inp.q.dtype).reshape(inp.q.shape)
@@ -78,7 +78,7 @@ def run_gpu(pr: Prepared, deterministic=False, out_pad=0, step_split=False, dq_a
                   max_seqlen_q=max(inp.lens_q), max_seqlen_k=max(inp.lens_k))
     args = fa.make_args(do, q, k, v, o, lse, dq, dk, dv, wl.scale, wl.causal,
                         deterministic=deterministic, dq_accumulate=dq_accumulate,
-                        window=wl.window, **kw)
+                        window=wl.window, softcap=wl.softcap, **kw)
     ws = fa.alloc_workspace(args, dev)
     ws.fill_(0xA5)   # garbage: the preprocess must clear what it uses
     if steps is not None:
@@ -115,7 +115,7 @@ def compare(gpu: torch.Tensor, ref: np.ndarray, what: str, tol=TOL):
 def oracle_backward(pr: Prepared):
     wl = pr.inp.wl
     return O.backward(pr.q64, pr.k64, pr.v64, pr.do64, pr.cu_q, pr.cu_k, wl.scale, wl.causal,
-                      window=wl.window_sizes)
+                      window=wl.window_sizes, softcap=wl.softcap)
 
 
 def oracle_backward_unit(pr: Prepared, s: int, g: int):
@@ -128,7 +128,7 @@ def oracle_backward_unit(pr: Prepared, s: int, g: int):
     ks, ke = pr.cu_k[s], pr.cu_k[s + 1]
     ref = O.backward(pr.q64[qs:qe][:, heads], pr.k64[ks:ke][:, [g]], pr.v64[ks:ke][:, [g]],
                      pr.do64[qs:qe][:, heads], [0, qe - qs], [0, ke - ks], wl.scale,
-                     wl.causal, window=wl.window_sizes)
+                     wl.causal, window=wl.window_sizes, softcap=wl.softcap)
     return (slice(qs, qe), heads, slice(ks, ke), ref)
 
 
@@ -148,7 +148,8 @@ def run_gpu_fwd(inp: W.Inputs):
         kw = dict(cu_seqlens_q=torch.tensor(cu_np(inp.lens_q), dtype=torch.int32, device=dev),
                   cu_seqlens_k=torch.tensor(cu_np(inp.lens_k), dtype=torch.int32, device=dev),
                   max_seqlen_q=maxq, max_seqlen_k=max(inp.lens_k))
-    args = fa.make_fwd_args(q, k, v, out, lse, wl.scale, wl.causal, window=wl.window, **kw)
+    args = fa.make_fwd_args(q, k, v, out, lse, wl.scale, wl.causal, window=wl.window,
+                            softcap=wl.softcap, **kw)
     fa.run_fwd(args)
     torch.cuda.synchronize()
     return out.cpu(), lse.cpu()

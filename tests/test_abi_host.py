@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(fa.EXPORTED)
-    assert lib.fa_bwd_abi_version() == 4
+    assert lib.fa_bwd_abi_version() == 5
 
 
 @pytest.mark.parametrize("header,struct,mirror", [
@@ -144,6 +144,9 @@ def test_valid_args_pass_validation():
     # without local_window the sizes are not read (a zero-filled struct has
     # no window, and causal with a positive right size is no error then)
     assert fa.validate(_with_ws(_args(causal=1, window_size_right=5))) == fa.FA_OK
+    # soft cap: any finite positive value, 0 = off
+    for cap in (0.0, 1e-30, 30.0, 1e30):
+        assert fa.validate(_with_ws(_args(softcap=cap))) == fa.FA_OK
 
 
 @pytest.mark.parametrize("over,status", [
@@ -159,6 +162,9 @@ def test_valid_args_pass_validation():
     ({"causal": 2}, fa.FA_ERR_INVALID_ARG),
     ({"causal": 1, "local_window": 1, "window_size_right": 4}, fa.FA_ERR_INVALID_ARG),
     ({"local_window": 2}, fa.FA_ERR_INVALID_ARG),
+    ({"softcap": -1.0}, fa.FA_ERR_INVALID_ARG),
+    ({"softcap": float("nan")}, fa.FA_ERR_INVALID_ARG),
+    ({"softcap": float("inf")}, fa.FA_ERR_INVALID_ARG),
     ({"seqlen_k": (1 << 29) + 1}, fa.FA_ERR_UNSUPPORTED),
     ({"softmax_scale": float("nan")}, fa.FA_ERR_INVALID_ARG),
     ({"cu_seqlens_q": BASE}, fa.FA_ERR_INVALID_ARG),      # only one cu_seqlens
@@ -250,6 +256,7 @@ def test_forward_valid_args_pass_validation():
     ({"causal": 2}, fa.FA_ERR_INVALID_ARG),
     ({"local_window": 1, "window_size_right": 1}, fa.FA_ERR_INVALID_ARG),   # causal = 1
     ({"local_window": -1}, fa.FA_ERR_INVALID_ARG),
+    ({"softcap": -0.5}, fa.FA_ERR_INVALID_ARG),
     ({"seqlen_q": (1 << 29) + 1}, fa.FA_ERR_UNSUPPORTED),
     ({"softmax_scale": float("inf")}, fa.FA_ERR_INVALID_ARG),
     ({"cu_seqlens_k": BASE}, fa.FA_ERR_INVALID_ARG),

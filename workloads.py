@@ -36,6 +36,8 @@ class Workload:
     seed: int = SEED_BASE
     # local window (left, right), negative = unbounded; None: no window
     window: Optional[Tuple[int, int]] = None
+    # soft cap c > 0 of the scaled scores (c * tanh(x / c)); 0: none
+    softcap: float = 0.0
 
     @property
     def window_sizes(self) -> Tuple[int, int]:
@@ -126,18 +128,19 @@ def make_inputs(wl: Workload, lengths: Optional[List[int]] = None,
 
 def custom(name: str, batch: int, heads: int, heads_k: int, seqlen_q: int,
            seqlen_k: int, head_dim: int, causal: bool, seed: int,
-           window: Optional[Tuple[int, int]] = None) -> Workload:
+           window: Optional[Tuple[int, int]] = None, softcap: float = 0.0) -> Workload:
     """A dense workload of any shape (used for ragged / edge-case tests)."""
     return Workload(name, batch, heads, heads_k, seqlen_q, seqlen_k, head_dim,
-                    causal, seed=seed, window=window)
+                    causal, seed=seed, window=window, softcap=softcap)
 
 
 def custom_varlen(name: str, lens_q: List[int], lens_k: List[int], heads: int,
                   heads_k: int, head_dim: int, causal: bool, seed: int,
-                  dtype=torch.bfloat16, window: Optional[Tuple[int, int]] = None) -> Inputs:
+                  dtype=torch.bfloat16, window: Optional[Tuple[int, int]] = None,
+                  softcap: float = 0.0) -> Inputs:
     """Packed inputs with explicit (possibly unequal or zero) q/k lengths."""
     wl = Workload(name, len(lens_q), heads, heads_k, 0, 0, head_dim, causal,
-                  varlen=True, seed=seed, window=window)
+                  varlen=True, seed=seed, window=window, softcap=softcap)
     gen = torch.Generator(device="cpu")
     gen.manual_seed(seed)
     Tq, Tk = sum(lens_q), sum(lens_k)
