@@ -14,15 +14,24 @@
  *                  && (wl < 0 || j >= i + Lk - Lq - wl)   (local window, left)
  *   LSE_i = log sum_{visible j} exp(S_ij)                 (-inf if none visible)
  *   P_ij  = exp(S_ij - LSE_i) if visible else 0           (softmax)
- *   O_i   = sum_j P_ij V_j
+ *   M_ij  = Z_ij / (1 - p)      (dropout with probability p; 1 without)
+ *   O_i   = sum_j P_ij M_ij V_j
  *
  *   backward of f = sum(dO * O):
  *   dP_ij = sum_d dO_id V_jd
- *   dS_i  = J_i dP_i,   J_i = diag(P_i) - P_i P_i^T       (softmax Jacobian)
+ *   dS_i  = J_i (M_i * dP_i),   J_i = diag(P_i) - P_i P_i^T   (softmax Jacobian)
  *   dS_ij <- dS_ij * (1 - (S_ij / c)^2)       (softcap: d/dx c tanh(x/c))
  *   dQ_i  = scale * sum_j dS_ij K_j
  *   dK_j  = scale * sum_{h in group g} sum_i dS^(h)_ij Q^(h)_i
- *   dV_j  =         sum_{h in group g} sum_i P^(h)_ij dO^(h)_i
+ *   dV_j  =         sum_{h in group g} sum_i P^(h)_ij M^(h)_ij dO^(h)_i
+ *
+ *   Dropout keep bits Z (0 or 1) come from Philox4x32-10 (Salmon, Moraes,
+ *   Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011),
+ *   written here from that definition: for sequence b, query head h of H,
+ *   query row i and key j (local indices), the counter is
+ *   (j / 4, i, b * H + h, offset mod 2^32) and the key (seed mod 2^32,
+ *   (seed / 2^32) xor (offset / 2^32)); word j mod 4 of the output is the
+ *   element's random u, and Z = (u >= floor(p * 2^32)).
  *
  * Passages followed (page titles as listed in the design notes):
  *   - sm90 backward kernel page (FlashAttentionBackwardSm90), mma_one_m_block:
@@ -42,6 +51,14 @@
  *     define further; its softcap argument (a kernel variant switched on by
  *     softcap > 0), read as the usual logit soft-capping c * tanh(x / c) of
  *     the scaled score x, with the gradient through it by the chain rule.
+ *   - Triton FA2 teaching page, dropout_mask and the forward inner loop:
+ *     elements dropped by a Philox draw keyed by the seed, at a counter
+ *     derived from the element's position and the offset, and the kept ones
+ *     scaled by 1 / (1 - p); the page's comparison is read as the drop test
+ *     (u below p * 2^32 is dropped, so that the scale keeps the expectation),
+ *     and the counter layout above is this library's own (the page's call is
+ *     garbled).  Backward call-trace page: the backward replays the
+ *     forward's rng_state (seed, offset).
  *
  * Two backward evaluations are provided and tested against each other:
  *   oracle_backward_explicit -- materialises P, dP and each row's Jacobian
@@ -72,6 +89,80 @@
 #ifdef _OPENMP
 #include <omp.h>
 #endif
+
+/* ---- Philox4x32-10 (SC 2011 paper): ten rounds of two 32x32->64 products
+ * with the multipliers 0xD2511F53 and 0xCD9E8D57, the key bumped by the Weyl
+ * constants 0x9E3779B9 and 0xBB67AE85 between rounds. ---- */
+static void philox_round(uint32_t c[4], const uint32_t k[2])
+{
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    const uint32_t n0 = hi1 ^ c[1] ^ k[0];
+    const uint32_t n2 = hi0 ^ c[3] ^ k[1];
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+}
+
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    uint32_t c[4] = {ctr[0], ctr[1], ctr[2], ctr[3]};
+    uint32_t k[2] = {key[0], key[1]};
+    for (int r = 0; r < 10; r++) {
+        if (r > 0) {
+            k[0] += 0x9E3779B9u;
+            k[1] += 0xBB67AE85u;
+        }
+        philox_round(c, k);
+    }
+    for (int w = 0; w < 4; w++)
+        out[w] = c[w];
+}
+
+/* Dropout parameters of one call: p = 0 means none. */
+typedef struct {
+    double p;
+    uint64_t seed, offset;
+} drop_t;
+
+/* Keep bit Z of element (b, h, i, j), H query heads. */
+static int drop_keep(const drop_t *dr, int b, int h, int H, int i, int j)
+{
+    if (dr->p <= 0.0)
+        return 1;
+    const uint32_t ctr[4] = {(uint32_t)j >> 2, (uint32_t)i, (uint32_t)((int64_t)b * H + h),
+                             (uint32_t)dr->offset};
+    const uint32_t key[2] = {(uint32_t)dr->seed,
+                             (uint32_t)(dr->seed >> 32) ^ (uint32_t)(dr->offset >> 32)};
+    uint32_t out[4];
+    oracle_philox4x32_10(ctr, key, out);
+    const uint32_t thr = (uint32_t)floor(dr->p * 4294967296.0);
+    return out[j & 3] >= thr;
+}
+
+/* Dropout multiplier M_ij = Z_ij / (1 - p) (1 without dropout). */
+static double drop_mult(const drop_t *dr, int b, int h, int H, int i, int j)
+{
+    if (dr->p <= 0.0)
+        return 1.0;
+    return drop_keep(dr, b, h, H, i, j) ? 1.0 / (1.0 - dr->p) : 0.0;
+}
+
+/* The keep bits of one (sequence, head) as a [Lq][Lk] byte matrix. */
+int oracle_dropout_mask(double p, uint64_t seed, uint64_t offset, int b, int h, int H,
+                        int Lq, int Lk, uint8_t *mask)
+{
+    if (!(p >= 0.0 && p < 1.0) || Lq < 0 || Lk < 0 || H <= 0)
+        return -1;
+    const drop_t dr = {p, seed, offset};
+    for (int i = 0; i < Lq; i++)
+        for (int j = 0; j < Lk; j++)
+            mask[(size_t)i * Lk + j] = (uint8_t)drop_keep(&dr, b, h, H, i, j);
+    return 0;
+}
 
 /* Dot product over the head dimension.  Fixed summation order: four
  * interleaved partial sums (d = 0,4,8.. / 1,5,9.. / ...) added as
@@ -171,12 +262,14 @@ static int max_len(int nseq, const int64_t *cu)
 /* Forward: O and LSE for every (row, head). */
 int oracle_forward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
                    int H, int Hk, int D, double scale, int causal, int wl, int wr,
-                   double softcap, const double *mask,
+                   double softcap, double drop_p, uint64_t drop_seed, uint64_t drop_offset,
+                   const double *mask,
                    const double *q, const double *k, const double *v,
                    double *out, double *lse)
 {
-    if (check_common(nseq, cu_q, cu_k, H, Hk, D, mask))
+    if (check_common(nseq, cu_q, cu_k, H, Hk, D, mask) || !(drop_p >= 0.0 && drop_p < 1.0))
         return -1;
+    const drop_t dr = {drop_p, drop_seed, drop_offset};
     const int G = H / Hk;
     const int Lk_max = max_len(nseq, cu_k);
     const int64_t nunits = (int64_t)nseq * H;
@@ -212,7 +305,7 @@ int oracle_forward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
                 for (int j = 0; j < Lk; j++) {
                     if (s[j] == -INFINITY)
                         continue;
-                    const double p = exp(s[j] - L);
+                    const double p = exp(s[j] - L) * drop_mult(&dr, b, h, H, i, j);
                     const double *vj = v + ((k0 + j) * Hk + g) * D;
                     for (int d = 0; d < D; d++)
                         o[d] += p * vj[d];
@@ -266,14 +359,16 @@ static void group_sum(int64_t total_k, int H, int Hk, int D,
  */
 int oracle_backward_explicit(int nseq, const int64_t *cu_q, const int64_t *cu_k,
                              int H, int Hk, int D, double scale, int causal, int wl, int wr,
-                             double softcap, const double *mask,
+                             double softcap, double drop_p, uint64_t drop_seed,
+                             uint64_t drop_offset, const double *mask,
                              const double *q, const double *k, const double *v,
                              const double *dout,
                              double *dq, double *dk, double *dv,
                              double *ds_out, double *dj_out)
 {
-    if (check_common(nseq, cu_q, cu_k, H, Hk, D, mask))
+    if (check_common(nseq, cu_q, cu_k, H, Hk, D, mask) || !(drop_p >= 0.0 && drop_p < 1.0))
         return -1;
+    const drop_t dr = {drop_p, drop_seed, drop_offset};
     if (ds_out && nseq != 1)
         return -1;
     const int G = H / Hk;
@@ -322,10 +417,11 @@ int oracle_backward_explicit(int nseq, const int64_t *cu_q, const int64_t *cu_k,
                 P[(size_t)i * Lk + j] = (L == -INFINITY || sij == -INFINITY) ? 0.0 : exp(sij - L);
             }
         }
-        /* dP = dO V^T */
+        /* dP = dO V^T, times the dropout multiplier (the gradient with
+         * respect to P of O = (P * M) V) */
         for (int i = 0; i < Lq; i++)
             for (int j = 0; j < Lk; j++) {
-                dP[(size_t)i * Lk + j] = dot(DOP(i), VP(j), D);
+                dP[(size_t)i * Lk + j] = dot(DOP(i), VP(j), D) * drop_mult(&dr, b, h, H, i, j);
             }
         /* dS_i = J_i dP_i with J_i = diag(P_i) - P_i P_i^T, then through the
          * soft cap (invisible pairs have P = 0 and so dS = 0 already) */
@@ -366,7 +462,7 @@ int oracle_backward_explicit(int nseq, const int64_t *cu_q, const int64_t *cu_k,
                 double acck = 0.0, accv = 0.0;
                 for (int i = 0; i < Lq; i++) {
                     acck += dS[(size_t)i * Lk + j] * QP(i)[d];
-                    accv += P[(size_t)i * Lk + j] * DOP(i)[d];
+                    accv += P[(size_t)i * Lk + j] * drop_mult(&dr, b, h, H, i, j) * DOP(i)[d];
                 }
                 ok[d] = scale * acck;
                 ov[d] = accv;
@@ -402,14 +498,16 @@ int oracle_backward_explicit(int nseq, const int64_t *cu_q, const int64_t *cu_k,
  */
 int oracle_backward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
                     int H, int Hk, int D, double scale, int causal, int wl, int wr,
-                    double softcap, const double *mask,
+                    double softcap, double drop_p, uint64_t drop_seed, uint64_t drop_offset,
+                    const double *mask,
                     const double *q, const double *k, const double *v,
                     const double *dout,
                     double *dq, double *dk, double *dv,
                     double *dj_out, double *lse_out)
 {
-    if (check_common(nseq, cu_q, cu_k, H, Hk, D, mask))
+    if (check_common(nseq, cu_q, cu_k, H, Hk, D, mask) || !(drop_p >= 0.0 && drop_p < 1.0))
         return -1;
+    const drop_t dr = {drop_p, drop_seed, drop_offset};
     const int G = H / Hk;
     const int64_t total_q = cu_q[nseq];
     const int Lk_max = max_len(nseq, cu_k);
@@ -468,7 +566,7 @@ int oracle_backward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
                     cg[j] = cap_grad(s[j], softcap);
                     s[j] = exp(s[j] - L); /* s now holds P_ij */
                     const double *vj = v + ((k0 + j) * Hk + g) * D;
-                    dp[j] = dot(doi, vj, D);
+                    dp[j] = dot(doi, vj, D) * drop_mult(&dr, b, h, H, i, j);   /* M_ij dP_ij */
                 }
                 for (int j = 0; j < Lk; j++)
                     dj += s[j] * dp[j];
@@ -542,12 +640,13 @@ int oracle_backward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
                         if (sij == -INFINITY)
                             continue;
                         const double p = exp(sij - L);
+                        const double m = drop_mult(&dr, b, h, H, i, j);
                         const double *doi = dout + (r * H + h) * D;
-                        const double dpij = dot(doi, vj, D);
+                        const double dpij = dot(doi, vj, D) * m;
                         const double dsij = p * (dpij - DJ[r * H + h]) * cap_grad(sij, softcap);
                         for (int d = 0; d < D; d++) {
                             acck[d] += dsij * qi[d];
-                            accv[d] += p * doi[d];
+                            accv[d] += p * m * doi[d];
                         }
                     }
                     for (int d = 0; d < D; d++) {

@@ -28,7 +28,7 @@ def _lib():
         lib = ctypes.CDLL(_build.LIB)
         common = [ctypes.c_int, _i64p, _i64p, ctypes.c_int, ctypes.c_int,
                   ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                  ctypes.c_double, _dp]
+                  ctypes.c_double, ctypes.c_double, ctypes.c_uint64, ctypes.c_uint64, _dp]
         lib.oracle_forward.argtypes = common + [_dp, _dp, _dp, _dp, _dp]
         lib.oracle_backward.argtypes = common + [_dp] * 4 + [_dp] * 3 + [_dp, _dp]
         lib.oracle_backward_explicit.argtypes = common + [_dp] * 4 + [_dp] * 3 + [_dp, _dp]
@@ -37,6 +37,14 @@ def _lib():
         for f in (lib.oracle_forward, lib.oracle_backward,
                   lib.oracle_backward_explicit, lib.oracle_rowdot):
             f.restype = ctypes.c_int
+        u32p = ctypes.POINTER(ctypes.c_uint32)
+        lib.oracle_philox4x32_10.argtypes = [u32p, u32p, u32p]
+        lib.oracle_philox4x32_10.restype = None
+        lib.oracle_dropout_mask.argtypes = [ctypes.c_double, ctypes.c_uint64, ctypes.c_uint64,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int,
+                                            ctypes.POINTER(ctypes.c_uint8)]
+        lib.oracle_dropout_mask.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         _LIB = lib
@@ -73,11 +81,22 @@ def num_threads() -> int:
     return int(_lib().oracle_num_threads())
 
 
-def forward(q, k, v, cu_q, cu_k, scale, causal, mask=None, window=(-1, -1), softcap=0.0):
+def _drop(dropout):
+    """dropout = None or (p, seed, offset) -> the three C arguments."""
+    if dropout is None:
+        return 0.0, 0, 0
+    p, seed, offset = dropout
+    return float(p), int(seed) & (2**64 - 1), int(offset) & (2**64 - 1)
+
+
+def forward(q, k, v, cu_q, cu_k, scale, causal, mask=None, window=(-1, -1), softcap=0.0,
+            dropout=None):
     """Returns (out [total_q,H,D], lse [total_q,H]) in fp64.  window =
     (left, right): query i sees keys i + Lk - Lq - left .. i + Lk - Lq + right
     (a negative size leaves that side unbounded).  softcap c > 0: every
-    scaled score x becomes c * tanh(x / c) (LSE of the capped scores)."""
+    scaled score x becomes c * tanh(x / c) (LSE of the capped scores).
+    dropout = (p, seed, offset): O uses P * Z / (1 - p) with the keep bits Z
+    of dropout_mask (the LSE is that of the undropped scores)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     cu_q, cu_k = _cu(cu_q), _cu(cu_k)
     nseq, H, Hk, D = _shapes(q, k, cu_q, cu_k)
@@ -86,7 +105,7 @@ def forward(q, k, v, cu_q, cu_k, scale, causal, mask=None, window=(-1, -1), soft
     lse = np.empty(q.shape[:2], np.float64)
     rc = _lib().oracle_forward(nseq, cu_q.ctypes.data_as(_i64p), cu_k.ctypes.data_as(_i64p),
                                H, Hk, D, float(scale), int(bool(causal)), int(window[0]),
-                               int(window[1]), float(softcap), _ptr(mask),
+                               int(window[1]), float(softcap), *_drop(dropout), _ptr(mask),
                                _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse))
     if rc:
         raise RuntimeError("oracle_forward failed (%d)" % rc)
@@ -94,7 +113,7 @@ def forward(q, k, v, cu_q, cu_k, scale, causal, mask=None, window=(-1, -1), soft
 
 
 def backward(q, k, v, dout, cu_q, cu_k, scale, causal, mask=None,
-             mode="contracted", want_ds=False, window=(-1, -1), softcap=0.0):
+             mode="contracted", want_ds=False, window=(-1, -1), softcap=0.0, dropout=None):
     """Exact attention gradient in fp64.
 
     mode="contracted": any size; mode="explicit": materialised softmax
@@ -116,7 +135,7 @@ def backward(q, k, v, dout, cu_q, cu_k, scale, causal, mask=None,
     lib = _lib()
     common = (nseq, cu_q.ctypes.data_as(_i64p), cu_k.ctypes.data_as(_i64p), H, Hk, D,
               float(scale), int(bool(causal)), int(window[0]), int(window[1]), float(softcap),
-              _ptr(mask),
+              *_drop(dropout), _ptr(mask),
               _ptr(q), _ptr(k), _ptr(v),
               _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv))
     if mode == "contracted":
@@ -149,3 +168,23 @@ def rowdot(dout, out):
     if rc:
         raise RuntimeError("oracle_rowdot failed")
     return res
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 of a 4-word counter and a 2-word key -> 4 uint32 words."""
+    c = (ctypes.c_uint32 * 4)(*[int(x) & 0xFFFFFFFF for x in ctr])
+    kk = (ctypes.c_uint32 * 2)(*[int(x) & 0xFFFFFFFF for x in key])
+    out = (ctypes.c_uint32 * 4)()
+    _lib().oracle_philox4x32_10(c, kk, out)
+    return [int(x) for x in out]
+
+
+def dropout_mask(p, seed, offset, b, h, H, Lq, Lk):
+    """Keep bits (uint8 0/1, [Lq, Lk]) of sequence b, query head h of H."""
+    m = np.empty((Lq, Lk), np.uint8)
+    rc = _lib().oracle_dropout_mask(float(p), int(seed) & (2**64 - 1), int(offset) & (2**64 - 1),
+                                    int(b), int(h), int(H), int(Lq), int(Lk),
+                                    m.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)))
+    if rc:
+        raise RuntimeError("oracle_dropout_mask failed")
+    return m

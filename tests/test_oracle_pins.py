@@ -418,3 +418,95 @@ def test_capped_scores_are_bounded_by_the_cap():
     _, lse = O.forward(q, k, v, cu_q, cu_k, 1.0, True, softcap=cap)
     n = np.arange(1, 11)[:, None]
     assert np.all(np.abs(lse - np.log(n)) <= cap)
+
+
+# ---- dropout: keep bits Z from Philox4x32-10, O = (P * Z / (1 - p)) V ----
+
+def test_philox_known_answer_vectors():
+    gd = json.load(open(os.path.join(GOLDEN, "philox4x32_10_kat.json")))
+    for vec in gd["vectors"]:
+        ctr = [int(x, 16) for x in vec["ctr"]]
+        key = [int(x, 16) for x in vec["key"]]
+        assert O.philox4x32_10(ctr, key) == [int(x, 16) for x in vec["out"]]
+
+
+def test_dropout_mask_layout_and_threshold():
+    """Element (b, h, i, j): word j % 4 of Philox at counter
+    (j // 4, i, b*H + h, offset mod 2^32), key (seed lo, seed hi ^ offset hi);
+    kept iff the word is >= floor(p * 2^32)."""
+    p, seed, offset = 0.37, 0x0123456789ABCDEF, (5 << 32) + 77
+    b, h, H, Lq, Lk = 3, 2, 5, 7, 11
+    m = O.dropout_mask(p, seed, offset, b, h, H, Lq, Lk)
+    thr = int(np.floor(p * 2**32))
+    key = [seed & 0xFFFFFFFF, (seed >> 32) ^ (offset >> 32)]
+    for i in range(Lq):
+        for j in range(Lk):
+            w = O.philox4x32_10([j // 4, i, b * H + h, offset & 0xFFFFFFFF], key)[j % 4]
+            assert m[i, j] == (w >= thr)
+
+
+@pytest.mark.parametrize("p", [0.1, 0.5, 0.9])
+def test_dropout_keeps_one_minus_p(p):
+    """Kept fraction within 6 binomial standard deviations of 1 - p over 256K
+    elements, and no visible dependence between neighbouring heads."""
+    a = O.dropout_mask(p, 1234, 0, 0, 0, 2, 256, 1024).astype(np.float64)
+    b = O.dropout_mask(p, 1234, 0, 0, 1, 2, 256, 1024).astype(np.float64)
+    n = a.size
+    sd = np.sqrt(p * (1 - p) / n)
+    assert abs(a.mean() - (1 - p)) <= 6 * sd
+    corr = np.corrcoef(a.ravel(), b.ravel())[0, 1]
+    assert abs(corr) <= 6 / np.sqrt(n)
+    assert np.all(O.dropout_mask(0.0, 1234, 0, 0, 0, 2, 8, 8) == 1)
+
+
+def test_dropout_zero_is_no_dropout():
+    q, k, v, do, cu_q, cu_k = _problem(51, [6, 9], [8, 7], 4, 2, 5)
+    a = O.backward(q, k, v, do, cu_q, cu_k, 0.6, True)
+    b = O.backward(q, k, v, do, cu_q, cu_k, 0.6, True, dropout=(0.0, 99, 7))
+    for key in ("dq", "dk", "dv", "lse"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+DROP_FD_CASES = [
+    # (lens_q, lens_k, H, Hk, D, causal, window, softcap, p)
+    ([5], [7], 2, 1, 3, False, (-1, -1), 0.0, 0.3),
+    ([4, 6], [5, 6], 2, 1, 3, True, (2, 0), 0.0, 0.5),
+    ([7], [5], 2, 2, 4, True, (-1, -1), 1.1, 0.2),        # rows without keys, softcap
+]
+
+
+@pytest.mark.parametrize("case", DROP_FD_CASES)
+@pytest.mark.parametrize("mode", ["contracted", "explicit"])
+def test_dropout_gradient_matches_central_differences(case, mode):
+    """With the seed fixed the keep bits are constants, so the gradient of
+    sum(dO * O) is that of a smooth function: central differences of the
+    oracle's own dropout forward."""
+    lq, lk, H, Hk, D, causal, window, cap, p = case
+    q, k, v, do, cu_q, cu_k = _problem(52, lq, lk, H, Hk, D)
+    drop = (p, 0xDEADBEEF12345, 3)
+
+    def loss():
+        out, _ = O.forward(q, k, v, cu_q, cu_k, 0.8, causal, window=window, softcap=cap,
+                           dropout=drop)
+        return float(np.sum(do * out))
+    g = O.backward(q, k, v, do, cu_q, cu_k, 0.8, causal, mode=mode, window=window,
+                   softcap=cap, dropout=drop)
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        fd = _central_diff(x, loss)
+        err = np.abs(g[name] - fd)
+        assert np.all(err <= 1e-7 * np.maximum(1.0, np.abs(g[name]))), (name, err.max())
+
+
+def test_dropout_output_is_unbiased():
+    """E[Z / (1 - p)] = 1: averaged over 4000 offsets, O with dropout matches O
+    without within 6 standard errors of the per-element sample mean."""
+    q, k, v, do, cu_q, cu_k = _problem(53, [4], [6], 1, 1, 3)
+    ref, lse_ref = O.forward(q, k, v, cu_q, cu_k, 0.9, False)
+    outs = []
+    for off in range(4000):
+        o, lse = O.forward(q, k, v, cu_q, cu_k, 0.9, False, dropout=(0.4, 77, off))
+        assert np.array_equal(lse, lse_ref)      # the LSE ignores dropout
+        outs.append(o)
+    outs = np.array(outs)
+    se = outs.std(axis=0) / np.sqrt(len(outs))
+    assert np.all(np.abs(outs.mean(axis=0) - ref) <= 6 * se + 1e-12)
