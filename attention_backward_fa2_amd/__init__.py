@@ -49,6 +49,9 @@ class FaBwdArgs(ctypes.Structure):
         ("window_size_left", ctypes.c_int32),
         ("window_size_right", ctypes.c_int32),
         ("softcap", ctypes.c_float),
+        ("dropout_p", ctypes.c_float),
+        ("philox_seed", ctypes.c_uint64),
+        ("philox_offset", ctypes.c_uint64),
         ("deterministic", ctypes.c_int32),
         ("dq_accumulate", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
@@ -91,6 +94,9 @@ class FaFwdArgs(ctypes.Structure):
         ("window_size_left", ctypes.c_int32),
         ("window_size_right", ctypes.c_int32),
         ("softcap", ctypes.c_float),
+        ("dropout_p", ctypes.c_float),
+        ("philox_seed", ctypes.c_uint64),
+        ("philox_offset", ctypes.c_uint64),
     ]
 
 
@@ -174,10 +180,20 @@ def _set_window(a, window):
         a.window_size_left, a.window_size_right = int(window[0]), int(window[1])
 
 
+def _set_dropout(a, dropout):
+    """dropout = None or (p, seed, offset): the forward's rng state."""
+    if dropout is None:
+        a.dropout_p, a.philox_seed, a.philox_offset = 0.0, 0, 0
+    else:
+        p, seed, offset = dropout
+        a.dropout_p = float(p)
+        a.philox_seed, a.philox_offset = int(seed) & (2**64 - 1), int(offset) & (2**64 - 1)
+
+
 def make_args(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
               cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
               max_seqlen_k=None, deterministic=False, workspace=None,
-              dq_accumulate=False, window=None, softcap=0.0) -> FaBwdArgs:
+              dq_accumulate=False, window=None, softcap=0.0, dropout=None) -> FaBwdArgs:
     """Fill fa_bwd_args from tensors.  Dense tensors are (B, S, H, D); packed
     ones (total, H, D) with int32 device cu_seqlens and host max lengths.
     dq_accumulate=False: dQ by the separate query-tile pass (default);
@@ -213,6 +229,7 @@ def make_args(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
     a.causal = int(bool(causal))
     _set_window(a, window)
     a.softcap = float(softcap)
+    _set_dropout(a, dropout)
     a.deterministic = int(bool(deterministic))
     a.dq_accumulate = int(bool(dq_accumulate))
     if workspace is not None:
@@ -270,7 +287,7 @@ def run(args: FaBwdArgs, step: str = "all", stream=None):
 def fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
            cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
            deterministic=False, workspace=None, stream=None, dq_accumulate=False,
-           window=None, softcap=0.0):
+           window=None, softcap=0.0, dropout=None):
     """dQ, dK, dV of attention, written into dq, dk, dv (same layouts as q, k, v).
 
     lse is the forward's natural-log log-sum-exp, (B, H, Sq) fp32 (packed:
@@ -278,7 +295,7 @@ def fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
     holds the fp32 dQ accumulator and the row sums afterwards)."""
     args = make_args(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
                      cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                     deterministic, workspace, dq_accumulate, window, softcap)
+                     deterministic, workspace, dq_accumulate, window, softcap, dropout)
     if workspace is None:
         workspace = alloc_workspace(args, q.device)
     run(args, "all", stream)
@@ -287,7 +304,7 @@ def fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
 
 def make_fwd_args(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q=None,
                   cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
-                  window=None, softcap=0.0) -> FaFwdArgs:
+                  window=None, softcap=0.0, dropout=None) -> FaFwdArgs:
     """Fill fa_fwd_args from tensors (layouts as in make_args)."""
     varlen = cu_seqlens_q is not None or cu_seqlens_k is not None
     a = FaFwdArgs()
@@ -316,6 +333,7 @@ def make_fwd_args(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q=None,
     a.causal = int(bool(causal))
     _set_window(a, window)
     a.softcap = float(softcap)
+    _set_dropout(a, dropout)
     return a
 
 
@@ -329,9 +347,10 @@ def run_fwd(args: FaFwdArgs, stream=None):
 
 
 def fa_fwd(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q=None, cu_seqlens_k=None,
-           max_seqlen_q=None, max_seqlen_k=None, stream=None, window=None, softcap=0.0):
+           max_seqlen_q=None, max_seqlen_k=None, stream=None, window=None, softcap=0.0,
+           dropout=None):
     """O and the natural-log LSE of attention, written into out (layout of q)
     and lse ((B, H, Sq) fp32; packed: (num_seqs, H, max_seqlen_q))."""
     args = make_fwd_args(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q, cu_seqlens_k,
-                         max_seqlen_q, max_seqlen_k, window, softcap)
+                         max_seqlen_q, max_seqlen_k, window, softcap, dropout)
     run_fwd(args, stream)

@@ -56,6 +56,16 @@ void set_softcap(fa::Params &p, float c)
     p.cap_out = c > 0.f ? (float)((double)c * log2e) : 0.f;
 }
 
+void set_dropout(fa::Params &p, float drop_p, uint64_t seed, uint64_t offset)
+{
+    p.drop_p = drop_p;
+    p.drop_inv = drop_p > 0.f ? (float)(1.0 / (1.0 - (double)drop_p)) : 1.f;
+    p.drop_thr = (uint32_t)std::floor((double)drop_p * 4294967296.0);
+    p.drop_k0 = (uint32_t)seed;
+    p.drop_k1 = (uint32_t)(seed >> 32) ^ (uint32_t)(offset >> 32);
+    p.drop_c3 = (uint32_t)offset;
+}
+
 void set_window(fa::Params &p, int causal, int left, int right)
 {
     p.win_l = left < 0 ? -1 : std::min(left, kMaxSeqlen);
@@ -160,6 +170,8 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
         return fail(FA_ERR_INVALID_ARG, "softmax_scale is not finite");
     if (!(a->softcap >= 0.f) || std::isinf(a->softcap))
         return fail(FA_ERR_INVALID_ARG, "softcap must be finite and >= 0");
+    if (!(a->dropout_p >= 0.f && a->dropout_p < 1.f))
+        return fail(FA_ERR_INVALID_ARG, "dropout_p must lie in [0, 1)");
     if ((a->causal != 0 && a->causal != 1) || (a->deterministic != 0 && a->deterministic != 1) ||
         (a->dq_accumulate != 0 && a->dq_accumulate != 1))
         return fail(FA_ERR_INVALID_ARG, "causal, deterministic and dq_accumulate must be 0 or 1");
@@ -208,6 +220,7 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
     p.scale = a->softmax_scale;
     p.scale_log2 = (float)((double)a->softmax_scale * 1.4426950408889634);
     set_softcap(p, a->softcap);
+    set_dropout(p, a->dropout_p, a->philox_seed, a->philox_offset);
     p.causal = a->causal;
     set_window(p, a->causal, a->local_window ? a->window_size_left : -1,
                a->local_window ? a->window_size_right : -1);
@@ -355,6 +368,8 @@ fa_status make_fwd_plan(const fa_fwd_args *a, fa::Params *pp, int *dpad_out)
         return fail(FA_ERR_INVALID_ARG, "softmax_scale is not finite");
     if (!(a->softcap >= 0.f) || std::isinf(a->softcap))
         return fail(FA_ERR_INVALID_ARG, "softcap must be finite and >= 0");
+    if (!(a->dropout_p >= 0.f && a->dropout_p < 1.f))
+        return fail(FA_ERR_INVALID_ARG, "dropout_p must lie in [0, 1)");
     if (a->causal != 0 && a->causal != 1)
         return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
     if (a->local_window != 0 && a->local_window != 1)
@@ -392,6 +407,7 @@ fa_status make_fwd_plan(const fa_fwd_args *a, fa::Params *pp, int *dpad_out)
     p.scale = a->softmax_scale;
     p.scale_log2 = (float)((double)a->softmax_scale * 1.4426950408889634);
     set_softcap(p, a->softcap);
+    set_dropout(p, a->dropout_p, a->philox_seed, a->philox_offset);
     p.causal = a->causal;
     set_window(p, a->causal, a->local_window ? a->window_size_left : -1,
                a->local_window ? a->window_size_right : -1);

@@ -37,6 +37,11 @@
 //
 // LDS (D_pad = 128): 3 x (K, V) x 16 KB = 96 KB.
 #include "fa_mfma.h"
+#include "fa_philox.h"
+
+#ifndef FA_TU_DROPOUT
+#define FA_TU_DROPOUT 0
+#endif
 
 namespace fa {
 
@@ -58,8 +63,9 @@ struct __attribute__((aligned(16))) DqSmem {
 
 // LOCAL: a left window bounds the visible keys from below (win_l >= 0);
 // otherwise win_l < 0 and only the upper bound (causal / right window / key
-// end) is masked.  SOFTCAP: scores soft-capped (softcap > 0).
-template <int DP, bool F16, bool LOCAL, bool SOFTCAP>
+// end) is masked.  SOFTCAP: scores soft-capped (softcap > 0).  DROP:
+// dropout replayed from the forward's rng state (drop_p > 0).
+template <int DP, bool F16, bool LOCAL, bool SOFTCAP, bool DROP>
 __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
 {
     constexpr int KS = DP / 16;                  // k-steps over the head dim
@@ -98,6 +104,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
     const int off = Lk - Lq;
     const int qrow = q0 + 32 * w + l32;          // this lane's query row
     const bool qok = qrow < Lq;
+    const uint32_t drop_c2 = (uint32_t)(b * p.H + h);   // Philox counter word 2
 
     // Key tiles t_lo .. nkt-1 hold the keys visible to some row of this
     // query tile (rows q0 .. q_last see keys k_lo .. k_hi at most).
@@ -336,6 +343,9 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
 
             f32x16 st[2], dpt[2];
             const f32x16 z = {};
+            // dropout keep bits of the tile: bit 16*mb + 4*r4 + tt for the
+            // lane's row and key 32*mb + 8*r4 + 4*g2 + tt
+            uint32_t kw = 0;
             e16x4 dh[4];
             e16x8 dsa[4];
             f32x4 dv;
@@ -356,7 +366,15 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                     constexpr int ke = 32 * mb + 8 * r4 + tt;
                     x = ke <= kthr && (!LOCAL || ke >= kthr_lo) ? x : 0.f;
                 }
-                float d = SOFTCAP ? x * cg * -dpt[mb][e] : x * -dpt[mb][e];   // dpt: rowdot - dP
+                // dpt holds rowdot - dP; with dropout dS = P (M dP - rowdot)
+                float d;
+                if constexpr (DROP) {
+                    const float zi = keep_mult(kw, 16 * mb + 4 * r4 + tt, p.drop_inv);
+                    const float rd_ = rdt[e];
+                    d = x * cg * fmaf(zi, rd_ - dpt[mb][e], -rd_);
+                } else {
+                    d = SOFTCAP ? x * cg * -dpt[mb][e] : x * -dpt[mb][e];
+                }
                 keep_here(d);
                 dv[tt] = d;
                 if constexpr (tt == 3) {
@@ -366,6 +384,17 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                 }
             };
 
+            // one Philox call: keys 4 (8*mb + 2*r4 + g2) .. +3 of the lane's
+            // row (row and half from the lane index: no register holds
+            // them across the loop)
+            auto drop_call = [&](auto cc) {
+                constexpr int c = decltype(cc)::value, mb = c >> 2, r4 = c & 3;
+                const int ln = lane_here();
+                const uint32_t c0 = (uint32_t)(n0 >> 2) + 8 * mb + 2 * r4 + (ln >> 5);
+                const uint32_t row = (uint32_t)(r0w + (ln & 31));
+                kw |= keep_nibble(c0, row, drop_c2, p) << (16 * mb + 4 * r4);
+            };
+
             static_for<NSLOT>([&](auto ic) {
                 constexpr int i = decltype(ic)::value;
                 const e16x8 a = ring[i % RA];
@@ -373,6 +402,14 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                     ring[i % RA] = op_read(IC<i + RA>{});
                 else
                     ring[i % RA] = op_read(IC<i + RA - NSLOT>{});   // next tile
+                // Philox calls: block 0's over its S^T / dP^T slots, block 1's
+                // over the next NB slots (before each block's dS)
+                if constexpr (DROP && i < 2 * NB)
+                    static_for<4>([&](auto rc) {
+                        constexpr int r4 = decltype(rc)::value;
+                        if constexpr ((i % NB) == r4 * NB / 4)
+                            drop_call(IC<4 * (i / NB) + r4>{});
+                    });
                 if constexpr (i < 2 * NB) {
                     constexpr int mb = i / NB, jj = i % NB, ks = jj >> 1;
                     if constexpr ((jj & 1) != 0) {
@@ -458,7 +495,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
     }
 }
 
-template <bool LOCAL, bool SOFTCAP>
+template <bool LOCAL, bool SOFTCAP, bool DROP>
 static hipError_t launch_dq_t(const Params &p, int dpad, hipStream_t st)
 {
     const int nqt = (p.Sq + kDqRows - 1) / kDqRows;
@@ -467,21 +504,21 @@ static hipError_t launch_dq_t(const Params &p, int dpad, hipStream_t st)
     switch (dpad) {
     case 64:
         if (p.f16)
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<64, true, LOCAL, SOFTCAP>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<64, true, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
         else
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<64, false, LOCAL, SOFTCAP>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<64, false, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
         break;
     case 96:
         if (p.f16)
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<96, true, LOCAL, SOFTCAP>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<96, true, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
         else
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<96, false, LOCAL, SOFTCAP>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<96, false, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
         break;
     case 128:
         if (p.f16)
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<128, true, LOCAL, SOFTCAP>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<128, true, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
         else
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<128, false, LOCAL, SOFTCAP>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_bwd_dq_kernel<128, false, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
         break;
     default:
         return hipErrorInvalidValue;
@@ -489,13 +526,28 @@ static hipError_t launch_dq_t(const Params &p, int dpad, hipStream_t st)
     return hipGetLastError();
 }
 
-hipError_t launch_dq(const Params &p, int dpad, hipStream_t st)
+// The dropout instantiations build in a translation unit of their own
+// (fa_dq_dropout.hip includes this file with FA_TU_DROPOUT = 1), so that the
+// two halves compile in parallel.
+template <bool DROP>
+hipError_t launch_dq_v(const Params &p, int dpad, hipStream_t st)
 {
     if (p.softcap > 0.f)
-        return p.win_l >= 0 ? launch_dq_t<true, true>(p, dpad, st)
-                            : launch_dq_t<false, true>(p, dpad, st);
-    return p.win_l >= 0 ? launch_dq_t<true, false>(p, dpad, st)
-                        : launch_dq_t<false, false>(p, dpad, st);
+        return p.win_l >= 0 ? launch_dq_t<true, true, DROP>(p, dpad, st)
+                            : launch_dq_t<false, true, DROP>(p, dpad, st);
+    return p.win_l >= 0 ? launch_dq_t<true, false, DROP>(p, dpad, st)
+                        : launch_dq_t<false, false, DROP>(p, dpad, st);
 }
+
+#if FA_TU_DROPOUT
+template hipError_t launch_dq_v<true>(const Params &, int, hipStream_t);
+#else
+extern template hipError_t launch_dq_v<true>(const Params &, int, hipStream_t);
+
+hipError_t launch_dq(const Params &p, int dpad, hipStream_t st)
+{
+    return p.drop_p > 0.f ? launch_dq_v<true>(p, dpad, st) : launch_dq_v<false>(p, dpad, st);
+}
+#endif
 
 }  // namespace fa

@@ -35,6 +35,11 @@
 // 0-31), then the O^T k-steps, with P of keys 0-31 formed before them and P
 // of keys 32-63 alongside the first half.
 #include "fa_mfma.h"
+#include "fa_philox.h"
+
+#ifndef FA_TU_DROPOUT
+#define FA_TU_DROPOUT 0
+#endif
 
 namespace fa {
 
@@ -56,8 +61,8 @@ struct __attribute__((aligned(16))) FwdSmem {
 
 // LOCAL: a left window bounds the visible keys from below (win_l >= 0);
 // otherwise win_l < 0 and only the upper bound is masked.  SOFTCAP: scores
-// soft-capped (softcap > 0).
-template <int DP, bool F16, bool LOCAL, bool SOFTCAP>
+// soft-capped (softcap > 0).  DROP: dropout on P for O (drop_p > 0).
+template <int DP, bool F16, bool LOCAL, bool SOFTCAP, bool DROP>
 __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
 {
     constexpr int KS = DP / 16;                  // k-steps over the head dim
@@ -92,6 +97,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
     const int off = Lk - Lq;                     // bottom-right alignment offset
     const int qrow = q0 + 32 * w + l32;          // this lane's query row
     const bool qok = qrow < Lq;
+    const uint32_t drop_c2 = (uint32_t)(b * p.H + h);   // Philox counter word 2
 
     // Key tiles t_lo .. nkt-1 hold the keys visible to some row of this
     // query tile (rows q0 .. q_last see keys k_lo .. k_hi at most).
@@ -250,6 +256,9 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
 
             f32x16 st[2];
             const f32x16 z = {};
+            // dropout keep bits of the tile: bit 16*mb + 4*r4 + tt for the
+            // lane's row and key 32*mb + 8*r4 + 4*g2 + tt
+            uint32_t kw = 0;
             float mx0 = -INFINITY, mx1 = -INFINITY;   // raw-score maxima of the two blocks
             float mu = 0.f;                           // maximum used for P (base 2)
             e16x4 ph[4];
@@ -285,8 +294,11 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
                 if constexpr (MASK)
                     x = visible(mbc, ec) ? x : 0.f;
                 keep_here(x);
-                lsum += x;
-                pv[tt] = x;
+                lsum += x;   // the normaliser ignores dropout
+                if constexpr (DROP)
+                    pv[tt] = x * keep_mult(kw, 16 * mb + 4 * r4 + tt, p.drop_inv);
+                else
+                    pv[tt] = x;
                 if constexpr (tt == 3) {
                     ph[r4] = to_elem<F16>(pv);
                     if constexpr ((r4 & 1) != 0)
@@ -294,9 +306,23 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
                 }
             };
 
+            // one Philox call: keys 4 (8*mb + 2*r4 + g2) .. +3 of the lane's row
+            auto drop_call = [&](auto cc) {
+                constexpr int c = decltype(cc)::value, mb = c >> 2, r4 = c & 3;
+                const uint32_t c0 = (uint32_t)(n0 >> 2) + 8 * mb + 2 * r4 + g2;
+                kw |= keep_nibble(c0, (uint32_t)qrow, drop_c2, p) << (16 * mb + 4 * r4);
+            };
+
             static_for<NSLOT>([&](auto ic) {
                 constexpr int i = decltype(ic)::value;
                 const e16x8 a = ring[i % RA];
+                // the eight Philox calls of the tile over the S^T slots,
+                // before the first P
+                if constexpr (DROP && i < 2 * NB - 1)
+                    static_for<8>([&](auto cc) {
+                        if constexpr (decltype(cc)::value * (2 * NB - 1) / 8 == i)
+                            drop_call(cc);
+                    });
                 if constexpr (i + RA < NSLOT)
                     ring[i % RA] = op_read(IC<i + RA>{});
                 else
@@ -409,7 +435,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
     }
 }
 
-template <bool LOCAL, bool SOFTCAP>
+template <bool LOCAL, bool SOFTCAP, bool DROP>
 static hipError_t launch_fwd_t(const Params &p, int dpad, hipStream_t st)
 {
     const int nqt = (p.Sq + kFwdRows - 1) / kFwdRows;
@@ -418,21 +444,21 @@ static hipError_t launch_fwd_t(const Params &p, int dpad, hipStream_t st)
     switch (dpad) {
     case 64:
         if (p.f16)
-            hipLaunchKernelGGL((fa_fwd_kernel<64, true, LOCAL, SOFTCAP>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_fwd_kernel<64, true, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
         else
-            hipLaunchKernelGGL((fa_fwd_kernel<64, false, LOCAL, SOFTCAP>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_fwd_kernel<64, false, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
         break;
     case 96:
         if (p.f16)
-            hipLaunchKernelGGL((fa_fwd_kernel<96, true, LOCAL, SOFTCAP>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_fwd_kernel<96, true, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
         else
-            hipLaunchKernelGGL((fa_fwd_kernel<96, false, LOCAL, SOFTCAP>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_fwd_kernel<96, false, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
         break;
     case 128:
         if (p.f16)
-            hipLaunchKernelGGL((fa_fwd_kernel<128, true, LOCAL, SOFTCAP>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_fwd_kernel<128, true, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
         else
-            hipLaunchKernelGGL((fa_fwd_kernel<128, false, LOCAL, SOFTCAP>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((fa_fwd_kernel<128, false, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
         break;
     default:
         return hipErrorInvalidValue;
@@ -440,13 +466,28 @@ static hipError_t launch_fwd_t(const Params &p, int dpad, hipStream_t st)
     return hipGetLastError();
 }
 
-hipError_t launch_fwd(const Params &p, int dpad, hipStream_t st)
+// The dropout instantiations build in a translation unit of their own
+// (fa_fwd_dropout.hip includes this file with FA_TU_DROPOUT = 1), so that
+// the two halves compile in parallel.
+template <bool DROP>
+hipError_t launch_fwd_v(const Params &p, int dpad, hipStream_t st)
 {
     if (p.softcap > 0.f)
-        return p.win_l >= 0 ? launch_fwd_t<true, true>(p, dpad, st)
-                            : launch_fwd_t<false, true>(p, dpad, st);
-    return p.win_l >= 0 ? launch_fwd_t<true, false>(p, dpad, st)
-                        : launch_fwd_t<false, false>(p, dpad, st);
+        return p.win_l >= 0 ? launch_fwd_t<true, true, DROP>(p, dpad, st)
+                            : launch_fwd_t<false, true, DROP>(p, dpad, st);
+    return p.win_l >= 0 ? launch_fwd_t<true, false, DROP>(p, dpad, st)
+                        : launch_fwd_t<false, false, DROP>(p, dpad, st);
 }
+
+#if FA_TU_DROPOUT
+template hipError_t launch_fwd_v<true>(const Params &, int, hipStream_t);
+#else
+extern template hipError_t launch_fwd_v<true>(const Params &, int, hipStream_t);
+
+hipError_t launch_fwd(const Params &p, int dpad, hipStream_t st)
+{
+    return p.drop_p > 0.f ? launch_fwd_v<true>(p, dpad, st) : launch_fwd_v<false>(p, dpad, st);
+}
+#endif
 
 }  // namespace fa

@@ -61,6 +61,11 @@ struct Params {
     // q.k, tanh(s * scale / c) = 1 - 2 / (exp2(s * cap_in) + 1) and the capped
     // score in base 2 is tanh * cap_out.
     float softcap, cap_in, cap_out;
+    // Dropout (drop_p > 0): an element is kept iff its Philox word is >=
+    // drop_thr; kept values are scaled by drop_inv = 1 / (1 - p).  Key
+    // (drop_k0, drop_k1), last counter word drop_c3.
+    float drop_p, drop_inv;
+    uint32_t drop_thr, drop_k0, drop_k1, drop_c3;
     int fused_dq;       // 1: dQ partials added into dq_acc by the key-tile kernel
     int f16;            // 1: fp16 elements, 0: bf16
 };
@@ -125,7 +130,6 @@ __device__ inline float elem2f(uint16_t x)
 
 // Host-side launchers (one translation unit each).
 hipError_t launch_preprocess(const Params &p, int dpad, hipStream_t st);
-hipError_t launch_main_softcap(const Params &p, int dpad, hipStream_t st);
 hipError_t launch_main(const Params &p, int dpad, hipStream_t st);
 hipError_t launch_convert(const Params &p, int dpad, hipStream_t st);
 hipError_t launch_dq(const Params &p, int dpad, hipStream_t st);

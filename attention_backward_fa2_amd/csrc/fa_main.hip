@@ -47,6 +47,14 @@
 #include <type_traits>
 
 #include "fa_mfma.h"
+#include "fa_philox.h"
+
+#ifndef FA_TU_SOFTCAP
+#define FA_TU_SOFTCAP 0
+#endif
+#ifndef FA_TU_DROPOUT
+#define FA_TU_DROPOUT 0
+#endif
 
 namespace fa {
 
@@ -190,8 +198,9 @@ __device__ inline void dq_partial(const Params &p, FusedSmem<DP> &sm, int buf, i
 
 // LOCAL: a left window bounds the visible keys from below (win_l >= 0);
 // otherwise win_l < 0 and only the upper bound is masked.  SOFTCAP: scores
-// soft-capped (softcap > 0).
-template <int DP, bool FUSED, bool F16, bool LOCAL, bool SOFTCAP>
+// soft-capped (softcap > 0).  DROP: dropout replayed from the forward's rng
+// state (drop_p > 0).
+template <int DP, bool FUSED, bool F16, bool LOCAL, bool SOFTCAP, bool DROP>
 __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
 {
     constexpr int KS = DP / 16;       // MFMA k-steps over the head dim
@@ -525,7 +534,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         int cur = 0;
         // One query tile, with (IC<1>) or without (IC<0>) the element mask
         // (the same slots otherwise).
-        auto tile = [&](int it, int m, auto maskc) {
+        auto tile = [&](int it, int m, int hh, auto maskc) {
             if constexpr (FUSED)
                 issue(cur ^ 1);
             const int q0 = m * kQTile;
@@ -544,6 +553,9 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             const int delta = cur == NBUF - 1 ? -(NBUF - 1) * BUFB : BUFB;
 
             f32x16 s[2], dp[2];
+            // dropout keep bits of the tile: bit 16*mb + 4*t + r4 for the
+            // lane's key and row 32*mb + 8*r4 + 4*g2 + t
+            uint32_t kw = 0;
             e16x8 pb[4], dsb[4];
             e16x4 ph[4], dh[4];
             f32x4 l2v[4];
@@ -566,10 +578,20 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 }
                 if constexpr (decltype(maskc)::value)
                     x = qc + t >= limv && (!LOCAL || qc + t <= limu) ? x : 0.f;
-                float d = SOFTCAP ? x * cg * -dp[mb][e] : x * -dp[mb][e];   // dp: rowdot - dP
-                keep_here(x);
+                // dp holds rowdot - dP; with dropout dV takes P M and
+                // dS = P (M dP - rowdot), M = keep / (1 - p)
+                float d, pm = x;
+                if constexpr (DROP) {
+                    const float zi = keep_mult(kw, 16 * mb + 4 * t + r4, p.drop_inv);
+                    const float rd_ = rdc[mb][e];
+                    d = x * cg * fmaf(zi, rd_ - dp[mb][e], -rd_);
+                    pm = x * zi;
+                } else {
+                    d = SOFTCAP ? x * cg * -dp[mb][e] : x * -dp[mb][e];
+                }
+                keep_here(pm);
                 keep_here(d);
-                pv[t] = x;
+                pv[t] = pm;
                 dv[t] = d;
                 if constexpr (t == 3) {
                     ph[r4] = to_elem<F16>(pv);
@@ -583,6 +605,26 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 }
             };
 
+            // One Philox call per (block, 4-row group): lane a of each lane
+            // quad (four consecutive keys) draws row 4*g2 + a of the group
+            // for the quad's four keys; the quad then trades the nibbles so
+            // that every lane holds its own key's bits for the four rows.
+            auto drop_call = [&](auto cc) {
+                constexpr int c = decltype(cc)::value, mb = c >> 2, r4 = c & 3;
+                const int a = l32 & 3;
+                const uint32_t row = (uint32_t)(q0 + 32 * mb + 8 * r4 + 4 * g2 + a);
+                const uint32_t c2 = (uint32_t)(b * p.H + hk * p.G + hh);
+                const int nib = (int)keep_nibble((uint32_t)key >> 2, row, c2, p);
+                // quad broadcasts of lanes 0..3 (quad_perm [t, t, t, t])
+                const uint32_t q0n = (uint32_t)__builtin_amdgcn_mov_dpp(nib, 0x00, 0xF, 0xF, false);
+                const uint32_t q1n = (uint32_t)__builtin_amdgcn_mov_dpp(nib, 0x55, 0xF, 0xF, false);
+                const uint32_t q2n = (uint32_t)__builtin_amdgcn_mov_dpp(nib, 0xAA, 0xF, 0xF, false);
+                const uint32_t q3n = (uint32_t)__builtin_amdgcn_mov_dpp(nib, 0xFF, 0xF, 0xF, false);
+                const uint32_t all16 = q0n | (q1n << 4) | (q2n << 8) | (q3n << 12);
+                // bit 4t: row t of the group, this lane's key
+                kw |= ((all16 >> a) & 0x1111u) << (16 * mb + r4);
+            };
+
             pin_acc();
             static_for<NSLOT>([&](auto ic) {
                 constexpr int i = decltype(ic)::value;
@@ -591,6 +633,14 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     ring[i % RA] = op_read(IC<i + RA>{});
                 else if constexpr (!FUSED)
                     ring[i % RA] = op_read(IC<i + RA - NSLOT>{});   // next tile
+                // Philox calls: block 0's over its S / dP slots, block 1's
+                // over the next NB slots (before each block's P and dS)
+                if constexpr (DROP && i < 2 * NB)
+                    static_for<4>([&](auto rc) {
+                        constexpr int r4 = decltype(rc)::value;
+                        if constexpr ((i % NB) == r4 * NB / 4)
+                            drop_call(IC<4 * (i / NB) + r4>{});
+                    });
                 // row vectors of block 0, read during the slots before its
                 // pointwise work starts
                 if constexpr (i >= NB / 2 && i < NB / 2 + 4) {
@@ -604,9 +654,12 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     constexpr int mb = i / NB, jj = i % NB, ks = jj >> 1;
                     if constexpr ((jj & 1) != 0) {
                         // dp = rowdot - dO V^T (vf holds -V)
-                        if constexpr (ks == 0)
-                            dp[mb] = rdc[mb];
-                        mfma32_vacc<F16>(dp[mb], a, vf[ks]);
+                        if constexpr (ks == 0) {
+                            dp[mb] = rdc[mb];   // a vector copy: FRESH waits for it
+                            mfma32_vacc<F16, true>(dp[mb], a, vf[ks]);
+                        } else {
+                            mfma32_vacc<F16>(dp[mb], a, vf[ks]);
+                        }
                     } else if constexpr (ks == 0) {
                         mfma32_vz<F16>(s[mb], a, kf[ks]);
                     } else {
@@ -703,7 +756,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 rv0 += delta;
                 wait_loads<0>();
                 __syncthreads();   // next tile in LDS; dS^T[cur] complete
-                const int h = hk * p.G + it / nm;
+                const int h = hk * p.G + hh;
                 const int rows_valid = min(kQTile, Lq - q0);
                 dq_partial<DP, F16>(p, sm, cur, w, lane, l32, g2, tid, b, h, m, j, q0, rows_valid, Lq,
                                off, nt_b, si.ws_row);
@@ -716,7 +769,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         };
         if constexpr (FUSED) {
             for (int it = 0; it < total; ++it)
-                tile(it, tile_m(it), IC<1>{});
+                tile(it, tile_m(it), it / nm, IC<1>{});
         } else {
             // The wave's keys kw0 .. kw_last are visible to every row of the
             // query tiles mf_lo .. mf_hi (none if a key is past the end):
@@ -744,11 +797,11 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 const int it_h = it + nh, it_u = it_h + nu, it_e = it + nm;
                 if constexpr (LOCAL)
                     for (; it < it_h; ++it, --m)
-                        tile(it, m, IC<1>{});
+                        tile(it, m, hh, IC<1>{});
                 for (; it < it_u; ++it, --m)
-                    tile(it, m, IC<0>{});
+                    tile(it, m, hh, IC<0>{});
                 for (; it < it_e; ++it, --m)
-                    tile(it, m, IC<1>{});
+                    tile(it, m, hh, IC<1>{});
             }
         }
         // The last iterations issued loads past the final tile (empty bound,
@@ -781,13 +834,14 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
     }
 }
 
-template <bool LOCAL, bool SOFTCAP>
+template <bool LOCAL, bool SOFTCAP, bool DROP>
 static hipError_t launch_main_t(const Params &p, int dpad, hipStream_t st)
 {
     const dim3 grid((unsigned)p.ntiles * p.Hk * p.batch);
     const dim3 block(kThreads);
 #define FA_LAUNCH_MAIN(D, FU, H16)                                                               \
-    hipLaunchKernelGGL((fa_bwd_main_kernel<D, FU, H16, LOCAL, SOFTCAP>), grid, block, 0, st, p)
+    hipLaunchKernelGGL((fa_bwd_main_kernel<D, FU, H16, LOCAL, SOFTCAP, DROP>), grid, block, 0,    \
+                       st, p)
 #define FA_LAUNCH_MAIN_D(D)                                                                      \
     if (p.fused_dq && p.f16)                                                                     \
         FA_LAUNCH_MAIN(D, true, true);                                                           \
@@ -815,22 +869,31 @@ static hipError_t launch_main_t(const Params &p, int dpad, hipStream_t st)
     return hipGetLastError();
 }
 
-// The soft-capped instantiations build in a translation unit of their own
-// (fa_main_softcap.hip includes this file with FA_MAIN_SOFTCAP_TU defined),
-// so that the two halves compile in parallel.
-#ifdef FA_MAIN_SOFTCAP_TU
-hipError_t launch_main_softcap(const Params &p, int dpad, hipStream_t st)
+// The (softcap, dropout) variants build in four translation units
+// (fa_main_softcap.hip, fa_main_dropout.hip and fa_main_softcap_dropout.hip
+// include this file with FA_TU_SOFTCAP / FA_TU_DROPOUT set), so that they
+// compile in parallel.
+template <bool SOFTCAP, bool DROP>
+hipError_t launch_main_v(const Params &p, int dpad, hipStream_t st)
 {
-    return p.win_l >= 0 ? launch_main_t<true, true>(p, dpad, st)
-                        : launch_main_t<false, true>(p, dpad, st);
+    return p.win_l >= 0 ? launch_main_t<true, SOFTCAP, DROP>(p, dpad, st)
+                        : launch_main_t<false, SOFTCAP, DROP>(p, dpad, st);
 }
+
+#if FA_TU_SOFTCAP || FA_TU_DROPOUT
+template hipError_t launch_main_v<FA_TU_SOFTCAP != 0, FA_TU_DROPOUT != 0>(const Params &, int,
+                                                                          hipStream_t);
 #else
+extern template hipError_t launch_main_v<true, false>(const Params &, int, hipStream_t);
+extern template hipError_t launch_main_v<false, true>(const Params &, int, hipStream_t);
+extern template hipError_t launch_main_v<true, true>(const Params &, int, hipStream_t);
+
 hipError_t launch_main(const Params &p, int dpad, hipStream_t st)
 {
-    if (p.softcap > 0.f)
-        return launch_main_softcap(p, dpad, st);
-    return p.win_l >= 0 ? launch_main_t<true, false>(p, dpad, st)
-                        : launch_main_t<false, false>(p, dpad, st);
+    const bool sc = p.softcap > 0.f, dr = p.drop_p > 0.f;
+    if (dr)
+        return sc ? launch_main_v<true, true>(p, dpad, st) : launch_main_v<false, true>(p, dpad, st);
+    return sc ? launch_main_v<true, false>(p, dpad, st) : launch_main_v<false, false>(p, dpad, st);
 }
 #endif
 

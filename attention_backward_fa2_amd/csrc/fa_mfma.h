@@ -62,9 +62,11 @@ __device__ inline f32x16 mfma32(e16x8 a, e16x8 b, f32x16 c)
 // before the vector math can read it.  These are not MFMAs to the compiler,
 // so the caller covers the hazards it would otherwise cover (gfx950,
 // 32x32x16: a vector read of the result needs 12 wait states after the last
-// product -- mfma_settle(); an accumulation chain needs none; operand A must
-// not come from a vector instruction of the two preceding wait states -- the
-// callers feed it straight from LDS reads).
+// product -- mfma_settle(); an accumulation chain needs none; no operand may
+// come from a vector instruction of the two preceding wait states -- the
+// callers feed A straight from LDS reads, and an accumulator just written by
+// vector instructions (a copied initial value) goes through mfma32_vacc
+// with FRESH, which waits those two states first).
 template <bool F16>
 __device__ inline void mfma32_vz(f32x16 &d, e16x8 a, e16x8 b)   // d = A B
 {
@@ -74,11 +76,15 @@ __device__ inline void mfma32_vz(f32x16 &d, e16x8 a, e16x8 b)   // d = A B
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
 }
 
-template <bool F16>
+template <bool F16, bool FRESH = false>
 __device__ inline void mfma32_vacc(f32x16 &d, e16x8 a, e16x8 b)   // d += A B
 {
-    if constexpr (F16)
+    if constexpr (F16 && FRESH)
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+    else if constexpr (F16)
         asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+    else if constexpr (FRESH)
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
     else
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
@@ -236,16 +242,21 @@ __device__ inline uint32_t lds_addr(const void *p)
     return (uint32_t)reinterpret_cast<uintptr_t>((const lds_void *)p);
 }
 
+// The descriptor operand may have just been written by a vector instruction
+// (the compiler restores spilled scalar registers with v_readlane), and a
+// buffer instruction must not read such a register within five wait states;
+// the compiler covers that hazard for its own loads but cannot see into these
+// statements, so each waits the five states itself.
 __device__ inline void load16_to_lds(u32x4_rsrc r, void *lds, uint32_t voffset)
 {
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset), "s"(r),
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset), "s"(r),
                  "{m0}"(lds_addr(lds))
                  : "memory");
 }
 
 __device__ inline void load4_to_lds(u32x4_rsrc r, void *lds, uint32_t voffset)
 {
-    asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voffset), "s"(r),
+    asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voffset), "s"(r),
                  "{m0}"(lds_addr(lds))
                  : "memory");
 }

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define FA_BWD_ABI_VERSION 5
+#define FA_BWD_ABI_VERSION 6
 
 typedef enum {
     FA_OK = 0,
@@ -130,7 +130,18 @@ typedef enum {
  *     softmax_scale * q.k becomes c * tanh(x / c) before the softmax, and lse
  *     must be the forward's log-sum-exp of those capped scores; the gradients
  *     pass the cap by the chain rule (factor 1 - tanh^2).  0 switches it off;
- *     a negative or non-finite value is FA_ERR_INVALID_ARG.  Rows that see no key behave as under the
+ *     a negative or non-finite value is FA_ERR_INVALID_ARG.
+ *   - dropout_p = p > 0 (mha_bwd's p_dropout and rng_state, the backward
+ *     call-trace page; the keep test of the Triton FA2 teaching page's
+ *     dropout_mask, read so that kept values scaled by 1 / (1 - p) keep the
+ *     expectation): element (i, j) of query head h of sequence b is kept iff
+ *     word j % 4 of Philox4x32-10 (Salmon et al., SC 2011) at counter
+ *     (j / 4, i, b * num_heads + h, philox_offset mod 2^32) with key
+ *     (philox_seed mod 2^32, (philox_seed / 2^32) xor (philox_offset /
+ *     2^32)) is >= floor(p * 2^32); i, j are the sequence-local row and key.
+ *     The forward's O is sum_j P_ij Z_ij / (1 - p) V_j (its lse ignores
+ *     dropout); the backward must be called with the forward's p, seed and
+ *     offset.  p outside [0, 1) or non-finite is FA_ERR_INVALID_ARG.  Rows that see no key behave as under the
  *     causal rule (dq = 0, and they add nothing to dk / dv).
  *   - lse is the NATURAL-log log-sum-exp of the scaled scores of each row,
  *     -inf for a row with no visible key (its dQ is then 0).
@@ -175,6 +186,9 @@ typedef struct fa_bwd_args {
     int32_t window_size_left;      /* local window (see Semantics); < 0: unbounded */
     int32_t window_size_right;     /* < 0: unbounded; with causal = 1 only < 0 or 0 */
     float softcap;                 /* > 0: soft-capped scores (see Semantics); 0: none */
+    float dropout_p;               /* dropout probability in [0, 1); 0: none */
+    uint64_t philox_seed;          /* the forward's rng state (see Semantics) */
+    uint64_t philox_offset;
     int32_t deterministic;         /* 0 or 1 (see Reproducibility) */
     int32_t dq_accumulate;         /* 0: separate dQ pass (default); 1: fp32 accumulator */
 

@@ -72,6 +72,9 @@ typedef struct fa_fwd_args {
     int32_t window_size_left;
     int32_t window_size_right;
     float softcap;                 /* soft-capped scores as in fa_bwd_args; 0: none */
+    float dropout_p;               /* dropout as in fa_bwd_args; 0: none */
+    uint64_t philox_seed;
+    uint64_t philox_offset;
 } fa_fwd_args;
 
 /* FA_OK if fa_fwd would accept `args`; otherwise the error it would return. */

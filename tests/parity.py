@@ -36,7 +36,8 @@ class Prepared:
         self.v64 = to64(inp.packed(inp.v))
         self.do64 = to64(inp.packed(inp.dout))
         out, lse = O.forward(self.q64, self.k64, self.v64, self.cu_q, self.cu_k, wl.scale,
-                             wl.causal, window=wl.window_sizes, softcap=wl.softcap)
+                             wl.causal, window=wl.window_sizes, softcap=wl.softcap,
+                             dropout=wl.dropout_f32)
         self.o64_exact = out                      # [total_q, H, D] fp64
         self.lse_rows = lse                       # [total_q, H] fp64
         self.o = torch.from_numpy(out).to(inp.q.dtype).reshape(inp.q.shape)
@@ -78,7 +79,7 @@ def run_gpu(pr: Prepared, deterministic=False, out_pad=0, step_split=False, dq_a
                   max_seqlen_q=max(inp.lens_q), max_seqlen_k=max(inp.lens_k))
     args = fa.make_args(do, q, k, v, o, lse, dq, dk, dv, wl.scale, wl.causal,
                         deterministic=deterministic, dq_accumulate=dq_accumulate,
-                        window=wl.window, softcap=wl.softcap, **kw)
+                        window=wl.window, softcap=wl.softcap, dropout=wl.dropout, **kw)
     ws = fa.alloc_workspace(args, dev)
     ws.fill_(0xA5)   # garbage: the preprocess must clear what it uses
     if steps is not None:
@@ -115,20 +116,23 @@ def compare(gpu: torch.Tensor, ref: np.ndarray, what: str, tol=TOL):
 def oracle_backward(pr: Prepared):
     wl = pr.inp.wl
     return O.backward(pr.q64, pr.k64, pr.v64, pr.do64, pr.cu_q, pr.cu_k, wl.scale, wl.causal,
-                      window=wl.window_sizes, softcap=wl.softcap)
+                      window=wl.window_sizes, softcap=wl.softcap, dropout=wl.dropout_f32)
 
 
 def oracle_backward_unit(pr: Prepared, s: int, g: int):
     """Exact gradients of sequence s and KV head g alone (the query heads of
     its group), as (rows_q, heads, rows_k, ref) for sampled comparisons."""
     wl = pr.inp.wl
+    # the keep bits depend on the sequence and head numbers of the whole call
+    assert wl.dropout is None, "sampled units do not renumber dropout counters"
     G = wl.heads // wl.heads_k
     heads = list(range(g * G, (g + 1) * G))
     qs, qe = pr.cu_q[s], pr.cu_q[s + 1]
     ks, ke = pr.cu_k[s], pr.cu_k[s + 1]
     ref = O.backward(pr.q64[qs:qe][:, heads], pr.k64[ks:ke][:, [g]], pr.v64[ks:ke][:, [g]],
                      pr.do64[qs:qe][:, heads], [0, qe - qs], [0, ke - ks], wl.scale,
-                     wl.causal, window=wl.window_sizes, softcap=wl.softcap)
+                     wl.causal, window=wl.window_sizes, softcap=wl.softcap,
+                     dropout=wl.dropout_f32)
     return (slice(qs, qe), heads, slice(ks, ke), ref)
 
 
@@ -149,7 +153,7 @@ def run_gpu_fwd(inp: W.Inputs):
                   cu_seqlens_k=torch.tensor(cu_np(inp.lens_k), dtype=torch.int32, device=dev),
                   max_seqlen_q=maxq, max_seqlen_k=max(inp.lens_k))
     args = fa.make_fwd_args(q, k, v, out, lse, wl.scale, wl.causal, window=wl.window,
-                            softcap=wl.softcap, **kw)
+                            softcap=wl.softcap, dropout=wl.dropout, **kw)
     fa.run_fwd(args)
     torch.cuda.synchronize()
     return out.cpu(), lse.cpu()

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(fa.EXPORTED)
-    assert lib.fa_bwd_abi_version() == 5
+    assert lib.fa_bwd_abi_version() == 6
 
 
 @pytest.mark.parametrize("header,struct,mirror", [
@@ -147,6 +147,10 @@ def test_valid_args_pass_validation():
     # soft cap: any finite positive value, 0 = off
     for cap in (0.0, 1e-30, 30.0, 1e30):
         assert fa.validate(_with_ws(_args(softcap=cap))) == fa.FA_OK
+    # dropout: p in [0, 1), any seed and offset
+    for pd in (0.0, 0.1, 0.999):
+        a = _with_ws(_args(dropout_p=pd, philox_seed=2**64 - 1, philox_offset=2**63))
+        assert fa.validate(a) == fa.FA_OK
 
 
 @pytest.mark.parametrize("over,status", [
@@ -163,6 +167,9 @@ def test_valid_args_pass_validation():
     ({"causal": 1, "local_window": 1, "window_size_right": 4}, fa.FA_ERR_INVALID_ARG),
     ({"local_window": 2}, fa.FA_ERR_INVALID_ARG),
     ({"softcap": -1.0}, fa.FA_ERR_INVALID_ARG),
+    ({"dropout_p": 1.0}, fa.FA_ERR_INVALID_ARG),
+    ({"dropout_p": -0.1}, fa.FA_ERR_INVALID_ARG),
+    ({"dropout_p": float("nan")}, fa.FA_ERR_INVALID_ARG),
     ({"softcap": float("nan")}, fa.FA_ERR_INVALID_ARG),
     ({"softcap": float("inf")}, fa.FA_ERR_INVALID_ARG),
     ({"seqlen_k": (1 << 29) + 1}, fa.FA_ERR_UNSUPPORTED),
@@ -257,6 +264,7 @@ def test_forward_valid_args_pass_validation():
     ({"local_window": 1, "window_size_right": 1}, fa.FA_ERR_INVALID_ARG),   # causal = 1
     ({"local_window": -1}, fa.FA_ERR_INVALID_ARG),
     ({"softcap": -0.5}, fa.FA_ERR_INVALID_ARG),
+    ({"dropout_p": 1.5}, fa.FA_ERR_INVALID_ARG),
     ({"seqlen_q": (1 << 29) + 1}, fa.FA_ERR_UNSUPPORTED),
     ({"softmax_scale": float("inf")}, fa.FA_ERR_INVALID_ARG),
     ({"cu_seqlens_k": BASE}, fa.FA_ERR_INVALID_ARG),

@@ -26,7 +26,8 @@ def _reference(inp):
     pk = lambda t: PT.to64(inp.packed(t))
     cu_q, cu_k = PT.cu_np(inp.lens_q), PT.cu_np(inp.lens_k)
     return O.forward(pk(inp.q), pk(inp.k), pk(inp.v), cu_q, cu_k, inp.wl.scale, inp.wl.causal,
-                     window=inp.wl.window_sizes, softcap=inp.wl.softcap)
+                     window=inp.wl.window_sizes, softcap=inp.wl.softcap,
+                     dropout=inp.wl.dropout_f32)
 
 
 def _check(inp, out, lse, what):

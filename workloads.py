@@ -38,6 +38,18 @@ class Workload:
     window: Optional[Tuple[int, int]] = None
     # soft cap c > 0 of the scaled scores (c * tanh(x / c)); 0: none
     softcap: float = 0.0
+    # dropout (p, philox seed, philox offset); None: none
+    dropout: Optional[Tuple[float, int, int]] = None
+
+    @property
+    def dropout_f32(self):
+        """dropout with p rounded to fp32, the precision of the C ABI field
+        (so that both sides draw the same keep threshold)."""
+        if self.dropout is None:
+            return None
+        import numpy as np
+        p, seed, offset = self.dropout
+        return (float(np.float32(p)), seed, offset)
 
     @property
     def window_sizes(self) -> Tuple[int, int]:
@@ -128,19 +140,21 @@ def make_inputs(wl: Workload, lengths: Optional[List[int]] = None,
 
 def custom(name: str, batch: int, heads: int, heads_k: int, seqlen_q: int,
            seqlen_k: int, head_dim: int, causal: bool, seed: int,
-           window: Optional[Tuple[int, int]] = None, softcap: float = 0.0) -> Workload:
+           window: Optional[Tuple[int, int]] = None, softcap: float = 0.0,
+           dropout: Optional[Tuple[float, int, int]] = None) -> Workload:
     """A dense workload of any shape (used for ragged / edge-case tests)."""
     return Workload(name, batch, heads, heads_k, seqlen_q, seqlen_k, head_dim,
-                    causal, seed=seed, window=window, softcap=softcap)
+                    causal, seed=seed, window=window, softcap=softcap, dropout=dropout)
 
 
 def custom_varlen(name: str, lens_q: List[int], lens_k: List[int], heads: int,
                   heads_k: int, head_dim: int, causal: bool, seed: int,
                   dtype=torch.bfloat16, window: Optional[Tuple[int, int]] = None,
-                  softcap: float = 0.0) -> Inputs:
+                  softcap: float = 0.0,
+                  dropout: Optional[Tuple[float, int, int]] = None) -> Inputs:
     """Packed inputs with explicit (possibly unequal or zero) q/k lengths."""
     wl = Workload(name, len(lens_q), heads, heads_k, 0, 0, head_dim, causal,
-                  varlen=True, seed=seed, window=window, softcap=softcap)
+                  varlen=True, seed=seed, window=window, softcap=softcap, dropout=dropout)
     gen = torch.Generator(device="cpu")
     gen.manual_seed(seed)
     Tq, Tk = sum(lens_q), sum(lens_k)
