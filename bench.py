@@ -39,7 +39,7 @@ KERNEL_SOURCES = ["attention_backward_fa2_amd/csrc/fa_main.hip",
                   "attention_backward_fa2_amd/csrc/fa_internal.h"]
 TRAFFIC_SUMMARY = "profiles/hbm_traffic_main_kernel_gqa_b2_h32_hk8_s4096_d128_causal.json"
 TRACE_SUMMARY = "profiles/kernel_trace_gqa_b2_h32_hk8_s4096_d128_causal.md"
-MAIN_KERNEL = "fa_bwd_main_kernel<128, false, false, false, false>"
+MAIN_KERNEL = "fa_bwd_main_kernel<128, false, false, false, false, false>"
 
 
 def kernel_source_hash():
@@ -307,7 +307,7 @@ def cpu_baseline(wl, units):
         do = f64(inp.dout[b][:, hs])
         t0 = time.perf_counter()
         O.backward(q, k, v, do, [0, wl.seqlen_q], [0, wl.seqlen_k], wl.scale, wl.causal,
-                   window=wl.window_sizes, softcap=wl.softcap)
+                   window=wl.window_sizes, softcap=wl.softcap, dropout=wl.dropout_f32)
         t_total += time.perf_counter() - t0
         flops += conv_flops(1, G, wl.seqlen_q, wl.seqlen_k, wl.head_dim, wl.causal, wl.window)
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(),
@@ -319,22 +319,25 @@ def cpu_baseline(wl, units):
 
 def window_suffix(wl):
     suffix = "" if wl.window is None else ", local window (%d, %d)" % tuple(wl.window)
-    return suffix + (", softcap %g" % wl.softcap if wl.softcap > 0 else "")
+    suffix += ", softcap %g" % wl.softcap if wl.softcap > 0 else ""
+    return suffix + (", dropout %g" % wl.dropout[0] if wl.dropout else "")
 
 
 def main_kernel_name(fused, wl):
     local = wl.window is not None and wl.window[0] >= 0
-    return "fa_bwd_main_kernel<128, %s, false, %s, %s>" % (
-        str(bool(fused)).lower(), str(local).lower(), str(wl.softcap > 0).lower())
+    return "fa_bwd_main_kernel<128, %s, false, %s, %s, %s>" % (
+        str(bool(fused)).lower(), str(local).lower(), str(wl.softcap > 0).lower(),
+        str(wl.dropout is not None).lower())
 
 
 def fwd_kernel_name(wl):
     local = wl.window is not None and wl.window[0] >= 0
-    return "fa_fwd_kernel<128, false, %s, %s>" % (str(local).lower(), str(wl.softcap > 0).lower())
+    return "fa_fwd_kernel<128, false, %s, %s, %s>" % (str(local).lower(), str(wl.softcap > 0).lower(),
+                                                   str(wl.dropout is not None).lower())
 
 
 FWD_METRIC = "fwd TFLOP/s (O, LSE) bf16 and % of MFMA peak, S=4096 D=128 causal GQA"
-FWD_KERNEL = "fa_fwd_kernel<128, false, false, false>"
+FWD_KERNEL = "fa_fwd_kernel<128, false, false, false, false>"
 
 
 def fwd_flops(B, H, Sq, Sk, D, causal, window=None):
@@ -359,7 +362,7 @@ def cpu_baseline_fwd(wl, units):
         v = f64(inp.v[b][:, [h // G]])
         t0 = time.perf_counter()
         O.forward(q, k, v, [0, wl.seqlen_q], [0, wl.seqlen_k], wl.scale, wl.causal,
-                  window=wl.window_sizes, softcap=wl.softcap)
+                  window=wl.window_sizes, softcap=wl.softcap, dropout=wl.dropout_f32)
         t_total += time.perf_counter() - t0
         flops += fwd_flops(1, 1, wl.seqlen_q, wl.seqlen_k, wl.head_dim, wl.causal, wl.window)
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(),
@@ -377,7 +380,7 @@ def bench_forward(args, wl, dev):
     out = torch.empty_like(q)
     lse = torch.empty(wl.batch, wl.heads, wl.seqlen_q, dtype=torch.float32, device=dev)
     a = fa.make_fwd_args(q, k, v, out, lse, wl.scale, wl.causal, window=wl.window,
-                         softcap=wl.softcap)
+                         softcap=wl.softcap, dropout=wl.dropout)
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         fa.run_fwd(a, stream)
@@ -403,7 +406,8 @@ def bench_forward(args, wl, dev):
         "config": {"workload": wl.name, "batch": B, "heads": H, "heads_k": Hk,
                    "seqlen_q": Sq, "seqlen_k": Sk, "head_dim": D, "causal": wl.causal,
                    "window": list(wl.window) if wl.window else None,
-                   "softcap": wl.softcap or None, "pass": "forward"},
+                   "softcap": wl.softcap or None,
+                   "dropout": wl.dropout[0] if wl.dropout else None, "pass": "forward"},
         "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
         "flops_per_step": flops,
         "kernel_ms": {"fwd": round(ms, 4)},
@@ -441,6 +445,8 @@ def main():
                     help="local window (negative = unbounded): times the workload with it")
     ap.add_argument("--softcap", type=float, default=0.0,
                     help="soft cap c > 0 of the scaled scores: times the workload with it")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="dropout probability p > 0: times the workload with it (fixed seed)")
     ap.add_argument("--summarize-profile", metavar="PROF_DIR",
                     help="write the profiles/ summaries from rocprofv3 outputs in PROF_DIR "
                          "(trace/, FETCH_SIZE/, WRITE_SIZE/, copy_FETCH_SIZE/, copy_WRITE_SIZE/)")
@@ -483,6 +489,10 @@ def main():
         import dataclasses
         wl = dataclasses.replace(wl, name="%s_softcap%g" % (wl.name, args.softcap),
                                  softcap=float(args.softcap))
+    if args.dropout > 0:
+        import dataclasses
+        wl = dataclasses.replace(wl, name="%s_dropout%g" % (wl.name, args.dropout),
+                                 dropout=(float(args.dropout), 0x243F6A8885A308D3, 0))
     if wl.varlen:
         print("bench.py times dense workloads only", file=sys.stderr)
         sys.exit(2)
@@ -493,11 +503,18 @@ def main():
         return
     inp = W.make_inputs(wl)
     q, k, v, do = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v, inp.dout))
-    o, lse = forward_inputs_torch(q, k, v, wl.scale, wl.causal, wl.window, wl.softcap)
+    if wl.dropout:
+        # the backward needs the dropout forward's O: this library's forward
+        o = torch.empty_like(q)
+        lse = torch.empty(wl.batch, wl.heads, wl.seqlen_q, dtype=torch.float32, device=dev)
+        fa.fa_fwd(q, k, v, o, lse, wl.scale, wl.causal, window=wl.window, softcap=wl.softcap,
+                  dropout=wl.dropout)
+    else:
+        o, lse = forward_inputs_torch(q, k, v, wl.scale, wl.causal, wl.window, wl.softcap)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     a = fa.make_args(do, q, k, v, o, lse, dq, dk, dv, wl.scale, wl.causal,
                      deterministic=args.deterministic, dq_accumulate=args.dq_accumulate,
-                     window=wl.window, softcap=wl.softcap)
+                     window=wl.window, softcap=wl.softcap, dropout=wl.dropout)
     # the steps of one backward, in the order fa_bwd enqueues them
     seq = ["preprocess", "main", "dq_convert"] if args.dq_accumulate else ["dq", "main"]
     ws = fa.alloc_workspace(a, dev)
@@ -564,6 +581,7 @@ def main():
                    "seqlen_q": Sq, "seqlen_k": Sk, "head_dim": D, "causal": wl.causal,
                    "window": list(wl.window) if wl.window else None,
                    "softcap": wl.softcap or None,
+                   "dropout": wl.dropout[0] if wl.dropout else None,
                    "dq_mode": ("ordered" if args.deterministic else "atomic")
                    if args.dq_accumulate else "separate"},
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
@@ -578,7 +596,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None if args.dq_accumulate or wl.window or wl.softcap > 0
-                     else committed_traffic(),
+                     or wl.dropout else committed_traffic(),
                      "kernel": main_kernel_name(args.dq_accumulate, wl),
                      "algorithmic_flops_per_launch": main_flops},
         "wall_s": round(wall, 3),
