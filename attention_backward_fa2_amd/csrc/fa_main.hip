@@ -476,7 +476,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         constexpr int NB = 2 * KS;            // S / dP MFMAs per query block
         constexpr int NG = 4 * DB;            // dV / dK MFMAs per two k-steps
         constexpr int NSLOT = 2 * NB + 2 * NG;
-        constexpr int RA = 4;                 // read-ahead distance (slots)
+        constexpr int RA = 8;                 // read-ahead distance (slots)
         constexpr int BAR = 2 * NB + NG / 2;  // barrier slot (non-fused)
         // The ring of in-flight operands continues across tiles, so its
         // length must divide the slot count; the barrier (and the move of
