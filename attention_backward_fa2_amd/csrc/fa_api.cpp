@@ -82,6 +82,10 @@ int pad_head_dim(int d)
         return 96;
     if (d <= 128)
         return 128;
+    if (d <= 192)
+        return 192;
+    if (d <= 256)
+        return 256;
     return 0;
 }
 
@@ -125,7 +129,7 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
                     a->head_dim);
     const int dpad = pad_head_dim(a->head_dim);
     if (!dpad)
-        return fail(FA_ERR_UNSUPPORTED, "head_dim %d > 128 is not built", a->head_dim);
+        return fail(FA_ERR_UNSUPPORTED, "head_dim %d is not built", a->head_dim);
     const bool varlen = a->cu_seqlens_q || a->cu_seqlens_k;
     if (varlen && !(a->cu_seqlens_q && a->cu_seqlens_k))
         return fail(FA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k must be given together");
@@ -175,6 +179,10 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
     if ((a->causal != 0 && a->causal != 1) || (a->deterministic != 0 && a->deterministic != 1) ||
         (a->dq_accumulate != 0 && a->dq_accumulate != 1))
         return fail(FA_ERR_INVALID_ARG, "causal, deterministic and dq_accumulate must be 0 or 1");
+    if (a->dq_accumulate && a->head_dim > 128)
+        return fail(FA_ERR_UNSUPPORTED,
+                    "dq_accumulate = 1 is built for head_dim <= 128 only (the default dQ pass "
+                    "covers head_dim %d)", a->head_dim);
     if (a->local_window != 0 && a->local_window != 1)
         return fail(FA_ERR_INVALID_ARG, "local_window must be 0 or 1");
     if (a->local_window && a->causal && a->window_size_right > 0)
@@ -336,7 +344,7 @@ fa_status make_fwd_plan(const fa_fwd_args *a, fa::Params *pp, int *dpad_out)
                     a->head_dim);
     const int dpad = pad_head_dim(a->head_dim);
     if (!dpad)
-        return fail(FA_ERR_UNSUPPORTED, "head_dim %d > 128 is not built", a->head_dim);
+        return fail(FA_ERR_UNSUPPORTED, "head_dim %d is not built", a->head_dim);
     const bool varlen = a->cu_seqlens_q || a->cu_seqlens_k;
     if (varlen && !(a->cu_seqlens_q && a->cu_seqlens_k))
         return fail(FA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k must be given together");

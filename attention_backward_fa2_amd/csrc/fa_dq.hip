@@ -45,10 +45,20 @@
 
 namespace fa {
 
-constexpr int kDqWaves = 8;                 // two waves per SIMD
-constexpr int kDqThreads = 64 * kDqWaves;
-constexpr int kDqRows = 32 * kDqWaves;      // query rows per workgroup
 constexpr int kDqKeys = 64;                 // keys per streamed tile
+
+// Workgroup shape by padded head dim: up to 128, eight waves (two per SIMD,
+// 256 rows) and three K/V buffers; at 192 and 256 a wave's Q, dO and dQ
+// fragments need all 512 registers of a SIMD, so four waves (128 rows), and
+// three 64-key K/V buffers would not fit the LDS, so two.
+template <int DP>
+struct DqShape {
+    static constexpr bool BIG = DP > 128;
+    static constexpr int WAVES = BIG ? 4 : 8;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int ROWS = 32 * WAVES;     // query rows per workgroup
+    static constexpr int NBUF = BIG ? 2 : 3;
+};
 
 template <int DP>
 struct __attribute__((aligned(16))) KVBuf {
@@ -58,7 +68,7 @@ struct __attribute__((aligned(16))) KVBuf {
 
 template <int DP>
 struct __attribute__((aligned(16))) DqSmem {
-    KVBuf<DP> buf[3];
+    KVBuf<DP> buf[DqShape<DP>::NBUF];
 };
 
 // LOCAL: a left window bounds the visible keys from below (win_l >= 0);
@@ -66,14 +76,16 @@ struct __attribute__((aligned(16))) DqSmem {
 // end) is masked.  SOFTCAP: scores soft-capped (softcap > 0).  DROP:
 // dropout replayed from the forward's rng state (drop_p > 0).
 template <int DP, bool F16, bool LOCAL, bool SOFTCAP, bool DROP>
-__global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
+__global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Params p)
 {
     constexpr int KS = DP / 16;                  // k-steps over the head dim
     constexpr int DB = DP / 32;                  // 32-wide head-dim blocks
-    constexpr int NBUF = 3;
+    constexpr int NBUF = DqShape<DP>::NBUF;
+    constexpr int WAVES = DqShape<DP>::WAVES;
+    constexpr int ROWS = DqShape<DP>::ROWS;
     using L = Tile64<DP>;
-    constexpr int PERW = L::NLOAD / kDqWaves;    // 1 KB wave loads per tensor per wave
-    static_assert(PERW >= 1 && L::NLOAD % kDqWaves == 0, "tile load split");
+    constexpr int PERW = L::NLOAD / WAVES;       // 1 KB wave loads per tensor per wave
+    static_assert(PERW >= 1 && L::NLOAD % WAVES == 0, "tile load split");
     __shared__ DqSmem<DP> sm;
 
     const int tid = threadIdx.x;
@@ -86,7 +98,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
     // heads sharing a K/V tile on one XCD of the round-robin dispatch when
     // batch * Hk is a multiple of the XCD count.
     const int nbg = p.batch * p.Hk;
-    const int nqt = (p.Sq + kDqRows - 1) / kDqRows;
+    const int nqt = (p.Sq + ROWS - 1) / ROWS;
     const int lin = blockIdx.x;
     const int bg = lin % nbg;
     const int hh = (lin / nbg) % p.G;
@@ -97,7 +109,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
     if (lin == 0 && tid < 4)
         p.flags[tid] = 0;   // the workspace flags (this pass never raises one)
     const SeqInfo si = seq_info(p, b);
-    const int q0 = mt * kDqRows;
+    const int q0 = mt * ROWS;
     if (q0 >= si.Lq)
         return;
     const int Lq = si.Lq, Lk = si.Lk;
@@ -108,7 +120,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
 
     // Key tiles t_lo .. nkt-1 hold the keys visible to some row of this
     // query tile (rows q0 .. q_last see keys k_lo .. k_hi at most).
-    const int q_last = min(q0 + kDqRows, Lq) - 1;
+    const int q_last = min(q0 + ROWS, Lq) - 1;
     const int k_lo = LOCAL ? max(0, q0 + off - p.win_l) : 0;
     const int k_hi = p.win_r >= 0 ? min(Lk - 1, q_last + off + p.win_r) : Lk - 1;
     const int t_lo = k_lo / kDqKeys;
@@ -118,14 +130,21 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
 
     // Global byte offsets of the 16-byte chunk each lane loads for wave
     // load i (LDS row pr holds tile chunk (lane % PCH) ^ swz(pr)).
-    uint32_t vok[PERW], vov[PERW];
+    // (head dims above 128: formed per load from the lane index instead, as
+    // these would hold 16 registers across the loop)
+    constexpr int NVO = DqShape<DP>::BIG ? 1 : PERW;
+    uint32_t vok[NVO], vov[NVO];
+    auto load_off = [&](int i, int ln, int ss) -> uint32_t {
+        const int pr = (w * PERW + i) * L::RPL + ln / L::PCH;
+        const int c = (ln % L::PCH) ^ swz<L::PCH>(pr);
+        return c * 8 < p.D ? (uint32_t)(pr * ss * 2 + c * 16) : kOutOfRange;
+    };
+    if constexpr (!DqShape<DP>::BIG) {
 #pragma unroll
-    for (int i = 0; i < PERW; ++i) {
-        const int pr = (w * PERW + i) * L::RPL + lane / L::PCH;
-        const int c = (lane % L::PCH) ^ swz<L::PCH>(pr);
-        const bool ok = c * 8 < p.D;
-        vok[i] = ok ? (uint32_t)(pr * (int)p.k_ss * 2 + c * 16) : kOutOfRange;
-        vov[i] = ok ? (uint32_t)(pr * (int)p.v_ss * 2 + c * 16) : kOutOfRange;
+        for (int i = 0; i < PERW; ++i) {
+            vok[i] = load_off(i, lane, (int)p.k_ss);
+            vov[i] = load_off(i, lane, (int)p.v_ss);
+        }
     }
     // Issue the loads of the next key tile into buffer bf (tiles are loaded
     // strictly in order; past the last tile: empty bound, zeros, no memory
@@ -138,7 +157,8 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
     k_next += t_lo * kstep;
     v_next += t_lo * vstep;
     auto issue = [&](int bf) {
-        keep_scalar_here(n_next, n_left, k_next, v_next);
+        if constexpr (!DqShape<DP>::BIG)   // (at 256 the pins leave no legal register class)
+            keep_scalar_here(n_next, n_left, k_next, v_next);
         const int kv = n_left > 0 ? min(kDqKeys, Lk - n_next) : 0;
         const uint32_t nk = kv ? (uint32_t)((kv - 1) * (int)p.k_ss * 2 + p.D * 2) : 0u;
         const uint32_t nv = kv ? (uint32_t)((kv - 1) * (int)p.v_ss * 2 + p.D * 2) : 0u;
@@ -148,20 +168,28 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
         --n_left;
         k_next += kstep;
         v_next += vstep;
-        keep_scalar_here(n_next, n_left, k_next, v_next);
+        if constexpr (!DqShape<DP>::BIG)   // (at 256 the pins leave no legal register class)
+            keep_scalar_here(n_next, n_left, k_next, v_next);
         KVBuf<DP> &kb = sm.buf[bf];
 #pragma unroll
         for (int i = 0; i < PERW; ++i) {
             const int ld = (w * PERW + i) * 1024;
-            load16_to_lds(rk, kb.k + ld, vok[i]);
-            load16_to_lds(rv, kb.v + ld, vov[i]);
+            if constexpr (DqShape<DP>::BIG) {
+                const int ln = lane_here();
+                load16_to_lds(rk, kb.k + ld, load_off(i, ln, (int)p.k_ss));
+                load16_to_lds(rv, kb.v + ld, load_off(i, ln, (int)p.v_ss));
+            } else {
+                load16_to_lds(rk, kb.k + ld, vok[i]);
+                load16_to_lds(rv, kb.v + ld, vov[i]);
+            }
         }
     };
-    // The first two key tiles are in flight while the row vectors below
-    // are formed.
+    // The first key tiles (two with three buffers, one with two) are in
+    // flight while the row vectors below are formed.
     if (nkt > t_lo) {
         issue(0);
-        issue(1);
+        if constexpr (NBUF == 3)
+            issue(1);
     }
 
     // ---- Q and dO rows of the lane (B operands), lse2 / rowdot ----
@@ -193,9 +221,10 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
     //      pairs the two lane halves.  The results are bit-identical. ----
     float l2 = INFINITY, rd = 0.f;
     {
-        float cs[8];
+        constexpr int NCS = KS > 8 ? KS : 8;
+        float cs[NCS];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
+        for (int ks = 0; ks < NCS; ++ks)
             cs[ks] = 0.f;
         if (qok) {
             const uint16_t *orow = p.o + row_offset(p, b, si.tok_q, qrow, p.o_sb, p.o_ss) + h * p.o_sh;
@@ -216,12 +245,21 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                 }
             }
         }
-        float a4[4];
+        float half;
+        if constexpr (KS <= 8) {
+            float a4[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            a4[ks] = cs[ks] + cs[ks ^ 4];
-        const float a2_0 = a4[0] + a4[2], a2_1 = a4[1] + a4[3];
-        const float half = a2_0 + a2_1;
+            for (int ks = 0; ks < 4; ++ks)
+                a4[ks] = cs[ks] + cs[ks ^ 4];
+            const float a2_0 = a4[0] + a4[2], a2_1 = a4[1] + a4[3];
+            half = a2_0 + a2_1;
+        } else {
+            // (no preprocess pass runs at these head dims: any fixed order)
+            half = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                half += cs[ks];
+        }
         const float sum = half + __shfl_xor(half, 32);
         if (qok) {
             const float lse = p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + qrow];
@@ -322,6 +360,10 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
         // One key tile, with (IC<1>) or without (IC<0>) the element mask (the
         // same slots otherwise).
         auto tile = [&](int t, auto maskc) {
+            // two buffers: the next tile's loads go into the buffer every
+            // wave finished with before the barrier that ended the last tile
+            if constexpr (NBUF == 2)
+                issue(__builtin_amdgcn_readfirstlane(cur ^ 1));   // (scalar: an LDS base)
             const int n0 = t * kDqKeys;
             // Masked tiles: element (32*mb + 8*r4 + t) of the lane's keys (+
             // 4*g2) is kept iff it is <= kthr and (LOCAL) >= kthr_lo (the
@@ -400,7 +442,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                 const e16x8 a = ring[i % RA];
                 if constexpr (i + RA < NSLOT)
                     ring[i % RA] = op_read(IC<i + RA>{});
-                else
+                else if constexpr (NBUF == 3)
                     ring[i % RA] = op_read(IC<i + RA - NSLOT>{});   // next tile
                 // Philox calls: block 0's over its S^T / dP^T slots, block 1's
                 // over the next NB slots (before each block's dS)
@@ -436,7 +478,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                     static_for<16 * (u + 1) / NQ - 16 * u / NQ>(
                         [&](auto ec) { pw_elem(IC<1>{}, IC<16 * u / NQ + decltype(ec)::value>{}); });
                 }
-                if constexpr (i == BAR) {
+                if constexpr (NBUF == 3 && i == BAR) {
                     // every 16-byte read of this tile is issued: move them on
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks)
@@ -448,7 +490,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                     asm volatile("" ::: "memory");
                     issue(cur == 0 ? NBUF - 1 : cur - 1);
                 }
-                if constexpr (i == NSLOT - RA - 1) {
+                if constexpr (NBUF == 3 && i == NSLOT - RA - 1) {
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
                         tq[db][0] += delta;
@@ -457,6 +499,21 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
+            if constexpr (NBUF == 2) {
+                // the next tile: its loads landed and every wave is done
+                // with this buffer; reads restart from the other one
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    gq[ks] += delta;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    tq[db][0] += delta;
+                    tq[db][1] += delta;
+                }
+                wait_loads<0>();
+                __syncthreads();
+                static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
+            }
             cur = cur == NBUF - 1 ? 0 : cur + 1;
         };
         // Masked tiles t_lo .. f_lo-1, unmasked f_lo .. f_hi-1, masked
@@ -495,34 +552,34 @@ __global__ void __launch_bounds__(kDqThreads, 1) fa_bwd_dq_kernel(Params p)
     }
 }
 
+template <int DP, bool F16, bool LOCAL, bool SOFTCAP, bool DROP>
+static void launch_dq_d(const Params &p, hipStream_t st)
+{
+    const int nqt = (p.Sq + DqShape<DP>::ROWS - 1) / DqShape<DP>::ROWS;
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<DP, F16, LOCAL, SOFTCAP, DROP>),
+                       dim3((unsigned)nqt * p.H * p.batch), dim3(DqShape<DP>::THREADS), 0, st, p);
+}
+
 template <bool LOCAL, bool SOFTCAP, bool DROP>
 static hipError_t launch_dq_t(const Params &p, int dpad, hipStream_t st)
 {
-    const int nqt = (p.Sq + kDqRows - 1) / kDqRows;
-    const dim3 grid((unsigned)nqt * p.H * p.batch);
-    const dim3 block(kDqThreads);
+#define FA_DQ_CASE(D)                                                 \
+    case D:                                                           \
+        if (p.f16)                                                    \
+            launch_dq_d<D, true, LOCAL, SOFTCAP, DROP>(p, st);        \
+        else                                                          \
+            launch_dq_d<D, false, LOCAL, SOFTCAP, DROP>(p, st);       \
+        break;
     switch (dpad) {
-    case 64:
-        if (p.f16)
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<64, true, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
-        else
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<64, false, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
-        break;
-    case 96:
-        if (p.f16)
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<96, true, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
-        else
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<96, false, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
-        break;
-    case 128:
-        if (p.f16)
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<128, true, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
-        else
-            hipLaunchKernelGGL((fa_bwd_dq_kernel<128, false, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
-        break;
+        FA_DQ_CASE(64)
+        FA_DQ_CASE(96)
+        FA_DQ_CASE(128)
+        FA_DQ_CASE(192)
+        FA_DQ_CASE(256)
     default:
         return hipErrorInvalidValue;
     }
+#undef FA_DQ_CASE
     return hipGetLastError();
 }
 

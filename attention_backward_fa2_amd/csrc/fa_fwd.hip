@@ -43,10 +43,19 @@
 
 namespace fa {
 
-constexpr int kFwdWaves = 8;                 // two waves per SIMD
-constexpr int kFwdThreads = 64 * kFwdWaves;
-constexpr int kFwdRows = 32 * kFwdWaves;     // query rows per workgroup
 constexpr int kFwdKeys = 64;                 // keys per streamed tile
+
+// Workgroup shape by padded head dim (as for the dQ kernel): up to 128,
+// eight waves (two per SIMD, 256 rows) and three K/V buffers; at 192 and
+// 256, four waves (128 rows) and two buffers.
+template <int DP>
+struct FwdShape {
+    static constexpr bool BIG = DP > 128;
+    static constexpr int WAVES = BIG ? 4 : 8;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int ROWS = 32 * WAVES;
+    static constexpr int NBUF = BIG ? 2 : 3;
+};
 
 template <int DP>
 struct __attribute__((aligned(16))) FwdKV {
@@ -56,21 +65,24 @@ struct __attribute__((aligned(16))) FwdKV {
 
 template <int DP>
 struct __attribute__((aligned(16))) FwdSmem {
-    FwdKV<DP> buf[3];
+    FwdKV<DP> buf[FwdShape<DP>::NBUF];
 };
 
 // LOCAL: a left window bounds the visible keys from below (win_l >= 0);
 // otherwise win_l < 0 and only the upper bound is masked.  SOFTCAP: scores
 // soft-capped (softcap > 0).  DROP: dropout on P for O (drop_p > 0).
 template <int DP, bool F16, bool LOCAL, bool SOFTCAP, bool DROP>
-__global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
+__global__ void __launch_bounds__(FwdShape<DP>::THREADS, 1) fa_fwd_kernel(Params p)
 {
     constexpr int KS = DP / 16;                  // k-steps over the head dim
     constexpr int DB = DP / 32;                  // 32-wide head-dim blocks
-    constexpr int NBUF = 3;
+    constexpr bool BIG = FwdShape<DP>::BIG;
+    constexpr int NBUF = FwdShape<DP>::NBUF;
+    constexpr int WAVES = FwdShape<DP>::WAVES;
+    constexpr int ROWS = FwdShape<DP>::ROWS;
     using L = Tile64<DP>;
-    constexpr int PERW = L::NLOAD / kFwdWaves;   // 1 KB wave loads per tensor per wave
-    static_assert(PERW >= 1 && L::NLOAD % kFwdWaves == 0, "tile load split");
+    constexpr int PERW = L::NLOAD / WAVES;       // 1 KB wave loads per tensor per wave
+    static_assert(PERW >= 1 && L::NLOAD % WAVES == 0, "tile load split");
     __shared__ FwdSmem<DP> sm;
 
     const int tid = threadIdx.x;
@@ -81,7 +93,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
     // (last query tile under the causal mask) first; the (batch, KV head)
     // index is the fastest.
     const int nbg = p.batch * p.Hk;
-    const int nqt = (p.Sq + kFwdRows - 1) / kFwdRows;
+    const int nqt = (p.Sq + ROWS - 1) / ROWS;
     const int lin = blockIdx.x;
     const int bg = lin % nbg;
     const int hh = (lin / nbg) % p.G;
@@ -90,7 +102,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
     const int h = hk * p.G + hh;
 
     const SeqInfo si = seq_info(p, b);
-    const int q0 = mt * kFwdRows;
+    const int q0 = mt * ROWS;
     if (q0 >= si.Lq)
         return;
     const int Lq = si.Lq, Lk = si.Lk;
@@ -101,7 +113,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
 
     // Key tiles t_lo .. nkt-1 hold the keys visible to some row of this
     // query tile (rows q0 .. q_last see keys k_lo .. k_hi at most).
-    const int q_last = min(q0 + kFwdRows, Lq) - 1;
+    const int q_last = min(q0 + ROWS, Lq) - 1;
     const int k_lo = LOCAL ? max(0, q0 + off - p.win_l) : 0;
     const int k_hi = p.win_r >= 0 ? min(Lk - 1, q_last + off + p.win_r) : Lk - 1;
     const int t_lo = k_lo / kFwdKeys;
@@ -112,14 +124,21 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
 
     // Global byte offsets of the 16-byte chunk each lane loads for wave
     // load i (LDS row pr holds tile chunk (lane % PCH) ^ swz(pr)).
-    uint32_t vok[PERW], vov[PERW];
+    // (head dims above 128: formed per load from the lane index instead, as
+    // these would hold 16 registers across the loop)
+    constexpr int NVO = BIG ? 1 : PERW;
+    uint32_t vok[NVO], vov[NVO];
+    auto load_off = [&](int i, int ln, int ss) -> uint32_t {
+        const int pr = (w * PERW + i) * L::RPL + ln / L::PCH;
+        const int c = (ln % L::PCH) ^ swz<L::PCH>(pr);
+        return c * 8 < p.D ? (uint32_t)(pr * ss * 2 + c * 16) : kOutOfRange;
+    };
+    if constexpr (!BIG) {
 #pragma unroll
-    for (int i = 0; i < PERW; ++i) {
-        const int pr = (w * PERW + i) * L::RPL + lane / L::PCH;
-        const int c = (lane % L::PCH) ^ swz<L::PCH>(pr);
-        const bool ok = c * 8 < p.D;
-        vok[i] = ok ? (uint32_t)(pr * (int)p.k_ss * 2 + c * 16) : kOutOfRange;
-        vov[i] = ok ? (uint32_t)(pr * (int)p.v_ss * 2 + c * 16) : kOutOfRange;
+        for (int i = 0; i < PERW; ++i) {
+            vok[i] = load_off(i, lane, (int)p.k_ss);
+            vov[i] = load_off(i, lane, (int)p.v_ss);
+        }
     }
     // Loads of the next key tile into buffer bf (tiles strictly in order;
     // past the last tile: empty bound, zeros, no memory access).
@@ -130,7 +149,8 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
     k_next += t_lo * kstep;
     v_next += t_lo * vstep;
     auto issue = [&](int bf) {
-        keep_scalar_here(n_next, n_left, k_next, v_next);
+        if constexpr (!BIG)   // (at 256 the pins leave no legal register class)
+            keep_scalar_here(n_next, n_left, k_next, v_next);
         const int kv = n_left > 0 ? min(kFwdKeys, Lk - n_next) : 0;
         const uint32_t nk = kv ? (uint32_t)((kv - 1) * (int)p.k_ss * 2 + p.D * 2) : 0u;
         const uint32_t nv = kv ? (uint32_t)((kv - 1) * (int)p.v_ss * 2 + p.D * 2) : 0u;
@@ -140,18 +160,26 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
         --n_left;
         k_next += kstep;
         v_next += vstep;
-        keep_scalar_here(n_next, n_left, k_next, v_next);
+        if constexpr (!BIG)   // (at 256 the pins leave no legal register class)
+            keep_scalar_here(n_next, n_left, k_next, v_next);
         FwdKV<DP> &kb = sm.buf[bf];
 #pragma unroll
         for (int i = 0; i < PERW; ++i) {
             const int ld = (w * PERW + i) * 1024;
-            load16_to_lds(rk, kb.k + ld, vok[i]);
-            load16_to_lds(rv, kb.v + ld, vov[i]);
+            if constexpr (BIG) {
+                const int ln = lane_here();
+                load16_to_lds(rk, kb.k + ld, load_off(i, ln, (int)p.k_ss));
+                load16_to_lds(rv, kb.v + ld, load_off(i, ln, (int)p.v_ss));
+            } else {
+                load16_to_lds(rk, kb.k + ld, vok[i]);
+                load16_to_lds(rv, kb.v + ld, vov[i]);
+            }
         }
     };
     if (nkt > t_lo) {
         issue(0);
-        issue(1);
+        if constexpr (NBUF == 3)
+            issue(1);
     }
 
     // ---- Q rows of the lane (B operand of S^T) ----
@@ -247,6 +275,10 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
         int cur = 0;
         auto tile = [&](int t, auto maskc) {
             constexpr bool MASK = decltype(maskc)::value != 0;
+            // two buffers: the next tile's loads go into the buffer every
+            // wave finished with before the barrier that ended the last tile
+            if constexpr (NBUF == 2)
+                issue(__builtin_amdgcn_readfirstlane(cur ^ 1));   // (scalar: an LDS base)
             const int n0 = t * kFwdKeys;
             // element (32*mb + 8*r4 + tt) of the lane's keys (+ 4*g2) is
             // visible iff it is <= kthr and (LOCAL) >= kthr_lo
@@ -325,7 +357,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
                     });
                 if constexpr (i + RA < NSLOT)
                     ring[i % RA] = op_read(IC<i + RA>{});
-                else
+                else if constexpr (NBUF == 3)
                     ring[i % RA] = op_read(IC<i + RA - NSLOT>{});   // next tile
                 if constexpr (i < 2 * NB) {
                     constexpr int mb = i / NB, ks = i % NB;
@@ -370,7 +402,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
                     static_for<16 * (u + 1) / (2 * DB) - 16 * u / (2 * DB)>(
                         [&](auto ec) { p_elem(IC<1>{}, IC<16 * u / (2 * DB) + decltype(ec)::value>{}); });
                 }
-                if constexpr (i == BAR) {
+                if constexpr (NBUF == 3 && i == BAR) {
                     // every 16-byte read of this tile is issued: move them on
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks)
@@ -382,7 +414,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
                     asm volatile("" ::: "memory");
                     issue(cur == 0 ? NBUF - 1 : cur - 1);
                 }
-                if constexpr (i == NSLOT - RA - 1) {
+                if constexpr (NBUF == 3 && i == NSLOT - RA - 1) {
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
                         tq[db][0] += delta;
@@ -391,6 +423,21 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
+            if constexpr (NBUF == 2) {
+                // the next tile: its loads landed and every wave is done
+                // with this buffer; reads restart from the other one
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    gq[ks] += delta;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    tq[db][0] += delta;
+                    tq[db][1] += delta;
+                }
+                wait_loads<0>();
+                __syncthreads();
+                static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
+            }
             cur = cur == NBUF - 1 ? 0 : cur + 1;
         };
         // Masked tiles t_lo .. f_lo-1, unmasked f_lo .. f_hi-1, masked
@@ -435,34 +482,34 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fa_fwd_kernel(Params p)
     }
 }
 
+template <int DP, bool F16, bool LOCAL, bool SOFTCAP, bool DROP>
+static void launch_fwd_d(const Params &p, hipStream_t st)
+{
+    const int nqt = (p.Sq + FwdShape<DP>::ROWS - 1) / FwdShape<DP>::ROWS;
+    hipLaunchKernelGGL((fa_fwd_kernel<DP, F16, LOCAL, SOFTCAP, DROP>),
+                       dim3((unsigned)nqt * p.H * p.batch), dim3(FwdShape<DP>::THREADS), 0, st, p);
+}
+
 template <bool LOCAL, bool SOFTCAP, bool DROP>
 static hipError_t launch_fwd_t(const Params &p, int dpad, hipStream_t st)
 {
-    const int nqt = (p.Sq + kFwdRows - 1) / kFwdRows;
-    const dim3 grid((unsigned)nqt * p.H * p.batch);
-    const dim3 block(kFwdThreads);
+#define FA_FWD_CASE(D)                                                \
+    case D:                                                           \
+        if (p.f16)                                                    \
+            launch_fwd_d<D, true, LOCAL, SOFTCAP, DROP>(p, st);       \
+        else                                                          \
+            launch_fwd_d<D, false, LOCAL, SOFTCAP, DROP>(p, st);      \
+        break;
     switch (dpad) {
-    case 64:
-        if (p.f16)
-            hipLaunchKernelGGL((fa_fwd_kernel<64, true, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
-        else
-            hipLaunchKernelGGL((fa_fwd_kernel<64, false, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
-        break;
-    case 96:
-        if (p.f16)
-            hipLaunchKernelGGL((fa_fwd_kernel<96, true, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
-        else
-            hipLaunchKernelGGL((fa_fwd_kernel<96, false, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
-        break;
-    case 128:
-        if (p.f16)
-            hipLaunchKernelGGL((fa_fwd_kernel<128, true, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
-        else
-            hipLaunchKernelGGL((fa_fwd_kernel<128, false, LOCAL, SOFTCAP, DROP>), grid, block, 0, st, p);
-        break;
+        FA_FWD_CASE(64)
+        FA_FWD_CASE(96)
+        FA_FWD_CASE(128)
+        FA_FWD_CASE(192)
+        FA_FWD_CASE(256)
     default:
         return hipErrorInvalidValue;
     }
+#undef FA_FWD_CASE
     return hipGetLastError();
 }
 

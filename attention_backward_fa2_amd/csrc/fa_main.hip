@@ -2,6 +2,7 @@
 // gfx950 (CDNA4): dK and dV, and in the fused mode also the dQ partials.
 //
 // One workgroup (4 wave64s) owns a tile of kKTile = 128 keys of one KV head
+// (64 at head dims above 128, see BIG below)
 // (KV-tile-stationary order of the sm90 backward page: grid over key blocks,
 // K and V loaded once, query tiles streamed).  It loops over every query head
 // of the KV head's group and, for each, over the 64-row query tiles that can
@@ -206,15 +207,29 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
     constexpr int KS = DP / 16;       // MFMA k-steps over the head dim
     constexpr int DB = DP / 32;       // 32-wide blocks of the head dim
     using L = Tile64<DP>;
+    // Head dims above 128: a wave's dK and dV accumulators over the whole
+    // head dim and its K, V operands would need more than a SIMD's 512
+    // registers, so each pair of waves shares 32 keys and splits the head
+    // dim of dK and dV (both recompute S and dP over the whole head dim): 64
+    // keys per workgroup.  The fused dQ modes are not built for them.
+    constexpr bool BIG = DP > 128;
+    static_assert(!(BIG && FUSED), "fused dQ for head dims above 128");
+    constexpr int KT = BIG ? 64 : kKTile;    // keys per workgroup
+    constexpr int DBL = BIG ? DB / 2 : DB;   // dK / dV head-dim blocks of a wave
     // Query-tile buffers in flight: three (loads run two tiles ahead) unless
-    // the fused mode's dS^T and K tiles leave LDS room for only two.
-    constexpr int NBUF = FUSED ? 2 : 3;
+    // the fused mode's dS^T and K tiles, or tiles of more than 128 columns,
+    // leave LDS room for only two; then each tile loads the next one at its
+    // start and waits for it at its end.
+    constexpr bool TWO = FUSED || BIG;
+    constexpr int NBUF = TWO ? 2 : 3;
     using Smem = std::conditional_t<FUSED, FusedSmem<DP>, TileSmem<DP, NBUF>>;
     __shared__ Smem sm;
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, g2 = lane >> 5;
+    const int kgrp = BIG ? w >> 1 : w;               // the wave's 32 keys
+    const int dbo = BIG ? (w & 1) * DBL : 0;         // first dK / dV head-dim block
 
     // Workgroup -> (batch, KV head, key tile).
     //  - default: longest work first.  Key tile 0 sees the most query tiles
@@ -227,7 +242,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
     //    descending order along the linear id, so every workgroup waits only
     //    on one with a lower id (which the in-order dispatch has already
     //    placed on a CU).
-    const int nt = p.ntiles;
+    const int nt = BIG ? (p.Sk + KT - 1) / KT : p.ntiles;
     const int nbg = p.batch * p.Hk;
     const int lin = blockIdx.x;
     int j, bg;
@@ -241,12 +256,12 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
     const int hk = bg % p.Hk, b = bg / p.Hk;
 
     const SeqInfo si = seq_info(p, b);
-    const int n0 = j * kKTile;
+    const int n0 = j * KT;
     if (n0 >= si.Lk)
         return;
     const int Lq = si.Lq, Lk = si.Lk;
     const int off = Lk - Lq;                // bottom-right alignment offset
-    const int key_local = w * 32 + l32;
+    const int key_local = kgrp * 32 + l32;
     const int key = n0 + key_local;
 
     // ---- K, V rows of this wave's 32 keys: B operands of S and dP; in
@@ -276,9 +291,9 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         wait_loads<0>();
     }
 
-    f32x16 dk_acc[DB], dv_acc[DB];
+    f32x16 dk_acc[DBL], dv_acc[DBL];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DBL; ++db) {
         zero(dk_acc[db]);
         zero(dv_acc[db]);
     }
@@ -287,13 +302,13 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
     // sees keys i + off - win_l .. i + off + win_r).
     const int first_q = p.win_r >= 0 ? max(0, n0 - off - p.win_r) : 0;
     const int last_q =
-        LOCAL ? min(Lq - 1, min(Lk - 1, n0 + kKTile - 1) - off + p.win_l) : Lq - 1;
+        LOCAL ? min(Lq - 1, min(Lk - 1, n0 + KT - 1) - off + p.win_l) : Lq - 1;
     if (first_q <= last_q) {
         const int m_begin = first_q / kQTile;
         const int m_end = last_q / kQTile + 1;
         const int nm = m_end - m_begin;
         const int total = p.G * nm;
-        const int nt_b = (Lk + kKTile - 1) / kKTile;
+        const int nt_b = (Lk + KT - 1) / KT;
 
         // Global byte offset of the 16-byte chunk each lane loads for wave
         // load i of this wave: LDS row pr, LDS chunk lane % PCH, which holds
@@ -320,7 +335,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         //  rv0:       lse2 / rowdot of row 4*g2.
         // All move to the next buffer (cyclically) after each tile.
         constexpr int BUFB = (int)sizeof(QBuf<DP>);
-        int gq[KS], tq[DB][2], rv0;
+        int gq[KS], tq[DBL][2], rv0;
         {
             const int sw = swz<L::PCH>(l32);
 #pragma unroll
@@ -328,12 +343,13 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 gq[ks] = l32 * L::PB + (((2 * ks + g2) ^ sw) << 4);
             const int c16 = lane & 15, rr = c16 >> 2, h16 = (lane >> 4) & 1, b1 = (c16 >> 1) & 1;
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < DBL; ++db)
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
                     const int row = 4 * g2 + rr + 8 * hf;
                     tq[db][hf] = row * L::PB +
-                                 (((4 * db + 2 * h16 + b1) ^ swz<L::PCH>(row)) << 4) + (c16 & 1) * 8;
+                                 (((4 * (dbo + db) + 2 * h16 + b1) ^ swz<L::PCH>(row)) << 4) +
+                                 (c16 & 1) * 8;
                 }
             rv0 = 2 * L::BYTES + 16 * g2;
         }
@@ -474,7 +490,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         // buffers, a buffer refilled after the barrier of tile t held tile
         // t-1, which every wave has finished by then).
         constexpr int NB = 2 * KS;            // S / dP MFMAs per query block
-        constexpr int NG = 4 * DB;            // dV / dK MFMAs per two k-steps
+        constexpr int NG = 4 * DBL;           // dV / dK MFMAs per two k-steps
         constexpr int NSLOT = 2 * NB + 2 * NG;
         constexpr int RA = 8;                 // read-ahead distance (slots)
         constexpr int BAR = 2 * NB + NG / 2;  // barrier slot (non-fused)
@@ -494,8 +510,8 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 constexpr int mb = i / NB, jj = i % NB, ks = jj >> 1;
                 return lds16b(lds + gq[ks] + 32 * mb * L::PB + ((jj & 1) ? L::BYTES : 0));
             } else {
-                constexpr int jj = (i - 2 * NB) % NG, kk = 2 * ((i - 2 * NB) / NG) + jj / (2 * DB);
-                constexpr int db = (jj % (2 * DB)) >> 1;
+                constexpr int jj = (i - 2 * NB) % NG, kk = 2 * ((i - 2 * NB) / NG) + jj / (2 * DBL);
+                constexpr int db = (jj % (2 * DBL)) >> 1;
                 constexpr int base = (jj & 1) ? 0 : L::BYTES;   // even: dO^T (dV), odd: Q^T (dK)
                 return tr_pair(lds + base + tq[db][0] + 16 * kk * L::PB,
                                lds + base + tq[db][1] + 16 * kk * L::PB);
@@ -507,7 +523,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         // tile).
         auto pin_acc = [&]() {
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < DBL; ++db)
                 asm volatile("" : "+a"(dk_acc[db]), "+a"(dv_acc[db]));
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
@@ -535,7 +551,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         // One query tile, with (IC<1>) or without (IC<0>) the element mask
         // (the same slots otherwise).
         auto tile = [&](int it, int m, int hh, auto maskc) {
-            if constexpr (FUSED)
+            if constexpr (TWO)
                 issue(cur ^ 1);
             const int q0 = m * kQTile;
             // This lane's key is visible to tile rows 4*g2 + (32*mb + 8*r4 +
@@ -631,7 +647,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 const e16x8 a = ring[i % RA];
                 if constexpr (i + RA < NSLOT)
                     ring[i % RA] = op_read(IC<i + RA>{});
-                else if constexpr (!FUSED)
+                else if constexpr (!TWO)
                     ring[i % RA] = op_read(IC<i + RA - NSLOT>{});   // next tile
                 // Philox calls: block 0's over its S / dP slots, block 1's
                 // over the next NB slots (before each block's P and dS)
@@ -667,8 +683,8 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     }
                 } else {
                     constexpr int jj = (i - 2 * NB) % NG;
-                    constexpr int kk = 2 * ((i - 2 * NB) / NG) + jj / (2 * DB);
-                    constexpr int db = (jj % (2 * DB)) >> 1;
+                    constexpr int kk = 2 * ((i - 2 * NB) / NG) + jj / (2 * DBL);
+                    constexpr int db = (jj % (2 * DBL)) >> 1;
                     if constexpr ((jj & 1) != 0) {
                         dk_acc[db] = mfma32<F16>(a, dsb[kk], dk_acc[db]);
                         keep_here_acc(dk_acc[db]);
@@ -700,7 +716,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 }
                 if constexpr (i == NB || i == 2 * NB)
                     pin_acc();
-                if constexpr (!FUSED && i == BAR) {
+                if constexpr (!TWO && i == BAR) {
                     // The 16-byte operand reads of this tile and its row
                     // vectors are all issued: move them to the next buffer.
 #pragma unroll
@@ -720,21 +736,21 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 // barrier on, into the buffer every wave has finished with;
                 // then the pointers and descriptors for the tile after that
                 // (the scalar work spread over slots in the MFMAs' shadow).
-                if constexpr (!FUSED && i >= BAR && i < BAR + (LPT + 1) / 2) {
+                if constexpr (!TWO && i >= BAR && i < BAR + (LPT + 1) / 2) {
                     constexpr int j0 = 2 * (i - BAR);
                     const int bf = cur == 0 ? NBUF - 1 : cur - 1;
                     issue_one(IC<j0>{}, bf);
                     if constexpr (j0 + 1 < LPT)
                         issue_one(IC<j0 + 1>{}, bf);
                 }
-                if constexpr (!FUSED && i >= BAR + (LPT + 1) / 2 && i < BAR + (LPT + 1) / 2 + 6)
+                if constexpr (!TWO && i >= BAR + (LPT + 1) / 2 && i < BAR + (LPT + 1) / 2 + 6)
                     setup_part(IC<i - BAR - (LPT + 1) / 2>{});
-                if constexpr (!FUSED && i > BAR && i <= BAR + 4)
+                if constexpr (!TWO && i > BAR && i <= BAR + 4)
                     read_rowdot(0, i - BAR - 1);   // next tile (buffer published at BAR)
-                if constexpr (!FUSED && i == NSLOT - RA - 1) {
+                if constexpr (!TWO && i == NSLOT - RA - 1) {
                     // last transposing read of this tile issued
 #pragma unroll
-                    for (int db = 0; db < DB; ++db) {
+                    for (int db = 0; db < DBL; ++db) {
                         tq[db][0] += delta;
                         tq[db][1] += delta;
                     }
@@ -743,23 +759,25 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             });
             pin_acc();
 
-            if constexpr (FUSED) {
+            if constexpr (TWO) {
                 // Next tile's buffer.
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
                     gq[ks] += delta;
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
+                for (int db = 0; db < DBL; ++db) {
                     tq[db][0] += delta;
                     tq[db][1] += delta;
                 }
                 rv0 += delta;
                 wait_loads<0>();
                 __syncthreads();   // next tile in LDS; dS^T[cur] complete
-                const int h = hk * p.G + hh;
-                const int rows_valid = min(kQTile, Lq - q0);
-                dq_partial<DP, F16>(p, sm, cur, w, lane, l32, g2, tid, b, h, m, j, q0, rows_valid, Lq,
-                               off, nt_b, si.ws_row);
+                if constexpr (FUSED) {
+                    const int h = hk * p.G + hh;
+                    const int rows_valid = min(kQTile, Lq - q0);
+                    dq_partial<DP, F16>(p, sm, cur, w, lane, l32, g2, tid, b, h, m, j, q0,
+                                        rows_valid, Lq, off, nt_b, si.ws_row);
+                }
                 static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4)
@@ -778,7 +796,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             // tiles and before the masked rest.  (Three loops per head: a
             // single masked loop spanning the heads makes the register
             // allocator spill.)
-            const int kw0 = n0 + 32 * w, kw_last = kw0 + 31;
+            const int kw0 = n0 + 32 * kgrp, kw_last = kw0 + 31;
             int nh = 0, nu = 0;
             if (kw_last < Lk) {
                 const int need = kw_last - off - p.win_r;
@@ -815,10 +833,10 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         uint16_t *dkrow = p.dk + row_offset(p, b, si.tok_k, key, p.dk_sb, p.dk_ss) + hk * p.dk_sh;
         uint16_t *dvrow = p.dv + row_offset(p, b, si.tok_k, key, p.dv_sb, p.dv_ss) + hk * p.dv_sh;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+        for (int db = 0; db < DBL; ++db) {
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const int d = 32 * db + 8 * r4 + 4 * g2;
+                const int d = 32 * (dbo + db) + 8 * r4 + 4 * g2;
                 if (d < p.D) {
                     u16x4 kq, vq;
 #pragma unroll
@@ -838,10 +856,21 @@ template <bool LOCAL, bool SOFTCAP, bool DROP>
 static hipError_t launch_main_t(const Params &p, int dpad, hipStream_t st)
 {
     const dim3 grid((unsigned)p.ntiles * p.Hk * p.batch);
+    // head dims above 128: 64 keys per workgroup
+    const dim3 grid_big((unsigned)((p.Sk + 63) / 64) * p.Hk * p.batch);
     const dim3 block(kThreads);
 #define FA_LAUNCH_MAIN(D, FU, H16)                                                               \
     hipLaunchKernelGGL((fa_bwd_main_kernel<D, FU, H16, LOCAL, SOFTCAP, DROP>), grid, block, 0,    \
                        st, p)
+#define FA_LAUNCH_MAIN_BIG(D)                                                                    \
+    if (p.fused_dq)                                                                              \
+        return hipErrorInvalidValue;                                                             \
+    else if (p.f16)                                                                              \
+        hipLaunchKernelGGL((fa_bwd_main_kernel<D, false, true, LOCAL, SOFTCAP, DROP>), grid_big,  \
+                           block, 0, st, p);                                                     \
+    else                                                                                         \
+        hipLaunchKernelGGL((fa_bwd_main_kernel<D, false, false, LOCAL, SOFTCAP, DROP>), grid_big, \
+                           block, 0, st, p);
 #define FA_LAUNCH_MAIN_D(D)                                                                      \
     if (p.fused_dq && p.f16)                                                                     \
         FA_LAUNCH_MAIN(D, true, true);                                                           \
@@ -861,9 +890,16 @@ static hipError_t launch_main_t(const Params &p, int dpad, hipStream_t st)
     case 128:
         FA_LAUNCH_MAIN_D(128);
         break;
+    case 192:
+        FA_LAUNCH_MAIN_BIG(192);
+        break;
+    case 256:
+        FA_LAUNCH_MAIN_BIG(256);
+        break;
     default:
         return hipErrorInvalidValue;
     }
+#undef FA_LAUNCH_MAIN_BIG
 #undef FA_LAUNCH_MAIN_D
 #undef FA_LAUNCH_MAIN
     return hipGetLastError();

@@ -272,7 +272,7 @@ __device__ inline void wait_loads()
 
 // ---- Swizzled row-major tiles in LDS ----
 // Rows of 16-byte chunks with no padding; chunk c of row r is stored at
-// chunk position c ^ swz<PCH>(r) (PCH = chunks per row, 16 or 8).  The LDS
+// chunk position c ^ swz<PCH>(r) (PCH = chunks per row, 8, 16 or 32).  The LDS
 // serves 256 bytes (64 banks) per clock: a 16-byte read by 16 lanes or an
 // 8-byte read by 32 lanes.  The swizzle makes both conflict-free for the
 // operand reads of the tile kernels:
@@ -285,7 +285,9 @@ __device__ inline void wait_loads()
 template <int PCH>
 __device__ __host__ constexpr int swz(int r)
 {
-    return PCH == 16 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+    // PCH = 32 (512-byte rows, two bank lines each): the PCH = 16 swizzle
+    // within each half of the row keeps both read patterns conflict-free
+    return PCH >= 16 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
 __device__ inline e16x8 lds16b(const uint8_t *p)
@@ -344,7 +346,7 @@ __device__ inline void static_for(F &&f)
 // (64 query rows in the key-tile kernel, 64 keys in the query-tile kernel).
 template <int DP>
 struct Tile64 {
-    static constexpr int PCH = DP <= 64 ? 8 : 16;   // 16-byte chunks per LDS row
+    static constexpr int PCH = DP <= 64 ? 8 : (DP <= 128 ? 16 : 32);   // 16-byte chunks per row
     static constexpr int PB = 16 * PCH;             // row pitch (bytes)
     static constexpr int BYTES = 64 * PB;
     static constexpr int NLOAD = BYTES / 1024;      // 1 KB wave loads per tile

@@ -319,21 +319,25 @@ def cpu_baseline(wl, units):
 
 def window_suffix(wl):
     suffix = "" if wl.window is None else ", local window (%d, %d)" % tuple(wl.window)
+    suffix += ", head_dim %d" % wl.head_dim if wl.head_dim != 128 else ""
     suffix += ", softcap %g" % wl.softcap if wl.softcap > 0 else ""
     return suffix + (", dropout %g" % wl.dropout[0] if wl.dropout else "")
 
 
 def main_kernel_name(fused, wl):
     local = wl.window is not None and wl.window[0] >= 0
-    return "fa_bwd_main_kernel<128, %s, false, %s, %s, %s>" % (
-        str(bool(fused)).lower(), str(local).lower(), str(wl.softcap > 0).lower(),
+    dpad = next(d for d in (64, 96, 128, 192, 256) if d >= wl.head_dim)
+    return "fa_bwd_main_kernel<%d, %s, false, %s, %s, %s>" % (
+        dpad, str(bool(fused)).lower(), str(local).lower(), str(wl.softcap > 0).lower(),
         str(wl.dropout is not None).lower())
 
 
 def fwd_kernel_name(wl):
     local = wl.window is not None and wl.window[0] >= 0
-    return "fa_fwd_kernel<128, false, %s, %s, %s>" % (str(local).lower(), str(wl.softcap > 0).lower(),
-                                                   str(wl.dropout is not None).lower())
+    dpad = next(d for d in (64, 96, 128, 192, 256) if d >= wl.head_dim)
+    return "fa_fwd_kernel<%d, false, %s, %s, %s>" % (dpad, str(local).lower(),
+                                                  str(wl.softcap > 0).lower(),
+                                                  str(wl.dropout is not None).lower())
 
 
 FWD_METRIC = "fwd TFLOP/s (O, LSE) bf16 and % of MFMA peak, S=4096 D=128 causal GQA"
@@ -445,6 +449,8 @@ def main():
                     help="local window (negative = unbounded): times the workload with it")
     ap.add_argument("--softcap", type=float, default=0.0,
                     help="soft cap c > 0 of the scaled scores: times the workload with it")
+    ap.add_argument("--head-dim", type=int, default=0,
+                    help="head dim other than the workload's (up to 256): times the workload with it")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="dropout probability p > 0: times the workload with it (fixed seed)")
     ap.add_argument("--summarize-profile", metavar="PROF_DIR",
@@ -481,6 +487,10 @@ def main():
 
     fa.load_library()
     wl = W.WORKLOADS[args.config]
+    if args.head_dim:
+        import dataclasses
+        wl = dataclasses.replace(wl, name=wl.name.replace("_d%d" % wl.head_dim, "_d%d" % args.head_dim),
+                                 head_dim=int(args.head_dim))
     if args.window is not None:
         import dataclasses
         wl = dataclasses.replace(wl, name="%s_window%d_%d" % (wl.name, *args.window),

@@ -19,7 +19,8 @@
  *                  reduction of the GQA/MQA page's backward section happens
  *                  in registers) and over the visible 64-row query tiles;
  *   - dQ, in one of two ways (fa_bwd_args.dq_accumulate):
- *      0 (default) dq  : one workgroup per 256 query rows of one head loops
+ *      0 (default) dq  : one workgroup per 256 query rows (128 at head_dim
+ *                        > 128) of one head loops
  *                        over the visible key tiles and forms dQ = scale *
  *                        dS K directly (dS recomputed; no atomics; the way
  *                        the Triton FA2 teaching page's dQ kernel works).
@@ -29,7 +30,8 @@
  *                        fp32 accumulator (hardware atomics, or a fixed
  *                        order when deterministic = 1), which the preprocess
  *                        clears, and dq_convert forms dQ = scale * acc
- *                        rounded to the element type
+ *                        rounded to the element type (head_dim <= 128
+ *                        only; above, FA_ERR_UNSUPPORTED)
  *                        (the dq_accum buffer and its reduction step on the
  *                        backward call-trace page); the sequence is
  *                        preprocess, main, dq_convert.
@@ -65,7 +67,7 @@ extern "C" {
 typedef enum {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1, /* null pointer, bad size, H % Hk != 0, bad stride */
-    FA_ERR_UNSUPPORTED = 2, /* dtype other than bf16 / fp16, head_dim > 128 or not a multiple of 8 */
+    FA_ERR_UNSUPPORTED = 2, /* dtype other than bf16 / fp16, head_dim > 256 or not a multiple of 8 */
     FA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than fa_bwd_workspace_size() */
     FA_ERR_HIP = 4          /* a HIP launch or attribute call failed */
 } fa_status;
@@ -148,9 +150,10 @@ typedef enum {
  *   - dq, dk, dv are fully overwritten over their valid rows and the first
  *     head_dim columns; dk/dv of keys no query can see are written as 0.
  *     They must not alias any input or the workspace.
- *   - head_dim padding: head_dim must be a multiple of 8 and <= 128; kernels
- *     run at a padded tile width of 64, 96 or 128 with zero-filled loads and
- *     masked stores (sm90 backward page, __init__: head dim rounded up to
+ *   - head_dim padding: head_dim must be a multiple of 8 and <= 256; kernels
+ *     run at a padded tile width of 64, 96, 128, 192 or 256 with zero-filled
+ *     loads and masked stores (above 128 the key-tile kernel takes 64 keys
+ *     per workgroup, two waves per 32 keys splitting the head dim of dK/dV) (sm90 backward page, __init__: head dim rounded up to
  *     the tile multiple; backward call-trace page, dout padding step).
  *   - Reproducibility: with dq_accumulate = 0 every output is a fixed-order
  *     sum, so repeated calls give bit-identical dq, dk, dv whatever

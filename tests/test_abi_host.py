@@ -101,7 +101,7 @@ def test_workspace_layout_formula():
 
 
 @pytest.mark.parametrize("d,pad", [(8, 64), (64, 64), (72, 96), (96, 96), (104, 128),
-                                   (128, 128)])
+                                   (128, 128), (136, 192), (192, 192), (200, 256), (256, 256)])
 def test_head_dim_padding(d, pad):
     a = _args(head_dim=d, do_stride=(256 * 8 * d, 8 * d, d), q_stride=(256 * 8 * d, 8 * d, d),
               o_stride=(256 * 8 * d, 8 * d, d), dq_stride=(256 * 8 * d, 8 * d, d),
@@ -178,7 +178,8 @@ def test_valid_args_pass_validation():
     ({"dtype": 2}, fa.FA_ERR_UNSUPPORTED),
     ({"head_dim": 300}, fa.FA_ERR_UNSUPPORTED),
     ({"head_dim": 100}, fa.FA_ERR_UNSUPPORTED),           # not a multiple of 8
-    ({"head_dim": 192}, fa.FA_ERR_UNSUPPORTED),           # > 128 not built
+    ({"head_dim": 264}, fa.FA_ERR_UNSUPPORTED),           # > 256
+    ({"head_dim": 192, "dq_accumulate": 1}, fa.FA_ERR_UNSUPPORTED),   # fused dQ: <= 128
 ])
 def test_validation_errors(over, status):
     a = _args(**over)
@@ -269,7 +270,7 @@ def test_forward_valid_args_pass_validation():
     ({"softmax_scale": float("inf")}, fa.FA_ERR_INVALID_ARG),
     ({"cu_seqlens_k": BASE}, fa.FA_ERR_INVALID_ARG),
     ({"dtype": 2}, fa.FA_ERR_UNSUPPORTED),
-    ({"head_dim": 192}, fa.FA_ERR_UNSUPPORTED),
+    ({"head_dim": 264}, fa.FA_ERR_UNSUPPORTED),
     ({"v_stride": (1 << 30, 1 << 24, 128)}, fa.FA_ERR_UNSUPPORTED),
 ])
 def test_forward_validation_errors(over, status):
