@@ -81,6 +81,7 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
     constexpr int KS = DP / 16;                  // k-steps over the head dim
     constexpr int DB = DP / 32;                  // 32-wide head-dim blocks
     constexpr int NBUF = DqShape<DP>::NBUF;
+    constexpr bool BIG = DqShape<DP>::BIG;
     constexpr int WAVES = DqShape<DP>::WAVES;
     constexpr int ROWS = DqShape<DP>::ROWS;
     using L = Tile64<DP>;
@@ -280,6 +281,13 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         of[ks] = __builtin_bit_cast(e16x8, __builtin_bit_cast(u32x4, of[ks]) ^ 0x80008000u);
+    if constexpr (DqShape<DP>::BIG) {
+        // Q and -dO rows live in accumulation registers (operands of the
+        // inline S^T / dP^T products)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            asm volatile("" : "+a"(qf[ks]), "+a"(of[ks]));
+    }
 #pragma unroll
     for (int e = 0; e < 16; ++e)
         rdt[e] = rd;
@@ -452,7 +460,26 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
                         if constexpr ((i % NB) == r4 * NB / 4)
                             drop_call(IC<4 * (i / NB) + r4>{});
                     });
-                if constexpr (i < 2 * NB) {
+                if constexpr (i < 2 * NB && BIG) {
+                    // above 128 the kernel needs more than 256 registers, so
+                    // the compiler's MFMAs use accumulation registers: S^T and
+                    // dP^T as inline MFMAs in ordinary registers instead (Q and
+                    // dO operands in accumulation registers), as the key-tile
+                    // kernel does
+                    constexpr int mb = i / NB, jj = i % NB, ks = jj >> 1;
+                    if constexpr ((jj & 1) != 0) {
+                        if constexpr (ks == 0) {
+                            dpt[mb] = rdt;   // a vector copy: FRESH waits for it
+                            mfma32_vacc<F16, true>(dpt[mb], a, of[ks]);
+                        } else {
+                            mfma32_vacc<F16>(dpt[mb], a, of[ks]);
+                        }
+                    } else if constexpr (ks == 0) {
+                        mfma32_vz<F16>(st[mb], a, qf[ks]);
+                    } else {
+                        mfma32_vacc<F16>(st[mb], a, qf[ks]);
+                    }
+                } else if constexpr (i < 2 * NB) {
                     constexpr int mb = i / NB, jj = i % NB, ks = jj >> 1;
                     if constexpr ((jj & 1) != 0) {
                         dpt[mb] = mfma32<F16>(a, of[ks], ks == 0 ? rdt : dpt[mb]);
@@ -464,8 +491,16 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
                 } else {
                     constexpr int jj = i - 2 * NB, kk = jj / DB, db = jj % DB;
                     acc[db] = mfma32<F16>(dsa[kk], a, acc[db]);
-                    keep_here(acc[db]);
+                    if constexpr (BIG)
+                        keep_here_acc(acc[db]);
+                    else
+                        keep_here(acc[db]);
                 }
+                // inline MFMA results: 12 wait states before the first read
+                if constexpr (BIG && i == NB)
+                    mfma_settle(st[0], dpt[0]);
+                if constexpr (BIG && i == 2 * NB)
+                    mfma_settle(st[1], dpt[1]);
                 // dS of keys 0-31 over slots NB .. 2NB-1, of keys 32-63 over
                 // 2NB .. 2NB+NQ-1 (16 elements each)
                 if constexpr (i >= NB && i < 2 * NB) {

@@ -195,6 +195,13 @@ __global__ void __launch_bounds__(FwdShape<DP>::THREADS, 1) fa_fwd_kernel(Params
                 a = *reinterpret_cast<const u32x4 *>(qp + d0);
             qf[ks] = __builtin_bit_cast(e16x8, a);
         }
+        if constexpr (BIG) {
+            // Q rows live in accumulation registers (operands of the inline
+            // S^T products)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                asm volatile("" : "+a"(qf[ks]));
+        }
     }
     wait_loads();   // land them and the first key tiles before the tile loop
 
@@ -359,15 +366,33 @@ __global__ void __launch_bounds__(FwdShape<DP>::THREADS, 1) fa_fwd_kernel(Params
                     ring[i % RA] = op_read(IC<i + RA>{});
                 else if constexpr (NBUF == 3)
                     ring[i % RA] = op_read(IC<i + RA - NSLOT>{});   // next tile
-                if constexpr (i < 2 * NB) {
+                if constexpr (i < 2 * NB && BIG) {
+                    // above 128 the kernel needs more than 256 registers, so
+                    // the compiler's MFMAs use accumulation registers: S^T as
+                    // inline MFMAs in ordinary registers instead (Q operand in
+                    // accumulation registers), as the key-tile kernel does
+                    constexpr int mb = i / NB, ks = i % NB;
+                    if constexpr (ks == 0)
+                        mfma32_vz<F16>(st[mb], a, qf[ks]);
+                    else
+                        mfma32_vacc<F16>(st[mb], a, qf[ks]);
+                } else if constexpr (i < 2 * NB) {
                     constexpr int mb = i / NB, ks = i % NB;
                     st[mb] = mfma32<F16>(a, qf[ks], ks == 0 ? z : st[mb]);
                     keep_here(st[mb]);
                 } else {
                     constexpr int jj = i - 2 * NB, kk = jj / DB, db = jj % DB;
                     acc[db] = mfma32<F16>(a, pb[kk], acc[db]);
-                    keep_here(acc[db]);
+                    if constexpr (BIG)
+                        keep_here_acc(acc[db]);
+                    else
+                        keep_here(acc[db]);
                 }
+                // inline MFMA results: 12 wait states before the first read
+                if constexpr (BIG && i == NB)
+                    mfma_settle(st[0]);
+                if constexpr (BIG && i == 2 * NB - 1)
+                    mfma_settle(st[1]);
                 // maximum of keys 0-31 over the S^T slots of keys 32-63
                 if constexpr (i >= NB && i < 2 * NB) {
                     constexpr int u = i - NB;

@@ -96,6 +96,13 @@ __device__ inline void mfma_settle(f32x16 &s, f32x16 &t)
     asm volatile("s_nop 11" : "+v"(s), "+v"(t));
 }
 
+// The same for one product (passing one value twice to mfma_settle would make
+// the compiler copy it first).
+__device__ inline void mfma_settle(f32x16 &s)
+{
+    asm volatile("s_nop 11" : "+v"(s));
+}
+
 // Keeps the computation of x at this point of the instruction stream.  The
 // compiler's basic-block scheduler places pure arithmetic next to its first
 // use, across the scheduling fences that separate the MFMA slots; an empty

@@ -317,9 +317,14 @@ def cpu_baseline(wl, units):
                       % (len(units), wl.batch * wl.heads_k, t_total)}
 
 
+def metric_name(base, wl):
+    """The metric label with the variant's head dim and extra features."""
+    name = base.replace("D=128", "D=%d" % wl.head_dim)
+    return name + window_suffix(wl)
+
+
 def window_suffix(wl):
     suffix = "" if wl.window is None else ", local window (%d, %d)" % tuple(wl.window)
-    suffix += ", head_dim %d" % wl.head_dim if wl.head_dim != 128 else ""
     suffix += ", softcap %g" % wl.softcap if wl.softcap > 0 else ""
     return suffix + (", dropout %g" % wl.dropout[0] if wl.dropout else "")
 
@@ -403,7 +408,7 @@ def bench_forward(args, wl, dev):
     flops = fwd_flops(B, H, Sq, Sk, D, wl.causal, wl.window)
     tf = flops / (ms * 1e-3) / 1e12
     rec = {
-        "metric": FWD_METRIC + window_suffix(wl), "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": metric_name(FWD_METRIC, wl), "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
@@ -575,7 +580,7 @@ def main():
     flags = ws[off_flags:off_flags + 16].cpu().view(torch.int32)
 
     rec = {
-        "metric": METRIC + window_suffix(wl),
+        "metric": metric_name(METRIC, wl),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
