@@ -79,6 +79,12 @@
  * applied to every head on top of the causal rule; used by the tests to show
  * that the causal rule equals an explicit -inf mask.
  *
+ * Optional `drop_base` (nullable): {b0, h0, hc}, the place of this call's
+ * sequences and heads in a larger call whose dropout bits it replays:
+ * sequence b and head h here draw the bits of sequence b + b0 and head
+ * h + h0 of hc heads there (h0 + H <= hc).  Used to evaluate one sampled
+ * (sequence, head group) of a large dropout run alone.
+ *
  * Return value: 0 on success, -1 on bad arguments, -2 on allocation failure.
  */
 #include <math.h>
@@ -122,19 +128,42 @@ void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t
         out[w] = c[w];
 }
 
-/* Dropout parameters of one call: p = 0 means none. */
+/* Dropout parameters of one call: p = 0 means none.  The counter names the
+ * element's sequence and query head within the whole attention call; a call
+ * that evaluates part of it (one sequence, one group of heads) gives that
+ * part's place: sequence b of the part is sequence b + b0 of the whole, head h
+ * is head h + h0 of hc heads (b0 = h0 = 0, hc = the part's own H when no base
+ * is given). */
 typedef struct {
     double p;
     uint64_t seed, offset;
+    int64_t b0, h0, hc;
 } drop_t;
+
+static int bad_base(const int64_t *base, int H)
+{
+    return base && (base[0] < 0 || base[1] < 0 || base[2] < base[1] + H);
+}
+
+static drop_t make_drop(double p, uint64_t seed, uint64_t offset, const int64_t *base)
+{
+    drop_t dr = {p, seed, offset, 0, 0, 0};
+    if (base) {
+        dr.b0 = base[0];
+        dr.h0 = base[1];
+        dr.hc = base[2];
+    }
+    return dr;
+}
 
 /* Keep bit Z of element (b, h, i, j), H query heads. */
 static int drop_keep(const drop_t *dr, int b, int h, int H, int i, int j)
 {
     if (dr->p <= 0.0)
         return 1;
-    const uint32_t ctr[4] = {(uint32_t)j >> 2, (uint32_t)i, (uint32_t)((int64_t)b * H + h),
-                             (uint32_t)dr->offset};
+    const int64_t hc = dr->hc > 0 ? dr->hc : H;
+    const uint32_t ctr[4] = {(uint32_t)j >> 2, (uint32_t)i,
+                             (uint32_t)((b + dr->b0) * hc + h + dr->h0), (uint32_t)dr->offset};
     const uint32_t key[2] = {(uint32_t)dr->seed,
                              (uint32_t)(dr->seed >> 32) ^ (uint32_t)(dr->offset >> 32)};
     uint32_t out[4];
@@ -157,7 +186,7 @@ int oracle_dropout_mask(double p, uint64_t seed, uint64_t offset, int b, int h, 
 {
     if (!(p >= 0.0 && p < 1.0) || Lq < 0 || Lk < 0 || H <= 0)
         return -1;
-    const drop_t dr = {p, seed, offset};
+    const drop_t dr = make_drop(p, seed, offset, NULL);
     for (int i = 0; i < Lq; i++)
         for (int j = 0; j < Lk; j++)
             mask[(size_t)i * Lk + j] = (uint8_t)drop_keep(&dr, b, h, H, i, j);
@@ -263,13 +292,14 @@ static int max_len(int nseq, const int64_t *cu)
 int oracle_forward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
                    int H, int Hk, int D, double scale, int causal, int wl, int wr,
                    double softcap, double drop_p, uint64_t drop_seed, uint64_t drop_offset,
-                   const double *mask,
+                   const int64_t *drop_base, const double *mask,
                    const double *q, const double *k, const double *v,
                    double *out, double *lse)
 {
-    if (check_common(nseq, cu_q, cu_k, H, Hk, D, mask) || !(drop_p >= 0.0 && drop_p < 1.0))
+    if (check_common(nseq, cu_q, cu_k, H, Hk, D, mask) || !(drop_p >= 0.0 && drop_p < 1.0) ||
+        bad_base(drop_base, H))
         return -1;
-    const drop_t dr = {drop_p, drop_seed, drop_offset};
+    const drop_t dr = make_drop(drop_p, drop_seed, drop_offset, drop_base);
     const int G = H / Hk;
     const int Lk_max = max_len(nseq, cu_k);
     const int64_t nunits = (int64_t)nseq * H;
@@ -360,15 +390,17 @@ static void group_sum(int64_t total_k, int H, int Hk, int D,
 int oracle_backward_explicit(int nseq, const int64_t *cu_q, const int64_t *cu_k,
                              int H, int Hk, int D, double scale, int causal, int wl, int wr,
                              double softcap, double drop_p, uint64_t drop_seed,
-                             uint64_t drop_offset, const double *mask,
+                             uint64_t drop_offset, const int64_t *drop_base,
+                             const double *mask,
                              const double *q, const double *k, const double *v,
                              const double *dout,
                              double *dq, double *dk, double *dv,
                              double *ds_out, double *dj_out)
 {
-    if (check_common(nseq, cu_q, cu_k, H, Hk, D, mask) || !(drop_p >= 0.0 && drop_p < 1.0))
+    if (check_common(nseq, cu_q, cu_k, H, Hk, D, mask) || !(drop_p >= 0.0 && drop_p < 1.0) ||
+        bad_base(drop_base, H))
         return -1;
-    const drop_t dr = {drop_p, drop_seed, drop_offset};
+    const drop_t dr = make_drop(drop_p, drop_seed, drop_offset, drop_base);
     if (ds_out && nseq != 1)
         return -1;
     const int G = H / Hk;
@@ -499,15 +531,16 @@ int oracle_backward_explicit(int nseq, const int64_t *cu_q, const int64_t *cu_k,
 int oracle_backward(int nseq, const int64_t *cu_q, const int64_t *cu_k,
                     int H, int Hk, int D, double scale, int causal, int wl, int wr,
                     double softcap, double drop_p, uint64_t drop_seed, uint64_t drop_offset,
-                    const double *mask,
+                    const int64_t *drop_base, const double *mask,
                     const double *q, const double *k, const double *v,
                     const double *dout,
                     double *dq, double *dk, double *dv,
                     double *dj_out, double *lse_out)
 {
-    if (check_common(nseq, cu_q, cu_k, H, Hk, D, mask) || !(drop_p >= 0.0 && drop_p < 1.0))
+    if (check_common(nseq, cu_q, cu_k, H, Hk, D, mask) || !(drop_p >= 0.0 && drop_p < 1.0) ||
+        bad_base(drop_base, H))
         return -1;
-    const drop_t dr = {drop_p, drop_seed, drop_offset};
+    const drop_t dr = make_drop(drop_p, drop_seed, drop_offset, drop_base);
     const int G = H / Hk;
     const int64_t total_q = cu_q[nseq];
     const int Lk_max = max_len(nseq, cu_k);

@@ -28,7 +28,8 @@ def _lib():
         lib = ctypes.CDLL(_build.LIB)
         common = [ctypes.c_int, _i64p, _i64p, ctypes.c_int, ctypes.c_int,
                   ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                  ctypes.c_double, ctypes.c_double, ctypes.c_uint64, ctypes.c_uint64, _dp]
+                  ctypes.c_double, ctypes.c_double, ctypes.c_uint64, ctypes.c_uint64, _i64p,
+                  _dp]
         lib.oracle_forward.argtypes = common + [_dp, _dp, _dp, _dp, _dp]
         lib.oracle_backward.argtypes = common + [_dp] * 4 + [_dp] * 3 + [_dp, _dp]
         lib.oracle_backward_explicit.argtypes = common + [_dp] * 4 + [_dp] * 3 + [_dp, _dp]
@@ -81,22 +82,32 @@ def num_threads() -> int:
     return int(_lib().oracle_num_threads())
 
 
-def _drop(dropout):
-    """dropout = None or (p, seed, offset) -> the three C arguments."""
+def _drop(dropout, drop_base=None):
+    """dropout = None or (p, seed, offset), drop_base = None or (b0, h0, hc)
+    -> the four C arguments (a pointer from ndarray.ctypes.data_as holds a
+    reference to its array)."""
+    base = None
+    if drop_base is not None:
+        base = np.ascontiguousarray(np.array(drop_base, dtype=np.int64))
+        if base.shape != (3,):
+            raise ValueError("drop_base is (b0, h0, hc)")
+    bp = None if base is None else base.ctypes.data_as(_i64p)
     if dropout is None:
-        return 0.0, 0, 0
+        return 0.0, 0, 0, bp
     p, seed, offset = dropout
-    return float(p), int(seed) & (2**64 - 1), int(offset) & (2**64 - 1)
+    return float(p), int(seed) & (2**64 - 1), int(offset) & (2**64 - 1), bp
 
 
 def forward(q, k, v, cu_q, cu_k, scale, causal, mask=None, window=(-1, -1), softcap=0.0,
-            dropout=None):
+            dropout=None, drop_base=None):
     """Returns (out [total_q,H,D], lse [total_q,H]) in fp64.  window =
     (left, right): query i sees keys i + Lk - Lq - left .. i + Lk - Lq + right
     (a negative size leaves that side unbounded).  softcap c > 0: every
     scaled score x becomes c * tanh(x / c) (LSE of the capped scores).
     dropout = (p, seed, offset): O uses P * Z / (1 - p) with the keep bits Z
-    of dropout_mask (the LSE is that of the undropped scores)."""
+    of dropout_mask (the LSE is that of the undropped scores).  drop_base =
+    (b0, h0, hc): these sequences and heads replay the bits of sequences
+    b0.. and heads h0.. of an hc-head call."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     cu_q, cu_k = _cu(cu_q), _cu(cu_k)
     nseq, H, Hk, D = _shapes(q, k, cu_q, cu_k)
@@ -105,20 +116,21 @@ def forward(q, k, v, cu_q, cu_k, scale, causal, mask=None, window=(-1, -1), soft
     lse = np.empty(q.shape[:2], np.float64)
     rc = _lib().oracle_forward(nseq, cu_q.ctypes.data_as(_i64p), cu_k.ctypes.data_as(_i64p),
                                H, Hk, D, float(scale), int(bool(causal)), int(window[0]),
-                               int(window[1]), float(softcap), *_drop(dropout), _ptr(mask),
-                               _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse))
+                               int(window[1]), float(softcap), *_drop(dropout, drop_base),
+                               _ptr(mask), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse))
     if rc:
         raise RuntimeError("oracle_forward failed (%d)" % rc)
     return out, lse
 
 
 def backward(q, k, v, dout, cu_q, cu_k, scale, causal, mask=None,
-             mode="contracted", want_ds=False, window=(-1, -1), softcap=0.0, dropout=None):
+             mode="contracted", want_ds=False, window=(-1, -1), softcap=0.0, dropout=None,
+             drop_base=None):
     """Exact attention gradient in fp64.
 
     mode="contracted": any size; mode="explicit": materialised softmax
     Jacobian, small inputs only (want_ds=True returns dS [H, Lq, Lk] for a
-    single sequence).  Returns a dict with dq, dk, dv, dj (sum_k P_ik dP_ik)
+    single sequence).  drop_base as in forward().  Returns a dict with dq, dk, dv, dj (sum_k P_ik dP_ik)
     and, in contracted mode, lse; in explicit mode with want_ds, ds.
     """
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
@@ -135,7 +147,7 @@ def backward(q, k, v, dout, cu_q, cu_k, scale, causal, mask=None,
     lib = _lib()
     common = (nseq, cu_q.ctypes.data_as(_i64p), cu_k.ctypes.data_as(_i64p), H, Hk, D,
               float(scale), int(bool(causal)), int(window[0]), int(window[1]), float(softcap),
-              *_drop(dropout), _ptr(mask),
+              *_drop(dropout, drop_base), _ptr(mask),
               _ptr(q), _ptr(k), _ptr(v),
               _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv))
     if mode == "contracted":

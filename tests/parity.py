@@ -121,10 +121,9 @@ def oracle_backward(pr: Prepared):
 
 def oracle_backward_unit(pr: Prepared, s: int, g: int):
     """Exact gradients of sequence s and KV head g alone (the query heads of
-    its group), as (rows_q, heads, rows_k, ref) for sampled comparisons."""
+    its group), as (rows_q, heads, rows_k, ref) for sampled comparisons (with
+    dropout, the unit replays the keep bits of its place in the whole call)."""
     wl = pr.inp.wl
-    # the keep bits depend on the sequence and head numbers of the whole call
-    assert wl.dropout is None, "sampled units do not renumber dropout counters"
     G = wl.heads // wl.heads_k
     heads = list(range(g * G, (g + 1) * G))
     qs, qe = pr.cu_q[s], pr.cu_q[s + 1]
@@ -132,7 +131,7 @@ def oracle_backward_unit(pr: Prepared, s: int, g: int):
     ref = O.backward(pr.q64[qs:qe][:, heads], pr.k64[ks:ke][:, [g]], pr.v64[ks:ke][:, [g]],
                      pr.do64[qs:qe][:, heads], [0, qe - qs], [0, ke - ks], wl.scale,
                      wl.causal, window=wl.window_sizes, softcap=wl.softcap,
-                     dropout=wl.dropout_f32)
+                     dropout=wl.dropout_f32, drop_base=(s, g * G, wl.heads))
     return (slice(qs, qe), heads, slice(ks, ke), ref)
 
 
@@ -167,3 +166,32 @@ def lse_rows(inp: W.Inputs, lse: torch.Tensor) -> np.ndarray:
     for s in range(len(inp.lens_q)):
         rows[cu[s]:cu[s + 1]] = L[s, :, :inp.lens_q[s]].T
     return rows
+
+
+def check_full_size_units(inp: W.Inputs, units=((0, 0), (1, 5))):
+    """GPU forward, then the GPU backward on its O and LSE, at a size the
+    oracle cannot take whole: each (sequence, KV head) unit's O, LSE and
+    gradients against the oracle computed for that unit alone (with dropout,
+    replaying the bits of the unit's place in the whole call)."""
+    wl = inp.wl
+    out, lse = run_gpu_fwd(inp)
+    pr = Prepared.__new__(Prepared)
+    pr.inp = inp
+    pr.cu_q, pr.cu_k = cu_np(inp.lens_q), cu_np(inp.lens_k)
+    pr.q64, pr.k64, pr.v64, pr.do64 = (to64(inp.packed(t)) for t in
+                                       (inp.q, inp.k, inp.v, inp.dout))
+    pr.o, pr.lse = out, lse
+    res = run_gpu(pr)
+    lrows = lse_rows(inp, lse)
+    G = wl.heads // wl.heads_k
+    for s, g in units:
+        qs, heads, ks, ref = oracle_backward_unit(pr, s, g)
+        ro, rl = O.forward(pr.q64[qs][:, heads], pr.k64[ks][:, [g]], pr.v64[ks][:, [g]],
+                           [0, qs.stop - qs.start], [0, ks.stop - ks.start], wl.scale,
+                           wl.causal, window=wl.window_sizes, softcap=wl.softcap,
+                           dropout=wl.dropout_f32, drop_base=(s, g * G, wl.heads))
+        compare(inp.packed(out)[qs][:, heads], ro, "unit %d/%d O" % (s, g))
+        assert np.abs(lrows[qs][:, heads] - rl).max() <= 1e-3
+        compare(inp.packed(res["dq"])[qs][:, heads], ref["dq"], "unit %d/%d dq" % (s, g))
+        compare(inp.packed(res["dk"])[ks][:, [g]], ref["dk"], "unit %d/%d dk" % (s, g))
+        compare(inp.packed(res["dv"])[ks][:, [g]], ref["dv"], "unit %d/%d dv" % (s, g))

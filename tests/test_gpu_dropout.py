@@ -207,3 +207,18 @@ def test_forward_then_backward_with_dropout(gpu_lib):
     ref = PT.oracle_backward(pr)
     for key in ("dq", "dk", "dv"):
         PT.compare(pr.inp.packed(res[key]), ref[key], "fwd->bwd %s" % key)
+
+
+@pytest.mark.slow
+def test_dropout_full_size_sampled_units(gpu_lib):
+    """Batch 2, 32 query / 8 KV heads, 4096 x 4096, head_dim 128, causal,
+    p = 0.1 with the benchmark's seed: GPU forward, then the GPU backward on
+    its O and LSE; two (sequence, KV head) units against the oracle computed
+    for them alone, replaying the keep bits of their place in the whole call
+    (so the counters of the last sequence and of heads past 32 are covered)."""
+    _flush("dropout full size sampled units")
+    base = W.WORKLOADS[3]
+    wl = W.Workload("gqa_b2_h32_hk8_s4096_d128_causal_dropout0.1", base.batch, base.heads,
+                    base.heads_k, base.seqlen_q, base.seqlen_k, base.head_dim, True,
+                    seed=base.seed, dropout=(0.1, SEED, 0))
+    PT.check_full_size_units(W.make_inputs(wl), units=((0, 0), (1, 7)))

@@ -85,3 +85,18 @@ def test_columns_past_a_padded_head_dim_untouched(gpu_lib, prepared):
         buf = res[key + "_buf"]
         assert torch.isnan(buf[..., 232:].float()).all(), key
         PT.compare(pr.inp.packed(res[key]), ref[key], "padded " + key)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("head_dim", [256, 192])
+def test_big_head_dim_full_size_sampled_units(gpu_lib, head_dim):
+    """Batch 2, 32 query / 8 KV heads, 4096 x 4096, causal, head_dim 256 and
+    192, in the launch configuration the benchmark times: GPU forward, then
+    the GPU backward on its O and LSE, two (sequence, KV head) units against
+    the oracle computed for them alone."""
+    _flush("head_dim %d full size sampled units" % head_dim)
+    base = W.WORKLOADS[3]
+    wl = W.Workload("gqa_b2_h32_hk8_s4096_d%d_causal" % head_dim, base.batch, base.heads,
+                    base.heads_k, base.seqlen_q, base.seqlen_k, head_dim, True,
+                    seed=base.seed)
+    PT.check_full_size_units(W.make_inputs(wl))

@@ -13,7 +13,6 @@ import workloads as W
 from tests import parity as PT
 from tests.test_gpu_forward import _check as check_forward
 from tests.test_gpu_parity import MODES
-from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
 
@@ -156,23 +155,4 @@ def test_window_full_size_sampled_units(gpu_lib):
                     base.heads_k, base.seqlen_q, base.seqlen_k, base.head_dim, True,
                     seed=base.seed, window=(1024, 0))
     inp = W.make_inputs(wl)
-    out, lse = PT.run_gpu_fwd(inp)
-    # the backward consumes the GPU forward's O and LSE
-    pr = PT.Prepared.__new__(PT.Prepared)
-    pr.inp = inp
-    pr.cu_q, pr.cu_k = PT.cu_np(inp.lens_q), PT.cu_np(inp.lens_k)
-    pr.q64, pr.k64, pr.v64, pr.do64 = (PT.to64(inp.packed(t)) for t in
-                                       (inp.q, inp.k, inp.v, inp.dout))
-    pr.o, pr.lse = out, lse
-    res = PT.run_gpu(pr)
-    lrows = PT.lse_rows(inp, lse)
-    for s, g in [(0, 0), (1, 5)]:
-        qs, heads, ks, ref = PT.oracle_backward_unit(pr, s, g)
-        ro, rl = O.forward(pr.q64[qs][:, heads], pr.k64[ks][:, [g]], pr.v64[ks][:, [g]],
-                           [0, qs.stop - qs.start], [0, ks.stop - ks.start], wl.scale, True,
-                           window=wl.window_sizes)
-        PT.compare(inp.packed(out)[qs][:, heads], ro, "unit %d/%d O" % (s, g))
-        assert np.abs(lrows[qs][:, heads] - rl).max() <= 1e-3
-        PT.compare(inp.packed(res["dq"])[qs][:, heads], ref["dq"], "unit %d/%d dq" % (s, g))
-        PT.compare(inp.packed(res["dk"])[ks][:, [g]], ref["dk"], "unit %d/%d dk" % (s, g))
-        PT.compare(inp.packed(res["dv"])[ks][:, [g]], ref["dv"], "unit %d/%d dv" % (s, g))
+    PT.check_full_size_units(inp)

@@ -510,3 +510,34 @@ def test_dropout_output_is_unbiased():
     outs = np.array(outs)
     se = outs.std(axis=0) / np.sqrt(len(outs))
     assert np.all(np.abs(outs.mean(axis=0) - ref) <= 6 * se + 1e-12)
+
+
+def test_dropout_unit_with_base_replays_the_whole_call():
+    """One (sequence, KV-head group) evaluated alone with drop_base = (its
+    sequence, its first head, all heads) gives exactly the whole call's
+    forward and gradients there (the keep bits name the element's place in
+    the whole call); without the base it draws other bits and differs."""
+    lens_q, lens_k, H, Hk, D = [9, 12, 7], [11, 12, 10], 6, 2, 5
+    q, k, v, do, cu_q, cu_k = _problem(54, lens_q, lens_k, H, Hk, D)
+    drop = (0.4, 0x5EED, 9)
+    whole = O.backward(q, k, v, do, cu_q, cu_k, 0.7, True, dropout=drop)
+    o_whole, lse_whole = O.forward(q, k, v, cu_q, cu_k, 0.7, True, dropout=drop)
+    G = H // Hk
+    for s, g in [(1, 1), (2, 0)]:
+        qs, ks = slice(cu_q[s], cu_q[s + 1]), slice(cu_k[s], cu_k[s + 1])
+        heads = list(range(g * G, (g + 1) * G))
+        args = (q[qs][:, heads], k[ks][:, [g]], v[ks][:, [g]])
+        cu1q, cu1k = [0, lens_q[s]], [0, lens_k[s]]
+        unit = O.backward(*args, do[qs][:, heads], cu1q, cu1k, 0.7, True, dropout=drop,
+                          drop_base=(s, g * G, H))
+        assert np.array_equal(unit["dq"], whole["dq"][qs][:, heads])
+        o, lse = O.forward(*args, cu1q, cu1k, 0.7, True, dropout=drop, drop_base=(s, g * G, H))
+        assert np.array_equal(o, o_whole[qs][:, heads])
+        assert np.array_equal(lse, lse_whole[qs][:, heads])
+        # dK, dV of the whole call sum the group's heads only
+        assert np.array_equal(unit["dk"], whole["dk"][ks][:, [g]])
+        assert np.array_equal(unit["dv"], whole["dv"][ks][:, [g]])
+        other = O.backward(*args, do[qs][:, heads], cu1q, cu1k, 0.7, True, dropout=drop)
+        assert np.abs(other["dv"] - unit["dv"]).max() > 0.1 * np.abs(unit["dv"]).max()
+    with pytest.raises(RuntimeError):
+        O.backward(q, k, v, do, cu_q, cu_k, 0.7, True, dropout=drop, drop_base=(0, 1, H))
