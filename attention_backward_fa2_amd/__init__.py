@@ -68,7 +68,8 @@ class FaBwdWsLayout(ctypes.Structure):
         ("k_tile", ctypes.c_int32),
         ("off_lse2", ctypes.c_size_t), ("off_rowdot", ctypes.c_size_t),
         ("off_dq_acc", ctypes.c_size_t), ("off_turns", ctypes.c_size_t),
-        ("off_flags", ctypes.c_size_t),
+        ("off_flags", ctypes.c_size_t), ("off_keep", ctypes.c_size_t),
+        ("keep_words", ctypes.c_int32),
         ("total_bytes", ctypes.c_size_t),
     ]
 

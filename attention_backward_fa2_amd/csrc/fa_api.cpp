@@ -259,6 +259,13 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
         off = align256(off + (size_t)p.batch * p.H * p.mtiles * sizeof(int32_t));
     ws.off_flags = off;
     off = align256(off + 4 * sizeof(int32_t));
+    // Dropout keep bits, written by the dQ pass for the key-tile kernel (the
+    // accumulate mode's key-tile kernel draws them itself).
+    ws.off_keep = off;
+    if (p.drop_p > 0.f && !p.fused_dq) {
+        ws.keep_words = 2 * ((p.Sk + 63) / 64);
+        off = align256(off + (size_t)ws.keep_words * hr * sizeof(uint32_t));
+    }
     ws.total_bytes = off;
     pl->dpad = dpad;
 
@@ -276,6 +283,7 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
         p.dq_acc = p.fused_dq ? (float *)(base + ws.off_dq_acc) : nullptr;
         p.turns = p.fused_dq ? (int *)(base + ws.off_turns) : nullptr;
         p.flags = (int *)(base + ws.off_flags);
+        p.keep = ws.keep_words ? (uint32_t *)(base + ws.off_keep) : nullptr;
     }
     g_last_error.clear();
     return FA_OK;

@@ -336,6 +336,7 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
         constexpr int RA = 4;                        // read-ahead (divides NSLOT)
         constexpr int BAR = (2 * NB + NQ / 2 < NSLOT - RA) ? 2 * NB + NQ / 2 : NSLOT - RA - 1;
         static_assert(NSLOT % RA == 0, "ring length must divide the slot count");
+        static_assert(NBUF != 3 || BAR + 1 >= 2 * NB, "keep words stored after the last Philox call");
         static_assert(BAR >= 2 * NB - RA && BAR + RA < NSLOT, "barrier slot");
         constexpr int LPT = 2 * PERW;             // loads per wave per tile
 
@@ -445,6 +446,22 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
                 kw |= keep_nibble(c0, row, drop_c2, p) << (16 * mb + 4 * r4);
             };
 
+            // The tile's keep bits for the key-tile kernel: lane half g
+            // writes the word of keys 32*g .. 32*g+31 (word 2t + g) of its
+            // row, nibble 2*r4 + g2 of it from lane half g2 (one exchange
+            // between the halves).
+            auto keep_store = [&]() {
+                const uint32_t other = (uint32_t)__shfl_xor((int)kw, 32);
+                const int ln = lane_here();
+                const int g = ln >> 5;
+                const uint32_t n_lo = g ? other >> 16 : kw & 0xFFFFu;   // half 0's nibbles
+                const uint32_t n_hi = g ? kw >> 16 : other & 0xFFFFu;   // half 1's nibbles
+                const uint32_t word = spread_nibbles(n_lo) | (spread_nibbles(n_hi) << 4);
+                const int row = r0w + (ln & 31);
+                if (row < Lq)
+                    p.keep[((int64_t)(2 * t + g) * p.H + h) * p.rows + si.ws_row + row] = word;
+            };
+
             static_for<NSLOT>([&](auto ic) {
                 constexpr int i = decltype(ic)::value;
                 const e16x8 a = ring[i % RA];
@@ -452,6 +469,10 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
                     ring[i % RA] = op_read(IC<i + RA>{});
                 else if constexpr (NBUF == 3)
                     ring[i % RA] = op_read(IC<i + RA - NSLOT>{});   // next tile
+                // after the tile's last Philox call; with three buffers after
+                // the barrier slot's wait for every load (and store) in flight
+                if constexpr (DROP && i == (NBUF == 3 ? BAR + 1 : 2 * NB))
+                    keep_store();
                 // Philox calls: block 0's over its S^T / dP^T slots, block 1's
                 // over the next NB slots (before each block's dS)
                 if constexpr (DROP && i < 2 * NB)

@@ -66,6 +66,11 @@ struct Params {
     // (drop_k0, drop_k1), last counter word drop_c3.
     float drop_p, drop_inv;
     uint32_t drop_thr, drop_k0, drop_k1, drop_c3;
+    // Keep bits of the separate-dQ backward with dropout: word w of row r of
+    // head h (keys 32 w .. 32 w + 31 of the row's sequence, bit x for key
+    // 32 w + x) at keep[(w * H + h) * rows + r]; written by the dQ kernel,
+    // read by the key-tile kernel.  Null otherwise.
+    uint32_t *keep;
     int fused_dq;       // 1: dQ partials added into dq_acc by the key-tile kernel
     int f16;            // 1: fp16 elements, 0: bf16
 };

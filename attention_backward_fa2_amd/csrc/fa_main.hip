@@ -68,9 +68,16 @@ struct __attribute__((aligned(16))) QBuf {
     float rowdot[kQTile];
 };
 
-template <int DP, int NBUF>
+// With dropout in the separate-dQ mode a tile also carries each wave's keep
+// words: the word of the wave's 32 keys for each of the 64 rows.
+template <int DP>
+struct __attribute__((aligned(16))) QBufKeep : QBuf<DP> {
+    uint32_t keep[kThreads / 64][kQTile];
+};
+
+template <int DP, int NBUF, bool KEEP = false>
 struct __attribute__((aligned(16))) TileSmem {
-    QBuf<DP> buf[NBUF];
+    std::conditional_t<KEEP, QBufKeep<DP>, QBuf<DP>> buf[NBUF];
 };
 
 template <int DP>
@@ -222,7 +229,10 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
     // start and waits for it at its end.
     constexpr bool TWO = FUSED || BIG;
     constexpr int NBUF = TWO ? 2 : 3;
-    using Smem = std::conditional_t<FUSED, FusedSmem<DP>, TileSmem<DP, NBUF>>;
+    // Dropout keep bits: drawn here in the fused mode, else read from the
+    // words the dQ kernel (which runs first) wrote.
+    constexpr bool KEEP = DROP && !FUSED;
+    using Smem = std::conditional_t<FUSED, FusedSmem<DP>, TileSmem<DP, NBUF, KEEP>>;
     __shared__ Smem sm;
 
     const int tid = threadIdx.x;
@@ -334,8 +344,9 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         //             c16 & 1;
         //  rv0:       lse2 / rowdot of row 4*g2.
         // All move to the next buffer (cyclically) after each tile.
-        constexpr int BUFB = (int)sizeof(QBuf<DP>);
-        int gq[KS], tq[DBL][2], rv0;
+        using Buf = std::conditional_t<KEEP, QBufKeep<DP>, QBuf<DP>>;
+        constexpr int BUFB = (int)sizeof(Buf);
+        int gq[KS], tq[DBL][2], rv0, kv0 = 0;
         {
             const int sw = swz<L::PCH>(l32);
 #pragma unroll
@@ -352,6 +363,8 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                                  (c16 & 1) * 8;
                 }
             rv0 = 2 * L::BYTES + 16 * g2;
+            if constexpr (KEEP)   // keep word of row 4*g2 of the wave's rows
+                kv0 = (int)sizeof(QBuf<DP>) + w * 4 * kQTile + 16 * g2;
         }
         const uint8_t *lds = reinterpret_cast<const uint8_t *>(&sm.buf[0]);
 
@@ -384,12 +397,21 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         const float *nr_head = ((w & 1) ? p.rowdot : p.lse2) + si.ws_row + (int64_t)h0 * p.rows + q0_first;
         const uint16_t *nq_ptr = nq_head, *nd_ptr = nd_head;
         const float *nr_ptr = nr_head;
+        // The keep words of the wave's 32 keys (word (n0 + 32 kgrp) / 32)
+        // sit a fixed distance from the row vectors of the same (head, row)
+        // (both arrays are [.][head][row] of 4-byte values in the workspace).
+        int64_t kdelta = 0;
+        if constexpr (KEEP) {
+            const int kwi = (n0 >> 5) + kgrp;
+            kdelta = reinterpret_cast<const char *>(p.keep + (int64_t)kwi * p.H * p.rows) -
+                     reinterpret_cast<const char *>((w & 1) ? p.rowdot : p.lse2);
+        }
         int n_r = 0, n_q0 = q0_first, n_left = total;
         const int64_t step_q = (int64_t)dq0 * p.q_ss, step_d = (int64_t)dq0 * p.do_ss;
         // Buffer descriptors of the next tile (bounded by its valid rows),
         // formed in three parts (q, dO, row vectors) that can sit in
         // different MFMA slots.
-        u32x4_rsrc rq_n, rd_n, rr_n;
+        u32x4_rsrc rq_n, rd_n, rr_n, rk_n;
         int n_rv = 0;
         auto prep_part = [&](auto pc) {
             constexpr int part = decltype(pc)::value;
@@ -408,14 +430,20 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 keep_scalar_here(n_rv, nr_ptr);
                 rr_n = make_rsrc(nr_ptr, (uint32_t)n_rv * 4);
                 keep_scalar_here(rr_n);
+                if constexpr (KEEP) {
+                    rk_n = make_rsrc(reinterpret_cast<const char *>(nr_ptr) + kdelta,
+                                     (uint32_t)n_rv * 4);
+                    keep_scalar_here(rk_n);
+                }
             }
         };
-        // Loads per wave per tile (each Q / dO wave load, and lse2 / rowdot).
-        constexpr int LPT = 2 * L::PERW + 1;
+        // Loads per wave per tile (each Q / dO wave load, lse2 / rowdot, and
+        // the keep words).
+        constexpr int LPT = 2 * L::PERW + 1 + (KEEP ? 1 : 0);
         // Load j of the next tile into buffer bf.
         auto issue_one = [&](auto jc, int bf) {
             constexpr int j = decltype(jc)::value;
-            QBuf<DP> &qbuf = sm.buf[bf];
+            Buf &qbuf = sm.buf[bf];
             if constexpr (j < 2 * L::PERW) {
                 constexpr int i = j >> 1;
                 const int ld = (w * L::PERW + i) * 1024;
@@ -423,10 +451,12 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     load16_to_lds(rd_n, qbuf.dO + ld, vod[i]);
                 else
                     load16_to_lds(rq_n, qbuf.q + ld, voq[i]);
-            } else {
+            } else if constexpr (j == 2 * L::PERW) {
                 // lse2 (even waves) / rowdot (odd waves): the two waves of a
                 // kind write the same values.
                 load4_to_lds(rr_n, (w & 1) ? qbuf.rowdot : qbuf.lse2, (uint32_t)lane * 4);
+            } else if constexpr (KEEP) {
+                load4_to_lds(rk_n, qbuf.keep[w], (uint32_t)lane * 4);
             }
         };
         // Move the row pointers on to the tile after (branch-free selects),
@@ -572,6 +602,8 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             // dropout keep bits of the tile: bit 16*mb + 4*t + r4 for the
             // lane's key and row 32*mb + 8*r4 + 4*g2 + t
             uint32_t kw = 0;
+            u32x4 kq[4];
+            constexpr int KD = NB / 4 > 2 ? 2 : 1;
             e16x8 pb[4], dsb[4];
             e16x4 ph[4], dh[4];
             f32x4 l2v[4];
@@ -649,9 +681,24 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     ring[i % RA] = op_read(IC<i + RA>{});
                 else if constexpr (!TWO)
                     ring[i % RA] = op_read(IC<i + RA - NSLOT>{});   // next tile
+                // Keep words (separate-dQ mode): the four rows of group
+                // (block, r4) read from LDS where the Philox call would be,
+                // this lane's key bit of each moved into kw KD slots later.
+                if constexpr (KEEP && i < 2 * NB)
+                    static_for<4>([&](auto rc) {
+                        constexpr int r4 = decltype(rc)::value, mb = i / NB;
+                        if constexpr ((i % NB) == r4 * NB / 4)
+                            kq[r4] = *reinterpret_cast<const u32x4 *>(lds + kv0 + 4 * (32 * mb + 8 * r4));
+                        if constexpr ((i % NB) == r4 * NB / 4 + KD)
+                            static_for<4>([&](auto tc) {
+                                constexpr int t = decltype(tc)::value;
+                                kw |= __builtin_amdgcn_ubfe(kq[r4][t], (uint32_t)l32, 1u)
+                                      << (16 * mb + 4 * t + r4);
+                            });
+                    });
                 // Philox calls: block 0's over its S / dP slots, block 1's
                 // over the next NB slots (before each block's P and dS)
-                if constexpr (DROP && i < 2 * NB)
+                if constexpr (DROP && !KEEP && i < 2 * NB)
                     static_for<4>([&](auto rc) {
                         constexpr int r4 = decltype(rc)::value;
                         if constexpr ((i % NB) == r4 * NB / 4)
@@ -723,6 +770,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     for (int ks = 0; ks < KS; ++ks)
                         gq[ks] += delta;
                     rv0 += delta;
+                    kv0 += delta;
                     // The only loads in flight are the next tile's (issued
                     // at this slot of the previous tile).
                     // (A bare barrier: the LDS reads still in flight read
@@ -770,6 +818,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     tq[db][1] += delta;
                 }
                 rv0 += delta;
+                kv0 += delta;
                 wait_loads<0>();
                 __syncthreads();   // next tile in LDS; dS^T[cur] complete
                 if constexpr (FUSED) {

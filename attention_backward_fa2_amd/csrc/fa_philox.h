@@ -42,6 +42,13 @@ __device__ inline uint32_t keep_nibble(uint32_t c0, uint32_t c1, uint32_t c2, co
     return (w0 >= t ? 1u : 0u) | (w1 >= t ? 2u : 0u) | (w2 >= t ? 4u : 0u) | (w3 >= t ? 8u : 0u);
 }
 
+// Nibble r (bits 4r .. 4r+3) of a 16-bit value moved to bits 8r .. 8r+3.
+__device__ inline uint32_t spread_nibbles(uint32_t x)
+{
+    x = (x | (x << 8)) & 0x00FF00FFu;
+    return (x | (x << 4)) & 0x0F0F0F0Fu;
+}
+
 // Dropout multiplier of a keep bit: 1 / (1 - p) if set, else 0.
 __device__ inline float keep_mult(uint32_t bits, int pos, float inv)
 {

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define FA_BWD_ABI_VERSION 6
+#define FA_BWD_ABI_VERSION 7
 
 typedef enum {
     FA_OK = 0,
@@ -211,13 +211,21 @@ typedef struct fa_bwd_args {
  *            (dq_accumulate = 1 only)
  *   flags  : int32[4]  flags[0] != 0 if an ordered wait gave up (should
  *                      never happen; dq is then not bit-reproducible)
+ *   keep   : uint32[keep_words][num_heads][rows]  dropout keep bits (dropout_p
+ *            > 0 and dq_accumulate = 0 only; zero bytes otherwise): bit x of
+ *            word w of a row is the keep bit of key 32 w + x of its sequence;
+ *            keep_words = 2 * ceil(seqlen_k / 64) (max_seqlen_k when packed).
+ *            Written by the dq step for every key tile a row's query tile
+ *            visits (words of keys a row cannot see may hold anything), read
+ *            by the main step instead of drawing the bits again.
  */
 typedef struct fa_bwd_ws_layout {
     int64_t rows;
     int32_t head_dim_pad;
     int32_t q_tile;                /* 64: rows per query tile */
     int32_t k_tile;                /* 128: keys per workgroup */
-    size_t off_lse2, off_rowdot, off_dq_acc, off_turns, off_flags;
+    size_t off_lse2, off_rowdot, off_dq_acc, off_turns, off_flags, off_keep;
+    int32_t keep_words;            /* 0 when there is no keep region */
     size_t total_bytes;
 } fa_bwd_ws_layout;
 
@@ -242,7 +250,9 @@ fa_status fa_bwd(const fa_bwd_args *a, void *stream);
  * fa_bwd_preprocess writes lse2 / rowdot (and, with dq_accumulate = 1, clears
  * the accumulator); fa_bwd_dq writes the same lse2 / rowdot values (bit for
  * bit) itself and needs nothing before it; fa_bwd_main needs a completed
- * fa_bwd_preprocess or fa_bwd_dq on the same workspace; fa_bwd_dq_convert
+ * fa_bwd_preprocess or fa_bwd_dq on the same workspace (with dropout_p > 0 and
+ * dq_accumulate = 0, a completed fa_bwd_dq: it writes the keep bits that
+ * fa_bwd_main reads); fa_bwd_dq_convert
  * needs a completed fa_bwd_main.  fa_bwd_dq requires dq_accumulate = 0 and
  * fa_bwd_dq_convert dq_accumulate = 1 (FA_ERR_INVALID_ARG otherwise). */
 fa_status fa_bwd_preprocess(const fa_bwd_args *a, void *stream);

@@ -86,7 +86,10 @@ def run_gpu(pr: Prepared, deterministic=False, out_pad=0, step_split=False, dq_a
         for step in steps:
             fa.run(args, step)
     elif step_split:
-        for step in ("preprocess", "main", "dq_convert" if dq_accumulate else "dq"):
+        # separate mode: dq before main (with dropout main reads the keep
+        # bits dq writes)
+        for step in (("preprocess", "main", "dq_convert") if dq_accumulate else
+                     ("preprocess", "dq", "main")):
             fa.run(args, step)
     else:
         fa.run(args, "all")

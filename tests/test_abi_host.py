@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(fa.EXPORTED)
-    assert lib.fa_bwd_abi_version() == 6
+    assert lib.fa_bwd_abi_version() == 7
 
 
 @pytest.mark.parametrize("header,struct,mirror", [
@@ -119,6 +119,22 @@ def test_separate_dq_mode_needs_no_accumulator():
         return (x + 255) // 256 * 256
     assert lay.off_dq_acc == lay.off_turns == lay.off_flags == 2 * al(8 * rows * 4)
     assert lay.total_bytes == lay.off_flags + 256
+
+
+def test_dropout_keep_region_in_the_separate_dq_mode_only():
+    """With dropout, the separate-dQ backward keeps one 32-key word per (key
+    word, head, row): 2 * ceil(seqlen_k / 64) words, after the flags; the
+    accumulate mode and calls without dropout have none."""
+    def al(x):
+        return (x + 255) // 256 * 256
+    rows = 2 * 256
+    lay = fa.workspace_layout(_args(dropout_p=0.1))
+    assert lay.keep_words == 2 * ((384 + 63) // 64) == 12
+    assert lay.off_keep == lay.off_flags + 256
+    assert lay.total_bytes == lay.off_keep + al(12 * 8 * rows * 4)
+    for over in ({"dropout_p": 0.1, "dq_accumulate": 1}, {"dropout_p": 0.0}):
+        lay = fa.workspace_layout(_args(**over))
+        assert lay.keep_words == 0 and lay.total_bytes == lay.off_keep == lay.off_flags + 256
 
 
 def test_step_entry_points_check_the_dq_mode_before_launching():

@@ -222,3 +222,55 @@ def test_dropout_full_size_sampled_units(gpu_lib):
                     base.heads_k, base.seqlen_q, base.seqlen_k, base.head_dim, True,
                     seed=base.seed, dropout=(0.1, SEED, 0))
     PT.check_full_size_units(W.make_inputs(wl), units=((0, 0), (1, 7)))
+
+
+@pytest.mark.parametrize("name", ["causal_gqa2_d128_p0.25", "varlen_causal_left64_cap1.5_d96_p0.25",
+                                  "causal_sq_gt_sk_empty_rows_d128_p0.125",
+                                  "two_sided_window_d128_p0.1"])
+def test_dq_pass_writes_the_oracles_keep_bits(gpu_lib, prepared, name):
+    """The separate-dQ backward hands the key-tile kernel the keep bits
+    through the workspace (word w of a row: keys 32w .. 32w+31); on every
+    element a row sees, the word's bit equals the oracle's keep bit."""
+    _flush("dropout keep words %s" % name)
+    pr = prepared(name)
+    wl = pr.inp.wl
+    res = PT.run_gpu(pr)
+    lay = res["layout"]
+    kwn, H, rows = lay.keep_words, wl.heads, lay.rows
+    assert kwn == 2 * ((max(pr.inp.lens_k) + 63) // 64)
+    words = res["ws"][lay.off_keep:lay.off_keep + kwn * H * rows * 4].view(torch.int32)
+    words = words.numpy().view(np.uint32).reshape(kwn, H, rows)
+    p, seed, offset = wl.dropout_f32
+    lw, rw = wl.window_sizes
+    checked = 0
+    for s, (lq, lk) in enumerate(zip(pr.inp.lens_q, pr.inp.lens_k)):
+        if lq == 0 or lk == 0:
+            continue
+        r0 = int(pr.cu_q[s]) if wl.varlen else s * wl.seqlen_q
+        i = np.arange(lq)[:, None]
+        j = np.arange(lk)[None, :]
+        d = i + lk - lq
+        vis = np.ones((lq, lk), bool)
+        if wl.causal:
+            vis &= j <= d
+        if rw >= 0:
+            vis &= j <= d + rw
+        if lw >= 0:
+            vis &= j >= d - lw
+        for h in range(H):
+            ref = O.dropout_mask(p, seed, offset, s, h, H, lq, lk)
+            got = (words[j // 32, h, r0 + i] >> (j % 32).astype(np.uint32)) & 1
+            assert np.array_equal(got[vis], ref[vis]), (s, h)
+            checked += int(vis.sum())
+    assert checked > 0
+
+
+def test_dropout_step_by_step_equals_whole_call(gpu_lib, prepared):
+    """preprocess, dq, main as separate calls (main reading the keep bits the
+    dq step wrote) give the whole call's gradients bit for bit."""
+    _flush("dropout step by step")
+    pr = prepared("causal_gqa2_d128_p0.25")
+    a = PT.run_gpu(pr)
+    b = PT.run_gpu(pr, step_split=True)
+    for key in ("dq", "dk", "dv"):
+        assert torch.equal(a[key].view(torch.int16), b[key].view(torch.int16)), key
