@@ -49,10 +49,13 @@ __device__ inline uint32_t spread_nibbles(uint32_t x)
     return (x | (x << 4)) & 0x0F0F0F0Fu;
 }
 
-// Dropout multiplier of a keep bit: 1 / (1 - p) if set, else 0.
+// Dropout multiplier of a keep bit: 1 / (1 - p) if set, else 0 (the bit
+// sign-extended to a full mask and ANDed with inv's bits: two operations,
+// no compare).
 __device__ inline float keep_mult(uint32_t bits, int pos, float inv)
 {
-    return (bits >> pos) & 1u ? inv : 0.f;
+    const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)bits, pos, 1);
+    return __builtin_bit_cast(float, m & __builtin_bit_cast(uint32_t, inv));
 }
 
 }  // namespace fa
