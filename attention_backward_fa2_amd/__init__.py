@@ -56,6 +56,7 @@ class FaBwdArgs(ctypes.Structure):
         ("dq_accumulate", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
+        ("dropout_keep_max_bytes", ctypes.c_size_t),
     ]
 
 
@@ -194,12 +195,15 @@ def _set_dropout(a, dropout):
 def make_args(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
               cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
               max_seqlen_k=None, deterministic=False, workspace=None,
-              dq_accumulate=False, window=None, softcap=0.0, dropout=None) -> FaBwdArgs:
+              dq_accumulate=False, window=None, softcap=0.0, dropout=None,
+              dropout_keep_max_bytes=0) -> FaBwdArgs:
     """Fill fa_bwd_args from tensors.  Dense tensors are (B, S, H, D); packed
     ones (total, H, D) with int32 device cu_seqlens and host max lengths.
     dq_accumulate=False: dQ by the separate query-tile pass (default);
     True: dQ partials accumulated in fp32 by the key-tile pass (atomic, or
-    ordered when deterministic) and converted afterwards."""
+    ordered when deterministic) and converted afterwards.
+    dropout_keep_max_bytes: bound on the dropout keep-bit region of the
+    workspace (0: the library's default)."""
     varlen = cu_seqlens_q is not None or cu_seqlens_k is not None
     a = FaBwdArgs()
     a.dtype = _DTYPES.get(q.dtype, 99)
@@ -233,6 +237,7 @@ def make_args(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
     _set_dropout(a, dropout)
     a.deterministic = int(bool(deterministic))
     a.dq_accumulate = int(bool(dq_accumulate))
+    a.dropout_keep_max_bytes = int(dropout_keep_max_bytes)
     if workspace is not None:
         a.workspace = workspace.data_ptr()
         a.workspace_bytes = workspace.numel() * workspace.element_size()

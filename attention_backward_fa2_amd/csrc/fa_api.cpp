@@ -261,10 +261,17 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
     off = align256(off + 4 * sizeof(int32_t));
     // Dropout keep bits, written by the dQ pass for the key-tile kernel (the
     // accumulate mode's key-tile kernel draws them itself).
+    // One bit per (row, key) pair: bounded (default 4 GiB), else the
+    // key-tile kernel draws the bits itself.
     ws.off_keep = off;
     if (p.drop_p > 0.f && !p.fused_dq) {
-        ws.keep_words = 2 * ((p.Sk + 63) / 64);
-        off = align256(off + (size_t)ws.keep_words * hr * sizeof(uint32_t));
+        const size_t kw = 2 * (size_t)((p.Sk + 63) / 64);
+        const size_t bytes = kw * hr * sizeof(uint32_t);
+        const size_t cap = a->dropout_keep_max_bytes ? a->dropout_keep_max_bytes : (size_t)4 << 30;
+        if (bytes <= cap) {
+            ws.keep_words = (int32_t)kw;
+            off = align256(off + bytes);
+        }
     }
     ws.total_bytes = off;
     pl->dpad = dpad;

@@ -472,7 +472,8 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
                 // after the tile's last Philox call; with three buffers after
                 // the barrier slot's wait for every load (and store) in flight
                 if constexpr (DROP && i == (NBUF == 3 ? BAR + 1 : 2 * NB))
-                    keep_store();
+                    if (p.keep)   // (no keep words when they would be too large)
+                        keep_store();
                 // Philox calls: block 0's over its S^T / dP^T slots, block 1's
                 // over the next NB slots (before each block's dS)
                 if constexpr (DROP && i < 2 * NB)

@@ -207,8 +207,9 @@ __device__ inline void dq_partial(const Params &p, FusedSmem<DP> &sm, int buf, i
 // LOCAL: a left window bounds the visible keys from below (win_l >= 0);
 // otherwise win_l < 0 and only the upper bound is masked.  SOFTCAP: scores
 // soft-capped (softcap > 0).  DROP: dropout replayed from the forward's rng
-// state (drop_p > 0).
-template <int DP, bool FUSED, bool F16, bool LOCAL, bool SOFTCAP, bool DROP>
+// state (drop_p > 0), 1: the keep bits drawn here, 2: read from the words
+// the dQ kernel wrote.
+template <int DP, bool FUSED, bool F16, bool LOCAL, bool SOFTCAP, int DROP>
 __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
 {
     constexpr int KS = DP / 16;       // MFMA k-steps over the head dim
@@ -231,7 +232,8 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
     constexpr int NBUF = TWO ? 2 : 3;
     // Dropout keep bits: drawn here in the fused mode, else read from the
     // words the dQ kernel (which runs first) wrote.
-    constexpr bool KEEP = DROP && !FUSED;
+    constexpr bool KEEP = DROP == 2;
+    static_assert(!(KEEP && FUSED), "the fused modes draw the keep bits");
     using Smem = std::conditional_t<FUSED, FusedSmem<DP>, TileSmem<DP, NBUF, KEEP>>;
     __shared__ Smem sm;
 
@@ -901,33 +903,44 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
     }
 }
 
+// Dropout mode of the key-tile kernel: 0 none, 1 draws the keep bits (fused
+// modes, or no keep words in the workspace), 2 reads the dQ pass's words.
+template <int D, bool FU, bool H16, bool LOCAL, bool SOFTCAP, bool DROP>
+static void launch_main_k(const Params &p, dim3 grid, hipStream_t st)
+{
+    const dim3 block(kThreads);
+    if constexpr (!DROP)
+        hipLaunchKernelGGL((fa_bwd_main_kernel<D, FU, H16, LOCAL, SOFTCAP, 0>), grid, block, 0, st, p);
+    else if constexpr (FU)
+        hipLaunchKernelGGL((fa_bwd_main_kernel<D, FU, H16, LOCAL, SOFTCAP, 1>), grid, block, 0, st, p);
+    else if (p.keep)
+        hipLaunchKernelGGL((fa_bwd_main_kernel<D, FU, H16, LOCAL, SOFTCAP, 2>), grid, block, 0, st, p);
+    else
+        hipLaunchKernelGGL((fa_bwd_main_kernel<D, FU, H16, LOCAL, SOFTCAP, 1>), grid, block, 0, st, p);
+}
+
 template <bool LOCAL, bool SOFTCAP, bool DROP>
 static hipError_t launch_main_t(const Params &p, int dpad, hipStream_t st)
 {
     const dim3 grid((unsigned)p.ntiles * p.Hk * p.batch);
     // head dims above 128: 64 keys per workgroup
     const dim3 grid_big((unsigned)((p.Sk + 63) / 64) * p.Hk * p.batch);
-    const dim3 block(kThreads);
-#define FA_LAUNCH_MAIN(D, FU, H16)                                                               \
-    hipLaunchKernelGGL((fa_bwd_main_kernel<D, FU, H16, LOCAL, SOFTCAP, DROP>), grid, block, 0,    \
-                       st, p)
-#define FA_LAUNCH_MAIN_BIG(D)                                                                    \
-    if (p.fused_dq)                                                                              \
-        return hipErrorInvalidValue;                                                             \
-    else if (p.f16)                                                                              \
-        hipLaunchKernelGGL((fa_bwd_main_kernel<D, false, true, LOCAL, SOFTCAP, DROP>), grid_big,  \
-                           block, 0, st, p);                                                     \
-    else                                                                                         \
-        hipLaunchKernelGGL((fa_bwd_main_kernel<D, false, false, LOCAL, SOFTCAP, DROP>), grid_big, \
-                           block, 0, st, p);
-#define FA_LAUNCH_MAIN_D(D)                                                                      \
-    if (p.fused_dq && p.f16)                                                                     \
-        FA_LAUNCH_MAIN(D, true, true);                                                           \
-    else if (p.fused_dq)                                                                         \
-        FA_LAUNCH_MAIN(D, true, false);                                                          \
-    else if (p.f16)                                                                              \
-        FA_LAUNCH_MAIN(D, false, true);                                                          \
-    else                                                                                         \
+#define FA_LAUNCH_MAIN(D, FU, H16) launch_main_k<D, FU, H16, LOCAL, SOFTCAP, DROP>(p, grid, st)
+#define FA_LAUNCH_MAIN_BIG(D)                                                   \
+    if (p.fused_dq)                                                             \
+        return hipErrorInvalidValue;                                            \
+    else if (p.f16)                                                             \
+        launch_main_k<D, false, true, LOCAL, SOFTCAP, DROP>(p, grid_big, st);    \
+    else                                                                        \
+        launch_main_k<D, false, false, LOCAL, SOFTCAP, DROP>(p, grid_big, st);
+#define FA_LAUNCH_MAIN_D(D)                                                     \
+    if (p.fused_dq && p.f16)                                                    \
+        FA_LAUNCH_MAIN(D, true, true);                                          \
+    else if (p.fused_dq)                                                        \
+        FA_LAUNCH_MAIN(D, true, false);                                         \
+    else if (p.f16)                                                             \
+        FA_LAUNCH_MAIN(D, false, true);                                         \
+    else                                                                        \
         FA_LAUNCH_MAIN(D, false, false);
     switch (dpad) {
     case 64:

@@ -39,7 +39,7 @@ KERNEL_SOURCES = ["attention_backward_fa2_amd/csrc/fa_main.hip",
                   "attention_backward_fa2_amd/csrc/fa_internal.h"]
 TRAFFIC_SUMMARY = "profiles/hbm_traffic_main_kernel_gqa_b2_h32_hk8_s4096_d128_causal.json"
 TRACE_SUMMARY = "profiles/kernel_trace_gqa_b2_h32_hk8_s4096_d128_causal.md"
-MAIN_KERNEL = "fa_bwd_main_kernel<128, false, false, false, false, false>"
+MAIN_KERNEL = "fa_bwd_main_kernel<128, false, false, false, false, 0>"
 
 
 def kernel_source_hash():
@@ -332,9 +332,11 @@ def window_suffix(wl):
 def main_kernel_name(fused, wl):
     local = wl.window is not None and wl.window[0] >= 0
     dpad = next(d for d in (64, 96, 128, 192, 256) if d >= wl.head_dim)
-    return "fa_bwd_main_kernel<%d, %s, false, %s, %s, %s>" % (
-        dpad, str(bool(fused)).lower(), str(local).lower(), str(wl.softcap > 0).lower(),
-        str(wl.dropout is not None).lower())
+    # dropout mode: 2 when the keep words of the dQ pass are read (separate
+    # dQ), 1 when drawn in the kernel (fused dQ)
+    drop = 0 if wl.dropout is None else (1 if fused else 2)
+    return "fa_bwd_main_kernel<%d, %s, false, %s, %s, %d>" % (
+        dpad, str(bool(fused)).lower(), str(local).lower(), str(wl.softcap > 0).lower(), drop)
 
 
 def fwd_kernel_name(wl):

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define FA_BWD_ABI_VERSION 7
+#define FA_BWD_ABI_VERSION 8
 
 typedef enum {
     FA_OK = 0,
@@ -197,6 +197,11 @@ typedef struct fa_bwd_args {
 
     void *workspace;               /* device, 256-byte aligned, caller-owned */
     size_t workspace_bytes;
+    /* Largest keep region (see the workspace layout) the call may use; 0: 4 GiB.
+     * The region is one bit per (query row, key) pair of every head, so it
+     * grows with seqlen_q * seqlen_k; above the bound the main step draws the
+     * keep bits itself instead (same bits, same results, slower). */
+    size_t dropout_keep_max_bytes;
 } fa_bwd_args;
 
 /*
@@ -212,7 +217,8 @@ typedef struct fa_bwd_args {
  *   flags  : int32[4]  flags[0] != 0 if an ordered wait gave up (should
  *                      never happen; dq is then not bit-reproducible)
  *   keep   : uint32[keep_words][num_heads][rows]  dropout keep bits (dropout_p
- *            > 0 and dq_accumulate = 0 only; zero bytes otherwise): bit x of
+ *            > 0, dq_accumulate = 0 and at most dropout_keep_max_bytes only;
+ *            zero bytes and keep_words = 0 otherwise): bit x of
  *            word w of a row is the keep bit of key 32 w + x of its sequence;
  *            keep_words = 2 * ceil(seqlen_k / 64) (max_seqlen_k when packed).
  *            Written by the dq step for every key tile a row's query tile

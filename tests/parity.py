@@ -55,7 +55,7 @@ class Prepared:
 
 
 def run_gpu(pr: Prepared, deterministic=False, out_pad=0, step_split=False, dq_accumulate=False,
-            steps=None):
+            steps=None, keep_max=0):
     """Backward on cuda:0.  Outputs start as NaN so unwritten elements show.
     out_pad > 0 gives dq/dk/dv a row pitch of head_dim + out_pad (strided
     views) to check that columns past head_dim are left alone."""
@@ -79,7 +79,8 @@ def run_gpu(pr: Prepared, deterministic=False, out_pad=0, step_split=False, dq_a
                   max_seqlen_q=max(inp.lens_q), max_seqlen_k=max(inp.lens_k))
     args = fa.make_args(do, q, k, v, o, lse, dq, dk, dv, wl.scale, wl.causal,
                         deterministic=deterministic, dq_accumulate=dq_accumulate,
-                        window=wl.window, softcap=wl.softcap, dropout=wl.dropout, **kw)
+                        window=wl.window, softcap=wl.softcap, dropout=wl.dropout,
+                        dropout_keep_max_bytes=keep_max, **kw)
     ws = fa.alloc_workspace(args, dev)
     ws.fill_(0xA5)   # garbage: the preprocess must clear what it uses
     if steps is not None:

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(fa.EXPORTED)
-    assert lib.fa_bwd_abi_version() == 7
+    assert lib.fa_bwd_abi_version() == 8
 
 
 @pytest.mark.parametrize("header,struct,mirror", [
@@ -132,7 +132,11 @@ def test_dropout_keep_region_in_the_separate_dq_mode_only():
     assert lay.keep_words == 2 * ((384 + 63) // 64) == 12
     assert lay.off_keep == lay.off_flags + 256
     assert lay.total_bytes == lay.off_keep + al(12 * 8 * rows * 4)
-    for over in ({"dropout_p": 0.1, "dq_accumulate": 1}, {"dropout_p": 0.0}):
+    # the bound: at it the region exists, one byte below it does not
+    need = 12 * 8 * rows * 4
+    assert fa.workspace_layout(_args(dropout_p=0.1, dropout_keep_max_bytes=need)).keep_words == 12
+    for over in ({"dropout_p": 0.1, "dq_accumulate": 1}, {"dropout_p": 0.0},
+                 {"dropout_p": 0.1, "dropout_keep_max_bytes": need - 1}):
         lay = fa.workspace_layout(_args(**over))
         assert lay.keep_words == 0 and lay.total_bytes == lay.off_keep == lay.off_flags + 256
 

@@ -274,3 +274,21 @@ def test_dropout_step_by_step_equals_whole_call(gpu_lib, prepared):
     b = PT.run_gpu(pr, step_split=True)
     for key in ("dq", "dk", "dv"):
         assert torch.equal(a[key].view(torch.int16), b[key].view(torch.int16)), key
+
+
+@pytest.mark.parametrize("name", ["causal_gqa2_d128_p0.25", "varlen_causal_left64_cap1.5_d96_p0.25"])
+def test_key_tile_kernel_drawing_its_own_bits_when_the_keep_region_is_bounded(gpu_lib, prepared,
+                                                                               name):
+    """With the keep region bounded below its size (1 byte) the workspace has
+    none and the key-tile kernel draws the bits itself: same bits, so the
+    gradients equal those of the default path bit for bit (and the oracle)."""
+    _flush("dropout without keep words %s" % name)
+    pr = prepared(name)
+    a = PT.run_gpu(pr)
+    b = PT.run_gpu(pr, keep_max=1)
+    assert a["layout"].keep_words > 0 and b["layout"].keep_words == 0
+    for key in ("dq", "dk", "dv"):
+        assert torch.equal(a[key].view(torch.int16), b[key].view(torch.int16)), key
+    ref = PT.oracle_backward(pr)
+    for key in ("dq", "dk", "dv"):
+        PT.compare(pr.inp.packed(b[key]), ref[key], "%s %s" % (name, key))
