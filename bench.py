@@ -103,6 +103,53 @@ def _pmc_means(path):
     return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
 
 
+def summarize_variant_trace(trace_dir, bench_args, out_dir):
+    """Write profiles/kernel_trace_<workload>.md from the outputs of
+        rocprofv3 --kernel-trace --stats -f csv -d TRACE_DIR -o c3 --
+            python bench.py BENCH_ARGS > TRACE_DIR.log
+    (a variant of the headline workload: another head dim, window, cap,
+    dropout or the forward), named for the workload its bench line reports."""
+    stats = _csv_rows(_find(trace_dir, "kernel_stats.csv"))
+    trace = _csv_rows(_find(trace_dir, "kernel_trace.csv"))
+    bench_line = None
+    with open(trace_dir.rstrip("/") + ".log") as fh:
+        for line in fh:
+            if line.startswith("{") and '"metric"' in line:
+                bench_line = json.loads(line)
+    steps, cfg = bench_line["steps"], bench_line["config"]
+    per_kernel = {}
+    for r in trace:
+        if "fa::" in r["Kernel_Name"]:
+            per_kernel.setdefault(_kname(r["Kernel_Name"]), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    rel = os.path.relpath(trace_dir, ROOT) if os.path.isabs(trace_dir) else trace_dir
+    lines = ["# Kernel trace: %s%s" % ("forward, " if cfg.get("pass") == "forward" else "",
+                                        cfg["workload"]), "",
+             "Workload: `%s` (%s)." % (json.dumps(cfg), bench_line["metric"]), "",
+             "Command (repo root, MI355X):", "",
+             "    rocprofv3 --kernel-trace --stats -f csv -d %s -o c3 -- python bench.py %s" % (
+                 rel, bench_args), "",
+             "| kernel | calls | average (us) | min (us) | max (us) | average of the %d timed "
+             "steps (us) |" % steps, "|---|---|---|---|---|---|"]
+    for r in stats:
+        if "fa::" in r["Name"]:
+            name = _kname(r["Name"])
+            timed = per_kernel[name][-steps:]
+            lines.append("| %s | %s | %.1f | %.1f | %.1f | %.1f |" % (
+                name, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                float(r["MaxNs"]) / 1e3, sum(timed) / len(timed)))
+    lines += ["", "Calls include the warm-up and any forward calls that produce the "
+              "backward's inputs; the timed-steps column averages the last %d calls." % steps, "",
+              "The same run's bench line: %.4f ms per step, %.1f TFLOP/s; per-kernel HIP-event "
+              "times (ms per launch): `%s`." % (bench_line["ms_per_step"], bench_line["value"],
+                                                json.dumps(bench_line.get("kernel_ms")))]
+    fwd = "fwd_" if cfg.get("pass") == "forward" else ""
+    path = os.path.join(out_dir, "kernel_trace_%s%s.md" % (fwd, cfg["workload"]))
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return path
+
+
 def summarize_profile(prof_dir, out_dir):
     """Write the profile summaries committed under profiles/ from the
     rocprofv3 outputs of the commands they list, run from the repo root
@@ -463,6 +510,9 @@ def main():
     ap.add_argument("--summarize-profile", metavar="PROF_DIR",
                     help="write the profiles/ summaries from rocprofv3 outputs in PROF_DIR "
                          "(trace/, FETCH_SIZE/, WRITE_SIZE/, copy_FETCH_SIZE/, copy_WRITE_SIZE/)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_ARGS"),
+                    help="write profiles/kernel_trace_<workload>.md from a rocprofv3 kernel "
+                         "trace of 'python bench.py BENCH_ARGS' in TRACE_DIR (log: TRACE_DIR.log)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB (4 times), the reference "
                          "kernel for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -470,6 +520,10 @@ def main():
 
     if args.summarize_profile:
         summarize_profile(args.summarize_profile, os.path.join(ROOT, "profiles"))
+        return
+    if args.summarize_trace:
+        print(summarize_variant_trace(args.summarize_trace[0], args.summarize_trace[1],
+                                      os.path.join(ROOT, "profiles")))
         return
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
