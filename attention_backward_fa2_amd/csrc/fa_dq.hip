@@ -443,7 +443,7 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
                 const int ln = lane_here();
                 const uint32_t c0 = (uint32_t)(n0 >> 2) + 8 * mb + 2 * r4 + (ln >> 5);
                 const uint32_t row = (uint32_t)(r0w + (ln & 31));
-                kw |= keep_nibble(c0, row, drop_c2, p) << (16 * mb + 4 * r4);
+                kw |= keep_nibble<false>(c0, row, drop_c2, p) << (16 * mb + 4 * r4);
             };
 
             // The tile's keep bits for the key-tile kernel: lane half g

@@ -17,8 +17,20 @@
 
 namespace fa {
 
+// a ^ b ^ k in one instruction: gfx950's three-input bit operation with
+// truth table 0x96 (inputs 0xF0, 0xCC, 0xAA); the compiler leaves the two
+// xors of each Philox round separate otherwise.
+__device__ inline uint32_t xor3_sk(uint32_t a, uint32_t b, uint32_t k)
+{
+    return __builtin_amdgcn_bitop3_b32(a, b, k, 0x96);
+}
+
 // Keep bits of keys 4*c0 .. 4*c0+3 of query row c1 (bit x: key 4*c0 + x).
 // c2 = b * H + h.  The key and the last counter word are wave-uniform.
+// X3: each round's two xors as one three-input operation (about a tenth of
+// the vector instructions of a dropout kernel fewer; the dQ kernel, which
+// has no register left, spills with it and keeps the two-xor form).
+template <bool X3 = true>
 __device__ inline uint32_t keep_nibble(uint32_t c0, uint32_t c1, uint32_t c2, const Params &p)
 {
     uint32_t w0 = c0, w1 = c1, w2 = c2, w3 = p.drop_c3;
@@ -31,8 +43,14 @@ __device__ inline uint32_t keep_nibble(uint32_t c0, uint32_t c1, uint32_t c2, co
         }
         const uint64_t p0 = (uint64_t)0xD2511F53u * w0;
         const uint64_t p1 = (uint64_t)0xCD9E8D57u * w2;
-        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ w1 ^ k0;
-        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ w3 ^ k1;
+        uint32_t n0, n2;
+        if constexpr (X3) {
+            n0 = xor3_sk((uint32_t)(p1 >> 32), w1, k0);
+            n2 = xor3_sk((uint32_t)(p0 >> 32), w3, k1);
+        } else {
+            n0 = (uint32_t)(p1 >> 32) ^ w1 ^ k0;
+            n2 = (uint32_t)(p0 >> 32) ^ w3 ^ k1;
+        }
         w1 = (uint32_t)p1;
         w3 = (uint32_t)p0;
         w0 = n0;
