@@ -541,3 +541,37 @@ def test_dropout_unit_with_base_replays_the_whole_call():
         assert np.abs(other["dv"] - unit["dv"]).max() > 0.1 * np.abs(unit["dv"]).max()
     with pytest.raises(RuntimeError):
         O.backward(q, k, v, do, cu_q, cu_k, 0.7, True, dropout=drop, drop_base=(0, 1, H))
+
+
+SUM_CASES = [
+    # (lens_q, lens_k, H, Hk, D, causal, window, dropout)
+    ([6, 9], [8, 7], 4, 2, 5, True, (-1, -1), None),
+    ([11], [6], 2, 1, 4, True, (-1, -1), None),            # rows without keys
+    ([10], [12], 2, 2, 3, False, (3, 2), None),
+    ([9, 7], [9, 10], 4, 1, 4, True, (-1, -1), (0.3, 77, 5)),
+]
+
+
+@pytest.mark.parametrize("case", SUM_CASES)
+@pytest.mark.parametrize("mode", ["contracted", "explicit"])
+def test_key_gradient_sums_to_zero_and_value_gradient_to_summed_dout(case, mode):
+    """Each row of dS sums to zero (P's rows sum to one; under dropout the
+    row term is sum_j P M dP, which cancels it too), so sum_j dK_j = 0 per
+    sequence and KV head; without dropout sum_j dV_j is the sum of dO over
+    the group's rows that see a key."""
+    lq, lk, H, Hk, D, causal, window, drop = case
+    q, k, v, do, cu_q, cu_k = _problem(55, lq, lk, H, Hk, D)
+    g = O.backward(q, k, v, do, cu_q, cu_k, 0.7, causal, mode=mode, window=window,
+                   dropout=drop)
+    _, lse = O.forward(q, k, v, cu_q, cu_k, 0.7, causal, window=window)
+    G = H // Hk
+    for s in range(len(lq)):
+        ks, qs = slice(cu_k[s], cu_k[s + 1]), slice(cu_q[s], cu_q[s + 1])
+        for kh in range(Hk):
+            dk = g["dk"][ks, kh]
+            assert np.abs(dk.sum(0)).max() <= 1e-12 * max(1.0, np.abs(dk).sum(0).max())
+            if drop is None:
+                heads = range(kh * G, (kh + 1) * G)
+                want = sum((do[qs, h] * np.isfinite(lse[qs, h])[:, None]).sum(0) for h in heads)
+                dv = g["dv"][ks, kh]
+                assert np.abs(dv.sum(0) - want).max() <= 1e-12 * max(1.0, np.abs(dv).sum(0).max())
