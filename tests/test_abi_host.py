@@ -300,3 +300,18 @@ def test_forward_validation_errors(over, status):
     assert lib.fa_bwd_last_error().decode() != ""
     assert lib.fa_fwd(ctypes.byref(a), None) == status     # rejected before any launch
     assert lib.fa_fwd(None, None) == fa.FA_ERR_INVALID_ARG
+
+
+def test_missing_library_fails_loudly():
+    """No CPU fallback: without the built library the binding raises (checked
+    in a fresh interpreter, since a loaded library is cached)."""
+    import subprocess
+    import sys
+    code = ("import attention_backward_fa2_amd as fa\n"
+            "try:\n"
+            "    fa.load_library('/nonexistent/libfa_bwd.so')\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0 and "raised: libfa_bwd.so is not built" in r.stdout, r.stdout + r.stderr
