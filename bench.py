@@ -79,9 +79,9 @@ def _find(root, suffix):
 
 
 WORKLOAD_TAG = "gqa_b2_h32_hk8_s4096_d128_causal"
-TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof/trace -o c3 -- "
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d {prof}/trace -o c3 -- "
              "python bench.py")
-FWD_TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof/fwd_trace -o c3 -- "
+FWD_TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d {prof}/fwd_trace -o c3 -- "
                  "python bench.py --forward")
 PMC_RUN = "python bench.py --no-cpu-baseline --steps 3 --warmup 1"
 SQ_PASSES = [
@@ -155,6 +155,11 @@ def summarize_profile(prof_dir, out_dir):
     rocprofv3 outputs of the commands they list, run from the repo root
     with the outputs under PROF_DIR (trace/ + trace.log, FETCH_SIZE/,
     WRITE_SIZE/, copy_FETCH_SIZE/, copy_WRITE_SIZE/, sq1/, sq2/)."""
+    # the commands as run: outputs under PROF_DIR (relative to the repo root)
+    rel = os.path.relpath(prof_dir, ROOT) if os.path.isabs(prof_dir) else prof_dir.rstrip("/")
+
+    def cmd(c):
+        return c.replace("{prof}", rel)
     # -- kernel trace: per-kernel durations, all calls and the timed steps --
     stats = _csv_rows(_find(os.path.join(prof_dir, "trace"), "kernel_stats.csv"))
     trace = _csv_rows(_find(os.path.join(prof_dir, "trace"), "kernel_trace.csv"))
@@ -172,7 +177,7 @@ def summarize_profile(prof_dir, out_dir):
     lines = ["# Kernel trace: %s" % WORKLOAD_TAG, "",
              "B=2, H=32, Hk=8, Sq=Sk=4096, D=128, causal, bf16; dQ by the separate "
              "query-tile kernel (the default path of `fa_bwd`).", "",
-             "Command (repo root, MI355X):", "", "    " + TRACE_CMD, "",
+             "Command (repo root, MI355X):", "", "    " + cmd(TRACE_CMD), "",
              "| kernel | calls | average (us) | min (us) | max (us) | average of the %d timed "
              "steps (us) |" % steps, "|---|---|---|---|---|---|"]
     for r in stats:
@@ -195,15 +200,16 @@ def summarize_profile(prof_dir, out_dir):
     res = {"kernel": MAIN_KERNEL, "workload": WORKLOAD_TAG,
            "source_files": KERNEL_SOURCES, "source_sha256": kernel_source_hash(),
            "commands": [
-               "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof/FETCH_SIZE -o c3 -- " + PMC_RUN,
-               "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof/WRITE_SIZE -o c3 -- " + PMC_RUN,
-               "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof/copy_FETCH_SIZE -o copy -- "
+               "rocprofv3 --pmc FETCH_SIZE -f csv -d {prof}/FETCH_SIZE -o c3 -- " + PMC_RUN,
+               "rocprofv3 --pmc WRITE_SIZE -f csv -d {prof}/WRITE_SIZE -o c3 -- " + PMC_RUN,
+               "rocprofv3 --pmc FETCH_SIZE -f csv -d {prof}/copy_FETCH_SIZE -o copy -- "
                "python bench.py --copy-calibration",
-               "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof/copy_WRITE_SIZE -o copy -- "
+               "rocprofv3 --pmc WRITE_SIZE -f csv -d {prof}/copy_WRITE_SIZE -o copy -- "
                "python bench.py --copy-calibration"],
            "note": "kib_per_dispatch is the counter's mean over the kernel's dispatches; "
                    "scale_factor = copied bytes / (counter KiB * 1024) of a 1 GiB "
                    "device-to-device copy"}
+    res["commands"] = [cmd(c) for c in res["commands"]]
     copy_bytes = float(1 << 30)
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         m = _pmc_means(_find(os.path.join(prof_dir, c), "counter_collection.csv"))
@@ -231,7 +237,7 @@ def summarize_profile(prof_dir, out_dir):
     cols = sorted({c for d in sq.values() for c in d})
     lines = ["# SQ counters per dispatch: %s" % WORKLOAD_TAG, "", "Commands (repo root, MI355X):", ""]
     for i, cs in enumerate(SQ_PASSES):
-        lines.append("    rocprofv3 --pmc %s -f csv -d gpurun_out/prof/sq%d -o c3 -- %s" % (
+        lines.append(cmd("    rocprofv3 --pmc %s -f csv -d {prof}/sq%d -o c3 -- %s") % (
             cs, i + 1, PMC_RUN))
     lines += ["", "| counter | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
     for c in cols:
@@ -257,7 +263,7 @@ def summarize_profile(prof_dir, out_dir):
                     fwd_line = json.loads(line)
         lines = ["# Kernel trace: forward, %s" % WORKLOAD_TAG, "",
                  "B=2, H=32, Hk=8, Sq=Sk=4096, D=128, causal, bf16; O and LSE by `fa_fwd`.",
-                 "", "Command (repo root, MI355X):", "", "    " + FWD_TRACE_CMD, "",
+                 "", "Command (repo root, MI355X):", "", "    " + cmd(FWD_TRACE_CMD), "",
                  "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
         for r in stats:
             if "fa::" in r["Name"]:
