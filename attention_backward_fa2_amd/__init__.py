@@ -103,8 +103,8 @@ class FaFwdArgs(ctypes.Structure):
 
 
 EXPORTED = ("fa_bwd", "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_dq", "fa_bwd_dq_convert",
-            "fa_bwd_validate", "fa_bwd_workspace_size", "fa_bwd_workspace_layout",
-            "fa_bwd_last_error", "fa_bwd_abi_version", "fa_fwd", "fa_fwd_validate")
+            "fa_bwd_debug_rowsum", "fa_bwd_validate", "fa_bwd_workspace_size",
+            "fa_bwd_workspace_layout", "fa_bwd_last_error", "fa_bwd_abi_version", "fa_fwd", "fa_fwd_validate")
 
 _LIB = None
 
@@ -123,6 +123,8 @@ def load_library(path: str = LIB_PATH):
         f = getattr(lib, name)
         f.argtypes = [P, ctypes.c_void_p]
         f.restype = ctypes.c_int
+    lib.fa_bwd_debug_rowsum.argtypes = [P, ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_bwd_debug_rowsum.restype = ctypes.c_int
     lib.fa_bwd_validate.argtypes = [P]
     lib.fa_bwd_validate.restype = ctypes.c_int
     lib.fa_bwd_workspace_size.argtypes = [P]
@@ -290,6 +292,24 @@ def run(args: FaBwdArgs, step: str = "all", stream=None):
     _check(f(ctypes.byref(args), _stream(stream)))
 
 
+def debug_rowsum(args: FaBwdArgs, d_out: torch.Tensor, stream=None):
+    """Enqueue fa_bwd_debug_rowsum: the preprocess step, also writing
+    D = rowsum(dO * O) into d_out, an fp32 tensor with the lse tensor's
+    shape and strides."""
+    if d_out.dtype != torch.float32:
+        raise ValueError("d_out must be float32")
+    _check(load_library().fa_bwd_debug_rowsum(ctypes.byref(args), d_out.data_ptr(),
+                                              _stream(stream)))
+
+
+def ordered_wait_gave_up(args: FaBwdArgs, workspace: torch.Tensor) -> bool:
+    """True if an ordered (deterministic accumulate-mode) wait of the last
+    call on this workspace gave up -- its dq is then not bit-reproducible.
+    Reads flags[0] of the workspace (synchronizes with the device)."""
+    off = workspace_layout(args).off_flags
+    return int(workspace[off:off + 4].view(torch.int32).item()) != 0
+
+
 def fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
            cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
            deterministic=False, workspace=None, stream=None, dq_accumulate=False,
@@ -298,13 +318,18 @@ def fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
 
     lse is the forward's natural-log log-sum-exp, (B, H, Sq) fp32 (packed:
     (num_seqs, H, max_seqlen_q)).  Returns the workspace tensor used (it
-    holds the fp32 dQ accumulator and the row sums afterwards)."""
+    holds the fp32 dQ accumulator and the row sums afterwards).
+    With dq_accumulate and deterministic both set, the call waits for the
+    device and raises if an ordered wait gave up (dq would then not be
+    bit-reproducible)."""
     args = make_args(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
                      cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                      deterministic, workspace, dq_accumulate, window, softcap, dropout)
     if workspace is None:
         workspace = alloc_workspace(args, q.device)
     run(args, "all", stream)
+    if deterministic and dq_accumulate and ordered_wait_gave_up(args, workspace):
+        raise FaError(FA_ERR_HIP, "an ordered dQ wait gave up: dq is not bit-reproducible")
     return workspace
 
 

@@ -305,13 +305,15 @@ fa_status hip_status(hipError_t e, const char *what)
 
 enum Step { kPre = 1, kMain = 2, kConv = 4, kDq = 8 };
 
-fa_status run(const fa_bwd_args *a, void *stream, int steps)
+// rowsum_out: debug copy of the row sums (preprocess step only), or null.
+fa_status run(const fa_bwd_args *a, void *stream, int steps, float *rowsum_out = nullptr)
 {
     Plan pl;
     fa_status st = make_plan(a, &pl, true);
     if (st)
         return st;
     hipStream_t s = (hipStream_t)stream;
+    pl.p.rowsum_out = rowsum_out;
     const fa::Params &p = pl.p;
     const bool has_rows = p.batch > 0 && p.Sq > 0 && p.rows > 0;
     const bool has_keys = p.batch > 0 && p.ntiles > 0;
@@ -497,6 +499,19 @@ fa_status fa_bwd(const fa_bwd_args *a, void *stream)
     return run(a, stream, a->dq_accumulate ? kPre | kMain | kConv : kDq | kMain);
 }
 fa_status fa_bwd_preprocess(const fa_bwd_args *a, void *stream) { return run(a, stream, kPre); }
+
+fa_status fa_bwd_debug_rowsum(const fa_bwd_args *a, float *D_out, void *stream)
+{
+    if (!a)
+        return fail(FA_ERR_INVALID_ARG, "args is NULL");
+    const bool varlen = a->cu_seqlens_q || a->cu_seqlens_k;
+    const int64_t nq = varlen ? a->total_q : (int64_t)a->batch * a->seqlen_q;
+    if (nq > 0 && !D_out)
+        return fail(FA_ERR_INVALID_ARG, "D_out is NULL");
+    if (!aligned(D_out, 4))
+        return fail(FA_ERR_INVALID_ARG, "D_out is not 4-byte aligned");
+    return run(a, stream, kPre, D_out);
+}
 fa_status fa_bwd_main(const fa_bwd_args *a, void *stream) { return run(a, stream, kMain); }
 fa_status fa_bwd_dq_convert(const fa_bwd_args *a, void *stream) { return run(a, stream, kConv); }
 fa_status fa_bwd_dq(const fa_bwd_args *a, void *stream) { return run(a, stream, kDq); }

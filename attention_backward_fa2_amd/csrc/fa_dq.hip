@@ -214,19 +214,20 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
     }
     // ---- lse2 and rowdot of the lane's row, written for the key-tile kernel
     //      (which runs after this one).  rowdot = sum_d dO * O with the same
-    //      operations in the same order as the preprocess kernel: each
-    //      16-byte chunk j of the row summed left to right, then the chunk
-    //      sums combined as the preprocess's butterfly over 16 lanes does
-    //      (partners j^8, j^4, j^2, j^1); chunk j = 2*ks + g2 lives in lane
-    //      half g2, so the first three steps are in-lane and the last one
-    //      pairs the two lane halves.  The results are bit-identical. ----
+    //      operations in the same order as the preprocess kernel, whose lane
+    //      c (of 16 per row) keeps one running sum over chunks c, c + 16, ...
+    //      of the row (16 bytes each, summed left to right) before a
+    //      butterfly over the 16 lanes (partners c^8, c^4, c^2, c^1).  Chunk
+    //      j = 2*ks + g2 lives in lane half g2 and belongs to preprocess lane
+    //      j % 16 = 2*(ks % 8) + g2, so cs[ks % 8] carries that lane's sum;
+    //      the first three butterfly steps are in-lane and the last one pairs
+    //      the two lane halves.  The results are bit-identical. ----
     float l2 = INFINITY, rd = 0.f;
     {
-        constexpr int NCS = KS > 8 ? KS : 8;
-        float cs[NCS];
+        float cs[8];
 #pragma unroll
-        for (int ks = 0; ks < NCS; ++ks)
-            cs[ks] = 0.f;
+        for (int c = 0; c < 8; ++c)
+            cs[c] = 0.f;
         if (qok) {
             const uint16_t *orow = p.o + row_offset(p, b, si.tok_q, qrow, p.o_sb, p.o_ss) + h * p.o_sh;
 #pragma unroll
@@ -236,31 +237,22 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
                     const uint4 ov = *reinterpret_cast<const uint4 *>(orow + d0);
                     const u32x4 dw = __builtin_bit_cast(u32x4, of[ks]);
                     const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w};
-                    float acc = 0.f;
+                    float acc = cs[ks & 7];
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         acc += elem2f<F16>((uint16_t)(ow[t] & 0xffff)) * elem2f<F16>((uint16_t)(dw[t] & 0xffff));
                         acc += elem2f<F16>((uint16_t)(ow[t] >> 16)) * elem2f<F16>((uint16_t)(dw[t] >> 16));
                     }
-                    cs[ks] = acc;
+                    cs[ks & 7] = acc;
                 }
             }
         }
-        float half;
-        if constexpr (KS <= 8) {
-            float a4[4];
+        float a4[4];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                a4[ks] = cs[ks] + cs[ks ^ 4];
-            const float a2_0 = a4[0] + a4[2], a2_1 = a4[1] + a4[3];
-            half = a2_0 + a2_1;
-        } else {
-            // (no preprocess pass runs at these head dims: any fixed order)
-            half = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                half += cs[ks];
-        }
+        for (int c = 0; c < 4; ++c)
+            a4[c] = cs[c] + cs[c ^ 4];
+        const float a2_0 = a4[0] + a4[2], a2_1 = a4[1] + a4[3];
+        const float half = a2_0 + a2_1;
         const float sum = half + __shfl_xor(half, 32);
         if (qok) {
             const float lse = p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + qrow];

@@ -71,6 +71,9 @@ struct Params {
     // 32 w + x) at keep[(w * H + h) * rows + r]; written by the dQ kernel,
     // read by the key-tile kernel.  Null otherwise.
     uint32_t *keep;
+    // Debug copy of rowdot in the lse layout (same batch / head strides,
+    // row stride 1), written by the preprocess kernel when not null.
+    float *rowsum_out;
     int fused_dq;       // 1: dQ partials added into dq_acc by the key-tile kernel
     int f16;            // 1: fp16 elements, 0: bf16
 };

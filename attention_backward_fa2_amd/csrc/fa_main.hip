@@ -160,9 +160,12 @@ __device__ inline void dq_partial(const Params &p, FusedSmem<DP> &sm, int buf, i
                     }
                     const int rank = jmax - j;
                     turn = p.turns + ((int64_t)b * p.H + h) * p.mtiles + m;
+                    // (wait while the turn is below this tile's rank: a late
+                    // add of a workgroup that gave up can push the counter
+                    // past a rank, which must then not wait forever)
                     if (tid == 0) {
                         int spins = 0;
-                        while (__hip_atomic_load(turn, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) !=
+                        while (__hip_atomic_load(turn, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) <
                                rank) {
                             __builtin_amdgcn_s_sleep(2);
                             if (++spins > kSpinLimit) {

@@ -14,6 +14,9 @@
 //                    (mma_one_m_block pointwise step 1).
 //   accumulate mode only: dq_acc[h][row][:] = 0, and (ordered adds) the
 //                    turn counter of the row's query tile = 0.
+//   debug copy (rowsum_out set): rowdot also written in the lse layout (the
+//                    softmax_d the backward call-trace page's
+//                    _flash_attn_backward returns for inspection).
 //
 // HBM-bound: reads O and dO once (2 * 2 * D bytes per row and head), writes
 // 8 bytes (+ 4 * D_pad in accumulate mode).  16 lanes per row; each lane owns
@@ -63,23 +66,28 @@ __global__ void __launch_bounds__(kThreads) fa_bwd_preprocess_kernel(Params p)
     if (c == 0) {
         const float lse = p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + i];
         p.rowdot[wr] = acc;
+        if (p.rowsum_out)
+            p.rowsum_out[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + i] = acc;
         p.lse2[wr] = (lse == -INFINITY) ? INFINITY : lse * 1.4426950408889634f;
         if (p.fused_dq && p.deterministic && (i % kQTile) == 0)
             p.turns[((int64_t)b * p.H + h) * p.mtiles + i / kQTile] = 0;
     }
-    if (!p.fused_dq)
-        return;
-    // Clear this row of the fp32 dQ accumulator: DP / 16 floats per lane.
-    constexpr int PER = DP / 16;
-    float *dst = p.dq_acc + wr * DP + c * PER;
-    if constexpr (PER % 4 == 0) {
+    // Accumulate mode (head_dim <= 128 only): clear this row of the fp32 dQ
+    // accumulator, DP / 16 floats per lane.
+    if constexpr (DP <= 128) {
+        if (!p.fused_dq)
+            return;
+        constexpr int PER = DP / 16;
+        float *dst = p.dq_acc + wr * DP + c * PER;
+        if constexpr (PER % 4 == 0) {
 #pragma unroll
-        for (int t = 0; t < PER; t += 4)
-            *reinterpret_cast<float4 *>(dst + t) = make_float4(0.f, 0.f, 0.f, 0.f);
-    } else {
+            for (int t = 0; t < PER; t += 4)
+                *reinterpret_cast<float4 *>(dst + t) = make_float4(0.f, 0.f, 0.f, 0.f);
+        } else {
 #pragma unroll
-        for (int t = 0; t < PER; t += 2)
-            *reinterpret_cast<float2 *>(dst + t) = make_float2(0.f, 0.f);
+            for (int t = 0; t < PER; t += 2)
+                *reinterpret_cast<float2 *>(dst + t) = make_float2(0.f, 0.f);
+        }
     }
 }
 
@@ -87,28 +95,23 @@ hipError_t launch_preprocess(const Params &p, int dpad, hipStream_t st)
 {
     const dim3 grid((p.Sq + kRowsPerBlock - 1) / kRowsPerBlock, p.H, p.batch);
     const dim3 block(kThreads);
+#define FA_PRE_CASE(D)                                                                    \
+    case D:                                                                               \
+        if (p.f16)                                                                        \
+            hipLaunchKernelGGL((fa_bwd_preprocess_kernel<D, true>), grid, block, 0, st, p);  \
+        else                                                                              \
+            hipLaunchKernelGGL((fa_bwd_preprocess_kernel<D, false>), grid, block, 0, st, p); \
+        break;
     switch (dpad) {
-    case 64:
-        if (p.f16)
-            hipLaunchKernelGGL((fa_bwd_preprocess_kernel<64, true>), grid, block, 0, st, p);
-        else
-            hipLaunchKernelGGL((fa_bwd_preprocess_kernel<64, false>), grid, block, 0, st, p);
-        break;
-    case 96:
-        if (p.f16)
-            hipLaunchKernelGGL((fa_bwd_preprocess_kernel<96, true>), grid, block, 0, st, p);
-        else
-            hipLaunchKernelGGL((fa_bwd_preprocess_kernel<96, false>), grid, block, 0, st, p);
-        break;
-    case 128:
-        if (p.f16)
-            hipLaunchKernelGGL((fa_bwd_preprocess_kernel<128, true>), grid, block, 0, st, p);
-        else
-            hipLaunchKernelGGL((fa_bwd_preprocess_kernel<128, false>), grid, block, 0, st, p);
-        break;
+        FA_PRE_CASE(64)
+        FA_PRE_CASE(96)
+        FA_PRE_CASE(128)
+        FA_PRE_CASE(192)
+        FA_PRE_CASE(256)
     default:
         return hipErrorInvalidValue;
     }
+#undef FA_PRE_CASE
     return hipGetLastError();
 }
 

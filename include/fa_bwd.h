@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define FA_BWD_ABI_VERSION 8
+#define FA_BWD_ABI_VERSION 9
 
 typedef enum {
     FA_OK = 0,
@@ -215,7 +215,10 @@ typedef struct fa_bwd_args {
  *   turns  : int32[batch][num_heads][ceil(seqlen_q / 64)] ordering counters
  *            (dq_accumulate = 1 only)
  *   flags  : int32[4]  flags[0] != 0 if an ordered wait gave up (should
- *                      never happen; dq is then not bit-reproducible)
+ *                      never happen; dq is then not bit-reproducible).  The
+ *                      call still returns FA_OK (the wait is on the device):
+ *                      a caller that relies on deterministic = 1 with
+ *                      dq_accumulate = 1 reads flags[0] after the call.
  *   keep   : uint32[keep_words][num_heads][rows]  dropout keep bits (dropout_p
  *            > 0, dq_accumulate = 0 and at most dropout_keep_max_bytes only;
  *            zero bytes and keep_words = 0 otherwise): bit x of
@@ -265,6 +268,24 @@ fa_status fa_bwd_preprocess(const fa_bwd_args *a, void *stream);
 fa_status fa_bwd_main(const fa_bwd_args *a, void *stream);
 fa_status fa_bwd_dq(const fa_bwd_args *a, void *stream);
 fa_status fa_bwd_dq_convert(const fa_bwd_args *a, void *stream);
+
+/* Debug read of D = rowsum(dO * O), the per-row term of dS = P (dP - D)
+ * (the softmax_d that the backward call-trace page's _flash_attn_backward
+ * returns, filled by the dsoftmax_sum step of set_params_dgrad): enqueues
+ * the preprocess step only (exactly fa_bwd_preprocess: the workspace's lse2 /
+ * rowdot are written, and with dq_accumulate = 1 the accumulator cleared)
+ * and also writes each row's D into D_out.
+ *   D_out : DEVICE float buffer with the layout and strides of `lse`
+ *           (D_out + b * lse_stride[0] + h * lse_stride[1] + i for query row
+ *           i of sequence / batch b and head h), caller-owned, 4-byte
+ *           aligned; entries of packed rows past a sequence's length are not
+ *           written.  It must not alias any input, output or the workspace.
+ *   D is sum_d dO_id * O_id in fp32 (exact 16-bit products, fixed order),
+ *   bit-identical to the value the backward's kernels use; it is computed
+ *   for every row, including rows whose LSE is -inf (their O is 0).
+ * Validation as fa_bwd (a workspace is required), plus D_out non-NULL when
+ * there are query rows (FA_ERR_INVALID_ARG). */
+fa_status fa_bwd_debug_rowsum(const fa_bwd_args *a, float *D_out, void *stream);
 
 /* Reason of the last non-FA_OK status on this thread ("" if none). */
 const char *fa_bwd_last_error(void);

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(fa.EXPORTED)
-    assert lib.fa_bwd_abi_version() == 8
+    assert lib.fa_bwd_abi_version() == 9
 
 
 @pytest.mark.parametrize("header,struct,mirror", [
@@ -227,6 +227,22 @@ def test_launch_entry_points_reject_before_touching_the_gpu():
     for name in ("fa_bwd", "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_dq", "fa_bwd_dq_convert"):
         assert getattr(lib, name)(ctypes.byref(a), None) == fa.FA_ERR_INVALID_ARG
     assert lib.fa_bwd(None, None) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_bwd_debug_rowsum(ctypes.byref(a), BASE, None) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_bwd_debug_rowsum(None, BASE, None) == fa.FA_ERR_INVALID_ARG
+
+
+def test_debug_rowsum_checks_its_output_before_touching_the_gpu():
+    """fa_bwd_debug_rowsum: D_out must be given (when there are query rows)
+    and 4-byte aligned; everything else is validated as for fa_bwd (a
+    workspace is required)."""
+    lib = fa.load_library()
+    a = _args()
+    _with_ws(a)
+    assert lib.fa_bwd_debug_rowsum(ctypes.byref(a), None, None) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_bwd_debug_rowsum(ctypes.byref(a), BASE + 2, None) == fa.FA_ERR_INVALID_ARG
+    b = _args()
+    assert lib.fa_bwd_debug_rowsum(ctypes.byref(b), BASE, None) == fa.FA_ERR_WORKSPACE
+    assert "workspace" in fa.load_library().fa_bwd_last_error().decode()
 
 
 def test_varlen_layout_uses_total_rows():
