@@ -103,7 +103,7 @@ class FaFwdArgs(ctypes.Structure):
 
 
 EXPORTED = ("fa_bwd", "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_dq", "fa_bwd_dq_convert",
-            "fa_bwd_debug_rowsum", "fa_bwd_validate", "fa_bwd_workspace_size",
+            "fa_bwd_debug_rowsum", "fa_bwd_noalloc", "fa_bwd_validate", "fa_bwd_workspace_size",
             "fa_bwd_workspace_layout", "fa_bwd_last_error", "fa_bwd_abi_version", "fa_fwd", "fa_fwd_validate")
 
 _LIB = None
@@ -119,7 +119,8 @@ def load_library(path: str = LIB_PATH):
             "libfa_bwd.so is not built (run python -c 'import __graft_entry__ as g; g.build()')")
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER(FaBwdArgs)
-    for name in ("fa_bwd", "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_dq", "fa_bwd_dq_convert"):
+    for name in ("fa_bwd", "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_dq", "fa_bwd_dq_convert",
+                 "fa_bwd_noalloc"):
         f = getattr(lib, name)
         f.argtypes = [P, ctypes.c_void_p]
         f.restype = ctypes.c_int
@@ -285,10 +286,13 @@ def _stream(stream) -> int:
 
 
 def run(args: FaBwdArgs, step: str = "all", stream=None):
-    """Enqueue one of 'all', 'preprocess', 'main', 'dq', 'dq_convert'."""
+    """Enqueue one of 'all', 'preprocess', 'main', 'dq', 'dq_convert', or
+    'noalloc' (the whole backward on the library's scratch array; the
+    args' workspace is ignored)."""
     lib = load_library()
     f = {"all": lib.fa_bwd, "preprocess": lib.fa_bwd_preprocess, "main": lib.fa_bwd_main,
-         "dq": lib.fa_bwd_dq, "dq_convert": lib.fa_bwd_dq_convert}[step]
+         "dq": lib.fa_bwd_dq, "dq_convert": lib.fa_bwd_dq_convert,
+         "noalloc": lib.fa_bwd_noalloc}[step]
     _check(f(ctypes.byref(args), _stream(stream)))
 
 

@@ -444,6 +444,17 @@ fa_status make_fwd_plan(const fa_fwd_args *a, fa::Params *pp, int *dpad_out)
 
 }  // namespace
 
+namespace fa {
+
+// Sets the thread's last-error message for the entry points defined in other
+// translation units.
+int report_error(int status, const char *msg)
+{
+    return fail((fa_status)status, "%s", msg);
+}
+
+}  // namespace fa
+
 extern "C" {
 
 fa_status fa_fwd_validate(const fa_fwd_args *a)

@@ -287,6 +287,26 @@ fa_status fa_bwd_dq_convert(const fa_bwd_args *a, void *stream);
  * there are query rows (FA_ERR_INVALID_ARG). */
 fa_status fa_bwd_debug_rowsum(const fa_bwd_args *a, float *D_out, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the whole
+ * backward as fa_bwd enqueues it, with `workspace` / `workspace_bytes`
+ * ignored and a scratch array owned by the library used instead.  No
+ * allocation happens on any call.
+ *   - The scratch array holds FA_BWD_NOALLOC_MAX_WORKSPACE bytes on every GPU
+ *     the library runs on, from library load to process end; a call whose
+ *     fa_bwd_workspace_size (computed without a dropout keep region) is larger
+ *     returns FA_ERR_WORKSPACE before touching the GPU.
+ *   - With dropout, the key-tile step draws the keep bits itself instead of
+ *     reading them from a keep region (same bits, bit-identical results).
+ *   - All calls on one GPU share its scratch array: calls that can overlap
+ *     on one GPU (different streams or threads, no ordering between them)
+ *     race and give wrong results.  Calls ordered on one stream are safe:
+ *     each call writes or clears the scratch it reads.
+ *   - Other arguments, semantics and errors as fa_bwd; FA_ERR_HIP also if
+ *     the scratch array's device address cannot be obtained. */
+#define FA_BWD_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+fa_status fa_bwd_noalloc(const fa_bwd_args *a, void *stream);
+
 /* Reason of the last non-FA_OK status on this thread ("" if none). */
 const char *fa_bwd_last_error(void);
 

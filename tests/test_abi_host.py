@@ -231,6 +231,23 @@ def test_launch_entry_points_reject_before_touching_the_gpu():
     assert lib.fa_bwd_debug_rowsum(None, BASE, None) == fa.FA_ERR_INVALID_ARG
 
 
+def test_noalloc_rejects_before_touching_the_gpu():
+    """fa_bwd_noalloc ignores the caller's workspace; a call whose workspace
+    (without a dropout keep region) exceeds the library's scratch array, or
+    with invalid arguments, is rejected on the host.  (No GPU here: any device
+    call would fail with FA_ERR_HIP instead.)"""
+    lib = fa.load_library()
+    big = _args(batch=64, seqlen_q=4096, seqlen_k=4096, num_heads=32, num_heads_k=8,
+                dq_accumulate=1)
+    assert fa.workspace_size(big) > (64 << 20)
+    assert lib.fa_bwd_noalloc(ctypes.byref(big), None) == fa.FA_ERR_WORKSPACE
+    msg = lib.fa_bwd_last_error().decode()
+    assert "fa_bwd_noalloc" in msg and str(64 << 20) in msg
+    bad = _args(num_heads_k=3)
+    assert lib.fa_bwd_noalloc(ctypes.byref(bad), None) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_bwd_noalloc(None, None) == fa.FA_ERR_INVALID_ARG
+
+
 def test_debug_rowsum_checks_its_output_before_touching_the_gpu():
     """fa_bwd_debug_rowsum: D_out must be given (when there are query rows)
     and 4-byte aligned; everything else is validated as for fa_bwd (a
