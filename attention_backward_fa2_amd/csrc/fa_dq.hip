@@ -32,8 +32,8 @@
 // math of keys 0-31, the dQ k-steps over keys 0-31 alongside the pointwise
 // math of keys 32-63, the dQ k-steps over keys 32-63.  Operand reads run a
 // fixed number of slots ahead, across tile boundaries; the wait for the next
-// tile, the workgroup barrier and the loads of the tile after next sit at
-// one slot of the dQ phase.
+// tile, the workgroup barrier and the loads of the tile after next sit early
+// in the tile, where the S^T / dP^T products leave the issue slots idle.
 //
 // LDS (D_pad = 128): 3 x (K, V) x 16 KB = 96 KB.
 #include "fa_mfma.h"
@@ -326,10 +326,13 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
         constexpr int NQ = 2 * DB;
         constexpr int NSLOT = 2 * NB + 2 * NQ;
         constexpr int RA = 4;                        // read-ahead (divides NSLOT)
-        constexpr int BAR = (2 * NB + NQ / 2 < NSLOT - RA) ? 2 * NB + NQ / 2 : NSLOT - RA - 1;
+        // the barrier and the loads of the tile after next early in the
+        // tile, where the S^T / dP^T products leave the issue slots idle; the
+        // 16-byte read offsets move at MOV, after the tile's last such read
+        constexpr int BAR = 2;
+        constexpr int MOV = 2 * NB;
         static_assert(NSLOT % RA == 0, "ring length must divide the slot count");
-        static_assert(NBUF != 3 || BAR + 1 >= 2 * NB, "keep words stored after the last Philox call");
-        static_assert(BAR >= 2 * NB - RA && BAR + RA < NSLOT, "barrier slot");
+        static_assert(BAR + 1 < NB && MOV >= 2 * NB - RA && MOV + RA < NSLOT, "slot events");
         constexpr int LPT = 2 * PERW;             // loads per wave per tile
 
         auto op_read = [&](auto ic) -> e16x8 {
@@ -461,9 +464,8 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
                     ring[i % RA] = op_read(IC<i + RA>{});
                 else if constexpr (NBUF == 3)
                     ring[i % RA] = op_read(IC<i + RA - NSLOT>{});   // next tile
-                // after the tile's last Philox call; with three buffers after
-                // the barrier slot's wait for every load (and store) in flight
-                if constexpr (DROP && i == (NBUF == 3 ? BAR + 1 : 2 * NB))
+                // after the tile's last Philox call
+                if constexpr (DROP && i == 2 * NB)
                     if (p.keep)   // (no keep words when they would be too large)
                         keep_store();
                 // Philox calls: block 0's over its S^T / dP^T slots, block 1's
@@ -528,16 +530,21 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
                         [&](auto ec) { pw_elem(IC<1>{}, IC<16 * u / NQ + decltype(ec)::value>{}); });
                 }
                 if constexpr (NBUF == 3 && i == BAR) {
+                    // every wave has finished with the last tile's buffer and
+                    // the only loads in flight are the next tile's (issued one
+                    // tile ago); a bare barrier (reads in flight touch this
+                    // tile's buffer only)
+                    wait_loads<0>();
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                }
+                if constexpr (NBUF == 3 && i == BAR + 1)
+                    issue(cur == 0 ? NBUF - 1 : cur - 1);
+                if constexpr (NBUF == 3 && i == MOV) {
                     // every 16-byte read of this tile is issued: move them on
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks)
                         gq[ks] += delta;
-                    // the only loads in flight are the next tile's; a bare
-                    // barrier (reads in flight touch this tile's buffer only)
-                    wait_loads<0>();
-                    __builtin_amdgcn_s_barrier();
-                    asm volatile("" ::: "memory");
-                    issue(cur == 0 ? NBUF - 1 : cur - 1);
                 }
                 if constexpr (NBUF == 3 && i == NSLOT - RA - 1) {
 #pragma unroll

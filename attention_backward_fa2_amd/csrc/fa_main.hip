@@ -520,23 +520,30 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         // MFMA and a share of the vector work; a scheduling fence after
         // every slot keeps this order.  Without the fused dQ, the reads run
         // ahead across the tile boundary, and the wait for the next tile's
-        // loads, the workgroup barrier and the issue of the loads of the tile
-        // after next sit at slot BAR, in the shadow of the MFMAs (with three
-        // buffers, a buffer refilled after the barrier of tile t held tile
-        // t-1, which every wave has finished by then).
+        // loads, the workgroup barrier, the loads of the tile after next and
+        // their scalar set-up sit early in the tile, in the shadow of the S /
+        // dP products, which leave most issue slots free (with three buffers,
+        // a buffer refilled after the barrier of tile t held tile t-1, which
+        // every wave has finished by then).
         constexpr int NB = 2 * KS;            // S / dP MFMAs per query block
         constexpr int NG = 4 * DBL;           // dV / dK MFMAs per two k-steps
         constexpr int NSLOT = 2 * NB + 2 * NG;
         constexpr int RA = 8;                 // read-ahead distance (slots)
-        constexpr int BAR = 2 * NB + NG / 2;  // barrier slot (non-fused)
+        // Non-fused (three buffers): the barrier early in the tile, where the
+        // S / dP products leave the issue slots idle; the loads of the tile
+        // after next and the scalar set-up of the one after that in the
+        // following slots; the 16-byte read offsets and the row-vector
+        // offset move to the next buffer at MOV, after the tile's last such
+        // read and before the next tile's first, followed by the next
+        // tile's rowdot reads.
+        constexpr int BAR = 2;                 // barrier slot
+        constexpr int NLD = (LPT + 1) / 2;     // load slots (two loads each)
+        constexpr int SU0 = BAR + 1 + NLD;     // first of six set-up slots
+        constexpr int MOV = NSLOT - RA - 6;    // read offsets to the next buffer
         // The ring of in-flight operands continues across tiles, so its
-        // length must divide the slot count; the barrier (and the move of
-        // the 16-byte read offsets to the next buffer) must come after the
-        // last such read and row-vector read of the tile and before the
-        // first read of the next tile.
+        // length must divide the slot count.
         static_assert(NB >= 8 && NG >= 8 && NSLOT % RA == 0, "slot plan");
-        static_assert(BAR >= 2 * NB && BAR + RA < NSLOT, "barrier slot");
-        static_assert(BAR + (LPT + 1) / 2 + 6 <= NSLOT, "tile loads after the barrier");
+        static_assert(SU0 + 6 <= MOV && MOV >= 2 * NB && MOV + 5 <= NSLOT - RA, "slot events");
 
         // A operand of slot i of a tile (offsets of the tile's buffer).
         auto op_read = [&](auto ic) -> e16x8 {
@@ -769,37 +776,40 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 if constexpr (i == NB || i == 2 * NB)
                     pin_acc();
                 if constexpr (!TWO && i == BAR) {
-                    // The 16-byte operand reads of this tile and its row
-                    // vectors are all issued: move them to the next buffer.
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks)
-                        gq[ks] += delta;
-                    rv0 += delta;
-                    kv0 += delta;
-                    // The only loads in flight are the next tile's (issued
-                    // at this slot of the previous tile).
-                    // (A bare barrier: the LDS reads still in flight read
-                    // this tile's buffer, which no load issued after the
-                    // barrier touches.)
+                    // Every wave has finished with the buffer of the last
+                    // tile, and the only loads in flight are the next tile's
+                    // (issued one tile ago): wait for them, then publish.
+                    // (A bare barrier: the LDS reads in flight read this
+                    // tile's buffer, which no load issued after the barrier
+                    // touches.)
                     wait_loads<0>();
                     __builtin_amdgcn_s_barrier();
                     asm volatile("" ::: "memory");
                 }
-                // The loads of the tile after next, two per slot from the
-                // barrier on, into the buffer every wave has finished with;
-                // then the pointers and descriptors for the tile after that
-                // (the scalar work spread over slots in the MFMAs' shadow).
-                if constexpr (!TWO && i >= BAR && i < BAR + (LPT + 1) / 2) {
-                    constexpr int j0 = 2 * (i - BAR);
+                // The loads of the tile after next, two per slot after the
+                // barrier, into the buffer of the last tile; then the
+                // pointers and descriptors of the tile after that (the
+                // scalar work spread over slots in the MFMAs' shadow).
+                if constexpr (!TWO && i > BAR && i <= BAR + NLD) {
+                    constexpr int j0 = 2 * (i - BAR - 1);
                     const int bf = cur == 0 ? NBUF - 1 : cur - 1;
                     issue_one(IC<j0>{}, bf);
                     if constexpr (j0 + 1 < LPT)
                         issue_one(IC<j0 + 1>{}, bf);
                 }
-                if constexpr (!TWO && i >= BAR + (LPT + 1) / 2 && i < BAR + (LPT + 1) / 2 + 6)
-                    setup_part(IC<i - BAR - (LPT + 1) / 2>{});
-                if constexpr (!TWO && i > BAR && i <= BAR + 4)
-                    read_rowdot(0, i - BAR - 1);   // next tile (buffer published at BAR)
+                if constexpr (!TWO && i >= SU0 && i < SU0 + 6)
+                    setup_part(IC<i - SU0>{});
+                if constexpr (!TWO && i == MOV) {
+                    // the 16-byte operand reads, row-vector and keep-word
+                    // reads of this tile are all issued
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        gq[ks] += delta;
+                    rv0 += delta;
+                    kv0 += delta;
+                }
+                if constexpr (!TWO && i > MOV && i <= MOV + 4)
+                    read_rowdot(0, i - MOV - 1);   // next tile (published at this tile's barrier)
                 if constexpr (!TWO && i == NSLOT - RA - 1) {
                     // last transposing read of this tile issued
 #pragma unroll
