@@ -160,12 +160,17 @@ __device__ inline void dq_partial(const Params &p, FusedSmem<DP> &sm, int buf, i
                     }
                     const int rank = jmax - j;
                     turn = p.turns + ((int64_t)b * p.H + h) * p.mtiles + m;
-                    // (wait while the turn is below this tile's rank: a late
+                    // Wait while the turn is below this tile's rank (a late
                     // add of a workgroup that gave up can push the counter
-                    // past a rank, which must then not wait forever)
+                    // past a rank, which must then not wait forever).  The
+                    // polls are relaxed: this workgroup reads nothing the
+                    // lower ranks wrote, it only adds into the accumulator
+                    // with atomics, which are never served from a stale
+                    // cache line, so an acquire (an invalidation of the XCD's
+                    // L2 per poll) would protect nothing.
                     if (tid == 0) {
                         int spins = 0;
-                        while (__hip_atomic_load(turn, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) <
+                        while (__hip_atomic_load(turn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
                                rank) {
                             __builtin_amdgcn_s_sleep(2);
                             if (++spins > kSpinLimit) {
@@ -200,10 +205,16 @@ __device__ inline void dq_partial(const Params &p, FusedSmem<DP> &sm, int buf, i
                     }
                 }
                 if (p.deterministic) {
-                    __threadfence();
+                    // The next rank may add once every wave's adds are done:
+                    // each wave waits for its atomics to complete, then the
+                    // turn moves on.  (No release fence: the accumulator is
+                    // written by atomics only, which are performed at the
+                    // device's coherence point, so a write-back of the XCD's
+                    // L2 would publish nothing; it cost a factor of ~4 here.)
+                    wait_loads<0>();
                     __syncthreads();
                     if (tid == 0)
-                        __hip_atomic_fetch_add(turn, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_fetch_add(turn, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
 }
 
