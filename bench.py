@@ -2,17 +2,22 @@
 """Benchmark of the MI355X attention backward (dQ, dK, dV).
 
 One step = one whole backward (dq then main; with --dq-accumulate preprocess,
-main, dq_convert) over the
-headline workload: B=2, H=32, Hk=8, Sq=Sk=4096, D=128, causal, bf16, inputs
-resident in HBM.  Prints ONE JSON line.
+main, dq_convert) over one workload, by default the headline one: B=2, H=32,
+Hk=8, Sq=Sk=4096, D=128, causal, bf16, inputs resident in HBM (--config picks
+another of workloads.py, packed variable-length batches included).  Prints ONE
+JSON line.
 
-FLOP convention: 2.5 x the forward's 4*B*H*Sq*Sk*D, halved for causal.
+FLOP convention: 2.5 x the forward's 4*B*H*Sq*Sk*D, halved for causal (packed
+batches: B*Sq*Sk replaced by the sum of the squared sequence lengths).  The
+exact count over the visible (query, key) pairs (bottom-right causal
+alignment) is reported beside it, since the convention undercounts Sq < Sk.
 The roofline object is for the main kernel (the dominant one), timed with
 HIP events recorded on the stream it is launched on.
 
 Inputs: Q, K, V, dO from the seeded generator (workloads.py); O and LSE from a
-plain fp32 torch forward on the GPU (input preparation only, not timed).
-The CPU baseline leg times the fp64 oracle on a bounded sample.
+plain fp32 torch forward on the GPU, one (sequence, head) at a time (input
+preparation only, not timed).  The CPU baseline leg times the fp64 oracle on
+a bounded sample.
 
 --forward measures the forward kernel (O and LSE) on the same workload
 instead and prints one JSON line of the same shape for it (not the headline
@@ -36,6 +41,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X published HBM3E bandwidth
 # the kernel built from exactly these files (sha256 recorded with it).
 KERNEL_SOURCES = ["attention_backward_fa2_amd/csrc/fa_main.hip",
                   "attention_backward_fa2_amd/csrc/fa_mfma.h",
+                  "attention_backward_fa2_amd/csrc/fa_philox.h",
                   "attention_backward_fa2_amd/csrc/fa_internal.h"]
 TRAFFIC_SUMMARY = "profiles/hbm_traffic_main_kernel_gqa_b2_h32_hk8_s4096_d128_causal.json"
 TRACE_SUMMARY = "profiles/kernel_trace_gqa_b2_h32_hk8_s4096_d128_causal.md"
@@ -62,6 +68,30 @@ def committed_traffic():
     if d.get("source_sha256") != kernel_source_hash():
         return None
     return d.get("traffic_bytes_per_launch")
+
+
+PEAK_CLOCK_MHZ = 2400.0       # the clock the published peak is quoted at
+CLOCK_SUMMARY = "profiles/clock_gqa_b2_h32_hk8_s4096_d128_causal.json"
+
+
+def committed_clock():
+    """Clock (MHz) the key-tile kernel ran at in the committed GRBM-counter
+    profile, or None if there is none or the kernel changed since."""
+    path = os.path.join(ROOT, CLOCK_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("source_sha256") != kernel_source_hash():
+        return None
+    k = d.get("kernels", {}).get(MAIN_KERNEL)
+    return {"mhz": k["mhz"]} if k else None
+
+
+def headline_path(args, wl):
+    """True for the kernel and workload the committed profiles cover."""
+    return (not args.dq_accumulate and wl.name == WORKLOAD_TAG and not wl.window
+            and not wl.softcap and not wl.dropout)
 
 
 def _csv_rows(path):
@@ -280,6 +310,128 @@ def summarize_profile(prof_dir, out_dir):
     print("wrote profile summaries to", out_dir)
 
 
+CLOCK_CMD = ("rocprofv3 --kernel-trace --pmc GRBM_GUI_ACTIVE GRBM_COUNT -f csv -d {prof}/clock "
+             "-o c3 -- " + PMC_RUN)
+ACC_RUN = "python bench.py --dq-accumulate --no-cpu-baseline --steps 3 --warmup 1"
+ACC_TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d {prof}/acc_trace -o c3 -- "
+                 "python bench.py --dq-accumulate --no-cpu-baseline")
+
+
+def _agent(prof_sub):
+    """The GPU agent's row of a rocprofv3 run's agent_info.csv."""
+    return next(r for r in _csv_rows(_find(prof_sub, "agent_info.csv"))
+                if r.get("Agent_Type") == "GPU")
+
+
+def summarize_clock(prof_dir, out_dir):
+    """profiles/clock_<workload>.json: the clock each kernel of the headline
+    backward ran at, from the GRBM cycle counters of a kernel-trace run
+    (PROF_DIR/clock): busy cycles per dispatch, summed by the counter over
+    the accelerator's XCDs, over the dispatch's duration."""
+    rel = os.path.relpath(prof_dir, ROOT) if os.path.isabs(prof_dir) else prof_dir.rstrip("/")
+    sub = os.path.join(prof_dir, "clock")
+    agent = _agent(sub)
+    nxcc = int(agent["Num_Xcc"])
+    durs = {}
+    for r in _csv_rows(_find(sub, "kernel_trace.csv")):
+        if "fa::" in r["Kernel_Name"]:
+            durs.setdefault(_kname(r["Kernel_Name"]), []).append(
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    res = {"workload": WORKLOAD_TAG, "source_files": KERNEL_SOURCES,
+           "source_sha256": kernel_source_hash(), "command": CLOCK_CMD.replace("{prof}", rel),
+           "num_xcc": nxcc, "max_engine_clock_mhz": float(agent["Max_Engine_Clk_Fcompute"]),
+           "note": "mhz = mean GRBM_GUI_ACTIVE per dispatch / num_xcc / mean dispatch duration "
+                   "(same run); the published dense bf16 peak is quoted at 2400 MHz",
+           "kernels": {}}
+    for (k, c), (v, n) in _pmc_means(_find(sub, "counter_collection.csv")).items():
+        if "fa::" in k and c == "GRBM_GUI_ACTIVE":
+            name = _kname(k)
+            d = sum(durs[name]) / len(durs[name])
+            res["kernels"][name] = {"grbm_gui_active": v, "dispatches": n,
+                                    "duration_us": d / 1e3, "mhz": round(v / nxcc / d * 1e3, 1)}
+    path = os.path.join(out_dir, os.path.basename(CLOCK_SUMMARY))
+    with open(path, "w") as fh:
+        json.dump(res, fh, indent=1)
+        fh.write("\n")
+    return path
+
+
+def summarize_accumulate(prof_dir, out_dir):
+    """profiles/hbm_traffic_accumulate_mode_<workload>.md: the HBM-bound
+    steps of the accumulate-mode backward (preprocess, dq_convert) and its
+    key-tile kernel: durations from a kernel trace (PROF_DIR/acc_trace), HBM
+    bytes from FETCH_SIZE / WRITE_SIZE runs (PROF_DIR/acc_FETCH_SIZE,
+    acc_WRITE_SIZE) scaled by the plain-copy runs (copy_FETCH_SIZE,
+    copy_WRITE_SIZE), and the algorithmic (compulsory) bytes."""
+    rel = os.path.relpath(prof_dir, ROOT) if os.path.isabs(prof_dir) else prof_dir.rstrip("/")
+
+    def cmd(c):
+        return c.replace("{prof}", rel)
+    bench_line = None
+    with open(os.path.join(prof_dir, "acc_trace.log")) as fh:
+        for line in fh:
+            if line.startswith("{") and '"metric"' in line:
+                bench_line = json.loads(line)
+    cfg = bench_line["config"]
+    rows, H, D = cfg["batch"] * cfg["seqlen_q"], cfg["heads"], cfg["head_dim"]
+    dpad = next(d for d in (64, 96, 128, 192, 256) if d >= D)
+    algo = {"preprocess": rows * H * (2 * D * 2 + 4 + 8) + rows * H * 4 * dpad,
+            "dq_convert": rows * H * (4 * dpad + 2 * D)}
+    trace = _csv_rows(_find(os.path.join(prof_dir, "acc_trace"), "kernel_trace.csv"))
+    durs = {}
+    for r in trace:
+        if "fa::" in r["Kernel_Name"]:
+            durs.setdefault(_kname(r["Kernel_Name"]), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    copy_bytes = float(1 << 30)
+    meas = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        cm = _pmc_means(_find(os.path.join(prof_dir, "copy_" + c), "counter_collection.csv"))
+        ckib, _ = next(v for (k, cn), v in cm.items() if "copyBuffer" in k and cn == c)
+        factor = copy_bytes / (ckib * 1024.0)
+        for (k, cn), (kib, n) in _pmc_means(
+                _find(os.path.join(prof_dir, "acc_" + c), "counter_collection.csv")).items():
+            if "fa::" in k and cn == c:
+                meas.setdefault(_kname(k), {})[c] = (kib * 1024.0 * factor, factor)
+    lines = ["# HBM traffic, accumulate mode: %s" % cfg["workload"], "",
+             "dQ by fp32 partial adds in the key-tile kernel (`--dq-accumulate`, unordered "
+             "atomics): preprocess, key-tile kernel, dq_convert.", "",
+             "Commands (repo root, MI355X):", "",
+             "    " + cmd(ACC_TRACE_CMD) + " > %s/acc_trace.log" % rel,
+             "    rocprofv3 --pmc FETCH_SIZE -f csv -d %s/acc_FETCH_SIZE -o c3 -- %s" % (rel, ACC_RUN),
+             "    rocprofv3 --pmc WRITE_SIZE -f csv -d %s/acc_WRITE_SIZE -o c3 -- %s" % (rel, ACC_RUN),
+             "    rocprofv3 --pmc FETCH_SIZE -f csv -d %s/copy_FETCH_SIZE -o copy -- "
+             "python bench.py --copy-calibration" % rel,
+             "    rocprofv3 --pmc WRITE_SIZE -f csv -d %s/copy_WRITE_SIZE -o copy -- "
+             "python bench.py --copy-calibration" % rel, "",
+             "Counter bytes are FETCH_SIZE and WRITE_SIZE per dispatch scaled by what the same "
+             "counters read for a 1 GiB device copy (factors %.3f and %.3f)." % (
+                 next(iter(meas.values()))["FETCH_SIZE"][1],
+                 next(iter(meas.values()))["WRITE_SIZE"][1]), "",
+             "| kernel | mean duration (us) | algorithmic bytes | algorithmic GB/s | "
+             "counter bytes read + written | counter GB/s |", "|---|---|---|---|---|---|"]
+    for name in sorted(meas):
+        d = sum(durs[name]) / len(durs[name])
+        step = next((s for s in ("preprocess", "convert") if s in name), None)
+        a = algo["dq_convert" if step == "convert" else "preprocess"] if step else None
+        rd, wr = meas[name]["FETCH_SIZE"][0], meas[name]["WRITE_SIZE"][0]
+        lines.append("| %s | %.1f | %s | %s | %.4g + %.4g | %.0f |" % (
+            name, d, "%.4g" % a if a else "-", "%.0f" % (a / d / 1e3) if a else "-",
+            rd, wr, (rd + wr) / d / 1e3))
+    lines += ["", "Algorithmic bytes: preprocess reads O and dO (2 x 2 x D B per row and "
+              "head), writes lse2 and rowdot (8 B) and clears the fp32 accumulator (4 x D_pad "
+              "B); dq_convert reads the accumulator (4 x D_pad B) and writes dQ (2 x D B).  "
+              "The key-tile kernel is MFMA-bound; its row shows the fp32 partial adds.", "",
+              "The same run's bench line: %.4f ms per step, %.1f TFLOP/s, per-kernel HIP-event "
+              "times (ms): `%s`, GB/s: `%s`." % (bench_line["ms_per_step"], bench_line["value"],
+                                                json.dumps(bench_line["kernel_ms"]),
+                                                json.dumps(bench_line.get("hbm_kernels_GBs")))]
+    path = os.path.join(out_dir, "hbm_traffic_accumulate_mode_%s.md" % cfg["workload"])
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return path
+
+
 def visible_pairs(Sq, Sk, causal, window=None):
     """(query, key) pairs of one (batch, head) that the products cover: the
     usual convention Sq*Sk, halved for causal, without a local window; the
@@ -299,6 +451,29 @@ def visible_pairs(Sq, Sk, causal, window=None):
 def conv_flops(B, H, Sq, Sk, D, causal, window=None):
     """Five products of 2*D FLOPs per visible (query, key) pair each."""
     return 2.5 * 4.0 * B * H * D * visible_pairs(Sq, Sk, causal, window)
+
+
+def exact_pairs(Sq, Sk, causal, window=None):
+    """The (query, key) pairs of one (sequence, head) that are visible: with
+    the bottom-right causal rule (row i sees keys <= i + Sk - Sq) and any
+    local window, counted exactly."""
+    if not causal and window is None:
+        return float(Sq * Sk)
+    return visible_pairs(Sq, Sk, causal, window if window is not None else (-1, -1))
+
+
+def workload_flops(wl, lens_q, lens_k):
+    """(conventional FLOPs, exact visible-pair FLOPs) of one backward: five
+    products of 2*D FLOPs per pair.  Packed batches sum over the sequences
+    (the convention's B*Sq*Sk becomes the sum of Lq*Lk)."""
+    H, D = wl.heads, wl.head_dim
+    if wl.varlen:
+        conv = sum(conv_flops(1, H, lq, lk, D, wl.causal, wl.window) for lq, lk in zip(lens_q, lens_k))
+    else:
+        conv = conv_flops(wl.batch, H, wl.seqlen_q, wl.seqlen_k, D, wl.causal, wl.window)
+    exact = sum(2.5 * 4.0 * H * D * exact_pairs(lq, lk, wl.causal, wl.window)
+                for lq, lk in zip(lens_q, lens_k))
+    return conv, exact
 
 
 def forward_inputs_torch(q, k, v, scale, causal, window=None, softcap=0.0):
@@ -339,14 +514,47 @@ def forward_inputs_torch(q, k, v, scale, causal, window=None, softcap=0.0):
     return out, lse
 
 
-def cpu_baseline(wl, units):
-    """fp64 oracle backward on a bounded sample: `units` (batch, KV-head
+def forward_inputs_packed(q, k, v, lens_q, lens_k, scale, causal, window=None, softcap=0.0):
+    """O and LSE of a packed batch ((total, H, D) tensors) by the same plain
+    fp32 forward, one sequence at a time; LSE is (nseq, H, max_len_q), rows
+    past a sequence's length -inf."""
+    import torch
+    nseq, H = len(lens_q), q.shape[1]
+    out = torch.zeros_like(q)
+    lse = torch.full((nseq, H, max(lens_q)), float("-inf"), dtype=torch.float32, device=q.device)
+    oq = ok = 0
+    for s_, (lq, lk) in enumerate(zip(lens_q, lens_k)):
+        if lq and lk:
+            o1, l1 = forward_inputs_torch(q[oq:oq + lq][None], k[ok:ok + lk][None],
+                                          v[ok:ok + lk][None], scale, causal, window, softcap)
+            out[oq:oq + lq] = o1[0]
+            lse[s_, :, :lq] = l1[0]
+        oq += lq
+        ok += lk
+    return out, lse
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(wl, units, inp=None):
+    """fp64 oracle backward on a bounded sample: `units` (sequence, KV-head
     group) pairs of the workload, each its own exact sub-problem."""
     import numpy as np
     import workloads as W
     from oracle import oracle as O
-    inp = W.make_inputs(wl)
+    inp = inp if inp is not None else W.make_inputs(wl)
     G = wl.heads // wl.heads_k
+    cu_q, cu_k = inp.cu_q.tolist(), inp.cu_k.tolist()
     t_total = 0.0
     flops = 0.0
     for (b, g) in units:
@@ -354,20 +562,25 @@ def cpu_baseline(wl, units):
 
         def f64(t):
             return t.float().numpy().astype(np.float64)
-        q = f64(inp.q[b][:, hs])
-        k = f64(inp.k[b][:, [g]])
-        v = f64(inp.v[b][:, [g]])
-        do = f64(inp.dout[b][:, hs])
+        rq = slice(cu_q[b], cu_q[b + 1])
+        rk = slice(cu_k[b], cu_k[b + 1])
+        lq, lk = rq.stop - rq.start, rk.stop - rk.start
+        q = f64(inp.packed(inp.q)[rq][:, hs])
+        k = f64(inp.packed(inp.k)[rk][:, [g]])
+        v = f64(inp.packed(inp.v)[rk][:, [g]])
+        do = f64(inp.packed(inp.dout)[rq][:, hs])
         t0 = time.perf_counter()
-        O.backward(q, k, v, do, [0, wl.seqlen_q], [0, wl.seqlen_k], wl.scale, wl.causal,
-                   window=wl.window_sizes, softcap=wl.softcap, dropout=wl.dropout_f32)
+        O.backward(q, k, v, do, [0, lq], [0, lk], wl.scale, wl.causal,
+                   window=wl.window_sizes, softcap=wl.softcap, dropout=wl.dropout_f32,
+                   drop_base=(b, g * G, wl.heads) if wl.dropout else None)
         t_total += time.perf_counter() - t0
-        flops += conv_flops(1, G, wl.seqlen_q, wl.seqlen_k, wl.head_dim, wl.causal, wl.window)
+        flops += conv_flops(1, G, lq, lk, wl.head_dim, wl.causal, wl.window)
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(),
-            "kind": "oracle",
-            "sample": "%d of %d (batch, KV-head group) units of the workload, fp64 "
+            "cpu_model": cpu_model(), "seconds": round(t_total, 2), "kind": "oracle",
+            "sample": "%d of %d (%s, KV-head group) units of the workload, fp64 "
                       "contracted-Jacobian backward incl. its forward recompute, %.1f s"
-                      % (len(units), wl.batch * wl.heads_k, t_total)}
+                      % (len(units), (len(cu_q) - 1) * wl.heads_k,
+                         "sequence" if wl.varlen else "batch", t_total)}
 
 
 def metric_name(base, wl):
@@ -526,6 +739,10 @@ def main():
 
     if args.summarize_profile:
         summarize_profile(args.summarize_profile, os.path.join(ROOT, "profiles"))
+        if os.path.isdir(os.path.join(args.summarize_profile, "clock")):
+            print(summarize_clock(args.summarize_profile, os.path.join(ROOT, "profiles")))
+        if os.path.isdir(os.path.join(args.summarize_profile, "acc_trace")):
+            print(summarize_accumulate(args.summarize_profile, os.path.join(ROOT, "profiles")))
         return
     if args.summarize_trace:
         print(summarize_variant_trace(args.summarize_trace[0], args.summarize_trace[1],
@@ -570,28 +787,36 @@ def main():
         import dataclasses
         wl = dataclasses.replace(wl, name="%s_dropout%g" % (wl.name, args.dropout),
                                  dropout=(float(args.dropout), 0x243F6A8885A308D3, 0))
-    if wl.varlen:
-        print("bench.py times dense workloads only", file=sys.stderr)
-        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.forward:
+        if wl.varlen:
+            print("bench.py --forward times dense workloads only", file=sys.stderr)
+            sys.exit(2)
         bench_forward(args, wl, dev)
         return
     inp = W.make_inputs(wl)
     q, k, v, do = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v, inp.dout))
+    kw = {}
+    if wl.varlen:
+        kw = dict(cu_seqlens_q=inp.cu_q.to(dev), cu_seqlens_k=inp.cu_k.to(dev),
+                  max_seqlen_q=max(inp.lens_q), max_seqlen_k=max(inp.lens_k))
     if wl.dropout:
         # the backward needs the dropout forward's O: this library's forward
         o = torch.empty_like(q)
-        lse = torch.empty(wl.batch, wl.heads, wl.seqlen_q, dtype=torch.float32, device=dev)
+        lse = torch.empty(len(inp.lens_q), wl.heads, max(inp.lens_q), dtype=torch.float32,
+                          device=dev)
         fa.fa_fwd(q, k, v, o, lse, wl.scale, wl.causal, window=wl.window, softcap=wl.softcap,
-                  dropout=wl.dropout)
+                  dropout=wl.dropout, **kw)
+    elif wl.varlen:
+        o, lse = forward_inputs_packed(q, k, v, inp.lens_q, inp.lens_k, wl.scale, wl.causal,
+                                       wl.window, wl.softcap)
     else:
         o, lse = forward_inputs_torch(q, k, v, wl.scale, wl.causal, wl.window, wl.softcap)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     a = fa.make_args(do, q, k, v, o, lse, dq, dk, dv, wl.scale, wl.causal,
                      deterministic=args.deterministic, dq_accumulate=args.dq_accumulate,
-                     window=wl.window, softcap=wl.softcap, dropout=wl.dropout)
+                     window=wl.window, softcap=wl.softcap, dropout=wl.dropout, **kw)
     # the steps of one backward, in the order fa_bwd enqueues them
     seq = ["preprocess", "main", "dq_convert"] if args.dq_accumulate else ["dq", "main"]
     ws = fa.alloc_workspace(a, dev)
@@ -621,23 +846,28 @@ def main():
     wall = time.perf_counter() - t0
     gpu_ms = evs[0][0].elapsed_time(evs[-1][-1])
     kms = {name: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / K for i, name in enumerate(seq)}
+    per_step = sorted(e[0].elapsed_time(e[-1]) for e in evs)
     main_ms = kms["main"]
     ms_per_step = gpu_ms / K
 
     B, H, Hk, Sq, Sk, D = wl.batch, wl.heads, wl.heads_k, wl.seqlen_q, wl.seqlen_k, wl.head_dim
-    flops = conv_flops(B, H, Sq, Sk, D, wl.causal, wl.window)
+    flops, exact = workload_flops(wl, inp.lens_q, inp.lens_k)
     value = flops / (ms_per_step * 1e-3) / 1e12
     # Algorithmic work per launch.  MFMA-bound kernels: the key-tile pass
     # does 4 of the 5 products (S, dP, dV, dK; + dQ in accumulate mode), the
     # separate dQ pass 3 (S, dP, dQ); FLOPs counted over the causal half like
-    # the headline convention.  HBM-bound kernels: compulsory bytes.
-    rows = B * Sq
+    # the headline convention.  HBM-bound kernels: compulsory bytes (the
+    # preprocess reads O and dO, writes lse2 / rowdot and clears the fp32
+    # accumulator; dq_convert reads the accumulator and writes dQ).
+    rows = sum(inp.lens_q)
+    dpad = next(d for d in (64, 96, 128, 192, 256) if d >= D)
     gemm = flops / 5.0                   # one of the five products
     main_flops = 5 * gemm if args.dq_accumulate else 4 * gemm
     dq_flops = 0.0 if args.dq_accumulate else 3 * gemm
-    pre_bytes = rows * H * (2 * D * 2 + 4 + 8) + rows * H * 4 * D   # accumulate mode
-    conv_bytes = rows * H * (4 * D + 2 * D)
+    pre_bytes = rows * H * (2 * D * 2 + 4 + 8) + rows * H * 4 * dpad   # accumulate mode
+    conv_bytes = rows * H * (4 * dpad + 2 * D)
     main_tflops = main_flops / (main_ms * 1e-3) / 1e12
+    clock = committed_clock()
     off_flags = fa.workspace_layout(a).off_flags
     flags = ws[off_flags:off_flags + 16].cpu().view(torch.int32)
 
@@ -663,6 +893,10 @@ def main():
                    if args.dq_accumulate else "separate"},
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "flops_per_step": flops,
+        "ms_per_step_median": round(per_step[K // 2], 4),
+        "ms_per_step_min": round(per_step[0], 4),
+        "visible_flops_per_step": exact,
+        "visible_tflops": round(exact / (ms_per_step * 1e-3) / 1e12, 2),
         "kernel_ms": {name: round(t, 4) for name, t in kms.items()},
         "kernel_tflops": {"main": round(main_tflops, 1)} if args.dq_accumulate else
         {"main": round(main_tflops, 1), "dq": round(dq_flops / (kms["dq"] * 1e-3) / 1e12, 1)},
@@ -672,18 +906,24 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(main_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None if args.dq_accumulate or wl.window or wl.softcap > 0
-                     or wl.dropout else committed_traffic(),
+                     "traffic": committed_traffic() if headline_path(args, wl) else None,
                      "kernel": main_kernel_name(args.dq_accumulate, wl),
                      "algorithmic_flops_per_launch": main_flops},
         "wall_s": round(wall, 3),
         "ordered_wait_gave_up": bool(int(flags[0]) != 0),
     }
+    if clock and headline_path(args, wl):
+        # the dense bf16 peak scaled to the clock the kernel ran at (GRBM
+        # cycle counters of the committed profile)
+        pk = PEAK_BF16_TFLOPS * clock["mhz"] / PEAK_CLOCK_MHZ
+        rec["roofline"]["clock_mhz"] = clock["mhz"]
+        rec["roofline"]["peak_at_clock"] = round(pk, 1)
+        rec["roofline"]["frac_at_clock"] = round(main_tflops / pk, 4)
     if not args.no_cpu_baseline:
-        all_units = [(b, g) for b in range(B) for g in range(Hk)]
+        all_units = [(b, g) for b in range(len(inp.lens_q)) for g in range(Hk)]
         pick = [all_units[(i * len(all_units)) // args.cpu_units]
                 for i in range(min(args.cpu_units, len(all_units)))]
-        rec["cpu_baseline"] = cpu_baseline(wl, pick)
+        rec["cpu_baseline"] = cpu_baseline(wl, pick, inp)
     print(json.dumps(rec), flush=True)
 
 
