@@ -104,7 +104,8 @@ class FaFwdArgs(ctypes.Structure):
 
 EXPORTED = ("fa_bwd", "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_dq", "fa_bwd_dq_convert",
             "fa_bwd_debug_rowsum", "fa_bwd_noalloc", "fa_bwd_validate", "fa_bwd_workspace_size",
-            "fa_bwd_workspace_layout", "fa_bwd_last_error", "fa_bwd_abi_version", "fa_fwd", "fa_fwd_validate")
+            "fa_bwd_workspace_layout", "fa_bwd_last_error", "fa_bwd_abi_version", "fa_fwd",
+            "fa_fwd_validate", "fa_probe_mfma_rate")
 
 _LIB = None
 
@@ -141,6 +142,9 @@ def load_library(path: str = LIB_PATH):
     lib.fa_fwd.restype = ctypes.c_int
     lib.fa_fwd_validate.argtypes = [PF]
     lib.fa_fwd_validate.restype = ctypes.c_int
+    lib.fa_probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_probe_mfma_rate.restype = ctypes.c_int
     _LIB = lib
     return lib
 

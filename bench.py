@@ -432,6 +432,90 @@ def summarize_accumulate(prof_dir, out_dir):
     return path
 
 
+def mfma_ceiling(fa, torch, iters=4000, reps=3):
+    """TFLOP/s of the library's MFMA probe (fa_probe_mfma_rate) in both
+    operand modes, one workgroup of four waves per CU; best of `reps`."""
+    lib = fa.load_library()
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.zeros(blocks * 256, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for mode, name in ((0, "operands_in_registers"), (1, "a_operand_from_lds")):
+        assert lib.fa_probe_mfma_rate(mode, blocks, 50, 1, out.data_ptr(), stream.cuda_stream) == 0
+        best = None
+        for r in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            assert lib.fa_probe_mfma_rate(mode, blocks, iters, 2 + r, out.data_ptr(),
+                                          stream.cuda_stream) == 0
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        flops = blocks * 4.0 * 16 * iters * 32768
+        tf = flops / (best * 1e-3) / 1e12
+        res[name] = {"tflops": round(tf, 1), "frac_of_published_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "ns_per_mfma_per_wave": round(best * 1e6 / (16 * iters), 2)}
+    return {"mfma_ceiling": res, "blocks": blocks, "waves_per_simd": 1,
+            "instruction": "v_mfma_f32_32x32x16_bf16", "operands": "random bf16 bits",
+            "published_peak_tflops": PEAK_BF16_TFLOPS}
+
+
+def summarize_ceiling(prof_dir, out_dir):
+    """profiles/mfma_ceiling_random_operands.md from
+        python bench.py --mfma-ceiling > PROF_DIR/ceiling.log
+        rocprofv3 --kernel-trace --pmc GRBM_GUI_ACTIVE GRBM_COUNT -f csv
+            -d PROF_DIR/ceiling_clock -o probe -- python bench.py --mfma-ceiling"""
+    rel = os.path.relpath(prof_dir, ROOT) if os.path.isabs(prof_dir) else prof_dir.rstrip("/")
+    line = None
+    with open(os.path.join(prof_dir, "ceiling.log")) as fh:
+        for ln in fh:
+            if ln.startswith("{") and "mfma_ceiling" in ln:
+                line = json.loads(ln)
+    sub = os.path.join(prof_dir, "ceiling_clock")
+    nxcc = int(_agent(sub)["Num_Xcc"])
+    trace = _csv_rows(_find(sub, "kernel_trace.csv"))
+    cnt = _csv_rows(_find(sub, "counter_collection.csv"))
+    durs = {}
+    for r in trace:
+        if "probe_kernel" in r["Kernel_Name"]:
+            durs.setdefault(r["Kernel_Name"], []).append(
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    gui = {}
+    for r in cnt:
+        if "probe_kernel" in r["Kernel_Name"] and r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+            gui.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    lines = ["# MFMA rate with random operands (v_mfma_f32_32x32x16_bf16, one wave per SIMD "
+             "on every CU)", "",
+             "Commands (repo root, MI355X):", "",
+             "    python bench.py --mfma-ceiling > %s/ceiling.log" % rel,
+             "    rocprofv3 --kernel-trace --pmc GRBM_GUI_ACTIVE GRBM_COUNT -f csv -d "
+             "%s/ceiling_clock -o probe -- python bench.py --mfma-ceiling" % rel, "",
+             "| operand supply | TFLOP/s | fraction of the published 2.5 PFLOP/s | ns per MFMA "
+             "per wave |", "|---|---|---|---|"]
+    for name, d in line["mfma_ceiling"].items():
+        lines.append("| %s | %.1f | %.3f | %.2f |" % (name.replace("_", " "), d["tflops"],
+                                                        d["frac_of_published_peak"],
+                                                        d["ns_per_mfma_per_wave"]))
+    lines += ["", "Clock during the probe (GRBM busy cycles / %d XCDs / dispatch duration, "
+              "the profiled run; the long dispatches of each mode):" % nxcc, ""]
+    for k in sorted(gui):
+        ds = durs.get(k, [])
+        pairs = sorted(zip(ds, gui[k]))[-3:]   # the long (timed) dispatches
+        mhz = sum(g / nxcc / d * 1e3 for d, g in pairs) / len(pairs)
+        lines.append("- `%s`: %.0f MHz over %d dispatches of %.1f ms" % (
+            _kname(k).replace("(anonymous namespace)::", ""), mhz, len(pairs),
+            sum(d for d, _ in pairs) / len(pairs) / 1e6))
+    lines += ["", "The published peak assumes 2400 MHz; a 32x32x16 product takes 32 cycles "
+              "per SIMD, so the rate at clock f is 2.5 PFLOP/s x f / 2400 MHz.  The probe's "
+              "products have no other work between them: this is the rate the tile kernels' "
+              "products can approach on data of this kind."]
+    path = os.path.join(out_dir, "mfma_ceiling_random_operands.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return path
+
+
 def visible_pairs(Sq, Sk, causal, window=None):
     """(query, key) pairs of one (batch, head) that the products cover: the
     usual convention Sq*Sk, halved for causal, without a local window; the
@@ -732,6 +816,10 @@ def main():
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_ARGS"),
                     help="write profiles/kernel_trace_<workload>.md from a rocprofv3 kernel "
                          "trace of 'python bench.py BENCH_ARGS' in TRACE_DIR (log: TRACE_DIR.log)")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only time the library's MFMA rate probe (32x32x16 bf16 products on "
+                         "random operands, one wave per SIMD on every CU): the rate the tile "
+                         "kernels' products can approach at the clock the chip then runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB (4 times), the reference "
                          "kernel for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -743,6 +831,8 @@ def main():
             print(summarize_clock(args.summarize_profile, os.path.join(ROOT, "profiles")))
         if os.path.isdir(os.path.join(args.summarize_profile, "acc_trace")):
             print(summarize_accumulate(args.summarize_profile, os.path.join(ROOT, "profiles")))
+        if os.path.isdir(os.path.join(args.summarize_profile, "ceiling_clock")):
+            print(summarize_ceiling(args.summarize_profile, os.path.join(ROOT, "profiles")))
         return
     if args.summarize_trace:
         print(summarize_variant_trace(args.summarize_trace[0], args.summarize_trace[1],
@@ -769,6 +859,9 @@ def main():
                           "dispatches": 4}), flush=True)
         return
 
+    if args.mfma_ceiling:
+        print(json.dumps(mfma_ceiling(fa, torch)), flush=True)
+        return
     fa.load_library()
     wl = W.WORKLOADS[args.config]
     if args.head_dim:
