@@ -37,7 +37,7 @@ extern "C" {
  *           batch = number of sequences and seqlen_q the maximum length.
  * Every stride but the head_dim one a multiple of 8 elements, every base
  * pointer 16-byte aligned (lse 4-byte aligned), head_dim a multiple of 8 and
- * <= 128 and the row strides of k and v below 2^24 elements (a 64-key tile
+ * <= 256 (padded tile widths 64, 96, 128, 192, 256) and the row strides of k and v below 2^24 elements (a 64-key tile
  * is addressed with 32-bit offsets) -- FA_ERR_UNSUPPORTED otherwise -- and
  * dtype bf16 or fp16 (inputs and out share it).
  *
