@@ -384,25 +384,34 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         }
         const uint8_t *lds = reinterpret_cast<const uint8_t *>(&sm.buf[0]);
 
-        // Query tile of step `it`: heads of the group in turn; within a head
-        // the last query tile first, so the workgroups of one (batch, KV
-        // head) running side by side on an XCD read the same tile at about
-        // the same time (L2 reuse).  Ordered dQ adds keep the ascending
-        // order, in which no workgroup waits on its first tile unless a
-        // right window reaches into the next key tile.
+        // Order of the query tiles.  Separate dQ: the last query tile first,
+        // and at each query tile the heads of the group in turn.  Every key
+        // tile starts at the same (last) query tile and moves down one tile
+        // per G steps, so the workgroups of one (batch, KV head) running side
+        // by side on an XCD read the same Q / dO tiles at about the same
+        // time (L2 reuse), however many tiles each sees.  (Head by head,
+        // workgroups that see fewer tiles would move on to the next head
+        // early and the group would read up to G heads at once.)  Fused dQ
+        // modes: heads in turn, within a head the last tile first; ordered
+        // adds use the ascending order, in which no workgroup waits on its
+        // first tile unless a right window reaches into the next key tile.
         const bool ascending = FUSED && p.deterministic;
         auto tile_m = [&](int it) {
             const int r = it % nm;
             return ascending ? m_begin + r : m_end - 1 - r;
         };
+        // Steps of the ring the loads walk: G heads per query tile (separate
+        // dQ) or nm query tiles per head (fused).
+        const int ring_n = FUSED ? nm : p.G;
 
         // Loads of the query tiles into LDS, strictly in the order they are
         // computed: issue(bf) loads the next tile into buffer bf.  Past the
         // last tile the loads are issued with an empty bound (no memory
         // access, zeros written) so that the tile loop has no branch.  The
-        // tile's row pointers advance incrementally (scalar registers):
-        // within a head by one tile, at the end of a head to the first tile
-        // of the next head of the group.
+        // tile's row pointers advance incrementally (scalar registers): one
+        // step along the ring (the next head at the same query tile, or the
+        // next query tile of the head), and at the end of the ring back to
+        // its first position, moved one step along the other axis.
         const int q0_first = (ascending ? m_begin : m_end - 1) * kQTile;
         const int dq0 = ascending ? kQTile : -kQTile;
         const int h0 = hk * p.G;
@@ -478,26 +487,35 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         // Move the row pointers on to the tile after (branch-free selects),
         // in three parts like the descriptors.
         int n_wrap = 0;
+        // Steps along the ring (in) and of the ring's first position (out):
+        // heads are the ring in the separate-dQ order, query tiles in the
+        // fused one.
+        const int64_t in_q = FUSED ? step_q : (int64_t)p.q_sh, out_q = FUSED ? (int64_t)p.q_sh : step_q;
+        const int64_t in_d = FUSED ? step_d : (int64_t)p.do_sh, out_d = FUSED ? (int64_t)p.do_sh : step_d;
+        const int64_t in_r = FUSED ? (int64_t)dq0 : p.rows, out_r = FUSED ? p.rows : (int64_t)dq0;
         auto advance_part = [&](auto pc) {
             constexpr int part = decltype(pc)::value;
             if constexpr (part == 0) {
                 keep_scalar_here(n_left, n_r, n_q0);
                 --n_left;
-                n_wrap = __builtin_amdgcn_readfirstlane(n_r == nm - 1 ? 1 : 0);   // scalar
+                n_wrap = __builtin_amdgcn_readfirstlane(n_r == ring_n - 1 ? 1 : 0);   // scalar
                 n_r = n_wrap ? 0 : n_r + 1;
-                n_q0 = n_wrap ? q0_first : n_q0 + dq0;
+                if constexpr (FUSED)
+                    n_q0 = n_wrap ? q0_first : n_q0 + dq0;
+                else
+                    n_q0 = n_wrap ? n_q0 + dq0 : n_q0;
                 keep_scalar_here(n_left, n_r, n_q0, n_wrap);
             } else if constexpr (part == 1) {
                 keep_scalar_here(n_wrap, nq_head, nq_ptr, nd_head, nd_ptr);
-                nq_head = n_wrap ? nq_head + p.q_sh : nq_head;
-                nd_head = n_wrap ? nd_head + p.do_sh : nd_head;
-                nq_ptr = n_wrap ? nq_head : nq_ptr + step_q;
-                nd_ptr = n_wrap ? nd_head : nd_ptr + step_d;
+                nq_head = n_wrap ? nq_head + out_q : nq_head;
+                nd_head = n_wrap ? nd_head + out_d : nd_head;
+                nq_ptr = n_wrap ? nq_head : nq_ptr + in_q;
+                nd_ptr = n_wrap ? nd_head : nd_ptr + in_d;
                 keep_scalar_here(nq_head, nq_ptr, nd_head, nd_ptr);
             } else {
                 keep_scalar_here(n_wrap, nr_head, nr_ptr);
-                nr_head = n_wrap ? nr_head + p.rows : nr_head;
-                nr_ptr = n_wrap ? nr_head : nr_ptr + dq0;
+                nr_head = n_wrap ? nr_head + out_r : nr_head;
+                nr_ptr = n_wrap ? nr_head : nr_ptr + in_r;
                 keep_scalar_here(nr_head, nr_ptr);
             }
         };
@@ -867,10 +885,10 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             // The wave's keys kw0 .. kw_last are visible to every row of the
             // query tiles mf_lo .. mf_hi (none if a key is past the end):
             // rows >= kw_last - off - win_r and rows <= kw0 - off + win_l.
-            // In the descending order of a head those come after nh masked
-            // tiles and before the masked rest.  (Three loops per head: a
-            // single masked loop spanning the heads makes the register
-            // allocator spill.)
+            // In the descending order those come after nh masked tiles and
+            // before the masked rest; each query tile is visited for the G
+            // heads in turn.  (Three loops: one masked loop entered from both
+            // edges makes the register allocator spill.)
             const int kw0 = n0 + 32 * kgrp, kw_last = kw0 + 31;
             int nh = 0, nu = 0;
             if (kw_last < Lk) {
@@ -884,18 +902,21 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     nu = mf_hi - mf_lo + 1;
                 }
             }
-            int it = 0;
-            for (int hh = 0; hh < p.G; ++hh) {
-                int m = m_end - 1;
-                const int it_h = it + nh, it_u = it_h + nu, it_e = it + nm;
-                if constexpr (LOCAL)
-                    for (; it < it_h; ++it, --m)
-                        tile(it, m, hh, IC<1>{});
-                for (; it < it_u; ++it, --m)
-                    tile(it, m, hh, IC<0>{});
-                for (; it < it_e; ++it, --m)
+            const int it_h = nh * p.G, it_u = it_h + nu * p.G;
+            int it = 0, m = m_end - 1, hh = 0;
+            auto next = [&]() {
+                ++it;
+                const int wrap = hh == p.G - 1;
+                hh = wrap ? 0 : hh + 1;
+                m -= wrap;
+            };
+            if constexpr (LOCAL)
+                for (; it < it_h; next())
                     tile(it, m, hh, IC<1>{});
-            }
+            for (; it < it_u; next())
+                tile(it, m, hh, IC<0>{});
+            for (; it < total; next())
+                tile(it, m, hh, IC<1>{});
         }
         // The last iterations issued loads past the final tile (empty bound,
         // zeros into LDS); let them land before the workgroup's LDS is
