@@ -80,6 +80,14 @@ struct __attribute__((aligned(16))) TileSmem {
     std::conditional_t<KEEP, QBufKeep<DP>, QBuf<DP>> buf[NBUF];
 };
 
+// Head dims above 128: the P and dS operands each wave hands to the other
+// wave of its pair, [wave][P, dS][k-step of the wave's query block][lane],
+// 16 bytes each.
+template <int DP, int NBUF, bool KEEP>
+struct __attribute__((aligned(16))) PairSmem : TileSmem<DP, NBUF, KEEP> {
+    uint8_t xch[kThreads / 64][2][2][64 * 16];
+};
+
 template <int DP>
 struct __attribute__((aligned(16))) FusedSmem : TileSmem<DP, 2> {
     static constexpr int RQ = DP + 16;       // pitch of k (elements)
@@ -231,9 +239,12 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
     using L = Tile64<DP>;
     // Head dims above 128: a wave's dK and dV accumulators over the whole
     // head dim and its K, V operands would need more than a SIMD's 512
-    // registers, so each pair of waves shares 32 keys and splits the head
-    // dim of dK and dV (both recompute S and dP over the whole head dim): 64
-    // keys per workgroup.  The fused dQ modes are not built for them.
+    // registers, so each pair of waves shares 32 keys (64 keys per
+    // workgroup) and splits the work: wave w & 1 of a pair computes S, dP,
+    // P and dS of query block w & 1 (rows 32 (w & 1) .. +31) of each tile
+    // over the whole head dim, the two waves trade their P and dS operands
+    // through LDS, and each accumulates dK and dV of its half of the head
+    // dim over all 64 rows.  The fused dQ modes are not built for them.
     constexpr bool BIG = DP > 128;
     static_assert(!(BIG && FUSED), "fused dQ for head dims above 128");
     constexpr int KT = BIG ? 64 : kKTile;    // keys per workgroup
@@ -248,7 +259,9 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
     // words the dQ kernel (which runs first) wrote.
     constexpr bool KEEP = DROP == 2;
     static_assert(!(KEEP && FUSED), "the fused modes draw the keep bits");
-    using Smem = std::conditional_t<FUSED, FusedSmem<DP>, TileSmem<DP, NBUF, KEEP>>;
+    using Smem = std::conditional_t<
+        FUSED, FusedSmem<DP>,
+        std::conditional_t<BIG, PairSmem<DP, NBUF, KEEP>, TileSmem<DP, NBUF, KEEP>>>;
     __shared__ Smem sm;
 
     const int tid = threadIdx.x;
@@ -382,36 +395,49 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             if constexpr (KEEP)   // keep word of row 4*g2 of the wave's rows
                 kv0 = (int)sizeof(QBuf<DP>) + w * 4 * kQTile + 16 * g2;
         }
+        // Head dims above 128: the wave's own query block mbr enters the
+        // 16-byte reads, the row vectors and keep words, and the
+        // transposing reads of its own two k-steps (tq); tqp reads the two
+        // k-steps of the other wave's block.
+        const int mbr = BIG ? (w & 1) : 0;
+        int tqp[DBL][2];
+        if constexpr (BIG) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                gq[ks] += 32 * mbr * L::PB;
+#pragma unroll
+            for (int db = 0; db < DBL; ++db)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    tqp[db][hf] = tq[db][hf] + 32 * (1 - mbr) * L::PB;
+                    tq[db][hf] += 32 * mbr * L::PB;
+                }
+            rv0 += 128 * mbr;
+            kv0 += 128 * mbr;
+        }
         const uint8_t *lds = reinterpret_cast<const uint8_t *>(&sm.buf[0]);
 
-        // Order of the query tiles.  Separate dQ: the last query tile first,
-        // and at each query tile the heads of the group in turn.  Every key
-        // tile starts at the same (last) query tile and moves down one tile
-        // per G steps, so the workgroups of one (batch, KV head) running side
-        // by side on an XCD read the same Q / dO tiles at about the same
-        // time (L2 reuse), however many tiles each sees.  (Head by head,
-        // workgroups that see fewer tiles would move on to the next head
-        // early and the group would read up to G heads at once.)  Fused dQ
-        // modes: heads in turn, within a head the last tile first; ordered
-        // adds use the ascending order, in which no workgroup waits on its
-        // first tile unless a right window reaches into the next key tile.
+        // Order of the query tiles: the last query tile first, and at each
+        // query tile the heads of the group in turn.  Every key tile starts
+        // at the same (last) query tile and moves down one tile per G steps,
+        // so the workgroups of one (batch, KV head) running side by side on
+        // an XCD read the same Q / dO tiles at about the same time (L2
+        // reuse), however many tiles each sees.  (Head by head, workgroups
+        // that see fewer tiles would move on to the next head early and the
+        // group would read up to G heads at once.)  Ordered dQ adds go up
+        // from the first query tile instead, in which order no workgroup
+        // waits on its first tile unless a right window reaches into the
+        // next key tile.  dK and dV sum in the same order in every mode
+        // except the ordered one.
         const bool ascending = FUSED && p.deterministic;
-        auto tile_m = [&](int it) {
-            const int r = it % nm;
-            return ascending ? m_begin + r : m_end - 1 - r;
-        };
-        // Steps of the ring the loads walk: G heads per query tile (separate
-        // dQ) or nm query tiles per head (fused).
-        const int ring_n = FUSED ? nm : p.G;
 
         // Loads of the query tiles into LDS, strictly in the order they are
         // computed: issue(bf) loads the next tile into buffer bf.  Past the
         // last tile the loads are issued with an empty bound (no memory
         // access, zeros written) so that the tile loop has no branch.  The
-        // tile's row pointers advance incrementally (scalar registers): one
-        // step along the ring (the next head at the same query tile, or the
-        // next query tile of the head), and at the end of the ring back to
-        // its first position, moved one step along the other axis.
+        // tile's row pointers advance incrementally (scalar registers): the
+        // next head at the same query tile, and after the last head the
+        // first head one query tile further.
         const int q0_first = (ascending ? m_begin : m_end - 1) * kQTile;
         const int dq0 = ascending ? kQTile : -kQTile;
         const int h0 = hk * p.G;
@@ -487,35 +513,28 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         // Move the row pointers on to the tile after (branch-free selects),
         // in three parts like the descriptors.
         int n_wrap = 0;
-        // Steps along the ring (in) and of the ring's first position (out):
-        // heads are the ring in the separate-dQ order, query tiles in the
-        // fused one.
-        const int64_t in_q = FUSED ? step_q : (int64_t)p.q_sh, out_q = FUSED ? (int64_t)p.q_sh : step_q;
-        const int64_t in_d = FUSED ? step_d : (int64_t)p.do_sh, out_d = FUSED ? (int64_t)p.do_sh : step_d;
-        const int64_t in_r = FUSED ? (int64_t)dq0 : p.rows, out_r = FUSED ? p.rows : (int64_t)dq0;
+        // (nq_head, nd_head, nr_head: the group's first head at the current
+        // query tile.)
         auto advance_part = [&](auto pc) {
             constexpr int part = decltype(pc)::value;
             if constexpr (part == 0) {
                 keep_scalar_here(n_left, n_r, n_q0);
                 --n_left;
-                n_wrap = __builtin_amdgcn_readfirstlane(n_r == ring_n - 1 ? 1 : 0);   // scalar
+                n_wrap = __builtin_amdgcn_readfirstlane(n_r == p.G - 1 ? 1 : 0);   // scalar
                 n_r = n_wrap ? 0 : n_r + 1;
-                if constexpr (FUSED)
-                    n_q0 = n_wrap ? q0_first : n_q0 + dq0;
-                else
-                    n_q0 = n_wrap ? n_q0 + dq0 : n_q0;
+                n_q0 = n_wrap ? n_q0 + dq0 : n_q0;
                 keep_scalar_here(n_left, n_r, n_q0, n_wrap);
             } else if constexpr (part == 1) {
                 keep_scalar_here(n_wrap, nq_head, nq_ptr, nd_head, nd_ptr);
-                nq_head = n_wrap ? nq_head + out_q : nq_head;
-                nd_head = n_wrap ? nd_head + out_d : nd_head;
-                nq_ptr = n_wrap ? nq_head : nq_ptr + in_q;
-                nd_ptr = n_wrap ? nd_head : nd_ptr + in_d;
+                nq_head = n_wrap ? nq_head + step_q : nq_head;
+                nd_head = n_wrap ? nd_head + step_d : nd_head;
+                nq_ptr = n_wrap ? nq_head : nq_ptr + p.q_sh;
+                nd_ptr = n_wrap ? nd_head : nd_ptr + p.do_sh;
                 keep_scalar_here(nq_head, nq_ptr, nd_head, nd_ptr);
             } else {
                 keep_scalar_here(n_wrap, nr_head, nr_ptr);
-                nr_head = n_wrap ? nr_head + out_r : nr_head;
-                nr_ptr = n_wrap ? nr_head : nr_ptr + in_r;
+                nr_head = n_wrap ? nr_head + dq0 : nr_head;
+                nr_ptr = n_wrap ? nr_head : nr_ptr + p.rows;
                 keep_scalar_here(nr_head, nr_ptr);
             }
         };
@@ -588,6 +607,31 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                                lds + base + tq[db][1] + 16 * kk * L::PB);
             }
         };
+        // Head dims above 128, slots of a tile: S of the wave's query block
+        // (KS k-steps), dP (KS), then dV and dK over the block's two k-steps
+        // (2 DBL each), then dV and dK over the other block's two k-steps.
+        constexpr int VO = 2 * KS, KO = VO + 2 * DBL, VP = KO + 2 * DBL, KP = VP + 2 * DBL;
+        constexpr int NSB = KP + 2 * DBL;
+        auto op_read_big = [&](auto ic) -> e16x8 {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (i < KS) {
+                return lds16b(lds + gq[i]);
+            } else if constexpr (i < VO) {
+                return lds16b(lds + gq[i - KS] + L::BYTES);
+            } else {
+                constexpr int u = i - VO, grp = u / (2 * DBL), kl = (u % (2 * DBL)) / DBL, db = u % DBL;
+                constexpr int base = (grp & 1) ? 0 : L::BYTES;   // dV: dO^T, dK: Q^T
+                const int(&t)[DBL][2] = grp < 2 ? tq : tqp;
+                return tr_pair(lds + base + t[db][0] + 16 * kl * L::PB,
+                               lds + base + t[db][1] + 16 * kl * L::PB);
+            }
+        };
+        auto op_first = [&](auto ic) -> e16x8 {
+            if constexpr (BIG)
+                return op_read_big(ic);
+            else
+                return op_read(ic);
+        };
         // dK / dV stay in accumulation registers for the whole loop
         // (without these pins the allocator parks some of them in ordinary
         // registers during the S / dP products and copies them back every
@@ -602,7 +646,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         };
 
         e16x8 ring[RA];
-        static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
+        static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_first(ic); });
         // rowdot of the rows of query block mb (accumulator layout: element
         // 4*r4 + t is row 32*mb + 8*r4 + 4*g2 + t): the initial value of the
         // dP accumulator.  Block 0 of the next tile is read once its buffer
@@ -701,7 +745,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             auto drop_call = [&](auto cc) {
                 constexpr int c = decltype(cc)::value, mb = c >> 2, r4 = c & 3;
                 const int a = l32 & 3;
-                const uint32_t row = (uint32_t)(q0 + 32 * mb + 8 * r4 + 4 * g2 + a);
+                const uint32_t row = (uint32_t)(q0 + 32 * (mb + mbr) + 8 * r4 + 4 * g2 + a);
                 const uint32_t c2 = (uint32_t)(b * p.H + hk * p.G + hh);
                 const int nib = (int)keep_nibble((uint32_t)key >> 2, row, c2, p);
                 // quad broadcasts of lanes 0..3 (quad_perm [t, t, t, t])
@@ -715,6 +759,161 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             };
 
             pin_acc();
+            if constexpr (BIG) {
+                // Rows of the wave's block: 32 mbr + 8 r4 + 4 g2 + t.
+                const int limv_b =
+                    key >= Lk ? INT_MAX
+                              : (p.win_r >= 0 ? key - q0 - off - p.win_r - 4 * g2 - 32 * mbr : INT_MIN);
+                const int limu_b = LOCAL ? key - q0 - off + p.win_l - 4 * g2 - 32 * mbr : INT_MAX;
+                constexpr int KDB = KS / 4 > 2 ? 2 : 1;
+                e16x8 pbo[2], dso[2], pbx[2], dsx[2];
+                float cgv[SOFTCAP ? 16 : 1];
+                uint8_t *xw = &sm.xch[w][0][0][16 * lane];
+                const uint8_t *xr = &sm.xch[w ^ 1][0][0][16 * lane];
+                // P of element e (kept in s for dS), packed by k-step.
+                auto pw_p = [&](auto ec) {
+                    constexpr int e = decltype(ec)::value, r4 = e >> 2, t = e & 3, qc = 8 * r4;
+                    float x;
+                    if constexpr (SOFTCAP) {
+                        const float th = cap_tanh(s[0][e], p.cap_in);
+                        x = __builtin_amdgcn_exp2f(fmaf(th, p.cap_out, -l2v[r4][t]));
+                        cgv[SOFTCAP ? e : 0] = fmaf(-th, th, 1.f);
+                    } else {
+                        x = __builtin_amdgcn_exp2f(s[0][e] * p.scale_log2 - l2v[r4][t]);
+                    }
+                    if constexpr (decltype(maskc)::value)
+                        x = qc + t >= limv_b && (!LOCAL || qc + t <= limu_b) ? x : 0.f;
+                    float pm = x;
+                    if constexpr (DROP)
+                        pm = x * keep_mult(kw, 4 * t + r4, p.drop_inv);
+                    keep_here(pm);
+                    s[0][e] = x;
+                    pv[t] = pm;
+                    if constexpr (t == 3) {
+                        ph[r4] = to_elem<F16>(pv);
+                        if constexpr ((r4 & 1) != 0)
+                            pbo[r4 >> 1] = concat(ph[r4 - 1], ph[r4]);
+                    }
+                };
+                // dS of element e (dp holds rowdot - dP).
+                auto pw_ds = [&](auto ec) {
+                    constexpr int e = decltype(ec)::value, r4 = e >> 2, t = e & 3;
+                    const float x = s[0][e];
+                    const float cg = SOFTCAP ? cgv[SOFTCAP ? e : 0] : 1.f;
+                    float d;
+                    if constexpr (DROP) {
+                        const float zi = keep_mult(kw, 4 * t + r4, p.drop_inv);
+                        const float rd_ = rdc[0][e];
+                        d = x * cg * fmaf(zi, rd_ - dp[0][e], -rd_);
+                    } else {
+                        d = SOFTCAP ? x * cg * -dp[0][e] : x * -dp[0][e];
+                    }
+                    keep_here(d);
+                    dv[t] = d;
+                    if constexpr (t == 3) {
+                        dh[r4] = to_elem<F16>(dv);
+                        if constexpr ((r4 & 1) != 0)
+                            dso[r4 >> 1] = concat(dh[r4 - 1], dh[r4]);
+                    }
+                };
+                static_for<NSB>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    const e16x8 a = ring[i % RA];
+                    if constexpr (i + RA < NSB)
+                        ring[i % RA] = op_read_big(IC<i + RA>{});
+                    // keep bits of the block's rows (words or Philox) over
+                    // the S slots; the row vectors before the first P
+                    if constexpr (KEEP && i < KS)
+                        static_for<4>([&](auto rc) {
+                            constexpr int r4 = decltype(rc)::value;
+                            if constexpr (i == r4 * KS / 4)
+                                kq[r4] = *reinterpret_cast<const u32x4 *>(lds + kv0 + 32 * r4);
+                            if constexpr (i == r4 * KS / 4 + KDB)
+                                static_for<4>([&](auto tc) {
+                                    constexpr int t = decltype(tc)::value;
+                                    kw |= __builtin_amdgcn_ubfe(kq[r4][t], (uint32_t)l32, 1u) << (4 * t + r4);
+                                });
+                        });
+                    if constexpr (DROP && !KEEP && i < KS)
+                        static_for<4>([&](auto rc) {
+                            constexpr int r4 = decltype(rc)::value;
+                            if constexpr (i == r4 * KS / 4)
+                                drop_call(IC<r4>{});
+                        });
+                    if constexpr (i >= 4 && i < 8)
+                        l2v[i - 4] = *reinterpret_cast<const f32x4 *>(l2s + 8 * (i - 4));
+                    if constexpr (i < KS) {
+                        if constexpr (i == 0)
+                            mfma32_vz<F16>(s[0], a, kf[0]);
+                        else
+                            mfma32_vacc<F16>(s[0], a, kf[i]);
+                    } else if constexpr (i < VO) {
+                        constexpr int ks = i - KS;
+                        if constexpr (ks == 0) {
+                            dp[0] = rdc[0];   // a vector copy: FRESH waits for it
+                            mfma32_vacc<F16, true>(dp[0], a, vf[0]);
+                        } else {
+                            mfma32_vacc<F16>(dp[0], a, vf[ks]);
+                        }
+                    } else {
+                        constexpr int u = i - VO, grp = u / (2 * DBL), kl = (u % (2 * DBL)) / DBL, db = u % DBL;
+                        if constexpr (grp == 0) {
+                            dv_acc[db] = mfma32<F16>(a, pbo[kl], dv_acc[db]);
+                            keep_here_acc(dv_acc[db]);
+                        } else if constexpr (grp == 1) {
+                            dk_acc[db] = mfma32<F16>(a, dso[kl], dk_acc[db]);
+                            keep_here_acc(dk_acc[db]);
+                        } else if constexpr (grp == 2) {
+                            dv_acc[db] = mfma32<F16>(a, pbx[kl], dv_acc[db]);
+                            keep_here_acc(dv_acc[db]);
+                        } else {
+                            dk_acc[db] = mfma32<F16>(a, dsx[kl], dk_acc[db]);
+                            keep_here_acc(dk_acc[db]);
+                        }
+                    }
+                    // P over the dP slots, dS over the own dV slots
+                    if constexpr (i >= KS && i < VO) {
+                        constexpr int u = i - KS;
+                        if constexpr (u == 0)
+                            mfma_settle(s[0]);
+                        static_for<16 * (u + 1) / KS - 16 * u / KS>(
+                            [&](auto ec) { pw_p(IC<16 * u / KS + decltype(ec)::value>{}); });
+                    }
+                    if constexpr (i >= VO && i < KO) {
+                        constexpr int u = i - VO;
+                        if constexpr (u == 0) {
+                            mfma_settle(dp[0]);
+                            *reinterpret_cast<e16x8 *>(xw) = pbo[0];
+                            *reinterpret_cast<e16x8 *>(xw + 1024) = pbo[1];
+                        }
+                        static_for<16 * (u + 1) / (2 * DBL) - 16 * u / (2 * DBL)>(
+                            [&](auto ec) { pw_ds(IC<16 * u / (2 * DBL) + decltype(ec)::value>{}); });
+                    }
+                    if constexpr (i == KO) {
+                        *reinterpret_cast<e16x8 *>(xw + 2048) = dso[0];
+                        *reinterpret_cast<e16x8 *>(xw + 3072) = dso[1];
+                    }
+                    if constexpr (i == KO + 1) {
+                        // Trade with the other wave of the pair once both
+                        // have written (only LDS operations are waited for:
+                        // the next tile's loads stay in flight).  Its
+                        // operands are read for its k-steps' products,
+                        // which come 2 DBL - 1 slots later; the area is
+                        // written again only after the tile's closing
+                        // barrier.
+                        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                        __builtin_amdgcn_s_barrier();
+                        asm volatile("" ::: "memory");
+                        pbx[0] = *reinterpret_cast<const e16x8 *>(xr);
+                        pbx[1] = *reinterpret_cast<const e16x8 *>(xr + 1024);
+                        dsx[0] = *reinterpret_cast<const e16x8 *>(xr + 2048);
+                        dsx[1] = *reinterpret_cast<const e16x8 *>(xr + 3072);
+                    }
+                    if constexpr (i == KS || i == VO)
+                        pin_acc();
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            } else
             static_for<NSLOT>([&](auto ic) {
                 constexpr int i = decltype(ic)::value;
                 const e16x8 a = ring[i % RA];
@@ -860,6 +1059,10 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 for (int db = 0; db < DBL; ++db) {
                     tq[db][0] += delta;
                     tq[db][1] += delta;
+                    if constexpr (BIG) {
+                        tqp[db][0] += delta;
+                        tqp[db][1] += delta;
+                    }
                 }
                 rv0 += delta;
                 kv0 += delta;
@@ -871,7 +1074,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     dq_partial<DP, F16>(p, sm, cur, w, lane, l32, g2, tid, b, h, m, j, q0,
                                         rows_valid, Lq, off, nt_b, si.ws_row);
                 }
-                static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
+                static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_first(ic); });
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4)
                     read_rowdot(0, r4);
@@ -879,8 +1082,14 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             cur = cur == NBUF - 1 ? 0 : cur + 1;
         };
         if constexpr (FUSED) {
-            for (int it = 0; it < total; ++it)
-                tile(it, tile_m(it), it / nm, IC<1>{});
+            const int dm = ascending ? 1 : -1;
+            int m = ascending ? m_begin : m_end - 1, hh = 0;
+            for (int it = 0; it < total; ++it) {
+                tile(it, m, hh, IC<1>{});
+                const int wrap = hh == p.G - 1;
+                hh = wrap ? 0 : hh + 1;
+                m += wrap ? dm : 0;
+            }
         } else {
             // The wave's keys kw0 .. kw_last are visible to every row of the
             // query tiles mf_lo .. mf_hi (none if a key is past the end):
