@@ -57,6 +57,8 @@ class FaBwdArgs(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("dropout_keep_max_bytes", ctypes.c_size_t),
+        ("dropout_keep", ctypes.c_void_p),
+        ("dropout_keep_bytes", ctypes.c_size_t),
     ]
 
 
@@ -99,13 +101,15 @@ class FaFwdArgs(ctypes.Structure):
         ("dropout_p", ctypes.c_float),
         ("philox_seed", ctypes.c_uint64),
         ("philox_offset", ctypes.c_uint64),
+        ("dropout_keep_out", ctypes.c_void_p),
+        ("dropout_keep_out_bytes", ctypes.c_size_t),
     ]
 
 
 EXPORTED = ("fa_bwd", "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_dq", "fa_bwd_dq_convert",
             "fa_bwd_debug_rowsum", "fa_bwd_noalloc", "fa_bwd_validate", "fa_bwd_workspace_size",
             "fa_bwd_workspace_layout", "fa_bwd_last_error", "fa_bwd_abi_version", "fa_fwd",
-            "fa_fwd_validate", "fa_probe_mfma_rate")
+            "fa_fwd_validate", "fa_fwd_keep_bytes", "fa_probe_mfma_rate")
 
 _LIB = None
 
@@ -142,6 +146,8 @@ def load_library(path: str = LIB_PATH):
     lib.fa_fwd.restype = ctypes.c_int
     lib.fa_fwd_validate.argtypes = [PF]
     lib.fa_fwd_validate.restype = ctypes.c_int
+    lib.fa_fwd_keep_bytes.argtypes = [PF]
+    lib.fa_fwd_keep_bytes.restype = ctypes.c_size_t
     lib.fa_probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
                                        ctypes.c_void_p, ctypes.c_void_p]
     lib.fa_probe_mfma_rate.restype = ctypes.c_int
@@ -203,14 +209,16 @@ def make_args(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
               cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
               max_seqlen_k=None, deterministic=False, workspace=None,
               dq_accumulate=False, window=None, softcap=0.0, dropout=None,
-              dropout_keep_max_bytes=0) -> FaBwdArgs:
+              dropout_keep_max_bytes=0, dropout_keep=None) -> FaBwdArgs:
     """Fill fa_bwd_args from tensors.  Dense tensors are (B, S, H, D); packed
     ones (total, H, D) with int32 device cu_seqlens and host max lengths.
     dq_accumulate=False: dQ by the separate query-tile pass (default);
     True: dQ partials accumulated in fp32 by the key-tile pass (atomic, or
     ordered when deterministic) and converted afterwards.
     dropout_keep_max_bytes: bound on the dropout keep-bit region of the
-    workspace (0: the library's default)."""
+    workspace (0: the library's default).
+    dropout_keep: the keep words a forward call wrote (a device tensor, see
+    make_fwd_args), read instead of drawing the bits."""
     varlen = cu_seqlens_q is not None or cu_seqlens_k is not None
     a = FaBwdArgs()
     a.dtype = _DTYPES.get(q.dtype, 99)
@@ -245,6 +253,9 @@ def make_args(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
     a.deterministic = int(bool(deterministic))
     a.dq_accumulate = int(bool(dq_accumulate))
     a.dropout_keep_max_bytes = int(dropout_keep_max_bytes)
+    if dropout_keep is not None:
+        a.dropout_keep = dropout_keep.data_ptr()
+        a.dropout_keep_bytes = dropout_keep.numel() * dropout_keep.element_size()
     if workspace is not None:
         a.workspace = workspace.data_ptr()
         a.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -321,7 +332,7 @@ def ordered_wait_gave_up(args: FaBwdArgs, workspace: torch.Tensor) -> bool:
 def fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
            cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
            deterministic=False, workspace=None, stream=None, dq_accumulate=False,
-           window=None, softcap=0.0, dropout=None):
+           window=None, softcap=0.0, dropout=None, dropout_keep=None):
     """dQ, dK, dV of attention, written into dq, dk, dv (same layouts as q, k, v).
 
     lse is the forward's natural-log log-sum-exp, (B, H, Sq) fp32 (packed:
@@ -329,10 +340,12 @@ def fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
     holds the fp32 dQ accumulator and the row sums afterwards).
     With dq_accumulate and deterministic both set, the call waits for the
     device and raises if an ordered wait gave up (dq would then not be
-    bit-reproducible)."""
+    bit-reproducible).  dropout_keep: the forward's keep words (fa_fwd with
+    keep=True), read instead of drawing the bits."""
     args = make_args(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
                      cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                     deterministic, workspace, dq_accumulate, window, softcap, dropout)
+                     deterministic, workspace, dq_accumulate, window, softcap, dropout,
+                     dropout_keep=dropout_keep)
     if workspace is None:
         workspace = alloc_workspace(args, q.device)
     run(args, "all", stream)
@@ -343,8 +356,10 @@ def fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, softmax_scale, causal,
 
 def make_fwd_args(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q=None,
                   cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
-                  window=None, softcap=0.0, dropout=None) -> FaFwdArgs:
-    """Fill fa_fwd_args from tensors (layouts as in make_args)."""
+                  window=None, softcap=0.0, dropout=None, keep_out=None) -> FaFwdArgs:
+    """Fill fa_fwd_args from tensors (layouts as in make_args).  keep_out: a
+    device tensor of at least keep_bytes() bytes that receives the dropout
+    keep words for the backward's dropout_keep."""
     varlen = cu_seqlens_q is not None or cu_seqlens_k is not None
     a = FaFwdArgs()
     a.dtype = _DTYPES.get(q.dtype, 99)
@@ -373,7 +388,15 @@ def make_fwd_args(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q=None,
     _set_window(a, window)
     a.softcap = float(softcap)
     _set_dropout(a, dropout)
+    if keep_out is not None:
+        a.dropout_keep_out = keep_out.data_ptr()
+        a.dropout_keep_out_bytes = keep_out.numel() * keep_out.element_size()
     return a
+
+
+def keep_bytes(args: FaFwdArgs) -> int:
+    """Bytes of the dropout keep words of a forward call (0 without dropout)."""
+    return int(load_library().fa_fwd_keep_bytes(ctypes.byref(args)))
 
 
 def validate_fwd(args: FaFwdArgs) -> int:
@@ -387,9 +410,20 @@ def run_fwd(args: FaFwdArgs, stream=None):
 
 def fa_fwd(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q=None, cu_seqlens_k=None,
            max_seqlen_q=None, max_seqlen_k=None, stream=None, window=None, softcap=0.0,
-           dropout=None):
+           dropout=None, keep=False):
     """O and the natural-log LSE of attention, written into out (layout of q)
-    and lse ((B, H, Sq) fp32; packed: (num_seqs, H, max_seqlen_q))."""
+    and lse ((B, H, Sq) fp32; packed: (num_seqs, H, max_seqlen_q)).  With
+    dropout and keep=True, also the keep words for the backward's
+    dropout_keep: returns them (a uint32 device tensor), else None."""
     args = make_fwd_args(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q, cu_seqlens_k,
                          max_seqlen_q, max_seqlen_k, window, softcap, dropout)
+    words = None
+    if keep and dropout is not None and float(dropout[0]) > 0.0:
+        n = keep_bytes(args)
+        if n == 0:
+            _check(validate_fwd(args) or FA_ERR_INVALID_ARG)
+        words = torch.empty((n + 3) // 4, dtype=torch.int32, device=q.device)
+        args.dropout_keep_out = words.data_ptr()
+        args.dropout_keep_out_bytes = words.numel() * 4
     run_fwd(args, stream)
+    return words

@@ -105,6 +105,30 @@ fa_status check_strides(const char *name, const int64_t s[3], bool varlen)
     return FA_OK;
 }
 
+// Keep words of a dropout call: 2 * ceil(seqlen_k / 64) per row of every head.
+size_t keep_words_bytes(int32_t seqlen_k, int32_t heads, int64_t rows)
+{
+    if (seqlen_k <= 0 || heads <= 0 || rows <= 0)
+        return 0;
+    return 2 * (size_t)((seqlen_k + 63) / 64) * (size_t)heads * (size_t)rows * sizeof(uint32_t);
+}
+
+// The caller's keep words (forward output / backward input): 4-byte aligned,
+// large enough, and one word's rows of all heads addressable with 31-bit
+// byte offsets (the kernels' per-lane load and store offsets).
+fa_status check_keep_words(const char *name, const void *ptr, size_t bytes, int32_t seqlen_k,
+                           int32_t heads, int64_t rows)
+{
+    if (!aligned(ptr, 4))
+        return fail(FA_ERR_INVALID_ARG, "%s is not 4-byte aligned", name);
+    const size_t need = keep_words_bytes(seqlen_k, heads, rows);
+    if (bytes < need)
+        return fail(FA_ERR_INVALID_ARG, "%s has %zu bytes, needs %zu", name, bytes, need);
+    if ((uint64_t)heads * (uint64_t)rows * 4u + 1024u >= (uint64_t(1) << 31))
+        return fail(FA_ERR_UNSUPPORTED, "%s: num_heads * rows >= 2^29 is not supported", name);
+    return FA_OK;
+}
+
 // Validates everything that can be checked on the host and fills the plan.
 // need_ws: also require a large-enough workspace.
 fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
@@ -188,6 +212,11 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
     if (a->local_window && a->causal && a->window_size_right > 0)
         return fail(FA_ERR_INVALID_ARG, "causal = 1 with window_size_right = %d > 0",
                     a->window_size_right);
+    const int64_t nq_rows = varlen ? a->total_q : (int64_t)a->batch * a->seqlen_q;
+    const bool keep_given = a->dropout_keep && a->dropout_p > 0.f && !a->dq_accumulate;
+    if (keep_given && (st = check_keep_words("dropout_keep", a->dropout_keep, a->dropout_keep_bytes,
+                                             a->seqlen_k, a->num_heads, nq_rows)))
+        return st;
 
     fa::Params &p = pl->p;
     std::memset(&p, 0, sizeof p);
@@ -264,7 +293,7 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
     // One bit per (row, key) pair: bounded (default 4 GiB), else the
     // key-tile kernel draws the bits itself.
     ws.off_keep = off;
-    if (p.drop_p > 0.f && !p.fused_dq) {
+    if (p.drop_p > 0.f && !p.fused_dq && !keep_given) {
         const size_t kw = 2 * (size_t)((p.Sk + 63) / 64);
         const size_t bytes = kw * hr * sizeof(uint32_t);
         const size_t cap = a->dropout_keep_max_bytes ? a->dropout_keep_max_bytes : (size_t)4 << 30;
@@ -291,6 +320,10 @@ fa_status make_plan(const fa_bwd_args *a, Plan *pl, bool need_ws)
         p.turns = p.fused_dq ? (int *)(base + ws.off_turns) : nullptr;
         p.flags = (int *)(base + ws.off_flags);
         p.keep = ws.keep_words ? (uint32_t *)(base + ws.off_keep) : nullptr;
+    }
+    if (keep_given) {
+        p.keep = const_cast<uint32_t *>(a->dropout_keep);   // read only (keep_given)
+        p.keep_given = 1;
     }
     g_last_error.clear();
     return FA_OK;
@@ -402,6 +435,10 @@ fa_status make_fwd_plan(const fa_fwd_args *a, fa::Params *pp, int *dpad_out)
     if (a->local_window && a->causal && a->window_size_right > 0)
         return fail(FA_ERR_INVALID_ARG, "causal = 1 with window_size_right = %d > 0",
                     a->window_size_right);
+    const bool keep_out = a->dropout_keep_out && a->dropout_p > 0.f;
+    if (keep_out && (st = check_keep_words("dropout_keep_out", a->dropout_keep_out,
+                                           a->dropout_keep_out_bytes, a->seqlen_k, a->num_heads, nq)))
+        return st;
 
     fa::Params &p = *pp;
     std::memset(&p, 0, sizeof p);
@@ -437,6 +474,7 @@ fa_status make_fwd_plan(const fa_fwd_args *a, fa::Params *pp, int *dpad_out)
     set_window(p, a->causal, a->local_window ? a->window_size_left : -1,
                a->local_window ? a->window_size_right : -1);
     p.f16 = a->dtype == FA_DTYPE_F16;
+    p.keep = keep_out ? a->dropout_keep_out : nullptr;
     *dpad_out = dpad;
     g_last_error.clear();
     return FA_OK;
@@ -456,6 +494,19 @@ int report_error(int status, const char *msg)
 }  // namespace fa
 
 extern "C" {
+
+size_t fa_fwd_keep_bytes(const fa_fwd_args *a)
+{
+    if (!a || !(a->dropout_p > 0.f))
+        return 0;
+    fa_fwd_args b = *a;
+    b.dropout_keep_out = nullptr;   // validate the rest
+    fa::Params p;
+    int dpad;
+    if (make_fwd_plan(&b, &p, &dpad))
+        return 0;
+    return keep_words_bytes(a->seqlen_k, a->num_heads, p.rows);
+}
 
 fa_status fa_fwd_validate(const fa_fwd_args *a)
 {

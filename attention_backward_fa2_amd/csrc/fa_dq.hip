@@ -36,6 +36,8 @@
 // in the tile, where the S^T / dP^T products leave the issue slots idle.
 //
 // LDS (D_pad = 128): 3 x (K, V) x 16 KB = 96 KB.
+#include <type_traits>
+
 #include "fa_mfma.h"
 #include "fa_philox.h"
 
@@ -66,18 +68,29 @@ struct __attribute__((aligned(16))) KVBuf {
     uint8_t v[Tile64<DP>::BYTES];
 };
 
+// Dropout from the caller's keep words: a tile also carries each wave's two
+// words of the tile's keys for its 32 rows (lane l of the wave's load: word
+// l / 32 of row l % 32).
 template <int DP>
+struct __attribute__((aligned(16))) KVBufKeep : KVBuf<DP> {
+    uint32_t keep[DqShape<DP>::WAVES][64];
+};
+
+template <int DP, bool KW = false>
 struct __attribute__((aligned(16))) DqSmem {
-    KVBuf<DP> buf[DqShape<DP>::NBUF];
+    std::conditional_t<KW, KVBufKeep<DP>, KVBuf<DP>> buf[DqShape<DP>::NBUF];
 };
 
 // LOCAL: a left window bounds the visible keys from below (win_l >= 0);
 // otherwise win_l < 0 and only the upper bound (causal / right window / key
 // end) is masked.  SOFTCAP: scores soft-capped (softcap > 0).  DROP:
-// dropout replayed from the forward's rng state (drop_p > 0).
-template <int DP, bool F16, bool LOCAL, bool SOFTCAP, bool DROP>
+// dropout (drop_p > 0) replayed from the forward's rng state (1: the keep
+// bits drawn here, and written for the key-tile kernel when p.keep is set)
+// or read from the words the forward wrote (2, p.keep).
+template <int DP, bool F16, bool LOCAL, bool SOFTCAP, int DROP>
 __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Params p)
 {
+    constexpr bool DRAW = DROP == 1, READW = DROP == 2;
     constexpr int KS = DP / 16;                  // k-steps over the head dim
     constexpr int DB = DP / 32;                  // 32-wide head-dim blocks
     constexpr int NBUF = DqShape<DP>::NBUF;
@@ -87,7 +100,8 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
     using L = Tile64<DP>;
     constexpr int PERW = L::NLOAD / WAVES;       // 1 KB wave loads per tensor per wave
     static_assert(PERW >= 1 && L::NLOAD % WAVES == 0, "tile load split");
-    __shared__ DqSmem<DP> sm;
+    __shared__ DqSmem<DP, READW> sm;
+    using Buf = std::remove_reference_t<decltype(sm.buf[0])>;
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -157,6 +171,13 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
     const int64_t kstep = (int64_t)kDqKeys * p.k_ss, vstep = (int64_t)kDqKeys * p.v_ss;
     k_next += t_lo * kstep;
     v_next += t_lo * vstep;
+    // Caller's keep words (READW): words 2t, 2t + 1 of the wave's first row,
+    // H * rows words apart; two words further per tile.
+    const uint32_t *w_next = nullptr;
+    const uint32_t hr4 = READW ? (uint32_t)(p.H * p.rows * 4) : 0u;
+    const int64_t wstep = 2 * (int64_t)p.H * p.rows;
+    if constexpr (READW)
+        w_next = p.keep + ((int64_t)(2 * t_lo) * p.H + h) * p.rows + si.ws_row + q0 + 32 * w;
     auto issue = [&](int bf) {
         if constexpr (!DqShape<DP>::BIG)   // (at 256 the pins leave no legal register class)
             keep_scalar_here(n_next, n_left, k_next, v_next);
@@ -165,13 +186,26 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
         const uint32_t nv = kv ? (uint32_t)((kv - 1) * (int)p.v_ss * 2 + p.D * 2) : 0u;
         const auto rk = make_rsrc(k_next, nk);
         const auto rv = make_rsrc(v_next, nv);
+        u32x4_rsrc rw;
+        if constexpr (READW) {
+            rw = make_rsrc(w_next, kv ? hr4 + 128u : 0u);
+            w_next += wstep;
+        }
         n_next += kDqKeys;
         --n_left;
         k_next += kstep;
         v_next += vstep;
         if constexpr (!DqShape<DP>::BIG)   // (at 256 the pins leave no legal register class)
             keep_scalar_here(n_next, n_left, k_next, v_next);
-        KVBuf<DP> &kb = sm.buf[bf];
+        Buf &kb = sm.buf[bf];
+        if constexpr (READW) {
+            // lane l: word l / 32 of row l % 32 (rows past the end: zeros)
+            const int ln = lane_here();
+            const uint32_t vw = q0 + 32 * w + (ln & 31) < Lq
+                                    ? (uint32_t)(ln >> 5) * hr4 + (uint32_t)(ln & 31) * 4u
+                                    : kOutOfRange;
+            load4_to_lds(rw, kb.keep[w], vw);
+        }
 #pragma unroll
         for (int i = 0; i < PERW; ++i) {
             const int ld = (w * PERW + i) * 1024;
@@ -297,7 +331,7 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
         //             rows per key block);
         //  tq[db][h]: transposing read of K rows 4*g2 + rr + 8*h (+ 16 rows per
         //             k-step), tile chunk 4*db + 2*h16 + b1, 8-byte half c16 & 1.
-        constexpr int BUFB = (int)sizeof(KVBuf<DP>);
+        constexpr int BUFB = (int)sizeof(Buf);
         int gq[KS], tq[DB][2];
         {
             const int sw = swz<L::PCH>(l32);
@@ -327,12 +361,20 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
         constexpr int NSLOT = 2 * NB + 2 * NQ;
         constexpr int RA = 4;                        // read-ahead (divides NSLOT)
         // the barrier and the loads of the tile after next early in the
-        // tile, where the S^T / dP^T products leave the issue slots idle; the
-        // 16-byte read offsets move at MOV, after the tile's last such read
-        constexpr int BAR = 2;
+        // tile, where the S^T / dP^T products leave the issue slots idle
+        // (when the keep bits are drawn, the Philox calls fill that phase
+        // and the load set-up there makes the allocator spill: then in the
+        // dQ phase, with the keep words stored right after the barrier's
+        // wait); the 16-byte read offsets move at MOV, after the tile's last
+        // such read
+        constexpr int BAR =
+            !DRAW ? 2 : (2 * NB + NQ / 2 < NSLOT - RA ? 2 * NB + NQ / 2 : NSLOT - RA - 1);
         constexpr int MOV = 2 * NB;
+        constexpr int KST = NBUF == 3 && DRAW ? BAR + 1 : 2 * NB;   // keep-word store slot
         static_assert(NSLOT % RA == 0, "ring length must divide the slot count");
-        static_assert(BAR + 1 < NB && MOV >= 2 * NB - RA && MOV + RA < NSLOT, "slot events");
+        static_assert((DRAW ? BAR >= 2 * NB - RA && BAR + RA < NSLOT : BAR + 1 < NB) &&
+                          MOV >= 2 * NB - RA && MOV + RA < NSLOT && KST >= 2 * NB,
+                      "slot events");
         constexpr int LPT = 2 * PERW;             // loads per wave per tile
 
         auto op_read = [&](auto ic) -> e16x8 {
@@ -391,7 +433,7 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
             const f32x16 z = {};
             // dropout keep bits of the tile: bit 16*mb + 4*r4 + tt for the
             // lane's row and key 32*mb + 8*r4 + 4*g2 + tt
-            uint32_t kw = 0;
+            uint32_t kw = 0, kwr0 = 0, kwr1 = 0;
             e16x4 dh[4];
             e16x8 dsa[4];
             f32x4 dv;
@@ -465,12 +507,26 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
                 else if constexpr (NBUF == 3)
                     ring[i % RA] = op_read(IC<i + RA - NSLOT>{});   // next tile
                 // after the tile's last Philox call
-                if constexpr (DROP && i == 2 * NB)
+                if constexpr (DRAW && i == KST)
                     if (p.keep)   // (no keep words when they would be too large)
                         keep_store();
+                // Caller's words: the lane's row's two words of the tile
+                // (slot 0), its half's nibbles of each into kw (slot 2;
+                // nibble 2 r4 + g2 of word mb is kw's nibble 4 mb + r4).
+                if constexpr (READW && i == 0) {
+                    const uint32_t *wl = reinterpret_cast<const uint32_t *>(
+                                             lds + cur * BUFB + (int)sizeof(KVBuf<DP>)) +
+                                         64 * w + (lane_here() & 31);
+                    kwr0 = wl[0];
+                    kwr1 = wl[32];
+                }
+                if constexpr (READW && i == 2) {
+                    const uint32_t sh = 4u * (uint32_t)(lane_here() >> 5);
+                    kw = gather_nibbles(kwr0 >> sh) | (gather_nibbles(kwr1 >> sh) << 16);
+                }
                 // Philox calls: block 0's over its S^T / dP^T slots, block 1's
                 // over the next NB slots (before each block's dS)
-                if constexpr (DROP && i < 2 * NB)
+                if constexpr (DRAW && i < 2 * NB)
                     static_for<4>([&](auto rc) {
                         constexpr int r4 = decltype(rc)::value;
                         if constexpr ((i % NB) == r4 * NB / 4)
@@ -608,7 +664,7 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
     }
 }
 
-template <int DP, bool F16, bool LOCAL, bool SOFTCAP, bool DROP>
+template <int DP, bool F16, bool LOCAL, bool SOFTCAP, int DROP>
 static void launch_dq_d(const Params &p, hipStream_t st)
 {
     const int nqt = (p.Sq + DqShape<DP>::ROWS - 1) / DqShape<DP>::ROWS;
@@ -616,7 +672,7 @@ static void launch_dq_d(const Params &p, hipStream_t st)
                        dim3((unsigned)nqt * p.H * p.batch), dim3(DqShape<DP>::THREADS), 0, st, p);
 }
 
-template <bool LOCAL, bool SOFTCAP, bool DROP>
+template <bool LOCAL, bool SOFTCAP, int DROP>
 static hipError_t launch_dq_t(const Params &p, int dpad, hipStream_t st)
 {
 #define FA_DQ_CASE(D)                                                 \
@@ -640,9 +696,10 @@ static hipError_t launch_dq_t(const Params &p, int dpad, hipStream_t st)
 }
 
 // The dropout instantiations build in a translation unit of their own
-// (fa_dq_dropout.hip includes this file with FA_TU_DROPOUT = 1), so that the
+// (fa_dq_dropout.hip and fa_dq_keep.hip include this file with
+// FA_TU_DROPOUT = 1 and 2), so that the
 // two halves compile in parallel.
-template <bool DROP>
+template <int DROP>
 hipError_t launch_dq_v(const Params &p, int dpad, hipStream_t st)
 {
     if (p.softcap > 0.f)
@@ -653,13 +710,16 @@ hipError_t launch_dq_v(const Params &p, int dpad, hipStream_t st)
 }
 
 #if FA_TU_DROPOUT
-template hipError_t launch_dq_v<true>(const Params &, int, hipStream_t);
+template hipError_t launch_dq_v<FA_TU_DROPOUT>(const Params &, int, hipStream_t);
 #else
-extern template hipError_t launch_dq_v<true>(const Params &, int, hipStream_t);
+extern template hipError_t launch_dq_v<1>(const Params &, int, hipStream_t);
+extern template hipError_t launch_dq_v<2>(const Params &, int, hipStream_t);
 
 hipError_t launch_dq(const Params &p, int dpad, hipStream_t st)
 {
-    return p.drop_p > 0.f ? launch_dq_v<true>(p, dpad, st) : launch_dq_v<false>(p, dpad, st);
+    if (!(p.drop_p > 0.f))
+        return launch_dq_v<0>(p, dpad, st);
+    return p.keep_given ? launch_dq_v<2>(p, dpad, st) : launch_dq_v<1>(p, dpad, st);
 }
 #endif
 

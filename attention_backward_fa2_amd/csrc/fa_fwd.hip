@@ -351,6 +351,18 @@ __global__ void __launch_bounds__(FwdShape<DP>::THREADS, 1) fa_fwd_kernel(Params
                 const uint32_t c0 = (uint32_t)(n0 >> 2) + 8 * mb + 2 * r4 + g2;
                 kw |= keep_nibble(c0, (uint32_t)qrow, drop_c2, p) << (16 * mb + 4 * r4);
             };
+            // The tile's keep bits for the backward (p.keep, the caller's
+            // buffer): lane half g writes the word of keys 32*g .. 32*g+31
+            // (word 2t + g) of its row, nibble 2*r4 + g2 of it from lane half
+            // g2 (one exchange between the halves).
+            auto keep_store = [&]() {
+                const uint32_t other = (uint32_t)__shfl_xor((int)kw, 32);
+                const uint32_t n_lo = g2 ? other >> 16 : kw & 0xFFFFu;   // half 0's nibbles
+                const uint32_t n_hi = g2 ? kw >> 16 : other & 0xFFFFu;   // half 1's nibbles
+                const uint32_t word = spread_nibbles(n_lo) | (spread_nibbles(n_hi) << 4);
+                if (qok)
+                    p.keep[((int64_t)(2 * t + g2) * p.H + h) * p.rows + si.ws_row + qrow] = word;
+            };
 
             static_for<NSLOT>([&](auto ic) {
                 constexpr int i = decltype(ic)::value;
@@ -362,6 +374,9 @@ __global__ void __launch_bounds__(FwdShape<DP>::THREADS, 1) fa_fwd_kernel(Params
                         if constexpr (decltype(cc)::value * (2 * NB - 1) / 8 == i)
                             drop_call(cc);
                     });
+                if constexpr (DROP && i == 2 * NB)
+                    if (p.keep)
+                        keep_store();
                 if constexpr (i + RA < NSLOT)
                     ring[i % RA] = op_read(IC<i + RA>{});
                 else if constexpr (NBUF == 3)

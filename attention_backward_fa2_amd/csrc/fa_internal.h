@@ -68,9 +68,12 @@ struct Params {
     uint32_t drop_thr, drop_k0, drop_k1, drop_c3;
     // Keep bits of the separate-dQ backward with dropout: word w of row r of
     // head h (keys 32 w .. 32 w + 31 of the row's sequence, bit x for key
-    // 32 w + x) at keep[(w * H + h) * rows + r]; written by the dQ kernel,
-    // read by the key-tile kernel.  Null otherwise.
+    // 32 w + x) at keep[(w * H + h) * rows + r]; written by the dQ kernel
+    // (keep_given = 0) or by the forward (the caller's words, keep_given =
+    // 1: the dQ kernel reads them), read by the key-tile kernel.  In the
+    // forward: where it writes them.  Null otherwise.
     uint32_t *keep;
+    int keep_given;
     // Debug copy of rowdot in the lse layout (same batch / head strides,
     // row stride 1), written by the preprocess kernel when not null.
     float *rowsum_out;

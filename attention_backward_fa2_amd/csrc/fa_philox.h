@@ -67,6 +67,14 @@ __device__ inline uint32_t spread_nibbles(uint32_t x)
     return (x | (x << 4)) & 0x0F0F0F0Fu;
 }
 
+// The inverse: nibbles 0, 2, 4, 6 of x into nibbles 0 .. 3.
+__device__ inline uint32_t gather_nibbles(uint32_t x)
+{
+    x &= 0x0F0F0F0Fu;
+    x = (x | (x >> 4)) & 0x00FF00FFu;
+    return (x | (x >> 8)) & 0x0000FFFFu;
+}
+
 // Dropout multiplier of a keep bit: 1 / (1 - p) if set, else 0 (the bit
 // sign-extended to a full mask and ANDed with inv's bits: two operations,
 // no compare).

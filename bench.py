@@ -742,6 +742,11 @@ def bench_forward(args, wl, dev):
     lse = torch.empty(wl.batch, wl.heads, wl.seqlen_q, dtype=torch.float32, device=dev)
     a = fa.make_fwd_args(q, k, v, out, lse, wl.scale, wl.causal, window=wl.window,
                          softcap=wl.softcap, dropout=wl.dropout)
+    words = None
+    if args.keep_words and wl.dropout:
+        words = torch.empty(fa.keep_bytes(a) // 4, dtype=torch.int32, device=dev)
+        a.dropout_keep_out = words.data_ptr()
+        a.dropout_keep_out_bytes = words.numel() * 4
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         fa.run_fwd(a, stream)
@@ -768,7 +773,8 @@ def bench_forward(args, wl, dev):
                    "seqlen_q": Sq, "seqlen_k": Sk, "head_dim": D, "causal": wl.causal,
                    "window": list(wl.window) if wl.window else None,
                    "softcap": wl.softcap or None,
-                   "dropout": wl.dropout[0] if wl.dropout else None, "pass": "forward"},
+                   "dropout": wl.dropout[0] if wl.dropout else None, "pass": "forward",
+                   "keep_words_out": words is not None},
         "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
         "flops_per_step": flops,
         "kernel_ms": {"fwd": round(ms, 4)},
@@ -810,6 +816,10 @@ def main():
                     help="head dim other than the workload's (up to 256): times the workload with it")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="dropout probability p > 0: times the workload with it (fixed seed)")
+    ap.add_argument("--keep-words", action="store_true",
+                    help="with --dropout: the forward writes the keep words and the backward "
+                         "reads them instead of drawing the bits (with --forward: times the "
+                         "forward writing them)")
     ap.add_argument("--summarize-profile", metavar="PROF_DIR",
                     help="write the profiles/ summaries from rocprofv3 outputs in PROF_DIR "
                          "(trace/, FETCH_SIZE/, WRITE_SIZE/, copy_FETCH_SIZE/, copy_WRITE_SIZE/)")
@@ -894,13 +904,15 @@ def main():
     if wl.varlen:
         kw = dict(cu_seqlens_q=inp.cu_q.to(dev), cu_seqlens_k=inp.cu_k.to(dev),
                   max_seqlen_q=max(inp.lens_q), max_seqlen_k=max(inp.lens_k))
+    keep_words = None
     if wl.dropout:
         # the backward needs the dropout forward's O: this library's forward
         o = torch.empty_like(q)
         lse = torch.empty(len(inp.lens_q), wl.heads, max(inp.lens_q), dtype=torch.float32,
                           device=dev)
-        fa.fa_fwd(q, k, v, o, lse, wl.scale, wl.causal, window=wl.window, softcap=wl.softcap,
-                  dropout=wl.dropout, **kw)
+        keep_words = fa.fa_fwd(q, k, v, o, lse, wl.scale, wl.causal, window=wl.window,
+                               softcap=wl.softcap, dropout=wl.dropout, keep=args.keep_words,
+                               **kw)
     elif wl.varlen:
         o, lse = forward_inputs_packed(q, k, v, inp.lens_q, inp.lens_k, wl.scale, wl.causal,
                                        wl.window, wl.softcap)
@@ -909,7 +921,8 @@ def main():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     a = fa.make_args(do, q, k, v, o, lse, dq, dk, dv, wl.scale, wl.causal,
                      deterministic=args.deterministic, dq_accumulate=args.dq_accumulate,
-                     window=wl.window, softcap=wl.softcap, dropout=wl.dropout, **kw)
+                     window=wl.window, softcap=wl.softcap, dropout=wl.dropout,
+                     dropout_keep=keep_words, **kw)
     # the steps of one backward, in the order fa_bwd enqueues them
     seq = ["preprocess", "main", "dq_convert"] if args.dq_accumulate else ["dq", "main"]
     ws = fa.alloc_workspace(a, dev)
@@ -983,7 +996,9 @@ def main():
                    "softcap": wl.softcap or None,
                    "dropout": wl.dropout[0] if wl.dropout else None,
                    "dq_mode": ("ordered" if args.deterministic else "atomic")
-                   if args.dq_accumulate else "separate"},
+                   if args.dq_accumulate else "separate",
+                   "keep_words": ("forward" if keep_words is not None else "drawn")
+                   if wl.dropout else None},
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "flops_per_step": flops,
         "ms_per_step_median": round(per_step[K // 2], 4),

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define FA_BWD_ABI_VERSION 9
+#define FA_BWD_ABI_VERSION 10
 
 typedef enum {
     FA_OK = 0,
@@ -153,7 +153,9 @@ typedef enum {
  *   - head_dim padding: head_dim must be a multiple of 8 and <= 256; kernels
  *     run at a padded tile width of 64, 96, 128, 192 or 256 with zero-filled
  *     loads and masked stores (above 128 the key-tile kernel takes 64 keys
- *     per workgroup, two waves per 32 keys splitting the head dim of dK/dV) (sm90 backward page, __init__: head dim rounded up to
+ *     per workgroup, two waves per 32 keys splitting the query rows of S
+ *     and dP and the head dim of dK/dV) (sm90 backward page, __init__: head
+ *     dim rounded up to
  *     the tile multiple; backward call-trace page, dout padding step).
  *   - Reproducibility: with dq_accumulate = 0 every output is a fixed-order
  *     sum, so repeated calls give bit-identical dq, dk, dv whatever
@@ -202,6 +204,18 @@ typedef struct fa_bwd_args {
      * grows with seqlen_q * seqlen_k; above the bound the main step draws the
      * keep bits itself instead (same bits, same results, slower). */
     size_t dropout_keep_max_bytes;
+    /* Optional (dropout_p > 0, dq_accumulate = 0): the keep words a forward
+     * call with the same shapes, p, seed and offset wrote (fa_fwd_args
+     * dropout_keep_out: the layout of the workspace's keep region, 4-byte
+     * aligned, at least fa_fwd_keep_bytes() bytes, stated in
+     * dropout_keep_bytes; FA_ERR_INVALID_ARG otherwise).  The dQ and
+     * key-tile steps then read the bits instead of drawing them
+     * (bit-identical results, no keep region in the workspace).  Contents
+     * are not checked: words of another call give wrong gradients.  NULL:
+     * the steps draw the bits.  Ignored when dropout_p = 0 or dq_accumulate
+     * = 1 (the fused step draws them). */
+    const uint32_t *dropout_keep;
+    size_t dropout_keep_bytes;
 } fa_bwd_args;
 
 /*
@@ -220,8 +234,9 @@ typedef struct fa_bwd_args {
  *                      a caller that relies on deterministic = 1 with
  *                      dq_accumulate = 1 reads flags[0] after the call.
  *   keep   : uint32[keep_words][num_heads][rows]  dropout keep bits (dropout_p
- *            > 0, dq_accumulate = 0 and at most dropout_keep_max_bytes only;
- *            zero bytes and keep_words = 0 otherwise): bit x of
+ *            > 0, dq_accumulate = 0, no dropout_keep words given and at most
+ *            dropout_keep_max_bytes only; zero bytes and keep_words = 0
+ *            otherwise): bit x of
  *            word w of a row is the keep bit of key 32 w + x of its sequence;
  *            keep_words = 2 * ceil(seqlen_k / 64) (max_seqlen_k when packed).
  *            Written by the dq step for every key tile a row's query tile

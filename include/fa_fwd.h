@@ -75,7 +75,25 @@ typedef struct fa_fwd_args {
     float dropout_p;               /* dropout as in fa_bwd_args; 0: none */
     uint64_t philox_seed;
     uint64_t philox_offset;
+    /* Optional (dropout_p > 0): device buffer of dropout_keep_out_bytes >=
+     * fa_fwd_keep_bytes() bytes, 4-byte aligned (FA_ERR_INVALID_ARG
+     * otherwise), that receives the keep bits the call draws, for the
+     * backward's dropout_keep: uint32[keep_words][num_heads][rows] with
+     * keep_words = 2 * ceil(seqlen_k / 64) (the maximum length when packed),
+     * rows and row index as in fa_bwd.h's workspace layout, bit x of word w
+     * of a row the keep bit of key 32 w + x of its sequence.  Only the words
+     * of the 64-key tiles that a 256-row query tile visits are written (128
+     * rows above head_dim 128); the backward reads no others and uses a bit
+     * only where its pair is visible.  The buffer holds one bit per (row,
+     * key) pair of every head: it grows with seqlen_q * seqlen_k.  NULL:
+     * nothing is written.  Ignored when dropout_p = 0. */
+    uint32_t *dropout_keep_out;
+    size_t dropout_keep_out_bytes;
 } fa_fwd_args;
+
+/* Bytes of the keep words of a dropout call (see dropout_keep_out): 0 when
+ * dropout_p = 0 or the arguments are otherwise invalid. */
+size_t fa_fwd_keep_bytes(const fa_fwd_args *args);
 
 /* FA_OK if fa_fwd would accept `args`; otherwise the error it would return. */
 fa_status fa_fwd_validate(const fa_fwd_args *args);

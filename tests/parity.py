@@ -55,10 +55,12 @@ class Prepared:
 
 
 def run_gpu(pr: Prepared, deterministic=False, out_pad=0, step_split=False, dq_accumulate=False,
-            steps=None, keep_max=0):
+            steps=None, keep_max=0, keep_words=None):
     """Backward on cuda:0.  Outputs start as NaN so unwritten elements show.
     out_pad > 0 gives dq/dk/dv a row pitch of head_dim + out_pad (strided
-    views) to check that columns past head_dim are left alone."""
+    views) to check that columns past head_dim are left alone.  keep_words:
+    a forward call's dropout keep words (device tensor) for the backward to
+    read."""
     inp, wl = pr.inp, pr.inp.wl
     dev = torch.device("cuda")
     q, k, v, do = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v, inp.dout))
@@ -80,7 +82,7 @@ def run_gpu(pr: Prepared, deterministic=False, out_pad=0, step_split=False, dq_a
     args = fa.make_args(do, q, k, v, o, lse, dq, dk, dv, wl.scale, wl.causal,
                         deterministic=deterministic, dq_accumulate=dq_accumulate,
                         window=wl.window, softcap=wl.softcap, dropout=wl.dropout,
-                        dropout_keep_max_bytes=keep_max, **kw)
+                        dropout_keep_max_bytes=keep_max, dropout_keep=keep_words, **kw)
     ws = fa.alloc_workspace(args, dev)
     ws.fill_(0xA5)   # garbage: the preprocess must clear what it uses
     if steps is not None:
@@ -139,10 +141,12 @@ def oracle_backward_unit(pr: Prepared, s: int, g: int):
     return (slice(qs, qe), heads, slice(ks, ke), ref)
 
 
-def run_gpu_fwd(inp: W.Inputs):
+def run_gpu_fwd(inp: W.Inputs, keep=False):
     """Forward on cuda:0 through the C ABI.  out and lse start as NaN so
     unwritten elements show.  Returns (out [same layout as q], lse
-    (B|nseq, H, Sq|max_q) fp32), both on the CPU."""
+    (B|nseq, H, Sq|max_q) fp32), both on the CPU; with keep=True also the
+    dropout keep words it wrote (a device int32 tensor that starts as a
+    garbage pattern, so words the forward does not write hold it)."""
     wl = inp.wl
     dev = torch.device("cuda")
     q, k, v = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v))
@@ -157,8 +161,17 @@ def run_gpu_fwd(inp: W.Inputs):
                   max_seqlen_q=maxq, max_seqlen_k=max(inp.lens_k))
     args = fa.make_fwd_args(q, k, v, out, lse, wl.scale, wl.causal, window=wl.window,
                             softcap=wl.softcap, dropout=wl.dropout, **kw)
+    words = None
+    if keep:
+        n = fa.keep_bytes(args)
+        assert n > 0
+        words = torch.full(((n + 3) // 4,), 0x5A5AA5A5, dtype=torch.int32, device=dev)
+        args.dropout_keep_out = words.data_ptr()
+        args.dropout_keep_out_bytes = words.numel() * 4
     fa.run_fwd(args)
     torch.cuda.synchronize()
+    if keep:
+        return out.cpu(), lse.cpu(), words
     return out.cpu(), lse.cpu()
 
 

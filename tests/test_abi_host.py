@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(fa.EXPORTED)
-    assert lib.fa_bwd_abi_version() == 9
+    assert lib.fa_bwd_abi_version() == 10
 
 
 @pytest.mark.parametrize("header,struct,mirror", [
@@ -139,6 +139,39 @@ def test_dropout_keep_region_in_the_separate_dq_mode_only():
                  {"dropout_p": 0.1, "dropout_keep_max_bytes": need - 1}):
         lay = fa.workspace_layout(_args(**over))
         assert lay.keep_words == 0 and lay.total_bytes == lay.off_keep == lay.off_flags + 256
+
+
+def test_forward_keep_words_need_no_keep_region():
+    """Given the forward's keep words, the separate-dQ backward reads them:
+    its workspace has no keep region.  The words are checked for alignment,
+    size (2 * ceil(seqlen_k / 64) words per row of every head) and 31-bit
+    addressability before anything touches the GPU; without dropout or in
+    the accumulate mode they are ignored."""
+    rows = 2 * 256
+    need = 12 * 8 * rows * 4
+    ok = _args(dropout_p=0.1, dropout_keep=BASE + (50 << 30), dropout_keep_bytes=need)
+    lay = fa.workspace_layout(ok)
+    assert lay.keep_words == 0 and lay.total_bytes == lay.off_keep == lay.off_flags + 256
+    assert fa.validate(_with_ws(ok)) == fa.FA_OK
+    for over, status in (({"dropout_keep_bytes": need - 1}, fa.FA_ERR_INVALID_ARG),
+                         ({"dropout_keep": BASE + (50 << 30) + 2}, fa.FA_ERR_INVALID_ARG)):
+        a = _args(dropout_p=0.1, dropout_keep=BASE + (50 << 30), dropout_keep_bytes=need)
+        for k, v in over.items():
+            setattr(a, k, v)
+        assert fa.load_library().fa_bwd_workspace_size(ctypes.byref(a)) == 0
+        assert fa.validate(a) == status
+    # ignored without dropout and in the accumulate mode (a bad pointer passes)
+    for over in ({"dropout_p": 0.0}, {"dropout_p": 0.1, "dq_accumulate": 1}):
+        a = _args(dropout_keep=BASE + 2, dropout_keep_bytes=1, **over)
+        assert fa.validate(_with_ws(a)) == fa.FA_OK
+    # num_heads * rows at 2^29 and above: the 31-bit word offsets would overflow
+    big = _args(batch=1 << 16, seqlen_q=1 << 10, seqlen_k=64, num_heads=8, dropout_p=0.1,
+                dropout_keep=BASE, dropout_keep_bytes=1 << 40,
+                do_stride=(1024 * 8 * 128, 8 * 128, 128), q_stride=(1024 * 8 * 128, 8 * 128, 128),
+                o_stride=(1024 * 8 * 128, 8 * 128, 128), dq_stride=(1024 * 8 * 128, 8 * 128, 128),
+                lse_stride=(8 * 1024, 1024))
+    assert fa.load_library().fa_bwd_workspace_size(ctypes.byref(big)) == 0
+    assert fa.validate(big) == fa.FA_ERR_UNSUPPORTED
 
 
 def test_step_entry_points_check_the_dq_mode_before_launching():
@@ -293,6 +326,31 @@ def _fwd_args(**over):
         else:
             setattr(a, k, v)
     return a
+
+
+def test_forward_keep_bytes_and_checks():
+    """fa_fwd_keep_bytes: 2 * ceil(seqlen_k / 64) words per row of every head
+    (dense rows batch * seqlen_q, packed total_q), 0 without dropout or for
+    invalid arguments; the output buffer is checked for alignment and size."""
+    lib = fa.load_library()
+    a = _fwd_args(dropout_p=0.2)
+    need = 12 * 8 * (2 * 256) * 4
+    assert fa.keep_bytes(a) == need
+    assert fa.keep_bytes(_fwd_args()) == 0
+    assert fa.keep_bytes(_fwd_args(dropout_p=0.2, num_heads_k=3)) == 0
+    packed = _fwd_args(dropout_p=0.2, cu_seqlens_q=BASE, cu_seqlens_k=BASE + 256, total_q=1000,
+                       total_k=1200, batch=5, seqlen_q=300, seqlen_k=700)
+    assert fa.keep_bytes(packed) == 2 * 11 * 8 * 1000 * 4
+    out = BASE + (50 << 30)
+    assert fa.validate_fwd(_fwd_args(dropout_p=0.2, dropout_keep_out=out,
+                                     dropout_keep_out_bytes=need)) == fa.FA_OK
+    for ptr, n in ((out, need - 4), (out + 2, need)):
+        b = _fwd_args(dropout_p=0.2, dropout_keep_out=ptr, dropout_keep_out_bytes=n)
+        assert fa.validate_fwd(b) == fa.FA_ERR_INVALID_ARG
+        assert lib.fa_fwd(ctypes.byref(b), None) == fa.FA_ERR_INVALID_ARG
+        assert "dropout_keep_out" in lib.fa_bwd_last_error().decode()
+    # ignored without dropout
+    assert fa.validate_fwd(_fwd_args(dropout_keep_out=out + 2, dropout_keep_out_bytes=1)) == fa.FA_OK
 
 
 def test_forward_valid_args_pass_validation():

@@ -47,6 +47,14 @@ DROPPED = {
         W.custom("d6", 1, 4, 2, 260, 260, 128, False, seed=406, window=(40, 30),
                  dropout=(0.1, 5, 1))),
 }
+# Cases for the forward's keep words only (above head_dim 128 the forward and
+# dQ kernels take 128 query rows per workgroup).
+KEEP_EXTRA = {
+    "causal_gqa2_d256_p0.25": lambda: W.make_inputs(
+        W.custom("d7", 1, 4, 2, 300, 300, 256, True, seed=407, dropout=(0.25, SEED, 3))),
+    "varlen_noncausal_d192_p0.5": lambda: W.custom_varlen(
+        "d8", [70, 0, 200], [90, 40, 130], 4, 4, 192, False, seed=408, dropout=(0.5, 9, 2)),
+}
 
 
 @pytest.fixture(scope="module")
@@ -239,14 +247,22 @@ def test_dq_pass_writes_the_oracles_keep_bits(gpu_lib, prepared, name):
     kwn, H, rows = lay.keep_words, wl.heads, lay.rows
     assert kwn == 2 * ((max(pr.inp.lens_k) + 63) // 64)
     words = res["ws"][lay.off_keep:lay.off_keep + kwn * H * rows * 4].view(torch.int32)
-    words = words.numpy().view(np.uint32).reshape(kwn, H, rows)
+    _check_words_against_oracle(pr.inp, words.numpy().view(np.uint32).reshape(kwn, H, rows))
+
+
+def _check_words_against_oracle(inp, words):
+    """words[w, h, row]: on every element a row sees, bit j % 32 of word
+    j // 32 equals the oracle's keep bit."""
+    wl = inp.wl
+    H = wl.heads
+    cu_q = PT.cu_np(inp.lens_q)
     p, seed, offset = wl.dropout_f32
     lw, rw = wl.window_sizes
     checked = 0
-    for s, (lq, lk) in enumerate(zip(pr.inp.lens_q, pr.inp.lens_k)):
+    for s, (lq, lk) in enumerate(zip(inp.lens_q, inp.lens_k)):
         if lq == 0 or lk == 0:
             continue
-        r0 = int(pr.cu_q[s]) if wl.varlen else s * wl.seqlen_q
+        r0 = int(cu_q[s]) if wl.varlen else s * wl.seqlen_q
         i = np.arange(lq)[:, None]
         j = np.arange(lk)[None, :]
         d = i + lk - lq
@@ -263,6 +279,51 @@ def test_dq_pass_writes_the_oracles_keep_bits(gpu_lib, prepared, name):
             assert np.array_equal(got[vis], ref[vis]), (s, h)
             checked += int(vis.sum())
     assert checked > 0
+
+
+KEEP_CASES = ["causal_gqa2_d128_p0.25", "varlen_causal_left64_cap1.5_d96_p0.25",
+              "causal_sq_gt_sk_empty_rows_d128_p0.125", "two_sided_window_d128_p0.1",
+              "noncausal_sq_lt_sk_d64_p0.5"] + list(KEEP_EXTRA)
+
+
+def _keep_inputs(prepared, name):
+    return prepared(name) if name in DROPPED else PT.Prepared(KEEP_EXTRA[name]())
+
+
+@pytest.mark.parametrize("name", KEEP_CASES)
+def test_forward_writes_the_oracles_keep_bits(gpu_lib, prepared, name):
+    """fa_fwd with dropout_keep_out writes the keep words in the workspace
+    layout: on every element a row sees, the bit equals the oracle's."""
+    _flush("forward keep words %s" % name)
+    pr = _keep_inputs(prepared, name)
+    wl = pr.inp.wl
+    _, _, words = PT.run_gpu_fwd(pr.inp, keep=True)
+    kwn = 2 * ((max(pr.inp.lens_k) + 63) // 64)
+    rows = sum(pr.inp.lens_q) if wl.varlen else wl.batch * wl.seqlen_q
+    assert words.numel() == kwn * wl.heads * rows
+    _check_words_against_oracle(pr.inp, words.cpu().numpy().view(np.uint32).reshape(
+        kwn, wl.heads, rows))
+
+
+@pytest.mark.parametrize("name", KEEP_CASES)
+def test_backward_reading_the_forwards_keep_words(gpu_lib, prepared, name):
+    """The backward given the forward's words (dropout_keep) reads the bits
+    instead of drawing them: no keep region in the workspace, dq / dk / dv
+    bit-identical to the drawing backward's, also as separate steps."""
+    _flush("backward from forward keep words %s" % name)
+    pr = _keep_inputs(prepared, name)
+    _, _, words = PT.run_gpu_fwd(pr.inp, keep=True)
+    a = PT.run_gpu(pr)
+    b = PT.run_gpu(pr, keep_words=words)
+    c = PT.run_gpu(pr, keep_words=words, step_split=True)
+    assert b["layout"].keep_words == 0 and c["layout"].keep_words == 0
+    for key in ("dq", "dk", "dv"):
+        assert torch.equal(a[key].view(torch.int16), b[key].view(torch.int16)), key
+        assert torch.equal(a[key].view(torch.int16), c[key].view(torch.int16)), key
+    if name in KEEP_EXTRA:
+        ref = PT.oracle_backward(pr)
+        for key in ("dq", "dk", "dv"):
+            PT.compare(pr.inp.packed(b[key]), ref[key], "%s %s" % (name, key))
 
 
 def test_dropout_step_by_step_equals_whole_call(gpu_lib, prepared):
