@@ -118,7 +118,8 @@ SQ_PASSES = [
     "SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY "
     "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS",
     "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_VALU_MFMA_BUSY_CYCLES "
-    "SQ_LDS_BANK_CONFLICT SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_VMEM"]
+    "SQ_LDS_BANK_CONFLICT SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_VMEM",
+    "TCC_HIT_sum TCC_MISS_sum TCC_REQ_sum"]
 
 
 def _kname(raw):
@@ -258,7 +259,9 @@ def summarize_profile(prof_dir, out_dir):
 
     # -- SQ counters per kernel --
     sq = {}
-    for sub in ("sq1", "sq2"):
+    for sub in ["sq%d" % (i + 1) for i in range(len(SQ_PASSES))]:
+        if not os.path.isdir(os.path.join(prof_dir, sub)):
+            continue
         for (k, c), (v, _) in _pmc_means(
                 _find(os.path.join(prof_dir, sub), "counter_collection.csv")).items():
             if "fa::" in k:
@@ -273,13 +276,18 @@ def summarize_profile(prof_dir, out_dir):
     for c in cols:
         lines.append("| %s | %s |" % (c, " | ".join("%.4g" % sq[n].get(c, float("nan"))
                                                       for n in names)))
-    lines += ["", "Derived (SQ_VALU_MFMA_BUSY_CYCLES is summed over the SIMDs):", ""]
+    lines += ["", "Derived (SQ_VALU_MFMA_BUSY_CYCLES is summed over the SIMDs; TCC = the L2, "
+              "summed over its channels and XCDs):", ""]
     for n in names:
         d = sq[n]
         if d.get("SQ_INSTS_MFMA"):
             lines.append("- %s: %.1f VALU instructions per MFMA; %.0f MFMA busy cycles per MFMA"
                          % (n, d["SQ_INSTS_VALU"] / d["SQ_INSTS_MFMA"],
                             d["SQ_VALU_MFMA_BUSY_CYCLES"] / d["SQ_INSTS_MFMA"]))
+        if d.get("TCC_HIT_sum") is not None and d.get("TCC_MISS_sum"):
+            lines.append("- %s: L2 hit rate %.3f (%.4g hits, %.4g misses, %.4g requests)"
+                         % (n, d["TCC_HIT_sum"] / (d["TCC_HIT_sum"] + d["TCC_MISS_sum"]),
+                            d["TCC_HIT_sum"], d["TCC_MISS_sum"], d.get("TCC_REQ_sum", float("nan"))))
     with open(os.path.join(out_dir, "sq_counters_%s.md" % WORKLOAD_TAG), "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
@@ -888,7 +896,8 @@ def main():
                                  softcap=float(args.softcap))
     if args.dropout > 0:
         import dataclasses
-        wl = dataclasses.replace(wl, name="%s_dropout%g" % (wl.name, args.dropout),
+        wl = dataclasses.replace(wl, name="%s_dropout%g%s" % (wl.name, args.dropout,
+                                                              "_keepwords" if args.keep_words else ""),
                                  dropout=(float(args.dropout), 0x243F6A8885A308D3, 0))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
