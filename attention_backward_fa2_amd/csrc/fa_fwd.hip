@@ -480,19 +480,70 @@ __global__ void __launch_bounds__(FwdShape<DP>::THREADS, 1) fa_fwd_kernel(Params
             }
             cur = cur == NBUF - 1 ? 0 : cur + 1;
         };
-        // Masked tiles t_lo .. f_lo-1, unmasked f_lo .. f_hi-1, masked
-        // f_hi .. nkt-1 (three loops: one masked loop entered twice makes
-        // the register allocator spill).
+        // A key tile none of the wave's rows sees: only the tile's shared
+        // work (the barrier that publishes the next tile, the wave's share of
+        // the loads, the read offsets moved to the next buffer, the operand
+        // reads of the next tile's first slots); the running maximum and sum
+        // are unchanged, and the other wave on the SIMD has the matrix unit
+        // to itself.
+        auto skip = [&]() {
+            const int delta = cur == NBUF - 1 ? -(NBUF - 1) * BUFB : BUFB;
+            if constexpr (NBUF == 2)
+                issue(__builtin_amdgcn_readfirstlane(cur ^ 1));
+            else {
+                wait_loads<0>();
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                issue(cur == 0 ? NBUF - 1 : cur - 1);
+            }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                gq[ks] += delta;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                tq[db][0] += delta;
+                tq[db][1] += delta;
+            }
+            if constexpr (NBUF == 2) {
+                wait_loads<0>();
+                __syncthreads();
+            }
+            static_for<RA>([&](auto ic) { ring[decltype(ic)::value] = op_read(ic); });
+            cur = cur == NBUF - 1 ? 0 : cur + 1;
+        };
+        // Key tiles the wave's rows see: tv_lo .. tv_end-1 (none if the wave
+        // has no row).  Skipped t_lo .. tv_lo-1, masked tv_lo .. f_lo-1,
+        // unmasked f_lo .. f_hi-1, masked f_hi .. tv_end-1, skipped tv_end ..
+        // nkt-1 (separate loops: one masked loop entered twice makes the
+        // register allocator spill).  The dQ kernel skips the same tiles of
+        // the same rows, and the key-tile kernel uses a keep bit only where
+        // its pair is visible, so no kernel uses a keep word this call
+        // leaves unwritten.
+        const int rl_w = min(r0w + 31, Lq - 1);   // the wave's last row
+        int tv_lo = t_lo, tv_end = t_lo;
+        if (r0w < Lq) {
+            const int kv_lo = LOCAL ? max(0, r0w + off - p.win_l) : 0;
+            const int kv_hi = p.win_r >= 0 ? min(Lk - 1, rl_w + off + p.win_r) : Lk - 1;
+            if (kv_hi >= kv_lo) {
+                tv_lo = max(t_lo, kv_lo / kFwdKeys);
+                tv_end = max(tv_lo, min(nkt, kv_hi / kFwdKeys + 1));
+            }
+        }
         int t = t_lo;
-        const int m_end = f_lo < f_hi ? f_lo : t_lo;
-        const int u_end = f_lo < f_hi ? f_hi : t_lo;
-        if constexpr (LOCAL)
+        const int m_end = f_lo < f_hi ? f_lo : tv_lo;
+        const int u_end = f_lo < f_hi ? f_hi : tv_lo;
+        if constexpr (LOCAL) {
+            for (; t < tv_lo; ++t)
+                skip();
             for (; t < m_end; ++t)
                 tile(t, IC<1>{});
+        }
         for (; t < u_end; ++t)
             tile(t, IC<0>{});
-        for (; t < nkt; ++t)
+        for (; t < tv_end; ++t)
             tile(t, IC<1>{});
+        for (; t < nkt; ++t)
+            skip();
         // loads issued past the last tile must land before LDS is released
         wait_loads<0>();
     }

@@ -109,7 +109,10 @@ def _states(line):
 def check_kernel(instrs, wrap=True):
     """Violations found in one kernel's instruction list (straight-line scan,
     with wrap: plus the first instructions again after the last, which
-    approximates loop back edges)."""
+    approximates loop back edges).  An unconditional branch or the end of
+    the program ends a straight line: the instruction after it is reached
+    only by a jump, so nothing pending carries over (a conditional branch
+    falls through and does carry)."""
     seq = instrs + instrs[:64] if wrap else list(instrs)
     found = []
     pend_res = []   # (index, result regs, states elapsed)
@@ -149,6 +152,8 @@ def check_kernel(instrs, wrap=True):
         # age the pending lists by this instruction's states
         pend_res = [(j, r, el + w) for (j, r, el) in pend_res if el + w < 12]
         pend_sw = [(j, r, el + w) for (j, r, el) in pend_sw if el + w < 5]
+        if op in ("s_branch", "s_endpgm", "s_setpc_b64"):
+            pend_res, pend_sw = [], []
         if op.startswith("v_mfma") and a and a[0].startswith("v"):
             res = _regs(a[0])
             # an MFMA accumulating into these registers restarts the window

@@ -27,6 +27,11 @@ def test_scanner_flags_each_hazard_kind():
     assert check([mfma, "s_nop 11", "v_add_f32_e32 v20, v3, v3"]) == []
     # an accumulation chain is not a hazard
     assert check([mfma, mfma]) == []
+    # a conditional branch falls through; after an unconditional one the
+    # next instruction is reached by a jump only
+    assert [f[0] for f in check([mfma, "s_cbranch_scc1 5", "v_add_f32_e32 v20, v3, v3"])] == \
+        ["mfma_result"]
+    assert check([mfma, "s_branch 5", "v_add_f32_e32 v20, v3, v3"]) == []
     # a descriptor restored by v_readlane right before an LDS-DMA load
     load = "buffer_load_dwordx4 v1, s[12:15], 0 offen lds"
     assert [f[0] for f in check(["v_readlane_b32 s13, v200, 3", load])] == ["vmem_sgpr"]
