@@ -568,6 +568,27 @@ def workload_flops(wl, lens_q, lens_k):
     return conv, exact
 
 
+def dq_add_bytes(wl, lens_q, lens_k):
+    """Bytes of fp32 dQ partial adds of one accumulate-mode backward (method
+    overhead): each 128-key tile adds its partial over the valid rows of
+    every 64-row query tile it visits, head_dim columns of 4 bytes (the
+    key-tile kernel's block bounds, causal bottom-right and window)."""
+    left, right = wl.window if wl.window is not None else (-1, -1)
+    if wl.causal:
+        right = 0 if right < 0 else min(right, 0)
+    total = 0
+    for lq, lk in zip(lens_q, lens_k):
+        off = lk - lq
+        for n0 in range(0, lk, 128):
+            first = max(0, n0 - off - right) if right >= 0 else 0
+            last = min(lq - 1, min(lk - 1, n0 + 127) - off + left) if left >= 0 else lq - 1
+            if first > last:
+                continue
+            m0, m1 = first // 64, last // 64 + 1
+            total += sum(min(64, lq - 64 * m) for m in range(m0, m1))
+    return total * wl.heads * wl.head_dim * 4
+
+
 def forward_inputs_torch(q, k, v, scale, causal, window=None, softcap=0.0):
     """O (bf16) and natural-log LSE (fp32, (B,H,Sq)) by a plain fp32 torch
     forward, one (batch, head) at a time.  Dense bshd inputs on the GPU."""
@@ -982,6 +1003,7 @@ def main():
     pre_bytes = rows * H * (2 * D * 2 + 4 + 8) + rows * H * 4 * dpad   # accumulate mode
     conv_bytes = rows * H * (4 * dpad + 2 * D)
     main_tflops = main_flops / (main_ms * 1e-3) / 1e12
+    add_bytes = dq_add_bytes(wl, inp.lens_q, inp.lens_k) if args.dq_accumulate else 0
     clock = committed_clock()
     off_flags = fa.workspace_layout(a).off_flags
     flags = ws[off_flags:off_flags + 16].cpu().view(torch.int32)
@@ -1014,12 +1036,22 @@ def main():
         "ms_per_step_min": round(per_step[0], 4),
         "visible_flops_per_step": exact,
         "visible_tflops": round(exact / (ms_per_step * 1e-3) / 1e12, 2),
+        # one exp2 per visible score (the method's count; this design's
+        # separate dQ pass evaluates each a second time)
+        "exp2_per_step": exact / (10.0 * D),
+        "exp2_G_per_s": round(exact / (10.0 * D) / (ms_per_step * 1e-3) / 1e9, 1),
         "kernel_ms": {name: round(t, 4) for name, t in kms.items()},
         "kernel_tflops": {"main": round(main_tflops, 1)} if args.dq_accumulate else
         {"main": round(main_tflops, 1), "dq": round(dq_flops / (kms["dq"] * 1e-3) / 1e12, 1)},
         "hbm_kernels_GBs": {"preprocess": round(pre_bytes / (kms["preprocess"] * 1e-3) / 1e9, 1),
                             "dq_convert": round(conv_bytes / (kms["dq_convert"] * 1e-3) / 1e9, 1)}
         if args.dq_accumulate else {},
+        # accumulate mode: the fp32 dQ partial adds of the key-tile kernel
+        # (method overhead beyond the compulsory bytes), and their rate over
+        # that kernel's time
+        "dq_partial_add": {"bytes": add_bytes,
+                           "GBs_over_main": round(add_bytes / (main_ms * 1e-3) / 1e9, 1)}
+        if args.dq_accumulate else None,
         "roofline": {"bound": "mfma", "achieved": round(main_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
