@@ -109,15 +109,16 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
 
     // Workgroup -> (query tile, batch, KV head, head in group).  Under the
     // causal mask the last query tiles see the most keys, so they come
-    // first; the (batch, KV head) index is the fastest, which keeps the
-    // heads sharing a K/V tile on one XCD of the round-robin dispatch when
-    // batch * Hk is a multiple of the XCD count.
+    // first within the (batch, KV head) groups an XCD runs side by side
+    // (xcd_group_order: the heads and query tiles that share a K/V stream
+    // stay on one XCD when batch * Hk is a multiple of the XCD count).
     const int nbg = p.batch * p.Hk;
     const int nqt = (p.Sq + ROWS - 1) / ROWS;
     const int lin = blockIdx.x;
-    const int bg = lin % nbg;
-    const int hh = (lin / nbg) % p.G;
-    const int mt = nqt - 1 - lin / (nbg * p.G);
+    int u, bg;   // u = (last query tile - mt) * G + hh
+    xcd_group_order(lin, nbg, nqt * p.G, u, bg);
+    const int hh = u % p.G;
+    const int mt = nqt - 1 - u / p.G;
     const int hk = bg % p.Hk, b = bg / p.Hk;
     const int h = hk * p.G + hh;
 

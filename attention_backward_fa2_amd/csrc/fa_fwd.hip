@@ -90,14 +90,15 @@ __global__ void __launch_bounds__(FwdShape<DP>::THREADS, 1) fa_fwd_kernel(Params
     const int lane = tid & 63, l32 = lane & 31, g2 = lane >> 5;
 
     // Workgroup -> (query tile, batch, KV head, head in group), longest
-    // (last query tile under the causal mask) first; the (batch, KV head)
-    // index is the fastest.
+    // (last query tile under the causal mask) first within the (batch, KV
+    // head) groups an XCD runs side by side (xcd_group_order).
     const int nbg = p.batch * p.Hk;
     const int nqt = (p.Sq + ROWS - 1) / ROWS;
     const int lin = blockIdx.x;
-    const int bg = lin % nbg;
-    const int hh = (lin / nbg) % p.G;
-    const int mt = nqt - 1 - lin / (nbg * p.G);
+    int u, bg;   // u = (last query tile - mt) * G + hh
+    xcd_group_order(lin, nbg, nqt * p.G, u, bg);
+    const int hh = u % p.G;
+    const int mt = nqt - 1 - u / p.G;
     const int hk = bg % p.Hk, b = bg / p.Hk;
     const int h = hk * p.G + hh;
 

@@ -272,11 +272,11 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
 
     // Workgroup -> (batch, KV head, key tile).
     //  - default: longest work first.  Key tile 0 sees the most query tiles
-    //    under the causal mask, so all workgroups of key tile 0 (every batch
-    //    and KV head) come first, then key tile 1, ...; the (batch, KV head)
-    //    index is the fast one, which keeps one (batch, KV head) on one XCD
-    //    of the round-robin dispatch when batch * Hk is a multiple of the
-    //    XCD count.
+    //    under the causal mask, so within the (batch, KV head) groups an XCD
+    //    runs side by side, key tile 0 comes first, then key tile 1, ...
+    //    (xcd_group_order: one (batch, KV head) stays on one XCD when batch *
+    //    Hk is a multiple of the XCD count, and the workgroups running on
+    //    an XCD together share few groups' Q / dO streams).
     //  - ordered dQ adds: within one (batch, KV head) the key tiles run in
     //    descending order along the linear id, so every workgroup waits only
     //    on one with a lower id (which the in-order dispatch has already
@@ -289,8 +289,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         j = nt - 1 - (lin % nt);
         bg = lin / nt;
     } else {
-        j = lin / nbg;
-        bg = lin % nbg;
+        xcd_group_order(lin, nbg, nt, j, bg);
     }
     const int hk = bg % p.Hk, b = bg / p.Hk;
 

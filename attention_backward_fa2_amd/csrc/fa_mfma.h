@@ -361,4 +361,35 @@ struct Tile64 {
     static constexpr int RPL = 1024 / PB;           // rows per wave load
 };
 
+// ---- Workgroup order across the XCDs ----
+// The dispatcher hands consecutive workgroups to the eight XCDs in turn, and
+// each XCD has its own L2.  A grid of nbg (batch, KV head) groups times
+// n_inner work items per group (key tiles, or query tiles x heads, heaviest
+// first) is ordered so that a group stays on one XCD (when nbg is a
+// multiple of 8) and the XCD runs the items of a few groups side by side,
+// which then read the same K/V or Q/dO tiles: each XCD takes its groups gs
+// at a time (gs * n_inner about 64 workgroups, two rounds of its 32 CUs),
+// items of the gs groups interleaved, heaviest first.  With two groups per
+// XCD and 32 items (the B=2, Hk=8, 4096-key case) this is the plain order
+// "item-major, group fastest".  lin -> (item u, group bg).
+constexpr int kXcds = 8;
+__device__ inline void xcd_group_order(int lin, int nbg, int n_inner, int &u, int &bg)
+{
+    if (nbg % kXcds != 0) {
+        u = lin / nbg;
+        bg = lin % nbg;
+        return;
+    }
+    const int nb = nbg / kXcds;                 // groups per XCD
+    int gs = n_inner >= 64 ? 1 : 64 / n_inner;  // groups side by side
+    gs = gs < nb ? gs : nb;
+    while (nb % gs != 0)
+        --gs;
+    const int x = lin % kXcds, s = lin / kXcds;
+    const int span = gs * n_inner;
+    const int r = s % span;
+    u = r / gs;
+    bg = x + kXcds * ((s / span) * gs + r % gs);
+}
+
 }  // namespace fa
