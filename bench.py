@@ -878,7 +878,7 @@ def main():
                                       os.path.join(ROOT, "profiles")))
         return
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+        print("bench.py: the library runs on one GPU; --gpus %d is not supported "
               "(the backward splits into independent (batch, KV-head) units that need "
               "no communication; N GPUs would each run 1/N of them)" % args.gpus, file=sys.stderr)
         sys.exit(2)
