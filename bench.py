@@ -744,21 +744,30 @@ def cpu_baseline_fwd(wl, units):
     inp = W.make_inputs(wl)
     G = wl.heads // wl.heads_k
     t_total, flops = 0.0, 0.0
+    cu_q = [0] + list(np.cumsum(inp.lens_q))
+    cu_k = [0] + list(np.cumsum(inp.lens_k))
     for (b, h) in units:
         def f64(t):
             return t.float().numpy().astype(np.float64)
-        q = f64(inp.q[b][:, [h]])
-        k = f64(inp.k[b][:, [h // G]])
-        v = f64(inp.v[b][:, [h // G]])
+        if wl.varlen:   # sequence b of the packed batch
+            q = f64(inp.q[cu_q[b]:cu_q[b + 1], [h]])
+            k = f64(inp.k[cu_k[b]:cu_k[b + 1], [h // G]])
+            v = f64(inp.v[cu_k[b]:cu_k[b + 1], [h // G]])
+        else:
+            q = f64(inp.q[b][:, [h]])
+            k = f64(inp.k[b][:, [h // G]])
+            v = f64(inp.v[b][:, [h // G]])
+        lq, lk = q.shape[0], k.shape[0]
         t0 = time.perf_counter()
-        O.forward(q, k, v, [0, wl.seqlen_q], [0, wl.seqlen_k], wl.scale, wl.causal,
+        O.forward(q, k, v, [0, lq], [0, lk], wl.scale, wl.causal,
                   window=wl.window_sizes, softcap=wl.softcap, dropout=wl.dropout_f32)
         t_total += time.perf_counter() - t0
-        flops += fwd_flops(1, 1, wl.seqlen_q, wl.seqlen_k, wl.head_dim, wl.causal, wl.window)
+        flops += fwd_flops(1, 1, lq, lk, wl.head_dim, wl.causal, wl.window)
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(),
             "kind": "oracle",
-            "sample": "%d of %d (batch, head) units of the workload, fp64 forward, %.1f s"
-                      % (len(units), wl.batch * wl.heads, t_total)}
+            "sample": "%d of %d (%s, head) units of the workload, fp64 forward, %.1f s"
+                      % (len(units), len(inp.lens_q) * wl.heads,
+                         "sequence" if wl.varlen else "batch", t_total)}
 
 
 def bench_forward(args, wl, dev):
@@ -768,9 +777,14 @@ def bench_forward(args, wl, dev):
     inp = W.make_inputs(wl)
     q, k, v = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v))
     out = torch.empty_like(q)
-    lse = torch.empty(wl.batch, wl.heads, wl.seqlen_q, dtype=torch.float32, device=dev)
+    kw = {}
+    if wl.varlen:
+        kw = dict(cu_seqlens_q=inp.cu_q.to(dev), cu_seqlens_k=inp.cu_k.to(dev),
+                  max_seqlen_q=max(inp.lens_q), max_seqlen_k=max(inp.lens_k))
+    lse = torch.empty(len(inp.lens_q), wl.heads, max(inp.lens_q), dtype=torch.float32,
+                      device=dev)
     a = fa.make_fwd_args(q, k, v, out, lse, wl.scale, wl.causal, window=wl.window,
-                         softcap=wl.softcap, dropout=wl.dropout)
+                         softcap=wl.softcap, dropout=wl.dropout, **kw)
     words = None
     if args.keep_words and wl.dropout:
         words = torch.empty(fa.keep_bytes(a) // 4, dtype=torch.int32, device=dev)
@@ -791,7 +805,9 @@ def bench_forward(args, wl, dev):
     wall = time.perf_counter() - t0
     ms = evs[0].elapsed_time(evs[-1]) / K
     B, H, Hk, Sq, Sk, D = wl.batch, wl.heads, wl.heads_k, wl.seqlen_q, wl.seqlen_k, wl.head_dim
-    flops = fwd_flops(B, H, Sq, Sk, D, wl.causal, wl.window)
+    # packed batches: exactly over the visible pairs of each sequence
+    flops = sum(fwd_flops(1, H, lq, lk, D, wl.causal, wl.window)
+                for lq, lk in zip(inp.lens_q, inp.lens_k))
     tf = flops / (ms * 1e-3) / 1e12
     rec = {
         "metric": metric_name(FWD_METRIC, wl), "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -815,7 +831,7 @@ def bench_forward(args, wl, dev):
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:
-        units = [(b, h) for b in range(B) for h in range(H)]
+        units = [(b, h) for b in range(len(inp.lens_q)) for h in range(H)]
         n = min(args.cpu_units, len(units))
         rec["cpu_baseline"] = cpu_baseline_fwd(wl, [units[(i * len(units)) // n]
                                                     for i in range(n)])
@@ -923,9 +939,6 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.forward:
-        if wl.varlen:
-            print("bench.py --forward times dense workloads only", file=sys.stderr)
-            sys.exit(2)
         bench_forward(args, wl, dev)
         return
     inp = W.make_inputs(wl)
