@@ -185,6 +185,17 @@ def lse_rows(inp: W.Inputs, lse: torch.Tensor) -> np.ndarray:
     return rows
 
 
+class _Rows64:
+    """fp64 rows of a packed (rows, H, D) tensor, converted when sliced (a
+    whole fp64 copy of a multi-GB input would take that many GB again)."""
+
+    def __init__(self, t: torch.Tensor):
+        self.t = t
+
+    def __getitem__(self, sl):
+        return to64(self.t[sl])
+
+
 def check_full_size_units(inp: W.Inputs, units=((0, 0), (1, 5))):
     """GPU forward, then the GPU backward on its O and LSE, at a size the
     oracle cannot take whole: each (sequence, KV head) unit's O, LSE and
@@ -195,7 +206,7 @@ def check_full_size_units(inp: W.Inputs, units=((0, 0), (1, 5))):
     pr = Prepared.__new__(Prepared)
     pr.inp = inp
     pr.cu_q, pr.cu_k = cu_np(inp.lens_q), cu_np(inp.lens_k)
-    pr.q64, pr.k64, pr.v64, pr.do64 = (to64(inp.packed(t)) for t in
+    pr.q64, pr.k64, pr.v64, pr.do64 = (_Rows64(inp.packed(t)) for t in
                                        (inp.q, inp.k, inp.v, inp.dout))
     pr.o, pr.lse = out, lse
     res = run_gpu(pr)

@@ -307,3 +307,19 @@ def test_full_size_parity(gpu_lib, cid):
             cid, mode, {k: "%.2e" % v for k, v in errs.items()}, time.time() - t0))
     for key in ("dk", "dv"):   # the two dQ strategies share the dK/dV pass
         assert torch.equal(_bits(runs["atomic"][0][key]), _bits(runs["separate"][0][key])), key
+
+
+@pytest.mark.slow
+def test_tensors_beyond_2gib_sampled_units(gpu_lib):
+    """B = 2112 sequences of 512 rows, 8 query / 2 KV heads, head_dim 128,
+    causal: q, out, dout and dq are 2.2 GB each, so the rows of the last
+    sequences start beyond 2^31 bytes (every kernel forms row addresses in
+    64 bits and keeps 32-bit offsets within a tile).  GPU forward, then the
+    GPU backward on its O and LSE; the first, a middle and the last
+    (sequence, KV head) units against the oracle computed for them alone."""
+    wl = W.custom("beyond_2gib", 2112, 8, 2, 512, 512, 128, True, seed=20261241)
+    inp = W.make_inputs(wl)
+    assert inp.q.numel() * inp.q.element_size() > 2 ** 31
+    assert (2111 * 512 * 8 * 128) * 2 > 2 ** 31   # first row of the last sequence
+    _flush("tensors beyond 2 GiB: inputs drawn")
+    PT.check_full_size_units(inp, units=((0, 0), (1060, 1), (2111, 1)))
