@@ -52,14 +52,20 @@ constexpr int kDqKeys = 64;                 // keys per streamed tile
 // Workgroup shape by padded head dim: up to 128, eight waves (two per SIMD,
 // 256 rows) and three K/V buffers; at 192 and 256 a wave's Q, dO and dQ
 // fragments need all 512 registers of a SIMD, so four waves (128 rows), and
-// three 64-key K/V buffers would not fit the LDS, so two.
-template <int DP>
+// three 64-key K/V buffers would not fit the LDS, so two.  SMALL (head dim
+// 64 only, for grids of few workgroups): four waves of 128 rows with two
+// workgroups per CU (48 KB of LDS each), the same two waves per SIMD at
+// half the granularity, so that the causal mask's uneven query tiles
+// spread over twice as many workgroups.
+template <int DP, bool SMALL = false>
 struct DqShape {
     static constexpr bool BIG = DP > 128;
-    static constexpr int WAVES = BIG ? 4 : 8;
+    static_assert(!SMALL || DP == 64, "the small shape is built for head dim 64");
+    static constexpr int WAVES = BIG || SMALL ? 4 : 8;
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int ROWS = 32 * WAVES;     // query rows per workgroup
     static constexpr int NBUF = BIG ? 2 : 3;
+    static constexpr int PER_CU = SMALL ? 2 : 1;   // workgroups per CU (launch bound)
 };
 
 template <int DP>
@@ -71,14 +77,14 @@ struct __attribute__((aligned(16))) KVBuf {
 // Dropout from the caller's keep words: a tile also carries each wave's two
 // words of the tile's keys for its 32 rows (lane l of the wave's load: word
 // l / 32 of row l % 32).
-template <int DP>
+template <int DP, bool SMALL>
 struct __attribute__((aligned(16))) KVBufKeep : KVBuf<DP> {
-    uint32_t keep[DqShape<DP>::WAVES][64];
+    uint32_t keep[DqShape<DP, SMALL>::WAVES][64];
 };
 
-template <int DP, bool KW = false>
+template <int DP, bool KW, bool SMALL>
 struct __attribute__((aligned(16))) DqSmem {
-    std::conditional_t<KW, KVBufKeep<DP>, KVBuf<DP>> buf[DqShape<DP>::NBUF];
+    std::conditional_t<KW, KVBufKeep<DP, SMALL>, KVBuf<DP>> buf[DqShape<DP, SMALL>::NBUF];
 };
 
 // LOCAL: a left window bounds the visible keys from below (win_l >= 0);
@@ -87,20 +93,22 @@ struct __attribute__((aligned(16))) DqSmem {
 // dropout (drop_p > 0) replayed from the forward's rng state (1: the keep
 // bits drawn here, and written for the key-tile kernel when p.keep is set)
 // or read from the words the forward wrote (2, p.keep).
-template <int DP, bool F16, bool LOCAL, bool SOFTCAP, int DROP>
-__global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Params p)
+template <int DP, bool F16, bool LOCAL, bool SOFTCAP, int DROP, bool SMALL = false>
+__global__ void __launch_bounds__((DqShape<DP, SMALL>::THREADS), (DqShape<DP, SMALL>::PER_CU))
+    fa_bwd_dq_kernel(Params p)
 {
+    using Shape = DqShape<DP, SMALL>;
     constexpr bool DRAW = DROP == 1, READW = DROP == 2;
     constexpr int KS = DP / 16;                  // k-steps over the head dim
     constexpr int DB = DP / 32;                  // 32-wide head-dim blocks
-    constexpr int NBUF = DqShape<DP>::NBUF;
-    constexpr bool BIG = DqShape<DP>::BIG;
-    constexpr int WAVES = DqShape<DP>::WAVES;
-    constexpr int ROWS = DqShape<DP>::ROWS;
+    constexpr int NBUF = Shape::NBUF;
+    constexpr bool BIG = Shape::BIG;
+    constexpr int WAVES = Shape::WAVES;
+    constexpr int ROWS = Shape::ROWS;
     using L = Tile64<DP>;
     constexpr int PERW = L::NLOAD / WAVES;       // 1 KB wave loads per tensor per wave
     static_assert(PERW >= 1 && L::NLOAD % WAVES == 0, "tile load split");
-    __shared__ DqSmem<DP, READW> sm;
+    __shared__ DqSmem<DP, READW, SMALL> sm;
     using Buf = std::remove_reference_t<decltype(sm.buf[0])>;
 
     const int tid = threadIdx.x;
@@ -148,14 +156,14 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
     // load i (LDS row pr holds tile chunk (lane % PCH) ^ swz(pr)).
     // (head dims above 128: formed per load from the lane index instead, as
     // these would hold 16 registers across the loop)
-    constexpr int NVO = DqShape<DP>::BIG ? 1 : PERW;
+    constexpr int NVO = Shape::BIG ? 1 : PERW;
     uint32_t vok[NVO], vov[NVO];
     auto load_off = [&](int i, int ln, int ss) -> uint32_t {
         const int pr = (w * PERW + i) * L::RPL + ln / L::PCH;
         const int c = (ln % L::PCH) ^ swz<L::PCH>(pr);
         return c * 8 < p.D ? (uint32_t)(pr * ss * 2 + c * 16) : kOutOfRange;
     };
-    if constexpr (!DqShape<DP>::BIG) {
+    if constexpr (!Shape::BIG) {
 #pragma unroll
         for (int i = 0; i < PERW; ++i) {
             vok[i] = load_off(i, lane, (int)p.k_ss);
@@ -180,7 +188,7 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
     if constexpr (READW)
         w_next = p.keep + ((int64_t)(2 * t_lo) * p.H + h) * p.rows + si.ws_row + q0 + 32 * w;
     auto issue = [&](int bf) {
-        if constexpr (!DqShape<DP>::BIG)   // (at 256 the pins leave no legal register class)
+        if constexpr (!Shape::BIG)   // (at 256 the pins leave no legal register class)
             keep_scalar_here(n_next, n_left, k_next, v_next);
         const int kv = n_left > 0 ? min(kDqKeys, Lk - n_next) : 0;
         const uint32_t nk = kv ? (uint32_t)((kv - 1) * (int)p.k_ss * 2 + p.D * 2) : 0u;
@@ -196,7 +204,7 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
         --n_left;
         k_next += kstep;
         v_next += vstep;
-        if constexpr (!DqShape<DP>::BIG)   // (at 256 the pins leave no legal register class)
+        if constexpr (!Shape::BIG)   // (at 256 the pins leave no legal register class)
             keep_scalar_here(n_next, n_left, k_next, v_next);
         Buf &kb = sm.buf[bf];
         if constexpr (READW) {
@@ -210,7 +218,7 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
 #pragma unroll
         for (int i = 0; i < PERW; ++i) {
             const int ld = (w * PERW + i) * 1024;
-            if constexpr (DqShape<DP>::BIG) {
+            if constexpr (Shape::BIG) {
                 const int ln = lane_here();
                 load16_to_lds(rk, kb.k + ld, load_off(i, ln, (int)p.k_ss));
                 load16_to_lds(rv, kb.v + ld, load_off(i, ln, (int)p.v_ss));
@@ -308,7 +316,7 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         of[ks] = __builtin_bit_cast(e16x8, __builtin_bit_cast(u32x4, of[ks]) ^ 0x80008000u);
-    if constexpr (DqShape<DP>::BIG) {
+    if constexpr (Shape::BIG) {
         // Q and -dO rows live in accumulation registers (operands of the
         // inline S^T / dP^T products)
 #pragma unroll
@@ -714,12 +722,30 @@ __global__ void __launch_bounds__(DqShape<DP>::THREADS, 1) fa_bwd_dq_kernel(Para
     }
 }
 
+template <int DP, bool F16, bool LOCAL, bool SOFTCAP, int DROP, bool SMALL>
+static void launch_dq_s(const Params &p, hipStream_t st)
+{
+    using S = DqShape<DP, SMALL>;
+    const int nqt = (p.Sq + S::ROWS - 1) / S::ROWS;
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<DP, F16, LOCAL, SOFTCAP, DROP, SMALL>),
+                       dim3((unsigned)nqt * p.H * p.batch), dim3(S::THREADS), 0, st, p);
+}
+
+// MI355X compute units: the small shape is taken at head dim 64 when the
+// standard grid has fewer than two workgroups per CU.
+constexpr int kCus = 256;
+
 template <int DP, bool F16, bool LOCAL, bool SOFTCAP, int DROP>
 static void launch_dq_d(const Params &p, hipStream_t st)
 {
-    const int nqt = (p.Sq + DqShape<DP>::ROWS - 1) / DqShape<DP>::ROWS;
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<DP, F16, LOCAL, SOFTCAP, DROP>),
-                       dim3((unsigned)nqt * p.H * p.batch), dim3(DqShape<DP>::THREADS), 0, st, p);
+    if constexpr (DP == 64) {
+        const int64_t nqt = (p.Sq + DqShape<64>::ROWS - 1) / DqShape<64>::ROWS;
+        if (nqt * p.H * p.batch < 2 * kCus) {
+            launch_dq_s<DP, F16, LOCAL, SOFTCAP, DROP, true>(p, st);
+            return;
+        }
+    }
+    launch_dq_s<DP, F16, LOCAL, SOFTCAP, DROP, false>(p, st);
 }
 
 template <bool LOCAL, bool SOFTCAP, int DROP>

@@ -323,3 +323,25 @@ def test_tensors_beyond_2gib_sampled_units(gpu_lib):
     assert (2111 * 512 * 8 * 128) * 2 > 2 ** 31   # first row of the last sequence
     _flush("tensors beyond 2 GiB: inputs drawn")
     PT.check_full_size_units(inp, units=((0, 0), (1060, 1), (2111, 1)))
+
+
+@pytest.mark.parametrize("shape", [
+    # (B, H, Hk, S): standard dQ shape (8 waves, 256 rows) when the grid of
+    # 256-row workgroups has at least 512 of them, else the small one (two
+    # 128-row workgroups per CU)
+    (2, 32, 8, 2048),   # 8 * 32 * 2 = 512 workgroups: standard
+    (1, 4, 2, 600),     # 3 * 4 * 1 = 12: small
+    (3, 6, 3, 1000),    # 4 * 6 * 3 = 72: small, ragged tail
+])
+def test_head_dim_64_both_dq_shapes(gpu_lib, shape):
+    """Head dim 64, causal GQA: both dQ workgroup shapes against the oracle
+    in the three dQ modes."""
+    B, H, Hk, S = shape
+    _flush("head dim 64 dq shapes %s" % (shape,))
+    pr = PT.Prepared(W.make_inputs(W.custom("d64_%d_%d" % (B, S), B, H, Hk, S, S, 64, True,
+                                            seed=20261250 + S)))
+    ref = PT.oracle_backward(pr)
+    for mode, (acc, det) in MODES.items():
+        res = PT.run_gpu(pr, deterministic=det, dq_accumulate=acc)
+        for key in ("dq", "dk", "dv"):
+            PT.compare(pr.inp.packed(res[key]), ref[key], "d64 %s %s %s" % (shape, mode, key))
