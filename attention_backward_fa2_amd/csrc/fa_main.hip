@@ -683,11 +683,12 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             const int delta = cur == NBUF - 1 ? -(NBUF - 1) * BUFB : BUFB;
 
             f32x16 s[2], dp[2];
-            // dropout keep bits of the tile: bit 16*mb + 4*t + r4 for the
-            // lane's key and row 32*mb + 8*r4 + 4*g2 + t
+            // dropout keep bits of the tile drawn here (Philox): bit 16*mb +
+            // 4*t + r4 for the lane's key and row 32*mb + 8*r4 + 4*g2 + t
             uint32_t kw = 0;
-            u32x4 kq[4];
-            constexpr int KD = NB / 4 > 2 ? 2 : 1;
+            // keep words (KEEP): word t of kq[mb][r4] is row 32*mb + 8*r4 +
+            // 4*g2 + t, and its bit l32 this lane's key
+            u32x4 kq[2][4];
             e16x8 pb[4], dsb[4];
             e16x4 ph[4], dh[4];
             f32x4 l2v[4];
@@ -714,7 +715,8 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 // dS = P (M dP - rowdot), M = keep / (1 - p)
                 float d, pm = x;
                 if constexpr (DROP) {
-                    const float zi = keep_mult(kw, 16 * mb + 4 * t + r4, p.drop_inv);
+                    const float zi = KEEP ? keep_mult(kq[mb][r4][t], l32, p.drop_inv)
+                                          : keep_mult(kw, 16 * mb + 4 * t + r4, p.drop_inv);
                     const float rd_ = rdc[mb][e];
                     d = x * cg * fmaf(zi, rd_ - dp[mb][e], -rd_);
                     pm = x * zi;
@@ -764,7 +766,6 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     key >= Lk ? INT_MAX
                               : (p.win_r >= 0 ? key - q0 - off - p.win_r - 4 * g2 - 32 * mbr : INT_MIN);
                 const int limu_b = LOCAL ? key - q0 - off + p.win_l - 4 * g2 - 32 * mbr : INT_MAX;
-                constexpr int KDB = KS / 4 > 2 ? 2 : 1;
                 e16x8 pbo[2], dso[2], pbx[2], dsx[2];
                 float cgv[SOFTCAP ? 16 : 1];
                 uint8_t *xw = &sm.xch[w][0][0][16 * lane];
@@ -784,7 +785,8 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                         x = qc + t >= limv_b && (!LOCAL || qc + t <= limu_b) ? x : 0.f;
                     float pm = x;
                     if constexpr (DROP)
-                        pm = x * keep_mult(kw, 4 * t + r4, p.drop_inv);
+                        pm = x * (KEEP ? keep_mult(kq[0][r4][t], l32, p.drop_inv)
+                                       : keep_mult(kw, 4 * t + r4, p.drop_inv));
                     keep_here(pm);
                     s[0][e] = x;
                     pv[t] = pm;
@@ -801,7 +803,8 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     const float cg = SOFTCAP ? cgv[SOFTCAP ? e : 0] : 1.f;
                     float d;
                     if constexpr (DROP) {
-                        const float zi = keep_mult(kw, 4 * t + r4, p.drop_inv);
+                        const float zi = KEEP ? keep_mult(kq[0][r4][t], l32, p.drop_inv)
+                                              : keep_mult(kw, 4 * t + r4, p.drop_inv);
                         const float rd_ = rdc[0][e];
                         d = x * cg * fmaf(zi, rd_ - dp[0][e], -rd_);
                     } else {
@@ -826,12 +829,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                         static_for<4>([&](auto rc) {
                             constexpr int r4 = decltype(rc)::value;
                             if constexpr (i == r4 * KS / 4)
-                                kq[r4] = *reinterpret_cast<const u32x4 *>(lds + kv0 + 32 * r4);
-                            if constexpr (i == r4 * KS / 4 + KDB)
-                                static_for<4>([&](auto tc) {
-                                    constexpr int t = decltype(tc)::value;
-                                    kw |= __builtin_amdgcn_ubfe(kq[r4][t], (uint32_t)l32, 1u) << (4 * t + r4);
-                                });
+                                kq[0][r4] = *reinterpret_cast<const u32x4 *>(lds + kv0 + 32 * r4);
                         });
                     if constexpr (DROP && !KEEP && i < KS)
                         static_for<4>([&](auto rc) {
@@ -921,19 +919,13 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 else if constexpr (!TWO)
                     ring[i % RA] = op_read(IC<i + RA - NSLOT>{});   // next tile
                 // Keep words (separate-dQ mode): the four rows of group
-                // (block, r4) read from LDS where the Philox call would be,
-                // this lane's key bit of each moved into kw KD slots later.
+                // (block, r4) read from LDS where the Philox call would be;
+                // the pointwise math takes this lane's key bit of each.
                 if constexpr (KEEP && i < 2 * NB)
                     static_for<4>([&](auto rc) {
                         constexpr int r4 = decltype(rc)::value, mb = i / NB;
                         if constexpr ((i % NB) == r4 * NB / 4)
-                            kq[r4] = *reinterpret_cast<const u32x4 *>(lds + kv0 + 4 * (32 * mb + 8 * r4));
-                        if constexpr ((i % NB) == r4 * NB / 4 + KD)
-                            static_for<4>([&](auto tc) {
-                                constexpr int t = decltype(tc)::value;
-                                kw |= __builtin_amdgcn_ubfe(kq[r4][t], (uint32_t)l32, 1u)
-                                      << (16 * mb + 4 * t + r4);
-                            });
+                            kq[mb][r4] = *reinterpret_cast<const u32x4 *>(lds + kv0 + 4 * (32 * mb + 8 * r4));
                     });
                 // Philox calls: block 0's over its S / dP slots, block 1's
                 // over the next NB slots (before each block's P and dS)
