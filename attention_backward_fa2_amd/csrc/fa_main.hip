@@ -821,6 +821,8 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 static_for<NSB>([&](auto ic) {
                     constexpr int i = decltype(ic)::value;
                     const e16x8 a = ring[i % RA];
+                    if constexpr ((i & 1) == 0 && i + 1 < NSB)   // paired waits, as below
+                        asm volatile("" ::"v"(ring[(i + 1) % RA]));
                     if constexpr (i + RA < NSB)
                         ring[i % RA] = op_read_big(IC<i + RA>{});
                     // keep bits of the block's rows (words or Philox) over
@@ -914,6 +916,11 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             static_for<NSLOT>([&](auto ic) {
                 constexpr int i = decltype(ic)::value;
                 const e16x8 a = ring[i % RA];
+                // One operand wait per two slots: an even slot also waits
+                // for the next slot's read (issued RA - 1 slots ago), so the
+                // odd slot issues no wait of its own.
+                if constexpr ((i & 1) == 0 && i + 1 < NSLOT)
+                    asm volatile("" ::"v"(ring[(i + 1) % RA]));
                 if constexpr (i + RA < NSLOT)
                     ring[i % RA] = op_read(IC<i + RA>{});
                 else if constexpr (!TWO)
