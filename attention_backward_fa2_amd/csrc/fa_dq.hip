@@ -153,22 +153,20 @@ __global__ void __launch_bounds__((DqShape<DP, SMALL>::THREADS), (DqShape<DP, SM
     const int klim = qok ? (p.win_r >= 0 ? min(Lk - 1, qrow + off + p.win_r) : Lk - 1) : -1;
 
     // Global byte offsets of the 16-byte chunk each lane loads for wave
-    // load i (LDS row pr holds tile chunk (lane % PCH) ^ swz(pr)).
-    // (head dims above 128: formed per load from the lane index instead, as
-    // these would hold 16 registers across the loop)
-    constexpr int NVO = Shape::BIG ? 1 : PERW;
-    uint32_t vok[NVO], vov[NVO];
+    // load i (LDS row pr holds tile chunk (lane % PCH) ^ swz(pr)), held in
+    // registers across the loop (at head dims above 128 too: forming them
+    // per load from the lane index took about 17 vector instructions per
+    // load pair, a quarter of the loop).
+    uint32_t vok[PERW], vov[PERW];
     auto load_off = [&](int i, int ln, int ss) -> uint32_t {
         const int pr = (w * PERW + i) * L::RPL + ln / L::PCH;
         const int c = (ln % L::PCH) ^ swz<L::PCH>(pr);
         return c * 8 < p.D ? (uint32_t)(pr * ss * 2 + c * 16) : kOutOfRange;
     };
-    if constexpr (!Shape::BIG) {
 #pragma unroll
-        for (int i = 0; i < PERW; ++i) {
-            vok[i] = load_off(i, lane, (int)p.k_ss);
-            vov[i] = load_off(i, lane, (int)p.v_ss);
-        }
+    for (int i = 0; i < PERW; ++i) {
+        vok[i] = load_off(i, lane, (int)p.k_ss);
+        vov[i] = load_off(i, lane, (int)p.v_ss);
     }
     // Issue the loads of the next key tile into buffer bf (tiles are loaded
     // strictly in order; past the last tile: empty bound, zeros, no memory
@@ -218,14 +216,8 @@ __global__ void __launch_bounds__((DqShape<DP, SMALL>::THREADS), (DqShape<DP, SM
 #pragma unroll
         for (int i = 0; i < PERW; ++i) {
             const int ld = (w * PERW + i) * 1024;
-            if constexpr (Shape::BIG) {
-                const int ln = lane_here();
-                load16_to_lds(rk, kb.k + ld, load_off(i, ln, (int)p.k_ss));
-                load16_to_lds(rv, kb.v + ld, load_off(i, ln, (int)p.v_ss));
-            } else {
-                load16_to_lds(rk, kb.k + ld, vok[i]);
-                load16_to_lds(rv, kb.v + ld, vov[i]);
-            }
+            load16_to_lds(rk, kb.k + ld, vok[i]);
+            load16_to_lds(rv, kb.v + ld, vov[i]);
         }
     };
     // The first key tiles (two with three buffers, one with two) are in

@@ -783,11 +783,17 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     }
                     if constexpr (decltype(maskc)::value)
                         x = qc + t >= limv_b && (!LOCAL || qc + t <= limu_b) ? x : 0.f;
+                    // (without dropout P itself is pinned: pinning a copy
+                    // would cost a register move per element)
                     float pm = x;
-                    if constexpr (DROP)
+                    if constexpr (DROP) {
                         pm = x * (KEEP ? keep_mult(kq[0][r4][t], l32, p.drop_inv)
                                        : keep_mult(kw, 4 * t + r4, p.drop_inv));
-                    keep_here(pm);
+                        keep_here(pm);
+                    } else {
+                        keep_here(x);
+                        pm = x;
+                    }
                     s[0][e] = x;
                     pv[t] = pm;
                     if constexpr (t == 3) {
@@ -848,12 +854,10 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                             mfma32_vacc<F16>(s[0], a, kf[i]);
                     } else if constexpr (i < VO) {
                         constexpr int ks = i - KS;
-                        if constexpr (ks == 0) {
-                            dp[0] = rdc[0];   // a vector copy: FRESH waits for it
-                            mfma32_vacc<F16, true>(dp[0], a, vf[0]);
-                        } else {
+                        if constexpr (ks == 0)   // from rowdot, without a copy
+                            mfma32_vc<F16>(dp[0], a, vf[0], rdc[0]);
+                        else
                             mfma32_vacc<F16>(dp[0], a, vf[ks]);
-                        }
                     } else {
                         constexpr int u = i - VO, grp = u / (2 * DBL), kl = (u % (2 * DBL)) / DBL, db = u % DBL;
                         if constexpr (grp == 0) {

@@ -89,6 +89,20 @@ __device__ inline void mfma32_vacc(f32x16 &d, e16x8 a, e16x8 b)   // d += A B
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
 
+// d = A B + c into ordinary registers, c from other registers (the initial
+// value several products share); the two wait states cover a c just
+// written by vector instructions.
+template <bool F16>
+__device__ inline void mfma32_vc(f32x16 &d, e16x8 a, e16x8 b, const f32x16 &c)
+{
+    if constexpr (F16)
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %3"
+                     : "=&v"(d) : "v"(a), "a"(b), "v"(c));
+    else
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3"
+                     : "=&v"(d) : "v"(a), "a"(b), "v"(c));
+}
+
 // 12 wait states, ordered after the last product into s and t and before
 // any read of them.
 __device__ inline void mfma_settle(f32x16 &s, f32x16 &t)
