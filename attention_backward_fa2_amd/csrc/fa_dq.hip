@@ -503,6 +503,11 @@ __global__ void __launch_bounds__((DqShape<DP, SMALL>::THREADS), (DqShape<DP, SM
             static_for<NSLOT>([&](auto ic) {
                 constexpr int i = decltype(ic)::value;
                 const e16x8 a = ring[i % RA];
+                // Above 128 (one wave per SIMD): one operand wait per two
+                // slots, an even slot also waiting for the next slot's read.
+                // (With two waves per SIMD the other wave covers the waits.)
+                if constexpr (BIG && (i & 1) == 0 && i + 1 < NSLOT)
+                    asm volatile("" ::"v"(ring[(i + 1) % RA]));
                 if constexpr (i + RA < NSLOT)
                     ring[i % RA] = op_read(IC<i + RA>{});
                 else if constexpr (NBUF == 3)
@@ -541,12 +546,10 @@ __global__ void __launch_bounds__((DqShape<DP, SMALL>::THREADS), (DqShape<DP, SM
                     // kernel does
                     constexpr int mb = i / NB, jj = i % NB, ks = jj >> 1;
                     if constexpr ((jj & 1) != 0) {
-                        if constexpr (ks == 0) {
-                            dpt[mb] = rdt;   // a vector copy: FRESH waits for it
-                            mfma32_vacc<F16, true>(dpt[mb], a, of[ks]);
-                        } else {
+                        if constexpr (ks == 0)   // from rowdot, without a copy
+                            mfma32_vc<F16>(dpt[mb], a, of[ks], rdt);
+                        else
                             mfma32_vacc<F16>(dpt[mb], a, of[ks]);
-                        }
                     } else if constexpr (ks == 0) {
                         mfma32_vz<F16>(st[mb], a, qf[ks]);
                     } else {
