@@ -46,12 +46,18 @@ KERNEL_SOURCES = ["attention_backward_fa2_amd/csrc/fa_main.hip",
 TRAFFIC_SUMMARY = "profiles/hbm_traffic_main_kernel_gqa_b2_h32_hk8_s4096_d128_causal.json"
 TRACE_SUMMARY = "profiles/kernel_trace_gqa_b2_h32_hk8_s4096_d128_causal.md"
 MAIN_KERNEL = "fa_bwd_main_kernel<128, false, false, false, false, 0>"
+# The headline's other launch, the query-tile dQ kernel, and its sources.
+DQ_KERNEL = "fa_bwd_dq_kernel<128, false, false, false, 0, false>"
+DQ_SOURCES = ["attention_backward_fa2_amd/csrc/fa_dq.hip",
+              "attention_backward_fa2_amd/csrc/fa_mfma.h",
+              "attention_backward_fa2_amd/csrc/fa_philox.h",
+              "attention_backward_fa2_amd/csrc/fa_internal.h"]
 
 
-def kernel_source_hash():
+def kernel_source_hash(files=None):
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files or KERNEL_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -253,6 +259,24 @@ def summarize_profile(prof_dir, out_dir):
                   "bytes_per_launch": kib * 1024.0 * factor}
     res["traffic_bytes_per_launch"] = (res["FETCH_SIZE"]["bytes_per_launch"] +
                                        res["WRITE_SIZE"]["bytes_per_launch"])
+    # The dQ kernel of the same runs, with its compulsory bytes: Q, dO, O
+    # (for the row sums), K, V and LSE read, dQ and the two row vectors
+    # written.
+    import workloads as W
+    wl = W.WORKLOADS[3]
+    rows, krows = wl.batch * wl.seqlen_q * wl.heads, wl.batch * wl.seqlen_k * wl.heads_k
+    dq = {"kernel": DQ_KERNEL, "source_files": DQ_SOURCES,
+          "source_sha256": kernel_source_hash(DQ_SOURCES),
+          "algorithmic_bytes_per_launch": (3 * rows * wl.head_dim * 2 + 2 * krows * wl.head_dim * 2
+                                           + rows * 4 + rows * wl.head_dim * 2 + 2 * rows * 4)}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        m = _pmc_means(_find(os.path.join(prof_dir, c), "counter_collection.csv"))
+        kib, n = next(v for (k, cn), v in m.items() if DQ_KERNEL in k and cn == c)
+        dq[c] = {"kib_per_dispatch": kib, "dispatches": n,
+                 "bytes_per_launch": kib * 1024.0 * res[c]["scale_factor"]}
+    dq["traffic_bytes_per_launch"] = (dq["FETCH_SIZE"]["bytes_per_launch"] +
+                                      dq["WRITE_SIZE"]["bytes_per_launch"])
+    res["dq_kernel"] = dq
     with open(os.path.join(out_dir, os.path.basename(TRAFFIC_SUMMARY)), "w") as fh:
         json.dump(res, fh, indent=1)
         fh.write("\n")
