@@ -348,18 +348,27 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         const int total = p.G * nm;
         const int nt_b = (Lk + KT - 1) / KT;
 
-        // Global byte offset of the 16-byte chunk each lane loads for wave
-        // load i of this wave: LDS row pr, LDS chunk lane % PCH, which holds
-        // tile chunk c = (lane % PCH) ^ swz(pr).  Chunks past head_dim (and
-        // the unused chunks of a padded row) load zeros.
-        uint32_t voq[L::PERW], vod[L::PERW];
+        // Tile loads: waves 0 and 1 load the Q tile, waves 2 and 3 the dO
+        // tile (half a tile, 2 PERW wave loads, each), so that every wave
+        // moves one row pointer and forms one descriptor per tile.  Global
+        // byte offset of the 16-byte chunk each lane loads for wave load i
+        // of this wave: LDS row pr, LDS chunk lane % PCH, which holds tile
+        // chunk c = (lane % PCH) ^ swz(pr).  Chunks past head_dim (and the
+        // unused chunks of a padded row) load zeros.
+        constexpr int MLD = 2 * L::PERW;        // Q or dO wave loads of a wave
+        const bool dow = w >= 2;                // (wave-uniform)
+        const int mss = dow ? (int)p.do_ss : (int)p.q_ss;
+        const int64_t msh = dow ? p.do_sh : p.q_sh;
+        // LDS byte offset of the wave's first load in a tile buffer (Q then
+        // dO in the buffer)
+        const int mlds = (dow ? L::BYTES : 0) + (w & 1) * MLD * 1024;
+        uint32_t vom[MLD];
 #pragma unroll
-        for (int i = 0; i < L::PERW; ++i) {
-            const int pr = (w * L::PERW + i) * L::RPL + lane / L::PCH;
+        for (int i = 0; i < MLD; ++i) {
+            const int pr = ((w & 1) * MLD + i) * L::RPL + lane / L::PCH;
             const int c = (lane % L::PCH) ^ swz<L::PCH>(pr);
             const bool ok = c * 8 < p.D;
-            voq[i] = ok ? (uint32_t)(pr * (int)p.q_ss * 2 + c * 16) : kOutOfRange;
-            vod[i] = ok ? (uint32_t)(pr * (int)p.do_ss * 2 + c * 16) : kOutOfRange;
+            vom[i] = ok ? (uint32_t)(pr * mss * 2 + c * 16) : kOutOfRange;
         }
 
         // LDS byte offsets of this lane's operand reads in the current
@@ -440,12 +449,13 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         const int q0_first = (ascending ? m_begin : m_end - 1) * kQTile;
         const int dq0 = ascending ? kQTile : -kQTile;
         const int h0 = hk * p.G;
-        const uint16_t *nq_head = p.q + row_offset(p, b, si.tok_q, q0_first, p.q_sb, p.q_ss) + h0 * p.q_sh;
-        const uint16_t *nd_head =
-            p.dout + row_offset(p, b, si.tok_q, q0_first, p.do_sb, p.do_ss) + h0 * p.do_sh;
+        // the wave's tensor (Q or dO) at the group's first head
+        const uint16_t *nm_head =
+            dow ? p.dout + row_offset(p, b, si.tok_q, q0_first, p.do_sb, p.do_ss) + h0 * p.do_sh
+                : p.q + row_offset(p, b, si.tok_q, q0_first, p.q_sb, p.q_ss) + h0 * p.q_sh;
         // lse2 (even waves) / rowdot (odd waves), see below
         const float *nr_head = ((w & 1) ? p.rowdot : p.lse2) + si.ws_row + (int64_t)h0 * p.rows + q0_first;
-        const uint16_t *nq_ptr = nq_head, *nd_ptr = nd_head;
+        const uint16_t *nm_ptr = nm_head;
         const float *nr_ptr = nr_head;
         // The keep words of the wave's 32 keys (word (n0 + 32 kgrp) / 32)
         // sit a fixed distance from the row vectors of the same (head, row)
@@ -457,25 +467,22 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                      reinterpret_cast<const char *>((w & 1) ? p.rowdot : p.lse2);
         }
         int n_r = 0, n_q0 = q0_first, n_left = total;
-        const int64_t step_q = (int64_t)dq0 * p.q_ss, step_d = (int64_t)dq0 * p.do_ss;
+        const int64_t step_m = (int64_t)dq0 * mss;
         // Buffer descriptors of the next tile (bounded by its valid rows),
-        // formed in three parts (q, dO, row vectors) that can sit in
+        // formed in parts (the wave's Q or dO, row vectors) that can sit in
         // different MFMA slots.
-        u32x4_rsrc rq_n, rd_n, rr_n, rk_n;
+        u32x4_rsrc rm_n, rr_n, rk_n;
         int n_rv = 0;
         auto prep_part = [&](auto pc) {
             constexpr int part = decltype(pc)::value;
             if constexpr (part == 0) {
-                keep_scalar_here(n_left, n_q0, nq_ptr);
+                keep_scalar_here(n_left, n_q0, nm_ptr);
                 n_rv = n_left > 0 ? min(kQTile, Lq - n_q0) : 0;
-                const uint32_t nq = n_rv ? (uint32_t)((n_rv - 1) * (int)p.q_ss * 2 + p.D * 2) : 0u;
-                rq_n = make_rsrc(nq_ptr, nq);
-                keep_scalar_here(rq_n, n_rv);
+                const uint32_t nb = n_rv ? (uint32_t)((n_rv - 1) * mss * 2 + p.D * 2) : 0u;
+                rm_n = make_rsrc(nm_ptr, nb);
+                keep_scalar_here(rm_n, n_rv);
             } else if constexpr (part == 1) {
-                keep_scalar_here(n_rv, nd_ptr);
-                const uint32_t nd = n_rv ? (uint32_t)((n_rv - 1) * (int)p.do_ss * 2 + p.D * 2) : 0u;
-                rd_n = make_rsrc(nd_ptr, nd);
-                keep_scalar_here(rd_n);
+                // (the second tensor's part: the other waves')
             } else {
                 keep_scalar_here(n_rv, nr_ptr);
                 rr_n = make_rsrc(nr_ptr, (uint32_t)n_rv * 4);
@@ -489,19 +496,14 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         };
         // Loads per wave per tile (each Q / dO wave load, lse2 / rowdot, and
         // the keep words).
-        constexpr int LPT = 2 * L::PERW + 1 + (KEEP ? 1 : 0);
+        constexpr int LPT = MLD + 1 + (KEEP ? 1 : 0);
         // Load j of the next tile into buffer bf.
         auto issue_one = [&](auto jc, int bf) {
             constexpr int j = decltype(jc)::value;
             Buf &qbuf = sm.buf[bf];
-            if constexpr (j < 2 * L::PERW) {
-                constexpr int i = j >> 1;
-                const int ld = (w * L::PERW + i) * 1024;
-                if constexpr ((j & 1) != 0)
-                    load16_to_lds(rd_n, qbuf.dO + ld, vod[i]);
-                else
-                    load16_to_lds(rq_n, qbuf.q + ld, voq[i]);
-            } else if constexpr (j == 2 * L::PERW) {
+            if constexpr (j < MLD) {
+                load16_to_lds(rm_n, reinterpret_cast<uint8_t *>(&qbuf) + mlds + j * 1024, vom[j]);
+            } else if constexpr (j == MLD) {
                 // lse2 (even waves) / rowdot (odd waves): the two waves of a
                 // kind write the same values.
                 load4_to_lds(rr_n, (w & 1) ? qbuf.rowdot : qbuf.lse2, (uint32_t)lane * 4);
@@ -512,7 +514,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         // Move the row pointers on to the tile after (branch-free selects),
         // in three parts like the descriptors.
         int n_wrap = 0;
-        // (nq_head, nd_head, nr_head: the group's first head at the current
+        // (nm_head, nr_head: the group's first head at the current
         // query tile.)
         auto advance_part = [&](auto pc) {
             constexpr int part = decltype(pc)::value;
@@ -524,12 +526,10 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 n_q0 = n_wrap ? n_q0 + dq0 : n_q0;
                 keep_scalar_here(n_left, n_r, n_q0, n_wrap);
             } else if constexpr (part == 1) {
-                keep_scalar_here(n_wrap, nq_head, nq_ptr, nd_head, nd_ptr);
-                nq_head = n_wrap ? nq_head + step_q : nq_head;
-                nd_head = n_wrap ? nd_head + step_d : nd_head;
-                nq_ptr = n_wrap ? nq_head : nq_ptr + p.q_sh;
-                nd_ptr = n_wrap ? nd_head : nd_ptr + p.do_sh;
-                keep_scalar_here(nq_head, nq_ptr, nd_head, nd_ptr);
+                keep_scalar_here(n_wrap, nm_head, nm_ptr);
+                nm_head = n_wrap ? nm_head + step_m : nm_head;
+                nm_ptr = n_wrap ? nm_head : nm_ptr + msh;
+                keep_scalar_here(nm_head, nm_ptr);
             } else {
                 keep_scalar_here(n_wrap, nr_head, nr_ptr);
                 nr_head = n_wrap ? nr_head + dq0 : nr_head;
