@@ -12,8 +12,9 @@
 // fp32 accumulator and no convert pass, and the result is bit-reproducible.
 //
 // One workgroup (8 wave64s, two per SIMD) owns 256 query rows of one query
-// head; wave w owns rows 32w .. 32w+31, whose Q and dO rows stay in
-// registers as the B operands of
+// head, or under a left window the same 256 / HPW rows of HPW query heads
+// that share a KV head (HPW = 4 for groups of four); each wave owns 32 rows
+// of one head, whose Q and dO rows stay in registers as the B operands of
 //     S^T  = K Q^T        dP^T = V (-dO)^T + rowdot   (64 keys x 32 rows per wave)
 // for each 64-key tile.  The accumulator of S^T holds one query row and 16
 // keys per lane, so lse2 and rowdot are one register each, and dS (16-bit)
@@ -36,6 +37,7 @@
 // in the tile, where the S^T / dP^T products leave the issue slots idle.
 //
 // LDS (D_pad = 128): 3 x (K, V) x 16 KB = 96 KB.
+#include <algorithm>
 #include <type_traits>
 
 #include "fa_mfma.h"
@@ -104,7 +106,6 @@ __global__ void __launch_bounds__((DqShape<DP, SMALL>::THREADS), (DqShape<DP, SM
     constexpr int NBUF = Shape::NBUF;
     constexpr bool BIG = Shape::BIG;
     constexpr int WAVES = Shape::WAVES;
-    constexpr int ROWS = Shape::ROWS;
     using L = Tile64<DP>;
     constexpr int PERW = L::NLOAD / WAVES;       // 1 KB wave loads per tensor per wave
     static_assert(PERW >= 1 && L::NLOAD % WAVES == 0, "tile load split");
@@ -115,36 +116,50 @@ __global__ void __launch_bounds__((DqShape<DP, SMALL>::THREADS), (DqShape<DP, SM
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, g2 = lane >> 5;
 
-    // Workgroup -> (query tile, batch, KV head, head in group).  Under the
-    // causal mask the last query tiles see the most keys, so they come
-    // first within the (batch, KV head) groups an XCD runs side by side
+    // Workgroup -> (query tile, batch, KV head, heads).  Under a left
+    // window the workgroup's waves cover HPW query heads of one KV head's
+    // group (the largest power of two dividing the group size, at most the
+    // wave count) and, for each, the same RW = 32 * WAVES / HPW query rows:
+    // all heads of a group read the same K/V tiles, so the workgroup's key
+    // range is the window band of RW rows rather than of all its 32 * WAVES
+    // rows, with fewer tiles that only some waves see (256-key window at the
+    // 4096-row GQA shape: this kernel 0.144 -> 0.130 ms).  Without one (HPW =
+    // 1) the band is the whole causal prefix either way and one head's 32 *
+    // WAVES consecutive rows measured as fast or faster.  Under the causal
+    // mask the last query tiles see the most keys, so they come first
+    // within the (batch, KV head) groups an XCD runs side by side
     // (xcd_group_order: the heads and query tiles that share a K/V stream
     // stay on one XCD when batch * Hk is a multiple of the XCD count).
+    const int hpw = LOCAL ? min(p.G & -p.G, WAVES) : 1;   // heads per workgroup
+    const int wph = WAVES / hpw;                 // waves per head
+    const int rw = 32 * wph;                     // query rows per head
+    const int ngrp = p.G / hpw;                  // head sets per group
     const int nbg = p.batch * p.Hk;
-    const int nqt = (p.Sq + ROWS - 1) / ROWS;
+    const int nqt = (p.Sq + rw - 1) / rw;
     const int lin = blockIdx.x;
-    int u, bg;   // u = (last query tile - mt) * G + hh
-    xcd_group_order(lin, nbg, nqt * p.G, u, bg);
-    const int hh = u % p.G;
-    const int mt = nqt - 1 - u / p.G;
+    int u, bg;   // u = (last query tile - mt) * ngrp + head set
+    xcd_group_order(lin, nbg, nqt * ngrp, u, bg);
+    const int mt = nqt - 1 - u / ngrp;
     const int hk = bg % p.Hk, b = bg / p.Hk;
-    const int h = hk * p.G + hh;
+    // the wave's query head and first row (wave-uniform)
+    const int h = hk * p.G + (u % ngrp) * hpw + w / wph;
 
     if (lin == 0 && tid < 4)
         p.flags[tid] = 0;   // the workspace flags (this pass never raises one)
     const SeqInfo si = seq_info(p, b);
-    const int q0 = mt * ROWS;
+    const int q0 = mt * rw;
     if (q0 >= si.Lq)
         return;
     const int Lq = si.Lq, Lk = si.Lk;
     const int off = Lk - Lq;
-    const int qrow = q0 + 32 * w + l32;          // this lane's query row
+    const int r0w = q0 + 32 * (w % wph);
+    const int qrow = r0w + l32;                  // this lane's query row
     const bool qok = qrow < Lq;
     const uint32_t drop_c2 = (uint32_t)(b * p.H + h);   // Philox counter word 2
 
     // Key tiles t_lo .. nkt-1 hold the keys visible to some row of this
     // query tile (rows q0 .. q_last see keys k_lo .. k_hi at most).
-    const int q_last = min(q0 + ROWS, Lq) - 1;
+    const int q_last = min(q0 + rw, Lq) - 1;
     const int k_lo = LOCAL ? max(0, q0 + off - p.win_l) : 0;
     const int k_hi = p.win_r >= 0 ? min(Lk - 1, q_last + off + p.win_r) : Lk - 1;
     const int t_lo = k_lo / kDqKeys;
@@ -184,7 +199,7 @@ __global__ void __launch_bounds__((DqShape<DP, SMALL>::THREADS), (DqShape<DP, SM
     const uint32_t hr4 = READW ? (uint32_t)(p.H * p.rows * 4) : 0u;
     const int64_t wstep = 2 * (int64_t)p.H * p.rows;
     if constexpr (READW)
-        w_next = p.keep + ((int64_t)(2 * t_lo) * p.H + h) * p.rows + si.ws_row + q0 + 32 * w;
+        w_next = p.keep + ((int64_t)(2 * t_lo) * p.H + h) * p.rows + si.ws_row + r0w;
     auto issue = [&](int bf) {
         if constexpr (!Shape::BIG)   // (at 256 the pins leave no legal register class)
             keep_scalar_here(n_next, n_left, k_next, v_next);
@@ -208,7 +223,7 @@ __global__ void __launch_bounds__((DqShape<DP, SMALL>::THREADS), (DqShape<DP, SM
         if constexpr (READW) {
             // lane l: word l / 32 of row l % 32 (rows past the end: zeros)
             const int ln = lane_here();
-            const uint32_t vw = q0 + 32 * w + (ln & 31) < Lq
+            const uint32_t vw = r0w + (ln & 31) < Lq
                                     ? (uint32_t)(ln >> 5) * hr4 + (uint32_t)(ln & 31) * 4u
                                     : kOutOfRange;
             load4_to_lds(rw, kb.keep[w], vw);
@@ -396,7 +411,6 @@ __global__ void __launch_bounds__((DqShape<DP, SMALL>::THREADS), (DqShape<DP, SM
         // past the end) and largest first visible key: key tiles wholly
         // between the two are visible to every row of the wave and need no
         // mask.  They are the tiles f_lo .. f_hi-1 (none if f_lo >= f_hi).
-        const int r0w = q0 + 32 * w;
         const int kmin_w =
             r0w + 31 < Lq ? (p.win_r >= 0 ? min(Lk - 1, r0w + off + p.win_r) : Lk - 1) : -1;
         const int kfirst_w = LOCAL ? r0w + 31 + off - p.win_l : 0;
@@ -708,7 +722,7 @@ __global__ void __launch_bounds__((DqShape<DP, SMALL>::THREADS), (DqShape<DP, SM
         if (d < p.D) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int qr = q0 + 32 * w + 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
+                const int qr = r0w + 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
                 if (qr < Lq)
                     p.dq[row_offset(p, b, si.tok_q, qr, p.dq_sb, p.dq_ss) + h * p.dq_sh + d] =
                         f2elem<F16>(acc[db][r] * p.scale);
@@ -717,13 +731,24 @@ __global__ void __launch_bounds__((DqShape<DP, SMALL>::THREADS), (DqShape<DP, SM
     }
 }
 
+// Workgroups of a shape: per batch and KV head, the head sets of its group
+// times the query tiles of the rows per head (the mapping at the top of the
+// kernel).
+template <int DP, bool SMALL, bool LOCAL>
+static int64_t dq_workgroups(const Params &p)
+{
+    constexpr int WAVES = DqShape<DP, SMALL>::WAVES;
+    const int hpw = LOCAL ? std::min(p.G & -p.G, WAVES) : 1;
+    const int rw = 32 * (WAVES / hpw);
+    return (int64_t)((p.Sq + rw - 1) / rw) * (p.G / hpw) * p.Hk * p.batch;
+}
+
 template <int DP, bool F16, bool LOCAL, bool SOFTCAP, int DROP, bool SMALL>
 static void launch_dq_s(const Params &p, hipStream_t st)
 {
     using S = DqShape<DP, SMALL>;
-    const int nqt = (p.Sq + S::ROWS - 1) / S::ROWS;
     hipLaunchKernelGGL((fa_bwd_dq_kernel<DP, F16, LOCAL, SOFTCAP, DROP, SMALL>),
-                       dim3((unsigned)nqt * p.H * p.batch), dim3(S::THREADS), 0, st, p);
+                       dim3((unsigned)dq_workgroups<DP, SMALL, LOCAL>(p)), dim3(S::THREADS), 0, st, p);
 }
 
 // MI355X compute units: the small shape is taken at head dim 64 when the
@@ -734,8 +759,7 @@ template <int DP, bool F16, bool LOCAL, bool SOFTCAP, int DROP>
 static void launch_dq_d(const Params &p, hipStream_t st)
 {
     if constexpr (DP == 64) {
-        const int64_t nqt = (p.Sq + DqShape<64>::ROWS - 1) / DqShape<64>::ROWS;
-        if (nqt * p.H * p.batch < 2 * kCus) {
+        if (dq_workgroups<64, false, false>(p) < 2 * kCus) {
             launch_dq_s<DP, F16, LOCAL, SOFTCAP, DROP, true>(p, st);
             return;
         }
