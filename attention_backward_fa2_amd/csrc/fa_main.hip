@@ -576,6 +576,16 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         constexpr int NG = 4 * DBL;           // dV / dK MFMAs per two k-steps
         constexpr int NSLOT = 2 * NB + 2 * NG;
         constexpr int RA = 8;                 // read-ahead distance (slots)
+        // Pointwise slots (below): block 0 over NB .. P0E-1, block 1 over
+        // P0E .. P1E-1.  Element 7 of a block must be packed before its
+        // first dV / dK k-step (2NB, 2NB + NG), element 15 before its second
+        // (2NB + NG/2, 2NB + 3NG/2), and block 1 starts after its S / dP.
+        constexpr int P0E = 2 * NB + NG / 8;
+        constexpr int P1E = 2 * NB + 3 * NG / 2 - NG / 8;
+        static_assert(P0E >= 2 * NB && P0E <= 2 * NB + NG / 2 - 1 &&
+                          NB + 7 * (P0E - NB) / 16 < 2 * NB - 1 &&
+                          P0E + 7 * (P1E - P0E) / 16 < 2 * NB + NG - 1 && P1E <= 2 * NB + 3 * NG / 2 - 1,
+                      "pointwise slots");
         // Non-fused (three buffers): the barrier early in the tile, where the
         // S / dP products leave the issue slots idle; the loads of the tile
         // after next and the scalar set-up of the one after that in the
@@ -691,7 +701,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
             u32x4 kq[2][4];
             e16x8 pb[4], dsb[4];
             e16x4 ph[4], dh[4];
-            f32x4 l2v[4];
+            f32x4 l2v[4], l2w[4];   // lse2 of the lane's rows, blocks 0 and 1
             f32x4 pv, dv;
 
             // element e (0..15) of query block mb: exp, mask, dS; packs a
@@ -704,10 +714,10 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                 if constexpr (SOFTCAP) {
                     // capped score tanh * c (base 2); dS picks up 1 - tanh^2
                     const float th = cap_tanh(s[mb][e], p.cap_in);
-                    x = __builtin_amdgcn_exp2f(fmaf(th, p.cap_out, -l2v[r4][t]));
+                    x = __builtin_amdgcn_exp2f(fmaf(th, p.cap_out, -(mb ? l2w : l2v)[r4][t]));
                     cg = fmaf(-th, th, 1.f);
                 } else {
-                    x = __builtin_amdgcn_exp2f(s[mb][e] * p.scale_log2 - l2v[r4][t]);
+                    x = __builtin_amdgcn_exp2f(s[mb][e] * p.scale_log2 - (mb ? l2w : l2v)[r4][t]);
                 }
                 if constexpr (decltype(maskc)::value)
                     x = qc + t >= limv && (!LOCAL || qc + t <= limu) ? x : 0.f;
@@ -983,25 +993,29 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     }
                 }
                 // vector work: the 16 elements of P, dS of block 0 spread over
-                // slots NB .. 2NB-1 (the row vectors of block 1 are read in
-                // the last four of them), of block 1 over 2NB .. 2NB+NG-1
-                if constexpr (i >= NB && i < 2 * NB) {
-                    constexpr int u = i - NB;
+                // slots NB .. P0E-1 and those of block 1 over P0E .. P1E-1
+                // (the row vectors of block 1 are read in four slots of
+                // block 1's S / dP).  The dV / dK k-step kk takes
+                // elements 8 (kk % 2) .. +7 of block kk / 2, so block 0 may
+                // run into the first dV / dK slots and block 1 into the last
+                // ones, which evens out the vector work per MFMA.
+                if constexpr (i >= NB + NB / 2 && i < NB + NB / 2 + 4) {
+                    constexpr int r4 = i - (NB + NB / 2);
+                    l2w[r4] = *reinterpret_cast<const f32x4 *>(l2s + 32 + 8 * r4);
+                }
+                if constexpr (i >= NB && i < P0E) {
+                    constexpr int u = i - NB, n = P0E - NB;
                     if constexpr (u == 0)
                         mfma_settle(s[0], dp[0]);
-                    static_for<16 * (u + 1) / NB - 16 * u / NB>(
-                        [&](auto ec) { pw_elem(IC<0>{}, IC<16 * u / NB + decltype(ec)::value>{}); });
-                    if constexpr (u >= NB - 4) {
-                        constexpr int r4 = u - (NB - 4);
-                        l2v[r4] = *reinterpret_cast<const f32x4 *>(l2s + 32 + 8 * r4);
-                    }
+                    static_for<16 * (u + 1) / n - 16 * u / n>(
+                        [&](auto ec) { pw_elem(IC<0>{}, IC<16 * u / n + decltype(ec)::value>{}); });
                 }
-                if constexpr (i >= 2 * NB && i < 2 * NB + NG) {
-                    constexpr int u = i - 2 * NB;
+                if constexpr (i >= P0E && i < P1E) {
+                    constexpr int u = i - P0E, n = P1E - P0E;
                     if constexpr (u == 0)
                         mfma_settle(s[1], dp[1]);
-                    static_for<16 * (u + 1) / NG - 16 * u / NG>(
-                        [&](auto ec) { pw_elem(IC<1>{}, IC<16 * u / NG + decltype(ec)::value>{}); });
+                    static_for<16 * (u + 1) / n - 16 * u / n>(
+                        [&](auto ec) { pw_elem(IC<1>{}, IC<16 * u / n + decltype(ec)::value>{}); });
                 }
                 if constexpr (i == NB || i == 2 * NB)
                     pin_acc();
