@@ -594,7 +594,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         // read and before the next tile's first, followed by the next
         // tile's rowdot reads.
         constexpr int BAR = 2;                 // barrier slot
-        constexpr int NLD = (LPT + 1) / 2;     // load slots (two loads each)
+        constexpr int NLD = LPT;               // load slots (one load each)
         constexpr int SU0 = BAR + 1 + NLD;     // first of six set-up slots
         constexpr int MOV = NSLOT - RA - 6;    // read offsets to the next buffer
         // The ring of in-flight operands continues across tiles, so its
@@ -1030,16 +1030,15 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
                     __builtin_amdgcn_s_barrier();
                     asm volatile("" ::: "memory");
                 }
-                // The loads of the tile after next, two per slot after the
-                // barrier, into the buffer of the last tile; then the
-                // pointers and descriptors of the tile after that (the
-                // scalar work spread over slots in the MFMAs' shadow).
+                // The loads of the tile after next, one per slot after the
+                // barrier (two per slot measured 0.7% slower at head dim
+                // 128, one every other slot slower still), into the buffer
+                // of the last tile; then the pointers and descriptors of the
+                // tile after that (the scalar work spread over slots in the
+                // MFMAs' shadow).
                 if constexpr (!TWO && i > BAR && i <= BAR + NLD) {
-                    constexpr int j0 = 2 * (i - BAR - 1);
                     const int bf = cur == 0 ? NBUF - 1 : cur - 1;
-                    issue_one(IC<j0>{}, bf);
-                    if constexpr (j0 + 1 < LPT)
-                        issue_one(IC<j0 + 1>{}, bf);
+                    issue_one(IC<i - BAR - 1>{}, bf);
                 }
                 if constexpr (!TWO && i >= SU0 && i < SU0 + 6)
                     setup_part(IC<i - SU0>{});
