@@ -593,7 +593,7 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         // offset move to the next buffer at MOV, after the tile's last such
         // read and before the next tile's first, followed by the next
         // tile's rowdot reads.
-        constexpr int BAR = 2;                 // barrier slot
+        constexpr int BAR = 0;                 // barrier slot (slots 2 and 5 measured slower)
         constexpr int NLD = LPT;               // load slots (one load each)
         constexpr int SU0 = BAR + 1 + NLD;     // first of six set-up slots
         constexpr int MOV = NSLOT - RA - 6;    // read offsets to the next buffer
