@@ -720,9 +720,23 @@ def cpu_baseline(wl, units, inp=None):
                          "sequence" if wl.varlen else "batch", t_total)}
 
 
+def workload_label(wl):
+    """Shape words of a workload in the style of the headline metric
+    ("S=4096 D=128 causal GQA")."""
+    if wl.varlen:
+        shape = "%d seqs L=%d..%d" % (wl.batch, wl.len_lo, wl.len_hi)
+    elif wl.seqlen_q == wl.seqlen_k:
+        shape = "S=%d" % wl.seqlen_q
+    else:
+        shape = "Sq=%d Sk=%d" % (wl.seqlen_q, wl.seqlen_k)
+    heads = "MHA" if wl.heads == wl.heads_k else ("MQA" if wl.heads_k == 1 else "GQA")
+    return "%s D=%d %s %s" % (shape, wl.head_dim, "causal" if wl.causal else "non-causal", heads)
+
+
 def metric_name(base, wl):
-    """The metric label with the variant's head dim and extra features."""
-    name = base.replace("D=128", "D=%d" % wl.head_dim)
+    """The metric label with the workload's shape and extra features (the
+    headline workload gives the base label unchanged)."""
+    name = base.replace("S=4096 D=128 causal GQA", workload_label(wl))
     return name + window_suffix(wl)
 
 
