@@ -18,10 +18,14 @@
 //     S^T  = K Q^T        dP^T = V (-dO)^T + rowdot   (64 keys x 32 rows per wave)
 // for each 64-key tile.  The accumulator of S^T holds one query row and 16
 // keys per lane, so lse2 and rowdot are one register each, and dS (16-bit)
-// is directly the A operand of dQ = dS K with the key index permuted as
-// described in fa_mfma.h; K then enters as a B operand through transposing
-// LDS reads.  dQ (32 x D per wave) accumulates in registers over all key
-// tiles and is scaled and stored once.  In the default mode this kernel
+// is directly the B operand of dQ^T = K^T dS^T with the key index permuted
+// as described in fa_mfma.h; K^T enters as the A operand through
+// transposing LDS reads.  dQ^T (D x 32 rows per wave) accumulates in
+// registers over all key tiles and is scaled and stored once: its
+// accumulator holds one row and runs of four head-dim columns per lane, so
+// the stores are 16 bytes per lane after one exchange between the lane
+// halves (a dQ = dS K accumulator would hold one column and sixteen rows
+// per lane: 2-byte stores, eight times as many).  In the default mode this kernel
 // also forms lse2 and rowdot (written to the workspace for the key-tile
 // kernel, which runs after it).
 //
@@ -50,6 +54,8 @@
 namespace fa {
 
 constexpr int kDqKeys = 64;                 // keys per streamed tile
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Workgroup shape by padded head dim: up to 128, eight waves (two per SIMD,
 // 256 rows) and three K/V buffers; at 192 and 256 a wave's Q, dO and dQ
@@ -589,7 +595,7 @@ __global__ void __launch_bounds__((DqShape<DP, SMALL>::THREADS), (DqShape<DP, SM
                     }
                 } else {
                     constexpr int jj = i - 2 * NB, kk = jj / DB, db = jj % DB;
-                    acc[db] = mfma32<F16>(dsa[kk], a, acc[db]);
+                    acc[db] = mfma32<F16>(a, dsa[kk], acc[db]);   // dQ^T
                     if constexpr (BIG)
                         keep_here_acc(acc[db]);
                     else
@@ -723,21 +729,38 @@ __global__ void __launch_bounds__((DqShape<DP, SMALL>::THREADS), (DqShape<DP, SM
         wait_loads<0>();
     }
 
-    // ---- dQ = scale * acc -> bf16.  Accumulator: column d = 32 db + l32,
-    //      rows 8 (r/4) + 4 g2 + r%4 of the wave's 32 query rows (lane
-    //      index formed again: no register holds it across the loop). ----
+    // ---- dQ = scale * acc -> elements.  Accumulator of head-dim block db:
+    //      column 32 db + 8 (r/4) + 4 g2 + r%4 of the lane's row l32 (lane
+    //      index formed again: no register holds it across the loop).  Per
+    //      pair of 8-column groups (j0 = 2 q, j1 = 2 q + 1) the halves
+    //      trade their 8-byte pieces so that half 0 holds columns 8 j0 ..
+    //      8 j0 + 7 and half 1 columns 8 j1 .. 8 j1 + 7: one 16-byte store
+    //      per lane and pair (columns past head_dim, a multiple of 8, and
+    //      rows past the end are not written). ----
     const int ln = lane_here();
+    const int orow = r0w + (ln & 31), half = ln >> 5;
+    uint16_t *dqrow =
+        p.dq + row_offset(p, b, si.tok_q, orow < Lq ? orow : 0, p.dq_sb, p.dq_ss) + h * p.dq_sh;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-        const int d = 32 * db + (ln & 31);
-        if (d < p.D) {
+        u32x2 pc[4];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int qr = r0w + 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
-                if (qr < Lq)
-                    p.dq[row_offset(p, b, si.tok_q, qr, p.dq_sb, p.dq_ss) + h * p.dq_sh + d] =
-                        f2elem<F16>(acc[db][r] * p.scale);
-            }
+        for (int j = 0; j < 4; ++j) {
+            f32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                v[i] = acc[db][4 * j + i] * p.scale;
+            pc[j] = __builtin_bit_cast(u32x2, to_elem<F16>(v));
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            // lanes 32-63 of pc[2q] <-> lanes 0-31 of pc[2q+1]
+            const auto s0 = __builtin_amdgcn_permlane32_swap(pc[2 * q][0], pc[2 * q + 1][0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(pc[2 * q][1], pc[2 * q + 1][1], false, false);
+            const u32x4 out = {s0[0], s1[0], s0[1], s1[1]};
+            const int col = 32 * db + 16 * q + 8 * half;
+            if (orow < Lq && col < p.D)
+                *reinterpret_cast<u32x4 *>(dqrow + col) = out;
         }
     }
 }
