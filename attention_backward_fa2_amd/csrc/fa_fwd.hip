@@ -43,6 +43,8 @@
 
 namespace fa {
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kFwdKeys = 64;                 // keys per streamed tile
 
 // Workgroup shape by padded head dim (as for the dQ kernel): up to 128,
@@ -545,21 +547,35 @@ __global__ void __launch_bounds__(FwdShape<DP>::THREADS, 1) fa_fwd_kernel(Params
     //      scaled scores); rows without a visible key: O = 0, LSE = -inf. ----
     const float l = lsum + __shfl_xor(lsum, 32);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    if (qok) {
-        uint16_t *orow = p.o_w + row_offset(p, b, si.tok_q, qrow, p.o_sb, p.o_ss) + h * p.o_sh;
+    // O^T accumulator of block db: column 32 db + 8 j + 4 g2 + tt of the
+    // lane's row; per pair of 8-column groups the lane halves (same row)
+    // trade their 8-byte pieces, so each lane stores 16 bytes.
+    {
+        uint16_t *orow = p.o_w + row_offset(p, b, si.tok_q, qok ? qrow : 0, p.o_sb, p.o_ss) + h * p.o_sh;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db) {
+            u32x2 pc[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int d = 32 * db + 8 * j + 4 * g2;
-                if (d < p.D) {
-                    f32x4 o4;
+                f32x4 o4;
 #pragma unroll
-                    for (int tt = 0; tt < 4; ++tt)
-                        o4[tt] = acc[db][4 * j + tt] * inv;
-                    *reinterpret_cast<e16x4 *>(orow + d) = to_elem<F16>(o4);
-                }
+                for (int tt = 0; tt < 4; ++tt)
+                    o4[tt] = acc[db][4 * j + tt] * inv;
+                pc[j] = __builtin_bit_cast(u32x2, to_elem<F16>(o4));
             }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                // lanes 32-63 of pc[2q] <-> lanes 0-31 of pc[2q+1]
+                const auto s0 = __builtin_amdgcn_permlane32_swap(pc[2 * q][0], pc[2 * q + 1][0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(pc[2 * q][1], pc[2 * q + 1][1], false, false);
+                const u32x4 out = {s0[0], s1[0], s0[1], s1[1]};
+                const int d = 32 * db + 16 * q + 8 * g2;
+                if (qok && d < p.D)
+                    *reinterpret_cast<u32x4 *>(orow + d) = out;
+            }
+        }
+    }
+    if (qok) {
         if (g2 == 0)
             p.lse_w[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + qrow] =
                 l > 0.f ? (mrun + __builtin_amdgcn_logf(l)) * 0.6931471805599453f : -INFINITY;

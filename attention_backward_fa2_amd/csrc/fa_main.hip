@@ -59,6 +59,8 @@
 
 namespace fa {
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 // One query tile in LDS: Q and dO in the swizzled layout, lse2, rowdot.
 template <int DP>
 struct __attribute__((aligned(16))) QBuf {
@@ -1148,26 +1150,40 @@ __global__ void __launch_bounds__(kThreads, 1) fa_bwd_main_kernel(Params p)
         wait_loads<0>();
     }
 
-    // ---- epilogue: dK = scale * acc, dV = acc, bf16, keys < Lk, d < D ----
-    if (key < Lk) {
-        uint16_t *dkrow = p.dk + row_offset(p, b, si.tok_k, key, p.dk_sb, p.dk_ss) + hk * p.dk_sh;
-        uint16_t *dvrow = p.dv + row_offset(p, b, si.tok_k, key, p.dv_sb, p.dv_ss) + hk * p.dv_sh;
-#pragma unroll
-        for (int db = 0; db < DBL; ++db) {
+    // ---- epilogue: dK = scale * acc, dV = acc, 16-bit, keys < Lk, d < D.
+    //      Accumulator of head-dim block db: column 32 (dbo + db) + 8 r4 +
+    //      4 g2 + t of the lane's key.  Per pair of 8-column groups the lane
+    //      halves trade their 8-byte pieces (both halves hold the same key),
+    //      so each lane stores 16 bytes: columns 16 q + 8 g2 .. +7 of the
+    //      pair q. ----
+    {
+        uint16_t *dkrow = p.dk + row_offset(p, b, si.tok_k, key < Lk ? key : 0, p.dk_sb, p.dk_ss) + hk * p.dk_sh;
+        uint16_t *dvrow = p.dv + row_offset(p, b, si.tok_k, key < Lk ? key : 0, p.dv_sb, p.dv_ss) + hk * p.dv_sh;
+        auto store16 = [&](uint16_t *row, const f32x16 &acc, float sc, int db) {
+            u32x2 pc[4];
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const int d = 32 * (dbo + db) + 8 * r4 + 4 * g2;
-                if (d < p.D) {
-                    u16x4 kq, vq;
+                f32x4 v;
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        kq[t] = f2elem<F16>(dk_acc[db][4 * r4 + t] * p.scale);
-                        vq[t] = f2elem<F16>(dv_acc[db][4 * r4 + t]);
-                    }
-                    *reinterpret_cast<u16x4 *>(dkrow + d) = kq;
-                    *reinterpret_cast<u16x4 *>(dvrow + d) = vq;
-                }
+                for (int t = 0; t < 4; ++t)
+                    v[t] = acc[4 * r4 + t] * sc;
+                pc[r4] = __builtin_bit_cast(u32x2, to_elem<F16>(v));
             }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                // lanes 32-63 of pc[2q] <-> lanes 0-31 of pc[2q+1]
+                const auto s0 = __builtin_amdgcn_permlane32_swap(pc[2 * q][0], pc[2 * q + 1][0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(pc[2 * q][1], pc[2 * q + 1][1], false, false);
+                const u32x4 out = {s0[0], s1[0], s0[1], s1[1]};
+                const int d = 32 * (dbo + db) + 16 * q + 8 * g2;
+                if (key < Lk && d < p.D)
+                    *reinterpret_cast<u32x4 *>(row + d) = out;
+            }
+        };
+#pragma unroll
+        for (int db = 0; db < DBL; ++db) {
+            store16(dkrow, dk_acc[db], p.scale, db);
+            store16(dvrow, dv_acc[db], 1.f, db);
         }
     }
 }
