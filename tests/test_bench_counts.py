@@ -44,3 +44,16 @@ def test_dq_add_bytes_by_brute_force(lq, lk, causal, window):
                 rows += min(64, lq - q0)
     wl = W.custom("t", 1, 3, 1, lq, lk, 96, causal, seed=1, window=window)
     assert bench.dq_add_bytes(wl, [lq], [lk]) == rows * 3 * 96 * 4
+
+
+def test_tile_kernel_hbm_rates_follow_the_committed_profile(monkeypatch):
+    """The default line's per-kernel HBM GB/s: counter bytes of the committed
+    profile over the kernel times at the headline, none elsewhere, and none
+    for a kernel whose sources changed since the profile."""
+    kms = {"main": 0.5, "dq": 0.4}
+    assert bench.tile_kernel_GBs(kms, False) == {}
+    monkeypatch.setattr(bench, "committed_traffic", lambda: 5.0e8)
+    monkeypatch.setattr(bench, "committed_dq_traffic", lambda: 4.0e8)
+    assert bench.tile_kernel_GBs(kms, True) == {"main": 1000.0, "dq": 1000.0}
+    monkeypatch.setattr(bench, "committed_dq_traffic", lambda: None)
+    assert bench.tile_kernel_GBs(kms, True) == {"main": 1000.0}
