@@ -44,6 +44,13 @@ WINDOWED = {
         window=(64, 16)),
     "varlen_causal_left90_d96": lambda: W.custom_varlen(
         "w9", [100, 257, 64], [100, 257, 64], 2, 2, 96, True, seed=209, window=(90, 0)),
+    # the dQ pass puts the heads of a KV group in one workgroup under a left
+    # window: eight heads of 32 rows each (MQA, ragged), and a group of six
+    # split into three sets of two heads of 128 rows
+    "causal_left70_mqa8_ragged_d128": lambda: W.make_inputs(
+        W.custom("w12", 1, 8, 1, 333, 333, 128, True, seed=212, window=(70, 0))),
+    "left50_right10_gqa6_sq_lt_sk_d128": lambda: W.make_inputs(
+        W.custom("w13", 1, 12, 2, 200, 260, 128, False, seed=213, window=(50, 10))),
 }
 
 
