@@ -57,3 +57,14 @@ def test_tile_kernel_hbm_rates_follow_the_committed_profile(monkeypatch):
     assert bench.tile_kernel_GBs(kms, True) == {"main": 1000.0, "dq": 1000.0}
     monkeypatch.setattr(bench, "committed_dq_traffic", lambda: None)
     assert bench.tile_kernel_GBs(kms, True) == {"main": 1000.0}
+
+
+def test_metric_labels_name_each_workload():
+    """The headline keeps the metric label it is quoted on; the other
+    workloads' lines name their own shape."""
+    assert bench.metric_name(bench.METRIC, W.WORKLOADS[3]) == bench.METRIC
+    labels = {c: bench.metric_name(bench.METRIC, W.WORKLOADS[c]) for c in (1, 2, 4, 5)}
+    assert labels[1].endswith("S=128 D=64 non-causal MHA")
+    assert labels[2].endswith("S=1024 D=64 causal MHA")
+    assert labels[4].endswith("Sq=2048 Sk=8192 D=128 causal GQA")
+    assert "16 seqs" in labels[5] and labels[5].endswith("D=96 causal MHA")
